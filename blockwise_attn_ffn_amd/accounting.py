@@ -1,0 +1,76 @@
+"""FLOP, byte and activation-memory accounting of the BPT layer forward.
+
+Formulas from "Blockwise Parallel Transformer — BPT" (aicassindra.com):
+  * "FLOPs are unchanged": attention 4 N^2 d (QK^T and AV), QKVO projections
+    8 N d^2, FFN (4d) 16 N d^2; attention dominates when N > 6d.
+  * "Memory accounting" and the activation audit of "The bottleneck that survives
+    FlashAttention": per layer 6 N d + 8 N d before fusion, 2 N d + O(b d) after.
+  * "A worked example at 32k context": the BPT tile 8 b d.
+  * "Choosing the block size": one block of b rows re-reads W_1 and W_2 (16 d^2
+    bytes in bf16) for 16 b d^2 FLOPs, so the FFN's intensity is b FLOP per byte.
+  * "On CPUs and small language models": the [N, 4d] hidden state versus a [b, 4d]
+    tile.
+"""
+from __future__ import annotations
+
+
+def attention_flops(n: int, d: int, causal: bool) -> int:
+    """Score and value products of one sequence: 2 matmuls x 2 FLOP per multiply-add.
+    Without a mask 4 N^2 d; with the causal mask only the N (N + 1) / 2 visible
+    (query, key) pairs count, so 2 d N (N + 1)."""
+    return 2 * d * n * (n + 1) if causal else 4 * n * n * d
+
+
+def projection_flops(n: int, d: int) -> int:
+    """W_Q, W_K, W_V, W_O: 4 matmuls of [N, d] x [d, d]."""
+    return 8 * n * d * d
+
+
+def ffn_flops(n: int, d: int, d_ff: int) -> int:
+    """W_1 [d, d_ff] and W_2 [d_ff, d]: 4 N d d_ff, i.e. 16 N d^2 at d_ff = 4d."""
+    return 4 * n * d * d_ff
+
+
+def layer_flops(n: int, d: int, d_ff: int, causal: bool) -> int:
+    """Algorithmic FLOPs of one layer on one sequence of N tokens."""
+    return attention_flops(n, d, causal) + projection_flops(n, d) + ffn_flops(n, d, d_ff)
+
+
+def workload_flops(batch: int, n: int, d: int, d_ff: int, causal: bool, n_layers: int = 1) -> int:
+    return batch * n_layers * layer_flops(n, d, d_ff, causal)
+
+
+def attention_crossover_tokens(d: int) -> int:
+    """Smallest N where 4 N^2 d exceeds 8 N d^2 + 16 N d^2 (N > 6 d), at d_ff = 4d."""
+    return 6 * d + 1
+
+
+def activation_elems_after_flash(n: int, d: int) -> dict:
+    """The per-layer activation audit once the h N^2 logits are gone (elements)."""
+    return {"residual": n * d, "qkv": 3 * n * d, "attn_out_proj": 2 * n * d,
+            "ffn_hidden": 8 * n * d, "rest": 6 * n * d}
+
+
+def logits_elems(n: int, n_heads: int) -> int:
+    return n_heads * n * n
+
+
+def bpt_tile_elems(b: int, d: int) -> int:
+    """The block-shaped live set the fused loop keeps for the FFN: two [b, 4d] tiles."""
+    return 8 * b * d
+
+
+def ffn_block_intensity(b: int) -> float:
+    """FLOP per byte of W_1 + W_2 (bf16) re-read once per block of b rows."""
+    d = 1  # cancels
+    return (16 * b * d * d) / (16 * d * d)
+
+
+def ffn_hidden_bytes(n: int, d_ff: int, bytes_per_elem: int = 2) -> int:
+    """One [N, d_ff] hidden tensor."""
+    return n * d_ff * bytes_per_elem
+
+
+def ffn_tile_bytes(b: int, d_ff: int, bytes_per_elem: int = 2) -> int:
+    """One [b, d_ff] hidden tile."""
+    return b * d_ff * bytes_per_elem

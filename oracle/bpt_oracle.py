@@ -1,0 +1,311 @@
+"""Plain CPU float64 oracle of the Blockwise Parallel Transformer (BPT) layer forward.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import or run this module. It shares no code with the HIP
+library (no kernels, headers, helpers or constants), and imports nothing from it.
+
+Sources (the pages this follows):
+  [BPT]  "Blockwise Parallel Transformer — BPT" (aicassindra.com, transformer_math):
+         sections "The fused blockwise algorithm", "The structural fact that makes
+         fusion legal", "Pitfalls and misconceptions" (causal block skipping).
+  [COST] "transformer-cost" (raminaeye.github.io): the FlashAttention paragraph and
+         its two-tile running-sum example; the causal-mask and pitfalls table.
+
+Notation follows [BPT]: X is the residual stream [N, d]; LN is a layer norm over
+the feature axis; W_Q, W_K, W_V, W_O are [d, d]; W_1 is [d, d_ff], W_2 is
+[d_ff, d]; every projection is y = x @ W (no linear biases); act is GELU with the
+tanh approximation. Matrices here are in that orientation (in, out).
+
+Readings of points the pages leave open (each also listed in the design notes):
+  * LN: biased variance over the feature axis, eps inside the square root,
+    separate (gain, bias) pairs for the attention LN and the FFN LN.
+  * act: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
+  * heads: head h uses columns [h*d_k, (h+1)*d_k) of Q, K, V; scores are scaled by
+    1/sqrt(d_k); head outputs are concatenated in head order before W_O.
+  * causal: query at position p sees key q iff q <= p (positions within one
+    sequence); different sequences of a batch never attend to each other.
+
+Every function below is float64 end to end. "Unfused" functions are the plain
+definition (full softmax, full [N, d_ff] hidden state); the blockwise function is
+the pages' fused loop, written from its description, used to pin the former.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F64 = np.float64
+
+# The weight names of one layer, in the pages' notation.
+WEIGHT_KEYS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o",
+               "ln2_g", "ln2_b", "w_1", "w_2")
+
+
+# ---------------------------------------------------------------------------
+# Row-wise pieces: [BPT] "The structural fact that makes fusion legal"
+# ---------------------------------------------------------------------------
+
+def layer_norm(x: np.ndarray, gain: np.ndarray, bias: np.ndarray, eps: float) -> np.ndarray:
+    """Normalise each row across the feature axis ([BPT] structural-fact section):
+    (x - mean) / sqrt(biased variance + eps) * gain + bias."""
+    x = np.asarray(x, dtype=F64)
+    mean = x.mean(axis=-1, keepdims=True)
+    centred = x - mean
+    var = (centred * centred).mean(axis=-1, keepdims=True)
+    return centred / np.sqrt(var + eps) * np.asarray(gain, F64) + np.asarray(bias, F64)
+
+
+def gelu_tanh(u: np.ndarray) -> np.ndarray:
+    """The tanh form of GELU used as the FFN's act ([BPT] fused algorithm, h_i line)."""
+    u = np.asarray(u, dtype=F64)
+    c = math.sqrt(2.0 / math.pi)
+    return 0.5 * u * (1.0 + np.tanh(c * (u + 0.044715 * u * u * u)))
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax with the row maximum subtracted first ([COST] FlashAttention
+    paragraph). Entries equal to -inf contribute zero; a row with no finite entry
+    is returned as all zeros rather than NaN (the fully-masked-row pitfall in
+    [COST]'s pitfalls table; it cannot occur under the causal mask used here)."""
+    s = np.asarray(s, dtype=F64)
+    m = s.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m)
+    tot = e.sum(axis=-1, keepdims=True)
+    return np.divide(e, tot, out=np.zeros_like(e), where=tot > 0)
+
+
+# ---------------------------------------------------------------------------
+# Attention: the unfused definition
+# ---------------------------------------------------------------------------
+
+def attention_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
+                       causal: bool, q_pos: np.ndarray | None = None) -> np.ndarray:
+    """Multi-head attention of one sequence with a full softmax.
+
+    q: [nq, d] queries at positions q_pos (default 0..nq-1); k, v: [nk, d] keys and
+    values at positions 0..nk-1. Returns the concatenated head outputs [nq, d].
+    Scores are q k^T / sqrt(d_k) ([BPT] fused algorithm, s line); with causal
+    masking key position j is visible to query position p iff j <= p.
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    nq, d = q.shape
+    nk = k.shape[0]
+    dk = d // n_heads
+    if q_pos is None:
+        q_pos = np.arange(nq)
+    out = np.empty((nq, d), dtype=F64)
+    scale = 1.0 / math.sqrt(dk)
+    if causal:
+        hidden = np.arange(nk)[None, :] > np.asarray(q_pos)[:, None]
+    for h in range(n_heads):
+        cols = slice(h * dk, (h + 1) * dk)
+        s = (q[:, cols] @ k[:, cols].T) * scale
+        if causal:
+            s = np.where(hidden, -np.inf, s)
+        out[:, cols] = softmax_rows(s) @ v[:, cols]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The unfused layer (the plain definition the fused loop must reproduce)
+# ---------------------------------------------------------------------------
+
+def _as_f64_layer(p: dict) -> dict:
+    return {k: np.asarray(p[k], dtype=F64) for k in WEIGHT_KEYS}
+
+
+def layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal: bool,
+                  eps: float = 1e-5, return_parts: bool = False):
+    """One pre-LN layer, unfused ([BPT] fused-algorithm section, last paragraph: the
+    whole [N, d] attention output first, then a full [N, d_ff] hidden state).
+
+    x: [B*seq_len, d], sequences stacked row-wise. p: weights in (in, out) form.
+      x1 = LN1(x);  Q, K, V = x1 W_Q, x1 W_K, x1 W_V
+      A  = attention(Q, K, V) per sequence and head
+      Y  = x + A W_O
+      H  = act(LN2(Y) W_1)          (full [N, d_ff])
+      Z  = Y + H W_2
+    """
+    x = np.asarray(x, F64)
+    p = _as_f64_layer(p)
+    rows, d = x.shape
+    assert rows % seq_len == 0
+    x1 = layer_norm(x, p["ln1_g"], p["ln1_b"], eps)
+    q = x1 @ p["w_q"]
+    k = x1 @ p["w_k"]
+    v = x1 @ p["w_v"]
+    a = np.empty_like(x)
+    for s0 in range(0, rows, seq_len):
+        sl = slice(s0, s0 + seq_len)
+        a[sl] = attention_sequence(q[sl], k[sl], v[sl], n_heads, causal)
+    y = x + a @ p["w_o"]
+    hidden = gelu_tanh(layer_norm(y, p["ln2_g"], p["ln2_b"], eps) @ p["w_1"])
+    z = y + hidden @ p["w_2"]
+    if return_parts:
+        return z, dict(x1=x1, q=q, k=k, v=v, a=a, y=y, hidden=hidden)
+    return z
+
+
+def layer_forward_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int,
+                       n_heads: int, causal: bool, eps: float = 1e-5,
+                       row_chunk: int = 4096) -> np.ndarray:
+    """The same layer, evaluated only at the given output rows (global row indices).
+
+    Keys and values are computed for every row a sampled query can see (with
+    causal masking, the prefix of its sequence up to the last sampled row);
+    queries, attention and the row-wise tail only for the sampled rows. Because
+    LN, the FFN and the residual adds act on each row alone ([BPT] structural-fact
+    section), this equals the corresponding rows of layer_forward.
+    K and V are formed in chunks of row_chunk rows purely to bound memory.
+    """
+    x = np.asarray(x, F64)
+    p = _as_f64_layer(p)
+    rows = np.asarray(rows, dtype=np.int64)
+    total, d = x.shape
+    out = np.empty((rows.size, d), dtype=F64)
+    seq_of = rows // seq_len
+    for sidx in np.unique(seq_of):
+        sel = np.nonzero(seq_of == sidx)[0]
+        pos = rows[sel] - sidx * seq_len
+        base = sidx * seq_len
+        n_keys = int(pos.max()) + 1 if causal else seq_len
+        k = np.empty((n_keys, d), F64)
+        v = np.empty((n_keys, d), F64)
+        for c0 in range(0, n_keys, row_chunk):
+            c1 = min(n_keys, c0 + row_chunk)
+            xk = layer_norm(x[base + c0: base + c1], p["ln1_g"], p["ln1_b"], eps)
+            k[c0:c1] = xk @ p["w_k"]
+            v[c0:c1] = xk @ p["w_v"]
+        xq = x[base + pos]
+        q = layer_norm(xq, p["ln1_g"], p["ln1_b"], eps) @ p["w_q"]
+        a = attention_sequence(q, k, v, n_heads, causal, q_pos=pos)
+        y = xq + a @ p["w_o"]
+        hidden = gelu_tanh(layer_norm(y, p["ln2_g"], p["ln2_b"], eps) @ p["w_1"])
+        out[sel] = y + hidden @ p["w_2"]
+    return out
+
+
+def stack_forward(x: np.ndarray, layers: list, *, seq_len: int, n_heads: int,
+                  causal: bool, eps: float = 1e-5) -> np.ndarray:
+    """L layers applied in turn, Z_l = layer_l(Z_{l-1}), in float64 with no rounding
+    between layers and no final LN."""
+    z = np.asarray(x, F64)
+    for p in layers:
+        z = layer_forward(z, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps)
+    return z
+
+
+def stack_forward_rows(x: np.ndarray, layers: list, rows: np.ndarray, *, seq_len: int,
+                       n_heads: int, causal: bool, eps: float = 1e-5) -> np.ndarray:
+    """Sampled rows of the stack's output: every layer but the last in full (a causal
+    row depends on all earlier rows of every earlier layer), the last one at the
+    sampled rows only."""
+    z = np.asarray(x, F64)
+    for p in layers[:-1]:
+        z = layer_forward(z, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps)
+    return layer_forward_rows(z, layers[-1], rows, seq_len=seq_len, n_heads=n_heads,
+                              causal=causal, eps=eps)
+
+
+# ---------------------------------------------------------------------------
+# The pages' fused loop, written from its description ([BPT] fused algorithm)
+# ---------------------------------------------------------------------------
+
+def online_softmax_tiles(s: np.ndarray, v: np.ndarray, tile: int):
+    """Running (m, l, o) over consecutive key tiles of one score row s [n] with value
+    rows v [n, dv] ([BPT] inner loop; [COST] two-tile running-sum example).
+
+    Start m = -inf, l = 0, o = 0; per tile: m' = max(m, max tile), alpha =
+    exp(m - m'), l = alpha l + sum exp(tile - m'), o = alpha o + exp(tile - m') v.
+    Returns (m, l, o); o / l is the softmax-weighted mean of v.
+    """
+    s = np.asarray(s, F64)
+    v = np.asarray(v, F64)
+    m, l, o = -np.inf, 0.0, np.zeros(v.shape[1], F64)
+    for t0 in range(0, s.size, tile):
+        st = s[t0:t0 + tile]
+        m_new = max(m, float(st.max()))
+        if m_new == -np.inf:          # nothing visible yet: state unchanged
+            continue
+        alpha = math.exp(m - m_new) if m > -np.inf else 0.0
+        e = np.exp(st - m_new)
+        l = alpha * l + float(e.sum())
+        o = alpha * o + e @ v[t0:t0 + tile]
+        m = m_new
+    return m, l, o
+
+
+def blockwise_layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int,
+                            causal: bool, block_q: int, block_kv: int,
+                            eps: float = 1e-5) -> np.ndarray:
+    """The fused blockwise layer, one sequence at a time ([BPT] fused algorithm).
+
+    Outer loop over query blocks i; per head an inner loop over key/value blocks j
+    with the running (m, l, o) state, recomputing k_j, v_j = LN(X[j]) W_K,
+    LN(X[j]) W_V inside the inner loop as the pages write it; blocks whose first
+    key lies after the query block's last row are skipped ([BPT] pitfalls: causal
+    block skipping), the rest are masked per element. Then the body finishes the
+    block: y_i = x_i + (o / l) W_O, h_i = act(LN(y_i) W_1), Z[i] = y_i + h_i W_2.
+    Ragged tails (seq_len not a multiple of the block sizes) use shorter last blocks.
+    Slow; meant for small inputs.
+    """
+    x = np.asarray(x, F64)
+    p = _as_f64_layer(p)
+    rows, d = x.shape
+    dk = d // n_heads
+    scale = 1.0 / math.sqrt(dk)
+    z = np.empty_like(x)
+    for s0 in range(0, rows, seq_len):
+        xs = x[s0:s0 + seq_len]
+        for i0 in range(0, seq_len, block_q):
+            i1 = min(seq_len, i0 + block_q)
+            x_i = xs[i0:i1]
+            q_i = layer_norm(x_i, p["ln1_g"], p["ln1_b"], eps) @ p["w_q"]
+            nb = i1 - i0
+            m = np.full((n_heads, nb), -np.inf)
+            l = np.zeros((n_heads, nb))
+            o = np.zeros((n_heads, nb, dk))
+            for j0 in range(0, seq_len, block_kv):
+                if causal and j0 > i1 - 1:
+                    break                      # block entirely in the future: skipped
+                j1 = min(seq_len, j0 + block_kv)
+                xj = layer_norm(xs[j0:j1], p["ln1_g"], p["ln1_b"], eps)
+                k_j = xj @ p["w_k"]
+                v_j = xj @ p["w_v"]
+                for h in range(n_heads):
+                    cols = slice(h * dk, (h + 1) * dk)
+                    s = (q_i[:, cols] @ k_j[:, cols].T) * scale
+                    if causal:
+                        fut = np.arange(j0, j1)[None, :] > np.arange(i0, i1)[:, None]
+                        s = np.where(fut, -np.inf, s)
+                    m_new = np.maximum(m[h], s.max(axis=1))
+                    shift = np.where(np.isfinite(m_new), m_new, 0.0)
+                    alpha = np.where(np.isfinite(m[h]), np.exp(m[h] - shift), 0.0)
+                    e = np.exp(s - shift[:, None])
+                    l[h] = alpha * l[h] + e.sum(axis=1)
+                    o[h] = alpha[:, None] * o[h] + e @ v_j[:, cols]
+                    m[h] = m_new
+            attn = np.concatenate([o[h] / l[h][:, None] for h in range(n_heads)], axis=1)
+            y_i = x_i + attn @ p["w_o"]
+            h_i = gelu_tanh(layer_norm(y_i, p["ln2_g"], p["ln2_b"], eps) @ p["w_1"])
+            z[s0 + i0:s0 + i1] = y_i + h_i @ p["w_2"]
+    return z
+
+
+# ---------------------------------------------------------------------------
+# Error metrics used by the parity checks
+# ---------------------------------------------------------------------------
+
+def max_abs_err(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.max(np.abs(np.asarray(got, F64) - np.asarray(ref, F64)))) if np.size(ref) else 0.0
+
+
+def rel_fro_err(got: np.ndarray, ref: np.ndarray) -> float:
+    ref = np.asarray(ref, F64)
+    den = float(np.linalg.norm(ref))
+    num = float(np.linalg.norm(np.asarray(got, F64) - ref))
+    return num / den if den > 0 else num

@@ -1,0 +1,327 @@
+"""Pins of the CPU oracle against things other than itself (no GPU needed).
+
+Each test names what fixes the expected value: a number or identity printed on
+the pages, a closed form, a brute-force loop on tiny inputs, or an independent
+library routine (torch's CPU float64 functional ops, scipy).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import bpt_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_layer(rng, d, d_ff, std=0.2, ln_random=True):
+    """float64 weights in (in, out) orientation for tiny oracle-only checks."""
+    g = lambda *s: rng.standard_normal(s)  # noqa: E731
+    p = dict(w_q=g(d, d) * std, w_k=g(d, d) * std, w_v=g(d, d) * std, w_o=g(d, d) * std,
+             w_1=g(d, d_ff) * std, w_2=g(d_ff, d) * std)
+    if ln_random:
+        p.update(ln1_g=1 + 0.1 * g(d), ln1_b=0.1 * g(d), ln2_g=1 + 0.1 * g(d), ln2_b=0.1 * g(d))
+    else:
+        p.update(ln1_g=np.ones(d), ln1_b=np.zeros(d), ln2_g=np.ones(d), ln2_b=np.zeros(d))
+    return p
+
+
+# --------------------------------------------------------------------------
+# Online softmax: the pages' two-tile running-sum example, generalised
+# --------------------------------------------------------------------------
+
+def test_two_tile_running_sum_prints_true():
+    """transformer-cost page, FlashAttention paragraph: 8 scores in two tiles of 4; the
+    rescaled tile sums equal the full sum (the page prints True)."""
+    g = json.load(open(os.path.join(GOLDEN, "pages_numbers.json")))["two_tile_running_sum"]
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        s = rng.standard_normal(g["scores"])
+        m, l, _o = oracle.online_softmax_tiles(s, np.ones((s.size, 1)), g["tile"])
+        full = np.exp(s - s.max()).sum()            # the page's "full" line
+        assert m == s.max()
+        assert bool(np.allclose(l, full)) is g["printed"]
+
+
+@pytest.mark.parametrize("n,tile", [(8, 4), (37, 5), (64, 64), (100, 7), (3, 10)])
+def test_online_softmax_accumulator_matches_scipy_softmax(n, tile):
+    """The (m, l, o) recurrence with o/l equals scipy's softmax-weighted mean, for any
+    number of tiles and a ragged last tile."""
+    rng = np.random.default_rng(n * 31 + tile)
+    s = rng.standard_normal(n) * 4
+    v = rng.standard_normal((n, 6))
+    m, l, o = oracle.online_softmax_tiles(s, v, tile)
+    ref = scipy.special.softmax(s) @ v
+    assert np.max(np.abs(o / l - ref)) < 1e-13
+    assert abs(l - np.exp(s - s.max()).sum()) < 1e-12 * l
+
+
+def test_online_softmax_leading_masked_tile_and_peaky_scores():
+    """A first tile with every score -inf leaves the state untouched; huge scores do not
+    overflow because the running maximum is subtracted."""
+    s = np.array([-np.inf] * 4 + [1000.0, 999.0, -3.0, 0.5])
+    v = np.arange(16, dtype=float).reshape(8, 2)
+    m, l, o = oracle.online_softmax_tiles(s, v, 4)
+    ref = scipy.special.softmax(s[4:]) @ v[4:]
+    assert m == 1000.0 and np.allclose(o / l, ref, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Attention: brute force and an independent library routine
+# --------------------------------------------------------------------------
+
+def brute_force_attention(q, k, v, n_heads, causal):
+    """Explicit loops over head, query and key with math.exp and one division."""
+    nq, d = q.shape
+    dk = d // n_heads
+    out = np.zeros((nq, d))
+    for h in range(n_heads):
+        for i in range(nq):
+            keys = range(i + 1) if causal else range(k.shape[0])
+            sc = {j: sum(q[i, h * dk + c] * k[j, h * dk + c] for c in range(dk)) / math.sqrt(dk)
+                  for j in keys}
+            mx = max(sc.values())
+            w = {j: math.exp(sc[j] - mx) for j in keys}
+            tot = sum(w.values())
+            for c in range(dk):
+                out[i, h * dk + c] = sum(w[j] * v[j, h * dk + c] for j in keys) / tot
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_matches_brute_force(causal):
+    rng = np.random.default_rng(1 + causal)
+    n, d, h = 9, 8, 2
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    got = oracle.attention_sequence(q, k, v, h, causal)
+    assert np.max(np.abs(got - brute_force_attention(q, k, v, h, causal))) < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_matches_torch_sdpa(causal):
+    rng = np.random.default_rng(7 + causal)
+    n, d, h = 50, 32, 4
+    q, k, v = (rng.standard_normal((n, d)) * 2 for _ in range(3))
+    got = oracle.attention_sequence(q, k, v, h, causal)
+    t = lambda a: torch.from_numpy(a).view(n, h, d // h).transpose(0, 1).contiguous()  # noqa: E731
+    ref = F.scaled_dot_product_attention(t(q)[None], t(k)[None], t(v)[None], is_causal=causal)
+    ref = ref[0].transpose(0, 1).reshape(n, d).numpy()
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_sampled_positions_match_full():
+    """Queries at arbitrary positions see exactly the keys up to their position."""
+    rng = np.random.default_rng(3)
+    n, d, h = 40, 16, 2
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    full = oracle.attention_sequence(q, k, v, h, True)
+    pos = np.array([0, 5, 17, 39])
+    part = oracle.attention_sequence(q[pos], k[:40], v[:40], h, True, q_pos=pos)
+    assert np.max(np.abs(part - full[pos])) < 1e-14
+
+
+def test_uniform_attention_closed_form():
+    """W_Q = 0 makes every score 0: causal row p returns mean(V[0..p]); without the
+    mask every row returns mean(V)."""
+    rng = np.random.default_rng(4)
+    n, d = 12, 8
+    v = rng.standard_normal((n, d))
+    q = np.zeros((n, d))
+    k = rng.standard_normal((n, d))
+    causal = oracle.attention_sequence(q, k, v, 2, True)
+    assert np.allclose(causal, np.cumsum(v, 0) / np.arange(1, n + 1)[:, None], atol=1e-14)
+    full = oracle.attention_sequence(q, k, v, 2, False)
+    assert np.allclose(full, np.broadcast_to(v.mean(0), (n, d)), atol=1e-14)
+
+
+def test_softmax_shift_invariance_and_masked_row():
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((4, 7))
+    assert np.allclose(oracle.softmax_rows(s), oracle.softmax_rows(s + 123.0), atol=1e-15)
+    assert np.all(oracle.softmax_rows(np.full((1, 3), -np.inf)) == 0)   # no NaN
+
+
+# --------------------------------------------------------------------------
+# LN and GELU: closed forms and torch
+# --------------------------------------------------------------------------
+
+def test_layer_norm_closed_forms_and_torch():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 16)) * 3 + 2
+    g, b = rng.standard_normal(16), rng.standard_normal(16)
+    ref = F.layer_norm(torch.from_numpy(x), (16,), torch.from_numpy(g), torch.from_numpy(b), 1e-5)
+    assert np.max(np.abs(oracle.layer_norm(x, g, b, 1e-5) - ref.numpy())) < 1e-13
+    # a constant row normalises to the bias
+    assert np.allclose(oracle.layer_norm(np.full((1, 16), 7.5), g, b, 1e-5), b, atol=0)
+    # two-valued row a +- delta: entries are +- delta / sqrt(delta^2 + eps) (eps inside sqrt)
+    delta, eps = 1e-3, 1e-5
+    row = np.array([[5 + delta, 5 - delta] * 4])
+    got = oracle.layer_norm(row, np.ones(8), np.zeros(8), eps)
+    assert np.allclose(got[0, 0], delta / math.sqrt(delta * delta + eps), rtol=1e-12)
+
+
+def test_gelu_tanh_values():
+    u = np.linspace(-8, 8, 2001)
+    ref = F.gelu(torch.from_numpy(u), approximate="tanh").numpy()
+    assert np.max(np.abs(oracle.gelu_tanh(u) - ref)) < 1e-15
+    # closed form at u = 1: 0.5 (1 + tanh(sqrt(2/pi) * 1.044715))
+    assert abs(oracle.gelu_tanh(np.array([1.0]))[0]
+               - 0.5 * (1 + math.tanh(math.sqrt(2 / math.pi) * 1.044715))) < 1e-15
+    # the tanh form is not the erf form: a swap would be visible here
+    erf_form = 0.5 * u * (1 + scipy.special.erf(u / math.sqrt(2)))
+    assert np.max(np.abs(oracle.gelu_tanh(u) - erf_form)) > 1e-4
+
+
+# --------------------------------------------------------------------------
+# The whole layer: the pages' fused loop, torch, closed forms, row independence
+# --------------------------------------------------------------------------
+
+def torch_layer(x, p, seq_len, n_heads, causal, eps=1e-5):
+    """The layer assembled from torch CPU float64 functional ops (layer_norm, matmul,
+    scaled_dot_product_attention, gelu) -- a second, library-built implementation."""
+    t = {k: torch.from_numpy(np.asarray(v, np.float64)) for k, v in p.items()}
+    xt = torch.from_numpy(x)
+    rows, d = xt.shape
+    dk = d // n_heads
+    x1 = F.layer_norm(xt, (d,), t["ln1_g"], t["ln1_b"], eps)
+    split = lambda a: a.view(rows // seq_len, seq_len, n_heads, dk).transpose(1, 2)  # noqa: E731
+    a = F.scaled_dot_product_attention(split(x1 @ t["w_q"]), split(x1 @ t["w_k"]),
+                                       split(x1 @ t["w_v"]), is_causal=causal)
+    a = a.transpose(1, 2).reshape(rows, d)
+    y = xt + a @ t["w_o"]
+    h = F.gelu(F.layer_norm(y, (d,), t["ln2_g"], t["ln2_b"], eps) @ t["w_1"], approximate="tanh")
+    return (y + h @ t["w_2"]).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_layer_matches_torch_built_layer(causal):
+    rng = np.random.default_rng(10 + causal)
+    seq, b, d, h = 24, 2, 16, 4
+    x = rng.standard_normal((seq * b, d))
+    p = rand_layer(rng, d, 4 * d)
+    got = oracle.layer_forward(x, p, seq_len=seq, n_heads=h, causal=causal)
+    ref = torch_layer(x, p, seq, h, causal)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("causal,seq,bq,bkv", [(False, 64, 16, 16), (True, 64, 16, 16),
+                                                (True, 64, 32, 16), (True, 50, 16, 8),
+                                                (False, 45, 32, 64), (True, 16, 16, 16)])
+def test_fused_blockwise_loop_equals_unfused(causal, seq, bq, bkv):
+    """The pages' fused loop (online softmax, causal block skip, K/V recomputed per block,
+    ragged last blocks) gives the unfused layer's values up to rounding."""
+    rng = np.random.default_rng(seq + bq + 3 * bkv + causal)
+    d, h = 16, 2
+    x = rng.standard_normal((2 * seq, d))
+    p = rand_layer(rng, d, 4 * d, std=0.4)
+    ref = oracle.layer_forward(x, p, seq_len=seq, n_heads=h, causal=causal)
+    got = oracle.blockwise_layer_forward(x, p, seq_len=seq, n_heads=h, causal=causal,
+                                         block_q=bq, block_kv=bkv)
+    assert oracle.rel_fro_err(got, ref) < 1e-12
+
+
+def test_layer_closed_forms():
+    rng = np.random.default_rng(12)
+    seq, d, h = 20, 16, 2
+    x = rng.standard_normal((seq, d))
+    p = rand_layer(rng, d, 64)
+    # W_O = 0 -> Y = X; W_V = 0 -> attention output 0 -> Y = X
+    for key in ("w_o", "w_v"):
+        q = dict(p, **{key: np.zeros_like(p[key])})
+        _z, parts = oracle.layer_forward(x, q, seq_len=seq, n_heads=h, causal=True, return_parts=True)
+        assert np.array_equal(parts["y"], x)
+    # W_2 = 0 -> Z = Y
+    q = dict(p, w_2=np.zeros_like(p["w_2"]))
+    z, parts = oracle.layer_forward(x, q, seq_len=seq, n_heads=h, causal=True, return_parts=True)
+    assert np.array_equal(z, parts["y"])
+    # W_Q = 0 -> causal row p of the attention output is mean(V[0..p]); here V = LN1(X) W_V
+    q = dict(p, w_q=np.zeros_like(p["w_q"]))
+    _z, parts = oracle.layer_forward(x, q, seq_len=seq, n_heads=h, causal=True, return_parts=True)
+    vv = oracle.layer_norm(x, p["ln1_g"], p["ln1_b"], 1e-5) @ p["w_v"]
+    assert np.allclose(parts["a"], np.cumsum(vv, 0) / np.arange(1, seq + 1)[:, None], atol=1e-13)
+
+
+def test_row_independence_of_tail_and_noncausal_permutation():
+    """LN, the FFN and the residuals are row-wise: permuting a non-causal sequence's rows
+    permutes the outputs; a single row evaluated alone equals that row of the full layer."""
+    rng = np.random.default_rng(13)
+    seq, d, h = 30, 16, 4
+    x = rng.standard_normal((seq, d))
+    p = rand_layer(rng, d, 64)
+    z = oracle.layer_forward(x, p, seq_len=seq, n_heads=h, causal=False)
+    perm = rng.permutation(seq)
+    zp = oracle.layer_forward(x[perm], p, seq_len=seq, n_heads=h, causal=False)
+    assert np.max(np.abs(zp - z[perm])) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_equal_full_rows(causal):
+    rng = np.random.default_rng(14 + causal)
+    seq, b, d, h = 33, 3, 16, 2
+    x = rng.standard_normal((seq * b, d))
+    p = rand_layer(rng, d, 64)
+    z = oracle.layer_forward(x, p, seq_len=seq, n_heads=h, causal=causal)
+    rows = np.array([0, 1, 32, 33, 34, 50, 65, 66, 98])
+    got = oracle.layer_forward_rows(x, p, rows, seq_len=seq, n_heads=h, causal=causal, row_chunk=7)
+    assert np.max(np.abs(got - z[rows])) < 1e-12
+
+
+def test_stack_rows_and_single_layer_stack():
+    rng = np.random.default_rng(15)
+    seq, d, h = 24, 16, 2
+    x = rng.standard_normal((2 * seq, d))
+    layers = [rand_layer(rng, d, 64, std=0.2 / math.sqrt(2 * i + 1)) for i in range(3)]
+    full = oracle.stack_forward(x, layers, seq_len=seq, n_heads=h, causal=True)
+    step = x
+    for p in layers:
+        step = torch_layer(step, p, seq, h, True)
+    assert np.max(np.abs(full - step)) < 1e-11
+    rows = np.array([0, 5, 23, 24, 47])
+    got = oracle.stack_forward_rows(x, layers, rows, seq_len=seq, n_heads=h, causal=True)
+    assert np.max(np.abs(got - full[rows])) < 1e-12
+    one = oracle.stack_forward(x, layers[:1], seq_len=seq, n_heads=h, causal=True)
+    assert np.array_equal(one, oracle.layer_forward(x, layers[0], seq_len=seq, n_heads=h, causal=True))
+
+
+# --------------------------------------------------------------------------
+# Planted mistakes: each pin above must catch a plausible error in the oracle
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mutation", ["scale_1_over_dk", "no_causal_mask", "erf_gelu",
+                                      "transposed_wo", "no_second_residual", "ln_no_eps"])
+def test_pins_catch_planted_oracle_mistakes(mutation, monkeypatch):
+    rng = np.random.default_rng(16)
+    seq, d, h = 24, 16, 2
+    x = rng.standard_normal((seq, d))
+    p = rand_layer(rng, d, 64, std=0.5)
+    ref = torch_layer(x, p, seq, h, True, eps=1e-2)
+    if mutation == "scale_1_over_dk":
+        orig = O.attention_sequence
+
+        def bad(q, k, v, n_heads, causal, q_pos=None):
+            return orig(q * math.sqrt(d // n_heads) ** -1, k, v, n_heads, causal, q_pos)
+        monkeypatch.setattr(O, "attention_sequence", bad)
+    elif mutation == "no_causal_mask":
+        orig = O.attention_sequence
+        monkeypatch.setattr(O, "attention_sequence",
+                            lambda q, k, v, n_heads, causal, q_pos=None: orig(q, k, v, n_heads, False, q_pos))
+    elif mutation == "erf_gelu":
+        monkeypatch.setattr(O, "gelu_tanh", lambda u: 0.5 * u * (1 + scipy.special.erf(u / math.sqrt(2))))
+    elif mutation == "transposed_wo":
+        p = dict(p)
+        ref = torch_layer(x, dict(p, w_o=p["w_o"].T.copy()), seq, h, True, eps=1e-2)
+    elif mutation == "no_second_residual":
+        z, parts = O.layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, eps=1e-2, return_parts=True)
+        assert np.max(np.abs((z - parts["y"]) - ref)) > 1e-3
+        return
+    elif mutation == "ln_no_eps":
+        orig_ln = O.layer_norm
+        monkeypatch.setattr(O, "layer_norm", lambda x_, g, b, eps: orig_ln(x_, g, b, 0.0))
+    got = O.layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, eps=1e-2)
+    assert np.max(np.abs(got - ref)) > 1e-6, mutation
