@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Throughput of the fused BPT layer forward on one MI355X.
+
+    python bench.py [--workload gpt2_medium] [--steps K] [--warmup W] [--gpus 1]
+
+A step is one bpt_layer_fwd (or bpt_stack_fwd) call over one batch of seeded
+synthetic input already resident in device memory. W untimed steps, then K
+steps timed with device events on the stream the library launches on. Prints
+ONE JSON line: algorithmic TFLOP/s (FLOPs from the pages' count: attention
+2 d N (N + 1) causal / 4 N^2 d, projections 8 N d^2, FFN 4 N d d_ff), the
+fraction of the bf16 dense matrix-core peak, the activation memory, a roofline
+entry for the kernel that takes the most time, and the CPU float64 oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused BPT layer fwd TFLOP/s (1 MI355X) + % bf16 MFMA peak; peak act mem"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense matrix-core peaks of MI355X
+KERNELS = ("ln_stats", "ln_qkv", "attention", "ffn_epilogue")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_medium")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU oracle sample")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def kernel_flops(w) -> dict:
+    """Algorithmic FLOPs per launch of each kernel (matrix products only)."""
+    from blockwise_attn_ffn_amd import accounting as A
+    b, n, d, f = w.batch, w.seq_len, w.d_model, w.d_ff
+    return {"ln_stats": 0,
+            "ln_qkv": b * 6 * n * d * d,
+            "attention": b * A.attention_flops(n, d, w.causal),
+            "ffn_epilogue": b * (2 * n * d * d + A.ffn_flops(n, d, f))}
+
+
+def cpu_baseline(w, inputs, target_s: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    from blockwise_attn_ffn_amd import accounting as A, synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    layers = [synth.oracle_weights(l) for l in inputs["layers"]]
+    x = inputs["x"]
+    if w.sample_rows == 0 and w.n_layers == 1:
+        def run(k):
+            xs = synth.to_f64(x[:k * w.seq_len])
+            t0 = time.perf_counter()
+            oracle.layer_forward(xs, layers[0], seq_len=w.seq_len, n_heads=w.n_heads,
+                                 causal=w.causal, eps=w.ln_eps)
+            return time.perf_counter() - t0
+        t1 = run(1)
+        k = int(max(1, min(w.batch, round(target_s / max(t1, 1e-3)))))
+        t = run(k) if k > 1 else t1
+        flops = k * A.layer_flops(w.seq_len, w.d_model, w.d_ff, w.causal)
+        sample = f"{k} of {w.batch} sequences, full layer (unfused, fp64)"
+    else:
+        # sampled rows of one layer: K, V for the visible prefix, the rest per row
+        rows = synth.sample_rows(w, 64 if w.sample_rows else 64, seed=0)
+        xs = synth.to_f64(x)
+        t0 = time.perf_counter()
+        oracle.layer_forward_rows(xs, layers[0], rows, seq_len=w.seq_len, n_heads=w.n_heads,
+                                  causal=w.causal, eps=w.ln_eps)
+        t = time.perf_counter() - t0
+        d, f = w.d_model, w.d_ff
+        nk = int(rows.max()) + 1
+        pos = rows % w.seq_len
+        flops = 4 * nk * d * d + len(rows) * (4 * d * d + 4 * d * f) + int(np.sum(4 * d * (pos + 1)))
+        sample = f"{len(rows)} sampled rows of layer 1 (K/V for {nk} rows), fp64"
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(t, 3), "flops": int(flops)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from blockwise_attn_ffn_amd import accounting as A, bpt, synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.init()
+    free_start, total_mem = torch.cuda.mem_get_info()
+
+    inputs = synth.make_inputs(w, seed=args.seed)
+    dev_x = inputs["x"].cuda()
+    dev_layers = [{k: v.cuda() for k, v in l.items()} for l in inputs["layers"]]
+    out_dtype = "f32"
+    desc = bpt.desc_for(w, out_dtype=out_dtype)
+    ws_bytes = (bpt.layer_workspace_bytes(desc) if w.n_layers == 1
+                else bpt.stack_workspace_bytes(desc, w.n_layers))
+    ws = bpt.alloc_workspace(ws_bytes)
+    z = torch.empty((w.rows, w.d_model), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    hip = Hip()
+    ev = [hip.event() for _ in range(5)]
+
+    def step(profiled: bool):
+        if w.n_layers == 1:
+            if profiled:
+                bpt.layer_fwd_profiled(desc, dev_x, dev_layers[0], z, ws, ev, stream)
+            else:
+                bpt.layer_fwd(desc, dev_x, dev_layers[0], z, ws, stream)
+        else:
+            bpt.stack_fwd(desc, dev_x, dev_layers, z, ws, stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(False)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    free_after, _ = torch.cuda.mem_get_info()
+
+    # per-kernel durations, recorded with events between the library's launches
+    per_kernel = {k: 0.0 for k in KERNELS}
+    if w.n_layers == 1:
+        for _ in range(args.steps):
+            step(True)
+            torch.cuda.synchronize()
+            for i, k in enumerate(KERNELS):
+                per_kernel[k] += hip.elapsed_ms(ev[i], ev[i + 1]) / args.steps
+    for e in ev:
+        hip.destroy(e)
+
+    total_flops = A.workload_flops(w.batch, w.seq_len, w.d_model, w.d_ff, w.causal, w.n_layers)
+    tflops = total_flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    kf = kernel_flops(w)
+    roofline = None
+    if w.n_layers == 1:
+        dom = max(KERNELS, key=lambda k: per_kernel[k])
+        achieved = kf[dom] / (per_kernel[dom] * 1e-3) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": None, "avg_ms": round(per_kernel[dom], 4),
+                    "flops_per_launch": kf[dom]}
+    act_bytes = ws_bytes + dev_x.numel() * dev_x.element_size() + z.numel() * z.element_size()
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian X and weights, random-init)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
+                   "d_model": w.d_model, "n_heads": w.n_heads, "d_ff": w.d_ff,
+                   "causal": w.causal, "block_q": w.block_q, "block_kv": w.block_kv,
+                   "n_layers": w.n_layers, "out_dtype": out_dtype, "parallelism": "none"},
+        "pct_peak": round(100 * tflops / peak, 2),
+        "flops_per_step": total_flops,
+        "kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "kernel_tflops": {k: round(kf[k] / (per_kernel[k] * 1e-3) / 1e12, 2)
+                          for k in KERNELS if per_kernel[k] > 0 and kf[k] > 0},
+        "memory": {"workspace_bytes": ws_bytes, "activation_bytes": act_bytes,
+                   "device_bytes_used": int(free_start - free_after),
+                   "ffn_hidden_unfused_bytes": w.rows * w.d_ff * 2,
+                   "logits_one_head_bytes": w.batch * w.seq_len * w.seq_len * 2},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+"""Thin ctypes binding of libbpt.so (declared in include/bpt.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. torch is used for device memory and streams; the binding passes
+``tensor.data_ptr()`` and the stream handle through unchanged.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+F32, BF16 = 0, 1
+STATUS = {0: "BPT_OK", 1: "BPT_ERR_NULL", 2: "BPT_ERR_SHAPE", 3: "BPT_ERR_UNSUPPORTED",
+          4: "BPT_ERR_ALIGN", 5: "BPT_ERR_WORKSPACE", 6: "BPT_ERR_ALIAS", 7: "BPT_ERR_HIP"}
+WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o", "ln2_g", "ln2_b", "w_1", "w_2")
+EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer_fwd",
+            "bpt_layer_fwd_profiled", "bpt_stack_fwd", "bpt_status_str", "bpt_last_error", "bpt_version")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("block_q", ctypes.c_int32),
+                ("block_kv", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("precision", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class BptError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m blockwise_attn_ffn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.bpt_layer_workspace_bytes.argtypes = [P(LayerDesc)]
+        L.bpt_layer_workspace_bytes.restype = ctypes.c_size_t
+        L.bpt_stack_workspace_bytes.argtypes = [P(LayerDesc), ctypes.c_int32]
+        L.bpt_stack_workspace_bytes.restype = ctypes.c_size_t
+        L.bpt_layer_fwd.argtypes = [P(LayerDesc), ctypes.c_void_p, P(LayerWeights),
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p]
+        L.bpt_layer_fwd.restype = ctypes.c_int
+        L.bpt_layer_fwd_profiled.argtypes = L.bpt_layer_fwd.argtypes + [P(ctypes.c_void_p)]
+        L.bpt_layer_fwd_profiled.restype = ctypes.c_int
+        L.bpt_stack_fwd.argtypes = [P(LayerDesc), ctypes.c_int32, ctypes.c_void_p,
+                                    P(LayerWeights), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]
+        L.bpt_stack_fwd.restype = ctypes.c_int
+        L.bpt_status_str.argtypes = [ctypes.c_int]
+        L.bpt_status_str.restype = ctypes.c_char_p
+        L.bpt_last_error.argtypes = []
+        L.bpt_last_error.restype = ctypes.c_char_p
+        L.bpt_version.argtypes = []
+        L.bpt_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def make_desc(*, batch, seq_len, d_model, n_heads, d_ff, block_q, block_kv, causal,
+              dtype, out_dtype=F32, ln_eps=1e-5, act=0, precision=0) -> LayerDesc:
+    as_code = lambda t: t if isinstance(t, int) else {"f32": F32, "bf16": BF16}[t]  # noqa: E731
+    return LayerDesc(batch, seq_len, d_model, n_heads, d_ff, block_q, block_kv, int(causal),
+                     ln_eps, as_code(dtype), as_code(out_dtype), act, precision)
+
+
+def desc_for(w, out_dtype=F32) -> LayerDesc:
+    """Descriptor of a synth.Workload."""
+    return make_desc(batch=w.batch, seq_len=w.seq_len, d_model=w.d_model, n_heads=w.n_heads,
+                     d_ff=w.d_ff, block_q=w.block_q, block_kv=w.block_kv, causal=w.causal,
+                     dtype=w.dtype, out_dtype=out_dtype, ln_eps=w.ln_eps)
+
+
+def layer_workspace_bytes(desc: LayerDesc) -> int:
+    return int(lib().bpt_layer_workspace_bytes(ctypes.byref(desc)))
+
+
+def stack_workspace_bytes(desc: LayerDesc, n_layers: int) -> int:
+    return int(lib().bpt_stack_workspace_bytes(ctypes.byref(desc), n_layers))
+
+
+def last_error() -> str:
+    return lib().bpt_last_error().decode()
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("device tensors are required")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensors are required")
+    return t.data_ptr()
+
+
+def _weights(layer: dict) -> LayerWeights:
+    return LayerWeights(*[_ptr(layer[n]) for n in WEIGHT_FIELDS])
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise BptError(status, last_error())
+
+
+def layer_fwd(desc: LayerDesc, x, layer: dict, z, workspace, stream=None) -> None:
+    """Enqueue Z = layer(X) on the stream (torch's current stream by default)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bpt_layer_fwd(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)),
+                               _ptr(z), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def layer_fwd_profiled(desc: LayerDesc, x, layer: dict, z, workspace, events, stream=None) -> None:
+    """layer_fwd, recording the five hipEvent_t handles in `events` around its kernels."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    arr = (ctypes.c_void_p * 5)(*events)
+    _check(lib().bpt_layer_fwd_profiled(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)),
+                                        _ptr(z), _ptr(workspace), nbytes, _stream(stream), arr))
+
+
+def stack_fwd(desc: LayerDesc, x, layers: list, z, workspace, stream=None) -> None:
+    """Enqueue Z = layer_{L-1}(... layer_0(X)) on the stream."""
+    arr = (LayerWeights * len(layers))(*[_weights(l) for l in layers])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bpt_stack_fwd(ctypes.byref(desc), len(layers), _ptr(x), arr, _ptr(z),
+                               _ptr(workspace), nbytes, _stream(stream)))
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    """A uint8 device tensor of nbytes (at least 1 byte), for the workspace argument."""
+    import torch
+    return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)

@@ -1,0 +1,250 @@
+// Host side of the C ABI declared in include/bpt.h: validation, workspace
+// sizing and carving, and the per-layer / per-stack launch sequence.
+// Plain C++ (no HIP headers): the launches themselves live in bpt_kernels.hip.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bpt_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bpt_status_t fail(bpt_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t esize(int dtype) { return dtype == BPT_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int ldv_of(int seq_len) { return (seq_len + 7) / 8 * 8; }
+
+// Layout of the layer workspace, plus the stack's fp32 residual buffer.
+bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
+  bpt::WorkspaceLayout L{};
+  const size_t rows = (size_t)d->batch * d->seq_len;
+  const size_t es = esize(d->dtype);
+  size_t off = 0;
+  L.stats_off = off;
+  off = round_up(off + rows * 8, kAlign);
+  L.q_off = off;
+  off = round_up(off + rows * d->d_model * es, kAlign);
+  L.k_off = off;
+  off = round_up(off + rows * d->d_model * es, kAlign);
+  L.vt_off = off;
+  off = round_up(off + (size_t)d->batch * d->d_model * ldv_of(d->seq_len) * es, kAlign);
+  L.resid_off = off;
+  if (stack_resid) off = round_up(off + rows * d->d_model * 4, kAlign);
+  L.total = off;
+  return L;
+}
+
+bool is_empty(const bpt_layer_desc_t* d) { return d->batch == 0 || d->seq_len == 0; }
+
+// Shape/option validation shared by both entry points (no pointers).
+bpt_status_t validate_desc(const bpt_layer_desc_t* d) {
+  if (!d) return fail(BPT_ERR_NULL, "desc is NULL");
+  if (d->batch < 0 || d->seq_len < 0) return fail(BPT_ERR_SHAPE, "batch and seq_len must be >= 0");
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->d_ff <= 0)
+    return fail(BPT_ERR_SHAPE, "d_model, n_heads and d_ff must be > 0");
+  if (d->d_model % d->n_heads != 0)
+    return fail(BPT_ERR_SHAPE, "d_model %d is not a multiple of n_heads %d", d->d_model, d->n_heads);
+  if (d->block_q <= 0 || d->block_kv <= 0) return fail(BPT_ERR_SHAPE, "block sizes must be > 0");
+  if (d->causal != 0 && d->causal != 1) return fail(BPT_ERR_SHAPE, "causal must be 0 or 1");
+  if (!(d->ln_eps > 0.0f) || !isfinite(d->ln_eps))
+    return fail(BPT_ERR_SHAPE, "ln_eps must be finite and > 0");
+  if ((d->dtype != BPT_F32 && d->dtype != BPT_BF16) ||
+      (d->out_dtype != BPT_F32 && d->out_dtype != BPT_BF16))
+    return fail(BPT_ERR_SHAPE, "dtype / out_dtype must be BPT_F32 or BPT_BF16");
+  if (d->act != 0) return fail(BPT_ERR_UNSUPPORTED, "act %d unsupported (0 = GELU tanh)", d->act);
+  if (d->precision != 0)
+    return fail(BPT_ERR_UNSUPPORTED, "precision %d unsupported (0 only)", d->precision);
+  if ((int64_t)d->batch * d->seq_len > (int64_t)INT32_MAX - 1024)
+    return fail(BPT_ERR_SHAPE, "batch * seq_len exceeds the 32-bit row index range");
+  char msg[256] = "";
+  if (!bpt::kernels_support(d->d_model, d->d_model / d->n_heads, d->block_q, d->block_kv,
+                            d->dtype == BPT_F32, 0, d->out_dtype == BPT_F32, d->d_ff, msg,
+                            sizeof(msg)))
+    return fail(BPT_ERR_UNSUPPORTED, "%s", msg);
+  return BPT_OK;
+}
+
+bpt_status_t validate_weights(const bpt_layer_weights_t* w, int idx) {
+  if (!w) return fail(BPT_ERR_NULL, "weights[%d] is NULL", idx);
+  const void* p[10] = {w->ln1_g, w->ln1_b, w->w_q, w->w_k, w->w_v,
+                       w->w_o,   w->ln2_g, w->ln2_b, w->w_1, w->w_2};
+  static const char* names[10] = {"ln1_g", "ln1_b", "w_q", "w_k", "w_v",
+                                  "w_o",   "ln2_g", "ln2_b", "w_1", "w_2"};
+  for (int i = 0; i < 10; ++i) {
+    if (!p[i]) return fail(BPT_ERR_NULL, "weights[%d].%s is NULL", idx, names[i]);
+    if (!aligned16(p[i]))
+      return fail(BPT_ERR_ALIGN, "weights[%d].%s is not 16-byte aligned", idx, names[i]);
+  }
+  return BPT_OK;
+}
+
+bpt_status_t validate_buffers(const bpt_layer_desc_t* d, const void* X, const void* Z,
+                              void* ws, size_t ws_bytes, size_t need) {
+  if (!X) return fail(BPT_ERR_NULL, "X is NULL");
+  if (!Z) return fail(BPT_ERR_NULL, "Z is NULL");
+  if (!aligned16(X)) return fail(BPT_ERR_ALIGN, "X is not 16-byte aligned");
+  if (!aligned16(Z)) return fail(BPT_ERR_ALIGN, "Z is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(BPT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  if (need > 0 && !ws) return fail(BPT_ERR_NULL, "workspace is NULL");
+  if (ws && !aligned16(ws)) return fail(BPT_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const size_t rows = (size_t)d->batch * d->seq_len;
+  const size_t xb = rows * d->d_model * esize(d->dtype);
+  const size_t zb = rows * d->d_model * esize(d->out_dtype);
+  if (overlap(X, xb, Z, zb)) return fail(BPT_ERR_ALIAS, "X and Z overlap");
+  if (overlap(ws, need, X, xb)) return fail(BPT_ERR_ALIAS, "workspace overlaps X");
+  if (overlap(ws, need, Z, zb)) return fail(BPT_ERR_ALIAS, "workspace overlaps Z");
+  return BPT_OK;
+}
+
+bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayout& L, void* ws) {
+  bpt::LayerLaunch p{};
+  p.batch = d->batch;
+  p.seq_len = d->seq_len;
+  p.d_model = d->d_model;
+  p.n_heads = d->n_heads;
+  p.d_head = d->d_model / d->n_heads;
+  p.d_ff = d->d_ff;
+  p.block_q = d->block_q;
+  p.block_kv = d->block_kv;
+  p.causal = d->causal;
+  p.ln_eps = d->ln_eps;
+  p.compute_f32 = d->dtype == BPT_F32;
+  p.ldv = ldv_of(d->seq_len);
+  char* base = static_cast<char*>(ws);
+  p.stats = base + L.stats_off;
+  p.q = base + L.q_off;
+  p.k = base + L.k_off;
+  p.vt = base + L.vt_off;
+  return p;
+}
+
+bpt_status_t run(bpt::LayerLaunch& p, void* stream) {
+  char msg[256] = "";
+  if (bpt::launch_layer(p, stream, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
+  return BPT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bpt_layer_workspace_bytes(const bpt_layer_desc_t* desc) {
+  if (validate_desc(desc) != BPT_OK) return 0;
+  if (is_empty(desc)) return 0;
+  return layout(desc, false).total;
+}
+
+size_t bpt_stack_workspace_bytes(const bpt_layer_desc_t* desc, int32_t n_layers) {
+  if (validate_desc(desc) != BPT_OK) return 0;
+  if (n_layers < 1) {
+    fail(BPT_ERR_SHAPE, "n_layers must be >= 1");
+    return 0;
+  }
+  if (is_empty(desc)) return 0;
+  return layout(desc, n_layers > 1 && desc->out_dtype != BPT_F32).total;
+}
+
+bpt_status_t bpt_layer_fwd(const bpt_layer_desc_t* desc, const void* X,
+                           const bpt_layer_weights_t* weights, void* Z, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  return bpt_layer_fwd_profiled(desc, X, weights, Z, workspace, workspace_bytes, hip_stream,
+                                nullptr);
+}
+
+bpt_status_t bpt_layer_fwd_profiled(const bpt_layer_desc_t* desc, const void* X,
+                                    const bpt_layer_weights_t* weights, void* Z, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream,
+                                    void* const events[5]) {
+  g_err[0] = 0;
+  if (events)
+    for (int i = 0; i < 5; ++i)
+      if (!events[i]) return fail(BPT_ERR_NULL, "events[%d] is NULL", i);
+  bpt_status_t st = validate_desc(desc);
+  if (st != BPT_OK) return st;
+  if (is_empty(desc)) return BPT_OK;
+  if ((st = validate_weights(weights, 0)) != BPT_OK) return st;
+  const bpt::WorkspaceLayout L = layout(desc, false);
+  if ((st = validate_buffers(desc, X, Z, workspace, workspace_bytes, L.total)) != BPT_OK) return st;
+  bpt::LayerLaunch p = make_launch(desc, L, workspace);
+  p.x = X;
+  p.x_f32 = desc->dtype == BPT_F32;
+  p.z = Z;
+  p.z_f32 = desc->out_dtype == BPT_F32;
+  p.w = *weights;
+  p.events = events;
+  return run(p, hip_stream);
+}
+
+bpt_status_t bpt_stack_fwd(const bpt_layer_desc_t* desc, int32_t n_layers, const void* X,
+                           const bpt_layer_weights_t* layers, void* Z, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_desc(desc);
+  if (st != BPT_OK) return st;
+  if (n_layers < 1) return fail(BPT_ERR_SHAPE, "n_layers must be >= 1");
+  if (is_empty(desc)) return BPT_OK;
+  if (!layers) return fail(BPT_ERR_NULL, "layers is NULL");
+  for (int i = 0; i < n_layers; ++i)
+    if ((st = validate_weights(&layers[i], i)) != BPT_OK) return st;
+  const bool resid = n_layers > 1 && desc->out_dtype != BPT_F32;
+  const bpt::WorkspaceLayout L = layout(desc, resid);
+  if ((st = validate_buffers(desc, X, Z, workspace, workspace_bytes, L.total)) != BPT_OK) return st;
+  // The fp32 residual stream lives in Z itself when Z is fp32, else in the
+  // workspace. Each epilogue tile reads its residual rows before writing the
+  // same rows, so layers after the first update it in place.
+  void* R = resid ? static_cast<char*>(workspace) + L.resid_off : Z;
+  for (int i = 0; i < n_layers; ++i) {
+    bpt::LayerLaunch p = make_launch(desc, L, workspace);
+    const bool last = i == n_layers - 1;
+    p.x = i == 0 ? X : R;
+    p.x_f32 = i == 0 ? desc->dtype == BPT_F32 : 1;
+    p.z = last ? Z : R;
+    p.z_f32 = last ? desc->out_dtype == BPT_F32 : 1;
+    p.w = layers[i];
+    if ((st = run(p, hip_stream)) != BPT_OK) return st;
+  }
+  return BPT_OK;
+}
+
+const char* bpt_status_str(bpt_status_t s) {
+  switch (s) {
+    case BPT_OK: return "ok";
+    case BPT_ERR_NULL: return "null pointer";
+    case BPT_ERR_SHAPE: return "invalid shape or option";
+    case BPT_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BPT_ERR_ALIGN: return "misaligned pointer";
+    case BPT_ERR_WORKSPACE: return "workspace too small";
+    case BPT_ERR_ALIAS: return "overlapping buffers";
+    case BPT_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+const char* bpt_last_error(void) { return g_err; }
+
+const char* bpt_version(void) { return "0.1.0"; }
+
+}  // extern "C"

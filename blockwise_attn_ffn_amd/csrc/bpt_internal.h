@@ -1,0 +1,48 @@
+// Internal interface between the host validation/dispatch layer (bpt_api.cpp,
+// plain C++) and the HIP launchers (bpt_kernels.hip). Nothing here is exported.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bpt.h"
+
+namespace bpt {
+
+// One layer's launch parameters after validation. All pointers are device
+// pointers; sizes are in elements unless named *_bytes.
+struct LayerLaunch {
+  // shape
+  int batch, seq_len, d_model, n_heads, d_head, d_ff;
+  int block_q, block_kv, causal;
+  float ln_eps;
+  int compute_f32;   // 1: fp32 operands everywhere; 0: bf16 operands
+  int x_f32;         // element type of X: 1 fp32, 0 bf16 (the weights' type otherwise)
+  int z_f32;         // element type of Z
+  int ldv;           // row stride (elements) of V^T: seq_len rounded up to 8
+  // tensors
+  const void* x;
+  bpt_layer_weights_t w;
+  void* z;
+  // workspace carve-up
+  void* stats;       // [rows] float2 (mean, rstd) of LN1
+  void* q;           // [rows, d] Q, then the attention output O (in place)
+  void* k;           // [rows, d]
+  void* vt;          // [batch, heads, d_head, ldv]
+  // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
+  void* const* events;
+};
+
+// Element counts/byte sizes of the workspace pieces (shared by sizing and carving).
+struct WorkspaceLayout {
+  size_t stats_off, q_off, k_off, vt_off, resid_off, total;
+};
+
+// Returns 0 on success, otherwise writes a message into err (errlen bytes).
+int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t errlen);
+
+// Whether a kernel instance exists for (d_model, d_head, block sizes, types).
+int kernels_support(int d_model, int d_head, int block_q, int block_kv, int compute_f32,
+                    int x_f32, int z_f32, int d_ff, char* err, size_t errlen);
+
+}  // namespace bpt

@@ -1,0 +1,49 @@
+// Which kernel instances exist: the host-side support table, kept beside the
+// dispatch in bpt_kernels.hip (every combination accepted here has an instance).
+#include <stdio.h>
+
+#include "bpt_internal.h"
+
+namespace bpt {
+namespace {
+void set_err(char* err, size_t n, const char* fmt, const char* a = "", int b = 0) {
+  if (err && n) snprintf(err, n, fmt, a, b);
+}
+}  // namespace
+
+int kernels_support(int d_model, int d_head, int block_q, int block_kv, int compute_f32,
+                    int x_f32, int z_f32, int d_ff, char* err, size_t errlen) {
+  (void)x_f32;
+  (void)z_f32;
+  const bool bf = !compute_f32;
+  bool d_ok = false;
+  if (bf) {
+    d_ok = d_model == 256 || d_model == 512 || d_model == 768 || d_model == 1024 ||
+           d_model == 2048;
+  } else {
+    d_ok = d_model == 128 || d_model == 256;
+  }
+  if (!d_ok) {
+    set_err(err, errlen, "d_model %s%d has no kernel instance for this dtype", "", d_model);
+    return 0;
+  }
+  if (d_head != 64 && d_head != 128) {
+    set_err(err, errlen, "head size %s%d unsupported (64 or 128)", "", d_head);
+    return 0;
+  }
+  if ((block_q != 64 && block_q != 128) || (block_kv != 64 && block_kv != 128)) {
+    set_err(err, errlen, "block sizes must be 64 or 128%s", "");
+    return 0;
+  }
+  if (!bf && d_head == 128 && block_kv == 128) {
+    set_err(err, errlen, "fp32 with head size 128 needs block_kv 64%s", "");
+    return 0;
+  }
+  if (d_ff % 256 != 0 || d_ff <= 0) {
+    set_err(err, errlen, "d_ff %s%d must be a positive multiple of 256", "", d_ff);
+    return 0;
+  }
+  return 1;
+}
+
+}  // namespace bpt

@@ -1,0 +1,146 @@
+/*
+ * bpt.h -- C ABI of the Blockwise Parallel Transformer (BPT) layer forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed ("Blockwise Parallel Transformer — BPT", aicassindra.com,
+ * section "The fused blockwise algorithm"): for every block of b query rows
+ *     q_i = LN1(x_i) W_Q;  for each key/value block j (online softmax, running
+ *     m, l, o):  s = q_i k_j^T / sqrt(d_k),  m' = max(m, rowmax s),
+ *     alpha = exp(m - m'), l = alpha l + sum exp(s - m'), o = alpha o + exp(s - m') v_j
+ *     y_i  = x_i + (o / l) W_O
+ *     h_i  = GELU_tanh(LN2(y_i) W_1)            -- [b, d_ff], never written to memory
+ *     Z[i] = y_i + h_i W_2
+ * per head (d_k = d_model / n_heads, heads concatenated in order), with causal
+ * key/value blocks that lie wholly after the query block skipped ("Pitfalls and
+ * misconceptions"). K and V are projected once per layer (a documented
+ * deviation from the pseudocode, which recomputes them in the inner loop; the
+ * values are identical).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named X, Z, workspace and every weight are DEVICE pointers to
+ *    contiguous row-major arrays, 16-byte aligned. Descriptors are HOST pointers.
+ *  - X: [batch * seq_len, d_model], sequences stacked row-wise, element type
+ *    desc->dtype.  Z: same shape, element type desc->out_dtype.
+ *  - LN parameters ln1_g, ln1_b, ln2_g, ln2_b: [d_model], type desc->dtype.
+ *    LN is (x - mean) / sqrt(biased variance + ln_eps) * g + b over the feature axis.
+ *  - Projection matrices are stored TRANSPOSED relative to the pages' y = x W
+ *    notation, i.e. row-major [out, in] (the torch.nn.Linear layout):
+ *      w_q, w_k, w_v, w_o: [d_model, d_model];  w_1: [d_ff, d_model];
+ *      w_2: [d_model, d_ff].  No linear biases.
+ *  - dtype BPT_F32: every product runs in fp32 (fp32 matrix cores).
+ *    dtype BPT_BF16: products take bf16 operands with fp32 accumulation;
+ *    softmax, LN, GELU and the residual stream are fp32.
+ *  - The library never allocates device memory. All transient state lives in
+ *    the caller's workspace, whose size the *_workspace_bytes functions return.
+ *  - Asynchronous: a call only validates on the host and enqueues kernels on
+ *    hip_stream (a hipStream_t; NULL = the default stream). Results are valid
+ *    once the stream has been synchronised. Buffers must stay alive until then.
+ *  - Errors: every argument is validated on the host before anything is
+ *    enqueued; a non-zero status means nothing was enqueued, except
+ *    BPT_ERR_HIP, returned when a launch fails (earlier launches of the same
+ *    call may then have been enqueued). bpt_last_error() gives a
+ *    human-readable detail for the calling thread. No C++ exception crosses
+ *    this interface.
+ *  - Thread-safe and reentrant: no mutable global state.
+ */
+#ifndef BPT_H_
+#define BPT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BPT_F32 = 0, BPT_BF16 = 1 } bpt_dtype_t;
+
+typedef enum {
+  BPT_OK = 0,
+  BPT_ERR_NULL = 1,        /* a required pointer is NULL */
+  BPT_ERR_SHAPE = 2,       /* a size is negative, or sizes disagree */
+  BPT_ERR_UNSUPPORTED = 3, /* valid, but outside what the kernels implement */
+  BPT_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  BPT_ERR_WORKSPACE = 5,   /* workspace smaller than *_workspace_bytes */
+  BPT_ERR_ALIAS = 6,       /* X, Z or workspace overlap */
+  BPT_ERR_HIP = 7          /* a HIP launch failed; see bpt_last_error() */
+} bpt_status_t;
+
+/* Shape and options of one layer (and of every layer of a stack). */
+typedef struct {
+  int32_t batch;      /* sequences; 0 gives an empty call that enqueues nothing  */
+  int32_t seq_len;    /* tokens per sequence N; 0 likewise                      */
+  int32_t d_model;    /* d; a multiple of 128, one of the sizes listed below     */
+  int32_t n_heads;    /* h; d_k = d_model / n_heads must be 64 or 128            */
+  int32_t d_ff;       /* FFN width (4 d in the pages); a multiple of 256         */
+  int32_t block_q;    /* b: query rows per outer-loop block; 64 or 128           */
+  int32_t block_kv;   /* key/value rows per inner-loop block; 64 or 128          */
+  int32_t causal;     /* 1: key j visible to query p iff j <= p; 0: no mask      */
+  float ln_eps;       /* LN epsilon, > 0 (1e-5 is usual)                         */
+  int32_t dtype;      /* bpt_dtype_t of X, the weights and the LN parameters     */
+  int32_t out_dtype;  /* bpt_dtype_t of Z                                        */
+  int32_t act;        /* 0 = GELU, tanh form (the only value)                    */
+  int32_t precision;  /* 0 (the only value implemented)                          */
+} bpt_layer_desc_t;
+
+/* Device pointers to one layer's parameters (layouts above). */
+typedef struct {
+  const void *ln1_g, *ln1_b, *w_q, *w_k, *w_v, *w_o;
+  const void *ln2_g, *ln2_b, *w_1, *w_2;
+} bpt_layer_weights_t;
+
+/* Supported d_model values: 128, 256, 512, 768, 1024, 1536, 2048, 3072, 4096
+ * (BPT_F32: 128, 256, 512). Sequence length, batch and d_ff (multiple of 256)
+ * are otherwise free; a sequence length that is not a multiple of the block
+ * sizes gets a shorter last block. */
+
+/* Bytes of workspace bpt_layer_fwd needs for *desc (0 for an empty call), or 0
+ * with bpt_last_error() set when desc is invalid. Holds LN statistics
+ * [rows, 2] fp32 and Q (reused for the attention output), K and V^T, each
+ * [rows, d_model] in the compute type. Nothing of size rows x d_ff or
+ * seq_len x seq_len is ever part of it. */
+size_t bpt_layer_workspace_bytes(const bpt_layer_desc_t* desc);
+
+/* Workspace of bpt_stack_fwd: the layer workspace, plus one fp32 residual
+ * buffer [rows, d_model] when n_layers > 1 and out_dtype is not BPT_F32. */
+size_t bpt_stack_workspace_bytes(const bpt_layer_desc_t* desc, int32_t n_layers);
+
+/* One layer: Z = layer(X). X and Z must not overlap; workspace must overlap
+ * neither. workspace_bytes >= bpt_layer_workspace_bytes(desc). */
+bpt_status_t bpt_layer_fwd(const bpt_layer_desc_t* desc, const void* X,
+                           const bpt_layer_weights_t* weights, void* Z,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* bpt_layer_fwd that also records five caller-created hipEvent_t handles
+ * (events: a HOST array of 5) on hip_stream, for timing each kernel:
+ * events[0] before the LN1 statistics, [1] after them, [2] after the QKV
+ * projection, [3] after attention, [4] after the FFN epilogue. The computation
+ * and every other rule are those of bpt_layer_fwd; events may be NULL (then it
+ * is bpt_layer_fwd), but not a NULL entry (BPT_ERR_NULL). */
+bpt_status_t bpt_layer_fwd_profiled(const bpt_layer_desc_t* desc, const void* X,
+                                    const bpt_layer_weights_t* weights, void* Z,
+                                    void* workspace, size_t workspace_bytes, void* hip_stream,
+                                    void* const events[5]);
+
+/* n_layers >= 1 layers applied in turn, all with the shape of *desc; layers is
+ * a HOST array of n_layers weight sets (each holding device pointers). Layer 0
+ * reads X in desc->dtype; the residual stream between layers is fp32; the last
+ * layer writes Z in desc->out_dtype. No final LN. */
+bpt_status_t bpt_stack_fwd(const bpt_layer_desc_t* desc, int32_t n_layers, const void* X,
+                           const bpt_layer_weights_t* layers, void* Z,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Static text for a status code. */
+const char* bpt_status_str(bpt_status_t status);
+
+/* Detail of the calling thread's last non-OK status ("" if none). */
+const char* bpt_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* bpt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPT_H_ */

@@ -1,0 +1,89 @@
+// Host-only driver for the C ABI's validation layer, built with ASan + UBSan by
+// tests/test_abi.py. The kernel launcher is replaced by a stub that records what
+// it was asked to do, so valid calls can be exercised without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../blockwise_attn_ffn_amd/csrc/bpt_internal.h"
+#include "bpt.h"
+
+namespace bpt {
+static int g_launches = 0;
+static LayerLaunch g_last[8];
+int launch_layer(const LayerLaunch& L, void*, char*, size_t) {
+  if (g_launches < 8) g_last[g_launches] = L;
+  ++g_launches;
+  return 0;
+}
+}  // namespace bpt
+
+static int g_fail = 0;
+#define EXPECT(c)                                               \
+  do {                                                          \
+    if (!(c)) {                                                 \
+      printf("FAILED line %d: %s (%s)\n", __LINE__, #c, bpt_last_error()); \
+      g_fail = 1;                                               \
+    }                                                           \
+  } while (0)
+
+static char* fake(uint64_t off) { return reinterpret_cast<char*>(uintptr_t(0x7f0000000000ull + off)); }
+
+int main() {
+  bpt_layer_desc_t d;
+  memset(&d, 0, sizeof(d));
+  d.batch = 2; d.seq_len = 200; d.d_model = 256; d.n_heads = 4; d.d_ff = 1024;
+  d.block_q = 128; d.block_kv = 64; d.causal = 1; d.ln_eps = 1e-5f;
+  d.dtype = BPT_BF16; d.out_dtype = BPT_BF16;
+  bpt_layer_weights_t w[3];
+  for (int l = 0; l < 3; ++l) {
+    const void** p = reinterpret_cast<const void**>(&w[l]);
+    for (int i = 0; i < 10; ++i) p[i] = fake((3ull << 36) + (uint64_t)(l * 10 + i) * (1ull << 30));
+  }
+  const size_t need = bpt_layer_workspace_bytes(&d);
+  EXPECT(need > 0);
+  // a valid layer call reaches the launcher once, with the carved workspace
+  EXPECT(bpt_layer_fwd(&d, fake(0), &w[0], fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_OK);
+  EXPECT(bpt::g_launches == 1);
+  EXPECT(bpt::g_last[0].ldv == 200 && bpt::g_last[0].d_head == 64);
+  EXPECT(bpt::g_last[0].stats == fake(2ull << 36));
+  EXPECT((char*)bpt::g_last[0].vt > (char*)bpt::g_last[0].k && (char*)bpt::g_last[0].k > (char*)bpt::g_last[0].q);
+  // a 3-layer stack with a bf16 Z uses the workspace residual buffer between layers
+  const size_t need3 = bpt_stack_workspace_bytes(&d, 3);
+  EXPECT(need3 > need);
+  bpt::g_launches = 0;
+  EXPECT(bpt_stack_fwd(&d, 3, fake(0), w, fake(1ull << 36), fake(2ull << 36), need3, nullptr) == BPT_OK);
+  EXPECT(bpt::g_launches == 3);
+  EXPECT(bpt::g_last[0].x == fake(0) && bpt::g_last[0].x_f32 == 0 && bpt::g_last[0].z_f32 == 1);
+  EXPECT(bpt::g_last[1].x == bpt::g_last[0].z && bpt::g_last[1].z == bpt::g_last[0].z);
+  EXPECT(bpt::g_last[2].z == fake(1ull << 36) && bpt::g_last[2].z_f32 == 0);
+  EXPECT(bpt_stack_fwd(&d, 3, fake(0), w, fake(1ull << 36), fake(2ull << 36), need3 - 1, nullptr) == BPT_ERR_WORKSPACE);
+  // with an fp32 Z the residual stream lives in Z
+  d.out_dtype = BPT_F32;
+  EXPECT(bpt_stack_workspace_bytes(&d, 3) == need);
+  bpt::g_launches = 0;
+  EXPECT(bpt_stack_fwd(&d, 3, fake(0), w, fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_OK);
+  EXPECT(bpt::g_last[0].z == fake(1ull << 36) && bpt::g_last[1].x == fake(1ull << 36));
+  // invalid inputs never reach the launcher
+  bpt::g_launches = 0;
+  bpt_layer_desc_t bad = d;
+  bad.ln_eps = NAN;
+  EXPECT(bpt_layer_fwd(&bad, fake(0), &w[0], fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_ERR_SHAPE);
+  bad = d; bad.n_heads = 3;
+  EXPECT(bpt_layer_fwd(&bad, fake(0), &w[0], fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_ERR_SHAPE);
+  bad = d; bad.block_kv = 32;
+  EXPECT(bpt_layer_fwd(&bad, fake(0), &w[0], fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_ERR_UNSUPPORTED);
+  EXPECT(bpt_layer_fwd(&d, fake(0), &w[0], fake(64), fake(2ull << 36), need, nullptr) == BPT_ERR_ALIAS);
+  EXPECT(bpt_layer_fwd(&d, fake(0), nullptr, fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_ERR_NULL);
+  EXPECT(bpt_layer_fwd(nullptr, fake(0), &w[0], fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_ERR_NULL);
+  EXPECT(bpt::g_launches == 0);
+  EXPECT(strlen(bpt_last_error()) > 0);
+  EXPECT(strcmp(bpt_status_str(BPT_ERR_ALIAS), "overlapping buffers") == 0);
+  // empty calls
+  bad = d; bad.batch = 0;
+  EXPECT(bpt_layer_fwd(&bad, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == BPT_OK);
+  EXPECT(bpt::g_launches == 0);
+  if (!g_fail) printf("ALL OK\n");
+  return g_fail;
+}

@@ -1,0 +1,188 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function the
+header declares, sizes the workspace by its formula, and rejects every invalid
+argument before anything is enqueued.
+
+Every call here fails validation (or is an empty call), so no kernel is ever
+launched: the pointers are fake, 16-byte-aligned integers.
+"""
+import ctypes
+import math
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from blockwise_attn_ffn_amd import bpt, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bpt.h")
+
+FAKE = 0x7f0000000000  # aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bpt_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = bpt.lib()
+    names = declared_functions()
+    assert set(names) == set(bpt.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.bpt_version().decode().count(".") == 2
+
+
+def test_status_strings():
+    lib = bpt.lib()
+    for code in range(8):
+        assert lib.bpt_status_str(code).decode() not in ("", "unknown status")
+    assert lib.bpt_status_str(99).decode() == "unknown status"
+
+
+def desc(**kw):
+    base = dict(batch=2, seq_len=200, d_model=256, n_heads=4, d_ff=1024, block_q=128,
+                block_kv=128, causal=True, dtype="bf16", out_dtype="f32")
+    base.update(kw)
+    return bpt.make_desc(**base)
+
+
+def expected_workspace(batch, n, d, es, stack_resid=False):
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    rows = batch * n
+    ldv = (n + 7) // 8 * 8
+    tot = up(rows * 8) + 2 * up(rows * d * es) + up(batch * d * ldv * es)
+    if stack_resid:
+        tot += up(rows * d * 4)
+    return tot
+
+
+@pytest.mark.parametrize("batch,n,d,h,dt", [(2, 200, 256, 4, "bf16"), (1, 131072, 2048, 16, "bf16"),
+                                            (64, 1024, 1024, 16, "bf16"), (1, 77, 128, 2, "f32")])
+def test_workspace_formula(batch, n, d, h, dt):
+    dsc = desc(batch=batch, seq_len=n, d_model=d, n_heads=h, d_ff=4 * d, dtype=dt,
+               block_q=64, block_kv=64)
+    es = 4 if dt == "f32" else 2
+    assert bpt.layer_workspace_bytes(dsc) == expected_workspace(batch, n, d, es)
+    assert bpt.stack_workspace_bytes(dsc, 1) == expected_workspace(batch, n, d, es)
+    dsc.out_dtype = bpt.BF16
+    assert bpt.stack_workspace_bytes(dsc, 3) == expected_workspace(batch, n, d, es, True)
+    dsc.out_dtype = bpt.F32
+    assert bpt.stack_workspace_bytes(dsc, 3) == expected_workspace(batch, n, d, es)
+
+
+def test_workspace_is_block_shaped_not_ffn_shaped():
+    """No [rows, d_ff] hidden state and no [N, N] logits are part of the footprint."""
+    for name in ("gpt2_medium", "long_128k"):
+        w = synth.WORKLOADS[name]
+        ws = bpt.layer_workspace_bytes(bpt.desc_for(w))
+        assert ws < w.rows * w.d_ff * 2                  # one bf16 [rows, 4d]
+        assert ws < 3.1 * w.rows * w.d_model * 2 + w.rows * 8
+    w = synth.WORKLOADS["long_128k"]
+    assert bpt.layer_workspace_bytes(bpt.desc_for(w)) < w.seq_len * w.seq_len * 2
+
+
+def call_layer(dsc, x=FAKE, z=FAKE + (1 << 36), ws=FAKE + (2 << 36), nbytes=1 << 40,
+               weights=None):
+    lib = bpt.lib()
+    if weights is None:
+        weights = bpt.LayerWeights(*[FAKE + (3 << 36) + i * (1 << 30) for i in range(10)])
+    return lib.bpt_layer_fwd(ctypes.byref(dsc) if dsc is not None else None, x,
+                             ctypes.byref(weights) if weights != 0 else None, z, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", -1, 2), ("seq_len", -5, 2), ("d_model", 0, 2), ("n_heads", 0, 2),
+    ("n_heads", 3, 2), ("d_ff", 0, 2), ("block_q", 0, 2), ("causal", 2, 2),
+    ("ln_eps", 0.0, 2), ("ln_eps", float("nan"), 2), ("ln_eps", float("inf"), 2),
+    ("dtype", 7, 2), ("out_dtype", -1, 2), ("act", 1, 3), ("precision", 1, 3),
+    ("d_model", 640, 3), ("n_heads", 8, 3),           # d_head 32
+    ("block_q", 96, 3), ("block_kv", 256, 3), ("d_ff", 1000, 3),
+])
+def test_invalid_descriptor(field, value, status):
+    dsc = desc()
+    setattr(dsc, field, value)
+    assert call_layer(dsc) == status
+    assert bpt.last_error() != ""
+    assert bpt.layer_workspace_bytes(dsc) == 0
+
+
+def test_row_count_overflow():
+    dsc = desc(batch=1 << 16, seq_len=1 << 16)
+    assert call_layer(dsc) == 2
+
+
+def test_null_and_alignment_and_workspace_and_alias():
+    dsc = desc()
+    need = bpt.layer_workspace_bytes(dsc)
+    assert need > 0
+    lib = bpt.lib()
+    assert lib.bpt_layer_fwd(None, FAKE, None, FAKE, FAKE, 0, None) == 1   # NULL desc
+    assert call_layer(dsc, weights=0) == 1                                # NULL weights
+    w = bpt.LayerWeights(*[FAKE + (3 << 36) + i * (1 << 30) for i in range(10)])
+    w.w_2 = None
+    assert call_layer(dsc, weights=w) == 1 and "w_2" in bpt.last_error()
+    w.w_2 = FAKE + 8
+    assert call_layer(dsc, weights=w) == 4                                # misaligned weight
+    assert call_layer(dsc, x=0) == 1
+    assert call_layer(dsc, z=0) == 1
+    assert call_layer(dsc, x=FAKE + 4) == 4
+    assert call_layer(dsc, ws=FAKE + (2 << 36) + 8) == 4
+    assert call_layer(dsc, nbytes=need - 1) == 5
+    assert call_layer(dsc, ws=0, nbytes=need) == 1
+    assert call_layer(dsc, z=FAKE + 256) == 6                             # X and Z overlap
+    assert call_layer(dsc, ws=FAKE + 1024, nbytes=need) == 6              # workspace over X
+    assert call_layer(dsc, ws=FAKE + (1 << 36) - 256, nbytes=need) == 6   # workspace over Z
+
+
+def test_empty_call_is_ok_with_null_pointers():
+    lib = bpt.lib()
+    for b, n in ((0, 10), (3, 0)):
+        dsc = desc(batch=b, seq_len=n)
+        assert lib.bpt_layer_fwd(ctypes.byref(dsc), None, None, None, None, 0, None) == 0
+        assert bpt.layer_workspace_bytes(dsc) == 0
+
+
+def test_stack_validation():
+    lib = bpt.lib()
+    dsc = desc()
+    arr = (bpt.LayerWeights * 2)(*[bpt.LayerWeights(*[FAKE + (3 << 36) + i * (1 << 30)
+                                                      for i in range(10)]) for _ in range(2)])
+    big = 1 << 40
+    assert lib.bpt_stack_fwd(ctypes.byref(dsc), 0, FAKE, arr, FAKE + (1 << 36), FAKE + (2 << 36),
+                             big, None) == 2
+    assert lib.bpt_stack_fwd(ctypes.byref(dsc), 2, FAKE, None, FAKE + (1 << 36), FAKE + (2 << 36),
+                             big, None) == 1
+    arr[1].w_k = None
+    assert lib.bpt_stack_fwd(ctypes.byref(dsc), 2, FAKE, arr, FAKE + (1 << 36), FAKE + (2 << 36),
+                             big, None) == 1
+    assert "weights[1].w_k" in bpt.last_error()
+    assert bpt.stack_workspace_bytes(dsc, 0) == 0
+
+
+def test_every_named_workload_is_supported():
+    for w in synth.WORKLOADS.values():
+        if w.d_model == 4096:
+            continue  # the 4096-wide stack has no epilogue instance yet
+        assert bpt.layer_workspace_bytes(bpt.desc_for(w)) > 0, (w.name, bpt.last_error())
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_host_abi_under_address_and_ub_sanitizers(tmp_path):
+    """Build the host validation layer alone with ASan + UBSan (launches stubbed) and
+    drive every entry point, including valid calls that reach the (stub) launcher."""
+    csrc = os.path.join(ROOT, "blockwise_attn_ffn_amd", "csrc")
+    drv = os.path.join(os.path.dirname(__file__), "abi_host_driver.cpp")
+    exe = str(tmp_path / "abi_host")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", f"-I{os.path.join(ROOT, 'include')}",
+           os.path.join(csrc, "bpt_api.cpp"), os.path.join(csrc, "bpt_support.cpp"), drv, "-o", exe]
+    subprocess.run(cmd, check=True)
+    res = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stdout
+    assert "ALL OK" in res.stdout

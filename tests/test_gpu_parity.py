@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path through the C ABI against the CPU float64 oracle.
+
+Tolerances (Z against the oracle): bf16 operands max|err| <= 2e-2 and relative
+Frobenius <= 5e-3; fp32 both <= 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+from blockwise_attn_ffn_amd import bpt, synth
+from tests._parity import check, oracle_full, oracle_rows, run_gpu, say, seq_rows
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def small(**kw) -> synth.Workload:
+    base = dict(name="small", batch=2, seq_len=200, d_model=256, n_heads=4, d_ff=1024,
+                causal=True, block_q=128, block_kv=128, dtype="bf16", ln_random=True)
+    base.update(kw)
+    return synth.Workload(**base)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_all_rows():
+    w = W["tiny_fp32"]
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=0)
+    got = run_gpu(w, inp, "f32")
+    check(got, oracle_full(w, inp), "f32", w.name)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gpt2_small_two_sequences(out):
+    w = W["gpt2_small"]
+    say(f"case {w} out={out}")
+    inp = synth.make_inputs(w, seed=0)
+    got = run_gpu(w, inp, out)
+    seqs = [0, 7]
+    check(got[torch.from_numpy(seq_rows(w, seqs))], oracle_full(w, inp, seqs), "bf16", w.name)
+
+
+def test_gpt2_medium_four_sequences():
+    w = W["gpt2_medium"]
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=0)
+    got = run_gpu(w, inp, "f32")
+    seqs = [0, 21, 42, 63]
+    check(got[torch.from_numpy(seq_rows(w, seqs))], oracle_full(w, inp, seqs), "bf16", w.name)
+
+
+def test_long_context_sampled_rows():
+    w = W["long_128k"]
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=0)
+    got = run_gpu(w, inp, "f32")
+    rows = synth.sample_rows(w, w.sample_rows, seed=0)
+    check(got[torch.from_numpy(rows)], oracle_rows(w, inp, rows), "bf16", w.name)
+
+
+# ---------------------------------------------------------------------------
+# Several tiles with ragged tails, both masks, every block-size pair
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("bq,bkv", [(128, 128), (128, 64), (64, 128), (64, 64)])
+def test_small_bf16_dk64_ragged(causal, bq, bkv):
+    w = small(causal=causal, block_q=bq, block_kv=bkv)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=3)
+    check(run_gpu(w, inp), oracle_full(w, inp), "bf16", "small dk64")
+
+
+@pytest.mark.parametrize("n", [100, 131, 256, 1])
+def test_small_bf16_dk128_ragged(n):
+    """d_k = 128, lengths that are not multiples of 8 or of the blocks."""
+    w = small(seq_len=n, n_heads=2, block_q=128, block_kv=64)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=4)
+    check(run_gpu(w, inp), oracle_full(w, inp), "bf16", f"small dk128 n={n}")
+
+
+@pytest.mark.parametrize("d,h", [(512, 8), (768, 12), (1024, 16), (2048, 16)])
+def test_each_model_width(d, h):
+    w = small(batch=1, seq_len=136, d_model=d, n_heads=h, d_ff=4 * d)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=5)
+    check(run_gpu(w, inp), oracle_full(w, inp), "bf16", f"d={d}")
+
+
+@pytest.mark.parametrize("n,causal,d,h", [(200, True, 128, 2), (77, False, 256, 4),
+                                          (64, True, 256, 2)])
+def test_small_fp32(n, causal, d, h):
+    w = small(dtype="f32", seq_len=n, causal=causal, d_model=d, n_heads=h, d_ff=4 * d,
+              block_q=64, block_kv=64)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=6)
+    check(run_gpu(w, inp), oracle_full(w, inp), "f32", f"fp32 n={n}")
+
+
+def test_peaky_attention_fp32_catches_gelu_and_scale():
+    """Larger weights: sharp softmax rows and large FFN pre-activations, in fp32 where
+    the 1e-4 tolerance resolves the tanh-vs-erf GELU gap and the 1/sqrt(d_k) scale."""
+    w = small(dtype="f32", seq_len=128, d_model=128, n_heads=2, d_ff=512, block_q=64,
+              block_kv=64, w_std=0.15)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=7)
+    check(run_gpu(w, inp), oracle_full(w, inp), "f32", "peaky fp32")
+
+
+def test_near_constant_rows_ln_eps():
+    """Rows whose spread is comparable to sqrt(eps): LN's epsilon placement matters."""
+    w = small(dtype="f32", seq_len=64, d_model=128, n_heads=2, d_ff=512, block_q=64,
+              block_kv=64, causal=False)
+    inp = synth.make_inputs(w, seed=8)
+    x = inp["x"].clone()
+    x[::3] = 4.0 + 3e-3 * x[::3]
+    inp["x"] = x
+    say(f"case near-constant rows {w}")
+    check(run_gpu(w, inp), oracle_full(w, inp), "f32", "near-constant rows")
+
+
+# ---------------------------------------------------------------------------
+# Stacks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_stack_three_layers(out):
+    w = small(n_layers=3, seq_len=96, w_std_layer_decay=True)
+    say(f"case {w} out={out}")
+    inp = synth.make_inputs(w, seed=9)
+    got = run_gpu(w, inp, out)
+    check(got, oracle_full(w, inp), "bf16", f"stack out={out}")
+
+
+def test_stack_fp32_two_layers():
+    w = small(dtype="f32", n_layers=2, seq_len=80, d_model=128, n_heads=2, d_ff=512,
+              block_q=64, block_kv=64)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=10)
+    check(run_gpu(w, inp), oracle_full(w, inp), "f32", "stack fp32")
+
+
+# ---------------------------------------------------------------------------
+# Degenerate inputs and the ABI's behaviour on the device
+# ---------------------------------------------------------------------------
+
+def test_empty_batch_is_a_no_op():
+    w = small(batch=0)
+    desc = bpt.desc_for(w)
+    assert bpt.layer_workspace_bytes(desc) == 0
+    z = torch.full((4,), 7.0, device="cuda")
+    bpt.layer_fwd(desc, None, {k: None for k in bpt.WEIGHT_FIELDS}, z, None)
+    torch.cuda.synchronize()
+    assert torch.all(z == 7.0)
+
+
+def test_bf16_output_is_rne_of_fp32_output():
+    """Z in bf16 is the round-to-nearest-even of the fp32 result, element for element."""
+    w = small(seq_len=64)
+    inp = synth.make_inputs(w, seed=11)
+    say(f"case {w} bf16 vs f32 out")
+    z32 = run_gpu(w, inp, "f32")
+    z16 = run_gpu(w, inp, "bf16")
+    assert torch.equal(z32.to(torch.bfloat16), z16)
+
+
+def test_repeatable_and_no_device_allocation():
+    """Two calls give bitwise-equal results; free device memory is unchanged by a call
+    (the library allocates nothing; its whole footprint is the caller's workspace)."""
+    w = small(seq_len=256)
+    inp = synth.make_inputs(w, seed=12)
+    dev = {"x": inp["x"].cuda(), "layers": [{k: v.cuda() for k, v in inp["layers"][0].items()}]}
+    desc = bpt.desc_for(w)
+    ws = bpt.alloc_workspace(bpt.layer_workspace_bytes(desc))
+    z1 = torch.empty((w.rows, w.d_model), device="cuda")
+    z2 = torch.empty_like(z1)
+    bpt.layer_fwd(desc, dev["x"], dev["layers"][0], z1, ws)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    ws.fill_(0xFF)  # NaN-poison the workspace between calls
+    bpt.layer_fwd(desc, dev["x"], dev["layers"][0], z2, ws)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free0 == free1
+    assert torch.equal(z1, z2)
