@@ -1,6 +1,6 @@
 // Host side of the C ABI declared in include/bpt.h: validation, workspace
 // sizing and carving, and the per-layer / per-stack launch sequence.
-// Plain C++ (no HIP headers): the launches themselves live in bpt_kernels.hip.
+// Plain C++ (no HIP headers): the launches themselves live in the k_*.hip units.
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -50,6 +50,9 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   off = round_up(off + rows * d->d_model * es, kAlign);
   L.vt_off = off;
   off = round_up(off + (size_t)d->batch * d->d_model * ldv_of(d->seq_len) * es, kAlign);
+  L.wpack_off = off;  // W_O, W_1, W_2 back to back, fragment order
+  off = round_up(off + ((size_t)d->d_model * d->d_model + 2 * (size_t)d->d_ff * d->d_model) * es,
+                 kAlign);
   L.resid_off = off;
   if (stack_resid) off = round_up(off + rows * d->d_model * 4, kAlign);
   L.total = off;
@@ -138,6 +141,7 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   p.q = base + L.q_off;
   p.k = base + L.k_off;
   p.vt = base + L.vt_off;
+  p.wpack = base + L.wpack_off;
   return p;
 }
 

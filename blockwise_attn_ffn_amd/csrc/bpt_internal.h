@@ -1,5 +1,5 @@
 // Internal interface between the host validation/dispatch layer (bpt_api.cpp,
-// plain C++) and the HIP launchers (bpt_kernels.hip). Nothing here is exported.
+// plain C++) and the HIP launchers (k_*.hip, bpt_launch.hip). Nothing here is exported.
 #pragma once
 
 #include <stddef.h>
@@ -29,13 +29,14 @@ struct LayerLaunch {
   void* q;           // [rows, d] Q, then the attention output O (in place)
   void* k;           // [rows, d]
   void* vt;          // [batch, heads, d_head, ldv]
+  void* wpack;       // W_O | W_1 | W_2 repacked in matrix-core fragment order
   // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
   void* const* events;
 };
 
 // Element counts/byte sizes of the workspace pieces (shared by sizing and carving).
 struct WorkspaceLayout {
-  size_t stats_off, q_off, k_off, vt_off, resid_off, total;
+  size_t stats_off, q_off, k_off, vt_off, wpack_off, resid_off, total;
 };
 
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).

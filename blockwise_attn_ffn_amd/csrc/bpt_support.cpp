@@ -1,5 +1,5 @@
 // Which kernel instances exist: the host-side support table, kept beside the
-// dispatch in bpt_kernels.hip (every combination accepted here has an instance).
+// dispatch in k_*.hip (every combination accepted here has an instance).
 #include <stdio.h>
 
 #include "bpt_internal.h"

@@ -1,0 +1,345 @@
+// Fused per-row-tile epilogue of the BPT layer (gfx950): output projection,
+// residual, LN2, FFN W_1 -> GELU -> W_2 and the second residual.
+//
+// "Blockwise Parallel Transformer — BPT" (aicassindra.com): section "The fused
+// blockwise algorithm" (y_i = x_i + (o/l) W_O, h_i = act(LN(y_i) W_1),
+// Z[i] = y_i + h_i W_2, then h_i is freed) and "The structural fact that makes
+// fusion legal" (LN, the FFN and the residuals act on each row alone, so a row
+// tile can be finished as soon as its attention output exists).
+//
+// One workgroup = BM token rows, 4 waves. Wave w owns output features
+// [w D/4, (w+1) D/4) of all BM rows; their fp32 accumulators stay in registers
+// from Y through Z. The [BM, d_ff] hidden state is produced and consumed in
+// chunks of HC units, each chunk living only in registers and LDS.
+//
+// Weight fragments (W_O, W_1, W_2, repacked so that each fragment is one
+// contiguous 64-lane load) stream from L2 into a ring of P register stages that
+// runs continuously across the three phases, so the loads of later stages are in
+// flight while the matrix cores work.
+#include <type_traits>
+
+#include "bpt_device.hpp"
+#include "bpt_launch.hpp"
+
+namespace bpt {
+
+// LDS layout of the [BM, K] operand tiles (LN2(Y) / the O tile with K = D, the
+// hidden chunk with K = HC): k-block major. A k-block holds 64 consecutive k of
+// all BM rows, one 8 * CB-byte row segment per row (CB = bytes of 8 elements);
+// inside a segment the 8-element chunk c sits at slot c ^ swz(row). A lane then
+// needs one offset per k-step of a block; blocks and row tiles are immediates.
+template <typename T, int BM>
+struct KBlockLayout {
+  static constexpr int CB = 8 * (int)sizeof(T);
+  static constexpr int RB = 8 * CB;        // bytes per row segment
+  static constexpr int KBB = BM * RB;      // bytes per k-block
+  __device__ static int off(int row, int chunk) {   // chunk = k / 8
+    return (chunk >> 3) * KBB + row * RB + (((chunk & 7) ^ swz(row)) * CB);
+  }
+};
+
+template <typename TX, typename T, typename TO, int D, int BM, int HC, int P>
+__global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
+    const TX* X, const T* __restrict__ Oin, const T* __restrict__ wp,
+    const T* __restrict__ ln_g, const T* __restrict__ ln_b, TO* Z, int R, int dff, float eps) {
+  // wp: W_O | W_1 | W_2 in matrix-core fragment order (k_pack.hip): fragment
+  // (row tile, k-step) = 64 lanes x 8 consecutive elements.
+  using O = Op<T>;
+  using F = typename O::frag;
+  using LY = KBlockLayout<T, BM>;
+  constexpr int NCW = D / 4;             // features per wave
+  constexpr int NT = NCW / 32;           // 32-feature tiles per wave
+  constexpr int RT = BM / 32;            // 32-row tiles
+  constexpr int FT = HC / 4 / 32;        // hidden tiles per wave per chunk
+  constexpr int KBO = D / 64;            // k-blocks when k runs over d (W_O, W_1)
+  constexpr int KB2 = HC / 64;           // k-blocks when k runs over a chunk (W_2)
+  constexpr int SA = 4;                  // stage = one 32-row weight tile x 4 k-steps
+  constexpr int N_WO = KBO * NT, N_W1 = KBO * FT, N_W2 = KB2 * NT;
+  static_assert(NT >= 1 && RT >= 1 && FT >= 1 && D % 64 == 0 && HC % 64 == 0, "tile");
+  static_assert(N_WO % P == 0 && N_W1 % P == 0 && N_W2 % P == 0, "stages per phase vs ring");
+  static_assert(P == 2 || P == 4, "ring depth");
+  static_assert(KBO % 4 == 0 || P == 2, "k-blocks vs unroll");
+  static_assert(8 * BM * 4 + 2 * D * (int)sizeof(T) <= KB2 * KBlockLayout<T, BM>::KBB,
+                "LN2 scratch must fit in the hidden-chunk buffer");
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  unsigned char* ys = smem_raw;                 // [KBO k-blocks]: O tile, then LN2(Y)
+  unsigned char* hs = smem_raw + KBO * LY::KBB; // [KB2 k-blocks]: hidden chunk
+  float* red = reinterpret_cast<float*>(hs);    // [2][4][BM] row partial sums
+  T* gb = reinterpret_cast<T*>(red + 8 * BM);   // [2][D] LN2 gain and bias (as given)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int rho = lane & 31, hf = lane >> 5;
+  const int r0 = blockIdx.x * BM;
+  const int n0w = wave * NCW;
+  const int n_chunks = dff / HC;
+  const int per_chunk = N_W1 + N_W2;
+  const int n_stages = N_WO + n_chunks * per_chunk;
+
+  // B-fragment byte offsets of this lane inside a k-block, one per k-step
+  int boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) boff[j] = rho * LY::RB + (((2 * j + hf) ^ swz(rho)) * LY::CB);
+
+  constexpr int FRAG = 64 * 8;                  // elements per packed fragment
+  constexpr int W1_FRAG = D * D / FRAG;         // first W_1 fragment
+  const int W2_FRAG = W1_FRAG + dff * D / FRAG; // first W_2 fragment
+
+  // Stage t of the weight stream: W_O (k-block major, then tile), then per chunk
+  // the W_1 and W_2 stages. Branch-free: every stage issues SA loads (stages past
+  // the end reload the last one), so the memory-counter waits stay exact.
+  auto load_stage = [&](int t, F (&dst)[SA]) {
+    t = __builtin_amdgcn_readfirstlane(min(t, n_stages - 1));
+    int frag;  // index of the stage's first fragment; 4 consecutive k-steps follow
+    if (t < N_WO) {
+      const int kb = t / NT, a = t - kb * NT;
+      frag = (wave * NT + a) * (D / 16) + kb * 4;
+    } else {
+      const int u = t - N_WO, c = u / per_chunk;
+      const int s = u - c * per_chunk;
+      if (s < N_W1) {
+        const int kb = s / FT, ft = s - kb * FT;
+        frag = W1_FRAG + (c * (HC / 32) + wave * FT + ft) * (D / 16) + kb * 4;
+      } else {
+        const int s2 = s - N_W1, kb = s2 / NT, a = s2 - kb * NT;
+        frag = W2_FRAG + (wave * NT + a) * (dff / 16) + c * (HC / 16) + kb * 4;
+      }
+    }
+    const T* base = wp + (size_t)frag * FRAG + lane * 8;
+#pragma unroll
+    for (int j = 0; j < SA; ++j) dst[j] = ld_frag(base + j * FRAG);
+  };
+
+  F ring[P][SA];
+  int t_next = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_stage(t_next++, ring[p]);
+
+  // ---- stage the attention-output tile O[r0 : r0 + BM, :] and LN2's gain/bias.
+  //      Rows past the end are clamped; their results are never stored.
+  for (int c = tid; c < BM * (D / 8); c += 256) {
+    const int row = c / (D / 8), cc = c - row * (D / 8);
+    const int r = min(r0 + row, R - 1);
+    st_chunk(reinterpret_cast<T*>(ys + LY::off(row, cc)), ld_chunk(Oin + (size_t)r * D + cc * 8));
+  }
+  for (int c = tid; c < D / 8; c += 256) {
+    st_chunk(gb + 8 * c, ld_chunk(ln_g + 8 * c));
+    st_chunk(gb + D + 8 * c, ld_chunk(ln_b + 8 * c));
+  }
+  __syncthreads();
+
+  // One GEMM phase: accs[tile][r] += A(ring stages) * B(LDS k-blocks of src).
+  // Stages run k-block major; B fragments of the next k-block are read at the
+  // first stage of the current one.
+  auto gemm_phase = [&](const unsigned char* src, int n_kb, auto& accs, auto tiles_c) {
+    constexpr int TT = decltype(tiles_c)::value;
+    // k-blocks unrolled together: even (B double buffer) and a multiple of the ring
+    constexpr int U = ((2 * TT) % P == 0) ? 2 : 4;
+    F bq[2][4][RT];
+    auto load_b = [&](int kb, F (&dst)[4][RT]) {
+      const unsigned char* blk = src + kb * LY::KBB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < RT; ++b)
+          dst[j][b] = *reinterpret_cast<const F*>(blk + b * 32 * LY::RB + boff[j]);
+    };
+    load_b(0, bq[0]);
+    for (int kb0 = 0; kb0 < n_kb; kb0 += U) {
+#pragma unroll
+      for (int ku = 0; ku < U; ++ku) {
+        const int kb = kb0 + ku;
+#pragma unroll
+        for (int a = 0; a < TT; ++a) {
+          const int p = (ku * TT + a) % P;
+          if (a == 0 && kb + 1 < n_kb) load_b(kb + 1, bq[(ku + 1) & 1]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int b = 0; b < RT; ++b) O::mma(accs[a][b], ring[p][j], bq[ku & 1][j][b]);
+          load_stage(t_next++, ring[p]);
+        }
+      }
+    }
+  };
+
+  // ---- Y^T = W_O O^T
+  f32x16 acc[NT][RT];
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int b = 0; b < RT; ++b) acc[a][b] = f32x16{};
+  gemm_phase(ys, KBO, acc, std::integral_constant<int, NT>{});
+
+  // ---- + X (residual) and LN2 statistics (biased variance, two passes)
+  float psum[RT];
+#pragma unroll
+  for (int b = 0; b < RT; ++b) {
+    const int r = min(r0 + b * 32 + rho, R - 1);
+    const TX* xr = X + (size_t)r * D + n0w + 8 * hf;
+    float s = 0.f;
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float xv[8];
+        load8_f32(xr + a * 32 + 16 * g, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[a][b][8 * g + e] += xv[e];
+          s += acc[a][b][8 * g + e];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    psum[b] = s + __shfl_xor(s, 32, 64);
+  }
+  __syncthreads();  // every wave is done reading the O tile
+  if (hf == 0) {
+#pragma unroll
+    for (int b = 0; b < RT; ++b) red[wave * BM + b * 32 + rho] = psum[b];
+  }
+  __syncthreads();
+  float mean[RT], rstd[RT];
+#pragma unroll
+  for (int b = 0; b < RT; ++b) {
+    const int row = b * 32 + rho;
+    mean[b] = (red[row] + red[BM + row] + red[2 * BM + row] + red[3 * BM + row]) / (float)D;
+    float q = 0.f;
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float t = acc[a][b][i] - mean[b];
+        q += t * t;
+      }
+    psum[b] = q + __shfl_xor(q, 32, 64);
+  }
+  if (hf == 0) {
+#pragma unroll
+    for (int b = 0; b < RT; ++b) red[4 * BM + wave * BM + b * 32 + rho] = psum[b];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < RT; ++b) {
+    const int row = b * 32 + rho;
+    const float q = red[4 * BM + row] + red[5 * BM + row] + red[6 * BM + row] + red[7 * BM + row];
+    rstd[b] = 1.0f / sqrtf(q / (float)D + eps);
+  }
+  // ---- LN2(Y) -> ys (compute type), 8 consecutive features per store
+#pragma unroll
+  for (int a = 0; a < NT; ++a) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int n = n0w + a * 32 + 16 * g + 8 * hf;
+      float gv[8], bv[8];
+      load8_f32(gb + n, gv);
+      load8_f32(gb + D + n, bv);
+#pragma unroll
+      for (int b = 0; b < RT; ++b) {
+        const int row = b * 32 + rho;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (acc[a][b][8 * g + e] - mean[b]) * rstd[b] * gv[e] + bv[e];
+        *reinterpret_cast<F*>(ys + LY::off(row, n >> 3)) = O::from_f32(v);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+
+  // ---- FFN over hidden chunks
+  for (int c = 0; c < n_chunks; ++c) {
+    // U^T = W_1[chunk] LN2(Y)^T : this wave's HC/4 hidden units of all BM rows
+    f32x16 u[FT][RT];
+#pragma unroll
+    for (int a = 0; a < FT; ++a)
+#pragma unroll
+      for (int b = 0; b < RT; ++b) u[a][b] = f32x16{};
+    gemm_phase(ys, KBO, u, std::integral_constant<int, FT>{});
+    // H = GELU(U) -> hs
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int fl = wave * (HC / 4) + ft * 32 + 16 * g + 8 * hf;   // unit within the chunk
+#pragma unroll
+        for (int b = 0; b < RT; ++b) {
+          const int row = b * 32 + rho;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = gelu_tanh(u[ft][b][8 * g + e]);
+          *reinterpret_cast<F*>(hs + LY::off(row, fl >> 3)) = O::from_f32(v);
+        }
+      }
+    }
+    __syncthreads();
+    // Z^T += W_2[:, chunk] H^T
+    gemm_phase(hs, KB2, acc, std::integral_constant<int, NT>{});
+    __syncthreads();
+  }
+
+  // ---- Z = Y + H W_2
+#pragma unroll
+  for (int b = 0; b < RT; ++b) {
+    const int r = r0 + b * 32 + rho;
+    if (r >= R) continue;
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = acc[a][b][8 * g + e];
+        store8_f32(Z + (size_t)r * D + n0w + a * 32 + 16 * g + 8 * hf, v);
+      }
+    }
+  }
+}
+
+namespace {
+
+template <typename TX, typename T, typename TO, int D, int BM, int HC, int P>
+int run_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
+  const int rows = L.batch * L.seq_len;
+  const size_t smem = (size_t)BM * (D + HC) * sizeof(T);
+  auto k = ffn_epilogue_kernel<TX, T, TO, D, BM, HC, P>;
+  if (set_smem(k, smem, err, n)) return 1;
+  hipLaunchKernelGGL(k, dim3((rows + BM - 1) / BM), dim3(256), smem, s, (const TX*)L.x,
+                     (const T*)L.q, (const T*)L.wpack, (const T*)L.w.ln2_g, (const T*)L.w.ln2_b,
+                     (TO*)L.z, rows, L.d_ff, L.ln_eps);
+  return check_launch("ffn_epilogue", err, n);
+}
+
+template <typename TX, typename T, typename TO>
+int dispatch_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
+  const int d = L.d_model;
+  if constexpr (sizeof(T) == 4) {
+    if (d == 128) return run_ffn<TX, T, TO, 128, 64, 256, 2>(L, s, err, n);
+    if (d == 256) return run_ffn<TX, T, TO, 256, 32, 256, 2>(L, s, err, n);
+  } else {
+    if (d == 256) return run_ffn<TX, T, TO, 256, 64, 256, 4>(L, s, err, n);
+    if (d == 512) return run_ffn<TX, T, TO, 512, 64, 256, 4>(L, s, err, n);
+    if (d == 768) return run_ffn<TX, T, TO, 768, 64, 256, 4>(L, s, err, n);
+    if (d == 1024) return run_ffn<TX, T, TO, 1024, 64, 256, 4>(L, s, err, n);
+    if (d == 2048) return run_ffn<TX, T, TO, 2048, 32, 256, 4>(L, s, err, n);
+  }
+  set_err(err, n, "no epilogue kernel for d_model %s%d", "", d);
+  return 1;
+}
+
+}  // namespace
+
+int launch_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
+  if (L.compute_f32)
+    return L.z_f32 ? dispatch_ffn<float, float, float>(L, s, err, n)
+                   : dispatch_ffn<float, float, bf16>(L, s, err, n);
+  if (L.x_f32)
+    return L.z_f32 ? dispatch_ffn<float, bf16, float>(L, s, err, n)
+                   : dispatch_ffn<float, bf16, bf16>(L, s, err, n);
+  return L.z_f32 ? dispatch_ffn<bf16, bf16, float>(L, s, err, n)
+                 : dispatch_ffn<bf16, bf16, bf16>(L, s, err, n);
+}
+
+}  // namespace bpt

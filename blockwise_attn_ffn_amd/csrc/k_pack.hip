@@ -1,0 +1,56 @@
+// Repacking of the epilogue's weight matrices into matrix-core fragment order.
+//
+// A weight W[n][k] (k contiguous, the library's [out, in] layout) is consumed as
+// the A operand of 32x32 matrix-core tiles: lane l = 32 * hf + rho holds row
+// pi(rho) of a 32-row tile and 8 consecutive k of a 16-wide k-step. Read straight
+// from W, one 64-lane load touches 32 rows, i.e. 32 cache lines per instruction,
+// and the vector-memory path is bound by lines, not bytes. The packed copy puts
+// each (row tile, k-step) fragment in 64 consecutive 8-element chunks in lane
+// order, so one load instruction reads contiguous memory.
+//
+//   packed[((tile * (K / 16) + ks) * 64 + 32 * hf + rho) * 8 + e]
+//       = W[32 * tile + pi(rho)][16 * ks + 8 * hf + e]
+#include "bpt_device.hpp"
+#include "bpt_launch.hpp"
+
+namespace bpt {
+
+// One thread per 8-element chunk of W; reads are row-contiguous.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_frag_kernel(const T* __restrict__ W, T* __restrict__ P,
+                                                        int n_rows, int K) {
+  const int kc = K / 8;                                   // chunks per row
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)n_rows * kc) return;
+  const int row = (int)(i / kc), c = (int)(i - (size_t)row * kc);
+  const int tile = row >> 5, rho = pi_row(row & 31);      // pi is its own inverse
+  const int ks = c >> 1, hf = c & 1;
+  const size_t dst = (((size_t)tile * (K / 16) + ks) * 64 + 32 * hf + rho) * 8;
+  st_chunk(P + dst, ld_chunk(W + (size_t)row * K + (size_t)c * 8));
+}
+
+namespace {
+template <typename T>
+int run_pack(const void* W, void* P, int n_rows, int K, hipStream_t s, char* err, size_t n) {
+  const size_t chunks = (size_t)n_rows * (K / 8);
+  hipLaunchKernelGGL(pack_frag_kernel<T>, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                     (const T*)W, (T*)P, n_rows, K);
+  return check_launch("pack_frag", err, n);
+}
+}  // namespace
+
+// W_O at element 0 of the packed region, W_1 at d*d, W_2 at d*d + d_ff*d.
+template <typename T>
+int pack_all(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
+  const int d = L.d_model, f = L.d_ff;
+  T* p = static_cast<T*>(L.wpack);
+  return run_pack<T>(L.w.w_o, p, d, d, s, err, n) ||
+         run_pack<T>(L.w.w_1, p + (size_t)d * d, f, d, s, err, n) ||
+         run_pack<T>(L.w.w_2, p + (size_t)d * d + (size_t)f * d, d, f, s, err, n);
+}
+
+int launch_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
+  return L.compute_f32 ? pack_all<float>(L, s, err, n) : pack_all<bf16>(L, s, err, n);
+}
+
+}  // namespace bpt

@@ -51,11 +51,13 @@ def desc(**kw):
     return bpt.make_desc(**base)
 
 
-def expected_workspace(batch, n, d, es, stack_resid=False):
+def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None):
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     rows = batch * n
     ldv = (n + 7) // 8 * 8
+    f = 4 * d if d_ff is None else d_ff
     tot = up(rows * 8) + 2 * up(rows * d * es) + up(batch * d * ldv * es)
+    tot += up((d * d + 2 * d * f) * es)
     if stack_resid:
         tot += up(rows * d * 4)
     return tot
@@ -81,7 +83,8 @@ def test_workspace_is_block_shaped_not_ffn_shaped():
         w = synth.WORKLOADS[name]
         ws = bpt.layer_workspace_bytes(bpt.desc_for(w))
         assert ws < w.rows * w.d_ff * 2                  # one bf16 [rows, 4d]
-        assert ws < 3.1 * w.rows * w.d_model * 2 + w.rows * 8
+        weights = (w.d_model * w.d_model + 2 * w.d_model * w.d_ff) * 2
+        assert ws < 3.1 * w.rows * w.d_model * 2 + w.rows * 8 + weights
     w = synth.WORKLOADS["long_128k"]
     assert bpt.layer_workspace_bytes(bpt.desc_for(w)) < w.seq_len * w.seq_len * 2
 
