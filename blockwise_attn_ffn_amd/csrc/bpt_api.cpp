@@ -35,24 +35,25 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int ldv_of(int seq_len) { return (seq_len + 7) / 8 * 8; }
+size_t rows_pad_of(const bpt_layer_desc_t* d) { return round_up((size_t)d->batch * d->seq_len, 256); }
 
 // Layout of the layer workspace, plus the stack's fp32 residual buffer.
 bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   bpt::WorkspaceLayout L{};
   const size_t rows = (size_t)d->batch * d->seq_len;
   const size_t es = esize(d->dtype);
+  const size_t dm = d->d_model, df = d->d_ff;
   size_t off = 0;
-  L.stats_off = off;
-  off = round_up(off + rows * 8, kAlign);
+  L.xpack_off = off;
+  off = round_up(off + rows_pad_of(d) * dm * es, kAlign);
   L.q_off = off;
   off = round_up(off + rows * d->d_model * es, kAlign);
   L.k_off = off;
   off = round_up(off + rows * d->d_model * es, kAlign);
   L.vt_off = off;
   off = round_up(off + (size_t)d->batch * d->d_model * ldv_of(d->seq_len) * es, kAlign);
-  L.wpack_off = off;  // W_O, W_1, W_2 back to back, fragment order
-  off = round_up(off + ((size_t)d->d_model * d->d_model + 2 * (size_t)d->d_ff * d->d_model) * es,
-                 kAlign);
+  L.wpack_off = off;  // W_Q, W_K, W_V, W_O, W_1, W_2 back to back, fragment order
+  off = round_up(off + (4 * dm * dm + 2 * df * dm) * es, kAlign);
   L.resid_off = off;
   if (stack_resid) off = round_up(off + rows * d->d_model * 4, kAlign);
   L.total = off;
@@ -137,7 +138,8 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   p.compute_f32 = d->dtype == BPT_F32;
   p.ldv = ldv_of(d->seq_len);
   char* base = static_cast<char*>(ws);
-  p.stats = base + L.stats_off;
+  p.rows_pad = (int)rows_pad_of(d);
+  p.xpack = base + L.xpack_off;
   p.q = base + L.q_off;
   p.k = base + L.k_off;
   p.vt = base + L.vt_off;

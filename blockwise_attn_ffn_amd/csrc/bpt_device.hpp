@@ -134,6 +134,58 @@ __device__ inline typename Op<T>::frag ld_frag(const T* p) {
   return *reinterpret_cast<const typename Op<T>::frag*>(p);
 }
 
+// ---------------------------------------------------------------------------
+// Packed fragments. A matrix-core operand fragment (a 32-row tile x one 16-wide
+// k-step, 8 values per lane) stored as PCS = sizeof(T)/2 pieces of 64 lanes x
+// 16 bytes: element e of lane l sits at piece e / EPP, position l * EPP + e % EPP
+// (EPP = 16 / sizeof(T) elements per piece). One piece is 1 KB of contiguous
+// memory, so a 64-lane load of it touches 8 whole cache lines.
+// ---------------------------------------------------------------------------
+constexpr int kFragElems = 512;
+
+template <typename T>
+__device__ __host__ constexpr int frag_pieces() { return (int)sizeof(T) / 2; }
+
+template <typename T>
+__device__ __host__ constexpr int packed_index(int lane, int e) {
+  return (e / (16 / (int)sizeof(T))) * 64 * (16 / (int)sizeof(T)) + lane * (16 / (int)sizeof(T)) +
+         e % (16 / (int)sizeof(T));
+}
+
+// Load lane's fragment from a packed fragment at p (global or LDS).
+__device__ inline bf16x8 ld_packed(const bf16* p, int lane) {
+  return *reinterpret_cast<const bf16x8*>(p + lane * 8);
+}
+__device__ inline f32x8 ld_packed(const float* p, int lane) {
+  const float4 a = *reinterpret_cast<const float4*>(p + lane * 4);
+  const float4 b = *reinterpret_cast<const float4*>(p + 256 + lane * 4);
+  return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+// Store 8 values of lane's slot in a packed fragment at p.
+__device__ inline void st_packed(bf16* p, int lane, const float* v) { store8_f32(p + lane * 8, v); }
+__device__ inline void st_packed(float* p, int lane, const float* v) {
+  *reinterpret_cast<float4*>(p + lane * 4) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 256 + lane * 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ inline void st_packed_chunk(bf16* p, int lane, const Chunk<bf16>::type& c) {
+  st_chunk(p + lane * 8, c);
+}
+__device__ inline void st_packed_chunk(float* p, int lane, const Chunk<float>::type& c) {
+  *reinterpret_cast<uint4*>(p + lane * 4) = c.a;
+  *reinterpret_cast<uint4*>(p + 256 + lane * 4) = c.b;
+}
+
+// LDS pointer for the direct global -> LDS copy instruction.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Copy 16 bytes per lane from global memory (per-lane address src) into LDS at
+// dst + 16 * lane (dst wave-uniform). Completion is tracked by the vector memory
+// counter of the issuing wave.
+__device__ inline void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+}
+// Wait until all of this wave's vector-memory operations (including LDS copies) are done.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ inline float bf16_round(float x) { return (float)(bf16)x; }
 
 // exp2 on the hardware transcendental unit (v_exp_f32).

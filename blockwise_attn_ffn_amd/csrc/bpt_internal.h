@@ -25,18 +25,19 @@ struct LayerLaunch {
   bpt_layer_weights_t w;
   void* z;
   // workspace carve-up
-  void* stats;       // [rows] float2 (mean, rstd) of LN1
+  int rows_pad;      // rows rounded up to a multiple of 256
+  void* xpack;       // LN1(X) as packed matrix-core B fragments, [rows_pad, d]
   void* q;           // [rows, d] Q, then the attention output O (in place)
   void* k;           // [rows, d]
   void* vt;          // [batch, heads, d_head, ldv]
-  void* wpack;       // W_O | W_1 | W_2 repacked in matrix-core fragment order
+  void* wpack;       // W_Q | W_K | W_V | W_O | W_1 | W_2 in packed fragment order
   // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
   void* const* events;
 };
 
 // Element counts/byte sizes of the workspace pieces (shared by sizing and carving).
 struct WorkspaceLayout {
-  size_t stats_off, q_off, k_off, vt_off, wpack_off, resid_off, total;
+  size_t xpack_off, q_off, k_off, vt_off, wpack_off, resid_off, total;
 };
 
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).

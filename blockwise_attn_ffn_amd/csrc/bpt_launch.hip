@@ -1,7 +1,7 @@
-// The per-layer launch sequence on one stream: LN1 statistics, LN1 + QKV
-// projection, attention, then the epilogue's weights repacked into matrix-core
-// fragment order and the fused FFN epilogue. Optional events between kernels
-// are for measurement only.
+// The per-layer launch sequence on one stream: the six weight matrices repacked
+// into matrix-core fragment order, LN1 into the packed activation operand, the
+// QKV projection, attention, and the fused FFN epilogue. Optional events
+// between the stages are for measurement only.
 #include "bpt_launch.hpp"
 
 namespace bpt {
@@ -20,10 +20,10 @@ int mark(const LayerLaunch& L, int i, hipStream_t s, char* err, size_t n) {
 
 int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t n) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return mark(L, 0, s, err, n) || launch_ln_qkv(L, s, err, n, 0) || mark(L, 1, s, err, n) ||
-         launch_ln_qkv(L, s, err, n, 1) || mark(L, 2, s, err, n) ||
-         launch_attention(L, s, err, n) || mark(L, 3, s, err, n) || launch_pack(L, s, err, n) ||
-         launch_ffn(L, s, err, n) || mark(L, 4, s, err, n);
+  return mark(L, 0, s, err, n) || launch_pack(L, s, err, n) || launch_ln_qkv(L, s, err, n, 0) ||
+         mark(L, 1, s, err, n) || launch_ln_qkv(L, s, err, n, 1) || mark(L, 2, s, err, n) ||
+         launch_attention(L, s, err, n) || mark(L, 3, s, err, n) || launch_ffn(L, s, err, n) ||
+         mark(L, 4, s, err, n);
 }
 
 }  // namespace bpt

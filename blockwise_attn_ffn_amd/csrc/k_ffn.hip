@@ -106,9 +106,9 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
         frag = W2_FRAG + (wave * NT + a) * (dff / 16) + c * (HC / 16) + kb * 4;
       }
     }
-    const T* base = wp + (size_t)frag * FRAG + lane * 8;
+    const T* base = wp + (size_t)frag * FRAG;
 #pragma unroll
-    for (int j = 0; j < SA; ++j) dst[j] = ld_frag(base + j * FRAG);
+    for (int j = 0; j < SA; ++j) dst[j] = ld_packed(base + j * FRAG, lane);
   };
 
   F ring[P][SA];
@@ -307,7 +307,8 @@ int run_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   auto k = ffn_epilogue_kernel<TX, T, TO, D, BM, HC, P>;
   if (set_smem(k, smem, err, n)) return 1;
   hipLaunchKernelGGL(k, dim3((rows + BM - 1) / BM), dim3(256), smem, s, (const TX*)L.x,
-                     (const T*)L.q, (const T*)L.wpack, (const T*)L.w.ln2_g, (const T*)L.w.ln2_b,
+                     (const T*)L.q, (const T*)L.wpack + 3 * (size_t)L.d_model * L.d_model,
+                     (const T*)L.w.ln2_g, (const T*)L.w.ln2_b,
                      (TO*)L.z, rows, L.d_ff, L.ln_eps);
   return check_launch("ffn_epilogue", err, n);
 }

@@ -6,10 +6,11 @@
 // from W, one 64-lane load touches 32 rows, i.e. 32 cache lines per instruction,
 // and the vector-memory path is bound by lines, not bytes. The packed copy puts
 // each (row tile, k-step) fragment in 64 consecutive 8-element chunks in lane
-// order, so one load instruction reads contiguous memory.
+// order (bpt_device.hpp: packed fragments), so one load instruction reads
+// contiguous memory:
 //
-//   packed[((tile * (K / 16) + ks) * 64 + 32 * hf + rho) * 8 + e]
-//       = W[32 * tile + pi(rho)][16 * ks + 8 * hf + e]
+//   fragment (tile, ks) = packed + (tile * (K / 16) + ks) * 512, and in it lane
+//   32 * hf + rho holds W[32 * tile + pi(rho)][16 * ks + 8 * hf + e], e = 0..7.
 #include "bpt_device.hpp"
 #include "bpt_launch.hpp"
 
@@ -25,8 +26,8 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const T* __restrict__ W,
   const int row = (int)(i / kc), c = (int)(i - (size_t)row * kc);
   const int tile = row >> 5, rho = pi_row(row & 31);      // pi is its own inverse
   const int ks = c >> 1, hf = c & 1;
-  const size_t dst = (((size_t)tile * (K / 16) + ks) * 64 + 32 * hf + rho) * 8;
-  st_chunk(P + dst, ld_chunk(W + (size_t)row * K + (size_t)c * 8));
+  T* frag = P + ((size_t)tile * (K / 16) + ks) * kFragElems;
+  st_packed_chunk(frag, 32 * hf + rho, ld_chunk(W + (size_t)row * K + (size_t)c * 8));
 }
 
 namespace {
@@ -39,14 +40,18 @@ int run_pack(const void* W, void* P, int n_rows, int K, hipStream_t s, char* err
 }
 }  // namespace
 
-// W_O at element 0 of the packed region, W_1 at d*d, W_2 at d*d + d_ff*d.
+// Packed region: W_Q, W_K, W_V (one [3d, d] operand), then W_O, W_1, W_2.
 template <typename T>
 int pack_all(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int d = L.d_model, f = L.d_ff;
+  const size_t dd = (size_t)d * d;
   T* p = static_cast<T*>(L.wpack);
-  return run_pack<T>(L.w.w_o, p, d, d, s, err, n) ||
-         run_pack<T>(L.w.w_1, p + (size_t)d * d, f, d, s, err, n) ||
-         run_pack<T>(L.w.w_2, p + (size_t)d * d + (size_t)f * d, d, f, s, err, n);
+  return run_pack<T>(L.w.w_q, p, d, d, s, err, n) ||
+         run_pack<T>(L.w.w_k, p + dd, d, d, s, err, n) ||
+         run_pack<T>(L.w.w_v, p + 2 * dd, d, d, s, err, n) ||
+         run_pack<T>(L.w.w_o, p + 3 * dd, d, d, s, err, n) ||
+         run_pack<T>(L.w.w_1, p + 4 * dd, f, d, s, err, n) ||
+         run_pack<T>(L.w.w_2, p + 4 * dd + (size_t)f * d, d, f, s, err, n);
 }
 
 int launch_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {

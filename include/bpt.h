@@ -95,11 +95,12 @@ typedef struct {
  * sizes gets a shorter last block. */
 
 /* Bytes of workspace bpt_layer_fwd needs for *desc (0 for an empty call), or 0
- * with bpt_last_error() set when desc is invalid. Holds LN statistics
- * [rows, 2] fp32; Q (reused for the attention output), K and V^T, each
- * [rows, d_model] in the compute type; and a copy of W_O, W_1, W_2 repacked
- * in matrix-core fragment order (d_model^2 + 2 d_model d_ff elements). Nothing
- * of size rows x d_ff or seq_len x seq_len is ever part of it. */
+ * with bpt_last_error() set when desc is invalid. Holds, in the compute type:
+ * LN1(X) [rows rounded up to 256, d_model]; Q (reused for the attention
+ * output), K and V^T, each [rows, d_model]; and a copy of the six projection
+ * matrices repacked in matrix-core fragment order (4 d_model^2 + 2 d_model d_ff
+ * elements). Nothing of size rows x d_ff or seq_len x seq_len is ever part of
+ * it. */
 size_t bpt_layer_workspace_bytes(const bpt_layer_desc_t* desc);
 
 /* Workspace of bpt_stack_fwd: the layer workspace, plus one fp32 residual

@@ -47,7 +47,7 @@ int main() {
   EXPECT(bpt_layer_fwd(&d, fake(0), &w[0], fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_OK);
   EXPECT(bpt::g_launches == 1);
   EXPECT(bpt::g_last[0].ldv == 200 && bpt::g_last[0].d_head == 64);
-  EXPECT(bpt::g_last[0].stats == fake(2ull << 36));
+  EXPECT(bpt::g_last[0].xpack == fake(2ull << 36) && bpt::g_last[0].rows_pad == 512);
   EXPECT((char*)bpt::g_last[0].vt > (char*)bpt::g_last[0].k && (char*)bpt::g_last[0].k > (char*)bpt::g_last[0].q);
   // a 3-layer stack with a bf16 Z uses the workspace residual buffer between layers
   const size_t need3 = bpt_stack_workspace_bytes(&d, 3);
