@@ -195,9 +195,9 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // z = sqrt(2/pi) (u + 0.044715 u^3). exp(-2z) = 2^(-2 z log2 e).
 __device__ inline float gelu_tanh(float u) {
   const float k = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
-  float z = u * (1.0f + 0.044715f * u * u);
-  float e = fast_exp2(k * z);
-  return u / (1.0f + e);
+  const float z = u * (1.0f + 0.044715f * u * u);
+  const float e = fast_exp2(k * z);
+  return u * __builtin_amdgcn_rcpf(1.0f + e);   // e = inf gives rcp = 0 and h = -0
 }
 
 }  // namespace bpt

@@ -90,22 +90,18 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
   // the W_1 and W_2 stages. Branch-free: every stage issues SA loads (stages past
   // the end reload the last one), so the memory-counter waits stay exact.
   auto load_stage = [&](int t, F (&dst)[SA]) {
+    // Branch-free scalar decode of stage t into its first fragment index (4
+    // consecutive k-steps follow); all three candidates are formed and selected.
     t = __builtin_amdgcn_readfirstlane(min(t, n_stages - 1));
-    int frag;  // index of the stage's first fragment; 4 consecutive k-steps follow
-    if (t < N_WO) {
-      const int kb = t / NT, a = t - kb * NT;
-      frag = (wave * NT + a) * (D / 16) + kb * 4;
-    } else {
-      const int u = t - N_WO, c = u / per_chunk;
-      const int s = u - c * per_chunk;
-      if (s < N_W1) {
-        const int kb = s / FT, ft = s - kb * FT;
-        frag = W1_FRAG + (c * (HC / 32) + wave * FT + ft) * (D / 16) + kb * 4;
-      } else {
-        const int s2 = s - N_W1, kb = s2 / NT, a = s2 - kb * NT;
-        frag = W2_FRAG + (wave * NT + a) * (dff / 16) + c * (HC / 16) + kb * 4;
-      }
-    }
+    const int u = max(t - N_WO, 0), c = u / per_chunk;
+    const int s = u - c * per_chunk, s2 = max(s - N_W1, 0);
+    const int kb_o = t / NT, a_o = t - kb_o * NT;
+    const int kb_1 = s / FT, f_1 = s - kb_1 * FT;
+    const int kb_2 = s2 / NT, a_2 = s2 - kb_2 * NT;
+    const int frag_o = (wave * NT + a_o) * (D / 16) + kb_o * 4;
+    const int frag_1 = W1_FRAG + (c * (HC / 32) + wave * FT + f_1) * (D / 16) + kb_1 * 4;
+    const int frag_2 = W2_FRAG + (wave * NT + a_2) * (dff / 16) + c * (HC / 16) + kb_2 * 4;
+    const int frag = t < N_WO ? frag_o : (s < N_W1 ? frag_1 : frag_2);
     const T* base = wp + (size_t)frag * FRAG;
 #pragma unroll
     for (int j = 0; j < SA; ++j) dst[j] = ld_packed(base + j * FRAG, lane);
@@ -153,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
 #pragma unroll
         for (int a = 0; a < TT; ++a) {
           const int p = (ku * TT + a) % P;
-          if (a == 0 && kb + 1 < n_kb) load_b(kb + 1, bq[(ku + 1) & 1]);
+          if (a == 0) load_b(min(kb + 1, n_kb - 1), bq[(ku + 1) & 1]);   // next k-block
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
