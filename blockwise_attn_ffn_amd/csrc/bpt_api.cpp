@@ -34,8 +34,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-int ldv_of(int seq_len) { return (seq_len + 7) / 8 * 8; }
-size_t rows_pad_of(const bpt_layer_desc_t* d) { return round_up((size_t)d->batch * d->seq_len, 256); }
+size_t seq_pad_of(const bpt_layer_desc_t* d) { return round_up((size_t)d->seq_len, 128); }
+size_t rows_pad_of(const bpt_layer_desc_t* d) { return round_up((size_t)d->batch * seq_pad_of(d), 256); }
 
 // Layout of the layer workspace, plus the stack's fp32 residual buffer.
 bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
@@ -43,19 +43,20 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   const size_t rows = (size_t)d->batch * d->seq_len;
   const size_t es = esize(d->dtype);
   const size_t dm = d->d_model, df = d->d_ff;
+  const size_t rp = rows_pad_of(d), used = (size_t)d->batch * seq_pad_of(d);
   size_t off = 0;
-  L.xpack_off = off;
-  off = round_up(off + rows_pad_of(d) * dm * es, kAlign);
-  L.q_off = off;
-  off = round_up(off + rows * d->d_model * es, kAlign);
-  L.k_off = off;
-  off = round_up(off + rows * d->d_model * es, kAlign);
-  L.vt_off = off;
-  off = round_up(off + (size_t)d->batch * d->d_model * ldv_of(d->seq_len) * es, kAlign);
+  L.xpack_off = off;  // LN1(X), packed
+  off = round_up(off + rp * dm * es, kAlign);
+  L.q_off = off;      // Q, then O, packed
+  off = round_up(off + rp * dm * es, kAlign);
+  L.k_off = off;      // K, packed per (sequence, head)
+  off = round_up(off + used * dm * es, kAlign);
+  L.vt_off = off;     // V^T, packed per (sequence, head)
+  off = round_up(off + used * dm * es, kAlign);
   L.wpack_off = off;  // W_Q, W_K, W_V, W_O, W_1, W_2 back to back, fragment order
   off = round_up(off + (4 * dm * dm + 2 * df * dm) * es, kAlign);
   L.resid_off = off;
-  if (stack_resid) off = round_up(off + rows * d->d_model * 4, kAlign);
+  if (stack_resid) off = round_up(off + rows * dm * 4, kAlign);
   L.total = off;
   return L;
 }
@@ -136,7 +137,7 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   p.causal = d->causal;
   p.ln_eps = d->ln_eps;
   p.compute_f32 = d->dtype == BPT_F32;
-  p.ldv = ldv_of(d->seq_len);
+  p.seq_pad = (int)seq_pad_of(d);
   char* base = static_cast<char*>(ws);
   p.rows_pad = (int)rows_pad_of(d);
   p.xpack = base + L.xpack_off;

@@ -19,17 +19,17 @@ struct LayerLaunch {
   int compute_f32;   // 1: fp32 operands everywhere; 0: bf16 operands
   int x_f32;         // element type of X: 1 fp32, 0 bf16 (the weights' type otherwise)
   int z_f32;         // element type of Z
-  int ldv;           // row stride (elements) of V^T: seq_len rounded up to 8
+  int seq_pad;       // seq_len rounded up to 128: rows per sequence in packed row space
   // tensors
   const void* x;
   bpt_layer_weights_t w;
   void* z;
   // workspace carve-up
-  int rows_pad;      // rows rounded up to a multiple of 256
-  void* xpack;       // LN1(X) as packed matrix-core B fragments, [rows_pad, d]
-  void* q;           // [rows, d] Q, then the attention output O (in place)
-  void* k;           // [rows, d]
-  void* vt;          // [batch, heads, d_head, ldv]
+  int rows_pad;      // batch * seq_pad rounded up to a multiple of 256
+  void* xpack;       // LN1(X) as packed B fragments over [rows_pad, d]
+  void* q;           // Q as packed B fragments over [rows_pad, d], then O in place
+  void* k;           // K: per (sequence, head) packed A fragments [seq_pad keys, d_head]
+  void* vt;          // V^T: per (sequence, head) packed A fragments [d_head, seq_pad keys]
   void* wpack;       // W_Q | W_K | W_V | W_O | W_1 | W_2 in packed fragment order
   // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
   void* const* events;

@@ -23,64 +23,57 @@
 
 namespace bpt {
 
-// LDS layout of the [BM, K] operand tiles (LN2(Y) / the O tile with K = D, the
-// hidden chunk with K = HC): k-block major. A k-block holds 64 consecutive k of
-// all BM rows, one 8 * CB-byte row segment per row (CB = bytes of 8 elements);
-// inside a segment the 8-element chunk c sits at slot c ^ swz(row). A lane then
-// needs one offset per k-step of a block; blocks and row tiles are immediates.
-template <typename T, int BM>
-struct KBlockLayout {
-  static constexpr int CB = 8 * (int)sizeof(T);
-  static constexpr int RB = 8 * CB;        // bytes per row segment
-  static constexpr int KBB = BM * RB;      // bytes per k-block
-  __device__ static int off(int row, int chunk) {   // chunk = k / 8
-    return (chunk >> 3) * KBB + row * RB + (((chunk & 7) ^ swz(row)) * CB);
-  }
-};
+// LDS holds the [BM, K] activation operands (the O tile, then LN2(Y), with
+// K = d; the hidden chunk with K = HC) as packed matrix-core B fragments:
+// fragment (row tile b, k-step ks) at (b * K / 16 + ks) * 512 elements, 64 lanes x
+// 8 consecutive elements in lane order. A lane reads a fragment with one base
+// register plus an immediate offset, and 64 lanes read 1 KB contiguously.
 
 template <typename TX, typename T, typename TO, int D, int BM, int HC, int P>
 __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
-    const TX* X, const T* __restrict__ Oin, const T* __restrict__ wp,
-    const T* __restrict__ ln_g, const T* __restrict__ ln_b, TO* Z, int R, int dff, float eps) {
+    const TX* X, const T* __restrict__ Opk, const T* __restrict__ wp,
+    const T* __restrict__ ln_g, const T* __restrict__ ln_b, TO* Z, int N, int Np, int dff,
+    float eps) {
+  // X, Z: [batch * N, d] real rows. Opk: the attention output as packed B fragments
+  // over [packed rows, d] (sequence b at packed rows [b Np, b Np + N)). A tile of
+  // BM packed rows lies inside one sequence (BM divides Np).
   // wp: W_O | W_1 | W_2 in matrix-core fragment order (k_pack.hip): fragment
   // (row tile, k-step) = 64 lanes x 8 consecutive elements.
   using O = Op<T>;
   using F = typename O::frag;
-  using LY = KBlockLayout<T, BM>;
   constexpr int NCW = D / 4;             // features per wave
   constexpr int NT = NCW / 32;           // 32-feature tiles per wave
   constexpr int RT = BM / 32;            // 32-row tiles
   constexpr int FT = HC / 4 / 32;        // hidden tiles per wave per chunk
   constexpr int KBO = D / 64;            // k-blocks when k runs over d (W_O, W_1)
   constexpr int KB2 = HC / 64;           // k-blocks when k runs over a chunk (W_2)
+  constexpr int PCS = frag_pieces<T>();
+  constexpr int FB = 1024 * PCS;         // bytes per fragment
   constexpr int SA = 4;                  // stage = one 32-row weight tile x 4 k-steps
   constexpr int N_WO = KBO * NT, N_W1 = KBO * FT, N_W2 = KB2 * NT;
   static_assert(NT >= 1 && RT >= 1 && FT >= 1 && D % 64 == 0 && HC % 64 == 0, "tile");
   static_assert(N_WO % P == 0 && N_W1 % P == 0 && N_W2 % P == 0, "stages per phase vs ring");
   static_assert(P == 2 || P == 4, "ring depth");
   static_assert(KBO % 4 == 0 || P == 2, "k-blocks vs unroll");
-  static_assert(8 * BM * 4 + 2 * D * (int)sizeof(T) <= KB2 * KBlockLayout<T, BM>::KBB,
+  static_assert(8 * BM * 4 + 2 * D * (int)sizeof(T) <= BM * HC * (int)sizeof(T),
                 "LN2 scratch must fit in the hidden-chunk buffer");
+  static_assert((RT * (D / 16) * PCS) % 4 == 0, "O-tile copies per wave");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  unsigned char* ys = smem_raw;                 // [KBO k-blocks]: O tile, then LN2(Y)
-  unsigned char* hs = smem_raw + KBO * LY::KBB; // [KB2 k-blocks]: hidden chunk
+  T* ys = reinterpret_cast<T*>(smem_raw);       // [RT][D/16] fragments: O tile, then LN2(Y)
+  T* hs = ys + BM * D;                          // [RT][HC/16] fragments: hidden chunk
   float* red = reinterpret_cast<float*>(hs);    // [2][4][BM] row partial sums
   T* gb = reinterpret_cast<T*>(red + 8 * BM);   // [2][D] LN2 gain and bias (as given)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int rho = lane & 31, hf = lane >> 5;
-  const int r0 = blockIdx.x * BM;
+  const int r0 = blockIdx.x * BM;              // first packed row of the tile
+  const int seq = r0 / Np, pos0 = r0 - seq * Np;
   const int n0w = wave * NCW;
   const int n_chunks = dff / HC;
   const int per_chunk = N_W1 + N_W2;
   const int n_stages = N_WO + n_chunks * per_chunk;
-
-  // B-fragment byte offsets of this lane inside a k-block, one per k-step
-  int boff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) boff[j] = rho * LY::RB + (((2 * j + hf) ^ swz(rho)) * LY::CB);
 
   constexpr int FRAG = 64 * 8;                  // elements per packed fragment
   constexpr int W1_FRAG = D * D / FRAG;         // first W_1 fragment
@@ -107,39 +100,44 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
     for (int j = 0; j < SA; ++j) dst[j] = ld_packed(base + j * FRAG, lane);
   };
 
+  // ---- the attention-output tile: RT row tiles x D/16 fragments, contiguous per
+  //      row tile in Opk, copied global -> LDS by the LDS-DMA path
+  {
+    constexpr int NC = RT * (D / 16) * PCS, CPW = NC / 4;
+    const T* src0 = Opk + (size_t)(r0 >> 5) * (D / 16) * kFragElems;
+#pragma unroll 4
+    for (int q = 0; q < CPW; ++q) {
+      const int idx = wave * CPW + q;       // = (row tile * D/16 + k-step) * PCS + piece
+      dma16(src0 + (size_t)idx * (kFragElems / PCS) + lane * (8 / PCS),
+            reinterpret_cast<unsigned char*>(ys) + idx * 1024);
+    }
+  }
   F ring[P][SA];
   int t_next = 0;
 #pragma unroll
   for (int p = 0; p < P; ++p) load_stage(t_next++, ring[p]);
-
-  // ---- stage the attention-output tile O[r0 : r0 + BM, :] and LN2's gain/bias.
-  //      Rows past the end are clamped; their results are never stored.
-  for (int c = tid; c < BM * (D / 8); c += 256) {
-    const int row = c / (D / 8), cc = c - row * (D / 8);
-    const int r = min(r0 + row, R - 1);
-    st_chunk(reinterpret_cast<T*>(ys + LY::off(row, cc)), ld_chunk(Oin + (size_t)r * D + cc * 8));
-  }
   for (int c = tid; c < D / 8; c += 256) {
     st_chunk(gb + 8 * c, ld_chunk(ln_g + 8 * c));
     st_chunk(gb + D + 8 * c, ld_chunk(ln_b + 8 * c));
   }
+  wait_vmem();
   __syncthreads();
 
   // One GEMM phase: accs[tile][r] += A(ring stages) * B(LDS k-blocks of src).
   // Stages run k-block major; B fragments of the next k-block are read at the
   // first stage of the current one.
-  auto gemm_phase = [&](const unsigned char* src, int n_kb, auto& accs, auto tiles_c) {
+  auto gemm_phase = [&](const T* src, int n_kb, auto& accs, auto tiles_c) {
     constexpr int TT = decltype(tiles_c)::value;
     // k-blocks unrolled together: even (B double buffer) and a multiple of the ring
     constexpr int U = ((2 * TT) % P == 0) ? 2 : 4;
     F bq[2][4][RT];
+    const int ks_tot = n_kb * 4;        // k-steps per row tile of src
     auto load_b = [&](int kb, F (&dst)[4][RT]) {
-      const unsigned char* blk = src + kb * LY::KBB;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int b = 0; b < RT; ++b)
-          dst[j][b] = *reinterpret_cast<const F*>(blk + b * 32 * LY::RB + boff[j]);
+          dst[j][b] = ld_packed(src + (size_t)(b * ks_tot + kb * 4 + j) * kFragElems, lane);
     };
     load_b(0, bq[0]);
     for (int kb0 = 0; kb0 < n_kb; kb0 += U) {
@@ -168,12 +166,13 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
     for (int b = 0; b < RT; ++b) acc[a][b] = f32x16{};
   gemm_phase(ys, KBO, acc, std::integral_constant<int, NT>{});
 
-  // ---- + X (residual) and LN2 statistics (biased variance, two passes)
+  // ---- + X (residual) and LN2 statistics (biased variance, two passes). Padding
+  //      rows read a clamped real row; their results are never stored.
   float psum[RT];
 #pragma unroll
   for (int b = 0; b < RT; ++b) {
-    const int r = min(r0 + b * 32 + rho, R - 1);
-    const TX* xr = X + (size_t)r * D + n0w + 8 * hf;
+    const int pos = min(pos0 + b * 32 + rho, N - 1);
+    const TX* xr = X + ((size_t)seq * N + pos) * D + n0w + 8 * hf;
     float s = 0.f;
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
@@ -238,7 +237,8 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (acc[a][b][8 * g + e] - mean[b]) * rstd[b] * gv[e] + bv[e];
-        *reinterpret_cast<F*>(ys + LY::off(row, n >> 3)) = O::from_f32(v);
+        (void)row;
+        st_packed(ys + (size_t)(b * (D / 16) + (n >> 4)) * kFragElems, lane, v);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -266,7 +266,8 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
           float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gelu_tanh(u[ft][b][8 * g + e]);
-          *reinterpret_cast<F*>(hs + LY::off(row, fl >> 3)) = O::from_f32(v);
+          (void)row;
+          st_packed(hs + (size_t)(b * (HC / 16) + (fl >> 4)) * kFragElems, lane, v);
         }
       }
     }
@@ -276,11 +277,12 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
     __syncthreads();
   }
 
-  // ---- Z = Y + H W_2
+  // ---- Z = Y + H W_2 (real rows only)
 #pragma unroll
   for (int b = 0; b < RT; ++b) {
-    const int r = r0 + b * 32 + rho;
-    if (r >= R) continue;
+    const int pos = pos0 + b * 32 + rho;
+    if (pos >= N) continue;
+    const size_t r = (size_t)seq * N + pos;
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
 #pragma unroll
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = acc[a][b][8 * g + e];
-        store8_f32(Z + (size_t)r * D + n0w + a * 32 + 16 * g + 8 * hf, v);
+        store8_f32(Z + r * D + n0w + a * 32 + 16 * g + 8 * hf, v);
       }
     }
   }
@@ -298,14 +300,16 @@ namespace {
 
 template <typename TX, typename T, typename TO, int D, int BM, int HC, int P>
 int run_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
-  const int rows = L.batch * L.seq_len;
   const size_t smem = (size_t)BM * (D + HC) * sizeof(T);
   auto k = ffn_epilogue_kernel<TX, T, TO, D, BM, HC, P>;
   if (set_smem(k, smem, err, n)) return 1;
-  hipLaunchKernelGGL(k, dim3((rows + BM - 1) / BM), dim3(256), smem, s, (const TX*)L.x,
+  // tiles of packed rows; tiles made only of padding rows are skipped by the grid
+  const int tiles_per_seq = (L.seq_len + BM - 1) / BM;
+  (void)tiles_per_seq;
+  hipLaunchKernelGGL(k, dim3(L.batch * L.seq_pad / BM), dim3(256), smem, s, (const TX*)L.x,
                      (const T*)L.q, (const T*)L.wpack + 3 * (size_t)L.d_model * L.d_model,
-                     (const T*)L.w.ln2_g, (const T*)L.w.ln2_b,
-                     (TO*)L.z, rows, L.d_ff, L.ln_eps);
+                     (const T*)L.w.ln2_g, (const T*)L.w.ln2_b, (TO*)L.z, L.seq_len, L.seq_pad,
+                     L.d_ff, L.ln_eps);
   return check_launch("ffn_epilogue", err, n);
 }
 

@@ -5,6 +5,8 @@
 // K and V are projected once for all rows instead of once per inner-loop visit;
 // the values are the same.
 //
+// Rows are handled in "packed row" space: sequence b occupies packed rows
+// [b Np, b Np + N) with Np = N rounded up to 128; the padding rows are zero.
 // ln_pack: per row, LN1 statistics (mean, biased variance, two passes over the
 //   row held in registers) and LN1(x) = (x - mean) / sqrt(var + eps) * g + b,
 //   written once in the compute type as matrix-core B fragments (packed order,
@@ -12,7 +14,8 @@
 // qkv_gemm: C^T[3d, rows] = [W_Q W_K W_V] LN1(X)^T with both operands packed;
 //   256 x 256 tiles, operands copied global -> LDS by the LDS-DMA path into two
 //   static LDS stages (no register staging), the next k-tile in flight while the
-//   current one is multiplied.
+//   current one is multiplied. Q, K and V are written as the attention kernel's
+//   packed operands (k_attention.hip).
 #include "bpt_device.hpp"
 #include "bpt_launch.hpp"
 
@@ -31,17 +34,18 @@ template <typename TX, typename T>
 __global__ __launch_bounds__(256) void ln_pack_kernel(const TX* __restrict__ X,
                                                       const T* __restrict__ ln_g,
                                                       const T* __restrict__ ln_b,
-                                                      T* __restrict__ XP, int R, int Rp, int d,
-                                                      float eps) {
+                                                      T* __restrict__ XP, int B, int N, int Np,
+                                                      int Rp, int d, float eps) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
+  const int row = blockIdx.x * 4 + wave;     // packed row
   if (row >= Rp) return;
   const int nch = d >> 3, KS = d >> 4;
   T* tile = XP + (size_t)(row >> 5) * KS * kFragElems;
   const int rho = row & 31;
+  const int bi = row / Np, pos = row - bi * Np;
   float v[8][8];
-  if (row < R) {
-    const TX* xr = X + (size_t)row * d;
+  if (bi < B && pos < N) {
+    const TX* xr = X + ((size_t)bi * N + pos) * d;
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -98,7 +102,10 @@ __global__ __launch_bounds__(256) void ln_pack_kernel(const TX* __restrict__ X,
 template <typename T, int BN, int BM>
 __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(
     const T* __restrict__ WP, const T* __restrict__ XP, T* __restrict__ Qo, T* __restrict__ Ko,
-    T* __restrict__ Vt, int R, int d, int N, int H, int dk, int ldv, int n_tiles_n) {
+    T* __restrict__ Vt, int rows_used, int d, int Np, int H, int dk, int n_tiles_n) {
+  // Qo: B fragments over [packed rows, d]; Ko: per (sequence, head) A fragments
+  // over [Np keys (pi order), d_k]; Vt: per (sequence, head) A fragments over
+  // [d_k (pi order), Np keys].
   using O = Op<T>;
   using F = typename O::frag;
   constexpr int PCS = frag_pieces<T>();
@@ -171,15 +178,16 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(
     compute(lds1);
   }
 
-  // epilogue: lane owns token row r and, per 8-register group, 8 consecutive n
+  // epilogue: lane owns packed row p and, per 8-register group, 8 consecutive n
   const int ng0 = nt * BN;                 // first output feature in [0, 3d)
   const int which = ng0 / d;               // 0 Q, 1 K, 2 V
   const int nc0 = ng0 - which * d;         // first column inside that matrix
+  const int KSD = dk / 16;
 #pragma unroll
   for (int b = 0; b < TR; ++b) {
-    const int r = rt * BM + wr * (BM / 2) + b * 32 + rho;
-    if (r >= R) continue;
-    const int bi = r / N, pos = r - bi * N;
+    const int p = rt * BM + wr * (BM / 2) + b * 32 + rho;
+    if (p >= rows_used) continue;
+    const int bi = p / Np, pos = p - bi * Np;
 #pragma unroll
     for (int a = 0; a < TN; ++a) {
 #pragma unroll
@@ -188,14 +196,23 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = acc[a][b][8 * g + e];
-        if (which < 2) {
-          store8_f32((which == 0 ? Qo : Ko) + (size_t)r * d + n, v);
+        const int head = n / dk, j0 = n - head * dk;
+        const size_t bhh = (size_t)bi * H + head;
+        if (which == 0) {
+          st_packed(Qo + ((size_t)(p >> 5) * KS + (n >> 4)) * kFragElems, 32 * ((n >> 3) & 1) + (p & 31), v);
+        } else if (which == 1) {
+          const size_t frag = (bhh * (Np / 32) + (pos >> 5)) * KSD + (j0 >> 4);
+          st_packed(Ko + frag * kFragElems, 32 * ((j0 >> 3) & 1) + pi_row(pos & 31), v);
         } else {
-          // V^T[seq, head, j, pos]: 8 consecutive j of one head, stride ldv
-          const int head = n / dk, j0 = n - head * dk;
-          T* vp = Vt + ((size_t)(bi * H + head) * dk + j0) * ldv + pos;
+          // 8 consecutive features of one key: 8 rows of the V^T fragments
+          const int lane_hf = 32 * ((pos >> 3) & 1), e_key = pos & 7;
+          T* vbase = Vt + (bhh * (dk / 32) * (size_t)(Np / 16) + (pos >> 4)) * kFragElems;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vp[(size_t)e * ldv] = (T)v[e];
+          for (int e = 0; e < 8; ++e) {
+            const int dd = j0 + e;
+            vbase[(size_t)(dd >> 5) * (Np / 16) * kFragElems +
+                  packed_index<T>(lane_hf + pi_row(dd & 31), e_key)] = (T)v[e];
+          }
         }
       }
     }
@@ -206,21 +223,19 @@ namespace {
 
 template <typename TX, typename T>
 int run_ln_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
-  const int rows = L.batch * L.seq_len;
   hipLaunchKernelGGL((ln_pack_kernel<TX, T>), dim3((L.rows_pad + 3) / 4), dim3(256), 0, s,
-                     (const TX*)L.x, (const T*)L.w.ln1_g, (const T*)L.w.ln1_b, (T*)L.xpack, rows,
-                     L.rows_pad, L.d_model, L.ln_eps);
+                     (const TX*)L.x, (const T*)L.w.ln1_g, (const T*)L.w.ln1_b, (T*)L.xpack, L.batch,
+                     L.seq_len, L.seq_pad, L.rows_pad, L.d_model, L.ln_eps);
   return check_launch("ln_pack", err, n);
 }
 
 template <typename T, int BN, int BM>
 int run_qkv(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
-  const int rows = L.batch * L.seq_len;
   const int ntn = 3 * L.d_model / BN;
   const int ntr = L.rows_pad / BM;
   hipLaunchKernelGGL((qkv_gemm_kernel<T, BN, BM>), dim3(ntn * ntr), dim3(256), 0, s,
-                     (const T*)L.wpack, (const T*)L.xpack, (T*)L.q, (T*)L.k, (T*)L.vt, rows,
-                     L.d_model, L.seq_len, L.n_heads, L.d_head, L.ldv, ntn);
+                     (const T*)L.wpack, (const T*)L.xpack, (T*)L.q, (T*)L.k, (T*)L.vt,
+                     L.batch * L.seq_pad, L.d_model, L.seq_pad, L.n_heads, L.d_head, ntn);
   return check_launch("qkv_gemm", err, n);
 }
 

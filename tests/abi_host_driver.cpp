@@ -46,7 +46,7 @@ int main() {
   // a valid layer call reaches the launcher once, with the carved workspace
   EXPECT(bpt_layer_fwd(&d, fake(0), &w[0], fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_OK);
   EXPECT(bpt::g_launches == 1);
-  EXPECT(bpt::g_last[0].ldv == 200 && bpt::g_last[0].d_head == 64);
+  EXPECT(bpt::g_last[0].seq_pad == 256 && bpt::g_last[0].d_head == 64);
   EXPECT(bpt::g_last[0].xpack == fake(2ull << 36) && bpt::g_last[0].rows_pad == 512);
   EXPECT((char*)bpt::g_last[0].vt > (char*)bpt::g_last[0].k && (char*)bpt::g_last[0].k > (char*)bpt::g_last[0].q);
   // a 3-layer stack with a bf16 Z uses the workspace residual buffer between layers

@@ -54,9 +54,10 @@ def desc(**kw):
 def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None):
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     rows = batch * n
-    ldv = (n + 7) // 8 * 8
+    npad = (n + 127) // 128 * 128
+    used = batch * npad
     f = 4 * d if d_ff is None else d_ff
-    tot = up(up(rows) * d * es) + 2 * up(rows * d * es) + up(batch * d * ldv * es)
+    tot = 2 * up(up(used) * d * es) + 2 * up(used * d * es)
     tot += up((4 * d * d + 2 * d * f) * es)
     if stack_resid:
         tot += up(rows * d * 4)
@@ -87,7 +88,7 @@ def test_workspace_is_block_shaped_not_ffn_shaped():
         weights = (4 * w.d_model * w.d_model + 2 * w.d_model * w.d_ff) * 2
         act = ws - weights
         nd = w.rows * w.d_model * 2
-        assert act <= 4 * nd + 8 * 256 + w.rows * 0 + 256 * w.d_model * 2
+        assert act <= 4 * nd + 8 * 256 + 256 * w.d_model * 2 * 2
         assert act < 2 * w.rows * w.d_ff * 2          # the unfused FFN hidden pair
         assert act < 14 * nd                          # after-Flash, unfused
     w = synth.WORKLOADS["long_128k"]
