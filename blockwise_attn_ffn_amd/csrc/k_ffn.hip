@@ -12,56 +12,62 @@
 // from Y through Z. The [BM, d_ff] hidden state is produced and consumed in
 // chunks of HC units, each chunk living only in registers and LDS.
 //
-// Weight fragments (W_O, W_1, W_2, repacked so that each fragment is one
-// contiguous 64-lane load) stream from L2 into a ring of P register stages that
-// runs continuously across the three phases, so the loads of later stages are in
-// flight while the matrix cores work.
+// The weights arrive as one linear stream per wave (ffn_stream.hpp): W_O, then
+// per chunk W_1[chunk] and W_2[chunk], each stage one 32-row tile x 4 k-steps in
+// matrix-core fragment order. Stages stream from L2 into a ring of P register
+// stages that runs continuously across the phases, so the loads of later stages
+// are in flight while the matrix cores work. The residual X initialises the
+// accumulators, so Y = X + O W_O leaves the matrix cores complete.
 #include <type_traits>
 
 #include "bpt_device.hpp"
 #include "bpt_launch.hpp"
+#include "ffn_stream.hpp"
 
 namespace bpt {
 
 // LDS holds the [BM, K] activation operands (the O tile, then LN2(Y), with
-// K = d; the hidden chunk with K = HC) as packed matrix-core B fragments:
-// fragment (row tile b, k-step ks) at (b * K / 16 + ks) * 512 elements, 64 lanes x
-// 8 consecutive elements in lane order. A lane reads a fragment with one base
-// register plus an immediate offset, and 64 lanes read 1 KB contiguously.
+// K = d; the hidden chunk with K = HC) as packed matrix-core B fragments,
+// row tiles interleaved: fragment (row tile b, k-step ks) at (ks * RT + b) * 512
+// elements, 64 lanes x 8 consecutive elements in lane order. A k-block's
+// fragments are adjacent, so a lane reaches them from one base register with
+// immediate offsets, and 64 lanes read 1 KB contiguously.
 
-template <typename TX, typename T, typename TO, int D, int BM, int HC, int P>
+template <typename TX, typename T, typename TO, int D, int BM, int P>
 __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
-    const TX* X, const T* __restrict__ Opk, const T* __restrict__ wp,
+    const TX* X, const T* __restrict__ Opk, const T* __restrict__ ws,
     const T* __restrict__ ln_g, const T* __restrict__ ln_b, TO* Z, int N, int Np, int dff,
     float eps) {
   // X, Z: [batch * N, d] real rows. Opk: the attention output as packed B fragments
   // over [packed rows, d] (sequence b at packed rows [b Np, b Np + N)). A tile of
   // BM packed rows lies inside one sequence (BM divides Np).
-  // wp: W_O | W_1 | W_2 in matrix-core fragment order (k_pack.hip): fragment
-  // (row tile, k-step) = 64 lanes x 8 consecutive elements.
   using O = Op<T>;
   using F = typename O::frag;
-  constexpr int NCW = D / 4;             // features per wave
-  constexpr int NT = NCW / 32;           // 32-feature tiles per wave
+  constexpr int HC = kFfnChunk;
+  constexpr FfnStream FS{D, 0};
+  constexpr int NCW = D / kFfnWaves;     // features per wave
+  constexpr int NT = FS.nt();            // 32-feature tiles per wave
   constexpr int RT = BM / 32;            // 32-row tiles
-  constexpr int FT = HC / 4 / 32;        // hidden tiles per wave per chunk
+  constexpr int FT = FS.ft();            // hidden tiles per wave per chunk
   constexpr int KBO = D / 64;            // k-blocks when k runs over d (W_O, W_1)
   constexpr int KB2 = HC / 64;           // k-blocks when k runs over a chunk (W_2)
   constexpr int PCS = frag_pieces<T>();
-  constexpr int FB = 1024 * PCS;         // bytes per fragment
-  constexpr int SA = 4;                  // stage = one 32-row weight tile x 4 k-steps
-  constexpr int N_WO = KBO * NT, N_W1 = KBO * FT, N_W2 = KB2 * NT;
-  static_assert(NT >= 1 && RT >= 1 && FT >= 1 && D % 64 == 0 && HC % 64 == 0, "tile");
-  static_assert(N_WO % P == 0 && N_W1 % P == 0 && N_W2 % P == 0, "stages per phase vs ring");
+  constexpr int SA = 4;                  // fragments per stage
+  constexpr int STAGE = SA * kFragElems; // elements per stage
+  // Y/Z tiles that move to ordinary registers while the W_1 accumulators need the
+  // accumulator registers (at most 256 of them per lane).
+  constexpr int ACC_REGS = (NT + FT) * RT * 16;
+  constexpr int PARK = ACC_REGS > 256 ? (ACC_REGS - 256 + 15) / 16 : 0;
+  static_assert(NT >= 1 && RT >= 1 && FT >= 1 && D % 128 == 0, "tile");
   static_assert(P == 2 || P == 4, "ring depth");
-  static_assert(KBO % 4 == 0 || P == 2, "k-blocks vs unroll");
+  static_assert(PARK <= NT * RT, "parked tiles");
   static_assert(8 * BM * 4 + 2 * D * (int)sizeof(T) <= BM * HC * (int)sizeof(T),
                 "LN2 scratch must fit in the hidden-chunk buffer");
-  static_assert((RT * (D / 16) * PCS) % 4 == 0, "O-tile copies per wave");
+  static_assert((RT * (D / 16) * PCS) % kFfnWaves == 0, "O-tile copies per wave");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* ys = reinterpret_cast<T*>(smem_raw);       // [RT][D/16] fragments: O tile, then LN2(Y)
-  T* hs = ys + BM * D;                          // [RT][HC/16] fragments: hidden chunk
+  T* ys = reinterpret_cast<T*>(smem_raw);       // [D/16][RT] fragments: O tile, then LN2(Y)
+  T* hs = ys + BM * D;                          // [HC/16][RT] fragments: hidden chunk
   float* red = reinterpret_cast<float*>(hs);    // [2][4][BM] row partial sums
   T* gb = reinterpret_cast<T*>(red + 8 * BM);   // [2][D] LN2 gain and bias (as given)
 
@@ -72,44 +78,30 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
   const int seq = r0 / Np, pos0 = r0 - seq * Np;
   const int n0w = wave * NCW;
   const int n_chunks = dff / HC;
-  const int per_chunk = N_W1 + N_W2;
-  const int n_stages = N_WO + n_chunks * per_chunk;
+  const int n_stages = FS.n_wo() + n_chunks * FS.per_chunk();
+  const T* stream = ws + (size_t)wave * n_stages * STAGE;
 
-  constexpr int FRAG = 64 * 8;                  // elements per packed fragment
-  constexpr int W1_FRAG = D * D / FRAG;         // first W_1 fragment
-  const int W2_FRAG = W1_FRAG + dff * D / FRAG; // first W_2 fragment
-
-  // Stage t of the weight stream: W_O (k-block major, then tile), then per chunk
-  // the W_1 and W_2 stages. Branch-free: every stage issues SA loads (stages past
-  // the end reload the last one), so the memory-counter waits stay exact.
+  // Stage t of this wave's stream; stages past the end reload the last one, so
+  // every call issues the same SA loads and the memory-counter waits stay exact.
   auto load_stage = [&](int t, F (&dst)[SA]) {
-    // Branch-free scalar decode of stage t into its first fragment index (4
-    // consecutive k-steps follow); all three candidates are formed and selected.
-    t = __builtin_amdgcn_readfirstlane(min(t, n_stages - 1));
-    const int u = max(t - N_WO, 0), c = u / per_chunk;
-    const int s = u - c * per_chunk, s2 = max(s - N_W1, 0);
-    const int kb_o = t / NT, a_o = t - kb_o * NT;
-    const int kb_1 = s / FT, f_1 = s - kb_1 * FT;
-    const int kb_2 = s2 / NT, a_2 = s2 - kb_2 * NT;
-    const int frag_o = (wave * NT + a_o) * (D / 16) + kb_o * 4;
-    const int frag_1 = W1_FRAG + (c * (HC / 32) + wave * FT + f_1) * (D / 16) + kb_1 * 4;
-    const int frag_2 = W2_FRAG + (wave * NT + a_2) * (dff / 16) + c * (HC / 16) + kb_2 * 4;
-    const int frag = t < N_WO ? frag_o : (s < N_W1 ? frag_1 : frag_2);
-    const T* base = wp + (size_t)frag * FRAG;
+    const T* base = stream + (size_t)min(t, n_stages - 1) * STAGE;
 #pragma unroll
-    for (int j = 0; j < SA; ++j) dst[j] = ld_packed(base + j * FRAG, lane);
+    for (int j = 0; j < SA; ++j) dst[j] = ld_packed(base + j * kFragElems, lane);
   };
 
   // ---- the attention-output tile: RT row tiles x D/16 fragments, contiguous per
-  //      row tile in Opk, copied global -> LDS by the LDS-DMA path
+  //      row tile in Opk, copied global -> LDS (row tiles interleaved) by the
+  //      LDS-DMA path, one 1 KB piece per instruction
   {
-    constexpr int NC = RT * (D / 16) * PCS, CPW = NC / 4;
+    constexpr int NC = RT * (D / 16) * PCS, CPW = NC / kFfnWaves;
     const T* src0 = Opk + (size_t)(r0 >> 5) * (D / 16) * kFragElems;
 #pragma unroll 4
     for (int q = 0; q < CPW; ++q) {
       const int idx = wave * CPW + q;       // = (row tile * D/16 + k-step) * PCS + piece
+      const int b = idx / ((D / 16) * PCS), rest = idx - b * ((D / 16) * PCS);
+      const int ks = rest / PCS, piece = rest - ks * PCS;
       dma16(src0 + (size_t)idx * (kFragElems / PCS) + lane * (8 / PCS),
-            reinterpret_cast<unsigned char*>(ys) + idx * 1024);
+            reinterpret_cast<unsigned char*>(ys) + ((ks * RT + b) * PCS + piece) * 1024);
     }
   }
   F ring[P][SA];
@@ -120,87 +112,106 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
     st_chunk(gb + 8 * c, ld_chunk(ln_g + 8 * c));
     st_chunk(gb + D + 8 * c, ld_chunk(ln_b + 8 * c));
   }
-  wait_vmem();
-  __syncthreads();
-
-  // One GEMM phase: accs[tile][r] += A(ring stages) * B(LDS k-blocks of src).
-  // Stages run k-block major; B fragments of the next k-block are read at the
-  // first stage of the current one.
-  auto gemm_phase = [&](const T* src, int n_kb, auto& accs, auto tiles_c) {
-    constexpr int TT = decltype(tiles_c)::value;
-    // k-blocks unrolled together: even (B double buffer) and a multiple of the ring
-    constexpr int U = ((2 * TT) % P == 0) ? 2 : 4;
-    F bq[2][4][RT];
-    const int ks_tot = n_kb * 4;        // k-steps per row tile of src
-    auto load_b = [&](int kb, F (&dst)[4][RT]) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int b = 0; b < RT; ++b)
-          dst[j][b] = ld_packed(src + (size_t)(b * ks_tot + kb * 4 + j) * kFragElems, lane);
-    };
-    load_b(0, bq[0]);
-    for (int kb0 = 0; kb0 < n_kb; kb0 += U) {
-#pragma unroll
-      for (int ku = 0; ku < U; ++ku) {
-        const int kb = kb0 + ku;
-#pragma unroll
-        for (int a = 0; a < TT; ++a) {
-          const int p = (ku * TT + a) % P;
-          if (a == 0) load_b(min(kb + 1, n_kb - 1), bq[(ku + 1) & 1]);   // next k-block
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int b = 0; b < RT; ++b) O::mma(accs[a][b], ring[p][j], bq[ku & 1][j][b]);
-          load_stage(t_next++, ring[p]);
-        }
-      }
-    }
-  };
-
-  // ---- Y^T = W_O O^T
+  // Accumulators start at the residual X (fp32). Register group g of feature tile
+  // a holds features a*32 + 16g + 8hf + [0, 8) of row rho. Padding rows read a
+  // clamped real row; their results are never stored.
   f32x16 acc[NT][RT];
-#pragma unroll
-  for (int a = 0; a < NT; ++a)
-#pragma unroll
-    for (int b = 0; b < RT; ++b) acc[a][b] = f32x16{};
-  gemm_phase(ys, KBO, acc, std::integral_constant<int, NT>{});
-
-  // ---- + X (residual) and LN2 statistics (biased variance, two passes). Padding
-  //      rows read a clamped real row; their results are never stored.
-  float psum[RT];
 #pragma unroll
   for (int b = 0; b < RT; ++b) {
     const int pos = min(pos0 + b * 32 + rho, N - 1);
     const TX* xr = X + ((size_t)seq * N + pos) * D + n0w + 8 * hf;
-    float s = 0.f;
 #pragma unroll
-    for (int a = 0; a < NT; ++a) {
+    for (int a = 0; a < NT; ++a)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         float xv[8];
         load8_f32(xr + a * 32 + 16 * g, xv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          acc[a][b][8 * g + e] += xv[e];
-          s += acc[a][b][8 * g + e];
+        for (int e = 0; e < 8; ++e) acc[a][b][8 * g + e] = xv[e];
+      }
+  }
+  wait_vmem();
+  __syncthreads();
+
+  // One GEMM phase: accs[tile][r] += A(ring stages) * B(LDS k-blocks of src).
+  // Stages run k-block major. The B fragments of a k-block are held in registers
+  // for its TT stages; during the last stage each k-step's fragments are reloaded
+  // in place with the next k-block's as soon as they have been used.
+  auto gemm_phase = [&](const T* src, int n_kb, auto& accs, auto tiles_c) {
+    constexpr int TT = decltype(tiles_c)::value;
+    // k-blocks unrolled together so that the ring slot of every stage is static
+    constexpr int U = (TT % P == 0) ? 1 : ((2 * TT) % P == 0 ? 2 : 4);
+    F bq[4][RT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < RT; ++b) bq[j][b] = ld_packed(src + (size_t)(j * RT + b) * kFragElems, lane);
+    for (int kb0 = 0; kb0 < n_kb; kb0 += U) {
+#pragma unroll
+      for (int ku = 0; ku < U; ++ku) {
+        const T* next = src + (size_t)min(kb0 + ku + 1, n_kb - 1) * (4 * RT * kFragElems);
+#pragma unroll
+        for (int a = 0; a < TT; ++a) {
+          const int p = (ku * TT + a) % P;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int b = 0; b < RT; ++b) O::mma(accs[a][b], ring[p][j], bq[j][b]);
+            if (a == TT - 1) {
+#pragma unroll
+              for (int b = 0; b < RT; ++b)
+                bq[j][b] = ld_packed(next + (size_t)(j * RT + b) * kFragElems, lane);
+              // issue each reload right after its last use: ~6 products of latency
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          load_stage(t_next++, ring[p]);
+          // keep the ring as written: the loads of stage t+P are issued here, P
+          // stages before their use, and not sunk towards it by the scheduler
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // Keep the last PARK Y/Z tiles in ordinary registers across a W_1 phase.
+  auto park = [&]() {
+#pragma unroll
+    for (int q = NT * RT - PARK; q < NT * RT; ++q) asm volatile("" : "+v"(acc[q / RT][q % RT]));
+  };
+  // Pin every Y/Z tile to the accumulator registers (the LN2 arithmetic reads
+  // them through transient copies instead of moving them out).
+  auto pin = [&]() {
+#pragma unroll
+    for (int q = 0; q < NT * RT; ++q) asm volatile("" : "+a"(acc[q / RT][q % RT]));
+  };
+
+  // ---- Y^T = X^T + W_O O^T
+  gemm_phase(ys, KBO, acc, std::integral_constant<int, NT>{});
+  pin();
+
+  // ---- LN2 statistics (biased variance, two passes)
+  float psum[RT];
+#pragma unroll
+  for (int b = 0; b < RT; ++b) {
+    float s = 0.f;
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += acc[a][b][i];
     psum[b] = s + __shfl_xor(s, 32, 64);
   }
-  __syncthreads();  // every wave is done reading the O tile
+  pin();   // each LN2 pass reads the tiles afresh (no long-lived copies)
   if (hf == 0) {
 #pragma unroll
     for (int b = 0; b < RT; ++b) red[wave * BM + b * 32 + rho] = psum[b];
   }
-  __syncthreads();
+  __syncthreads();  // partial sums visible; every wave is done reading the O tile
   float mean[RT], rstd[RT];
 #pragma unroll
   for (int b = 0; b < RT; ++b) {
     const int row = b * 32 + rho;
-    mean[b] = (red[row] + red[BM + row] + red[2 * BM + row] + red[3 * BM + row]) / (float)D;
+    mean[b] = (red[row] + red[BM + row] + red[2 * BM + row] + red[3 * BM + row]) * (1.0f / D);
     float q = 0.f;
 #pragma unroll
     for (int a = 0; a < NT; ++a)
@@ -211,6 +222,7 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
       }
     psum[b] = q + __shfl_xor(q, 32, 64);
   }
+  pin();
   if (hf == 0) {
 #pragma unroll
     for (int b = 0; b < RT; ++b) red[4 * BM + wave * BM + b * 32 + rho] = psum[b];
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
   for (int b = 0; b < RT; ++b) {
     const int row = b * 32 + rho;
     const float q = red[4 * BM + row] + red[5 * BM + row] + red[6 * BM + row] + red[7 * BM + row];
-    rstd[b] = 1.0f / sqrtf(q / (float)D + eps);
+    rstd[b] = 1.0f / sqrtf(q * (1.0f / D) + eps);
   }
   // ---- LN2(Y) -> ys (compute type), 8 consecutive features per store
 #pragma unroll
@@ -233,20 +245,19 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
       load8_f32(gb + D + n, bv);
 #pragma unroll
       for (int b = 0; b < RT; ++b) {
-        const int row = b * 32 + rho;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (acc[a][b][8 * g + e] - mean[b]) * rstd[b] * gv[e] + bv[e];
-        (void)row;
-        st_packed(ys + (size_t)(b * (D / 16) + (n >> 4)) * kFragElems, lane, v);
+        st_packed(ys + (size_t)((n >> 4) * RT + b) * kFragElems, lane, v);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
+  pin();
   __syncthreads();
 
   // ---- FFN over hidden chunks
   for (int c = 0; c < n_chunks; ++c) {
+    park();
     // U^T = W_1[chunk] LN2(Y)^T : this wave's HC/4 hidden units of all BM rows
     f32x16 u[FT][RT];
 #pragma unroll
@@ -262,15 +273,14 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
         const int fl = wave * (HC / 4) + ft * 32 + 16 * g + 8 * hf;   // unit within the chunk
 #pragma unroll
         for (int b = 0; b < RT; ++b) {
-          const int row = b * 32 + rho;
           float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gelu_tanh(u[ft][b][8 * g + e]);
-          (void)row;
-          st_packed(hs + (size_t)(b * (HC / 16) + (fl >> 4)) * kFragElems, lane, v);
+          st_packed(hs + (size_t)((fl >> 4) * RT + b) * kFragElems, lane, v);
         }
       }
     }
+    park();
     __syncthreads();
     // Z^T += W_2[:, chunk] H^T
     gemm_phase(hs, KB2, acc, std::integral_constant<int, NT>{});
@@ -298,14 +308,12 @@ __global__ __launch_bounds__(256, 1) void ffn_epilogue_kernel(
 
 namespace {
 
-template <typename TX, typename T, typename TO, int D, int BM, int HC, int P>
+template <typename TX, typename T, typename TO, int D, int BM, int P>
 int run_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
-  const size_t smem = (size_t)BM * (D + HC) * sizeof(T);
-  auto k = ffn_epilogue_kernel<TX, T, TO, D, BM, HC, P>;
+  const size_t smem = (size_t)BM * (D + kFfnChunk) * sizeof(T);
+  auto k = ffn_epilogue_kernel<TX, T, TO, D, BM, P>;
   if (set_smem(k, smem, err, n)) return 1;
-  // tiles of packed rows; tiles made only of padding rows are skipped by the grid
-  const int tiles_per_seq = (L.seq_len + BM - 1) / BM;
-  (void)tiles_per_seq;
+  // one workgroup per BM packed rows
   hipLaunchKernelGGL(k, dim3(L.batch * L.seq_pad / BM), dim3(256), smem, s, (const TX*)L.x,
                      (const T*)L.q, (const T*)L.wpack + 3 * (size_t)L.d_model * L.d_model,
                      (const T*)L.w.ln2_g, (const T*)L.w.ln2_b, (TO*)L.z, L.seq_len, L.seq_pad,
@@ -317,14 +325,14 @@ template <typename TX, typename T, typename TO>
 int dispatch_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int d = L.d_model;
   if constexpr (sizeof(T) == 4) {
-    if (d == 128) return run_ffn<TX, T, TO, 128, 64, 256, 2>(L, s, err, n);
-    if (d == 256) return run_ffn<TX, T, TO, 256, 32, 256, 2>(L, s, err, n);
+    if (d == 128) return run_ffn<TX, T, TO, 128, 64, 2>(L, s, err, n);
+    if (d == 256) return run_ffn<TX, T, TO, 256, 32, 2>(L, s, err, n);
   } else {
-    if (d == 256) return run_ffn<TX, T, TO, 256, 64, 256, 4>(L, s, err, n);
-    if (d == 512) return run_ffn<TX, T, TO, 512, 64, 256, 4>(L, s, err, n);
-    if (d == 768) return run_ffn<TX, T, TO, 768, 64, 256, 4>(L, s, err, n);
-    if (d == 1024) return run_ffn<TX, T, TO, 1024, 64, 256, 4>(L, s, err, n);
-    if (d == 2048) return run_ffn<TX, T, TO, 2048, 32, 256, 4>(L, s, err, n);
+    if (d == 256) return run_ffn<TX, T, TO, 256, 64, 4>(L, s, err, n);
+    if (d == 512) return run_ffn<TX, T, TO, 512, 64, 4>(L, s, err, n);
+    if (d == 768) return run_ffn<TX, T, TO, 768, 64, 4>(L, s, err, n);
+    if (d == 1024) return run_ffn<TX, T, TO, 1024, 64, 4>(L, s, err, n);
+    if (d == 2048) return run_ffn<TX, T, TO, 2048, 32, 4>(L, s, err, n);
   }
   set_err(err, n, "no epilogue kernel for d_model %s%d", "", d);
   return 1;
