@@ -16,6 +16,8 @@
 //   static LDS stages (no register staging), the next k-tile in flight while the
 //   current one is multiplied. Q, K and V are written as the attention kernel's
 //   packed operands (k_attention.hip).
+#include <type_traits>
+
 #include "bpt_device.hpp"
 #include "bpt_launch.hpp"
 
@@ -28,69 +30,83 @@ __device__ inline float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// LN1 into packed B fragments: one wave per row; rows in [R, Rp) are zero.
+// LN1 into packed B fragments, rows fed through pi: slot s of a fragment holds
+// packed row pi(s % 32) of its 32-row tile (so that the QKV product can emit the
+// V^T operand directly, see below). One workgroup per 32-row tile: the four
+// waves first compute the row statistics (8 rows each, rows read coalesced),
+// then write the tile's fragments one 1 KB fragment per wave instruction.
+// Rows of a sequence's padding and rows in [R, Rp) are zero.
 // ---------------------------------------------------------------------------
-template <typename TX, typename T>
+template <typename TX, typename T, int CPL>
 __global__ __launch_bounds__(256) void ln_pack_kernel(const TX* __restrict__ X,
                                                       const T* __restrict__ ln_g,
                                                       const T* __restrict__ ln_b,
                                                       T* __restrict__ XP, int B, int N, int Np,
-                                                      int Rp, int d, float eps) {
+                                                      int d, float eps) {
+  // CPL: 8-element chunks per lane per row (d <= 512 CPL)
+  __shared__ float2 stats[32];           // (mean, rstd); rstd = 0 marks a zero row
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;     // packed row
-  if (row >= Rp) return;
+  const int tile = blockIdx.x;
   const int nch = d >> 3, KS = d >> 4;
-  T* tile = XP + (size_t)(row >> 5) * KS * kFragElems;
-  const int rho = row & 31;
-  const int bi = row / Np, pos = row - bi * Np;
-  float v[8][8];
-  if (bi < B && pos < N) {
-    const TX* xr = X + ((size_t)bi * N + pos) * d;
-    float s = 0.f;
+#pragma unroll 2
+  for (int i = 0; i < 8; ++i) {
+    const int r = wave + 4 * i, row = tile * 32 + r;
+    const int bi = row / Np, pos = row - bi * Np;
+    float mean = 0.f, rstd = 0.f;
+    if (bi < B && pos < N) {
+      const TX* xr = X + ((size_t)bi * N + pos) * d;
+      float v[CPL][8];
+      float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nch) {
-        load8_f32(xr + 8 * c, v[j]);
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nch) {
+          load8_f32(xr + 8 * c, v[j]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += v[j][e];
-      }
-    }
-    const float mean = wave_sum(s) / (float)d;
-    float q = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nch) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float t = v[j][e] - mean;
-          q += t * t;
+          for (int e = 0; e < 8; ++e) sum += v[j][e];
         }
       }
-    }
-    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+      mean = wave_sum(sum) / (float)d;
+      float q = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nch) {
-        float g[8], b[8];
-        load8_f32(ln_g + 8 * c, g);
-        load8_f32(ln_b + 8 * c, b);
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nch) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[j][e] = (v[j][e] - mean) * rstd * g[e] + b[e];
+          for (int e = 0; e < 8; ++e) {
+            const float t = v[j][e] - mean;
+            q += t * t;
+          }
+        }
       }
+      rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+    if (lane == 0) stats[r] = make_float2(mean, rstd);
   }
+  __syncthreads();
+  // fragment ks: lane (hf, s) holds row pi(s) and k = 16 ks + 8 hf + [0, 8)
+  const int rr = pi_row(lane & 31), hf = lane >> 5;
+  const int row = tile * 32 + rr;
+  const int bi = row / Np, pos = row - bi * Np;
+  const float2 st = stats[rr];
+  const bool live = st.y != 0.f;
+  const TX* xr = X + ((size_t)bi * N + min(pos, N - 1)) * d;
+  T* out = XP + (size_t)tile * KS * kFragElems;
+  for (int ks = wave; ks < KS; ks += 4) {
+    const int k0 = 16 * ks + 8 * hf;
+    float v[8];
+    if (live) {
+      float x[8], g[8], b[8];
+      load8_f32(xr + k0, x);
+      load8_f32(ln_g + k0, g);
+      load8_f32(ln_b + k0, b);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = lane + 64 * j;
-    if (c < nch) st_packed(tile + (size_t)(c >> 1) * kFragElems, 32 * (c & 1) + rho, v[j]);
+      for (int e = 0; e < 8; ++e) v[e] = (x[e] - st.x) * st.y * g[e] + b[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    st_packed(out + (size_t)ks * kFragElems, lane, v);
   }
 }
 
@@ -123,7 +139,19 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rho = lane & 31, hf = lane >> 5;
   const int wn = wave >> 1, wr = wave & 1;
-  const int nt = blockIdx.x % n_tiles_n, rt = blockIdx.x / n_tiles_n;
+  // Tile order: dispatch is round-robin over the 8 XCDs, so consecutive workgroup
+  // ids are renumbered to give each XCD a contiguous range of tiles, and inside
+  // that range tiles run in groups of G row tiles per column tile: the ~32
+  // workgroups an XCD runs at once share G row tiles and few column tiles of the
+  // operands in its L2.
+  int id = blockIdx.x;
+  const int n_tiles = gridDim.x;
+  if ((n_tiles & 7) == 0) id = (id & 7) * (n_tiles >> 3) + (id >> 3);
+  constexpr int G = 8;
+  const int n_tiles_r = n_tiles / n_tiles_n;
+  const int grp = id / (G * n_tiles_n), in_grp = id - grp * G * n_tiles_n;
+  const int g_rows = min(G, n_tiles_r - grp * G);
+  const int rt = grp * G + in_grp % g_rows, nt = in_grp / g_rows;
   const int KS = d / 16, nk = d / 64;
 
   // Copy k-tile kt into an LDS stage: wave w issues copies [w CPW, (w+1) CPW).
@@ -147,7 +175,9 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(
 #pragma unroll
     for (int b = 0; b < TR; ++b) acc[a][b] = f32x16{};
 
-  auto compute = [&](const unsigned char* buf) {
+  // swap = false: acc[a][b] = C^T tile (rows: features, cols: tokens);
+  // swap = true:  acc[a][b] = C tile   (rows: tokens, cols: features).
+  auto compute = [&](const unsigned char* buf, auto swap) {
 #pragma unroll
     for (int ksl = 0; ksl < 4; ++ksl) {
       F af[TN], bfr[TR];
@@ -161,58 +191,80 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int b = 0; b < TR; ++b) O::mma(acc[a][b], af[a], bfr[b]);
+        for (int b = 0; b < TR; ++b) {
+          if constexpr (decltype(swap)::value) O::mma(acc[a][b], bfr[b], af[a]);
+          else O::mma(acc[a][b], af[a], bfr[b]);
+        }
     }
   };
 
   // nk is even (d is a multiple of 128): the two stages alternate with constant names.
-  issue(0, lds0);
-  for (int kt = 0; kt < nk; kt += 2) {
-    wait_vmem();
-    __syncthreads();           // stage 0 landed for every wave; stage 1 is free
-    issue(kt + 1, lds1);
-    compute(lds0);
-    wait_vmem();
-    __syncthreads();           // stage 1 landed; stage 0 is free
-    if (kt + 2 < nk) issue(kt + 2, lds0);
-    compute(lds1);
-  }
+  auto main_loop = [&](auto swap) {
+    issue(0, lds0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      wait_vmem();
+      __syncthreads();           // stage 0 landed for every wave; stage 1 is free
+      issue(kt + 1, lds1);
+      compute(lds0, swap);
+      wait_vmem();
+      __syncthreads();           // stage 1 landed; stage 0 is free
+      if (kt + 2 < nk) issue(kt + 2, lds0);
+      compute(lds1, swap);
+    }
+  };
 
-  // epilogue: lane owns packed row p and, per 8-register group, 8 consecutive n
   const int ng0 = nt * BN;                 // first output feature in [0, 3d)
   const int which = ng0 / d;               // 0 Q, 1 K, 2 V
   const int nc0 = ng0 - which * d;         // first column inside that matrix
   const int KSD = dk / 16;
+  if (which != 2) {
+    main_loop(std::false_type{});
+    // lane (hf, rho) holds packed row pi(rho) of its tile and, per register group
+    // g, the 8 consecutive features 16 g + 8 hf + [0, 8) of its feature tile
 #pragma unroll
-  for (int b = 0; b < TR; ++b) {
-    const int p = rt * BM + wr * (BM / 2) + b * 32 + rho;
-    if (p >= rows_used) continue;
-    const int bi = p / Np, pos = p - bi * Np;
+    for (int b = 0; b < TR; ++b) {
+      const int p = rt * BM + wr * (BM / 2) + b * 32 + pi_row(rho);
+      if (p >= rows_used) continue;
+      const int bi = p / Np, pos = p - bi * Np;
 #pragma unroll
-    for (int a = 0; a < TN; ++a) {
+      for (int a = 0; a < TN; ++a) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int n = nc0 + wn * (BN / 2) + a * 32 + 16 * g + 8 * hf;
-        float v[8];
+        for (int g = 0; g < 2; ++g) {
+          const int n = nc0 + wn * (BN / 2) + a * 32 + 16 * g + 8 * hf;
+          float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = acc[a][b][8 * g + e];
-        const int head = n / dk, j0 = n - head * dk;
-        const size_t bhh = (size_t)bi * H + head;
-        if (which == 0) {
-          st_packed(Qo + ((size_t)(p >> 5) * KS + (n >> 4)) * kFragElems, 32 * ((n >> 3) & 1) + (p & 31), v);
-        } else if (which == 1) {
-          const size_t frag = (bhh * (Np / 32) + (pos >> 5)) * KSD + (j0 >> 4);
-          st_packed(Ko + frag * kFragElems, 32 * ((j0 >> 3) & 1) + pi_row(pos & 31), v);
-        } else {
-          // 8 consecutive features of one key: 8 rows of the V^T fragments
-          const int lane_hf = 32 * ((pos >> 3) & 1), e_key = pos & 7;
-          T* vbase = Vt + (bhh * (dk / 32) * (size_t)(Np / 16) + (pos >> 4)) * kFragElems;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int dd = j0 + e;
-            vbase[(size_t)(dd >> 5) * (Np / 16) * kFragElems +
-                  packed_index<T>(lane_hf + pi_row(dd & 31), e_key)] = (T)v[e];
+          for (int e = 0; e < 8; ++e) v[e] = acc[a][b][8 * g + e];
+          if (which == 0) {
+            st_packed(Qo + ((size_t)(p >> 5) * KS + (n >> 4)) * kFragElems, 32 * hf + (p & 31), v);
+          } else {
+            const int head = n / dk, j0 = n - head * dk;
+            const size_t frag = (((size_t)bi * H + head) * (Np / 32) + (pos >> 5)) * KSD + (j0 >> 4);
+            st_packed(Ko + frag * kFragElems, 32 * hf + pi_row(pos & 31), v);   // = lane
           }
+        }
+      }
+    }
+  } else {
+    main_loop(std::true_type{});
+    // lane (hf, rho) holds feature pi(rho) of its feature tile and, per register
+    // group g, the 8 consecutive tokens 16 g + 8 hf + [0, 8) of its token tile:
+    // one V^T fragment slot (feature pi(rho), 8 consecutive keys) per group.
+#pragma unroll
+    for (int b = 0; b < TR; ++b) {
+      const int p0 = rt * BM + wr * (BM / 2) + b * 32;   // first token of the tile
+      if (p0 >= rows_used) continue;
+      const int bi = p0 / Np, pos0 = p0 - bi * Np;        // a tile lies inside one sequence
+#pragma unroll
+      for (int a = 0; a < TN; ++a) {
+        const int n0 = nc0 + wn * (BN / 2) + a * 32;      // first feature of the tile
+        const int head = n0 / dk, dt = (n0 - head * dk) >> 5;
+        T* vbase = Vt + ((((size_t)bi * H + head) * (dk / 32) + dt) * (Np / 16) + (pos0 >> 4)) * kFragElems;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = acc[a][b][8 * g + e];
+          st_packed(vbase + (size_t)g * kFragElems, lane, v);
         }
       }
     }
@@ -223,9 +275,11 @@ namespace {
 
 template <typename TX, typename T>
 int run_ln_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
-  hipLaunchKernelGGL((ln_pack_kernel<TX, T>), dim3((L.rows_pad + 3) / 4), dim3(256), 0, s,
-                     (const TX*)L.x, (const T*)L.w.ln1_g, (const T*)L.w.ln1_b, (T*)L.xpack, L.batch,
-                     L.seq_len, L.seq_pad, L.rows_pad, L.d_model, L.ln_eps);
+  auto k = L.d_model <= 1024 ? ln_pack_kernel<TX, T, 2>
+                             : (L.d_model <= 2048 ? ln_pack_kernel<TX, T, 4> : ln_pack_kernel<TX, T, 8>);
+  hipLaunchKernelGGL(k, dim3(L.rows_pad / 32), dim3(256), 0, s, (const TX*)L.x, (const T*)L.w.ln1_g,
+                     (const T*)L.w.ln1_b, (T*)L.xpack, L.batch, L.seq_len, L.seq_pad, L.d_model,
+                     L.ln_eps);
   return check_launch("ln_pack", err, n);
 }
 
