@@ -26,10 +26,28 @@ namespace bpt {
 // bf16, and most key/value blocks need no rescale of o at all.
 constexpr float kRescaleSlack = 8.0f;
 
+// Maximum / sum of a value over the two lanes that hold the same query row
+// (lanes l and l ^ 32): one lane-swap instruction, no LDS round trip.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Persistent workgroups. The work is a list of units: a unit is one query block,
+// or, with the causal mask, the pair of query blocks (nqb-1-p, p) so that every
+// unit has the same number of key/value blocks. Units are numbered (sequence,
+// head) major; the workgroups on one XCD (dispatch is round-robin over 8 XCDs)
+// take a contiguous range of units, so the query blocks of a head run together
+// and share its K and V in that XCD's L2. A workgroup walks its key/value blocks
+// ("visits") across all of its units without draining the copy pipeline.
 template <typename T, int DK, int BQ, int BKV>
 __global__ __launch_bounds__(BQ * 2, (4 * BKV * DK * (int)sizeof(T) <= 65536) ? 2 : 1) void
 attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int N, int Np, int H,
-                 int d, int causal, float scale_log2e, int n_qblocks, int n_items) {
+                 int d, int causal, float scale_log2e, int nqb, int n_bh) {
   using O = Op<T>;
   using F = typename O::frag;
   constexpr int NW = BQ / 32;
@@ -43,41 +61,61 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
   constexpr int STAGE = (KFR + VFR) * FB;
   constexpr int NCOPY = (KFR + VFR) * PCS;     // 1 KB copies per block
   constexpr int CPW = NCOPY / NW;
+  // next unit's Q fetched during the last block of the current one (spare registers)
+  constexpr bool kPrefetchQ = DK * (int)sizeof(T) <= 128;
   static_assert(NCOPY % NW == 0, "copies per wave");
   __shared__ __align__(16) unsigned char lds0[STAGE];
   __shared__ __align__(16) unsigned char lds1[STAGE];
 
-  // work item: XCD-aware (dispatch is round-robin over 8 XCDs), so one XCD walks
-  // consecutive items: all query blocks of a (sequence, head), longest first.
-  int item = blockIdx.x;
-  if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
-  const int bh = item / n_qblocks;
-  const int qb = n_qblocks - 1 - (item - bh * n_qblocks);
-  const int bi = bh / H, head = bh - bi * H;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rho = lane & 31, hf = lane >> 5;
-  const int q0 = qb * BQ;
-  const int qpos = q0 + wave * 32 + rho;       // this lane's query position
-  const int wave_q_first = q0 + wave * 32;
 
-  // this wave's Q fragments (B operand): packed row tile, the head's k-steps
-  T* qfrag = QP + ((size_t)((bi * Np + wave_q_first) >> 5) * (d / 16) + head * KSD) * kFragElems;
-  F qf[KSD];
-#pragma unroll
-  for (int kk = 0; kk < KSD; ++kk) qf[kk] = ld_packed(qfrag + kk * kFragElems, lane);
+  const int n_kvb = (N + BKV - 1) / BKV;
+  const int n_pairs = causal ? (nqb + 1) / 2 : nqb;
+  const int n_units = n_bh * n_pairs;
+  int part = 0, nparts = 1, j = blockIdx.x, M = gridDim.x;
+  if ((gridDim.x & 7) == 0) {
+    part = blockIdx.x & 7; nparts = 8; j = blockIdx.x >> 3; M = gridDim.x >> 3;
+  }
+  const int u_hi = (int)((long long)n_units * (part + 1) / nparts);
 
-  const int n_kv = (N + BKV - 1) / BKV;
-  const int q_last = min(q0 + BQ, N) - 1;
-  const int kv_end = causal ? (q_last / BKV + 1) : n_kv;
+  // ---- visit cursor (wave-uniform): unit u, half w of it, query block qb,
+  //      key/value block kb of kend, (sequence, head) bh
+  struct Cur { int u, w, qb, kb, kend, bh; };
+  auto qblock = [&](int u, int w) {     // query block of half w of unit u, -1 if none
+    const int p = u % n_pairs;
+    if (!causal) return w == 0 ? p : -1;
+    const int qa = nqb - 1 - p;
+    return w == 0 ? qa : (p != qa ? p : -1);
+  };
+  auto start_qblock = [&](Cur& c) {
+    c.qb = qblock(c.u, c.w);
+    c.kb = 0;
+    c.kend = causal ? (min(c.qb * BQ + BQ, N) - 1) / BKV + 1 : n_kvb;
+    c.bh = c.u / n_pairs;
+  };
+  auto advance = [&](Cur& c) {          // c.u >= u_hi afterwards means: no more visits
+    if (c.kb + 1 < c.kend) { ++c.kb; return; }
+    if (c.w == 0 && qblock(c.u, 1) >= 0) c.w = 1;
+    else { c.u += M; c.w = 0; }
+    if (c.u < u_hi) start_qblock(c);
+  };
+  Cur cur;
+  cur.u = (int)((long long)n_units * part / nparts) + j;
+  cur.w = 0;
+  if (cur.u >= u_hi) return;
+  start_qblock(cur);
 
-  const T* kbase = KP + (size_t)bh * (Np / 32) * KSD * kFragElems;
-  const T* vbase = VP + (size_t)bh * DT * (Np / 16) * kFragElems;
-
-  // copy key/value block kb into an LDS stage (K fragments, then V fragments)
-  auto issue = [&](int kb, unsigned char* buf) {
-    const int kv0 = kb * BKV;
+  auto qfrag_of = [&](const Cur& c) {   // this wave's Q fragments (B operand) of c's block
+    const int bi = c.bh / H, head = c.bh - bi * H;
+    return QP + ((size_t)((bi * Np + c.qb * BQ + wave * 32) >> 5) * (d / 16) + head * KSD) * kFragElems;
+  };
+  // copy key/value block c.kb of c.bh into an LDS stage (K fragments, then V fragments)
+  auto issue = [&](const Cur& c, unsigned char* buf) {
+    const int kv0 = c.kb * BKV;
+    const T* kbase = KP + (size_t)c.bh * (Np / 32) * KSD * kFragElems;
+    const T* vbase = VP + (size_t)c.bh * DT * (Np / 16) * kFragElems;
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
       const int idx = wave * CPW + q;
@@ -93,116 +131,165 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
     }
   };
 
+  F qf[KSD], qn[KSD];
+  auto load_q = [&](const Cur& c, F (&dst)[KSD]) {
+    const T* qp = qfrag_of(c);
+#pragma unroll
+    for (int kk = 0; kk < KSD; ++kk) dst[kk] = ld_packed(qp + kk * kFragElems, lane);
+  };
   f32x16 oacc[DT];
+  float m_run, l_run;                   // m_run in the exp2 domain (scores * scale_log2e)
+  auto reset = [&]() {
 #pragma unroll
-  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;   // m_run in the exp2 domain (scores * scale_log2e)
-
-  auto block = [&](int kb, const unsigned char* buf) {
-    const int kv0 = kb * BKV;
-    // a wave whose 32 rows all precede this block has nothing to add
-    if (causal && kv0 > wave_q_first + 31) return;
-    f32x16 s[KT];
-#pragma unroll
-    for (int t = 0; t < KT; ++t) s[t] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < KSD; ++kk)
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
-        O::mma(s[t], ld_packed(reinterpret_cast<const T*>(buf + (t * KSD + kk) * FB), lane), qf[kk]);
-    // mask future keys and keys past the end (only blocks that can contain them)
-    if ((kv0 + BKV > N) || (causal && kv0 + BKV - 1 > wave_q_first)) {
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kp = kv0 + t * 32 + c_row_pi(i, hf);
-          if (kp >= N || (causal && kp > qpos)) s[t][i] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2e;
-    // lazy rescale: only when some row's maximum grew past the slack
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      // 0 on a row's first visit (m_run = -inf); 1 if the row has seen no key yet
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
-    }
-    float lsum = 0.f;
-    F pf[KK];
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float pe = fast_exp2(fmaf(s[t][8 * g + e], scale_log2e, -m_run));
-          if constexpr (sizeof(T) == 2) pe = bf16_round(pe);
-          p[e] = pe;
-          lsum += pe;
-        }
-        pf[2 * t + g] = O::from_f32(p);
-      }
-    }
-    l_run += lsum;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-        O::mma(oacc[t], ld_packed(reinterpret_cast<const T*>(buf + (KFR + t * KK + kk) * FB), lane),
-               pf[kk]);
+    for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
   };
 
-  // two static stages alternate; kv_end may be odd
-  issue(0, lds0);
-  for (int kb = 0; kb < kv_end; kb += 2) {
+  // one key/value block of the current query block; the last one also writes
+  // O = o / l in place over this wave's Q fragments and resets the state
+  auto visit = [&](const Cur& c, const Cur& nx, const unsigned char* buf) {
+    const int kv0 = c.kb * BKV;
+    const int wave_q_first = c.qb * BQ + wave * 32, qpos = wave_q_first + rho;
+    const bool last = c.kb == c.kend - 1;
+    if (kPrefetchQ && last && nx.u < u_hi) load_q(nx, qn);
+    // a wave whose 32 rows all precede this block has nothing to add
+    if (!(causal && kv0 > wave_q_first + 31)) {
+      f32x16 s[KT];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) s[t] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KSD; ++kk)
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+          O::mma(s[t], ld_packed(reinterpret_cast<const T*>(buf + (t * KSD + kk) * FB), lane), qf[kk]);
+      // mask future keys and keys past the end (only blocks that can contain them):
+      // register i of tile t holds key kv0 + t*32 + (i&8)*2 + 8hf + (i&7)
+      if ((kv0 + BKV > N) || (causal && kv0 + BKV - 1 > wave_q_first)) {
+        const int lim = (causal ? min(qpos, N - 1) : N - 1) - kv0 - 8 * hf;
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (t * 32 + (i & 8) * 2 + (i & 7) > lim) s[t][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+      mx = pair_max(mx) * scale_log2e;
+      // lazy rescale: only when some row's maximum grew past the slack
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        // 0 on a row's first visit (m_run = -inf); 1 if the row has seen no key yet
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      }
+      // p = exp2(s * scale - m); l sums p in fp32, P feeds the product in T
+      float lsum = 0.f;
+      F pf[KK];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = fast_exp2(fmaf(s[t][8 * g + e], scale_log2e, -m_run));
+            lsum += p[e];
+          }
+          pf[2 * t + g] = O::from_f32(p);
+        }
+      }
+      l_run += lsum;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          O::mma(oacc[t], ld_packed(reinterpret_cast<const T*>(buf + (KFR + t * KK + kk) * FB), lane),
+                 pf[kk]);
+    }
+    if (last) {
+      // register group g of feature tile t holds features t*32 + 16g + 8hf + [0, 8)
+      T* qp = qfrag_of(c);
+      const float inv = 1.0f / pair_sum(l_run);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = oacc[t][8 * g + e] * inv;
+          st_packed(qp + (2 * t + g) * kFragElems, lane, v);
+        }
+      }
+      reset();
+      if (nx.u < u_hi) {
+        if constexpr (kPrefetchQ) {
+#pragma unroll
+          for (int kk = 0; kk < KSD; ++kk) qf[kk] = qn[kk];
+        } else {
+          load_q(nx, qf);
+        }
+      }
+    }
+  };
+
+  // two static stages alternate; visit v uses stage v % 2
+  reset();
+  load_q(cur, qf);
+  issue(cur, lds0);
+  Cur nxt = cur;
+  advance(nxt);
+  for (;;) {
     wait_vmem();
     __syncthreads();             // stage 0 landed for every wave; stage 1 is free
-    if (kb + 1 < kv_end) issue(kb + 1, lds1);
-    block(kb, lds0);
-    if (kb + 1 < kv_end) {
-      wait_vmem();
-      __syncthreads();           // stage 1 landed; stage 0 is free
-      if (kb + 2 < kv_end) issue(kb + 2, lds0);
-      block(kb + 1, lds1);
-    }
-  }
-
-  // O = o / l, written in place over this wave's Q fragments (B-fragment order):
-  // register group g of feature tile t holds features t*32 + 16g + 8hf + [0, 8).
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
-#pragma unroll
-  for (int t = 0; t < DT; ++t) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = oacc[t][8 * g + e] * inv;
-      st_packed(qfrag + (2 * t + g) * kFragElems, 32 * hf + rho, v);
-    }
+    if (nxt.u < u_hi) issue(nxt, lds1);
+    visit(cur, nxt, lds0);
+    if (nxt.u >= u_hi) break;
+    cur = nxt;
+    advance(nxt);
+    wait_vmem();
+    __syncthreads();             // stage 1 landed; stage 0 is free
+    if (nxt.u < u_hi) issue(nxt, lds0);
+    visit(cur, nxt, lds1);
+    if (nxt.u >= u_hi) break;
+    cur = nxt;
+    advance(nxt);
   }
 }
 
 namespace {
 
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
 template <typename T, int DK, int BQ, int BKV>
 int run_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int nqb = (L.seq_len + BQ - 1) / BQ;
-  const int items = L.batch * L.n_heads * nqb;
+  const int n_bh = L.batch * L.n_heads;
+  const int units = n_bh * (L.causal ? (nqb + 1) / 2 : nqb);
+  // workgroups resident at once: 2 per CU when a stage pair fits 64 KB of LDS
+  constexpr int per_cu = (4 * BKV * DK * (int)sizeof(T) <= 65536) ? 2 : 1;
+  int grid = device_cus() * per_cu;
+  if (units < grid) grid = units;
   const float scale = 1.4426950408889634f / sqrtf((float)DK);
-  hipLaunchKernelGGL((attention_kernel<T, DK, BQ, BKV>), dim3(items), dim3(BQ * 2), 0, s,
+  hipLaunchKernelGGL((attention_kernel<T, DK, BQ, BKV>), dim3(grid), dim3(BQ * 2), 0, s,
                      (T*)L.q, (const T*)L.k, (const T*)L.vt, L.seq_len, L.seq_pad, L.n_heads,
-                     L.d_model, L.causal, scale, nqb, items);
+                     L.d_model, L.causal, scale, nqb, n_bh);
   return check_launch("attention", err, n);
 }
 
