@@ -63,6 +63,8 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
   constexpr int CPW = NCOPY / NW;
   // next unit's Q fetched during the last block of the current one (spare registers)
   constexpr bool kPrefetchQ = DK * (int)sizeof(T) <= 128;
+  // bf16: the block's K and V fragments are held in registers (64 VGPRs each)
+  constexpr bool kPreload = sizeof(T) == 2;
   static_assert(NCOPY % NW == 0, "copies per wave");
   __shared__ __align__(16) unsigned char lds0[STAGE];
   __shared__ __align__(16) unsigned char lds1[STAGE];
@@ -155,14 +157,31 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
     if (kPrefetchQ && last && nx.u < u_hi) load_q(nx, qn);
     // a wave whose 32 rows all precede this block has nothing to add
     if (!(causal && kv0 > wave_q_first + 31)) {
+      // bf16: all K fragments of the block are read from LDS first (one wait per
+      // product instead of a round trip each); V's are issued right after the
+      // S products, in flight during the softmax
       f32x16 s[KT];
 #pragma unroll
       for (int t = 0; t < KT; ++t) s[t] = f32x16{};
+      F kf[kPreload ? KFR : 1];
+      if constexpr (kPreload) {
+#pragma unroll
+        for (int f = 0; f < KFR; ++f) kf[f] = ld_packed(reinterpret_cast<const T*>(buf + f * FB), lane);
+      }
 #pragma unroll
       for (int kk = 0; kk < KSD; ++kk)
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-          O::mma(s[t], ld_packed(reinterpret_cast<const T*>(buf + (t * KSD + kk) * FB), lane), qf[kk]);
+        for (int t = 0; t < KT; ++t) {
+          if constexpr (kPreload) O::mma(s[t], kf[t * KSD + kk], qf[kk]);
+          else O::mma(s[t], ld_packed(reinterpret_cast<const T*>(buf + (t * KSD + kk) * FB), lane), qf[kk]);
+        }
+      F vf[kPreload ? VFR : 1];
+      if constexpr (kPreload) {
+#pragma unroll
+        for (int f = 0; f < VFR; ++f)
+          vf[f] = ld_packed(reinterpret_cast<const T*>(buf + (KFR + f) * FB), lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // mask future keys and keys past the end (only blocks that can contain them):
       // register i of tile t holds key kv0 + t*32 + (i&8)*2 + 8hf + (i&7)
       if ((kv0 + BKV > N) || (causal && kv0 + BKV - 1 > wave_q_first)) {
@@ -209,9 +228,11 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-          O::mma(oacc[t], ld_packed(reinterpret_cast<const T*>(buf + (KFR + t * KK + kk) * FB), lane),
-                 pf[kk]);
+        for (int t = 0; t < DT; ++t) {
+          if constexpr (kPreload) O::mma(oacc[t], vf[t * KK + kk], pf[kk]);
+          else O::mma(oacc[t], ld_packed(reinterpret_cast<const T*>(buf + (KFR + t * KK + kk) * FB), lane),
+                      pf[kk]);
+        }
     }
     if (last) {
       // register group g of feature tile t holds features t*32 + 16g + 8hf + [0, 8)

@@ -177,24 +177,33 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(
 
   // swap = false: acc[a][b] = C^T tile (rows: features, cols: tokens);
   // swap = true:  acc[a][b] = C tile   (rows: tokens, cols: features).
+  // The fragments of k-step ksl+1 are read from LDS while the products of k-step
+  // ksl run (two register sets), so LDS latency is hidden inside a k-tile.
   auto compute = [&](const unsigned char* buf, auto swap) {
-#pragma unroll
-    for (int ksl = 0; ksl < 4; ++ksl) {
-      F af[TN], bfr[TR];
+    F af[2][TN], bfr[2][TR];
+    auto load = [&](int ksl, F (&a_)[TN], F (&b_)[TR]) {
 #pragma unroll
       for (int a = 0; a < TN; ++a)
-        af[a] = ld_packed(reinterpret_cast<const T*>(buf + ((wn * TN + a) * 4 + ksl) * FB), lane);
+        a_[a] = ld_packed(reinterpret_cast<const T*>(buf + ((wn * TN + a) * 4 + ksl) * FB), lane);
 #pragma unroll
       for (int b = 0; b < TR; ++b)
-        bfr[b] = ld_packed(
+        b_[b] = ld_packed(
             reinterpret_cast<const T*>(buf + STAGE_A + ((wr * TR + b) * 4 + ksl) * FB), lane);
+    };
+    load(0, af[0], bfr[0]);
+#pragma unroll
+    for (int ksl = 0; ksl < 4; ++ksl) {
+      const int cs = ksl & 1;
+      if (ksl < 3) load(ksl + 1, af[cs ^ 1], bfr[cs ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll
         for (int b = 0; b < TR; ++b) {
-          if constexpr (decltype(swap)::value) O::mma(acc[a][b], bfr[b], af[a]);
-          else O::mma(acc[a][b], af[a], bfr[b]);
+          if constexpr (decltype(swap)::value) O::mma(acc[a][b], bfr[cs][b], af[cs][a]);
+          else O::mma(acc[a][b], af[cs][a], bfr[cs][b]);
         }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
