@@ -11,13 +11,24 @@ ONE JSON line: algorithmic TFLOP/s (FLOPs from the pages' count: attention
 fraction of the bf16 dense matrix-core peak, the activation memory, a roofline
 entry for the kernel that takes the most time, and the CPU float64 oracle timed
 on a bounded sample of the same workload.
+
+Per-kernel durations come from HIP events that the library records on its
+launch stream between its kernels during the timed steps themselves. The
+roofline's "traffic" (HBM bytes per launch of that kernel) is read from the
+counter summaries committed under profiles/ (rocprofv3 FETCH_SIZE and
+WRITE_SIZE, calibrated against a plain copy); it is null when no summary
+matches the workload or when the kernel's source files have changed since the
+counters were taken (a SHA-256 over those files is stored with each entry).
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,7 +38,17 @@ if ROOT not in sys.path:
 
 METRIC = "fused BPT layer fwd TFLOP/s (1 MI355X) + % bf16 MFMA peak; peak act mem"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense matrix-core peaks of MI355X
-KERNELS = ("ln_stats", "ln_qkv", "attention", "ffn_epilogue")
+# stages of one layer, in launch order, separated by the library's events:
+# prep = weight repacking + LN1 into the packed operand; qkv = the projection GEMM
+KERNELS = ("prep", "qkv", "attention", "ffn_epilogue")
+CSRC = os.path.join(ROOT, "blockwise_attn_ffn_amd", "csrc")
+# source files that determine each stage's device code (for the traffic entries)
+KERNEL_SOURCES = {
+    "prep": ("k_pack.hip", "k_ln_qkv.hip", "ffn_stream.hpp", "bpt_device.hpp"),
+    "qkv": ("k_ln_qkv.hip", "bpt_device.hpp"),
+    "attention": ("k_attention.hip", "bpt_device.hpp"),
+    "ffn_epilogue": ("k_ffn.hip", "ffn_stream.hpp", "bpt_device.hpp"),
+}
 
 
 def parse():
@@ -71,10 +92,32 @@ def kernel_flops(w) -> dict:
     """Algorithmic FLOPs per launch of each kernel (matrix products only)."""
     from blockwise_attn_ffn_amd import accounting as A
     b, n, d, f = w.batch, w.seq_len, w.d_model, w.d_ff
-    return {"ln_stats": 0,
-            "ln_qkv": b * 6 * n * d * d,
+    return {"prep": 0,
+            "qkv": b * 6 * n * d * d,
             "attention": b * A.attention_flops(n, d, w.causal),
             "ffn_epilogue": b * (2 * n * d * d + A.ffn_flops(n, d, f))}
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from a committed counter summary, if still current."""
+    digest = source_digest(kernel)
+    pat = re.compile(r"<!--\s*traffic\s*(\{.*?\})\s*-->")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for m in pat.finditer(f.read()):
+                e = json.loads(m.group(1))
+                if (e.get("workload") == workload and e.get("kernel") == kernel
+                        and e.get("source_sha256") == digest):
+                    return int(e["fetch_bytes"]) + int(e["write_bytes"])
+    return None
 
 
 def cpu_baseline(w, inputs, target_s: float) -> dict:
@@ -147,19 +190,22 @@ def main():
     stream = torch.cuda.current_stream()
 
     hip = Hip()
-    ev = [hip.event() for _ in range(5)]
+    single = w.n_layers == 1
+    # one set of 5 events per timed step: the library records them on its launch
+    # stream between its kernels, so per-kernel durations come from the timed steps
+    evs = [[hip.event() for _ in range(5)] for _ in range(args.steps if single else 0)]
 
-    def step(profiled: bool):
-        if w.n_layers == 1:
-            if profiled:
-                bpt.layer_fwd_profiled(desc, dev_x, dev_layers[0], z, ws, ev, stream)
+    def step(events=None):
+        if single:
+            if events is not None:
+                bpt.layer_fwd_profiled(desc, dev_x, dev_layers[0], z, ws, events, stream)
             else:
                 bpt.layer_fwd(desc, dev_x, dev_layers[0], z, ws, stream)
         else:
             bpt.stack_fwd(desc, dev_x, dev_layers, z, ws, stream)
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
 
     # timed region: K whole steps
@@ -167,36 +213,32 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for _ in range(args.steps):
-        step(False)
+    for i in range(args.steps):
+        step(evs[i] if single else None)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
     free_after, _ = torch.cuda.mem_get_info()
 
-    # per-kernel durations, recorded with events between the library's launches
     per_kernel = {k: 0.0 for k in KERNELS}
-    if w.n_layers == 1:
-        for _ in range(args.steps):
-            step(True)
-            torch.cuda.synchronize()
-            for i, k in enumerate(KERNELS):
-                per_kernel[k] += hip.elapsed_ms(ev[i], ev[i + 1]) / args.steps
-    for e in ev:
-        hip.destroy(e)
+    for ev in evs:
+        for i, k in enumerate(KERNELS):
+            per_kernel[k] += hip.elapsed_ms(ev[i], ev[i + 1]) / args.steps
+        for e in ev:
+            hip.destroy(e)
 
     total_flops = A.workload_flops(w.batch, w.seq_len, w.d_model, w.d_ff, w.causal, w.n_layers)
     tflops = total_flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     kf = kernel_flops(w)
     roofline = None
-    if w.n_layers == 1:
+    if single:
         dom = max(KERNELS, key=lambda k: per_kernel[k])
         achieved = kf[dom] / (per_kernel[dom] * 1e-3) / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": None, "avg_ms": round(per_kernel[dom], 4),
-                    "flops_per_launch": kf[dom]}
+                    "traffic": recorded_traffic(w.name, dom), "traffic_unit": "bytes",
+                    "avg_ms": round(per_kernel[dom], 4), "flops_per_launch": kf[dom]}
     act_bytes = ws_bytes + dev_x.numel() * dev_x.element_size() + z.numel() * z.element_size()
     line = {
         "metric": METRIC,

@@ -110,6 +110,84 @@ __global__ __launch_bounds__(256) void ln_pack_kernel(const TX* __restrict__ X,
   }
 }
 
+// LDS-staged variant (d <= 2048): eight waves read the tile's 32 rows once
+// (4 rows each, coalesced), normalise them in registers and write the packed
+// fragments into LDS; the tile then leaves LDS for global memory as contiguous
+// 16-byte chunks. X is read exactly once.
+template <typename TX, typename T, int CPL>
+__global__ __launch_bounds__(512) void ln_pack_lds_kernel(const TX* __restrict__ X,
+                                                          const T* __restrict__ ln_g,
+                                                          const T* __restrict__ ln_b,
+                                                          T* __restrict__ XP, int B, int N, int Np,
+                                                          int d, float eps) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* tile_lds = reinterpret_cast<T*>(smem_raw);          // [d/16] packed fragments
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tile = blockIdx.x;
+  const int nch = d >> 3;
+#pragma unroll 2
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave + 8 * i, row = tile * 32 + r;
+    const int bi = row / Np, pos = row - bi * Np;
+    const bool live = bi < B && pos < N;
+    float v[CPL][8];
+    if (live) {
+      const TX* xr = X + ((size_t)bi * N + pos) * d;
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nch) {
+          load8_f32(xr + 8 * c, v[j]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum += v[j][e];
+        }
+      }
+      const float mean = wave_sum(sum) / (float)d;
+      float q = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nch) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float t = v[j][e] - mean;
+            q += t * t;
+          }
+        }
+      }
+      const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nch) {
+          float g[8], b[8];
+          load8_f32(ln_g + 8 * c, g);
+          load8_f32(ln_b + 8 * c, b);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[j][e] = (v[j][e] - mean) * rstd * g[e] + b[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+    }
+    // chunk c (k = 8c .. 8c+7) of row r: fragment c/2, slot 32 (c&1) + pi(r)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nch) st_packed(tile_lds + (size_t)(c >> 1) * kFragElems, 32 * (c & 1) + pi_row(r), v[j]);
+    }
+  }
+  __syncthreads();
+  const int n16 = (32 * d * (int)sizeof(T)) >> 4;         // 16-byte chunks in the tile
+  const uint4* src = reinterpret_cast<const uint4*>(tile_lds);
+  uint4* dst = reinterpret_cast<uint4*>(XP + (size_t)tile * 32 * d);
+  for (int q = threadIdx.x; q < n16; q += 512) dst[q] = src[q];
+}
+
 // ---------------------------------------------------------------------------
 // QKV GEMM on packed operands. Tile BN output features x BM token rows; 4 waves
 // in a 2 x 2 grid, each (BN/2) x (BM/2) as 32x32 tiles. A k-tile is 4 k-steps.
@@ -284,11 +362,20 @@ namespace {
 
 template <typename TX, typename T>
 int run_ln_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
-  auto k = L.d_model <= 1024 ? ln_pack_kernel<TX, T, 2>
-                             : (L.d_model <= 2048 ? ln_pack_kernel<TX, T, 4> : ln_pack_kernel<TX, T, 8>);
+  const int d = L.d_model;
+  if (d <= 2048) {
+    auto k = d <= 512 ? ln_pack_lds_kernel<TX, T, 1>
+                      : (d <= 1024 ? ln_pack_lds_kernel<TX, T, 2> : ln_pack_lds_kernel<TX, T, 4>);
+    const size_t smem = (size_t)32 * d * sizeof(T);
+    if (set_smem(k, smem, err, n)) return 1;
+    hipLaunchKernelGGL(k, dim3(L.rows_pad / 32), dim3(512), smem, s, (const TX*)L.x,
+                       (const T*)L.w.ln1_g, (const T*)L.w.ln1_b, (T*)L.xpack, L.batch, L.seq_len,
+                       L.seq_pad, d, L.ln_eps);
+    return check_launch("ln_pack", err, n);
+  }
+  auto k = ln_pack_kernel<TX, T, 8>;
   hipLaunchKernelGGL(k, dim3(L.rows_pad / 32), dim3(256), 0, s, (const TX*)L.x, (const T*)L.w.ln1_g,
-                     (const T*)L.w.ln1_b, (T*)L.xpack, L.batch, L.seq_len, L.seq_pad, L.d_model,
-                     L.ln_eps);
+                     (const T*)L.w.ln1_b, (T*)L.xpack, L.batch, L.seq_len, L.seq_pad, d, L.ln_eps);
   return check_launch("ln_pack", err, n);
 }
 

@@ -23,34 +23,39 @@ namespace bpt {
 
 enum PackOrder { kPlain = 0, kStreamWO = 1, kStreamW1 = 2, kStreamW2 = 3 };
 
-// One thread per 8-element chunk of W; reads are row-contiguous.
+// The six matrices of a layer, repacked by one launch: matrix m covers the
+// 8-element chunks [first_chunk[m], first_chunk[m+1]) of the grid.
 template <typename T>
-__global__ __launch_bounds__(256) void pack_frag_kernel(const T* __restrict__ W, T* __restrict__ P,
-                                                        int n_rows, int K, int order, FfnStream fs) {
-  const int kc = K / 8;                                   // chunks per row
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (size_t)n_rows * kc) return;
-  const int row = (int)(i / kc), c = (int)(i - (size_t)row * kc);
+struct PackJob {
+  const T* src[6];
+  T* dst[6];
+  int rows[6], K[6], order[6];
+  long long first_chunk[7];
+  FfnStream fs;
+};
+
+// One thread per 8-element chunk of a weight; reads are row-contiguous.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_frag_kernel(PackJob<T> job) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= job.first_chunk[6]) return;
+  int m = 0;
+#pragma unroll
+  for (int q = 1; q < 6; ++q) m += i >= job.first_chunk[q];
+  const long long li = i - job.first_chunk[m];
+  const int K = job.K[m], kc = K / 8;                     // chunks per row
+  const int row = (int)(li / kc), c = (int)(li - (long long)row * kc);
   const int tile = row >> 5, rho = pi_row(row & 31);      // pi is its own inverse
   const int ks = c >> 1, hf = c & 1;
   size_t slot;
-  if (order == kStreamWO) slot = fs.slot_wo(tile, ks);
-  else if (order == kStreamW1) slot = fs.slot_w1(tile, ks);
-  else if (order == kStreamW2) slot = fs.slot_w2(tile, ks);
+  const int order = job.order[m];
+  if (order == kStreamWO) slot = job.fs.slot_wo(tile, ks);
+  else if (order == kStreamW1) slot = job.fs.slot_w1(tile, ks);
+  else if (order == kStreamW2) slot = job.fs.slot_w2(tile, ks);
   else slot = (size_t)tile * (K / 16) + ks;
-  st_packed_chunk(P + slot * kFragElems, 32 * hf + rho, ld_chunk(W + (size_t)row * K + (size_t)c * 8));
+  st_packed_chunk(job.dst[m] + slot * kFragElems, 32 * hf + rho,
+                  ld_chunk(job.src[m] + (size_t)row * K + (size_t)c * 8));
 }
-
-namespace {
-template <typename T>
-int run_pack(const void* W, void* P, int n_rows, int K, int order, FfnStream fs, hipStream_t s,
-             char* err, size_t n) {
-  const size_t chunks = (size_t)n_rows * (K / 8);
-  hipLaunchKernelGGL(pack_frag_kernel<T>, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
-                     (const T*)W, (T*)P, n_rows, K, order, fs);
-  return check_launch("pack_frag", err, n);
-}
-}  // namespace
 
 // Packed region: W_Q, W_K, W_V (one [3d, d] operand), then the epilogue stream
 // holding W_O, W_1 and W_2 (d^2 + 2 d d_ff elements).
@@ -58,14 +63,25 @@ template <typename T>
 int pack_all(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int d = L.d_model, f = L.d_ff;
   const size_t dd = (size_t)d * d;
-  const FfnStream fs{d, f};
   T* p = static_cast<T*>(L.wpack);
-  return run_pack<T>(L.w.w_q, p, d, d, kPlain, fs, s, err, n) ||
-         run_pack<T>(L.w.w_k, p + dd, d, d, kPlain, fs, s, err, n) ||
-         run_pack<T>(L.w.w_v, p + 2 * dd, d, d, kPlain, fs, s, err, n) ||
-         run_pack<T>(L.w.w_o, p + 3 * dd, d, d, kStreamWO, fs, s, err, n) ||
-         run_pack<T>(L.w.w_1, p + 3 * dd, f, d, kStreamW1, fs, s, err, n) ||
-         run_pack<T>(L.w.w_2, p + 3 * dd, d, f, kStreamW2, fs, s, err, n);
+  PackJob<T> job{};
+  job.fs = FfnStream{d, f};
+  const void* srcs[6] = {L.w.w_q, L.w.w_k, L.w.w_v, L.w.w_o, L.w.w_1, L.w.w_2};
+  T* dsts[6] = {p, p + dd, p + 2 * dd, p + 3 * dd, p + 3 * dd, p + 3 * dd};
+  const int rows[6] = {d, d, d, d, f, d}, Ks[6] = {d, d, d, d, d, f};
+  const int orders[6] = {kPlain, kPlain, kPlain, kStreamWO, kStreamW1, kStreamW2};
+  job.first_chunk[0] = 0;
+  for (int m = 0; m < 6; ++m) {
+    job.src[m] = static_cast<const T*>(srcs[m]);
+    job.dst[m] = dsts[m];
+    job.rows[m] = rows[m];
+    job.K[m] = Ks[m];
+    job.order[m] = orders[m];
+    job.first_chunk[m + 1] = job.first_chunk[m] + (long long)rows[m] * (Ks[m] / 8);
+  }
+  const long long total = job.first_chunk[6];
+  hipLaunchKernelGGL(pack_frag_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, job);
+  return check_launch("pack_frag", err, n);
 }
 
 int launch_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
