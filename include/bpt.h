@@ -70,7 +70,7 @@ typedef enum {
 typedef struct {
   int32_t batch;      /* sequences; 0 gives an empty call that enqueues nothing  */
   int32_t seq_len;    /* tokens per sequence N; 0 likewise                      */
-  int32_t d_model;    /* d; a multiple of 128, one of the sizes listed below     */
+  int32_t d_model;    /* d; one of the sizes listed below                        */
   int32_t n_heads;    /* h; d_k = d_model / n_heads must be 64 or 128            */
   int32_t d_ff;       /* FFN width (4 d in the pages); a multiple of 256         */
   int32_t block_q;    /* b: query rows per outer-loop block; 64 or 128           */
@@ -89,10 +89,12 @@ typedef struct {
   const void *ln2_g, *ln2_b, *w_1, *w_2;
 } bpt_layer_weights_t;
 
-/* Supported d_model values: 128, 256, 512, 768, 1024, 1536, 2048, 3072, 4096
- * (BPT_F32: 128, 256, 512). Sequence length, batch and d_ff (multiple of 256)
- * are otherwise free; a sequence length that is not a multiple of the block
- * sizes gets a shorter last block. */
+/* Kernel instances exist for d_model 256, 512, 768, 1024, 2048 (BPT_BF16) and
+ * 128, 256 (BPT_F32), head sizes 64 and 128, block_q and block_kv 64 or 128
+ * (BPT_F32 with head size 128: block_kv 64), d_ff a multiple of 256. Any other
+ * combination returns BPT_ERR_UNSUPPORTED before anything is enqueued. Batch and
+ * sequence length are free; a sequence length that is not a multiple of the
+ * block sizes gets a shorter last block. */
 
 /* Bytes of workspace bpt_layer_fwd needs for *desc (0 for an empty call), or 0
  * with bpt_last_error() set when desc is invalid. Holds, in the compute type:
