@@ -81,14 +81,23 @@ def softmax_rows(s: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def attention_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
-                       causal: bool, q_pos: np.ndarray | None = None) -> np.ndarray:
+                       causal: bool, q_pos: np.ndarray | None = None,
+                       q_chunk: int | None = None) -> np.ndarray:
     """Multi-head attention of one sequence with a full softmax.
 
     q: [nq, d] queries at positions q_pos (default 0..nq-1); k, v: [nk, d] keys and
     values at positions 0..nk-1. Returns the concatenated head outputs [nq, d].
     Scores are q k^T / sqrt(d_k) ([BPT] fused algorithm, s line); with causal
     masking key position j is visible to query position p iff j <= p.
+    q_chunk, if given, evaluates the query rows in groups of that many rows to
+    bound memory; every row's scores, softmax and output are the same (rows are
+    independent: [BPT] fused algorithm, outer loop over query blocks).
     """
+    if q_chunk is not None and q.shape[0] > q_chunk:
+        qp = np.arange(q.shape[0]) if q_pos is None else np.asarray(q_pos)
+        return np.concatenate([attention_sequence(q[c:c + q_chunk], k, v, n_heads, causal,
+                                                  q_pos=qp[c:c + q_chunk])
+                               for c in range(0, q.shape[0], q_chunk)])
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
     v = np.asarray(v, F64)
@@ -119,7 +128,7 @@ def _as_f64_layer(p: dict) -> dict:
 
 
 def layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal: bool,
-                  eps: float = 1e-5, return_parts: bool = False):
+                  eps: float = 1e-5, return_parts: bool = False, q_chunk: int | None = None):
     """One pre-LN layer, unfused ([BPT] fused-algorithm section, last paragraph: the
     whole [N, d] attention output first, then a full [N, d_ff] hidden state).
 
@@ -141,7 +150,7 @@ def layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal:
     a = np.empty_like(x)
     for s0 in range(0, rows, seq_len):
         sl = slice(s0, s0 + seq_len)
-        a[sl] = attention_sequence(q[sl], k[sl], v[sl], n_heads, causal)
+        a[sl] = attention_sequence(q[sl], k[sl], v[sl], n_heads, causal, q_chunk=q_chunk)
     y = x + a @ p["w_o"]
     hidden = gelu_tanh(layer_norm(y, p["ln2_g"], p["ln2_b"], eps) @ p["w_1"])
     z = y + hidden @ p["w_2"]
@@ -200,13 +209,15 @@ def stack_forward(x: np.ndarray, layers: list, *, seq_len: int, n_heads: int,
 
 
 def stack_forward_rows(x: np.ndarray, layers: list, rows: np.ndarray, *, seq_len: int,
-                       n_heads: int, causal: bool, eps: float = 1e-5) -> np.ndarray:
+                       n_heads: int, causal: bool, eps: float = 1e-5,
+                       q_chunk: int | None = None) -> np.ndarray:
     """Sampled rows of the stack's output: every layer but the last in full (a causal
     row depends on all earlier rows of every earlier layer), the last one at the
-    sampled rows only."""
+    sampled rows only. q_chunk bounds the attention's memory (attention_sequence)."""
     z = np.asarray(x, F64)
     for p in layers[:-1]:
-        z = layer_forward(z, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps)
+        z = layer_forward(z, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps,
+                          q_chunk=q_chunk)
     return layer_forward_rows(z, layers[-1], rows, seq_len=seq_len, n_heads=n_heads,
                               causal=causal, eps=eps)
 

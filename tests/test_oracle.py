@@ -126,6 +126,22 @@ def test_attention_sampled_positions_match_full():
     assert np.max(np.abs(part - full[pos])) < 1e-14
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_query_chunks_match_brute_force(causal):
+    """Evaluating query rows in groups (a memory bound) is checked against the
+    brute-force loops, with ragged groups and sampled positions."""
+    rng = np.random.default_rng(11 + causal)
+    n, d, h = 23, 8, 2
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    ref = brute_force_attention(q, k, v, h, causal)
+    for chunk in (1, 5, 22, 23, 64):
+        got = oracle.attention_sequence(q, k, v, h, causal, q_chunk=chunk)
+        assert np.max(np.abs(got - ref)) < 1e-13, chunk
+    pos = np.array([2, 3, 11, 19, 22])
+    got = oracle.attention_sequence(q[pos], k, v, h, causal, q_pos=pos, q_chunk=2)
+    assert np.max(np.abs(got - ref[pos])) < 1e-13
+
+
 def test_uniform_attention_closed_form():
     """W_Q = 0 makes every score 0: causal row p returns mean(V[0..p]); without the
     mask every row returns mean(V)."""
@@ -304,13 +320,14 @@ def test_pins_catch_planted_oracle_mistakes(mutation, monkeypatch):
     if mutation == "scale_1_over_dk":
         orig = O.attention_sequence
 
-        def bad(q, k, v, n_heads, causal, q_pos=None):
-            return orig(q * math.sqrt(d // n_heads) ** -1, k, v, n_heads, causal, q_pos)
+        def bad(q, k, v, n_heads, causal, q_pos=None, q_chunk=None):
+            return orig(q * math.sqrt(d // n_heads) ** -1, k, v, n_heads, causal, q_pos, q_chunk)
         monkeypatch.setattr(O, "attention_sequence", bad)
     elif mutation == "no_causal_mask":
         orig = O.attention_sequence
         monkeypatch.setattr(O, "attention_sequence",
-                            lambda q, k, v, n_heads, causal, q_pos=None: orig(q, k, v, n_heads, False, q_pos))
+                            lambda q, k, v, n_heads, causal, q_pos=None, q_chunk=None:
+                            orig(q, k, v, n_heads, False, q_pos, q_chunk))
     elif mutation == "erf_gelu":
         monkeypatch.setattr(O, "gelu_tanh", lambda u: 0.5 * u * (1 + scipy.special.erf(u / math.sqrt(2))))
     elif mutation == "transposed_wo":
