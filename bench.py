@@ -45,9 +45,9 @@ CSRC = os.path.join(ROOT, "blockwise_attn_ffn_amd", "csrc")
 # source files that determine each stage's device code (for the traffic entries)
 KERNEL_SOURCES = {
     "prep": ("k_pack.hip", "k_ln_qkv.hip", "ffn_stream.hpp", "bpt_device.hpp"),
-    "qkv": ("k_ln_qkv.hip", "bpt_device.hpp"),
+    "qkv": ("k_gemm.hip", "bpt_device.hpp"),
     "attention": ("k_attention.hip", "bpt_device.hpp"),
-    "ffn_epilogue": ("k_ffn.hip", "ffn_stream.hpp", "bpt_device.hpp"),
+    "ffn_epilogue": ("k_ffn.hip", "k_gemm.hip", "ffn_stream.hpp", "bpt_device.hpp"),
 }
 
 

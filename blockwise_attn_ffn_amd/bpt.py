@@ -87,7 +87,8 @@ def desc_for(w, out_dtype=F32) -> LayerDesc:
     """Descriptor of a synth.Workload."""
     return make_desc(batch=w.batch, seq_len=w.seq_len, d_model=w.d_model, n_heads=w.n_heads,
                      d_ff=w.d_ff, block_q=w.block_q, block_kv=w.block_kv, causal=w.causal,
-                     dtype=w.dtype, out_dtype=out_dtype, ln_eps=w.ln_eps)
+                     dtype=w.dtype, out_dtype=out_dtype, ln_eps=w.ln_eps,
+                     precision=getattr(w, "precision", 0))
 
 
 def layer_workspace_bytes(desc: LayerDesc) -> int:

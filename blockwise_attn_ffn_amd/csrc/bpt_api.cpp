@@ -43,7 +43,12 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   const size_t rows = (size_t)d->batch * d->seq_len;
   const size_t es = esize(d->dtype);
   const size_t dm = d->d_model, df = d->d_ff;
-  const size_t rp = rows_pad_of(d), used = (size_t)d->batch * seq_pad_of(d);
+  const size_t rp = rows_pad_of(d);
+  const bool split = d->precision == 1;
+  const bool staged = bpt::staged_epilogue(d->d_model, split);
+  // K and V^T cover rows_pad rows on the staged path, so that the fp32 Y [rows_pad, d]
+  // fits over them once attention is done
+  const size_t used = staged ? rp : (size_t)d->batch * seq_pad_of(d);
   size_t off = 0;
   L.xpack_off = off;  // LN1(X), packed
   off = round_up(off + rp * dm * es, kAlign);
@@ -55,6 +60,16 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   off = round_up(off + used * dm * es, kAlign);
   L.wpack_off = off;  // W_Q, W_K, W_V, W_O, W_1, W_2 back to back, fragment order
   off = round_up(off + (4 * dm * dm + 2 * df * dm) * es, kAlign);
+  L.h_off = off;      // staged epilogue: hidden block [min(rows_pad, 4096), d_ff]
+  const size_t hr = rp < (size_t)bpt::kHiddenBlockRows ? rp : (size_t)bpt::kHiddenBlockRows;
+  if (staged) off = round_up(off + hr * df * es, kAlign);
+  if (split) {        // lo halves, same shapes as the hi ones
+    const size_t sizes[5] = {rp * dm * es, rp * dm * es, used * dm * es, used * dm * es, hr * df * es};
+    for (int i = 0; i < 5; ++i) {
+      L.lo_off[i] = off;
+      off = round_up(off + sizes[i], kAlign);
+    }
+  }
   L.resid_off = off;
   if (stack_resid) off = round_up(off + rows * dm * 4, kAlign);
   L.total = off;
@@ -79,14 +94,14 @@ bpt_status_t validate_desc(const bpt_layer_desc_t* d) {
       (d->out_dtype != BPT_F32 && d->out_dtype != BPT_BF16))
     return fail(BPT_ERR_SHAPE, "dtype / out_dtype must be BPT_F32 or BPT_BF16");
   if (d->act != 0) return fail(BPT_ERR_UNSUPPORTED, "act %d unsupported (0 = GELU tanh)", d->act);
-  if (d->precision != 0)
-    return fail(BPT_ERR_UNSUPPORTED, "precision %d unsupported (0 only)", d->precision);
+  if (d->precision != 0 && d->precision != 1)
+    return fail(BPT_ERR_SHAPE, "precision must be 0 (bf16) or 1 (bf16 pairs)");
   if ((int64_t)d->batch * d->seq_len > (int64_t)INT32_MAX - 1024)
     return fail(BPT_ERR_SHAPE, "batch * seq_len exceeds the 32-bit row index range");
   char msg[256] = "";
   if (!bpt::kernels_support(d->d_model, d->d_model / d->n_heads, d->block_q, d->block_kv,
-                            d->dtype == BPT_F32, 0, d->out_dtype == BPT_F32, d->d_ff, msg,
-                            sizeof(msg)))
+                            d->dtype == BPT_F32, 0, d->out_dtype == BPT_F32, d->d_ff,
+                            d->precision == 1, msg, sizeof(msg)))
     return fail(BPT_ERR_UNSUPPORTED, "%s", msg);
   return BPT_OK;
 }
@@ -138,6 +153,7 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   p.ln_eps = d->ln_eps;
   p.compute_f32 = d->dtype == BPT_F32;
   p.seq_pad = (int)seq_pad_of(d);
+  p.split = d->precision == 1;
   char* base = static_cast<char*>(ws);
   p.rows_pad = (int)rows_pad_of(d);
   p.xpack = base + L.xpack_off;
@@ -145,6 +161,18 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   p.k = base + L.k_off;
   p.vt = base + L.vt_off;
   p.wpack = base + L.wpack_off;
+  if (bpt::staged_epilogue(d->d_model, p.split)) {
+    p.ybuf = base + L.k_off;
+    p.hbuf = base + L.h_off;
+    p.h_rows = p.rows_pad < bpt::kHiddenBlockRows ? p.rows_pad : bpt::kHiddenBlockRows;
+  }
+  if (p.split) {
+    p.xpack_lo = base + L.lo_off[0];
+    p.q_lo = base + L.lo_off[1];
+    p.k_lo = base + L.lo_off[2];
+    p.vt_lo = base + L.lo_off[3];
+    p.hbuf_lo = base + L.lo_off[4];
+  }
   return p;
 }
 

@@ -20,6 +20,7 @@ struct LayerLaunch {
   int x_f32;         // element type of X: 1 fp32, 0 bf16 (the weights' type otherwise)
   int z_f32;         // element type of Z
   int seq_pad;       // seq_len rounded up to 128: rows per sequence in packed row space
+  int split;         // 1: activations carried as bf16 (hi, lo) pairs (precision 1)
   // tensors
   const void* x;
   bpt_layer_weights_t w;
@@ -30,21 +31,41 @@ struct LayerLaunch {
   void* q;           // Q as packed B fragments over [rows_pad, d], then O in place
   void* k;           // K: per (sequence, head) packed A fragments [seq_pad keys, d_head]
   void* vt;          // V^T: per (sequence, head) packed A fragments [d_head, seq_pad keys]
-  void* wpack;       // W_Q | W_K | W_V | W_O | W_1 | W_2 in packed fragment order
+  void* wpack;       // W_Q | W_K | W_V, then W_O, W_1, W_2 (epilogue stream, or plain
+                     // fragment order for the staged epilogue)
+  // staged epilogue (d_model above kFusedMaxWidth): Y fp32 [rows_pad, d] over the
+  // K and V^T buffers, and the hidden block [h_rows, d_ff] of packed fragments
+  void* ybuf;
+  void* hbuf;
+  int h_rows;
+  // split: the lo halves of LN1(X) / LN2(Y), Q / O, K, V^T and the hidden block
+  void* xpack_lo;
+  void* q_lo;
+  void* k_lo;
+  void* vt_lo;
+  void* hbuf_lo;
   // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
   void* const* events;
 };
 
 // Element counts/byte sizes of the workspace pieces (shared by sizing and carving).
 struct WorkspaceLayout {
-  size_t xpack_off, q_off, k_off, vt_off, wpack_off, resid_off, total;
+  size_t xpack_off, q_off, k_off, vt_off, wpack_off, h_off, resid_off, total;
+  size_t lo_off[5];   // split: lo halves of xpack, q, k, vt, hidden block
 };
+
+// Widest d_model whose per-tile fp32 accumulator fits the fused epilogue's
+// registers; wider layers use the staged epilogue (one GEMM per step, the FFN
+// hidden state for kHiddenBlockRows rows at a time in the workspace).
+constexpr int kFusedMaxWidth = 2048;
+constexpr int kHiddenBlockRows = 4096;
+inline bool staged_epilogue(int d_model, int split = 0) { return split || d_model > kFusedMaxWidth; }
 
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).
 int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t errlen);
 
 // Whether a kernel instance exists for (d_model, d_head, block sizes, types).
 int kernels_support(int d_model, int d_head, int block_q, int block_kv, int compute_f32,
-                    int x_f32, int z_f32, int d_ff, char* err, size_t errlen);
+                    int x_f32, int z_f32, int d_ff, int split, char* err, size_t errlen);
 
 }  // namespace bpt

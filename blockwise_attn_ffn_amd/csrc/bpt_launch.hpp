@@ -38,5 +38,8 @@ int launch_ln_qkv(const LayerLaunch& L, hipStream_t s, char* err, size_t n, int 
 int launch_attention(const LayerLaunch& L, hipStream_t s, char* err, size_t n);
 int launch_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n);
 int launch_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n);
+int launch_qkv(const LayerLaunch& L, hipStream_t s, char* err, size_t n);
+int launch_ffn_staged(const LayerLaunch& L, hipStream_t s, char* err, size_t n);
+int launch_ln_rows(const LayerLaunch& L, const void* y, int rows, hipStream_t s, char* err, size_t n);
 
 }  // namespace bpt

@@ -12,14 +12,14 @@ void set_err(char* err, size_t n, const char* fmt, const char* a = "", int b = 0
 }  // namespace
 
 int kernels_support(int d_model, int d_head, int block_q, int block_kv, int compute_f32,
-                    int x_f32, int z_f32, int d_ff, char* err, size_t errlen) {
+                    int x_f32, int z_f32, int d_ff, int split, char* err, size_t errlen) {
   (void)x_f32;
   (void)z_f32;
   const bool bf = !compute_f32;
   bool d_ok = false;
   if (bf) {
     d_ok = d_model == 256 || d_model == 512 || d_model == 768 || d_model == 1024 ||
-           d_model == 2048;
+           d_model == 2048 || d_model == 4096;
   } else {
     d_ok = d_model == 128 || d_model == 256;
   }
@@ -37,6 +37,10 @@ int kernels_support(int d_model, int d_head, int block_q, int block_kv, int comp
   }
   if (!bf && d_head == 128 && block_kv == 128) {
     set_err(err, errlen, "fp32 with head size 128 needs block_kv 64%s", "");
+    return 0;
+  }
+  if (split && !bf) {
+    set_err(err, errlen, "precision 1 (bf16 pairs) needs dtype BPT_BF16%s", "");
     return 0;
   }
   if (d_ff % 256 != 0 || d_ff <= 0) {

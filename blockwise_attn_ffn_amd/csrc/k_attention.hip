@@ -44,9 +44,15 @@ __device__ inline float pair_sum(float x) {
 // take a contiguous range of units, so the query blocks of a head run together
 // and share its K and V in that XCD's L2. A workgroup walks its key/value blocks
 // ("visits") across all of its units without draining the copy pipeline.
-template <typename T, int DK, int BQ, int BKV>
-__global__ __launch_bounds__(BQ * 2, (4 * BKV * DK * (int)sizeof(T) <= 65536) ? 2 : 1) void
-attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int N, int Np, int H,
+//
+// SPLIT: every operand computed in fp32 is carried as a pair of bf16 values
+// (hi = bf16(v), lo = bf16(v - hi)), so that products keep ~16 significant bits:
+// S = Qhi Khi + Qhi Klo + Qlo Khi and O += Vhi Phi + Vlo Phi + Vhi Plo; O is written
+// as such a pair too. The LDS stage holds the hi fragments, then the lo ones.
+template <typename T, int DK, int BQ, int BKV, bool SPLIT = false>
+__global__ __launch_bounds__(BQ * 2, (4 * BKV * DK * (int)sizeof(T) * (SPLIT ? 2 : 1) <= 65536) ? 2 : 1) void
+attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* QPlo,
+                 const T* __restrict__ KPlo, const T* __restrict__ VPlo, int N, int Np, int H,
                  int d, int causal, float scale_log2e, int nqb, int n_bh) {
   using O = Op<T>;
   using F = typename O::frag;
@@ -58,13 +64,14 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
   constexpr int DT = DK / 32;                  // feature tiles (O^T tiles)
   constexpr int KK = BKV / 16;                 // key k-steps per block
   constexpr int KFR = KT * KSD, VFR = DT * KK; // fragments per block
-  constexpr int STAGE = (KFR + VFR) * FB;
-  constexpr int NCOPY = (KFR + VFR) * PCS;     // 1 KB copies per block
+  constexpr int HALF = (KFR + VFR) * FB;       // bytes of the hi (or lo) fragments
+  constexpr int STAGE = HALF * (SPLIT ? 2 : 1);
+  constexpr int NCOPY = (KFR + VFR) * PCS * (SPLIT ? 2 : 1);   // 1 KB copies per block
   constexpr int CPW = NCOPY / NW;
   // next unit's Q fetched during the last block of the current one (spare registers)
-  constexpr bool kPrefetchQ = DK * (int)sizeof(T) <= 128;
+  constexpr bool kPrefetchQ = !SPLIT && DK * (int)sizeof(T) <= 128;
   // bf16: the block's K and V fragments are held in registers (64 VGPRs each)
-  constexpr bool kPreload = sizeof(T) == 2;
+  constexpr bool kPreload = sizeof(T) == 2 && !SPLIT;
   static_assert(NCOPY % NW == 0, "copies per wave");
   __shared__ __align__(16) unsigned char lds0[STAGE];
   __shared__ __align__(16) unsigned char lds1[STAGE];
@@ -113,31 +120,39 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
     const int bi = c.bh / H, head = c.bh - bi * H;
     return QP + ((size_t)((bi * Np + c.qb * BQ + wave * 32) >> 5) * (d / 16) + head * KSD) * kFragElems;
   };
-  // copy key/value block c.kb of c.bh into an LDS stage (K fragments, then V fragments)
+  // copy key/value block c.kb of c.bh into an LDS stage (K fragments, then V
+  // fragments; with SPLIT the lo fragments follow in the same order)
   auto issue = [&](const Cur& c, unsigned char* buf) {
     const int kv0 = c.kb * BKV;
-    const T* kbase = KP + (size_t)c.bh * (Np / 32) * KSD * kFragElems;
-    const T* vbase = VP + (size_t)c.bh * DT * (Np / 16) * kFragElems;
+    const size_t koff = (size_t)c.bh * (Np / 32) * KSD * kFragElems;
+    const size_t voff = (size_t)c.bh * DT * (Np / 16) * kFragElems;
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
       const int idx = wave * CPW + q;
-      const int piece = idx % PCS, f = idx / PCS;
+      const int piece = idx % PCS, f2 = idx / PCS;
+      const bool lo = SPLIT && f2 >= KFR + VFR;
+      const int f = lo ? f2 - (KFR + VFR) : f2;
       const T* src;
       if (f < KFR) {
-        src = kbase + ((size_t)(kv0 / 32) * KSD + f) * kFragElems;
+        src = (lo ? KPlo : KP) + koff + ((size_t)(kv0 / 32) * KSD + f) * kFragElems;
       } else {
         const int ff = f - KFR, dt = ff / KK, kk = ff - dt * KK;
-        src = vbase + ((size_t)dt * (Np / 16) + kv0 / 16 + kk) * kFragElems;
+        src = (lo ? VPlo : VP) + voff + ((size_t)dt * (Np / 16) + kv0 / 16 + kk) * kFragElems;
       }
-      dma16(src + piece * (kFragElems / PCS) + lane * (8 / PCS), buf + f * FB + piece * 1024);
+      dma16(src + piece * (kFragElems / PCS) + lane * (8 / PCS), buf + f2 * FB + piece * 1024);
     }
   };
 
-  F qf[KSD], qn[KSD];
+  F qf[KSD], qn[KSD], ql[SPLIT ? KSD : 1];
   auto load_q = [&](const Cur& c, F (&dst)[KSD]) {
     const T* qp = qfrag_of(c);
 #pragma unroll
     for (int kk = 0; kk < KSD; ++kk) dst[kk] = ld_packed(qp + kk * kFragElems, lane);
+    if constexpr (SPLIT) {
+      const T* qlp = QPlo + (qp - QP);
+#pragma unroll
+      for (int kk = 0; kk < KSD; ++kk) ql[kk] = ld_packed(qlp + kk * kFragElems, lane);
+    }
   };
   f32x16 oacc[DT];
   float m_run, l_run;                   // m_run in the exp2 domain (scores * scale_log2e)
@@ -172,8 +187,17 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
       for (int kk = 0; kk < KSD; ++kk)
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-          if constexpr (kPreload) O::mma(s[t], kf[t * KSD + kk], qf[kk]);
-          else O::mma(s[t], ld_packed(reinterpret_cast<const T*>(buf + (t * KSD + kk) * FB), lane), qf[kk]);
+          if constexpr (kPreload) {
+            O::mma(s[t], kf[t * KSD + kk], qf[kk]);
+          } else {
+            const F kh = ld_packed(reinterpret_cast<const T*>(buf + (t * KSD + kk) * FB), lane);
+            O::mma(s[t], kh, qf[kk]);
+            if constexpr (SPLIT) {
+              O::mma(s[t], ld_packed(reinterpret_cast<const T*>(buf + HALF + (t * KSD + kk) * FB), lane),
+                     qf[kk]);
+              O::mma(s[t], kh, ql[kk]);
+            }
+          }
         }
       F vf[kPreload ? VFR : 1];
       if constexpr (kPreload) {
@@ -210,7 +234,7 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
       }
       // p = exp2(s * scale - m); l sums p in fp32, P feeds the product in T
       float lsum = 0.f;
-      F pf[KK];
+      F pf[KK], pl[SPLIT ? KK : 1];
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
 #pragma unroll
@@ -222,6 +246,12 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
             lsum += p[e];
           }
           pf[2 * t + g] = O::from_f32(p);
+          if constexpr (SPLIT) {
+            float r[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[e] = p[e] - bf16_round(p[e]);
+            pl[2 * t + g] = O::from_f32(r);
+          }
         }
       }
       l_run += lsum;
@@ -229,9 +259,18 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
       for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          if constexpr (kPreload) O::mma(oacc[t], vf[t * KK + kk], pf[kk]);
-          else O::mma(oacc[t], ld_packed(reinterpret_cast<const T*>(buf + (KFR + t * KK + kk) * FB), lane),
-                      pf[kk]);
+          if constexpr (kPreload) {
+            O::mma(oacc[t], vf[t * KK + kk], pf[kk]);
+          } else {
+            const F vh = ld_packed(reinterpret_cast<const T*>(buf + (KFR + t * KK + kk) * FB), lane);
+            O::mma(oacc[t], vh, pf[kk]);
+            if constexpr (SPLIT) {
+              O::mma(oacc[t],
+                     ld_packed(reinterpret_cast<const T*>(buf + HALF + (KFR + t * KK + kk) * FB), lane),
+                     pf[kk]);
+              O::mma(oacc[t], vh, pl[kk]);
+            }
+          }
         }
     }
     if (last) {
@@ -246,6 +285,11 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, int 
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = oacc[t][8 * g + e] * inv;
           st_packed(qp + (2 * t + g) * kFragElems, lane, v);
+          if constexpr (SPLIT) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] -= bf16_round(v[e]);
+            st_packed(QPlo + (qp - QP) + (2 * t + g) * kFragElems, lane, v);
+          }
         }
       }
       reset();
@@ -298,25 +342,36 @@ int device_cus() {
   return cus;
 }
 
-template <typename T, int DK, int BQ, int BKV>
+template <typename T, int DK, int BQ, int BKV, bool SPLIT = false>
 int run_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int nqb = (L.seq_len + BQ - 1) / BQ;
   const int n_bh = L.batch * L.n_heads;
   const int units = n_bh * (L.causal ? (nqb + 1) / 2 : nqb);
   // workgroups resident at once: 2 per CU when a stage pair fits 64 KB of LDS
-  constexpr int per_cu = (4 * BKV * DK * (int)sizeof(T) <= 65536) ? 2 : 1;
+  constexpr int per_cu = (4 * BKV * DK * (int)sizeof(T) * (SPLIT ? 2 : 1) <= 65536) ? 2 : 1;
   int grid = device_cus() * per_cu;
   if (units < grid) grid = units;
   const float scale = 1.4426950408889634f / sqrtf((float)DK);
-  hipLaunchKernelGGL((attention_kernel<T, DK, BQ, BKV>), dim3(grid), dim3(BQ * 2), 0, s,
-                     (T*)L.q, (const T*)L.k, (const T*)L.vt, L.seq_len, L.seq_pad, L.n_heads,
-                     L.d_model, L.causal, scale, nqb, n_bh);
+  hipLaunchKernelGGL((attention_kernel<T, DK, BQ, BKV, SPLIT>), dim3(grid), dim3(BQ * 2), 0, s,
+                     (T*)L.q, (const T*)L.k, (const T*)L.vt, (T*)L.q_lo, (const T*)L.k_lo,
+                     (const T*)L.vt_lo, L.seq_len, L.seq_pad, L.n_heads, L.d_model, L.causal, scale,
+                     nqb, n_bh);
   return check_launch("attention", err, n);
 }
 
 template <typename T>
 int dispatch_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int dk = L.d_head, bq = L.block_q, bkv = L.block_kv;
+  if constexpr (sizeof(T) == 2) {
+    if (L.split) {
+      // pairs of fragments double the LDS stage: key/value tiles of 64 keys
+      // (value-neutral: the online softmax is exact for any tiling)
+      if (dk == 64 && bq == 64) return run_attn<T, 64, 64, 64, true>(L, s, err, n);
+      if (dk == 64 && bq == 128) return run_attn<T, 64, 128, 64, true>(L, s, err, n);
+      if (dk == 128 && bq == 64) return run_attn<T, 128, 64, 64, true>(L, s, err, n);
+      if (dk == 128 && bq == 128) return run_attn<T, 128, 128, 64, true>(L, s, err, n);
+    }
+  }
 #define BPT_ATTN(DK_, BQ_, BKV_) \
   if (dk == DK_ && bq == BQ_ && bkv == BKV_) return run_attn<T, DK_, BQ_, BKV_>(L, s, err, n);
   BPT_ATTN(64, 64, 64)

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(PackJob<T> job) {
 }
 
 // Packed region: W_Q, W_K, W_V (one [3d, d] operand), then the epilogue stream
-// holding W_O, W_1 and W_2 (d^2 + 2 d d_ff elements).
+// holding W_O, W_1 and W_2 (d^2 + 2 d d_ff elements); for the staged epilogue
+// W_O, W_1, W_2 in plain fragment order instead.
 template <typename T>
 int pack_all(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int d = L.d_model, f = L.d_ff;
@@ -67,9 +68,15 @@ int pack_all(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   PackJob<T> job{};
   job.fs = FfnStream{d, f};
   const void* srcs[6] = {L.w.w_q, L.w.w_k, L.w.w_v, L.w.w_o, L.w.w_1, L.w.w_2};
+  const bool staged = staged_epilogue(d, L.split);
   T* dsts[6] = {p, p + dd, p + 2 * dd, p + 3 * dd, p + 3 * dd, p + 3 * dd};
   const int rows[6] = {d, d, d, d, f, d}, Ks[6] = {d, d, d, d, d, f};
-  const int orders[6] = {kPlain, kPlain, kPlain, kStreamWO, kStreamW1, kStreamW2};
+  int orders[6] = {kPlain, kPlain, kPlain, kStreamWO, kStreamW1, kStreamW2};
+  if (staged) {   // the staged epilogue's GEMMs take W_O, W_1, W_2 in plain order
+    dsts[4] = p + 4 * dd;
+    dsts[5] = p + 4 * dd + (size_t)f * d;
+    orders[3] = orders[4] = orders[5] = kPlain;
+  }
   job.first_chunk[0] = 0;
   for (int m = 0; m < 6; ++m) {
     job.src[m] = static_cast<const T*>(srcs[m]);

@@ -41,6 +41,7 @@ class Workload:
     w_std_layer_decay: bool = False   # std 0.02 / sqrt(2 l + 1) for layer l (0-based)
     ln_eps: float = 1e-5
     sample_rows: int = 0  # 0 = compare every row; otherwise sampled rows
+    precision: int = 0    # 0: bf16 operands; 1: bf16 (hi, lo) pairs for computed operands
 
     @property
     def rows(self) -> int:
@@ -68,7 +69,7 @@ WORKLOADS = {
                           sample_rows=256),
     "stack4_32k": Workload("stack4_32k", batch=1, seq_len=32768, d_model=4096, n_heads=32,
                            d_ff=16384, causal=True, block_q=128, block_kv=128, dtype="bf16",
-                           n_layers=4, w_std_layer_decay=True, sample_rows=128),
+                           n_layers=4, w_std_layer_decay=True, sample_rows=128, precision=1),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}

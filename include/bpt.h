@@ -80,7 +80,12 @@ typedef struct {
   int32_t dtype;      /* bpt_dtype_t of X, the weights and the LN parameters     */
   int32_t out_dtype;  /* bpt_dtype_t of Z                                        */
   int32_t act;        /* 0 = GELU, tanh form (the only value)                    */
-  int32_t precision;  /* 0 (the only value implemented)                          */
+  int32_t precision;  /* 0: bf16 operands, fp32 accumulation; 1 (BPT_BF16 only):
+                         every operand computed on the GPU (LN outputs, Q, K, V,
+                         P, O, the FFN hidden state) is carried as a pair of bf16
+                         values hi + lo (~16 significant bits), each product
+                         taken over both halves; the FFN then runs staged (see
+                         the workspace note)                                    */
 } bpt_layer_desc_t;
 
 /* Device pointers to one layer's parameters (layouts above). */
@@ -102,7 +107,10 @@ typedef struct {
  * output), K and V^T, each [rows, d_model]; and a copy of the six projection
  * matrices repacked in matrix-core fragment order (4 d_model^2 + 2 d_model d_ff
  * elements). Nothing of size rows x d_ff or seq_len x seq_len is ever part of
- * it. */
+ * it. The staged epilogue (d_model 4096, or precision 1) adds the FFN hidden
+ * state of min(rows, 4096) rows [.., d_ff] and keeps Y fp32 [rows, d_model]
+ * over the K and V^T space; precision 1 doubles every activation buffer (the
+ * lo halves). */
 size_t bpt_layer_workspace_bytes(const bpt_layer_desc_t* desc);
 
 /* Workspace of bpt_stack_fwd: the layer workspace, plus one fp32 residual

@@ -51,21 +51,28 @@ def desc(**kw):
     return bpt.make_desc(**base)
 
 
-def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None):
+def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=False):
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     rows = batch * n
     npad = (n + 127) // 128 * 128
     used = batch * npad
+    rows_pad = up(used)
+    staged = d > 2048 or split  # staged epilogue: K, V^T over rows_pad rows + hidden block
     f = 4 * d if d_ff is None else d_ff
-    tot = 2 * up(up(used) * d * es) + 2 * up(used * d * es)
-    tot += up((4 * d * d + 2 * d * f) * es)
+    kv_rows = rows_pad if staged else used
+    acts = 2 * up(rows_pad * d * es) + 2 * up(kv_rows * d * es)
+    hidden = up(min(rows_pad, 4096) * f * es) if staged else 0
+    tot = acts + up((4 * d * d + 2 * d * f) * es) + hidden
+    if split:                   # lo halves of the bf16 pairs
+        tot += acts + hidden
     if stack_resid:
         tot += up(rows * d * 4)
     return tot
 
 
 @pytest.mark.parametrize("batch,n,d,h,dt", [(2, 200, 256, 4, "bf16"), (1, 131072, 2048, 16, "bf16"),
-                                            (64, 1024, 1024, 16, "bf16"), (1, 77, 128, 2, "f32")])
+                                            (64, 1024, 1024, 16, "bf16"), (1, 77, 128, 2, "f32"),
+                                            (1, 32768, 4096, 32, "bf16"), (3, 300, 4096, 32, "bf16")])
 def test_workspace_formula(batch, n, d, h, dt):
     dsc = desc(batch=batch, seq_len=n, d_model=d, n_heads=h, d_ff=4 * d, dtype=dt,
                block_q=64, block_kv=64)
@@ -76,6 +83,21 @@ def test_workspace_formula(batch, n, d, h, dt):
     assert bpt.stack_workspace_bytes(dsc, 3) == expected_workspace(batch, n, d, es, True)
     dsc.out_dtype = bpt.F32
     assert bpt.stack_workspace_bytes(dsc, 3) == expected_workspace(batch, n, d, es)
+
+
+@pytest.mark.parametrize("batch,n,d,h", [(2, 200, 256, 4), (1, 32768, 4096, 32), (3, 1500, 1024, 16)])
+def test_workspace_formula_bf16_pairs(batch, n, d, h):
+    dsc = desc(batch=batch, seq_len=n, d_model=d, n_heads=h, d_ff=4 * d, precision=1)
+    assert bpt.layer_workspace_bytes(dsc) == expected_workspace(batch, n, d, 2, split=True)
+    dsc.out_dtype = bpt.BF16
+    assert bpt.stack_workspace_bytes(dsc, 4) == expected_workspace(batch, n, d, 2, True, split=True)
+
+
+def test_bf16_pairs_need_bf16_inputs():
+    dsc = desc(dtype="f32", d_model=256, precision=1)
+    assert bpt.layer_workspace_bytes(dsc) == 0
+    assert call_layer(dsc) == 3
+    assert "precision 1" in bpt.last_error()
 
 
 def test_workspace_is_block_shaped_not_ffn_shaped():
@@ -93,6 +115,16 @@ def test_workspace_is_block_shaped_not_ffn_shaped():
         assert act < 14 * nd                          # after-Flash, unfused
     w = synth.WORKLOADS["long_128k"]
     assert bpt.layer_workspace_bytes(bpt.desc_for(w)) < w.seq_len * w.seq_len * 2
+    # the staged epilogue (d 4096) adds the FFN hidden state of 4096 rows only; the
+    # stack runs in bf16 pairs (precision 1), which doubles every activation
+    w = synth.WORKLOADS["stack4_32k"]
+    assert w.precision == 1
+    ws = bpt.layer_workspace_bytes(bpt.desc_for(w))
+    weights = (4 * w.d_model * w.d_model + 2 * w.d_model * w.d_ff) * 2
+    nd = w.rows * w.d_model * 2
+    hidden_block = 4096 * w.d_ff * 2
+    assert ws - weights <= 2 * (4 * nd + hidden_block) + 16 * 256
+    assert hidden_block * 8 == w.rows * w.d_ff * 2      # 1/8 of the [N, d_ff] hidden
 
 
 def call_layer(dsc, x=FAKE, z=FAKE + (1 << 36), ws=FAKE + (2 << 36), nbytes=1 << 40,
@@ -108,7 +140,7 @@ def call_layer(dsc, x=FAKE, z=FAKE + (1 << 36), ws=FAKE + (2 << 36), nbytes=1 <<
     ("batch", -1, 2), ("seq_len", -5, 2), ("d_model", 0, 2), ("n_heads", 0, 2),
     ("n_heads", 3, 2), ("d_ff", 0, 2), ("block_q", 0, 2), ("causal", 2, 2),
     ("ln_eps", 0.0, 2), ("ln_eps", float("nan"), 2), ("ln_eps", float("inf"), 2),
-    ("dtype", 7, 2), ("out_dtype", -1, 2), ("act", 1, 3), ("precision", 1, 3),
+    ("dtype", 7, 2), ("out_dtype", -1, 2), ("act", 1, 3), ("precision", 2, 2),
     ("d_model", 640, 3), ("n_heads", 8, 3),           # d_head 32
     ("block_q", 96, 3), ("block_kv", 256, 3), ("d_ff", 1000, 3),
 ])
@@ -175,8 +207,6 @@ def test_stack_validation():
 
 def test_every_named_workload_is_supported():
     for w in synth.WORKLOADS.values():
-        if w.d_model == 4096:
-            continue  # the 4096-wide stack has no epilogue instance yet
         assert bpt.layer_workspace_bytes(bpt.desc_for(w)) > 0, (w.name, bpt.last_error())
 
 
