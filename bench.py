@@ -256,7 +256,9 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
                    "d_model": w.d_model, "n_heads": w.n_heads, "d_ff": w.d_ff,
                    "causal": w.causal, "block_q": w.block_q, "block_kv": w.block_kv,
-                   "n_layers": w.n_layers, "out_dtype": out_dtype, "parallelism": "none"},
+                   "n_layers": w.n_layers, "out_dtype": out_dtype, "parallelism": "none",
+                   "precision": ("bf16 pairs (hi + lo) for computed operands" if w.precision
+                                 else "bf16 operands")},
         "pct_peak": round(100 * tflops / peak, 2),
         "flops_per_step": total_flops,
         "kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},

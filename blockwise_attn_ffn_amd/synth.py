@@ -17,6 +17,7 @@ float64 view the oracle takes.
 from __future__ import annotations
 
 import dataclasses
+import hashlib
 import math
 
 import numpy as np
@@ -116,6 +117,19 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         layers.append(dict(ln1_g=ln1_g, ln1_b=ln1_b, w_q=wq, w_k=wk, w_v=wv, w_o=wo,
                            ln2_g=ln2_g, ln2_b=ln2_b, w_1=w1, w_2=w2))
     return {"x": x, "layers": layers}
+
+
+LAYER_KEYS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o", "ln2_g", "ln2_b", "w_1", "w_2")
+
+
+def input_digest(inputs: dict) -> str:
+    """SHA-256 over the raw bytes of X and every layer's tensors, in draw order (to
+    check that stored expected values belong to exactly these inputs)."""
+    h = hashlib.sha256()
+    tensors = [inputs["x"]] + [layer[k] for layer in inputs["layers"] for k in LAYER_KEYS]
+    for t in tensors:
+        h.update(t.detach().contiguous().view(-1).view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
