@@ -96,21 +96,35 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
   const T* __restrict__ WP = g.w;
   const T* __restrict__ XP = g.a;
 
-  // Copy k-tile kt into an LDS stage: wave w issues copies [w CPW, (w+1) CPW).
-  auto issue = [&](int kt, unsigned char* buf) {
+  // Copy k-tile kt into an LDS stage: wave w issues copies [w CPW, (w+1) CPW). With
+  // square tiles the first two waves copy W and the other two A, so a wave has one
+  // source base; copy q's byte offset in k-tile 0 is loop-invariant (k-tile kw adds
+  // kw * 4 fragments), and so is its LDS destination.
+  static_assert(TA == TB, "square tiles: waves 0-1 copy W, waves 2-3 copy A");
+  const bool w_copier = wave < 2;
+  uint32_t c_off[CPW];
 #pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int idx = wave * CPW + q;
-      const int piece = idx % PCS, f = idx / PCS;
-      const bool is_a = f < TA * 4;
-      const int ff = is_a ? f : f - TA * 4;
-      const int tile = ff >> 2, ksl = ff & 3;
-      const bool lo = kt >= nk1;
-      const int kw = lo ? kt - nk1 : kt;
-      const size_t frag = (size_t)((is_a ? nt * TA : rt * TB) + tile) * KS + kw * 4 + ksl;
-      const T* src = (is_a ? WP : (lo ? g.a_lo : XP)) + frag * kFragElems + piece * (kFragElems / PCS);
-      dma16(src + lane * (8 / PCS), buf + f * FB + piece * 1024);
-    }
+  for (int q = 0; q < CPW; ++q) {
+    const int idx = wave * CPW + q;
+    const int piece = idx % PCS, f = idx / PCS;
+    const int ff = w_copier ? f : f - TA * 4;
+    const int tile = ff >> 2, ksl = ff & 3;
+    const uint32_t frag = (uint32_t)((w_copier ? nt * TA : rt * TB) + tile) * KS + ksl;
+    c_off[q] = (frag * kFragElems + piece * (kFragElems / PCS)) * (uint32_t)sizeof(T);
+  }
+  const uint32_t lane_off = (uint32_t)lane * 16u;
+  auto issue_one = [&](int kt, unsigned char* buf, int q) __attribute__((always_inline)) {
+    const int idx = wave * CPW + q;
+    const int piece = idx % PCS, f = idx / PCS;
+    const bool lo = kt >= nk1;
+    const uint32_t kw = (uint32_t)(lo ? kt - nk1 : kt);
+    const char* base = reinterpret_cast<const char*>(w_copier ? WP : (lo ? g.a_lo : XP));
+    dma16(base + (c_off[q] + kw * (4u * kFragElems * (uint32_t)sizeof(T)) + lane_off),
+          buf + f * FB + piece * 1024);
+  };
+  auto issue = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) issue_one(kt, buf, q);
   };
 
   f32x16 acc[TN][TR];
@@ -122,10 +136,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
   // swap = false: acc[a][b] = C^T tile (rows: features, cols: tokens);
   // swap = true:  acc[a][b] = C tile   (rows: tokens, cols: features).
   // The fragments of k-step ksl+1 are read from LDS while the products of k-step
-  // ksl run (two register sets), so LDS latency is hidden inside a k-tile.
-  auto compute = [&](const unsigned char* buf, auto swap) {
+  // ksl run (two register sets), so LDS latency is hidden inside a k-tile. The
+  // copies of the next k-tile (has_next) into nbuf are issued among the first
+  // k-step's products, so their address arithmetic runs in the products' shadow.
+  auto compute = [&](const unsigned char* buf, auto swap, auto has_next, int kt_next,
+                     unsigned char* nbuf) __attribute__((always_inline)) {
+    constexpr bool kNext = decltype(has_next)::value;
     F af[2][TN], bfr[2][TR];
-    auto load = [&](int ksl, F (&a_)[TN], F (&b_)[TR]) {
+    auto load = [&](int ksl, F (&a_)[TN], F (&b_)[TR]) __attribute__((always_inline)) {
 #pragma unroll
       for (int a = 0; a < TN; ++a)
         a_[a] = ld_packed(reinterpret_cast<const T*>(buf + ((wn * TN + a) * 4 + ksl) * FB), lane);
@@ -146,24 +164,41 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
         for (int b = 0; b < TR; ++b) {
           if constexpr (decltype(swap)::value) O::mma(acc[a][b], bfr[cs][b], af[cs][a]);
           else O::mma(acc[a][b], af[cs][a], bfr[cs][b]);
+          constexpr int kPer = CPW / (TN * TR) > 0 ? CPW / (TN * TR) : 1;
+          const int q0 = (a * TR + b) * kPer;
+          if (kNext && ksl == 0 && q0 < CPW) {
+#pragma unroll
+            for (int q = 0; q < kPer; ++q)
+              if (q0 + q < CPW) issue_one(kt_next, nbuf, q0 + q);
+          }
         }
+      if (kNext && ksl == 0) {
+#pragma unroll
+        for (int q = TN * TR * (CPW / (TN * TR) > 0 ? CPW / (TN * TR) : 1); q < CPW; ++q)
+          issue_one(kt_next, nbuf, q);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // nk is even (K is a multiple of 128): the two stages alternate with constant names.
-  auto main_loop = [&](auto swap) {
+  // nk is even (K is a multiple of 128): the two stages alternate with constant names;
+  // the last k-tile issues no copies.
+  auto main_loop = [&](auto swap) __attribute__((always_inline)) {
     issue(0, lds0);
-    for (int kt = 0; kt < nk; kt += 2) {
+    for (int kt = 0; kt < nk - 2; kt += 2) {
       wait_vmem();
       __syncthreads();           // stage 0 landed for every wave; stage 1 is free
-      issue(kt + 1, lds1);
-      compute(lds0, swap);
+      compute(lds0, swap, std::true_type{}, kt + 1, lds1);
       wait_vmem();
       __syncthreads();           // stage 1 landed; stage 0 is free
-      if (kt + 2 < nk) issue(kt + 2, lds0);
-      compute(lds1, swap);
+      compute(lds1, swap, std::true_type{}, kt + 2, lds0);
     }
+    wait_vmem();
+    __syncthreads();
+    compute(lds0, swap, std::true_type{}, nk - 1, lds1);
+    wait_vmem();
+    __syncthreads();
+    compute(lds1, swap, std::false_type{}, -1, lds0);
   };
 
   // Non-swapped tiles: lane (hf, rho) holds packed row row0 + ... + r(rho) of its
@@ -296,6 +331,13 @@ namespace {
 template <typename T, int BN, int BM, int MODE>
 int run_gemm(const GemmArgs<T>& g, int n_feat, int rows, hipStream_t s, const char* what, char* err,
              size_t n) {
+  // copy offsets are 32-bit byte offsets from each operand's base
+  const unsigned long long kMaxBytes = 1ull << 32;
+  if ((unsigned long long)n_feat * g.K * sizeof(T) >= kMaxBytes ||
+      (unsigned long long)rows * g.K * sizeof(T) >= kMaxBytes) {
+    set_err(err, n, "%s: an operand of 4 GiB or more is not supported", what);
+    return 1;
+  }
   GemmArgs<T> a = g;
   a.n_tiles_n = n_feat / BN;
   const int ntr = rows / BM;
