@@ -5,7 +5,7 @@ Only the oracle (oracle/) and the seeded input generator (blockwise_attn_ffn_amd
 are called; nothing comes from the GPU path. The file also stores a SHA-256 of
 every input tensor, so the GPU test can check that it regenerated the same inputs.
 
-    python tests/golden/make_stack4_32k.py        # CPU only, ~30 min, ~25 GB RAM
+    python tests/golden/make_stack4_32k.py        # CPU only, ~40 min on 8 cores, ~25 GB RAM
 """
 from __future__ import annotations
 

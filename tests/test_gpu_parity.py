@@ -3,6 +3,8 @@
 Tolerances (Z against the oracle): bf16 operands max|err| <= 2e-2 and relative
 Frobenius <= 5e-3; fp32 both <= 1e-4.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -61,6 +63,26 @@ def test_long_context_sampled_rows():
     got = run_gpu(w, inp, "f32")
     rows = synth.sample_rows(w, w.sample_rows, seed=0)
     check(got[torch.from_numpy(rows)], oracle_rows(w, inp, rows), "bf16", w.name)
+
+
+GOLDEN_STACK = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                            "stack4_32k_rows.npz")
+
+
+def test_stack4_32k_sampled_rows():
+    """The 4-layer, 32768-token, d 4096 stack (bf16 pairs) at its 128 sampled rows,
+    against the oracle's values written by tests/golden/make_stack4_32k.py (every
+    earlier layer in full in float64: too long to recompute here). The stored input
+    digest proves the regenerated inputs are the ones the oracle saw."""
+    w = W["stack4_32k"]
+    say(f"case {w}")
+    g = np.load(GOLDEN_STACK)
+    inp = synth.make_inputs(w, seed=0)
+    assert synth.input_digest(inp) == str(g["input_sha256"]), "inputs differ from the oracle's"
+    rows = synth.sample_rows(w, w.sample_rows, seed=0)
+    assert np.array_equal(rows, g["rows"])
+    got = run_gpu(w, inp, "f32")
+    check(got[torch.from_numpy(rows)], g["z"], "bf16", w.name)
 
 
 # ---------------------------------------------------------------------------

@@ -342,3 +342,15 @@ def test_pins_catch_planted_oracle_mistakes(mutation, monkeypatch):
         monkeypatch.setattr(O, "layer_norm", lambda x_, g, b, eps: orig_ln(x_, g, b, 0.0))
     got = O.layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, eps=1e-2)
     assert np.max(np.abs(got - ref)) > 1e-6, mutation
+
+
+def test_stack4_32k_golden_file_is_well_formed():
+    """The stored oracle rows of the 4-layer, 32768-token stack: the sampled rows the
+    generator draws, one finite d-wide output row each, and an input digest."""
+    from blockwise_attn_ffn_amd import synth
+    w = synth.WORKLOADS["stack4_32k"]
+    g = np.load(os.path.join(os.path.dirname(__file__), "golden", "stack4_32k_rows.npz"))
+    assert np.array_equal(g["rows"], synth.sample_rows(w, w.sample_rows, seed=0))
+    assert g["z"].shape == (w.sample_rows, w.d_model) and g["z"].dtype == np.float64
+    assert np.isfinite(g["z"]).all()
+    assert len(str(g["input_sha256"])) == 64
