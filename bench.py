@@ -47,7 +47,8 @@ KERNEL_SOURCES = {
     "prep": ("k_pack.hip", "k_ln_qkv.hip", "ffn_stream.hpp", "bpt_device.hpp"),
     "qkv": ("k_gemm.hip", "bpt_device.hpp"),
     "attention": ("k_attention.hip", "bpt_device.hpp"),
-    "ffn_epilogue": ("k_ffn.hip", "k_gemm.hip", "ffn_stream.hpp", "bpt_device.hpp"),
+    "ffn_epilogue": ("k_ffn.hip", "k_gemm.hip", "k_ln_qkv.hip", "ffn_stream.hpp", "bpt_device.hpp",
+                     "bpt_internal.h"),
 }
 
 

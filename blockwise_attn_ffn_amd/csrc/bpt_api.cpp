@@ -60,8 +60,8 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   off = round_up(off + used * dm * es, kAlign);
   L.wpack_off = off;  // W_Q, W_K, W_V, W_O, W_1, W_2 back to back, fragment order
   off = round_up(off + (4 * dm * dm + 2 * df * dm) * es, kAlign);
-  L.h_off = off;      // staged epilogue: hidden block [min(rows_pad, 4096), d_ff]
-  const size_t hr = rp < (size_t)bpt::kHiddenBlockRows ? rp : (size_t)bpt::kHiddenBlockRows;
+  L.h_off = off;      // staged epilogue: hidden block [hidden_block_rows, d_ff]
+  const size_t hr = bpt::hidden_block_rows(d->d_model, rp);
   if (staged) off = round_up(off + hr * df * es, kAlign);
   if (split) {        // lo halves, same shapes as the hi ones
     const size_t sizes[5] = {rp * dm * es, rp * dm * es, used * dm * es, used * dm * es, hr * df * es};
@@ -164,7 +164,7 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   if (bpt::staged_epilogue(d->d_model, p.split)) {
     p.ybuf = base + L.k_off;
     p.hbuf = base + L.h_off;
-    p.h_rows = p.rows_pad < bpt::kHiddenBlockRows ? p.rows_pad : bpt::kHiddenBlockRows;
+    p.h_rows = (int)bpt::hidden_block_rows(p.d_model, (size_t)p.rows_pad);
   }
   if (p.split) {
     p.xpack_lo = base + L.lo_off[0];

@@ -54,12 +54,23 @@ struct WorkspaceLayout {
   size_t lo_off[5];   // split: lo halves of xpack, q, k, vt, hidden block
 };
 
-// Widest d_model whose per-tile fp32 accumulator fits the fused epilogue's
-// registers; wider layers use the staged epilogue (one GEMM per step, the FFN
-// hidden state for kHiddenBlockRows rows at a time in the workspace).
-constexpr int kFusedMaxWidth = 2048;
-constexpr int kHiddenBlockRows = 4096;
+// Widest d_model that runs the fused epilogue. Its per-tile fp32 accumulator
+// [rows, d_model] lives in registers, which caps the rows per tile (64 at d 1024,
+// 32 at d 2048), and each weight fragment it streams feeds rows/32 products: at
+// d 2048 that is one product per 1 KB fragment, more weight traffic per CU than
+// L2 delivers, and the staged epilogue measured faster. Wider layers, and
+// precision 1, use the staged epilogue: one GEMM per step, Y in fp32 and the FFN
+// hidden state for a block of rows in the workspace.
+constexpr int kFusedMaxWidth = 1024;
 inline bool staged_epilogue(int d_model, int split = 0) { return split || d_model > kFusedMaxWidth; }
+// Rows of the staged epilogue's hidden block: enough that the W_2 product
+// (rows x d_model) spans 512 output tiles of 256 x 256 (2^25 / d_model, a
+// multiple of 256), at least 4096, at most the padded rows.
+inline size_t hidden_block_rows(int d_model, size_t rows_pad) {
+  size_t r = (((size_t)1 << 25) / (size_t)d_model) / 256 * 256;
+  if (r < 4096) r = 4096;
+  return r < rows_pad ? r : rows_pad;
+}
 
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).
 int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t errlen);

@@ -332,7 +332,6 @@ int dispatch_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
     if (d == 512) return run_ffn<TX, T, TO, 512, 64, 4>(L, s, err, n);
     if (d == 768) return run_ffn<TX, T, TO, 768, 64, 4>(L, s, err, n);
     if (d == 1024) return run_ffn<TX, T, TO, 1024, 64, 4>(L, s, err, n);
-    if (d == 2048) return run_ffn<TX, T, TO, 2048, 32, 4>(L, s, err, n);
   }
   set_err(err, n, "no epilogue kernel for d_model %s%d", "", d);
   return 1;

@@ -107,10 +107,11 @@ typedef struct {
  * output), K and V^T, each [rows, d_model]; and a copy of the six projection
  * matrices repacked in matrix-core fragment order (4 d_model^2 + 2 d_model d_ff
  * elements). Nothing of size rows x d_ff or seq_len x seq_len is ever part of
- * it. The staged epilogue (d_model 4096, or precision 1) adds the FFN hidden
- * state of min(rows, 4096) rows [.., d_ff] and keeps Y fp32 [rows, d_model]
- * over the K and V^T space; precision 1 doubles every activation buffer (the
- * lo halves). */
+ * it. The staged epilogue (d_model above 1024, or precision 1) adds one block
+ * of the FFN hidden state, [h, d_ff] with h = 2^25 / d_model rounded down to a
+ * multiple of 256, at least 4096 and at most rows rounded up to 256 (16384 rows
+ * at d_model 2048), and keeps Y fp32 [rows, d_model] over the K and V^T space;
+ * precision 1 doubles every activation buffer (the lo halves). */
 size_t bpt_layer_workspace_bytes(const bpt_layer_desc_t* desc);
 
 /* Workspace of bpt_stack_fwd: the layer workspace, plus one fp32 residual

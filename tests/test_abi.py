@@ -51,17 +51,24 @@ def desc(**kw):
     return bpt.make_desc(**base)
 
 
+def hidden_rows(d, rows_pad):
+    """Rows of the staged epilogue's hidden block: 2^25 / d rounded down to a
+    multiple of 256 (the W_2 product then spans 512 tiles of 256 x 256), at least
+    4096, at most the padded rows."""
+    return min(rows_pad, max(4096, (2 ** 25 // d) // 256 * 256))
+
+
 def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=False):
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     rows = batch * n
     npad = (n + 127) // 128 * 128
     used = batch * npad
     rows_pad = up(used)
-    staged = d > 2048 or split  # staged epilogue: K, V^T over rows_pad rows + hidden block
+    staged = d > 1024 or split  # staged epilogue: K, V^T over rows_pad rows + hidden block
     f = 4 * d if d_ff is None else d_ff
     kv_rows = rows_pad if staged else used
     acts = 2 * up(rows_pad * d * es) + 2 * up(kv_rows * d * es)
-    hidden = up(min(rows_pad, 4096) * f * es) if staged else 0
+    hidden = up(hidden_rows(d, rows_pad) * f * es) if staged else 0
     tot = acts + up((4 * d * d + 2 * d * f) * es) + hidden
     if split:                   # lo halves of the bf16 pairs
         tot += acts + hidden
@@ -72,7 +79,8 @@ def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=Fals
 
 @pytest.mark.parametrize("batch,n,d,h,dt", [(2, 200, 256, 4, "bf16"), (1, 131072, 2048, 16, "bf16"),
                                             (64, 1024, 1024, 16, "bf16"), (1, 77, 128, 2, "f32"),
-                                            (1, 32768, 4096, 32, "bf16"), (3, 300, 4096, 32, "bf16")])
+                                            (1, 32768, 4096, 32, "bf16"), (3, 300, 4096, 32, "bf16"),
+                                            (2, 5000, 2048, 16, "bf16"), (1, 300, 2048, 16, "bf16")])
 def test_workspace_formula(batch, n, d, h, dt):
     dsc = desc(batch=batch, seq_len=n, d_model=d, n_heads=h, d_ff=4 * d, dtype=dt,
                block_q=64, block_kv=64)
@@ -85,7 +93,8 @@ def test_workspace_formula(batch, n, d, h, dt):
     assert bpt.stack_workspace_bytes(dsc, 3) == expected_workspace(batch, n, d, es)
 
 
-@pytest.mark.parametrize("batch,n,d,h", [(2, 200, 256, 4), (1, 32768, 4096, 32), (3, 1500, 1024, 16)])
+@pytest.mark.parametrize("batch,n,d,h", [(2, 200, 256, 4), (1, 32768, 4096, 32), (3, 1500, 1024, 16),
+                                         (2, 40000, 768, 12)])
 def test_workspace_formula_bf16_pairs(batch, n, d, h):
     dsc = desc(batch=batch, seq_len=n, d_model=d, n_heads=h, d_ff=4 * d, precision=1)
     assert bpt.layer_workspace_bytes(dsc) == expected_workspace(batch, n, d, 2, split=True)
@@ -101,30 +110,33 @@ def test_bf16_pairs_need_bf16_inputs():
 
 
 def test_workspace_is_block_shaped_not_ffn_shaped():
-    """The activation part of the footprint is LN1(X), Q/O, K and V^T (4 N d): below
-    the two [N, 4d] hidden tensors (8 N d) and the page's after-Flash unfused total
-    (6 N d + 8 N d); no [N, N] logits exist."""
+    """The activation part of the footprint is LN1(X), Q/O, K and V^T (4 N d), plus,
+    on the staged epilogue, one block of the FFN hidden state: below the two [N, 4d]
+    hidden tensors (8 N d) and the page's after-Flash unfused total (6 N d + 8 N d);
+    no [N, N] logits exist."""
     for name in ("gpt2_small", "gpt2_medium", "long_128k"):
         w = synth.WORKLOADS[name]
         ws = bpt.layer_workspace_bytes(bpt.desc_for(w))
         weights = (4 * w.d_model * w.d_model + 2 * w.d_model * w.d_ff) * 2
         act = ws - weights
         nd = w.rows * w.d_model * 2
-        assert act <= 4 * nd + 8 * 256 + 256 * w.d_model * 2 * 2
+        staged = w.d_model > 1024
+        hidden_block = hidden_rows(w.d_model, w.rows) * w.d_ff * 2 if staged else 0
+        assert act <= 4 * nd + hidden_block + 8 * 256 + 256 * w.d_model * 2 * 2
         assert act < 2 * w.rows * w.d_ff * 2          # the unfused FFN hidden pair
         assert act < 14 * nd                          # after-Flash, unfused
     w = synth.WORKLOADS["long_128k"]
     assert bpt.layer_workspace_bytes(bpt.desc_for(w)) < w.seq_len * w.seq_len * 2
-    # the staged epilogue (d 4096) adds the FFN hidden state of 4096 rows only; the
-    # stack runs in bf16 pairs (precision 1), which doubles every activation
+    assert hidden_rows(w.d_model, w.rows) * 8 == w.rows   # 1/8 of the [N, d_ff] hidden
+    # the stack runs in bf16 pairs (precision 1), which doubles every activation
     w = synth.WORKLOADS["stack4_32k"]
     assert w.precision == 1
     ws = bpt.layer_workspace_bytes(bpt.desc_for(w))
     weights = (4 * w.d_model * w.d_model + 2 * w.d_model * w.d_ff) * 2
     nd = w.rows * w.d_model * 2
-    hidden_block = 4096 * w.d_ff * 2
+    hidden_block = hidden_rows(w.d_model, w.rows) * w.d_ff * 2
     assert ws - weights <= 2 * (4 * nd + hidden_block) + 16 * 256
-    assert hidden_block * 8 == w.rows * w.d_ff * 2      # 1/8 of the [N, d_ff] hidden
+    assert hidden_block * 4 == w.rows * w.d_ff * 2      # 1/4 of the [N, d_ff] hidden
 
 
 def call_layer(dsc, x=FAKE, z=FAKE + (1 << 36), ws=FAKE + (2 << 36), nbytes=1 << 40,
