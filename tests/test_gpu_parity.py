@@ -118,10 +118,10 @@ def test_each_model_width(d, h):
 @pytest.mark.parametrize("n,batch,d_ff", [(300, 2, 8192), (1500, 3, 4096)])
 def test_staged_epilogue_width_4096_bf16_pairs(n, batch, d_ff):
     """d_model 4096 takes the staged epilogue: Y = X + O W_O, LN2, then the FFN one
-    block of 4096 packed rows at a time. 3 x 1500 tokens span two hidden blocks
-    (the last sequence's rows past position 1024 fall in the second). At this width
-    the bf16 rounding of the computed operands alone exceeds max|err| 2e-2, so it
-    runs in precision 1 (bf16 pairs)."""
+    block of 8192 packed rows at a time (these shapes fit one block; several blocks
+    run in the stack4_32k and long-context tests, a ragged last block in the d 2048
+    test below). At this width the bf16 rounding of the computed operands alone
+    exceeds max|err| 2e-2, so it runs in precision 1 (bf16 pairs)."""
     w = small(batch=batch, seq_len=n, d_model=4096, n_heads=32, d_ff=d_ff, precision=1)
     say(f"case {w}")
     inp = synth.make_inputs(w, seed=6)
@@ -132,6 +132,20 @@ def test_staged_epilogue_width_4096_bf16_pairs(n, batch, d_ff):
         rows = synth.sample_rows(w, 48, seed=6)
         assert rows.max() == w.rows - 1
         check(got[torch.from_numpy(rows)], oracle_rows(w, inp, rows), "bf16", f"d=4096 pairs n={n}")
+
+
+def test_staged_epilogue_width_2048_ragged_hidden_block():
+    """d_model 2048 runs the staged epilogue with hidden blocks of 16384 packed rows:
+    3 x 6000 tokens pad to 3 x 6016 -> 18176 rows, so the FFN runs one full block and
+    a ragged one of 1792 rows. The sampled rows include both sides of the boundary
+    (packed row 16384 is sequence 2, position 4352) and the last row."""
+    w = small(batch=3, seq_len=6000, d_model=2048, n_heads=16, d_ff=8192, block_kv=64)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=8)
+    got = run_gpu(w, inp)
+    edge = [2 * 6000 + 4351, 2 * 6000 + 4352, 2 * 6000 + 5999]
+    rows = np.union1d(synth.sample_rows(w, 40, seed=8), np.asarray(edge, np.int64))
+    check(got[torch.from_numpy(rows)], oracle_rows(w, inp, rows), "bf16", "d=2048 staged ragged")
 
 
 def test_staged_epilogue_width_4096_plain_bf16():
