@@ -130,24 +130,44 @@ __global__ __launch_bounds__(512) void ln_pack_lds_kernel(const TX* __restrict__
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tile = blockIdx.x;
   const int nch = d >> 3;
-#pragma unroll 2
+  // all four rows of this wave are loaded before any arithmetic (four rows of
+  // loads in flight per wave), and the LN gain and bias once per wave
+  float v[4][CPL][8], g[CPL][8], b[CPL][8];
+  bool live[4];
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = wave + 8 * i, row = tile * 32 + r;
+    const int row = tile * 32 + wave + 8 * i;
     const int bi = row / Np, pos = row - bi * Np;
-    const bool live = bi < B && pos < N;
-    float v[CPL][8];
-    if (live) {
-      const TX* xr = X + ((size_t)bi * N + pos) * d;
+    live[i] = bi < B && pos < N;
+    const TX* xr = X + ((size_t)bi * N + pos) * d;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (live[i] && c < nch) {
+        load8_f32(xr + 8 * c, v[i][j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][j][e] = 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nch) {
+      load8_f32(ln_g + 8 * c, g[j]);
+      load8_f32(ln_b + 8 * c, b[j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave + 8 * i;
+    if (live[i]) {
       float sum = 0.f;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
-        if (c < nch) {
-          load8_f32(xr + 8 * c, v[j]);
+      for (int j = 0; j < CPL; ++j)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sum += v[j][e];
-        }
-      }
+        for (int e = 0; e < 8; ++e) sum += v[i][j][e];   // chunks past d hold 0
       const float mean = wave_sum(sum) / (float)d;
       float q = 0.f;
 #pragma unroll
@@ -156,7 +176,7 @@ __global__ __launch_bounds__(512) void ln_pack_lds_kernel(const TX* __restrict__
         if (c < nch) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float t = v[j][e] - mean;
+            const float t = v[i][j][e] - mean;
             q += t * t;
           }
         }
@@ -166,24 +186,16 @@ __global__ __launch_bounds__(512) void ln_pack_lds_kernel(const TX* __restrict__
       for (int j = 0; j < CPL; ++j) {
         const int c = lane + 64 * j;
         if (c < nch) {
-          float g[8], b[8];
-          load8_f32(ln_g + 8 * c, g);
-          load8_f32(ln_b + 8 * c, b);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[j][e] = (v[j][e] - mean) * rstd * g[e] + b[e];
+          for (int e = 0; e < 8; ++e) v[i][j][e] = (v[i][j][e] - mean) * rstd * g[j][e] + b[j][e];
         }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
     }
     // chunk c (k = 8c .. 8c+7) of row r: fragment c/2, slot 32 (c&1) + pi(r)
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
-      if (c < nch) st_packed(tile_lds + (size_t)(c >> 1) * kFragElems, 32 * (c & 1) + pi_row(r), v[j]);
+      if (c < nch) st_packed(tile_lds + (size_t)(c >> 1) * kFragElems, 32 * (c & 1) + pi_row(r), v[i][j]);
     }
   }
   __syncthreads();
