@@ -243,9 +243,19 @@ int launch_ln_qkv(const LayerLaunch& L, hipStream_t s, char* err, size_t n, int 
 // into pi-ordered packed fragments in the LN1 operand's buffer.
 int launch_ln_rows(const LayerLaunch& L, const void* y, int rows, hipStream_t s, char* err, size_t n) {
   const int d = L.d_model;
+  // every packed row is treated as live: sequences of Np rows, Np of them real
+  if (d <= 2048 && !L.split) {   // Y read once through LDS (tile [32, d] in bf16)
+    auto k = d <= 512 ? ln_pack_lds_kernel<float, bf16, 1>
+                      : (d <= 1024 ? ln_pack_lds_kernel<float, bf16, 2> : ln_pack_lds_kernel<float, bf16, 4>);
+    const size_t smem = (size_t)32 * d * sizeof(bf16);
+    if (set_smem(k, smem, err, n)) return 1;
+    hipLaunchKernelGGL(k, dim3(rows / 32), dim3(512), smem, s, (const float*)y,
+                       (const bf16*)L.w.ln2_g, (const bf16*)L.w.ln2_b, (bf16*)L.xpack,
+                       rows / L.seq_pad, L.seq_pad, L.seq_pad, d, L.ln_eps);
+    return check_launch("ln2_rows", err, n);
+  }
   auto k = d <= 1024 ? ln_pack_kernel<float, bf16, 2>
                      : (d <= 2048 ? ln_pack_kernel<float, bf16, 4> : ln_pack_kernel<float, bf16, 8>);
-  // every packed row is treated as live: sequences of Np rows, Np of them real
   hipLaunchKernelGGL(k, dim3(rows / 32), dim3(256), 0, s, (const float*)y, (const bf16*)L.w.ln2_g,
                      (const bf16*)L.w.ln2_b, (bf16*)L.xpack, (bf16*)L.xpack_lo, rows / L.seq_pad,
                      L.seq_pad, L.seq_pad, d, L.ln_eps);
