@@ -121,49 +121,38 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
     return QP + ((size_t)((bi * Np + c.qb * BQ + wave * 32) >> 5) * (d / 16) + head * KSD) * kFragElems;
   };
   // copy key/value block c.kb of c.bh into an LDS stage (K fragments, then V
-  // fragments; with SPLIT the lo fragments follow in the same order). At d_k 64
-  // (bf16) every wave's copies are of one kind (K or V), so a wave has one source
-  // base per block and copy q's byte offset from it is fixed for the whole kernel
-  // (measured 6% faster there; at d_k 128 the offsets' registers cost more than
-  // the address arithmetic they save, and it runs the per-copy form).
-  constexpr bool kOneKind = DK <= 64 && !SPLIT && sizeof(T) == 2 && (KFR * PCS) % CPW == 0 &&
-                            (VFR * PCS) % CPW == 0;
-  const int f_first = wave * CPW / PCS;                    // first fragment slot of this wave
+  // fragments; with SPLIT the lo fragments follow in the same order). Where every
+  // wave's copies are of one kind (K or V, hi or lo; bf16), a wave takes one
+  // branch per block and its copy sources are a base plus offsets that are
+  // compile-time multiples of the fragment size and of one V row stride. Measured:
+  // 10% faster with bf16 pairs, neutral at d_k 64; plain d_k 128 runs 9% faster
+  // with the per-copy form below, whose longer copy section keeps the two
+  // workgroups of a CU out of phase, and keeps it.
+  constexpr bool kOneKind = sizeof(T) == 2 && (DK <= 64 || SPLIT) && CPW % (BKV / 16) == 0 &&
+                            KFR % CPW == 0 && VFR % CPW == 0;
+  const int f_first = wave * CPW;                          // first fragment slot of this wave
   const bool c_lo = SPLIT && f_first >= KFR + VFR;
-  const bool c_k = (c_lo ? f_first - (KFR + VFR) : f_first) < KFR;
-  uint32_t c_off[kOneKind ? CPW : 1];
-  if constexpr (kOneKind) {
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int idx = wave * CPW + q;
-      const int piece = idx % PCS, f2 = idx / PCS;
-      const int f = c_lo ? f2 - (KFR + VFR) : f2;
-      uint32_t frag;
-      if (c_k) {
-        frag = (uint32_t)f;
-      } else {
-        const int ff = f - KFR, dt = ff / KK, kk = ff - dt * KK;
-        frag = (uint32_t)dt * (uint32_t)(Np / 16) + (uint32_t)kk;
-      }
-      c_off[q] = (frag * kFragElems + piece * (kFragElems / PCS)) * (uint32_t)sizeof(T);
-    }
-  }
+  const int f_kind = c_lo ? f_first - (KFR + VFR) : f_first;   // slot within its half
+  const bool c_k = f_kind < KFR;
   const uint32_t lane_off = (uint32_t)lane * 16u;
   auto issue = [&](const Cur& c, unsigned char* buf) __attribute__((always_inline)) {
     const int kv0 = c.kb * BKV;
     if constexpr (kOneKind) {
-      const T* base;
+      unsigned char* dst = buf + f_first * FB;
       if (c_k) {
-        base = (c_lo ? KPlo : KP) + ((size_t)c.bh * (Np / 32) + kv0 / 32) * KSD * kFragElems;
-      } else {
-        base = (c_lo ? VPlo : VP) + ((size_t)c.bh * DT * (Np / 16) + kv0 / 16) * kFragElems;
-      }
-      const char* b8 = reinterpret_cast<const char*>(base);
+        const char* kb = reinterpret_cast<const char*>(
+            (c_lo ? KPlo : KP) + ((size_t)c.bh * (Np / 32) + kv0 / 32) * KSD * kFragElems) +
+            (size_t)f_kind * FB;
 #pragma unroll
-      for (int q = 0; q < CPW; ++q) {
-        const int idx = wave * CPW + q;
-        const int piece = idx % PCS, f2 = idx / PCS;
-        dma16(b8 + (c_off[q] + lane_off), buf + f2 * FB + piece * 1024);
+        for (int q = 0; q < CPW; ++q) dma16(kb + q * FB + lane_off, dst + q * FB);
+      } else {
+        // V fragment ff = f_kind - KFR + q: feature tile ff / KK, key step ff % KK
+        const size_t S = (size_t)(Np / 16) * FB;          // bytes per feature tile
+        const char* vb = reinterpret_cast<const char*>(
+            (c_lo ? VPlo : VP) + ((size_t)c.bh * DT * (Np / 16) + kv0 / 16) * kFragElems) +
+            (size_t)((f_kind - KFR) / KK) * S;
+#pragma unroll
+        for (int q = 0; q < CPW; ++q) dma16(vb + (q / KK) * S + (q % KK) * FB + lane_off, dst + q * FB);
       }
     } else {
       const size_t koff = (size_t)c.bh * (Np / 32) * KSD * kFragElems;
