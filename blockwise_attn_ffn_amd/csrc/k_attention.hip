@@ -16,6 +16,8 @@
 // O^T += V^T P^T on the matrix cores, so each lane owns one query row: row max and
 // row sum are in-lane plus one exchange between the two lane halves. K and V
 // blocks are copied global -> LDS by the LDS-DMA path into two static stages.
+#include <type_traits>
+
 #include "bpt_device.hpp"
 #include "bpt_launch.hpp"
 
@@ -371,6 +373,283 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two-group schedule (bf16, d_k 128, query blocks of 128 rows). One workgroup of
+// 8 waves per CU takes a pair of adjacent query blocks ("super-block") that share
+// one key/value stream: group 0 (waves 0-3) the even block, group 1 (waves 4-7)
+// the odd one, 32 query rows per wave as above. The two groups run half a step
+// apart: while one group multiplies (P V of the previous key/value block, then S
+// of the current one), the other runs the softmax of its scores, so each SIMD,
+// which holds one wave of each group, has matrix-core and vector work in flight
+// together. K and V have two LDS buffers each; at the start of step k group 0
+// copies K of visit k+1 and group 1 copies V of visit k, and both land before
+// step k+1, when they are first read. Work units are pairs of super-blocks
+// (S-1-p, p) with the causal mask, as for the one-group kernel.
+// ---------------------------------------------------------------------------
+template <int DK, int BKV>
+__global__ __launch_bounds__(512, 1) void attention_pair_kernel(
+    bf16* QP, const bf16* __restrict__ KP, const bf16* __restrict__ VP, int N, int Np, int H,
+    int d, int causal, float scale_log2e, int nqb, int n_bh) {
+  using O = Op<bf16>;
+  using F = O::frag;
+  constexpr int BQ = 128, NWG = 4, FB = 1024;
+  constexpr int KSD = DK / 16;                 // k-steps over d_k
+  constexpr int KT = BKV / 32;                 // key tiles per block (S^T tiles)
+  constexpr int DT = DK / 32;                  // feature tiles (O^T tiles)
+  constexpr int KK = BKV / 16;                 // key k-steps per block
+  constexpr int KFR = KT * KSD, VFR = DT * KK; // fragments per block
+  constexpr int KCPW = KFR / NWG;              // K copies per group-0 wave
+  static_assert(VFR / NWG == KK, "a group-1 wave copies one feature tile of V");
+  __shared__ __align__(16) unsigned char kbuf[2][KFR * FB];
+  __shared__ __align__(16) unsigned char vbuf[2][VFR * FB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wq = wave & 3;
+  const int rho = lane & 31, hf = lane >> 5;
+  const uint32_t lane_off = (uint32_t)lane * 16u;
+
+  const int nsb = (nqb + 1) / 2;               // super-blocks
+  const int n_kvb = (N + BKV - 1) / BKV;
+  const int n_pairs = causal ? (nsb + 1) / 2 : nsb;
+  const int n_units = n_bh * n_pairs;
+  int part = 0, nparts = 1, j = blockIdx.x, M = gridDim.x;
+  if ((gridDim.x & 7) == 0) {
+    part = blockIdx.x & 7; nparts = 8; j = blockIdx.x >> 3; M = gridDim.x >> 3;
+  }
+  const int u_hi = (int)((long long)n_units * (part + 1) / nparts);
+
+  // visit cursor over super-blocks (wave-uniform), as in the one-group kernel
+  struct Cur { int u, w, sb, kb, kend, bh; };
+  auto sblock = [&](int u, int w) {
+    const int p = u % n_pairs;
+    if (!causal) return w == 0 ? p : -1;
+    const int qa = nsb - 1 - p;
+    return w == 0 ? qa : (p != qa ? p : -1);
+  };
+  auto start_half = [&](Cur& c) {
+    c.sb = sblock(c.u, c.w);
+    c.kb = 0;
+    c.kend = causal ? (min(c.sb * 2 * BQ + 2 * BQ, N) - 1) / BKV + 1 : n_kvb;
+    c.bh = c.u / n_pairs;
+  };
+  auto advance = [&](Cur& c) {          // c.u >= u_hi afterwards: no more visits
+    if (c.kb + 1 < c.kend) { ++c.kb; return; }
+    if (c.w == 0 && sblock(c.u, 1) >= 0) c.w = 1;
+    else { c.u += M; c.w = 0; }
+    if (c.u < u_hi) start_half(c);
+  };
+  Cur ck;
+  ck.u = (int)((long long)n_units * part / nparts) + j;
+  ck.w = 0;
+  if (ck.u >= u_hi) return;
+  start_half(ck);
+
+  // this wave's query block in visit c's super-block (-1 if the block is past the end)
+  auto my_qb = [&](const Cur& c) { const int qb = 2 * c.sb + grp; return qb < nqb ? qb : -1; };
+  auto qfrag_of = [&](const Cur& c, int qb) {
+    const int bi = c.bh / H, head = c.bh - bi * H;
+    return QP + ((size_t)((bi * Np + qb * BQ + wq * 32) >> 5) * (d / 16) + head * KSD) * kFragElems;
+  };
+  F qf[KSD];
+  auto load_q = [&](const Cur& c) __attribute__((always_inline)) {
+    const int qb = my_qb(c);
+    if (qb < 0) return;
+    const bf16* qp = qfrag_of(c, qb);
+#pragma unroll
+    for (int kk = 0; kk < KSD; ++kk) qf[kk] = ld_packed(qp + kk * kFragElems, lane);
+  };
+  // group 0 copies visit c's K block, group 1 its V block (one feature tile per wave)
+  auto issue_k = [&](const Cur& c, unsigned char* buf) __attribute__((always_inline)) {
+    const char* src = reinterpret_cast<const char*>(
+        KP + (((size_t)c.bh * (Np / 32) + c.kb * BKV / 32) * KSD + wq * KCPW) * kFragElems);
+#pragma unroll
+    for (int q = 0; q < KCPW; ++q) dma16(src + q * FB + lane_off, buf + (wq * KCPW + q) * FB);
+  };
+  auto issue_v = [&](const Cur& c, unsigned char* buf) __attribute__((always_inline)) {
+    const char* src = reinterpret_cast<const char*>(
+        VP + (((size_t)c.bh * DT + wq) * (Np / 16) + c.kb * BKV / 16) * kFragElems);
+#pragma unroll
+    for (int q = 0; q < KK; ++q) dma16(src + q * FB + lane_off, buf + (wq * KK + q) * FB);
+  };
+
+  f32x16 oacc[DT], s[KT];
+  F pf[KK];
+  float m_run = -INFINITY, l_run = 0.f;
+  bool s_valid = false, p_valid = false;
+  auto reset = [&]() {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+  reset();
+
+  // product step of visit k: P V of the previous visit (V in vb), O of the previous
+  // half when that visit was its last, then S of visit k (K in kb)
+  auto mstep = [&](const Cur& cp, bool has_p, const Cur& c, bool has_c, const unsigned char* kb,
+                   const unsigned char* vb) __attribute__((always_inline)) {
+    // the multiplying wave of a SIMD is issued ahead of the one in its softmax
+    // (measured 6% faster than equal priorities)
+    __builtin_amdgcn_s_setprio(1);
+    if (p_valid) {
+      // V fragments of key step kk+1 are read while the products of kk run
+      F va[2][DT];
+      auto ldv = [&](int kk, F (&dst)[DT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          dst[t] = ld_packed(reinterpret_cast<const bf16*>(vb + (t * KK + kk) * FB), lane);
+      };
+      ldv(0, va[0]);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) ldv(kk + 1, va[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) O::mma(oacc[t], va[kk & 1][t], pf[kk]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      p_valid = false;
+    }
+    if (has_p && cp.kb == cp.kend - 1) {
+      const int qb = my_qb(cp);
+      if (qb >= 0) {
+        // register group g of feature tile t holds features t*32 + 16g + 8hf + [0, 8)
+        bf16* qp = qfrag_of(cp, qb);
+        const float inv = 1.0f / pair_sum(l_run);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = oacc[t][8 * g + e] * inv;
+            st_packed(qp + (2 * t + g) * kFragElems, lane, v);
+          }
+        }
+      }
+      reset();
+    }
+    s_valid = false;
+    if (has_c) {
+      const int qb = my_qb(c);
+      const int wave_q_first = qb * BQ + wq * 32;
+      // a wave whose 32 rows all precede this block has nothing to add
+      if (qb >= 0 && !(causal && c.kb * BKV > wave_q_first + 31)) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t) s[t] = f32x16{};
+        // K fragments of k-step kk+1 are read while the products of kk run
+        F ka[2][KT];
+        auto ldk = [&](int kk, F (&dst)[KT]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int t = 0; t < KT; ++t)
+            dst[t] = ld_packed(reinterpret_cast<const bf16*>(kb + (t * KSD + kk) * FB), lane);
+        };
+        ldk(0, ka[0]);
+#pragma unroll
+        for (int kk = 0; kk < KSD; ++kk) {
+          if (kk + 1 < KSD) ldk(kk + 1, ka[(kk + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int t = 0; t < KT; ++t) O::mma(s[t], ka[kk & 1][t], qf[kk]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        s_valid = true;
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // softmax step of visit c: mask, running maximum (lazy rescale), P and l
+  auto vstep = [&](const Cur& c) __attribute__((always_inline)) {
+    if (!s_valid) return;
+    const int kv0 = c.kb * BKV;
+    const int wave_q_first = my_qb(c) * BQ + wq * 32, qpos = wave_q_first + rho;
+    // mask future keys and keys past the end (only blocks that can contain them):
+    // register i of tile t holds key kv0 + t*32 + (i&8)*2 + 8hf + (i&7)
+    if ((kv0 + BKV > N) || (causal && kv0 + BKV - 1 > wave_q_first)) {
+      const int lim = (causal ? min(qpos, N - 1) : N - 1) - kv0 - 8 * hf;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (t * 32 + (i & 8) * 2 + (i & 7) > lim) s[t][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+    mx = pair_max(mx) * scale_log2e;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(s[t][8 * g + e], scale_log2e, -m_run));
+          lsum += p[e];
+        }
+        pf[2 * t + g] = O::from_f32(p);
+      }
+    }
+    l_run += lsum;
+    s_valid = false;
+    p_valid = true;
+  };
+
+  // step k: [even half] group 0 multiplies for visit k, group 1 runs the softmax of
+  // visit k-1; [odd half] group 0 the softmax of visit k, group 1 multiplies for k.
+  // A final step with no visit k finishes P V and O of the last visit. Each group
+  // runs its own copy of the loop (the phase order is a compile-time constant);
+  // both execute the same sequence of barriers.
+  auto run = [&](auto group) __attribute__((always_inline)) {
+    constexpr int G = decltype(group)::value;
+    load_q(ck);
+    if constexpr (G == 0) issue_k(ck, kbuf[0]);
+    Cur cp = ck;                     // visit k-1 (valid from k = 1)
+    Cur cn = ck;                     // visit k+1
+    advance(cn);
+    for (int k = 0;; ++k) {
+      const bool has_k = ck.u < u_hi, has_n = cn.u < u_hi, has_p = k > 0;
+      wait_vmem();
+      __syncthreads();               // K(k) and V(k-1) have landed
+      // a new half starts at visit k: both groups are done with the old Q (their S
+      // of visit k-1 ran in the previous step), so its Q is read now, ahead of the
+      // copies (waiting for it does not wait for them)
+      if (has_p && has_k && cp.kb == cp.kend - 1) load_q(ck);
+      if constexpr (G == 0) {
+        if (has_n) issue_k(cn, kbuf[(k + 1) & 1]);
+        mstep(cp, has_p, ck, has_k, kbuf[k & 1], vbuf[(k + 1) & 1]);
+      } else {
+        if (has_k) issue_v(ck, vbuf[k & 1]);
+        if (has_p) vstep(cp);
+      }
+      __builtin_amdgcn_s_barrier();  // half step: no copy is waited for here
+      if constexpr (G == 0) {
+        if (has_k) vstep(ck);
+      } else {
+        mstep(cp, has_p, ck, has_k, kbuf[k & 1], vbuf[(k + 1) & 1]);
+      }
+      if (!has_k) break;
+      cp = ck;
+      ck = cn;
+      advance(cn);
+    }
+  };
+  if (grp == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
+}
+
 namespace {
 
 int device_cus() {
@@ -402,10 +681,29 @@ int run_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   return check_launch("attention", err, n);
 }
 
+template <int DK, int BKV>
+int run_attn_pair(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
+  const int nqb = (L.seq_len + 127) / 128;
+  const int n_bh = L.batch * L.n_heads;
+  const int nsb = (nqb + 1) / 2;
+  const int units = n_bh * (L.causal ? (nsb + 1) / 2 : nsb);
+  int grid = device_cus();
+  if (units < grid) grid = units;
+  const float scale = 1.4426950408889634f / sqrtf((float)DK);
+  hipLaunchKernelGGL((attention_pair_kernel<DK, BKV>), dim3(grid), dim3(512), 0, s, (bf16*)L.q,
+                     (const bf16*)L.k, (const bf16*)L.vt, L.seq_len, L.seq_pad, L.n_heads,
+                     L.d_model, L.causal, scale, nqb, n_bh);
+  return check_launch("attention", err, n);
+}
+
 template <typename T>
 int dispatch_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int dk = L.d_head, bq = L.block_q, bkv = L.block_kv;
   if constexpr (sizeof(T) == 2) {
+    if (!L.split && dk == 128 && bq == 128) {
+      if (bkv == 64) return run_attn_pair<128, 64>(L, s, err, n);
+      if (bkv == 128) return run_attn_pair<128, 128>(L, s, err, n);
+    }
     if (L.split) {
       // pairs of fragments double the LDS stage: key/value tiles of 64 keys
       // (value-neutral: the online softmax is exact for any tiling)

@@ -107,6 +107,20 @@ def test_small_bf16_dk128_ragged(n):
     check(run_gpu(w, inp), oracle_full(w, inp), "bf16", f"small dk128 n={n}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("bkv", [64, 128])
+@pytest.mark.parametrize("n", [300, 640])
+def test_dk128_query_block_pairs(causal, bkv, n):
+    """d_k = 128 with 128-row query blocks runs the two-group schedule: adjacent
+    query blocks share one key/value stream, half a step apart. 300 and 640 tokens
+    give 3 and 5 query blocks, so the last pair has one block only; ragged last
+    key/value block; both masks and both key/value block sizes."""
+    w = small(batch=2, seq_len=n, n_heads=2, block_q=128, block_kv=bkv, causal=causal)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=9)
+    check(run_gpu(w, inp), oracle_full(w, inp), "bf16", f"dk128 pairs n={n} bkv={bkv} causal={causal}")
+
+
 @pytest.mark.parametrize("d,h", [(512, 8), (768, 12), (1024, 16), (2048, 16)])
 def test_each_model_width(d, h):
     w = small(batch=1, seq_len=136, d_model=d, n_heads=h, d_ff=4 * d)
