@@ -399,7 +399,9 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
   constexpr int KK = BKV / 16;                 // key k-steps per block
   constexpr int KFR = KT * KSD, VFR = DT * KK; // fragments per block
   constexpr int KCPW = KFR / NWG;              // K copies per group-0 wave
-  static_assert(VFR / NWG == KK, "a group-1 wave copies one feature tile of V");
+  constexpr int VCPW = VFR / NWG;              // V copies per group-1 wave
+  static_assert(KFR % NWG == 0 && VFR % NWG == 0 && VCPW <= KK && KK % VCPW == 0,
+                "a group-1 wave copies consecutive key steps of one feature tile of V");
   __shared__ __align__(16) unsigned char kbuf[2][KFR * FB];
   __shared__ __align__(16) unsigned char vbuf[2][VFR * FB];
 
@@ -459,7 +461,8 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
 #pragma unroll
     for (int kk = 0; kk < KSD; ++kk) qf[kk] = ld_packed(qp + kk * kFragElems, lane);
   };
-  // group 0 copies visit c's K block, group 1 its V block (one feature tile per wave)
+  // group 0 copies visit c's K block, group 1 its V block (VCPW consecutive key
+  // steps of one feature tile per wave)
   auto issue_k = [&](const Cur& c, unsigned char* buf) __attribute__((always_inline)) {
     const char* src = reinterpret_cast<const char*>(
         KP + (((size_t)c.bh * (Np / 32) + c.kb * BKV / 32) * KSD + wq * KCPW) * kFragElems);
@@ -467,10 +470,11 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     for (int q = 0; q < KCPW; ++q) dma16(src + q * FB + lane_off, buf + (wq * KCPW + q) * FB);
   };
   auto issue_v = [&](const Cur& c, unsigned char* buf) __attribute__((always_inline)) {
+    const int dt = wq * VCPW / KK, kk0 = wq * VCPW % KK;
     const char* src = reinterpret_cast<const char*>(
-        VP + (((size_t)c.bh * DT + wq) * (Np / 16) + c.kb * BKV / 16) * kFragElems);
+        VP + (((size_t)c.bh * DT + dt) * (Np / 16) + c.kb * BKV / 16 + kk0) * kFragElems);
 #pragma unroll
-    for (int q = 0; q < KK; ++q) dma16(src + q * FB + lane_off, buf + (wq * KK + q) * FB);
+    for (int q = 0; q < VCPW; ++q) dma16(src + q * FB + lane_off, buf + (wq * VCPW + q) * FB);
   };
 
   f32x16 oacc[DT], s[KT];
@@ -700,10 +704,13 @@ template <typename T>
 int dispatch_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const int dk = L.d_head, bq = L.block_q, bkv = L.block_kv;
   if constexpr (sizeof(T) == 2) {
+    // two-group schedule for d_k 128 only: at d_k 64 the softmax half step is
+    // about twice the product half step and the one-group kernel measured faster
     if (!L.split && dk == 128 && bq == 128) {
       if (bkv == 64) return run_attn_pair<128, 64>(L, s, err, n);
       if (bkv == 128) return run_attn_pair<128, 128>(L, s, err, n);
     }
+
     if (L.split) {
       // pairs of fragments double the LDS stage: key/value tiles of 64 keys
       // (value-neutral: the online softmax is exact for any tiling)

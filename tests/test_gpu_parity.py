@@ -109,12 +109,13 @@ def test_small_bf16_dk128_ragged(n):
 
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("bkv", [64, 128])
-@pytest.mark.parametrize("n", [300, 640])
+@pytest.mark.parametrize("n", [1, 129, 300, 640])
 def test_dk128_query_block_pairs(causal, bkv, n):
     """d_k = 128 with 128-row query blocks runs the two-group schedule: adjacent
-    query blocks share one key/value stream, half a step apart. 300 and 640 tokens
-    give 3 and 5 query blocks, so the last pair has one block only; ragged last
-    key/value block; both masks and both key/value block sizes."""
+    query blocks share one key/value stream, half a step apart. 1 token (one query
+    block, one key/value block), 129 (a pair whose second block holds one row), 300
+    and 640 tokens (3 and 5 query blocks, so the last pair has one block only);
+    ragged last key/value block; both masks and both key/value block sizes."""
     w = small(batch=2, seq_len=n, n_heads=2, block_q=128, block_kv=bkv, causal=causal)
     say(f"case {w}")
     inp = synth.make_inputs(w, seed=9)
