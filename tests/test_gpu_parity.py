@@ -122,6 +122,16 @@ def test_dk128_query_block_pairs(causal, bkv, n):
     check(run_gpu(w, inp), oracle_full(w, inp), "bf16", f"dk128 pairs n={n} bkv={bkv} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("bkv", [64, 128])
+def test_small_bf16_dk128_block_q_64(causal, bkv):
+    """d_k = 128 with 64-row query blocks (the one-group kernel at d_k 128), ragged."""
+    w = small(seq_len=200, n_heads=2, block_q=64, block_kv=bkv, causal=causal)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=10)
+    check(run_gpu(w, inp), oracle_full(w, inp), "bf16", f"dk128 bq64 bkv={bkv} causal={causal}")
+
+
 @pytest.mark.parametrize("d,h", [(512, 8), (768, 12), (1024, 16), (2048, 16)])
 def test_each_model_width(d, h):
     w = small(batch=1, seq_len=136, d_model=d, n_heads=h, d_ff=4 * d)
@@ -179,7 +189,8 @@ def test_staged_epilogue_width_4096_plain_bf16():
     assert rf <= 5e-3 and mx <= 4.5e-2
 
 
-@pytest.mark.parametrize("d,h,causal", [(256, 4, True), (512, 8, False), (1024, 16, True)])
+@pytest.mark.parametrize("d,h,causal", [(256, 4, True), (512, 8, False), (1024, 16, True),
+                                         (2048, 16, True)])
 def test_bf16_pairs_small(d, h, causal):
     """precision 1 at small widths: the staged epilogue and the paired attention,
     ragged lengths; the error falls well below plain bf16's."""
@@ -188,6 +199,27 @@ def test_bf16_pairs_small(d, h, causal):
     inp = synth.make_inputs(w, seed=7)
     mx, rf = check(run_gpu(w, inp), oracle_full(w, inp), "bf16", f"pairs d={d}")
     assert mx <= 2e-3 and rf <= 5e-4
+
+
+@pytest.mark.parametrize("bq", [64, 128])
+def test_bf16_pairs_dk128(bq):
+    """precision 1 with d_k = 128 (paired attention at both query block sizes)."""
+    w = small(batch=2, seq_len=200, d_model=256, n_heads=2, d_ff=1024, block_q=bq, block_kv=128,
+              precision=1)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=11)
+    mx, rf = check(run_gpu(w, inp), oracle_full(w, inp), "bf16", f"pairs dk128 bq={bq}")
+    assert mx <= 2e-3 and rf <= 5e-4
+
+
+@pytest.mark.parametrize("dk,bq,bkv", [(64, 128, 128), (64, 128, 64), (64, 64, 128), (128, 128, 64)])
+def test_small_fp32_block_sizes(dk, bq, bkv):
+    """fp32 at the block sizes the 64/64 tests do not use (d_k 128 needs block_kv 64)."""
+    w = small(dtype="f32", seq_len=150, causal=True, d_model=256, n_heads=256 // dk, d_ff=1024,
+              block_q=bq, block_kv=bkv)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=12)
+    check(run_gpu(w, inp), oracle_full(w, inp), "f32", f"fp32 dk={dk} bq={bq} bkv={bkv}")
 
 
 @pytest.mark.parametrize("n,causal,d,h", [(200, True, 128, 2), (77, False, 256, 4),
