@@ -24,37 +24,47 @@ namespace bpt {
 enum PackOrder { kPlain = 0, kStreamWO = 1, kStreamW1 = 2, kStreamW2 = 3 };
 
 // The six matrices of a layer, repacked by one launch: matrix m covers the
-// 8-element chunks [first_chunk[m], first_chunk[m+1]) of the grid.
+// work items [first_item[m], first_item[m+1]) of the grid.
 template <typename T>
 struct PackJob {
   const T* src[6];
   T* dst[6];
   int rows[6], K[6], order[6];
-  long long first_chunk[7];
+  long long first_item[7];
   FfnStream fs;
 };
 
-// One thread per 8-element chunk of a weight; reads are row-contiguous.
+// One wave per work item = one 32-row tile and kPackSteps consecutive k-steps:
+// lane 32 hf + rho reads W[32 tile + pi(rho)][16 ks + 8 hf .. + 8] for each k-step
+// (a row's reads over the item are 256 contiguous bytes) and each k-step's
+// fragment is written as 1 KB of contiguous memory.
+constexpr int kPackSteps = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void pack_frag_kernel(PackJob<T> job) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= job.first_chunk[6]) return;
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= job.first_item[6]) return;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, rho = lane & 31;
   int m = 0;
 #pragma unroll
-  for (int q = 1; q < 6; ++q) m += i >= job.first_chunk[q];
-  const long long li = i - job.first_chunk[m];
-  const int K = job.K[m], kc = K / 8;                     // chunks per row
-  const int row = (int)(li / kc), c = (int)(li - (long long)row * kc);
-  const int tile = row >> 5, rho = pi_row(row & 31);      // pi is its own inverse
-  const int ks = c >> 1, hf = c & 1;
-  size_t slot;
+  for (int q = 1; q < 6; ++q) m += item >= job.first_item[q];
+  const long long li = item - job.first_item[m];
+  const int K = job.K[m], ksteps = K / 16;
+  const int groups = ksteps / kPackSteps;               // items per row tile
+  const int tile = (int)(li / groups), ks0 = (int)(li - (long long)tile * groups) * kPackSteps;
+  const int row = 32 * tile + pi_row(rho);              // pi is its own inverse
+  const T* src = job.src[m] + (size_t)row * K + 16 * ks0 + 8 * hf;
   const int order = job.order[m];
-  if (order == kStreamWO) slot = job.fs.slot_wo(tile, ks);
-  else if (order == kStreamW1) slot = job.fs.slot_w1(tile, ks);
-  else if (order == kStreamW2) slot = job.fs.slot_w2(tile, ks);
-  else slot = (size_t)tile * (K / 16) + ks;
-  st_packed_chunk(job.dst[m] + slot * kFragElems, 32 * hf + rho,
-                  ld_chunk(job.src[m] + (size_t)row * K + (size_t)c * 8));
+#pragma unroll
+  for (int j = 0; j < kPackSteps; ++j) {
+    const int ks = ks0 + j;
+    size_t slot;
+    if (order == kStreamWO) slot = job.fs.slot_wo(tile, ks);
+    else if (order == kStreamW1) slot = job.fs.slot_w1(tile, ks);
+    else if (order == kStreamW2) slot = job.fs.slot_w2(tile, ks);
+    else slot = (size_t)tile * ksteps + ks;
+    st_packed_chunk(job.dst[m] + slot * kFragElems, lane, ld_chunk(src + 16 * j));
+  }
 }
 
 // Packed region: W_Q, W_K, W_V (one [3d, d] operand), then the epilogue stream
@@ -77,17 +87,22 @@ int pack_all(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
     dsts[5] = p + 4 * dd + (size_t)f * d;
     orders[3] = orders[4] = orders[5] = kPlain;
   }
-  job.first_chunk[0] = 0;
+  job.first_item[0] = 0;
   for (int m = 0; m < 6; ++m) {
+    // rows are multiples of 32 and K of 16 * kPackSteps for every width supported
+    if (rows[m] % 32 != 0 || Ks[m] % (16 * kPackSteps) != 0) {
+      set_err(err, n, "weight shape not a multiple of the packing item%s", "");
+      return 1;
+    }
     job.src[m] = static_cast<const T*>(srcs[m]);
     job.dst[m] = dsts[m];
     job.rows[m] = rows[m];
     job.K[m] = Ks[m];
     job.order[m] = orders[m];
-    job.first_chunk[m + 1] = job.first_chunk[m] + (long long)rows[m] * (Ks[m] / 8);
+    job.first_item[m + 1] = job.first_item[m] + (long long)(rows[m] / 32) * (Ks[m] / (16 * kPackSteps));
   }
-  const long long total = job.first_chunk[6];
-  hipLaunchKernelGGL(pack_frag_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, job);
+  const long long total = job.first_item[6];
+  hipLaunchKernelGGL(pack_frag_kernel<T>, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, job);
   return check_launch("pack_frag", err, n);
 }
 
