@@ -119,6 +119,79 @@ def attention_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int
     return out
 
 
+def attention_lse_sequence(q: np.ndarray, k: np.ndarray, n_heads: int, causal: bool,
+                           q_pos: np.ndarray | None = None) -> np.ndarray:
+    """Per head and query row, the natural log of the softmax normaliser of the
+    scaled scores: lse[h, i] = log sum_{j visible to i} exp(q_i . k_j / sqrt(d_k)).
+
+    The forward pass keeps only each row's softmax statistics, a running maximum m
+    and the sum l of exp(s - m), so that the backward pass can rebuild the softmax
+    without re-deriving the normalisation ([BPT] "The backward pass"; [COST]
+    FlashAttention paragraph). Any pair (m, l) of one row determines the same
+    m + log l; this is that number, computed from the full row (maximum first).
+    q: [nq, d] at positions q_pos (default 0..nq-1); k: [nk, d] at 0..nk-1.
+    Returns [n_heads, nq].
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    nq, d = q.shape
+    nk = k.shape[0]
+    dk = d // n_heads
+    if q_pos is None:
+        q_pos = np.arange(nq)
+    scale = 1.0 / math.sqrt(dk)
+    out = np.empty((n_heads, nq), dtype=F64)
+    if causal:
+        hidden = np.arange(nk)[None, :] > np.asarray(q_pos)[:, None]
+    for h in range(n_heads):
+        cols = slice(h * dk, (h + 1) * dk)
+        s = (q[:, cols] @ k[:, cols].T) * scale
+        if causal:
+            s = np.where(hidden, -np.inf, s)
+        m = s.max(axis=1)
+        out[h] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    return out
+
+
+def layer_lse(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal: bool,
+              eps: float = 1e-5) -> np.ndarray:
+    """The attention statistics of one layer: [B, n_heads, seq_len], lse of every
+    row of every sequence (attention_lse_sequence on Q = LN1(x) W_Q, K = LN1(x) W_K)."""
+    x = np.asarray(x, F64)
+    p = _as_f64_layer(p)
+    rows = x.shape[0]
+    assert rows % seq_len == 0
+    x1 = layer_norm(x, p["ln1_g"], p["ln1_b"], eps)
+    q = x1 @ p["w_q"]
+    k = x1 @ p["w_k"]
+    return np.stack([attention_lse_sequence(q[s0:s0 + seq_len], k[s0:s0 + seq_len], n_heads, causal)
+                     for s0 in range(0, rows, seq_len)])
+
+
+def layer_lse_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int, n_heads: int,
+                   causal: bool, eps: float = 1e-5, row_chunk: int = 4096) -> np.ndarray:
+    """layer_lse at the given global rows only: [len(rows), n_heads]. Keys are formed
+    for the prefix each sampled query can see (in chunks of row_chunk rows, for
+    memory), queries for the sampled rows."""
+    x = np.asarray(x, F64)
+    p = _as_f64_layer(p)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, n_heads), dtype=F64)
+    seq_of = rows // seq_len
+    for sidx in np.unique(seq_of):
+        sel = np.nonzero(seq_of == sidx)[0]
+        pos = rows[sel] - sidx * seq_len
+        base = sidx * seq_len
+        n_keys = int(pos.max()) + 1 if causal else seq_len
+        k = np.empty((n_keys, x.shape[1]), F64)
+        for c0 in range(0, n_keys, row_chunk):
+            c1 = min(n_keys, c0 + row_chunk)
+            k[c0:c1] = layer_norm(x[base + c0: base + c1], p["ln1_g"], p["ln1_b"], eps) @ p["w_k"]
+        q = layer_norm(x[base + pos], p["ln1_g"], p["ln1_b"], eps) @ p["w_q"]
+        out[sel] = attention_lse_sequence(q, k, n_heads, causal, q_pos=pos).T
+    return out
+
+
 # ---------------------------------------------------------------------------
 # The unfused layer (the plain definition the fused loop must reproduce)
 # ---------------------------------------------------------------------------

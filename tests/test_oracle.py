@@ -354,3 +354,108 @@ def test_stack4_32k_golden_file_is_well_formed():
     assert g["z"].shape == (w.sample_rows, w.d_model) and g["z"].dtype == np.float64
     assert np.isfinite(g["z"]).all()
     assert len(str(g["input_sha256"])) == 64
+
+
+# --------------------------------------------------------------------------
+# Saved softmax statistics: lse = m + log l per row and head
+# --------------------------------------------------------------------------
+
+def brute_force_lse(q, k, n_heads, causal):
+    """Explicit loops, math.exp and math.log of the plain sum (no maximum taken:
+    for the small scores used here)."""
+    nq, d = q.shape
+    dk = d // n_heads
+    out = np.zeros((n_heads, nq))
+    for h in range(n_heads):
+        for i in range(nq):
+            keys = range(i + 1) if causal else range(k.shape[0])
+            tot = math.fsum(math.exp(sum(q[i, h * dk + c] * k[j, h * dk + c] for c in range(dk))
+                                     / math.sqrt(dk)) for j in keys)
+            out[h, i] = math.log(tot)
+    return out
+
+
+def _lse_pins(fn):
+    """True iff fn(q, k, n_heads, causal) passes every pin below."""
+    rng = np.random.default_rng(21)
+    for causal in (False, True):
+        q, k = rng.standard_normal((7, 8)), rng.standard_normal((7, 8))
+        if not np.allclose(fn(q, k, 2, causal), brute_force_lse(q, k, 2, causal), atol=1e-12, rtol=0):
+            return False
+        z = np.zeros((5, 8))
+        want = np.log(np.arange(1, 6)) if causal else np.full(5, math.log(5))
+        if not np.allclose(fn(z, rng.standard_normal((5, 8)), 2, causal), want[None, :], atol=1e-12, rtol=0):
+            return False
+    # two keys tie at a huge score: lse = that score + log 2, exactly representable path
+    q = np.zeros((1, 4)); q[0, 0] = 1.0
+    k = np.zeros((3, 4)); k[0, 0] = k[1, 0] = 1000.0 * 2.0; k[2, 0] = -1000.0
+    with np.errstate(over="ignore", invalid="ignore"):
+        got = fn(q, k, 1, False)
+    return bool(np.isfinite(got).all() and abs(got[0, 0] - (1000.0 + math.log(2.0))) < 1e-9)
+
+
+def test_lse_pins_hold_for_the_oracle():
+    assert _lse_pins(oracle.attention_lse_sequence)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_recovers_the_attention_output(causal):
+    """exp(S - lse) V, with S the scaled scores, is the oracle's attention output:
+    the saved statistic is the normaliser its softmax used."""
+    rng = np.random.default_rng(22 + causal)
+    n, d, h = 11, 16, 2
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    lse = oracle.attention_lse_sequence(q, k, h, causal)
+    want = oracle.attention_sequence(q, k, v, h, causal)
+    dk = d // h
+    for hh in range(h):
+        c = slice(hh * dk, (hh + 1) * dk)
+        s = q[:, c] @ k[:, c].T / math.sqrt(dk)
+        if causal:
+            s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+        assert np.max(np.abs(np.exp(s - lse[hh][:, None]) @ v[:, c] - want[:, c])) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_layer_lse_rows_equal_full(causal):
+    rng = np.random.default_rng(23 + causal)
+    n, b, d, h = 20, 2, 16, 2
+    p = rand_layer(rng, d, 4 * d)
+    x = rng.standard_normal((b * n, d))
+    full = oracle.layer_lse(x, p, seq_len=n, n_heads=h, causal=causal)
+    rows = np.array([0, 3, 19, 20, 31, 39])
+    got = oracle.layer_lse_rows(x, p, rows, seq_len=n, n_heads=h, causal=causal, row_chunk=7)
+    want = np.stack([full[r // n, :, r % n] for r in rows])
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_lse_pins_catch_planted_mistakes():
+    """Each plausible slip in the statistic fails at least one pin."""
+    base = oracle.attention_lse_sequence
+
+    def no_scale(q, k, nh, causal):
+        return base(q * math.sqrt(q.shape[1] // nh), k, nh, causal)
+
+    def log2(q, k, nh, causal):
+        return base(q, k, nh, causal) / math.log(2.0)
+
+    def max_dropped(q, k, nh, causal):
+        dk = q.shape[1] // nh
+        out = np.empty((nh, q.shape[0]))
+        for hh in range(nh):
+            c = slice(hh * dk, (hh + 1) * dk)
+            s = q[:, c] @ k[:, c].T / math.sqrt(dk)
+            if causal:
+                s = np.where(np.arange(k.shape[0])[None, :] > np.arange(q.shape[0])[:, None], -np.inf, s)
+            out[hh] = np.log(np.exp(s).sum(axis=1))
+        return out
+
+    def causal_off_by_one(q, k, nh, causal):
+        if not causal:
+            return base(q, k, nh, causal)
+        return base(q, k, nh, False) if q.shape[0] < 2 else np.concatenate(
+            [base(q[:1], k[:1], nh, False), base(q[1:], k, nh, True, q_pos=np.arange(q.shape[0] - 1))],
+            axis=1)
+
+    for planted in (no_scale, log2, max_dropped, causal_off_by_one):
+        assert not _lse_pins(planted), planted.__name__
