@@ -16,7 +16,8 @@ STATUS = {0: "BPT_OK", 1: "BPT_ERR_NULL", 2: "BPT_ERR_SHAPE", 3: "BPT_ERR_UNSUPP
           4: "BPT_ERR_ALIGN", 5: "BPT_ERR_WORKSPACE", 6: "BPT_ERR_ALIAS", 7: "BPT_ERR_HIP"}
 WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o", "ln2_g", "ln2_b", "w_1", "w_2")
 EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer_fwd",
-            "bpt_layer_fwd_profiled", "bpt_stack_fwd", "bpt_status_str", "bpt_last_error", "bpt_version")
+            "bpt_layer_fwd_profiled", "bpt_layer_fwd_lse", "bpt_stack_fwd", "bpt_status_str",
+            "bpt_last_error", "bpt_version")
 
 
 class LayerDesc(ctypes.Structure):
@@ -62,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.bpt_layer_fwd.restype = ctypes.c_int
         L.bpt_layer_fwd_profiled.argtypes = L.bpt_layer_fwd.argtypes + [P(ctypes.c_void_p)]
         L.bpt_layer_fwd_profiled.restype = ctypes.c_int
+        L.bpt_layer_fwd_lse.argtypes = [P(LayerDesc), ctypes.c_void_p, P(LayerWeights),
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+        L.bpt_layer_fwd_lse.restype = ctypes.c_int
         L.bpt_stack_fwd.argtypes = [P(LayerDesc), ctypes.c_int32, ctypes.c_void_p,
                                     P(LayerWeights), ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_size_t, ctypes.c_void_p]
@@ -144,6 +149,14 @@ def layer_fwd_profiled(desc: LayerDesc, x, layer: dict, z, workspace, events, st
     arr = (ctypes.c_void_p * 5)(*events)
     _check(lib().bpt_layer_fwd_profiled(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)),
                                         _ptr(z), _ptr(workspace), nbytes, _stream(stream), arr))
+
+
+def layer_fwd_lse(desc: LayerDesc, x, layer: dict, z, lse, workspace, stream=None) -> None:
+    """layer_fwd that also writes the attention statistic lse [batch, n_heads, seq_len]
+    (fp32, natural log of each row's softmax normaliser)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bpt_layer_fwd_lse(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)),
+                                   _ptr(z), _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def stack_fwd(desc: LayerDesc, x, layers: list, z, workspace, stream=None) -> None:

@@ -182,6 +182,37 @@ bpt_status_t run(bpt::LayerLaunch& p, void* stream) {
   return BPT_OK;
 }
 
+// One layer call: validation, launch record, launch. lse (optional) receives the
+// attention statistic [batch, n_heads, seq_len] fp32 and must overlap no other buffer.
+bpt_status_t layer_call(const bpt_layer_desc_t* desc, const void* X,
+                        const bpt_layer_weights_t* weights, void* Z, float* lse, void* workspace,
+                        size_t workspace_bytes, void* hip_stream, void* const* events) {
+  bpt_status_t st = validate_desc(desc);
+  if (st != BPT_OK) return st;
+  if (is_empty(desc)) return BPT_OK;
+  if ((st = validate_weights(weights, 0)) != BPT_OK) return st;
+  const bpt::WorkspaceLayout L = layout(desc, false);
+  if ((st = validate_buffers(desc, X, Z, workspace, workspace_bytes, L.total)) != BPT_OK) return st;
+  if (lse) {
+    const size_t rows = (size_t)desc->batch * desc->seq_len;
+    const size_t lb = (size_t)desc->n_heads * rows * sizeof(float);
+    if (overlap(lse, lb, X, rows * desc->d_model * esize(desc->dtype)))
+      return fail(BPT_ERR_ALIAS, "lse overlaps X");
+    if (overlap(lse, lb, Z, rows * desc->d_model * esize(desc->out_dtype)))
+      return fail(BPT_ERR_ALIAS, "lse overlaps Z");
+    if (overlap(lse, lb, workspace, L.total)) return fail(BPT_ERR_ALIAS, "lse overlaps the workspace");
+  }
+  bpt::LayerLaunch p = make_launch(desc, L, workspace);
+  p.x = X;
+  p.x_f32 = desc->dtype == BPT_F32;
+  p.z = Z;
+  p.z_f32 = desc->out_dtype == BPT_F32;
+  p.w = *weights;
+  p.events = events;
+  p.lse = lse;
+  return run(p, hip_stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,20 +248,19 @@ bpt_status_t bpt_layer_fwd_profiled(const bpt_layer_desc_t* desc, const void* X,
   if (events)
     for (int i = 0; i < 5; ++i)
       if (!events[i]) return fail(BPT_ERR_NULL, "events[%d] is NULL", i);
+  return layer_call(desc, X, weights, Z, nullptr, workspace, workspace_bytes, hip_stream, events);
+}
+
+bpt_status_t bpt_layer_fwd_lse(const bpt_layer_desc_t* desc, const void* X,
+                               const bpt_layer_weights_t* weights, void* Z, float* lse,
+                               void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_err[0] = 0;
   bpt_status_t st = validate_desc(desc);
   if (st != BPT_OK) return st;
   if (is_empty(desc)) return BPT_OK;
-  if ((st = validate_weights(weights, 0)) != BPT_OK) return st;
-  const bpt::WorkspaceLayout L = layout(desc, false);
-  if ((st = validate_buffers(desc, X, Z, workspace, workspace_bytes, L.total)) != BPT_OK) return st;
-  bpt::LayerLaunch p = make_launch(desc, L, workspace);
-  p.x = X;
-  p.x_f32 = desc->dtype == BPT_F32;
-  p.z = Z;
-  p.z_f32 = desc->out_dtype == BPT_F32;
-  p.w = *weights;
-  p.events = events;
-  return run(p, hip_stream);
+  if (!lse) return fail(BPT_ERR_NULL, "lse is NULL");
+  if (!aligned16(lse)) return fail(BPT_ERR_ALIGN, "lse is not 16-byte aligned");
+  return layer_call(desc, X, weights, Z, lse, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 bpt_status_t bpt_stack_fwd(const bpt_layer_desc_t* desc, int32_t n_layers, const void* X,

@@ -46,6 +46,8 @@ struct LayerLaunch {
   void* hbuf_lo;
   // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
   void* const* events;
+  // optional: attention statistic lse [batch, n_heads, seq_len] fp32
+  float* lse;
 };
 
 // Element counts/byte sizes of the workspace pieces (shared by sizing and carving).

@@ -27,6 +27,7 @@ namespace bpt {
 // the exp2 domain): exp2(s - m) then stays below 256, exact enough in fp32 and
 // bf16, and most key/value blocks need no rescale of o at all.
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // Maximum / sum of a value over the two lanes that hold the same query row
 // (lanes l and l ^ 32): one lane-swap instruction, no LDS round trip.
@@ -55,7 +56,7 @@ template <typename T, int DK, int BQ, int BKV, bool SPLIT = false>
 __global__ __launch_bounds__(BQ * 2, (4 * BKV * DK * (int)sizeof(T) * (SPLIT ? 2 : 1) <= 65536) ? 2 : 1) void
 attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* QPlo,
                  const T* __restrict__ KPlo, const T* __restrict__ VPlo, int N, int Np, int H,
-                 int d, int causal, float scale_log2e, int nqb, int n_bh) {
+                 int d, int causal, float scale_log2e, int nqb, int n_bh, float* lse) {
   using O = Op<T>;
   using F = typename O::frag;
   constexpr int NW = BQ / 32;
@@ -321,7 +322,12 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
     if (last) {
       // register group g of feature tile t holds features t*32 + 16g + 8hf + [0, 8)
       T* qp = qfrag_of(c);
-      const float inv = 1.0f / pair_sum(l_run);
+      const float l_tot = pair_sum(l_run);
+      const float inv = 1.0f / l_tot;
+      // saved statistic of the row: l_tot sums exp2(s * scale_log2e - m_run), so the
+      // softmax normaliser of the scaled scores is exp(ln2 (m_run + log2 l_tot))
+      if (lse != nullptr && hf == 0 && qpos < N)
+        lse[(size_t)c.bh * N + qpos] = (m_run + log2f(l_tot)) * kLn2;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
 #pragma unroll
@@ -389,7 +395,7 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
 template <int DK, int BKV>
 __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     bf16* QP, const bf16* __restrict__ KP, const bf16* __restrict__ VP, int N, int Np, int H,
-    int d, int causal, float scale_log2e, int nqb, int n_bh) {
+    int d, int causal, float scale_log2e, int nqb, int n_bh, float* lse) {
   using O = Op<bf16>;
   using F = O::frag;
   constexpr int BQ = 128, NWG = 4, FB = 1024;
@@ -520,7 +526,11 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
       if (qb >= 0) {
         // register group g of feature tile t holds features t*32 + 16g + 8hf + [0, 8)
         bf16* qp = qfrag_of(cp, qb);
-        const float inv = 1.0f / pair_sum(l_run);
+        const float l_tot = pair_sum(l_run);
+        const float inv = 1.0f / l_tot;
+        const int qpos = qb * BQ + wq * 32 + rho;
+        if (lse != nullptr && hf == 0 && qpos < N)
+          lse[(size_t)cp.bh * N + qpos] = (m_run + log2f(l_tot)) * kLn2;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
 #pragma unroll
@@ -681,7 +691,7 @@ int run_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   hipLaunchKernelGGL((attention_kernel<T, DK, BQ, BKV, SPLIT>), dim3(grid), dim3(BQ * 2), 0, s,
                      (T*)L.q, (const T*)L.k, (const T*)L.vt, (T*)L.q_lo, (const T*)L.k_lo,
                      (const T*)L.vt_lo, L.seq_len, L.seq_pad, L.n_heads, L.d_model, L.causal, scale,
-                     nqb, n_bh);
+                     nqb, n_bh, L.lse);
   return check_launch("attention", err, n);
 }
 
@@ -696,7 +706,7 @@ int run_attn_pair(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const float scale = 1.4426950408889634f / sqrtf((float)DK);
   hipLaunchKernelGGL((attention_pair_kernel<DK, BKV>), dim3(grid), dim3(512), 0, s, (bf16*)L.q,
                      (const bf16*)L.k, (const bf16*)L.vt, L.seq_len, L.seq_pad, L.n_heads,
-                     L.d_model, L.causal, scale, nqb, n_bh);
+                     L.d_model, L.causal, scale, nqb, n_bh, L.lse);
   return check_launch("attention", err, n);
 }
 

@@ -135,6 +135,22 @@ bpt_status_t bpt_layer_fwd_profiled(const bpt_layer_desc_t* desc, const void* X,
                                     void* workspace, size_t workspace_bytes, void* hip_stream,
                                     void* const events[5]);
 
+/* bpt_layer_fwd that also writes the attention statistic the backward pass
+ * needs. "Blockwise Parallel Transformer — BPT" (aicassindra.com), section "The
+ * backward pass": the forward keeps only each row's softmax statistics (m, l),
+ * from which every block's softmax is recomputed exactly; the FlashAttention
+ * paragraph of the transformer-cost page (raminaeye.github.io) likewise. A
+ * running maximum m and its sum l are not unique (any later maximum rescales
+ * both); the number they fix, m + ln l, is:
+ *   lse[(b * n_heads + h) * seq_len + p] = ln sum_{j visible to p} exp(q_p . k_j / sqrt(d_head))
+ * for sequence b, head h, query position p (fp32, DEVICE pointer, batch *
+ * n_heads * seq_len floats, 16-byte aligned, overlapping neither X, Z nor the
+ * workspace: BPT_ERR_NULL, BPT_ERR_ALIGN, BPT_ERR_ALIAS). Written by the same
+ * asynchronous launches as Z; every other argument and rule is bpt_layer_fwd's. */
+bpt_status_t bpt_layer_fwd_lse(const bpt_layer_desc_t* desc, const void* X,
+                               const bpt_layer_weights_t* weights, void* Z, float* lse,
+                               void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* n_layers >= 1 layers applied in turn, all with the shape of *desc; layers is
  * a HOST array of n_layers weight sets (each holding device pointers). Layer 0
  * reads X in desc->dtype; the residual stream between layers is fp32; the last

@@ -40,6 +40,36 @@ def run_gpu(w: synth.Workload, inputs: dict, out_dtype: str = "f32") -> torch.Te
     return z.cpu()
 
 
+def run_gpu_lse(w: synth.Workload, inputs: dict, out_dtype: str = "f32"):
+    """One layer through bpt_layer_fwd_lse; returns (Z, lse [batch, n_heads, seq_len]) on
+    the host."""
+    assert w.n_layers == 1
+    dev = to_device(inputs)
+    desc = bpt.desc_for(w, out_dtype=out_dtype)
+    z = torch.empty((w.rows, w.d_model), dtype=synth.TORCH_DTYPE[out_dtype], device="cuda")
+    lse = torch.full((w.batch, w.n_heads, w.seq_len), float("nan"), dtype=torch.float32, device="cuda")
+    ws = bpt.alloc_workspace(bpt.layer_workspace_bytes(desc))
+    bpt.layer_fwd_lse(desc, dev["x"], dev["layers"][0], z, lse, ws)
+    torch.cuda.synchronize()
+    return z.cpu(), lse.cpu()
+
+
+# Tolerance of the attention statistic lse (natural log, absolute): the scores it
+# sums carry the rounding of the computed operands Q and K (bf16: 2^-9 relative
+# each, pairs: ~2^-17), so its error is of the order of that relative error times
+# the scores' size; the bound is the Z bound's magnitude for bf16.
+LSE_TOL = {"bf16": 2e-2, "pairs": 1e-5, "f32": 1e-4}
+
+
+def check_lse(got: torch.Tensor, ref: np.ndarray, kind: str, what: str = "") -> float:
+    g = got.to(torch.float64).numpy()
+    assert np.all(np.isfinite(g)), f"{what}: non-finite lse"
+    mx = float(np.max(np.abs(g - ref)))
+    say(f"  {what}: lse max|err| = {mx:.3e} (tol {LSE_TOL[kind]:g})")
+    assert mx <= LSE_TOL[kind], what
+    return mx
+
+
 def oracle_full(w: synth.Workload, inputs: dict, seqs=None) -> np.ndarray:
     """Oracle Z of every row (or of the listed sequences, stacked in order)."""
     x = synth.to_f64(inputs["x"])

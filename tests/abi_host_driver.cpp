@@ -49,6 +49,12 @@ int main() {
   EXPECT(bpt::g_last[0].seq_pad == 256 && bpt::g_last[0].d_head == 64);
   EXPECT(bpt::g_last[0].xpack == fake(2ull << 36) && bpt::g_last[0].rows_pad == 512);
   EXPECT((char*)bpt::g_last[0].vt > (char*)bpt::g_last[0].k && (char*)bpt::g_last[0].k > (char*)bpt::g_last[0].q);
+  EXPECT(bpt::g_last[0].lse == nullptr);
+  // the statistics entry passes its lse buffer to the launcher
+  float* lse = reinterpret_cast<float*>(fake(3ull << 35));
+  bpt::g_launches = 0;
+  EXPECT(bpt_layer_fwd_lse(&d, fake(0), &w[0], fake(1ull << 36), lse, fake(2ull << 36), need, nullptr) == BPT_OK);
+  EXPECT(bpt::g_launches == 1 && bpt::g_last[0].lse == lse);
   // a 3-layer stack with a bf16 Z uses the workspace residual buffer between layers
   const size_t need3 = bpt_stack_workspace_bytes(&d, 3);
   EXPECT(need3 > need);
@@ -77,12 +83,18 @@ int main() {
   EXPECT(bpt_layer_fwd(&d, fake(0), &w[0], fake(64), fake(2ull << 36), need, nullptr) == BPT_ERR_ALIAS);
   EXPECT(bpt_layer_fwd(&d, fake(0), nullptr, fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_ERR_NULL);
   EXPECT(bpt_layer_fwd(nullptr, fake(0), &w[0], fake(1ull << 36), fake(2ull << 36), need, nullptr) == BPT_ERR_NULL);
+  EXPECT(bpt_layer_fwd_lse(&d, fake(0), &w[0], fake(1ull << 36), nullptr, fake(2ull << 36), need, nullptr) == BPT_ERR_NULL);
+  EXPECT(bpt_layer_fwd_lse(&d, fake(0), &w[0], fake(1ull << 36), lse + 1, fake(2ull << 36), need, nullptr) == BPT_ERR_ALIGN);
+  EXPECT(bpt_layer_fwd_lse(&d, fake(0), &w[0], fake(1ull << 36), reinterpret_cast<float*>(fake(64)), fake(2ull << 36), need, nullptr) == BPT_ERR_ALIAS);
+  EXPECT(bpt_layer_fwd_lse(&d, fake(0), &w[0], fake(1ull << 36), reinterpret_cast<float*>(fake((1ull << 36) + 64)), fake(2ull << 36), need, nullptr) == BPT_ERR_ALIAS);
+  EXPECT(bpt_layer_fwd_lse(&d, fake(0), &w[0], fake(1ull << 36), reinterpret_cast<float*>(fake((2ull << 36) + 4096)), fake(2ull << 36), need, nullptr) == BPT_ERR_ALIAS);
   EXPECT(bpt::g_launches == 0);
   EXPECT(strlen(bpt_last_error()) > 0);
   EXPECT(strcmp(bpt_status_str(BPT_ERR_ALIAS), "overlapping buffers") == 0);
   // empty calls
   bad = d; bad.batch = 0;
   EXPECT(bpt_layer_fwd(&bad, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == BPT_OK);
+  EXPECT(bpt_layer_fwd_lse(&bad, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == BPT_OK);
   EXPECT(bpt::g_launches == 0);
   if (!g_fail) printf("ALL OK\n");
   return g_fail;

@@ -11,7 +11,8 @@ import torch
 
 import oracle
 from blockwise_attn_ffn_amd import bpt, synth
-from tests._parity import check, oracle_full, oracle_rows, run_gpu, say, seq_rows
+from tests._parity import (check, check_lse, oracle_full, oracle_rows, run_gpu, run_gpu_lse, say,
+                           seq_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -318,3 +319,58 @@ def test_repeatable_and_no_device_allocation():
     free1, _ = torch.cuda.mem_get_info()
     assert free0 == free1
     assert torch.equal(z1, z2)
+
+
+# ---------------------------------------------------------------------------
+# The attention statistic (bpt_layer_fwd_lse)
+# ---------------------------------------------------------------------------
+
+def oracle_lse(w, inp, seqs=None):
+    x = synth.to_f64(inp["x"])
+    if seqs is not None:
+        x = np.concatenate([x[s * w.seq_len:(s + 1) * w.seq_len] for s in seqs])
+    return oracle.layer_lse(x, synth.oracle_weights(inp["layers"][0]), seq_len=w.seq_len,
+                            n_heads=w.n_heads, causal=w.causal, eps=w.ln_eps)
+
+
+@pytest.mark.parametrize("case", [
+    dict(n_heads=4, block_q=128, block_kv=128),                    # d_k 64, one-group kernel
+    dict(n_heads=4, block_q=64, block_kv=64, causal=False),
+    dict(n_heads=2, block_q=128, block_kv=64),                     # d_k 128, two-group kernel
+    dict(n_heads=2, block_q=128, block_kv=128, causal=False, seq_len=300),
+    dict(n_heads=2, block_q=64, block_kv=128),                     # d_k 128, one-group kernel
+    dict(n_heads=4, block_q=128, block_kv=64, precision=1),        # bf16 pairs
+    dict(n_heads=2, block_q=128, block_kv=128, precision=1),
+    dict(dtype="f32", d_model=128, n_heads=2, d_ff=512, block_q=64, block_kv=64),
+    dict(dtype="f32", n_heads=2, block_q=128, block_kv=64, causal=False),
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_lse_small(case):
+    """lse of every row and head against the oracle; Z identical to bpt_layer_fwd's."""
+    w = small(**case)
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=13)
+    z, lse = run_gpu_lse(w, inp)
+    assert torch.equal(z, run_gpu(w, inp)), "Z differs from bpt_layer_fwd"
+    kind = "f32" if w.dtype == "f32" else ("pairs" if w.precision else "bf16")
+    check_lse(lse, oracle_lse(w, inp), kind, f"lse {case}")
+
+
+def test_lse_gpt2_medium_four_sequences():
+    w = W["gpt2_medium"]
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=0)
+    _, lse = run_gpu_lse(w, inp)
+    seqs = [0, 21, 42, 63]
+    check_lse(lse[seqs], oracle_lse(w, inp, seqs), "bf16", "gpt2_medium lse")
+
+
+def test_lse_long_context_sampled_rows():
+    w = W["long_128k"]
+    say(f"case {w}")
+    inp = synth.make_inputs(w, seed=0)
+    _, lse = run_gpu_lse(w, inp)
+    rows = synth.sample_rows(w, w.sample_rows, seed=0)
+    ref = oracle.layer_lse_rows(synth.to_f64(inp["x"]), synth.oracle_weights(inp["layers"][0]), rows,
+                                seq_len=w.seq_len, n_heads=w.n_heads, causal=w.causal, eps=w.ln_eps)
+    got = lse[0][:, torch.from_numpy(rows)].T           # [rows, heads]
+    check_lse(got, ref, "bf16", "long_128k lse")
