@@ -192,6 +192,66 @@ def layer_lse_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int, n_
     return out
 
 
+def attention_backward_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                                n_heads: int, causal: bool):
+    """Gradients of one sequence's attention output A (attention_sequence) with
+    respect to Q, K and V, given dA = do. Per head, with S = Q_h K_h^T / sqrt(d_k)
+    (masked as in the forward) and P = softmax(S) by rows:
+        dV_h = P^T dO_h
+        dP   = dO_h V_h^T
+        dS   = P * (dP - rowsum(P * dP))      (the softmax's Jacobian, row by row)
+        dQ_h = dS K_h / sqrt(d_k),   dK_h = dS^T Q_h / sqrt(d_k)
+    This is the attention part of the backward pass the saved statistics serve
+    ([BPT] "The backward pass": each block recomputes s and the attention output
+    from the saved (m, l) and accumulates gradients); the plain definition here
+    builds the whole P. rowsum(P * dP) equals rowsum(dO * A), the form a block
+    recomputation uses. Returns (dq, dk, dv), each [n, d].
+    """
+    q, k, v, do = (np.asarray(a, F64) for a in (q, k, v, do))
+    n, d = q.shape
+    dk_ = d // n_heads
+    scale = 1.0 / math.sqrt(dk_)
+    dq = np.empty_like(q)
+    dkk = np.empty_like(k)
+    dv = np.empty_like(v)
+    hidden = np.arange(n)[None, :] > np.arange(n)[:, None] if causal else None
+    for h in range(n_heads):
+        c = slice(h * dk_, (h + 1) * dk_)
+        s = (q[:, c] @ k[:, c].T) * scale
+        if causal:
+            s = np.where(hidden, -np.inf, s)
+        pm = softmax_rows(s)
+        dv[:, c] = pm.T @ do[:, c]
+        dp = do[:, c] @ v[:, c].T
+        ds = pm * (dp - (pm * dp).sum(axis=1, keepdims=True))
+        dq[:, c] = ds @ k[:, c] * scale
+        dkk[:, c] = ds.T @ q[:, c] * scale
+    return dq, dkk, dv
+
+
+def attention_backward_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                               n_heads: int, causal: bool, rows: np.ndarray) -> np.ndarray:
+    """dQ of attention_backward_sequence at the given query rows only (a row's dQ
+    needs its own row of P and dP, i.e. every key it sees): [len(rows), d]."""
+    q, k, v, do = (np.asarray(a, F64) for a in (q, k, v, do))
+    rows = np.asarray(rows, dtype=np.int64)
+    d = q.shape[1]
+    dk_ = d // n_heads
+    scale = 1.0 / math.sqrt(dk_)
+    out = np.empty((rows.size, d), F64)
+    for r_i, r in enumerate(rows):
+        nk = r + 1 if causal else k.shape[0]
+        for h in range(n_heads):
+            c = slice(h * dk_, (h + 1) * dk_)
+            s = (k[:nk, c] @ q[r, c]) * scale
+            pm = np.exp(s - s.max())
+            pm /= pm.sum()
+            dp = v[:nk, c] @ do[r, c]
+            ds = pm * (dp - (pm * dp).sum())
+            out[r_i, c] = ds @ k[:nk, c] * scale
+    return out
+
+
 # ---------------------------------------------------------------------------
 # The unfused layer (the plain definition the fused loop must reproduce)
 # ---------------------------------------------------------------------------

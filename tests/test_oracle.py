@@ -459,3 +459,123 @@ def test_lse_pins_catch_planted_mistakes():
 
     for planted in (no_scale, log2, max_dropped, causal_off_by_one):
         assert not _lse_pins(planted), planted.__name__
+
+
+# --------------------------------------------------------------------------
+# Attention backward (the part of the backward pass the saved statistics serve)
+# --------------------------------------------------------------------------
+
+def _attn_loss(q, k, v, g, h, causal):
+    return float((oracle.attention_sequence(q, k, v, h, causal) * g).sum())
+
+
+def _bwd_pins(fn):
+    """True iff fn(q, k, v, do, n_heads, causal) -> (dq, dk, dv) passes the pins."""
+    rng = np.random.default_rng(31)
+    for causal in (False, True):
+        n, d, h = 6, 8, 2
+        q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+        dq, dk, dv = fn(q, k, v, g, h, causal)
+        eps = 1e-6
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            fd = np.empty_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                fd[idx] = (_attn_loss(*args_p, g, h, causal) - _attn_loss(*args_m, g, h, causal)) / (2 * eps)
+            if np.max(np.abs(fd - grad)) > 1e-7:
+                return False
+    return True
+
+
+def test_attention_backward_pins_hold_for_the_oracle():
+    assert _bwd_pins(oracle.attention_backward_sequence)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_backward_matches_torch_autograd(causal):
+    rng = np.random.default_rng(32 + causal)
+    n, d, h = 13, 16, 2
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    split = lambda t: t.view(n, h, d // h).transpose(0, 1)  # noqa: E731
+    a = F.scaled_dot_product_attention(split(tq)[None], split(tk)[None], split(tv)[None], is_causal=causal)
+    (a[0].transpose(0, 1).reshape(n, d) * torch.from_numpy(g)).sum().backward()
+    dq, dk, dv = oracle.attention_backward_sequence(q, k, v, g, h, causal)
+    for got, t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.max(np.abs(got - t.grad.numpy())) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_backward_invariants(causal):
+    """Shifting every key by one vector leaves each row's softmax unchanged, so the
+    gradients of a head's keys sum to zero; rowsum(P * dP) = rowsum(dO * A)."""
+    rng = np.random.default_rng(34 + causal)
+    n, d, h = 12, 16, 2
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    _, dk, _ = oracle.attention_backward_sequence(q, k, v, g, h, causal)
+    assert np.max(np.abs(dk.sum(axis=0))) < 1e-12
+    a = oracle.attention_sequence(q, k, v, h, causal)
+    dkh = d // h
+    for hh in range(h):
+        c = slice(hh * dkh, (hh + 1) * dkh)
+        s = q[:, c] @ k[:, c].T / math.sqrt(dkh)
+        if causal:
+            s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+        pm = oracle.softmax_rows(s)
+        assert np.max(np.abs((pm * (g[:, c] @ v[:, c].T)).sum(axis=1) - (g[:, c] * a[:, c]).sum(axis=1))) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_backward_dq_rows_equal_full(causal):
+    rng = np.random.default_rng(36 + causal)
+    n, d, h = 17, 16, 2
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    dq, _, _ = oracle.attention_backward_sequence(q, k, v, g, h, causal)
+    rows = np.array([0, 1, 8, 16])
+    got = oracle.attention_backward_dq_rows(q, k, v, g, h, causal, rows)
+    assert np.max(np.abs(got - dq[rows])) < 1e-12
+
+
+def test_attention_backward_pins_catch_planted_mistakes():
+    base = oracle.attention_backward_sequence
+
+    def no_rowsum_term(q, k, v, g, h, causal):
+        # dS = P * dP (the Jacobian's second term dropped)
+        dq, dk, dv = base(q, k, v, g, h, causal)
+        n, d = q.shape
+        dkh = d // h
+        dq2, dk2 = np.empty_like(dq), np.empty_like(dk)
+        for hh in range(h):
+            c = slice(hh * dkh, (hh + 1) * dkh)
+            s = q[:, c] @ k[:, c].T / math.sqrt(dkh)
+            if causal:
+                s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+            pm = oracle.softmax_rows(s)
+            ds = pm * (g[:, c] @ v[:, c].T)
+            dq2[:, c] = ds @ k[:, c] / math.sqrt(dkh)
+            dk2[:, c] = ds.T @ q[:, c] / math.sqrt(dkh)
+        return dq2, dk2, dv
+
+    def no_scale_on_dq(q, k, v, g, h, causal):
+        dq, dk, dv = base(q, k, v, g, h, causal)
+        return dq * math.sqrt(q.shape[1] // h), dk, dv
+
+    def p_not_transposed(q, k, v, g, h, causal):
+        dq, dk, dv = base(q, k, v, g, h, causal)
+        n, d = q.shape
+        dkh = d // h
+        dv2 = np.empty_like(dv)
+        for hh in range(h):
+            c = slice(hh * dkh, (hh + 1) * dkh)
+            s = q[:, c] @ k[:, c].T / math.sqrt(dkh)
+            if causal:
+                s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+            dv2[:, c] = oracle.softmax_rows(s) @ g[:, c]
+        return dq, dk, dv2
+
+    for planted in (no_rowsum_term, no_scale_on_dq, p_not_transposed):
+        assert not _bwd_pins(planted), planted.__name__
