@@ -16,7 +16,8 @@ STATUS = {0: "BPT_OK", 1: "BPT_ERR_NULL", 2: "BPT_ERR_SHAPE", 3: "BPT_ERR_UNSUPP
           4: "BPT_ERR_ALIGN", 5: "BPT_ERR_WORKSPACE", 6: "BPT_ERR_ALIAS", 7: "BPT_ERR_HIP"}
 WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o", "ln2_g", "ln2_b", "w_1", "w_2")
 EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer_fwd",
-            "bpt_layer_fwd_profiled", "bpt_layer_fwd_lse", "bpt_stack_fwd", "bpt_status_str",
+            "bpt_layer_fwd_profiled", "bpt_layer_fwd_lse", "bpt_stack_fwd",
+            "bpt_attention_bwd_workspace_bytes", "bpt_attention_bwd", "bpt_status_str",
             "bpt_last_error", "bpt_version")
 
 
@@ -28,6 +29,12 @@ class LayerDesc(ctypes.Structure):
                 ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("precision", ctypes.c_int32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -71,6 +78,11 @@ def lib() -> ctypes.CDLL:
                                     P(LayerWeights), ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_size_t, ctypes.c_void_p]
         L.bpt_stack_fwd.restype = ctypes.c_int
+        L.bpt_attention_bwd_workspace_bytes.argtypes = [P(AttnDesc)]
+        L.bpt_attention_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.bpt_attention_bwd.argtypes = [P(AttnDesc)] + [ctypes.c_void_p] * 10 + [
+            ctypes.c_size_t, ctypes.c_void_p]
+        L.bpt_attention_bwd.restype = ctypes.c_int
         L.bpt_status_str.argtypes = [ctypes.c_int]
         L.bpt_status_str.restype = ctypes.c_char_p
         L.bpt_last_error.argtypes = []
@@ -157,6 +169,24 @@ def layer_fwd_lse(desc: LayerDesc, x, layer: dict, z, lse, workspace, stream=Non
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().bpt_layer_fwd_lse(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)),
                                    _ptr(z), _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def make_attn_desc(*, batch, seq_len, d_model, n_heads, causal, dtype="bf16") -> AttnDesc:
+    code = dtype if isinstance(dtype, int) else {"f32": F32, "bf16": BF16}[dtype]
+    return AttnDesc(batch, seq_len, d_model, n_heads, int(causal), code)
+
+
+def attention_bwd_workspace_bytes(desc: AttnDesc) -> int:
+    return int(lib().bpt_attention_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def attention_bwd(desc: AttnDesc, q, k, v, o, do, lse, dq, dk, dv, workspace, stream=None) -> None:
+    """dQ, dK, dV (fp32 [batch * seq_len, d_model]) of the attention given the
+    forward's output o, the gradient do and the saved statistic lse."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bpt_attention_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(workspace), nbytes, _stream(stream)))
 
 
 def stack_fwd(desc: LayerDesc, x, layers: list, z, workspace, stream=None) -> None:

@@ -213,6 +213,41 @@ bpt_status_t layer_call(const bpt_layer_desc_t* desc, const void* X,
   return run(p, hip_stream);
 }
 
+
+// ---------------------------------------------------------------------------
+// Attention backward
+// ---------------------------------------------------------------------------
+
+bool attn_empty(const bpt_attn_desc_t* d) { return d->batch == 0 || d->seq_len == 0; }
+
+bpt_status_t validate_attn_desc(const bpt_attn_desc_t* d) {
+  if (!d) return fail(BPT_ERR_NULL, "desc is NULL");
+  if (d->batch < 0 || d->seq_len < 0) return fail(BPT_ERR_SHAPE, "batch and seq_len must be >= 0");
+  if (d->d_model <= 0 || d->n_heads <= 0) return fail(BPT_ERR_SHAPE, "d_model and n_heads must be > 0");
+  if (d->d_model % d->n_heads != 0)
+    return fail(BPT_ERR_SHAPE, "d_model %d is not a multiple of n_heads %d", d->d_model, d->n_heads);
+  if (d->causal != 0 && d->causal != 1) return fail(BPT_ERR_SHAPE, "causal must be 0 or 1");
+  if (d->dtype != BPT_F32 && d->dtype != BPT_BF16)
+    return fail(BPT_ERR_SHAPE, "dtype must be BPT_F32 or BPT_BF16");
+  if (d->dtype != BPT_BF16) return fail(BPT_ERR_UNSUPPORTED, "attention backward takes BPT_BF16 only");
+  const int dh = d->d_model / d->n_heads;
+  if (dh != 64 && dh != 128) return fail(BPT_ERR_UNSUPPORTED, "head size %d unsupported (64 or 128)", dh);
+  const size_t np = round_up((size_t)d->seq_len, 128);
+  if ((size_t)d->batch * np * (size_t)d->d_model >= ((size_t)1 << 31))
+    return fail(BPT_ERR_SHAPE, "batch * seq_len * d_model exceeds the 31-bit element index range");
+  return BPT_OK;
+}
+
+// D first, then the packed copies, each on a 256-byte boundary.
+size_t attn_bwd_layout(const bpt_attn_desc_t* d, size_t* packed_off, size_t* packed_bytes) {
+  const size_t np = round_up((size_t)d->seq_len, 128);
+  const size_t dbytes = round_up((size_t)d->batch * d->n_heads * d->seq_len * sizeof(float), kAlign);
+  const size_t pb = round_up((size_t)d->batch * np * d->d_model * 2, kAlign);
+  if (packed_off) *packed_off = dbytes;
+  if (packed_bytes) *packed_bytes = pb;
+  return dbytes + (size_t)bpt::kAttnBwdPacked * pb;
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,6 +326,64 @@ bpt_status_t bpt_stack_fwd(const bpt_layer_desc_t* desc, int32_t n_layers, const
     p.w = layers[i];
     if ((st = run(p, hip_stream)) != BPT_OK) return st;
   }
+  return BPT_OK;
+}
+
+size_t bpt_attention_bwd_workspace_bytes(const bpt_attn_desc_t* desc) {
+  if (validate_attn_desc(desc) != BPT_OK) return 0;
+  if (attn_empty(desc)) return 0;
+  return attn_bwd_layout(desc, nullptr, nullptr);
+}
+
+bpt_status_t bpt_attention_bwd(const bpt_attn_desc_t* desc, const void* Q, const void* K,
+                               const void* V, const void* O, const void* dO, const float* lse,
+                               float* dQ, float* dK, float* dV, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_attn_desc(desc);
+  if (st != BPT_OK) return st;
+  if (attn_empty(desc)) return BPT_OK;
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV, workspace};
+  const char* names[] = {"Q", "K", "V", "O", "dO", "lse", "dQ", "dK", "dV", "workspace"};
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) return fail(BPT_ERR_NULL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(BPT_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  size_t poff = 0, pbytes = 0;
+  const size_t need = attn_bwd_layout(desc, &poff, &pbytes);
+  if (workspace_bytes < need)
+    return fail(BPT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t rows = (size_t)desc->batch * desc->seq_len;
+  const size_t in_b = rows * desc->d_model * 2, out_b = rows * desc->d_model * sizeof(float);
+  const size_t lse_b = rows * desc->n_heads * sizeof(float);
+  // outputs and workspace against every other buffer
+  const size_t sizes[] = {in_b, in_b, in_b, in_b, in_b, lse_b, out_b, out_b, out_b, need};
+  for (int i = 6; i < 10; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (j != i && overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
+        return fail(BPT_ERR_ALIAS, "%s overlaps %s", names[i], names[j]);
+  bpt::AttnBwdLaunch p{};
+  p.batch = desc->batch;
+  p.seq_len = desc->seq_len;
+  p.d_model = desc->d_model;
+  p.n_heads = desc->n_heads;
+  p.d_head = desc->d_model / desc->n_heads;
+  p.causal = desc->causal;
+  p.seq_pad = (int)round_up((size_t)desc->seq_len, 128);
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.out = O;
+  p.dout = dO;
+  p.lse = lse;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  char* ws = static_cast<char*>(workspace);
+  p.D = reinterpret_cast<float*>(ws);
+  for (int i = 0; i < bpt::kAttnBwdPacked; ++i) p.packed[i] = ws + poff + (size_t)i * pbytes;
+  char msg[256] = "";
+  if (bpt::launch_attention_bwd(p, hip_stream, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
   return BPT_OK;
 }
 

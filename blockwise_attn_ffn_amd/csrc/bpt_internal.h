@@ -74,8 +74,24 @@ inline size_t hidden_block_rows(int d_model, size_t rows_pad) {
   return r < rows_pad ? r : rows_pad;
 }
 
+// Attention backward launch parameters after validation (device pointers).
+constexpr int kAttnBwdPacked = 11;
+struct AttnBwdLaunch {
+  int batch, seq_len, d_model, n_heads, d_head, causal;
+  int seq_pad;              // seq_len rounded up to 128
+  const void *q, *k, *v, *out, *dout;   // bf16 [batch * seq_len, d_model]
+  const float* lse;         // [batch, n_heads, seq_len]
+  float *dq, *dk, *dv;      // fp32 [batch * seq_len, d_model]
+  // workspace carve-up: D [batch, n_heads, seq_len] fp32, then kAttnBwdPacked
+  // bf16 copies of the operands in fragment order, [batch * seq_pad, d_model] each
+  float* D;
+  void* packed[kAttnBwdPacked];
+};
+
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).
 int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t errlen);
+
+int launch_attention_bwd(const AttnBwdLaunch& L, void* stream, char* err, size_t errlen);
 
 // Whether a kernel instance exists for (d_model, d_head, block sizes, types).
 int kernels_support(int d_model, int d_head, int block_q, int block_kv, int compute_f32,

@@ -157,3 +157,25 @@ def sample_rows(w: Workload, count: int, seed: int = 0) -> np.ndarray:
     pool = np.setdiff1d(np.arange(n), np.asarray(chosen))
     extra = rng.choice(pool, size=max(0, min(count, n) - len(chosen)), replace=False)
     return np.sort(np.concatenate([np.asarray(chosen, np.int64), extra.astype(np.int64)]))
+
+
+def make_attention_inputs(batch: int, seq_len: int, d_model: int, seed: int = 0,
+                          qk_std: float = 1.0, live_rows: np.ndarray | None = None) -> dict:
+    """Draw the attention backward's inputs on the CPU, bf16, each [batch * seq_len,
+    d_model] with heads concatenated along the features: Q, K ~ N(0, qk_std^2) (so a
+    score q.k / sqrt(d_head) has standard deviation qk_std^2), V, dO ~ N(0, 1), drawn
+    in that order from one generator. live_rows, if given, keeps dO only on those
+    global rows and zeroes the rest (the gradient is linear in dO; rows without one
+    contribute nothing)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    shape = (batch * seq_len, d_model)
+    q = _draw(gen, shape, qk_std, 0.0, torch.bfloat16)
+    k = _draw(gen, shape, qk_std, 0.0, torch.bfloat16)
+    v = _draw(gen, shape, 1.0, 0.0, torch.bfloat16)
+    do = _draw(gen, shape, 1.0, 0.0, torch.bfloat16)
+    if live_rows is not None:
+        keep = torch.zeros(shape[0], dtype=torch.bool)
+        keep[torch.from_numpy(np.asarray(live_rows, np.int64))] = True
+        do[~keep] = 0
+    return {"q": q, "k": k, "v": v, "do": do}

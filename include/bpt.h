@@ -151,6 +151,48 @@ bpt_status_t bpt_layer_fwd_lse(const bpt_layer_desc_t* desc, const void* X,
                                const bpt_layer_weights_t* weights, void* Z, float* lse,
                                void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Shape of one multi-head attention (the attention step of a layer). */
+typedef struct {
+  int32_t batch;      /* sequences; 0 gives an empty call that enqueues nothing  */
+  int32_t seq_len;    /* tokens per sequence N; 0 likewise                      */
+  int32_t d_model;    /* n_heads * d_head                                        */
+  int32_t n_heads;    /* d_head = d_model / n_heads: 64 or 128                   */
+  int32_t causal;     /* 1: key j visible to query p iff j <= p; 0: no mask      */
+  int32_t dtype;      /* of Q, K, V, O and dO: BPT_BF16 (the only value)         */
+} bpt_attn_desc_t;
+
+/* Bytes of workspace bpt_attention_bwd needs (0 for an empty call, or 0 with
+ * bpt_last_error() set when desc is invalid): the row statistic D [batch,
+ * n_heads, seq_len] fp32 and eleven bf16 copies of Q, K, V and dO rearranged in
+ * matrix-core fragment order, each [batch * Np, d_model] with Np = seq_len
+ * rounded up to 128. Nothing of size seq_len x seq_len. */
+size_t bpt_attention_bwd_workspace_bytes(const bpt_attn_desc_t* desc);
+
+/* Attention backward of one multi-head attention A = softmax(Q K^T / sqrt(d_head)) V
+ * per sequence and head (masked as desc->causal says), from the saved row
+ * statistics. "Blockwise Parallel Transformer — BPT" (aicassindra.com), section
+ * "The backward pass": the forward keeps only each row's softmax statistics, and
+ * each block's softmax is recomputed from them while the gradients accumulate;
+ * the FlashAttention paragraph of the transformer-cost page (raminaeye.github.io)
+ * likewise. With P = exp(Q_h K_h^T / sqrt(d_head) - lse) (the exact softmax) and
+ * D = rowsum(dO_h * O_h):
+ *   dV_h = P^T dO_h,  dS = P * (dO_h V_h^T - D),
+ *   dQ_h = dS K_h / sqrt(d_head),  dK_h = dS^T Q_h / sqrt(d_head).
+ *  - Q, K, V, O, dO: DEVICE pointers, bf16 [batch * seq_len, d_model] row-major,
+ *    heads concatenated along the features as in the layer (O is the attention
+ *    output A of the forward, dO the gradient of the loss with respect to it).
+ *  - lse: DEVICE, fp32 [batch, n_heads, seq_len], the statistic
+ *    bpt_layer_fwd_lse writes: lse = ln sum over visible keys of exp(score).
+ *  - dQ, dK, dV: DEVICE, fp32 [batch * seq_len, d_model], written (not added to).
+ *  - Every device pointer 16-byte aligned (BPT_ERR_ALIGN), none NULL
+ *    (BPT_ERR_NULL); the outputs and the workspace overlap no other buffer
+ *    (BPT_ERR_ALIAS); the inputs may overlap each other.
+ *  - Asynchronous on hip_stream, errors as for every entry point. */
+bpt_status_t bpt_attention_bwd(const bpt_attn_desc_t* desc, const void* Q, const void* K,
+                               const void* V, const void* O, const void* dO, const float* lse,
+                               float* dQ, float* dK, float* dV, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
+
 /* n_layers >= 1 layers applied in turn, all with the shape of *desc; layers is
  * a HOST array of n_layers weight sets (each holding device pointers). Layer 0
  * reads X in desc->dtype; the residual stream between layers is fp32; the last

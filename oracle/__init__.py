@@ -4,6 +4,7 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg use it; the
 HIP library never imports, links or calls anything here.
 """
 from .bpt_oracle import (WEIGHT_KEYS, attention_backward_dq_rows,  # noqa: F401
+                         attention_backward_kv_rows,
                          attention_backward_sequence, attention_lse_sequence, attention_sequence,
                          blockwise_layer_forward, gelu_tanh, layer_forward, layer_forward_rows,
                          layer_lse, layer_lse_rows, layer_norm,

@@ -252,6 +252,44 @@ def attention_backward_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: 
     return out
 
 
+
+def attention_backward_kv_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                               n_heads: int, causal: bool, rows: np.ndarray):
+    """dK and dV of attention_backward_sequence at the given key rows only:
+    (dk [len(rows), d], dv [len(rows), d]).
+
+    Key j's gradients sum over the queries p that see it: dV_j = sum_p P[p, j] dO_p
+    and dK_j = sum_p dS[p, j] Q_p / sqrt(d_k), where P[p, :] is query p's whole
+    softmax row (every key it sees) and dS[p, j] = P[p, j] (dO_p . V_j - dO_p . A_p).
+    A query whose dO row is zero has dS[p, :] = 0 and P[p, :] dO_p = 0, so it adds
+    nothing and is skipped: with dO nonzero on a few rows only, the cost is those
+    rows times the sequence length.
+    """
+    q, k, v, do = (np.asarray(a, F64) for a in (q, k, v, do))
+    rows = np.asarray(rows, dtype=np.int64)
+    n, d = q.shape
+    dk_ = d // n_heads
+    scale = 1.0 / math.sqrt(dk_)
+    dk_out = np.zeros((rows.size, d), F64)
+    dv_out = np.zeros((rows.size, d), F64)
+    live = np.flatnonzero(np.any(do != 0.0, axis=1))
+    for p in live:
+        nk = p + 1 if causal else k.shape[0]
+        seen = rows < nk                      # the requested keys query p sees
+        if not np.any(seen):
+            continue
+        for h in range(n_heads):
+            c = slice(h * dk_, (h + 1) * dk_)
+            s = (k[:nk, c] @ q[p, c]) * scale
+            pm = np.exp(s - s.max())
+            pm /= pm.sum()
+            dp = v[:nk, c] @ do[p, c]
+            ds = pm * (dp - (pm * dp).sum())
+            r = rows[seen]
+            dv_out[seen, c] += pm[r, None] * do[p, c][None, :]
+            dk_out[seen, c] += ds[r, None] * q[p, c][None, :] * scale
+    return dk_out, dv_out
+
 # ---------------------------------------------------------------------------
 # The unfused layer (the plain definition the fused loop must reproduce)
 # ---------------------------------------------------------------------------

@@ -17,6 +17,13 @@ int launch_layer(const LayerLaunch& L, void*, char*, size_t) {
   ++g_launches;
   return 0;
 }
+static int g_bwd_launches = 0;
+static AttnBwdLaunch g_bwd;
+int launch_attention_bwd(const AttnBwdLaunch& L, void*, char*, size_t) {
+  g_bwd = L;
+  ++g_bwd_launches;
+  return 0;
+}
 }  // namespace bpt
 
 static int g_fail = 0;
@@ -96,6 +103,80 @@ int main() {
   EXPECT(bpt_layer_fwd(&bad, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == BPT_OK);
   EXPECT(bpt_layer_fwd_lse(&bad, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == BPT_OK);
   EXPECT(bpt::g_launches == 0);
+
+  // attention backward: sizing, carving, validation
+  bpt_attn_desc_t a = {2, 200, 256, 2, 1, BPT_BF16};      // d_head 128, Np 256
+  const size_t anp = 256, dbytes = ((size_t)2 * 2 * 200 * 4 + 255) / 256 * 256;
+  const size_t pbytes = (size_t)2 * anp * 256 * 2;
+  const size_t aneed = bpt_attention_bwd_workspace_bytes(&a);
+  EXPECT(aneed == dbytes + 11 * pbytes);
+  const size_t in_b = (size_t)400 * 256 * 2;
+  char* base = fake(4ull << 36);
+  const void* in[5];
+  for (int i = 0; i < 5; ++i) in[i] = base + (size_t)i * in_b;      // Q K V O dO back to back
+  const float* alse = reinterpret_cast<const float*>(fake(5ull << 36));
+  float* outs[3];
+  for (int i = 0; i < 3; ++i) outs[i] = reinterpret_cast<float*>(fake((6ull + i) << 36));
+  char* aws = fake(9ull << 36);
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_OK);
+  EXPECT(bpt::g_bwd_launches == 1 && bpt::g_bwd.d_head == 128 && bpt::g_bwd.seq_pad == 256);
+  EXPECT(bpt::g_bwd.D == reinterpret_cast<float*>(aws) && (char*)bpt::g_bwd.packed[0] == aws + dbytes);
+  EXPECT((char*)bpt::g_bwd.packed[10] == aws + dbytes + 10 * pbytes);
+  EXPECT(bpt::g_bwd.q == in[0] && bpt::g_bwd.dout == in[4] && bpt::g_bwd.dv == outs[2]);
+  // inputs may coincide (Q = K, say)
+  EXPECT(bpt_attention_bwd(&a, in[0], in[0], in[0], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_OK);
+  bpt::g_bwd_launches = 0;
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed - 1, nullptr) == BPT_ERR_WORKSPACE);
+  EXPECT(bpt_attention_bwd(&a, nullptr, in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_NULL);
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], nullptr, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_NULL);
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], nullptr,
+                           aneed, nullptr) == BPT_ERR_NULL);
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse + 1, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_ALIGN);
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0] + 2, outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_ALIGN);
+  // dQ over the end of V; dK = dV; the workspace over dQ; lse inside dK
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse,
+                           reinterpret_cast<float*>(base + 2 * in_b + 4096), outs[1], outs[2], aws, aneed,
+                           nullptr) == BPT_ERR_ALIAS);
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[1], aws,
+                           aneed, nullptr) == BPT_ERR_ALIAS);
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2],
+                           reinterpret_cast<char*>(outs[0]) + 256, aneed, nullptr) == BPT_ERR_ALIAS);
+  EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], outs[1] + 64, outs[0], outs[1], outs[2],
+                           aws, aneed, nullptr) == BPT_ERR_ALIAS);
+  bpt_attn_desc_t ab = a;
+  ab.dtype = BPT_F32;
+  EXPECT(bpt_attention_bwd_workspace_bytes(&ab) == 0);
+  EXPECT(bpt_attention_bwd(&ab, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_UNSUPPORTED);
+  ab = a; ab.n_heads = 8;                                    // d_head 32
+  EXPECT(bpt_attention_bwd(&ab, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_UNSUPPORTED);
+  ab = a; ab.n_heads = 3;
+  EXPECT(bpt_attention_bwd(&ab, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_SHAPE);
+  ab = a; ab.causal = 2;
+  EXPECT(bpt_attention_bwd(&ab, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_SHAPE);
+  ab = a; ab.seq_len = -1;
+  EXPECT(bpt_attention_bwd(&ab, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_SHAPE);
+  EXPECT(bpt_attention_bwd(nullptr, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
+                           aneed, nullptr) == BPT_ERR_NULL);
+  ab = a; ab.batch = 1 << 20;                                 // 2^20 * 256 * 256 elements
+  EXPECT(bpt_attention_bwd_workspace_bytes(&ab) == 0);
+  EXPECT(bpt::g_bwd_launches == 0);
+  ab = a; ab.seq_len = 0;
+  EXPECT(bpt_attention_bwd_workspace_bytes(&ab) == 0);
+  EXPECT(bpt_attention_bwd(&ab, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, 0, nullptr) == BPT_OK);
+  EXPECT(bpt::g_bwd_launches == 0);
   if (!g_fail) printf("ALL OK\n");
   return g_fail;
 }

@@ -579,3 +579,22 @@ def test_attention_backward_pins_catch_planted_mistakes():
 
     for planted in (no_rowsum_term, no_scale_on_dq, p_not_transposed):
         assert not _bwd_pins(planted), planted.__name__
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_backward_kv_rows_equal_full(causal):
+    """dK, dV at chosen keys equal the full backward's, with dO dense and with dO
+    zero on most rows (those queries are then skipped)."""
+    rng = np.random.default_rng(38 + causal)
+    n, d, h = 19, 16, 2
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    rows = np.array([0, 3, 9, 17, 18])
+    for sparse in (False, True):
+        gg = g.copy()
+        if sparse:
+            gg[np.setdiff1d(np.arange(n), [2, 9, 18])] = 0.0
+        _, dk, dv = oracle.attention_backward_sequence(q, k, v, gg, h, causal)
+        got_k, got_v = oracle.attention_backward_kv_rows(q, k, v, gg, h, causal, rows)
+        assert np.max(np.abs(got_k - dk[rows])) < 1e-12
+        assert np.max(np.abs(got_v - dv[rows])) < 1e-12
+        assert np.max(np.abs(got_v[-1])) > 0          # key 18 is seen by query 18 (live)
