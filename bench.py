@@ -2,6 +2,7 @@
 """Throughput of the fused BPT layer forward on one MI355X.
 
     python bench.py [--workload gpt2_medium] [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --attention-bwd [--workload gpt2_medium] ...
 
 A step is one bpt_layer_fwd (or bpt_stack_fwd) call over one batch of seeded
 synthetic input already resident in device memory. W untimed steps, then K
@@ -19,6 +20,12 @@ counter summaries committed under profiles/ (rocprofv3 FETCH_SIZE and
 WRITE_SIZE, calibrated against a plain copy); it is null when no summary
 matches the workload or when the kernel's source files have changed since the
 counters were taken (a SHA-256 over those files is stored with each entry).
+
+--attention-bwd times bpt_attention_bwd instead, on the workload's attention
+shape (batch, seq_len, d_model, n_heads, mask): seeded Gaussian bf16 Q, K, V, dO,
+O ~ N(0, 0.1^2), and lse = ln(number of visible keys) (the statistic of uniform
+scores); the values do not change the work. FLOPs: 2.5 times the forward
+attention's (the score product recomputed, then four gradient products).
 """
 from __future__ import annotations
 
@@ -60,6 +67,8 @@ def parse():
     ap.add_argument("--workload", default="gpt2_medium")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attention-bwd", action="store_true",
+                    help="time the attention backward on the workload's attention shape")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample")
     return ap.parse_args()
@@ -162,12 +171,69 @@ def cpu_baseline(w, inputs, target_s: float) -> dict:
             "sample": sample, "seconds": round(t, 3), "flops": int(flops)}
 
 
+def bench_attention_bwd(args, w):
+    import torch
+    from blockwise_attn_ffn_amd import accounting as A, bpt, synth
+
+    b, n, d, h = w.batch, w.seq_len, w.d_model, w.n_heads
+    inp = synth.make_attention_inputs(b, n, d, seed=args.seed)
+    dev = {k: t.cuda() for k, t in inp.items()}
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(args.seed + 1)
+    o = (torch.randn(b * n, d, generator=gen) * 0.1).to(torch.bfloat16).cuda()
+    cnt = torch.arange(1, n + 1, dtype=torch.float64) if w.causal else torch.full((n,), float(n),
+                                                                                  dtype=torch.float64)
+    lse = cnt.log().float().expand(b, h, n).contiguous().cuda()
+    desc = bpt.make_attn_desc(batch=b, seq_len=n, d_model=d, n_heads=h, causal=w.causal)
+    ws_bytes = bpt.attention_bwd_workspace_bytes(desc)
+    ws = bpt.alloc_workspace(ws_bytes)
+    outs = [torch.empty(b * n, d, dtype=torch.float32, device="cuda") for _ in range(3)]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bpt.attention_bwd(desc, dev["q"], dev["k"], dev["v"], o, dev["do"], lse, *outs, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    flops = b * A.attention_bwd_flops(n, d, w.causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    line = {
+        "metric": "attention backward TFLOP/s (1 MI355X) + % bf16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian Q, K, V, dO, O)",
+        "config": {"workload": w.name + " attention backward", "batch": b, "seq_len": n,
+                   "d_model": d, "n_heads": h, "causal": w.causal, "parallelism": "none"},
+        "pct_peak": round(100 * tflops / peak, 2), "flops_per_step": flops,
+        "memory": {"workspace_bytes": ws_bytes},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.attention_bwd:
+        import torch
+        from blockwise_attn_ffn_amd import synth
+        if not torch.cuda.is_available():
+            print(json.dumps({"error": "no GPU visible"}))
+            sys.exit(1)
+        return bench_attention_bwd(args, synth.WORKLOADS[args.workload])
 
     import torch
     from blockwise_attn_ffn_amd import accounting as A, bpt, synth

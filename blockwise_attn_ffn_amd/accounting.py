@@ -21,6 +21,13 @@ def attention_flops(n: int, d: int, causal: bool) -> int:
     return 2 * d * n * (n + 1) if causal else 4 * n * n * d
 
 
+def attention_bwd_flops(n: int, d: int, causal: bool) -> int:
+    """Attention backward of one sequence: the scores recomputed from the saved
+    statistics, then dV = P^T dO, dP = dO V^T, dQ = dS K and dK = dS^T Q, five
+    products over the visible (query, key) pairs: 2.5 times attention_flops."""
+    return 5 * attention_flops(n, d, causal) // 2
+
+
 def projection_flops(n: int, d: int) -> int:
     """W_Q, W_K, W_V, W_O: 4 matmuls of [N, d] x [d, d]."""
     return 8 * n * d * d

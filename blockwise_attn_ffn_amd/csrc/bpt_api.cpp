@@ -238,14 +238,14 @@ bpt_status_t validate_attn_desc(const bpt_attn_desc_t* d) {
   return BPT_OK;
 }
 
-// D first, then the packed copies, each on a 256-byte boundary.
-size_t attn_bwd_layout(const bpt_attn_desc_t* d, size_t* packed_off, size_t* packed_bytes) {
+// The two row statistics first, then the transposed copies, each on a 256-byte boundary.
+size_t attn_bwd_layout(const bpt_attn_desc_t* d, size_t* stat_bytes, size_t* packed_bytes) {
   const size_t np = round_up((size_t)d->seq_len, 128);
-  const size_t dbytes = round_up((size_t)d->batch * d->n_heads * d->seq_len * sizeof(float), kAlign);
+  const size_t sb = round_up((size_t)d->batch * d->n_heads * np * sizeof(float), kAlign);
   const size_t pb = round_up((size_t)d->batch * np * d->d_model * 2, kAlign);
-  if (packed_off) *packed_off = dbytes;
+  if (stat_bytes) *stat_bytes = sb;
   if (packed_bytes) *packed_bytes = pb;
-  return dbytes + (size_t)bpt::kAttnBwdPacked * pb;
+  return 2 * sb + (size_t)bpt::kAttnBwdPacked * pb;
 }
 
 }  // namespace
@@ -349,8 +349,8 @@ bpt_status_t bpt_attention_bwd(const bpt_attn_desc_t* desc, const void* Q, const
     if (!ptrs[i]) return fail(BPT_ERR_NULL, "%s is NULL", names[i]);
     if (!aligned16(ptrs[i])) return fail(BPT_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
   }
-  size_t poff = 0, pbytes = 0;
-  const size_t need = attn_bwd_layout(desc, &poff, &pbytes);
+  size_t sbytes = 0, pbytes = 0;
+  const size_t need = attn_bwd_layout(desc, &sbytes, &pbytes);
   if (workspace_bytes < need)
     return fail(BPT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   const size_t rows = (size_t)desc->batch * desc->seq_len;
@@ -380,8 +380,9 @@ bpt_status_t bpt_attention_bwd(const bpt_attn_desc_t* desc, const void* Q, const
   p.dk = dK;
   p.dv = dV;
   char* ws = static_cast<char*>(workspace);
-  p.D = reinterpret_cast<float*>(ws);
-  for (int i = 0; i < bpt::kAttnBwdPacked; ++i) p.packed[i] = ws + poff + (size_t)i * pbytes;
+  p.stat_d = reinterpret_cast<float*>(ws);
+  p.stat_l2 = reinterpret_cast<float*>(ws + sbytes);
+  for (int i = 0; i < bpt::kAttnBwdPacked; ++i) p.packed[i] = ws + 2 * sbytes + (size_t)i * pbytes;
   char msg[256] = "";
   if (bpt::launch_attention_bwd(p, hip_stream, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
   return BPT_OK;

@@ -75,16 +75,18 @@ inline size_t hidden_block_rows(int d_model, size_t rows_pad) {
 }
 
 // Attention backward launch parameters after validation (device pointers).
-constexpr int kAttnBwdPacked = 11;
+constexpr int kAttnBwdPacked = 3;
 struct AttnBwdLaunch {
   int batch, seq_len, d_model, n_heads, d_head, causal;
   int seq_pad;              // seq_len rounded up to 128
   const void *q, *k, *v, *out, *dout;   // bf16 [batch * seq_len, d_model]
   const float* lse;         // [batch, n_heads, seq_len]
   float *dq, *dk, *dv;      // fp32 [batch * seq_len, d_model]
-  // workspace carve-up: D [batch, n_heads, seq_len] fp32, then kAttnBwdPacked
-  // bf16 copies of the operands in fragment order, [batch * seq_pad, d_model] each
-  float* D;
+  // workspace carve-up: the row statistics D and lse * log2(e), each fp32
+  // [batch * n_heads, seq_pad], then K^T, Q^T and dO^T as bf16 matrix-core
+  // fragments over [d_head, tokens] per (sequence, head), [batch * seq_pad, d_model] each
+  float* stat_d;
+  float* stat_l2;
   void* packed[kAttnBwdPacked];
 };
 

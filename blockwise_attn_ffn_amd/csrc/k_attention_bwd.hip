@@ -15,101 +15,121 @@
 // Two kernels, no atomics: one per query block for dQ (one lane per query row, as
 // in the forward: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T) and one per
 // key/value block for dK and dV (one lane per key: S = Q K^T, dP = dO V^T,
-// dV^T += dO^T P, dK^T += Q^T dS). The operands are first copied from the row-major
-// inputs into the matrix-core fragment layouts the products read (bpt_device.hpp):
-//   rows-B: B fragments over [token rows, d] (the forward's Q layout);
-//   rows-A: per (sequence, head) A fragments over [tokens (pi order), d_k] (K's);
-//   cols-A: per (sequence, head) A fragments over [d_k (pi order), tokens] (V^T's).
+// dV^T += dO^T P, dK^T += Q^T dS). Operands whose matrix-core fragments hold 8
+// consecutive features of one token (bpt_device.hpp) are read straight from the
+// row-major inputs. The products that contract over tokens (K^T dS^T, dO^T P,
+// Q^T dS) need 8 consecutive tokens of one feature per lane: for those, K, Q and
+// dO are first transposed into packed fragments in the workspace ("cols-A": per
+// (sequence, head) A fragments over [d_k (pi order), tokens], zero past seq_len).
+// A first kernel also writes, per (sequence, head) and padded to Np rows,
+// D = rowsum(dO * O) and lse * log2(e) (+inf past seq_len, so that padded query
+// rows get P = 0).
 #include "bpt_device.hpp"
 #include "bpt_launch.hpp"
 
 namespace bpt {
 
-enum BwdPackMode { kRowsB = 0, kRowsA = 1, kColsA = 2 };
+constexpr float kLog2e = 1.4426950408889634f;
 
-// One thread per 8 elements of the destination. Padded token positions (pos >= N)
-// are written as zeros.
-__global__ __launch_bounds__(256) void bwd_pack_kernel(const bf16* __restrict__ src,
-                                                       bf16* __restrict__ dst, int mode, int B,
-                                                       int N, int Np, int H, int dk, int d) {
-  const long long s = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long total = (long long)B * Np * (d / 8);
-  if (s >= total) return;
-  float v[8];
-  if (mode != kColsA) {
-    // 8 consecutive features of one token
-    const int cpr = d / 8;
-    const long long prow = s / cpr;
-    const int col = (int)(s - prow * cpr) * 8;
-    const int b = (int)(prow / Np), pos = (int)(prow - (long long)b * Np);
-    if (pos < N) load8_f32(src + ((size_t)b * N + pos) * d + col, v);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    size_t frag;
-    int slot;
-    if (mode == kRowsB) {
-      frag = (size_t)(prow >> 5) * (d / 16) + (col >> 4);
-      slot = 32 * ((col >> 3) & 1) + (int)(prow & 31);
-    } else {
-      const int h = col / dk, j = col - h * dk;
-      frag = (((size_t)b * H + h) * (Np / 32) + (pos >> 5)) * (dk / 16) + (j >> 4);
-      slot = 32 * ((j >> 3) & 1) + pi_row(pos & 31);
-    }
-    st_packed(dst + frag * kFragElems, slot, v);
-  } else {
-    // one feature of 8 consecutive tokens (a gather down the column)
-    const int ppr = Np / 8;                       // 8-token groups per sequence
-    const long long t = s / ppr;                  // (b, column)
-    const int g8 = (int)(s - t * ppr);
-    const int b = (int)(t / d), col = (int)(t - (long long)b * d);
-    const int h = col / dk, j = col - h * dk;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pos = g8 * 8 + e;
-      v[e] = pos < N ? (float)src[((size_t)b * N + pos) * d + col] : 0.f;
-    }
-    const size_t frag = (((size_t)b * H + h) * (dk / 32) + (j >> 5)) * (Np / 16) + (g8 >> 1);
-    const int slot = 32 * (g8 & 1) + pi_row(j & 31);
-    st_packed(dst + frag * kFragElems, slot, v);
-  }
-}
-
-// D[(b H + h) N + pos] = sum over the head's features of dO * O (fp32).
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16* __restrict__ dO,
-                                                         const bf16* __restrict__ O,
-                                                         float* __restrict__ D, int B, int N, int H,
-                                                         int dk, int d) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;   // (b, h, pos)
-  if (t >= (long long)B * H * N) return;
-  const int pos = (int)(t % N);
-  const long long bh = t / N;
-  const int h = (int)(bh % H), b = (int)(bh / H);
-  const size_t base = ((size_t)b * N + pos) * d + (size_t)h * dk;
+// Row statistics. One group of DK/8 consecutive threads per (token row, head),
+// each thread 8 consecutive features, so a wave reads whole rows contiguously:
+//   Dp[bh * Np + pos] = sum over the head's features of dO * O   (0 past N)
+//   L2[bh * Np + pos] = lse * log2(e)                          (+inf past N)
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const bf16* __restrict__ dO,
+                                                        const bf16* __restrict__ O,
+                                                        const float* __restrict__ lse,
+                                                        float* __restrict__ Dp,
+                                                        float* __restrict__ L2, int B, int N,
+                                                        int Np, int H) {
+  constexpr int CH = DK / 8;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  // B * Np * H * CH is a multiple of 256 (Np is a multiple of 128): no partial group
+  const int c = (int)(t % CH);
+  const long long rh = t / CH;
+  const int h = (int)(rh % H);
+  const long long row = rh / H;
+  const int b = (int)(row / Np), pos = (int)(row - (long long)b * Np);
   float acc = 0.f;
-  for (int j = 0; j < dk; j += 8) {
+  if (pos < N) {
+    const size_t off = ((size_t)b * N + pos) * (size_t)(H * DK) + (size_t)h * DK + c * 8;
     float x[8], y[8];
-    load8_f32(dO + base + j, x);
-    load8_f32(O + base + j, y);
+    load8_f32(dO + off, x);
+    load8_f32(O + off, y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
   }
-  D[t] = acc;
+#pragma unroll
+  for (int o = CH / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (c == 0) {
+    const size_t i = ((size_t)b * H + h) * Np + pos;
+    Dp[i] = acc;
+    L2[i] = pos < N ? lse[((size_t)b * H + h) * N + pos] * kLog2e : __builtin_inff();
+  }
+}
+
+// Transpose into cols-A fragments. One workgroup per (tensor, sequence, head,
+// 64-token tile, 64-feature tile): the tile is read row by row (coalesced) into
+// LDS, then written as 8 whole fragments (2 feature tiles of 32 x 4 token k-steps).
+struct TransposeJob {
+  const bf16* src[3];
+  bf16* dst[3];
+};
+
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(TransposeJob job, int N, int Np, int H,
+                                                            int dk) {
+  __shared__ __align__(16) bf16 tile[64][72];     // [token][feature], rows padded to 144 B
+  const bf16* __restrict__ src = job.src[blockIdx.y];
+  bf16* __restrict__ dst = job.dst[blockIdx.y];
+  const int d = H * dk, ftiles = dk / 64, ttiles = Np / 64;
+  int x = blockIdx.x;
+  const int ft = x % ftiles;
+  x /= ftiles;
+  const int tt = x % ttiles;
+  const int bh = x / ttiles;
+  const int b = bh / H, h = bh - b * H;
+#pragma unroll
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, c = i & 7, pos = tt * 64 + r;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (pos < N)
+      v = *reinterpret_cast<const uint4*>(src + ((size_t)b * N + pos) * d + (size_t)h * dk + ft * 64 + c * 8);
+    *reinterpret_cast<uint4*>(&tile[r][c * 8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int f = i >> 6, slot = i & 63;
+    const int dtl = f >> 2, ks = f & 3;
+    const int feat = dtl * 32 + pi_row(slot & 31), tok0 = ks * 16 + 8 * (slot >> 5);
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[tok0 + e][feat];
+    const size_t frag = ((size_t)bh * (dk / 32) + ft * 2 + dtl) * (Np / 16) + tt * 4 + ks;
+    *reinterpret_cast<bf16x8*>(dst + frag * kFragElems + slot * 8) = v;
+  }
 }
 
 struct BwdArgs {
-  const bf16 *qB, *doB, *kA, *vA, *kT;            // dQ kernel operands
-  const bf16 *kB, *vB, *qA, *doA, *qT, *doT;      // dK / dV kernel operands
-  const float* lse;                               // [B, H, N], natural log
-  const float* D;                                 // [B, H, N]
+  const bf16 *q, *k, *v, *dout;                   // row-major [B N, d]
+  const bf16 *kT, *qT, *doT;                      // cols-A fragments per (sequence, head)
+  const float *L2, *Dp;                           // [B H, Np]
   float *dq, *dk, *dv;                            // [B N, d] row-major
   int B, N, Np, H, d, causal;
   float scale_log2e, scale;                       // log2(e) / sqrt(d_k), 1 / sqrt(d_k)
 };
 
+// Lane's fragment of a B operand over token rows from row-major X: row `pos`
+// (zero past N), features f0 + [0, 8).
+__device__ inline bf16x8 ld_row_frag(const bf16* X, int b, int pos, int N, int d, int f0) {
+  if (pos >= N) return bf16x8{};
+  return *reinterpret_cast<const bf16x8*>(X + ((size_t)b * N + pos) * d + f0);
+}
+
 // dQ: one workgroup of 4 waves per (sequence, head, 128-row query block); one lane
 // per query row. Key/value blocks of 64 keys are copied into LDS (K and V as A
-// fragments over keys, K^T as A fragments over features), two stages.
+// fragments over keys, straight from the row-major inputs; K^T as A fragments over
+// features from the transposed copy), two stages.
 template <int DK>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
   using O = Op<bf16>;
@@ -128,10 +148,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
   const int rho = lane & 31, hf = lane >> 5;
   const int N = g.N, Np = g.Np, H = g.H, d = g.d;
   const int nqb = (N + BQ - 1) / BQ;
-  const int bh = blockIdx.x / nqb, qb = blockIdx.x - bh * nqb;
+  const int bh = blockIdx.x / nqb, qb = nqb - 1 - (int)(blockIdx.x - bh * nqb);   // longest first
   const int b = bh / H, h = bh - b * H;
   const int kend = g.causal ? (min(qb * BQ + BQ, N) - 1) / BKV + 1 : (N + BKV - 1) / BKV;
   const int wave_q_first = qb * BQ + wave * 32, qpos = wave_q_first + rho;
+  const int fcol = h * DK + 8 * hf;             // this lane's feature offset in a row
 
   auto issue = [&](int kb, unsigned char* buf) __attribute__((always_inline)) {
     const int kv0 = kb * BKV;
@@ -139,31 +160,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
     for (int q = 0; q < CPW; ++q) {
       const int f = wave * CPW + q;
       const bf16* src;
-      if (f < KFR) {
-        src = g.kA + (((size_t)bh * (Np / 32) + kv0 / 32) * KSD + f) * kFragElems;
-      } else if (f < 2 * KFR) {
-        src = g.vA + (((size_t)bh * (Np / 32) + kv0 / 32) * KSD + (f - KFR)) * kFragElems;
+      if (f < 2 * KFR) {
+        const int ff = f < KFR ? f : f - KFR, t = ff / KSD, kk = ff - t * KSD;
+        const int pos = min(kv0 + t * 32 + pi_row(rho), N - 1);
+        src = (f < KFR ? g.k : g.v) + ((size_t)b * N + pos) * d + fcol + kk * 16;
       } else {
         const int ff = f - 2 * KFR, dt = ff / KK, kk = ff - dt * KK;
-        src = g.kT + (((size_t)bh * DT + dt) * (Np / 16) + kv0 / 16 + kk) * kFragElems;
+        src = g.kT + (((size_t)bh * DT + dt) * (Np / 16) + kv0 / 16 + kk) * kFragElems + lane * 8;
       }
-      dma16(src + lane * 8, buf + f * FB);
+      dma16(src, buf + f * FB);
     }
   };
 
   // this wave's Q and dO (B fragments over its 32 query rows) and row statistics
   F qf[KSD], of[KSD];
-  {
-    const size_t fr = (size_t)((b * Np + wave_q_first) >> 5) * (d / 16) + h * KSD;
 #pragma unroll
-    for (int kk = 0; kk < KSD; ++kk) {
-      qf[kk] = ld_packed(g.qB + (fr + kk) * kFragElems, lane);
-      of[kk] = ld_packed(g.doB + (fr + kk) * kFragElems, lane);
-    }
+  for (int kk = 0; kk < KSD; ++kk) {
+    qf[kk] = ld_row_frag(g.q, b, qpos, N, d, fcol + kk * 16);
+    of[kk] = ld_row_frag(g.dout, b, qpos, N, d, fcol + kk * 16);
   }
-  const bool live = qpos < N;
-  const float lse2 = live ? g.lse[(size_t)bh * N + qpos] * 1.4426950408889634f : 0.f;
-  const float Dq = live ? g.D[(size_t)bh * N + qpos] : 0.f;
+  const float l2 = g.L2[(size_t)bh * Np + qpos];   // +inf past N: P = 0 on that lane
+  const float Dq = g.Dp[(size_t)bh * Np + qpos];
   f32x16 dq[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x16{};
@@ -171,6 +188,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
   auto visit = [&](int kb, const unsigned char* buf) __attribute__((always_inline)) {
     const int kv0 = kb * BKV;
     if (g.causal && kv0 > wave_q_first + 31) return;   // every key of the block is later
+    const bool need_mask = (g.causal && kv0 + BKV - 1 > wave_q_first) || kv0 + BKV > N;
     f32x16 s[KT], dp[KT];
 #pragma unroll
     for (int t = 0; t < KT; ++t) { s[t] = f32x16{}; dp[t] = f32x16{}; }
@@ -193,8 +211,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * gg + e;
-          const bool vis = live && (t * 32 + (i & 8) * 2 + (i & 7) <= lim);
-          const float p = vis ? fast_exp2(fmaf(s[t][i], g.scale_log2e, -lse2)) : 0.f;
+          float p = fast_exp2(fmaf(s[t][i], g.scale_log2e, -l2));
+          if (need_mask && t * 32 + (i & 8) * 2 + (i & 7) > lim) p = 0.f;
           v[e] = p * (dp[t][i] - Dq);
         }
         dsf[2 * t + gg] = O::from_f32(v);
@@ -221,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
     visit(kb + 1, lds1);
   }
   // register group gg of feature tile t holds features t*32 + 16gg + 8hf + [0, 8)
-  if (live) {
+  if (qpos < N) {
     float* out = g.dq + ((size_t)b * N + qpos) * d + (size_t)h * DK;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
@@ -237,7 +255,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
 
 // dK, dV: one workgroup of 4 waves per (sequence, head, 128-key block); one lane per
 // key. Query blocks of 64 rows are copied into LDS (Q and dO as A fragments over
-// queries, Q^T and dO^T as A fragments over features), two stages.
+// queries from the row-major inputs, Q^T and dO^T from the transposed copies, and
+// the 64 rows' statistics), two stages.
 template <int DK>
 __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
   using O = Op<bf16>;
@@ -248,19 +267,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
   constexpr int TFR = DT * QK;                  // Q^T (and dO^T) fragments per block
   constexpr int NFR = 2 * AFR + 2 * TFR;
   constexpr int CPW = NFR / 4;
+  constexpr int STAGE = (NFR + 1) * FB;         // + statistics: L2 then Dp, 64 floats each
   static_assert(NFR % 4 == 0, "copies per wave");
-  __shared__ __align__(16) unsigned char lds0[NFR * FB];
-  __shared__ __align__(16) unsigned char lds1[NFR * FB];
+  __shared__ __align__(16) unsigned char lds0[STAGE];
+  __shared__ __align__(16) unsigned char lds1[STAGE];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rho = lane & 31, hf = lane >> 5;
   const int N = g.N, Np = g.Np, H = g.H, d = g.d;
   const int nkb = (N + BK - 1) / BK;
-  const int bh = blockIdx.x / nkb, kbk = blockIdx.x - bh * nkb;
+  const int bh = blockIdx.x / nkb, kbk = blockIdx.x - bh * nkb;   // longest first under the mask
   const int b = bh / H, h = bh - b * H;
   const int wave_k_first = kbk * BK + wave * 32, kpos = wave_k_first + rho;
   const int nqs = (N + BQS - 1) / BQS;
   const int qs_begin = g.causal ? (kbk * BK) / BQS : 0;
+  const int fcol = h * DK + 8 * hf;
 
   auto issue = [&](int qs, unsigned char* buf) __attribute__((always_inline)) {
     const int q0 = qs * BQS;
@@ -269,38 +290,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
       const int f = wave * CPW + q;
       const bf16* src;
       if (f < 2 * AFR) {
-        const bf16* base = f < AFR ? g.qA : g.doA;
-        const int ff = f < AFR ? f : f - AFR;
-        src = base + (((size_t)bh * (Np / 32) + q0 / 32) * KSD + ff) * kFragElems;
+        const int ff = f < AFR ? f : f - AFR, t = ff / KSD, kk = ff - t * KSD;
+        const int pos = min(q0 + t * 32 + pi_row(rho), N - 1);
+        src = (f < AFR ? g.q : g.dout) + ((size_t)b * N + pos) * d + fcol + kk * 16;
       } else {
         const int f2 = f - 2 * AFR;
         const bf16* base = f2 < TFR ? g.qT : g.doT;
         const int ff = f2 < TFR ? f2 : f2 - TFR, dt = ff / QK, kk = ff - dt * QK;
-        src = base + (((size_t)bh * DT + dt) * (Np / 16) + q0 / 16 + kk) * kFragElems;
+        src = base + (((size_t)bh * DT + dt) * (Np / 16) + q0 / 16 + kk) * kFragElems + lane * 8;
       }
-      dma16(src + lane * 8, buf + f * FB);
+      dma16(src, buf + f * FB);
+    }
+    if (wave == 0) {
+      // lanes 0-15: L2[q0 .. q0+63], lanes 16-31: Dp[...]; lanes 32-63 repeat them
+      const int l = lane & 31;
+      const float* st = (l < 16 ? g.L2 : g.Dp) + (size_t)bh * Np + q0 + 4 * (l & 15);
+      dma16(st, buf + NFR * FB);
     }
   };
 
   // this wave's K and V (B fragments over its 32 keys)
   F kf[KSD], vf[KSD];
-  {
-    const size_t fr = (size_t)((b * Np + wave_k_first) >> 5) * (d / 16) + h * KSD;
 #pragma unroll
-    for (int kk = 0; kk < KSD; ++kk) {
-      kf[kk] = ld_packed(g.kB + (fr + kk) * kFragElems, lane);
-      vf[kk] = ld_packed(g.vB + (fr + kk) * kFragElems, lane);
-    }
+  for (int kk = 0; kk < KSD; ++kk) {
+    kf[kk] = ld_row_frag(g.k, b, kpos, N, d, fcol + kk * 16);
+    vf[kk] = ld_row_frag(g.v, b, kpos, N, d, fcol + kk * 16);
   }
   f32x16 dkacc[DT], dvacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) { dkacc[t] = f32x16{}; dvacc[t] = f32x16{}; }
-  const float* lse_bh = g.lse + (size_t)bh * N;
-  const float* D_bh = g.D + (size_t)bh * N;
 
   auto visit = [&](int qs, const unsigned char* buf) __attribute__((always_inline)) {
     const int q0 = qs * BQS;
     if (g.causal && wave_k_first > q0 + BQS - 1) return;   // every query of the block is earlier
+    const bool need_mask = g.causal && wave_k_first + 31 > q0;
     f32x16 s[QT], dp[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) { s[t] = f32x16{}; dp[t] = f32x16{}; }
@@ -313,25 +336,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
                vf[kk]);
       }
     // register i of tile t holds query q0 + t*32 + (i&8)*2 + 8hf + (i&7); lane holds key kpos
+    const float* st = reinterpret_cast<const float*>(buf + NFR * FB);
     F pf[QK], dsf[QK];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
-        const int qfirst = q0 + t * 32 + 16 * gg + 8 * hf;   // 8 consecutive queries
-        float l8[8], d8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int qq = qfirst + e;
-          l8[e] = qq < N ? lse_bh[qq] * 1.4426950408889634f : 0.f;
-          d8[e] = qq < N ? D_bh[qq] : 0.f;
-        }
+        const int qoff = t * 32 + 16 * gg + 8 * hf;          // 8 consecutive queries
+        const float4 la = *reinterpret_cast<const float4*>(st + qoff);
+        const float4 lb = *reinterpret_cast<const float4*>(st + qoff + 4);
+        const float4 da = *reinterpret_cast<const float4*>(st + 64 + qoff);
+        const float4 db = *reinterpret_cast<const float4*>(st + 64 + qoff + 4);
+        const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+        const float d8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
         float pv[8], dv8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int qq = qfirst + e;
-          const bool vis = kpos < N && qq < N && !(g.causal && kpos > qq);
-          const float p = vis ? fast_exp2(fmaf(s[t][8 * gg + e], g.scale_log2e, -l8[e])) : 0.f;
+          float p = fast_exp2(fmaf(s[t][8 * gg + e], g.scale_log2e, -l8[e]));
+          if (need_mask && kpos > q0 + qoff + e) p = 0.f;
           pv[e] = p;
           dv8[e] = p * (dp[t][8 * gg + e] - d8[e]);
         }
@@ -351,19 +373,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
       }
   };
 
-  if (qs_begin < nqs) {
-    issue(qs_begin, lds0);
-    for (int qs = qs_begin; qs < nqs; qs += 2) {
-      wait_vmem();
-      __syncthreads();
-      if (qs + 1 < nqs) issue(qs + 1, lds1);
-      visit(qs, lds0);
-      if (qs + 1 >= nqs) break;
-      wait_vmem();
-      __syncthreads();
-      if (qs + 2 < nqs) issue(qs + 2, lds0);
-      visit(qs + 1, lds1);
-    }
+  issue(qs_begin, lds0);
+  for (int qs = qs_begin; qs < nqs; qs += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (qs + 1 < nqs) issue(qs + 1, lds1);
+    visit(qs, lds0);
+    if (qs + 1 >= nqs) break;
+    wait_vmem();
+    __syncthreads();
+    if (qs + 2 < nqs) issue(qs + 2, lds0);
+    visit(qs + 1, lds1);
   }
   // register group gg of feature tile t holds features t*32 + 16gg + 8hf + [0, 8)
   if (kpos < N) {
@@ -387,46 +407,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
 
 namespace {
 
-int pack(const bf16* src, bf16* dst, int mode, const AttnBwdLaunch& L, hipStream_t s, char* err,
-         size_t n) {
-  const long long total = (long long)L.batch * L.seq_pad * (L.d_model / 8);
-  hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, src, dst,
-                     mode, L.batch, L.seq_len, L.seq_pad, L.n_heads, L.d_head, L.d_model);
-  return check_launch("bwd_pack", err, n);
-}
-
 template <int DK>
 int run_bwd(const AttnBwdLaunch& L, hipStream_t s, char* err, size_t n) {
-  BwdArgs g{};
-  const bf16* q = static_cast<const bf16*>(L.q);
-  const bf16* k = static_cast<const bf16*>(L.k);
-  const bf16* v = static_cast<const bf16*>(L.v);
-  const bf16* dO = static_cast<const bf16*>(L.dout);
-  bf16* P[kAttnBwdPacked];                          // packed copies in the workspace
-  for (int i = 0; i < kAttnBwdPacked; ++i) P[i] = static_cast<bf16*>(L.packed[i]);
-  if (pack(q, P[0], kRowsB, L, s, err, n) || pack(dO, P[1], kRowsB, L, s, err, n) ||
-      pack(k, P[2], kRowsA, L, s, err, n) || pack(v, P[3], kRowsA, L, s, err, n) ||
-      pack(k, P[4], kColsA, L, s, err, n) || pack(k, P[5], kRowsB, L, s, err, n) ||
-      pack(v, P[6], kRowsB, L, s, err, n) || pack(q, P[7], kRowsA, L, s, err, n) ||
-      pack(dO, P[8], kRowsA, L, s, err, n) || pack(q, P[9], kColsA, L, s, err, n) ||
-      pack(dO, P[10], kColsA, L, s, err, n))
+  // the kernels' shape assumptions
+  if (L.d_model != L.n_heads * DK || L.seq_pad % 128 != 0 || L.seq_pad < L.seq_len || L.seq_len < 1) {
+    set_err(err, n, "attention backward: inconsistent launch shape%s (seq_pad %d)", "", L.seq_pad);
     return 1;
-  const long long rows = (long long)L.batch * L.n_heads * L.seq_len;
-  hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, dO,
-                     static_cast<const bf16*>(L.out), L.D, L.batch, L.seq_len, L.n_heads, L.d_head,
-                     L.d_model);
-  if (check_launch("bwd_rowdot", err, n)) return 1;
-  g.qB = P[0]; g.doB = P[1]; g.kA = P[2]; g.vA = P[3]; g.kT = P[4];
-  g.kB = P[5]; g.vB = P[6]; g.qA = P[7]; g.doA = P[8]; g.qT = P[9]; g.doT = P[10];
-  g.lse = L.lse;
-  g.D = L.D;
-  g.dq = L.dq; g.dk = L.dk; g.dv = L.dv;
-  g.B = L.batch; g.N = L.seq_len; g.Np = L.seq_pad; g.H = L.n_heads; g.d = L.d_model;
+  }
+  BwdArgs g{};
+  g.q = static_cast<const bf16*>(L.q);
+  g.k = static_cast<const bf16*>(L.k);
+  g.v = static_cast<const bf16*>(L.v);
+  g.dout = static_cast<const bf16*>(L.dout);
+  bf16* kT = static_cast<bf16*>(L.packed[0]);
+  bf16* qT = static_cast<bf16*>(L.packed[1]);
+  bf16* doT = static_cast<bf16*>(L.packed[2]);
+  g.kT = kT;
+  g.qT = qT;
+  g.doT = doT;
+  g.Dp = L.stat_d;
+  g.L2 = L.stat_l2;
+  g.dq = L.dq;
+  g.dk = L.dk;
+  g.dv = L.dv;
+  g.B = L.batch;
+  g.N = L.seq_len;
+  g.Np = L.seq_pad;
+  g.H = L.n_heads;
+  g.d = L.d_model;
   g.causal = L.causal;
   g.scale = 1.0f / sqrtf((float)DK);
-  g.scale_log2e = 1.4426950408889634f * g.scale;
-  const int nqb = (L.seq_len + 127) / 128, nkb = (L.seq_len + 127) / 128;
+  g.scale_log2e = kLog2e * g.scale;
   const int bhs = L.batch * L.n_heads;
+  const long long stat_threads = (long long)bhs * L.seq_pad * (DK / 8);
+  hipLaunchKernelGGL(bwd_stats_kernel<DK>, dim3((unsigned)(stat_threads / 256)), dim3(256), 0, s,
+                     g.dout, static_cast<const bf16*>(L.out), L.lse, L.stat_d, L.stat_l2, L.batch,
+                     L.seq_len, L.seq_pad, L.n_heads);
+  if (check_launch("bwd_stats", err, n)) return 1;
+  TransposeJob job{{g.k, g.q, g.dout}, {kT, qT, doT}};
+  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(bhs * (L.seq_pad / 64) * (DK / 64)), 3),
+                     dim3(256), 0, s, job, L.seq_len, L.seq_pad, L.n_heads, DK);
+  if (check_launch("bwd_transpose", err, n)) return 1;
+  const int nqb = (L.seq_len + 127) / 128, nkb = (L.seq_len + 127) / 128;
   hipLaunchKernelGGL(bwd_dq_kernel<DK>, dim3(bhs * nqb), dim3(256), 0, s, g);
   if (check_launch("bwd_dq", err, n)) return 1;
   hipLaunchKernelGGL(bwd_dkv_kernel<DK>, dim3(bhs * nkb), dim3(256), 0, s, g);

@@ -162,10 +162,10 @@ typedef struct {
 } bpt_attn_desc_t;
 
 /* Bytes of workspace bpt_attention_bwd needs (0 for an empty call, or 0 with
- * bpt_last_error() set when desc is invalid): the row statistic D [batch,
- * n_heads, seq_len] fp32 and eleven bf16 copies of Q, K, V and dO rearranged in
- * matrix-core fragment order, each [batch * Np, d_model] with Np = seq_len
- * rounded up to 128. Nothing of size seq_len x seq_len. */
+ * bpt_last_error() set when desc is invalid): two fp32 row statistics [batch,
+ * n_heads, Np] (D = rowsum(dO * O) and lse in base 2), with Np = seq_len rounded
+ * up to 128, and transposed bf16 copies of K, Q and dO, each [batch * Np,
+ * d_model]. Nothing of size seq_len x seq_len. */
 size_t bpt_attention_bwd_workspace_bytes(const bpt_attn_desc_t* desc);
 
 /* Attention backward of one multi-head attention A = softmax(Q K^T / sqrt(d_head)) V

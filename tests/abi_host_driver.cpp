@@ -106,10 +106,10 @@ int main() {
 
   // attention backward: sizing, carving, validation
   bpt_attn_desc_t a = {2, 200, 256, 2, 1, BPT_BF16};      // d_head 128, Np 256
-  const size_t anp = 256, dbytes = ((size_t)2 * 2 * 200 * 4 + 255) / 256 * 256;
+  const size_t anp = 256, sbytes = (size_t)2 * 2 * anp * 4;
   const size_t pbytes = (size_t)2 * anp * 256 * 2;
   const size_t aneed = bpt_attention_bwd_workspace_bytes(&a);
-  EXPECT(aneed == dbytes + 11 * pbytes);
+  EXPECT(aneed == 2 * sbytes + 3 * pbytes);
   const size_t in_b = (size_t)400 * 256 * 2;
   char* base = fake(4ull << 36);
   const void* in[5];
@@ -121,8 +121,10 @@ int main() {
   EXPECT(bpt_attention_bwd(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
                            aneed, nullptr) == BPT_OK);
   EXPECT(bpt::g_bwd_launches == 1 && bpt::g_bwd.d_head == 128 && bpt::g_bwd.seq_pad == 256);
-  EXPECT(bpt::g_bwd.D == reinterpret_cast<float*>(aws) && (char*)bpt::g_bwd.packed[0] == aws + dbytes);
-  EXPECT((char*)bpt::g_bwd.packed[10] == aws + dbytes + 10 * pbytes);
+  EXPECT(bpt::g_bwd.stat_d == reinterpret_cast<float*>(aws));
+  EXPECT(bpt::g_bwd.stat_l2 == reinterpret_cast<float*>(aws + sbytes));
+  EXPECT((char*)bpt::g_bwd.packed[0] == aws + 2 * sbytes);
+  EXPECT((char*)bpt::g_bwd.packed[2] == aws + 2 * sbytes + 2 * pbytes);
   EXPECT(bpt::g_bwd.q == in[0] && bpt::g_bwd.dout == in[4] && bpt::g_bwd.dv == outs[2]);
   // inputs may coincide (Q = K, say)
   EXPECT(bpt_attention_bwd(&a, in[0], in[0], in[0], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
