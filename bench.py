@@ -171,6 +171,46 @@ def cpu_baseline(w, inputs, target_s: float) -> dict:
             "sample": sample, "seconds": round(t, 3), "flops": int(flops)}
 
 
+BWD_KERNELS = ("bwd_stats", "bwd_transpose", "bwd_dq", "bwd_dkv")
+
+
+def cpu_baseline_attention_bwd(w, inp, target_s: float) -> dict:
+    """The oracle's attention backward, as it stands, on a bounded sample."""
+    import numpy as np
+    import oracle
+    from blockwise_attn_ffn_amd import accounting as A, synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    n, d, h = w.seq_len, w.d_model, w.n_heads
+    if n <= 4096:
+        def run(k):
+            t0 = time.perf_counter()
+            for s_ in range(k):
+                r = slice(s_ * n, (s_ + 1) * n)
+                oracle.attention_backward_sequence(*(synth.to_f64(inp[x][r]) for x in ("q", "k", "v", "do")),
+                                                   h, w.causal)
+            return time.perf_counter() - t0
+        t1 = run(1)
+        k = int(max(1, min(w.batch, round(target_s / max(t1, 1e-3)))))
+        t = run(k) if k > 1 else t1
+        flops = k * A.attention_bwd_flops(n, d, w.causal)
+        sample = f"{k} of {w.batch} sequences, every head (full softmax, fp64)"
+    else:
+        rows = np.sort(np.random.default_rng(0).choice(n, 16, replace=False))
+        q, k_, v, g = (synth.to_f64(inp[x][:n]) for x in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        oracle.attention_backward_dq_rows(q, k_, v, g, h, w.causal, rows)
+        t = time.perf_counter() - t0
+        # per row and visible key: scores, dP and the dQ product (3 x 2 d FLOPs)
+        flops = int(sum(6 * d * ((r + 1) if w.causal else n) for r in rows))
+        sample = f"dQ of {len(rows)} sampled rows of sequence 0 (fp64)"
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(t, 3), "flops": int(flops)}
+
+
 def bench_attention_bwd(args, w):
     import torch
     from blockwise_attn_ffn_amd import accounting as A, bpt, synth
@@ -189,9 +229,15 @@ def bench_attention_bwd(args, w):
     ws = bpt.alloc_workspace(ws_bytes)
     outs = [torch.empty(b * n, d, dtype=torch.float32, device="cuda") for _ in range(3)]
     stream = torch.cuda.current_stream()
+    hip = Hip()
+    evs = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
 
-    def step():
-        bpt.attention_bwd(desc, dev["q"], dev["k"], dev["v"], o, dev["do"], lse, *outs, ws, stream)
+    def step(events=None):
+        if events is None:
+            bpt.attention_bwd(desc, dev["q"], dev["k"], dev["v"], o, dev["do"], lse, *outs, ws, stream)
+        else:
+            bpt.attention_bwd_profiled(desc, dev["q"], dev["k"], dev["v"], o, dev["do"], lse, *outs, ws,
+                                       events, stream)
 
     for _ in range(args.warmup):
         step()
@@ -199,14 +245,26 @@ def bench_attention_bwd(args, w):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs[i])
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    per_kernel = {k: 0.0 for k in BWD_KERNELS}
+    for ev in evs:
+        for i, k in enumerate(BWD_KERNELS):
+            per_kernel[k] += hip.elapsed_ms(ev[i], ev[i + 1]) / args.steps
+        for e in ev:
+            hip.destroy(e)
     flops = b * A.attention_bwd_flops(n, d, w.causal)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS["bf16"]
+    # products each kernel runs over the visible (query, key) pairs, each half of
+    # the forward attention's two: dQ kernel S, dP, dQ; dK / dV kernel S, dP, dV, dK
+    half = b * A.attention_flops(n, d, w.causal) // 2
+    kf = {"bwd_stats": 0, "bwd_transpose": 0, "bwd_dq": 3 * half, "bwd_dkv": 4 * half}
+    dom = max(BWD_KERNELS, key=lambda k: per_kernel[k])
+    achieved = kf[dom] / (per_kernel[dom] * 1e-3) / 1e12
     line = {
         "metric": "attention backward TFLOP/s (1 MI355X) + % bf16 MFMA peak",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -216,8 +274,16 @@ def bench_attention_bwd(args, w):
         "config": {"workload": w.name + " attention backward", "batch": b, "seq_len": n,
                    "d_model": d, "n_heads": h, "causal": w.causal, "parallelism": "none"},
         "pct_peak": round(100 * tflops / peak, 2), "flops_per_step": flops,
+        "kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "kernel_tflops": {k: round(kf[k] / (per_kernel[k] * 1e-3) / 1e12, 2)
+                          for k in BWD_KERNELS if kf[k] and per_kernel[k] > 0},
         "memory": {"workspace_bytes": ws_bytes},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_ms": round(per_kernel[dom], 4), "flops_per_launch": kf[dom]},
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_attention_bwd(w, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

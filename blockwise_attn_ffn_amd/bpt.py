@@ -17,7 +17,8 @@ STATUS = {0: "BPT_OK", 1: "BPT_ERR_NULL", 2: "BPT_ERR_SHAPE", 3: "BPT_ERR_UNSUPP
 WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o", "ln2_g", "ln2_b", "w_1", "w_2")
 EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer_fwd",
             "bpt_layer_fwd_profiled", "bpt_layer_fwd_lse", "bpt_stack_fwd",
-            "bpt_attention_bwd_workspace_bytes", "bpt_attention_bwd", "bpt_status_str",
+            "bpt_attention_bwd_workspace_bytes", "bpt_attention_bwd",
+            "bpt_attention_bwd_profiled", "bpt_status_str",
             "bpt_last_error", "bpt_version")
 
 
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.bpt_attention_bwd.argtypes = [P(AttnDesc)] + [ctypes.c_void_p] * 10 + [
             ctypes.c_size_t, ctypes.c_void_p]
         L.bpt_attention_bwd.restype = ctypes.c_int
+        L.bpt_attention_bwd_profiled.argtypes = L.bpt_attention_bwd.argtypes + [P(ctypes.c_void_p)]
+        L.bpt_attention_bwd_profiled.restype = ctypes.c_int
         L.bpt_status_str.argtypes = [ctypes.c_int]
         L.bpt_status_str.restype = ctypes.c_char_p
         L.bpt_last_error.argtypes = []
@@ -187,6 +190,16 @@ def attention_bwd(desc: AttnDesc, q, k, v, o, do, lse, dq, dk, dv, workspace, st
     _check(lib().bpt_attention_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                    _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                    _ptr(workspace), nbytes, _stream(stream)))
+
+
+def attention_bwd_profiled(desc: AttnDesc, q, k, v, o, do, lse, dq, dk, dv, workspace, events,
+                           stream=None) -> None:
+    """attention_bwd recording 5 hipEvent_t handles between its kernels."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    arr = (ctypes.c_void_p * 5)(*events)
+    _check(lib().bpt_attention_bwd_profiled(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                            _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                            _ptr(workspace), nbytes, _stream(stream), arr))
 
 
 def stack_fwd(desc: LayerDesc, x, layers: list, z, workspace, stream=None) -> None:

@@ -31,6 +31,10 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
 KERNEL_SOURCES = ["k_ln_qkv.hip", "k_gemm.hip", "k_attention.hip", "k_ffn.hip", "k_pack.hip",
                   "k_attention_bwd.hip", "bpt_launch.hip"]
 HOST_SOURCES = ["bpt_api.cpp", "bpt_support.cpp"]
+# Per-source extra flags. The attention backward keeps its matrix-core results in
+# ordinary VGPRs (they feed the softmax arithmetic at once); left to itself the
+# compiler places them in AGPRs and copies every value back.
+EXTRA_FLAGS = {"k_attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -54,7 +58,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in KERNEL_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append([cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([cc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         jobs.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])

@@ -339,7 +339,19 @@ bpt_status_t bpt_attention_bwd(const bpt_attn_desc_t* desc, const void* Q, const
                                const void* V, const void* O, const void* dO, const float* lse,
                                float* dQ, float* dK, float* dV, void* workspace,
                                size_t workspace_bytes, void* hip_stream) {
+  return bpt_attention_bwd_profiled(desc, Q, K, V, O, dO, lse, dQ, dK, dV, workspace,
+                                    workspace_bytes, hip_stream, nullptr);
+}
+
+bpt_status_t bpt_attention_bwd_profiled(const bpt_attn_desc_t* desc, const void* Q, const void* K,
+                                        const void* V, const void* O, const void* dO,
+                                        const float* lse, float* dQ, float* dK, float* dV,
+                                        void* workspace, size_t workspace_bytes, void* hip_stream,
+                                        void* const events[5]) {
   g_err[0] = 0;
+  if (events)
+    for (int i = 0; i < 5; ++i)
+      if (!events[i]) return fail(BPT_ERR_NULL, "events[%d] is NULL", i);
   bpt_status_t st = validate_attn_desc(desc);
   if (st != BPT_OK) return st;
   if (attn_empty(desc)) return BPT_OK;
@@ -383,6 +395,7 @@ bpt_status_t bpt_attention_bwd(const bpt_attn_desc_t* desc, const void* Q, const
   p.stat_d = reinterpret_cast<float*>(ws);
   p.stat_l2 = reinterpret_cast<float*>(ws + sbytes);
   for (int i = 0; i < bpt::kAttnBwdPacked; ++i) p.packed[i] = ws + 2 * sbytes + (size_t)i * pbytes;
+  p.events = events;
   char msg[256] = "";
   if (bpt::launch_attention_bwd(p, hip_stream, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
   return BPT_OK;

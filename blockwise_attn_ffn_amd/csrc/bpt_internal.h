@@ -88,6 +88,8 @@ struct AttnBwdLaunch {
   float* stat_d;
   float* stat_l2;
   void* packed[kAttnBwdPacked];
+  // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
+  void* const* events;
 };
 
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).

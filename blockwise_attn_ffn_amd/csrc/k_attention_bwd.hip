@@ -110,6 +110,9 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(TransposeJob job, in
   }
 }
 
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+struct RuntimeTag {};   // decide the masking inside the body, around the softmax only
+
 struct BwdArgs {
   const bf16 *q, *k, *v, *dout;                   // row-major [B N, d]
   const bf16 *kT, *qT, *doT;                      // cols-A fragments per (sequence, head)
@@ -126,21 +129,21 @@ __device__ inline bf16x8 ld_row_frag(const bf16* X, int b, int pos, int N, int d
   return *reinterpret_cast<const bf16x8*>(X + ((size_t)b * N + pos) * d + f0);
 }
 
-// dQ: one workgroup of 4 waves per (sequence, head, 128-row query block); one lane
-// per query row. Key/value blocks of 64 keys are copied into LDS (K and V as A
+// dQ: one workgroup of NW waves per (sequence, head, 32 NW-row query block); one
+// lane per query row. Key/value blocks of 64 keys are copied into LDS (K and V as A
 // fragments over keys, straight from the row-major inputs; K^T as A fragments over
-// features from the transposed copy), two stages.
-template <int DK>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
+// features from the transposed copy), two stages shared by all NW waves.
+template <int DK, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
   using O = Op<bf16>;
   using F = O::frag;
-  constexpr int BQ = 128, BKV = 64, FB = 1024;
+  constexpr int BQ = 32 * NW, BKV = 64, FB = 1024;
   constexpr int KSD = DK / 16, KT = BKV / 32, DT = DK / 32, KK = BKV / 16;
   constexpr int KFR = KT * KSD;                 // K (and V) fragments per block
   constexpr int TFR = DT * KK;                  // K^T fragments per block
   constexpr int NFR = 2 * KFR + TFR;
-  constexpr int CPW = NFR / 4;
-  static_assert(NFR % 4 == 0, "copies per wave");
+  constexpr int CPW = NFR / NW;
+  static_assert(KFR % NW == 0 && TFR % NW == 0, "copies per wave");
   __shared__ __align__(16) unsigned char lds0[NFR * FB];
   __shared__ __align__(16) unsigned char lds1[NFR * FB];
 
@@ -153,22 +156,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
   const int kend = g.causal ? (min(qb * BQ + BQ, N) - 1) / BKV + 1 : (N + BKV - 1) / BKV;
   const int wave_q_first = qb * BQ + wave * 32, qpos = wave_q_first + rho;
   const int fcol = h * DK + 8 * hf;             // this lane's feature offset in a row
+  const int prho = pi_row(rho);
+  static_assert(KSD % NW == 0 && NW % KK == 0, "copy slots");
 
+  // Copy slot q of wave w moves fragment NW q + w of the stage, so that the kind of
+  // copy (K, V or K^T) and its tile are the same in every wave: fixed at compile
+  // time; the wave's own part of each address is a wave-uniform offset.
   auto issue = [&](int kb, unsigned char* buf) __attribute__((always_inline)) {
     const int kv0 = kb * BKV;
+    size_t rowoff[KT];                            // this lane's key row in each 32-key tile
+#pragma unroll
+    for (int t = 0; t < KT; ++t) rowoff[t] = ((size_t)b * N + min(kv0 + t * 32 + prho, N - 1)) * d + fcol;
+    // K^T fragment (dt, k-step) = (slot / KK, slot % KK); the wave adds (w / KK, w % KK)
+    const bf16* kt_base =
+        g.kT + (((size_t)bh * DT + wave / KK) * (Np / 16) + kv0 / 16 + wave % KK) * kFragElems + lane * 8;
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
-      const int f = wave * CPW + q;
+      const int f0 = NW * q;
       const bf16* src;
-      if (f < 2 * KFR) {
-        const int ff = f < KFR ? f : f - KFR, t = ff / KSD, kk = ff - t * KSD;
-        const int pos = min(kv0 + t * 32 + pi_row(rho), N - 1);
-        src = (f < KFR ? g.k : g.v) + ((size_t)b * N + pos) * d + fcol + kk * 16;
+      if (f0 < 2 * KFR) {
+        const int ff0 = f0 < KFR ? f0 : f0 - KFR, t = ff0 / KSD, kk = ff0 % KSD + wave;
+        src = (f0 < KFR ? g.k : g.v) + rowoff[t] + kk * 16;
       } else {
-        const int ff = f - 2 * KFR, dt = ff / KK, kk = ff - dt * KK;
-        src = g.kT + (((size_t)bh * DT + dt) * (Np / 16) + kv0 / 16 + kk) * kFragElems + lane * 8;
+        const int dt0 = (f0 - 2 * KFR) / KK;
+        src = kt_base + (size_t)dt0 * (Np / 16) * kFragElems;
       }
-      dma16(src, buf + f * FB);
+      dma16(src, buf + (f0 + wave) * FB);
     }
   };
 
@@ -179,8 +192,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
     qf[kk] = ld_row_frag(g.q, b, qpos, N, d, fcol + kk * 16);
     of[kk] = ld_row_frag(g.dout, b, qpos, N, d, fcol + kk * 16);
   }
-  const float l2 = g.L2[(size_t)bh * Np + qpos];   // +inf past N: P = 0 on that lane
-  const float Dq = g.Dp[(size_t)bh * Np + qpos];
+  // rows past N (the last block may reach beyond the padded Np rows): P = 0
+  const bool live = qpos < N;
+  const float l2 = live ? g.L2[(size_t)bh * Np + qpos] : __builtin_inff();
+  const float Dq = live ? g.Dp[(size_t)bh * Np + qpos] : 0.f;
   f32x16 dq[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x16{};
@@ -190,40 +205,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
     if (g.causal && kv0 > wave_q_first + 31) return;   // every key of the block is later
     const bool need_mask = (g.causal && kv0 + BKV - 1 > wave_q_first) || kv0 + BKV > N;
     f32x16 s[KT], dp[KT];
-#pragma unroll
-    for (int t = 0; t < KT; ++t) { s[t] = f32x16{}; dp[t] = f32x16{}; }
-#pragma unroll
-    for (int kk = 0; kk < KSD; ++kk)
-#pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        O::mma(s[t], ld_packed(reinterpret_cast<const bf16*>(buf + (t * KSD + kk) * FB), lane), qf[kk]);
-        O::mma(dp[t], ld_packed(reinterpret_cast<const bf16*>(buf + (KFR + t * KSD + kk) * FB), lane),
-               of[kk]);
-      }
+    F dsf[KK];
     // register i of tile t holds key kv0 + t*32 + (i&8)*2 + 8hf + (i&7)
     const int lim = (g.causal ? min(qpos, N - 1) : N - 1) - kv0 - 8 * hf;
-    F dsf[KK];
+    auto softmax_grad = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
+      for (int t = 0; t < KT; ++t) {
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        float v[8];
+        for (int gg = 0; gg < 2; ++gg) {
+          float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 8 * gg + e;
-          float p = fast_exp2(fmaf(s[t][i], g.scale_log2e, -l2));
-          if (need_mask && t * 32 + (i & 8) * 2 + (i & 7) > lim) p = 0.f;
-          v[e] = p * (dp[t][i] - Dq);
+          for (int e = 0; e < 8; ++e) {
+            const int i = 8 * gg + e;
+            float p = fast_exp2(fmaf(s[t][i], g.scale_log2e, -l2));
+            if (decltype(masked)::value && t * 32 + (i & 8) * 2 + (i & 7) > lim) p = 0.f;
+            v[e] = p * (dp[t][i] - Dq);
+          }
+          dsf[2 * t + gg] = O::from_f32(v);
         }
-        dsf[2 * t + gg] = O::from_f32(v);
       }
-    }
+    };
+    // The body branches around the softmax only: a body specialised per masking
+    // mode (straight-line) holds more registers live and measured no faster.
+    auto body = [&](RuntimeTag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+      for (int t = 0; t < KT; ++t) { s[t] = f32x16{}; dp[t] = f32x16{}; }
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
-        O::mma(dq[t], ld_packed(reinterpret_cast<const bf16*>(buf + (2 * KFR + t * KK + kk) * FB), lane),
-               dsf[kk]);
+      for (int kk = 0; kk < KSD; ++kk)
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          O::mma(s[t], ld_packed(reinterpret_cast<const bf16*>(buf + (t * KSD + kk) * FB), lane), qf[kk]);
+          O::mma(dp[t], ld_packed(reinterpret_cast<const bf16*>(buf + (KFR + t * KSD + kk) * FB), lane),
+                 of[kk]);
+        }
+      if (need_mask) softmax_grad(BoolTag<true>{});
+      else softmax_grad(BoolTag<false>{});
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          O::mma(dq[t], ld_packed(reinterpret_cast<const bf16*>(buf + (2 * KFR + t * KK + kk) * FB), lane),
+                 dsf[kk]);
+    };
+    body(RuntimeTag{});
   };
 
   issue(0, lds0);
@@ -239,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
     visit(kb + 1, lds1);
   }
   // register group gg of feature tile t holds features t*32 + 16gg + 8hf + [0, 8)
-  if (qpos < N) {
+  if (live) {
     float* out = g.dq + ((size_t)b * N + qpos) * d + (size_t)h * DK;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
@@ -253,22 +277,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs g) {
   }
 }
 
-// dK, dV: one workgroup of 4 waves per (sequence, head, 128-key block); one lane per
-// key. Query blocks of 64 rows are copied into LDS (Q and dO as A fragments over
-// queries from the row-major inputs, Q^T and dO^T from the transposed copies, and
-// the 64 rows' statistics), two stages.
-template <int DK>
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
+// dK, dV: one workgroup of NW waves per (sequence, head, 32 NW-key block); one lane
+// per key. Query blocks of BQS rows are copied into LDS (Q and dO as A fragments
+// over queries from the row-major inputs, Q^T and dO^T from the transposed copies,
+// and the rows' statistics), two stages shared by all NW waves.
+template <int DK, int NW, int BQS>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
   using O = Op<bf16>;
   using F = O::frag;
-  constexpr int BK = 128, BQS = 64, FB = 1024;
+  constexpr int BK = 32 * NW, FB = 1024;
   constexpr int KSD = DK / 16, QT = BQS / 32, DT = DK / 32, QK = BQS / 16;
   constexpr int AFR = QT * KSD;                 // Q (and dO) fragments per block
   constexpr int TFR = DT * QK;                  // Q^T (and dO^T) fragments per block
   constexpr int NFR = 2 * AFR + 2 * TFR;
-  constexpr int CPW = NFR / 4;
-  constexpr int STAGE = (NFR + 1) * FB;         // + statistics: L2 then Dp, 64 floats each
-  static_assert(NFR % 4 == 0, "copies per wave");
+  constexpr int CPW = NFR / NW;
+  constexpr int STAGE = (NFR + 1) * FB;         // + statistics: L2 then Dp, BQS floats each
+  static_assert(AFR % NW == 0 && TFR % NW == 0, "copies per wave");
   __shared__ __align__(16) unsigned char lds0[STAGE];
   __shared__ __align__(16) unsigned char lds1[STAGE];
 
@@ -282,29 +306,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
   const int nqs = (N + BQS - 1) / BQS;
   const int qs_begin = g.causal ? (kbk * BK) / BQS : 0;
   const int fcol = h * DK + 8 * hf;
+  const int prho = pi_row(rho);
+  static_assert(KSD % NW == 0 && NW % QK == 0, "copy slots");
 
+  // Copy slot q of wave w moves fragment NW q + w of the stage (the kind of copy is
+  // the same in every wave); wave 0 also copies the BQS rows' statistics.
   auto issue = [&](int qs, unsigned char* buf) __attribute__((always_inline)) {
     const int q0 = qs * BQS;
+    size_t rowoff[QT];                            // this lane's query row in each 32-row tile
+#pragma unroll
+    for (int t = 0; t < QT; ++t) rowoff[t] = ((size_t)b * N + min(q0 + t * 32 + prho, N - 1)) * d + fcol;
+    // Q^T / dO^T fragment (dt, k-step) = (slot / QK, slot % QK); the wave adds (w / QK, w % QK)
+    const size_t toff =
+        (((size_t)bh * DT + wave / QK) * (Np / 16) + q0 / 16 + wave % QK) * kFragElems + lane * 8;
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
-      const int f = wave * CPW + q;
+      const int f0 = NW * q;
       const bf16* src;
-      if (f < 2 * AFR) {
-        const int ff = f < AFR ? f : f - AFR, t = ff / KSD, kk = ff - t * KSD;
-        const int pos = min(q0 + t * 32 + pi_row(rho), N - 1);
-        src = (f < AFR ? g.q : g.dout) + ((size_t)b * N + pos) * d + fcol + kk * 16;
+      if (f0 < 2 * AFR) {
+        const int ff0 = f0 < AFR ? f0 : f0 - AFR, t = ff0 / KSD, kk = ff0 % KSD + wave;
+        src = (f0 < AFR ? g.q : g.dout) + rowoff[t] + kk * 16;
       } else {
-        const int f2 = f - 2 * AFR;
-        const bf16* base = f2 < TFR ? g.qT : g.doT;
-        const int ff = f2 < TFR ? f2 : f2 - TFR, dt = ff / QK, kk = ff - dt * QK;
-        src = base + (((size_t)bh * DT + dt) * (Np / 16) + q0 / 16 + kk) * kFragElems + lane * 8;
+        const int f2 = f0 - 2 * AFR;
+        const int dt0 = (f2 < TFR ? f2 : f2 - TFR) / QK;
+        src = (f2 < TFR ? g.qT : g.doT) + toff + (size_t)dt0 * (Np / 16) * kFragElems;
       }
-      dma16(src, buf + f * FB);
+      dma16(src, buf + (f0 + wave) * FB);
     }
     if (wave == 0) {
-      // lanes 0-15: L2[q0 .. q0+63], lanes 16-31: Dp[...]; lanes 32-63 repeat them
-      const int l = lane & 31;
-      const float* st = (l < 16 ? g.L2 : g.Dp) + (size_t)bh * Np + q0 + 4 * (l & 15);
+      // lanes [0, BQS/4): L2[q0, q0 + BQS), the next BQS/4 lanes: Dp; the rest repeat them
+      const int l = lane % (BQS / 2);
+      const float* st = (l < BQS / 4 ? g.L2 : g.Dp) + (size_t)bh * Np + q0 + 4 * (l % (BQS / 4));
       dma16(st, buf + NFR * FB);
     }
   };
@@ -325,52 +357,60 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
     if (g.causal && wave_k_first > q0 + BQS - 1) return;   // every query of the block is earlier
     const bool need_mask = g.causal && wave_k_first + 31 > q0;
     f32x16 s[QT], dp[QT];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) { s[t] = f32x16{}; dp[t] = f32x16{}; }
-#pragma unroll
-    for (int kk = 0; kk < KSD; ++kk)
-#pragma unroll
-      for (int t = 0; t < QT; ++t) {
-        O::mma(s[t], ld_packed(reinterpret_cast<const bf16*>(buf + (t * KSD + kk) * FB), lane), kf[kk]);
-        O::mma(dp[t], ld_packed(reinterpret_cast<const bf16*>(buf + (AFR + t * KSD + kk) * FB), lane),
-               vf[kk]);
-      }
+    F pf[QK], dsf[QK];
     // register i of tile t holds query q0 + t*32 + (i&8)*2 + 8hf + (i&7); lane holds key kpos
     const float* st = reinterpret_cast<const float*>(buf + NFR * FB);
-    F pf[QK], dsf[QK];
+    auto softmax_grad = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
+      for (int t = 0; t < QT; ++t) {
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int qoff = t * 32 + 16 * gg + 8 * hf;          // 8 consecutive queries
-        const float4 la = *reinterpret_cast<const float4*>(st + qoff);
-        const float4 lb = *reinterpret_cast<const float4*>(st + qoff + 4);
-        const float4 da = *reinterpret_cast<const float4*>(st + 64 + qoff);
-        const float4 db = *reinterpret_cast<const float4*>(st + 64 + qoff + 4);
-        const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-        const float d8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-        float pv[8], dv8[8];
+        for (int gg = 0; gg < 2; ++gg) {
+          const int qoff = t * 32 + 16 * gg + 8 * hf;          // 8 consecutive queries
+          const float4 la = *reinterpret_cast<const float4*>(st + qoff);
+          const float4 lb = *reinterpret_cast<const float4*>(st + qoff + 4);
+          const float4 da = *reinterpret_cast<const float4*>(st + BQS + qoff);
+          const float4 db = *reinterpret_cast<const float4*>(st + BQS + qoff + 4);
+          const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+          const float d8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+          float pv[8], dv8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float p = fast_exp2(fmaf(s[t][8 * gg + e], g.scale_log2e, -l8[e]));
-          if (need_mask && kpos > q0 + qoff + e) p = 0.f;
-          pv[e] = p;
-          dv8[e] = p * (dp[t][8 * gg + e] - d8[e]);
+          for (int e = 0; e < 8; ++e) {
+            float p = fast_exp2(fmaf(s[t][8 * gg + e], g.scale_log2e, -l8[e]));
+            if (decltype(masked)::value && kpos > q0 + qoff + e) p = 0.f;
+            pv[e] = p;
+            dv8[e] = p * (dp[t][8 * gg + e] - d8[e]);
+          }
+          pf[2 * t + gg] = O::from_f32(pv);
+          dsf[2 * t + gg] = O::from_f32(dv8);
         }
-        pf[2 * t + gg] = O::from_f32(pv);
-        dsf[2 * t + gg] = O::from_f32(dv8);
       }
-    }
+    };
+    // branching around the softmax only (as in dQ)
+    auto body = [&](RuntimeTag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < QK; ++kk)
+      for (int t = 0; t < QT; ++t) { s[t] = f32x16{}; dp[t] = f32x16{}; }
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        O::mma(dvacc[t],
-               ld_packed(reinterpret_cast<const bf16*>(buf + (2 * AFR + TFR + t * QK + kk) * FB), lane),
-               pf[kk]);
-        O::mma(dkacc[t], ld_packed(reinterpret_cast<const bf16*>(buf + (2 * AFR + t * QK + kk) * FB), lane),
-               dsf[kk]);
-      }
+      for (int kk = 0; kk < KSD; ++kk)
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+          O::mma(s[t], ld_packed(reinterpret_cast<const bf16*>(buf + (t * KSD + kk) * FB), lane), kf[kk]);
+          O::mma(dp[t], ld_packed(reinterpret_cast<const bf16*>(buf + (AFR + t * KSD + kk) * FB), lane),
+                 vf[kk]);
+        }
+      if (need_mask) softmax_grad(BoolTag<true>{});
+      else softmax_grad(BoolTag<false>{});
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk)
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          O::mma(dvacc[t],
+                 ld_packed(reinterpret_cast<const bf16*>(buf + (2 * AFR + TFR + t * QK + kk) * FB), lane),
+                 pf[kk]);
+          O::mma(dkacc[t],
+                 ld_packed(reinterpret_cast<const bf16*>(buf + (2 * AFR + t * QK + kk) * FB), lane), dsf[kk]);
+        }
+    };
+    body(RuntimeTag{});
   };
 
   issue(qs_begin, lds0);
@@ -407,6 +447,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs g) {
 
 namespace {
 
+int mark(const AttnBwdLaunch& L, int i, hipStream_t s, char* err, size_t n) {
+  if (!L.events) return 0;
+  const hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(L.events[i]), s);
+  if (e != hipSuccess) {
+    set_err(err, n, "hipEventRecord: %s", hipGetErrorString(e));
+    return 1;
+  }
+  return 0;
+}
+
 template <int DK>
 int run_bwd(const AttnBwdLaunch& L, hipStream_t s, char* err, size_t n) {
   // the kernels' shape assumptions
@@ -440,19 +490,27 @@ int run_bwd(const AttnBwdLaunch& L, hipStream_t s, char* err, size_t n) {
   g.scale_log2e = kLog2e * g.scale;
   const int bhs = L.batch * L.n_heads;
   const long long stat_threads = (long long)bhs * L.seq_pad * (DK / 8);
+  if (mark(L, 0, s, err, n)) return 1;
   hipLaunchKernelGGL(bwd_stats_kernel<DK>, dim3((unsigned)(stat_threads / 256)), dim3(256), 0, s,
                      g.dout, static_cast<const bf16*>(L.out), L.lse, L.stat_d, L.stat_l2, L.batch,
                      L.seq_len, L.seq_pad, L.n_heads);
-  if (check_launch("bwd_stats", err, n)) return 1;
+  if (check_launch("bwd_stats", err, n) || mark(L, 1, s, err, n)) return 1;
   TransposeJob job{{g.k, g.q, g.dout}, {kT, qT, doT}};
   hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(bhs * (L.seq_pad / 64) * (DK / 64)), 3),
                      dim3(256), 0, s, job, L.seq_len, L.seq_pad, L.n_heads, DK);
-  if (check_launch("bwd_transpose", err, n)) return 1;
-  const int nqb = (L.seq_len + 127) / 128, nkb = (L.seq_len + 127) / 128;
-  hipLaunchKernelGGL(bwd_dq_kernel<DK>, dim3(bhs * nqb), dim3(256), 0, s, g);
-  if (check_launch("bwd_dq", err, n)) return 1;
-  hipLaunchKernelGGL(bwd_dkv_kernel<DK>, dim3(bhs * nkb), dim3(256), 0, s, g);
-  return check_launch("bwd_dkv", err, n);
+  if (check_launch("bwd_transpose", err, n) || mark(L, 2, s, err, n)) return 1;
+  // d_k 128: 8 waves share each key/value stage (two per SIMD, 256 query rows);
+  // d_k 64: 4 waves, and two workgroups fit one compute unit
+  constexpr int DQW = DK == 128 ? 8 : 4;
+  // dK / dV: 4 waves and 64-row query stages (8 waves with 32-row stages would
+  // give two waves per SIMD at d_k 128, but the accumulators then spill: slower)
+  constexpr int DKW = 4, DKQ = 64;
+  const int nqb = (L.seq_len + 32 * DQW - 1) / (32 * DQW);
+  const int nkb = (L.seq_len + 32 * DKW - 1) / (32 * DKW);
+  hipLaunchKernelGGL((bwd_dq_kernel<DK, DQW>), dim3(bhs * nqb), dim3(64 * DQW), 0, s, g);
+  if (check_launch("bwd_dq", err, n) || mark(L, 3, s, err, n)) return 1;
+  hipLaunchKernelGGL((bwd_dkv_kernel<DK, DKW, DKQ>), dim3(bhs * nkb), dim3(64 * DKW), 0, s, g);
+  return check_launch("bwd_dkv", err, n) || mark(L, 4, s, err, n);
 }
 
 }  // namespace

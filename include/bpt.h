@@ -193,6 +193,17 @@ bpt_status_t bpt_attention_bwd(const bpt_attn_desc_t* desc, const void* Q, const
                                float* dQ, float* dK, float* dV, void* workspace,
                                size_t workspace_bytes, void* hip_stream);
 
+/* bpt_attention_bwd that also records five caller-created hipEvent_t handles
+ * (events: a HOST array of 5) on hip_stream, for timing each kernel: events[0]
+ * before the row statistics, [1] after them, [2] after the transposed copies,
+ * [3] after the dQ kernel, [4] after the dK / dV kernel. events may be NULL (then
+ * it is bpt_attention_bwd), but not a NULL entry (BPT_ERR_NULL). */
+bpt_status_t bpt_attention_bwd_profiled(const bpt_attn_desc_t* desc, const void* Q, const void* K,
+                                        const void* V, const void* O, const void* dO,
+                                        const float* lse, float* dQ, float* dK, float* dV,
+                                        void* workspace, size_t workspace_bytes, void* hip_stream,
+                                        void* const events[5]);
+
 /* n_layers >= 1 layers applied in turn, all with the shape of *desc; layers is
  * a HOST array of n_layers weight sets (each holding device pointers). Layer 0
  * reads X in desc->dtype; the residual stream between layers is fp32; the last

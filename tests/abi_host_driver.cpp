@@ -126,6 +126,13 @@ int main() {
   EXPECT((char*)bpt::g_bwd.packed[0] == aws + 2 * sbytes);
   EXPECT((char*)bpt::g_bwd.packed[2] == aws + 2 * sbytes + 2 * pbytes);
   EXPECT(bpt::g_bwd.q == in[0] && bpt::g_bwd.dout == in[4] && bpt::g_bwd.dv == outs[2]);
+  void* bev[5] = {fake(1), fake(2), fake(3), fake(4), fake(5)};
+  EXPECT(bpt_attention_bwd_profiled(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2],
+                                    aws, aneed, nullptr, bev) == BPT_OK);
+  EXPECT(bpt::g_bwd.events == bev);
+  bev[3] = nullptr;
+  EXPECT(bpt_attention_bwd_profiled(&a, in[0], in[1], in[2], in[3], in[4], alse, outs[0], outs[1], outs[2],
+                                    aws, aneed, nullptr, bev) == BPT_ERR_NULL);
   // inputs may coincide (Q = K, say)
   EXPECT(bpt_attention_bwd(&a, in[0], in[0], in[0], in[3], in[4], alse, outs[0], outs[1], outs[2], aws,
                            aneed, nullptr) == BPT_OK);
