@@ -104,7 +104,7 @@ def kernel_flops(w) -> dict:
     b, n, d, f = w.batch, w.seq_len, w.d_model, w.d_ff
     return {"prep": 0,
             "qkv": b * 6 * n * d * d,
-            "attention": b * A.attention_flops(n, d, w.causal),
+            "attention": b * A.attention_flops(n, d, w.causal, w.window, w.chunk),
             "ffn_epilogue": b * (2 * n * d * d + A.ffn_flops(n, d, f))}
 
 
@@ -152,7 +152,7 @@ def cpu_baseline(w, inputs, target_s: float) -> dict:
         t1 = run(1)
         k = int(max(1, min(w.batch, round(target_s / max(t1, 1e-3)))))
         t = run(k) if k > 1 else t1
-        flops = k * A.layer_flops(w.seq_len, w.d_model, w.d_ff, w.causal)
+        flops = k * A.layer_flops(w.seq_len, w.d_model, w.d_ff, w.causal, w.window, w.chunk)
         sample = f"{k} of {w.batch} sequences, full layer (unfused, fp64)"
     else:
         # sampled rows of one layer: K, V for the visible prefix, the rest per row
@@ -360,7 +360,8 @@ def main():
         for e in ev:
             hip.destroy(e)
 
-    total_flops = A.workload_flops(w.batch, w.seq_len, w.d_model, w.d_ff, w.causal, w.n_layers)
+    total_flops = A.workload_flops(w.batch, w.seq_len, w.d_model, w.d_ff, w.causal, w.n_layers,
+                                   w.window, w.chunk)
     tflops = total_flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     kf = kernel_flops(w)

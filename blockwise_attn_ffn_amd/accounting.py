@@ -14,11 +14,28 @@ Formulas from "Blockwise Parallel Transformer — BPT" (aicassindra.com):
 from __future__ import annotations
 
 
-def attention_flops(n: int, d: int, causal: bool) -> int:
-    """Score and value products of one sequence: 2 matmuls x 2 FLOP per multiply-add.
-    Without a mask 4 N^2 d; with the causal mask only the N (N + 1) / 2 visible
-    (query, key) pairs count, so 2 d N (N + 1)."""
-    return 2 * d * n * (n + 1) if causal else 4 * n * n * d
+def visible_pairs(n: int, causal: bool, window: int = 0, chunk: int = 0) -> int:
+    """(query, key) pairs one sequence's attention computes: N^2 without a mask,
+    N (N + 1) / 2 causal; a window w leaves min(p + 1, w) keys to query p; chunked
+    streaming with chunk C leaves min(N, (p // C + 1) C) keys to query p."""
+    if not causal:
+        return n * n
+    if window:
+        w = min(window, n)
+        return w * (w + 1) // 2 + (n - w) * w
+    if chunk:
+        full, rest = divmod(n, chunk)
+        # chunk c (0-based) holds C queries, each seeing (c + 1) C keys; the last,
+        # partial chunk's queries see all n keys
+        return chunk * chunk * full * (full + 1) // 2 + rest * n
+    return n * (n + 1) // 2
+
+
+def attention_flops(n: int, d: int, causal: bool, window: int = 0, chunk: int = 0) -> int:
+    """Score and value products of one sequence: 2 matmuls x 2 FLOP per multiply-add
+    over the visible (query, key) pairs: 4 N^2 d without a mask, 2 d N (N + 1)
+    causal (visible_pairs for the window and chunk masks)."""
+    return 4 * d * visible_pairs(n, causal, window, chunk)
 
 
 def attention_bwd_flops(n: int, d: int, causal: bool) -> int:
@@ -38,13 +55,15 @@ def ffn_flops(n: int, d: int, d_ff: int) -> int:
     return 4 * n * d * d_ff
 
 
-def layer_flops(n: int, d: int, d_ff: int, causal: bool) -> int:
+def layer_flops(n: int, d: int, d_ff: int, causal: bool, window: int = 0, chunk: int = 0) -> int:
     """Algorithmic FLOPs of one layer on one sequence of N tokens."""
-    return attention_flops(n, d, causal) + projection_flops(n, d) + ffn_flops(n, d, d_ff)
+    return (attention_flops(n, d, causal, window, chunk) + projection_flops(n, d)
+            + ffn_flops(n, d, d_ff))
 
 
-def workload_flops(batch: int, n: int, d: int, d_ff: int, causal: bool, n_layers: int = 1) -> int:
-    return batch * n_layers * layer_flops(n, d, d_ff, causal)
+def workload_flops(batch: int, n: int, d: int, d_ff: int, causal: bool, n_layers: int = 1,
+                   window: int = 0, chunk: int = 0) -> int:
+    return batch * n_layers * layer_flops(n, d, d_ff, causal, window, chunk)
 
 
 def attention_crossover_tokens(d: int) -> int:

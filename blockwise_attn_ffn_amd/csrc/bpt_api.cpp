@@ -88,6 +88,10 @@ bpt_status_t validate_desc(const bpt_layer_desc_t* d) {
     return fail(BPT_ERR_SHAPE, "d_model %d is not a multiple of n_heads %d", d->d_model, d->n_heads);
   if (d->block_q <= 0 || d->block_kv <= 0) return fail(BPT_ERR_SHAPE, "block sizes must be > 0");
   if (d->causal != 0 && d->causal != 1) return fail(BPT_ERR_SHAPE, "causal must be 0 or 1");
+  if (d->window < 0 || d->chunk < 0) return fail(BPT_ERR_SHAPE, "window and chunk must be >= 0");
+  if ((d->window || d->chunk) && !d->causal)
+    return fail(BPT_ERR_SHAPE, "window and chunk apply to the causal mask only");
+  if (d->window && d->chunk) return fail(BPT_ERR_SHAPE, "window and chunk cannot be combined");
   if (!(d->ln_eps > 0.0f) || !isfinite(d->ln_eps))
     return fail(BPT_ERR_SHAPE, "ln_eps must be finite and > 0");
   if ((d->dtype != BPT_F32 && d->dtype != BPT_BF16) ||
@@ -150,6 +154,8 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   p.block_q = d->block_q;
   p.block_kv = d->block_kv;
   p.causal = d->causal;
+  p.window = d->window;
+  p.chunk = d->chunk;
   p.ln_eps = d->ln_eps;
   p.compute_f32 = d->dtype == BPT_F32;
   p.seq_pad = (int)seq_pad_of(d);

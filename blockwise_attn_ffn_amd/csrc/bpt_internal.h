@@ -15,6 +15,7 @@ struct LayerLaunch {
   // shape
   int batch, seq_len, d_model, n_heads, d_head, d_ff;
   int block_q, block_kv, causal;
+  int window, chunk;   // attention masks on top of the causal one (0: none)
   float ln_eps;
   int compute_f32;   // 1: fp32 operands everywhere; 0: bf16 operands
   int x_f32;         // element type of X: 1 fp32, 0 bf16 (the weights' type otherwise)

@@ -52,11 +52,12 @@ __device__ inline float pair_sum(float x) {
 // (hi = bf16(v), lo = bf16(v - hi)), so that products keep ~16 significant bits:
 // S = Qhi Khi + Qhi Klo + Qlo Khi and O += Vhi Phi + Vlo Phi + Vhi Plo; O is written
 // as such a pair too. The LDS stage holds the hi fragments, then the lo ones.
-template <typename T, int DK, int BQ, int BKV, bool SPLIT = false>
+template <typename T, int DK, int BQ, int BKV, bool SPLIT = false, bool MASKED = false>
 __global__ __launch_bounds__(BQ * 2, (4 * BKV * DK * (int)sizeof(T) * (SPLIT ? 2 : 1) <= 65536) ? 2 : 1) void
 attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* QPlo,
                  const T* __restrict__ KPlo, const T* __restrict__ VPlo, int N, int Np, int H,
-                 int d, int causal, float scale_log2e, int nqb, int n_bh, float* lse) {
+                 int d, int causal, int window, int chunk, float scale_log2e, int nqb, int n_bh,
+                 float* lse) {
   using O = Op<T>;
   using F = typename O::frag;
   constexpr int NW = BQ / 32;
@@ -83,7 +84,6 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rho = lane & 31, hf = lane >> 5;
 
-  const int n_kvb = (N + BKV - 1) / BKV;
   const int n_pairs = causal ? (nqb + 1) / 2 : nqb;
   const int n_units = n_bh * n_pairs;
   int part = 0, nparts = 1, j = blockIdx.x, M = gridDim.x;
@@ -92,6 +92,20 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
   }
   const int u_hi = (int)((long long)n_units * (part + 1) / nparts);
 
+  // Visible keys of query position p (p past the end behaves as the last row):
+  // causal: [0, p]; window w: [p - w + 1, p]; chunk C: up to the end of p's chunk.
+  // MASKED instances (a window or chunk mask) evaluate the general form; the others
+  // compile to the plain causal / unmasked bounds.
+  auto key_hi = [&](int p) {
+    const int pc = min(p, N - 1);
+    if (!causal) return N - 1;
+    if constexpr (MASKED) return chunk ? min((pc / chunk + 1) * chunk, N) - 1 : pc;
+    return pc;
+  };
+  auto key_lo = [&](int p) {
+    if constexpr (MASKED) return window ? max(0, min(p, N - 1) - window + 1) : 0;
+    return 0;
+  };
   // ---- visit cursor (wave-uniform): unit u, half w of it, query block qb,
   //      key/value block kb of kend, (sequence, head) bh
   struct Cur { int u, w, qb, kb, kend, bh; };
@@ -103,8 +117,8 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
   };
   auto start_qblock = [&](Cur& c) {
     c.qb = qblock(c.u, c.w);
-    c.kb = 0;
-    c.kend = causal ? (min(c.qb * BQ + BQ, N) - 1) / BKV + 1 : n_kvb;
+    c.kb = key_lo(c.qb * BQ) / BKV;
+    c.kend = key_hi(c.qb * BQ + BQ - 1) / BKV + 1;
     c.bh = c.u / n_pairs;
   };
   auto advance = [&](Cur& c) {          // c.u >= u_hi afterwards means: no more visits
@@ -205,8 +219,8 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
     const int wave_q_first = c.qb * BQ + wave * 32, qpos = wave_q_first + rho;
     const bool last = c.kb == c.kend - 1;
     if (kPrefetchQ && last && nx.u < u_hi) load_q(nx, qn);
-    // a wave whose 32 rows all precede this block has nothing to add
-    if (!(causal && kv0 > wave_q_first + 31)) {
+    // a wave whose 32 rows see no key of this block has nothing to add
+    if (kv0 <= key_hi(wave_q_first + 31) && (!MASKED || kv0 + BKV - 1 >= key_lo(wave_q_first))) {
       // bf16: all K fragments of the block are read from LDS first (one wait per
       // product instead of a round trip each); V's are issued right after the
       // S products, in flight during the softmax
@@ -253,13 +267,15 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
       }
       // mask future keys and keys past the end (only blocks that can contain them):
       // register i of tile t holds key kv0 + t*32 + (i&8)*2 + 8hf + (i&7)
-      if ((kv0 + BKV > N) || (causal && kv0 + BKV - 1 > wave_q_first)) {
-        const int lim = (causal ? min(qpos, N - 1) : N - 1) - kv0 - 8 * hf;
+      if (kv0 + BKV - 1 > key_hi(wave_q_first) || (MASKED && kv0 < key_lo(wave_q_first + 31))) {
+        const int lim = key_hi(qpos) - kv0 - 8 * hf, lim_lo = key_lo(qpos) - kv0 - 8 * hf;
 #pragma unroll
         for (int t = 0; t < KT; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (t * 32 + (i & 8) * 2 + (i & 7) > lim) s[t][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int off = t * 32 + (i & 8) * 2 + (i & 7);
+            if (off > lim || (MASKED && off < lim_lo)) s[t][i] = -INFINITY;
+          }
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -277,7 +293,9 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
 #pragma unroll
         for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
       }
-      // p = exp2(s * scale - m); l sums p in fp32, P feeds the product in T
+      // p = exp2(s * scale - m); l sums p in fp32, P feeds the product in T. A row
+      // that has seen no key yet (a window's first blocks) has m = -inf: shift 0
+      const float m_use = (MASKED && m_run == -INFINITY) ? 0.f : m_run;
       float lsum = 0.f;
       F pf[KK], pl[SPLIT ? KK : 1];
 #pragma unroll
@@ -287,7 +305,7 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
           float p[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(fmaf(s[t][8 * g + e], scale_log2e, -m_run));
+            p[e] = fast_exp2(fmaf(s[t][8 * g + e], scale_log2e, -m_use));
             lsum += p[e];
           }
           pf[2 * t + g] = O::from_f32(p);
@@ -392,10 +410,10 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
 // step k+1, when they are first read. Work units are pairs of super-blocks
 // (S-1-p, p) with the causal mask, as for the one-group kernel.
 // ---------------------------------------------------------------------------
-template <int DK, int BKV>
+template <int DK, int BKV, bool MASKED = false>
 __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     bf16* QP, const bf16* __restrict__ KP, const bf16* __restrict__ VP, int N, int Np, int H,
-    int d, int causal, float scale_log2e, int nqb, int n_bh, float* lse) {
+    int d, int causal, int window, int chunk, float scale_log2e, int nqb, int n_bh, float* lse) {
   using O = Op<bf16>;
   using F = O::frag;
   constexpr int BQ = 128, NWG = 4, FB = 1024;
@@ -418,7 +436,6 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
   const uint32_t lane_off = (uint32_t)lane * 16u;
 
   const int nsb = (nqb + 1) / 2;               // super-blocks
-  const int n_kvb = (N + BKV - 1) / BKV;
   const int n_pairs = causal ? (nsb + 1) / 2 : nsb;
   const int n_units = n_bh * n_pairs;
   int part = 0, nparts = 1, j = blockIdx.x, M = gridDim.x;
@@ -427,6 +444,20 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
   }
   const int u_hi = (int)((long long)n_units * (part + 1) / nparts);
 
+  // Visible keys of query position p (p past the end behaves as the last row):
+  // causal: [0, p]; window w: [p - w + 1, p]; chunk C: up to the end of p's chunk.
+  // MASKED instances (a window or chunk mask) evaluate the general form; the others
+  // compile to the plain causal / unmasked bounds.
+  auto key_hi = [&](int p) {
+    const int pc = min(p, N - 1);
+    if (!causal) return N - 1;
+    if constexpr (MASKED) return chunk ? min((pc / chunk + 1) * chunk, N) - 1 : pc;
+    return pc;
+  };
+  auto key_lo = [&](int p) {
+    if constexpr (MASKED) return window ? max(0, min(p, N - 1) - window + 1) : 0;
+    return 0;
+  };
   // visit cursor over super-blocks (wave-uniform), as in the one-group kernel
   struct Cur { int u, w, sb, kb, kend, bh; };
   auto sblock = [&](int u, int w) {
@@ -437,8 +468,8 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
   };
   auto start_half = [&](Cur& c) {
     c.sb = sblock(c.u, c.w);
-    c.kb = 0;
-    c.kend = causal ? (min(c.sb * 2 * BQ + 2 * BQ, N) - 1) / BKV + 1 : n_kvb;
+    c.kb = key_lo(c.sb * 2 * BQ) / BKV;
+    c.kend = key_hi(c.sb * 2 * BQ + 2 * BQ - 1) / BKV + 1;
     c.bh = c.u / n_pairs;
   };
   auto advance = [&](Cur& c) {          // c.u >= u_hi afterwards: no more visits
@@ -548,8 +579,9 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     if (has_c) {
       const int qb = my_qb(c);
       const int wave_q_first = qb * BQ + wq * 32;
-      // a wave whose 32 rows all precede this block has nothing to add
-      if (qb >= 0 && !(causal && c.kb * BKV > wave_q_first + 31)) {
+      // a wave whose 32 rows see no key of this block has nothing to add
+      if (qb >= 0 && c.kb * BKV <= key_hi(wave_q_first + 31) &&
+          (!MASKED || c.kb * BKV + BKV - 1 >= key_lo(wave_q_first))) {
 #pragma unroll
         for (int t = 0; t < KT; ++t) s[t] = f32x16{};
         // K fragments of k-step kk+1 are read while the products of kk run
@@ -580,13 +612,15 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     const int wave_q_first = my_qb(c) * BQ + wq * 32, qpos = wave_q_first + rho;
     // mask future keys and keys past the end (only blocks that can contain them):
     // register i of tile t holds key kv0 + t*32 + (i&8)*2 + 8hf + (i&7)
-    if ((kv0 + BKV > N) || (causal && kv0 + BKV - 1 > wave_q_first)) {
-      const int lim = (causal ? min(qpos, N - 1) : N - 1) - kv0 - 8 * hf;
+    if (kv0 + BKV - 1 > key_hi(wave_q_first) || (MASKED && kv0 < key_lo(wave_q_first + 31))) {
+      const int lim = key_hi(qpos) - kv0 - 8 * hf, lim_lo = key_lo(qpos) - kv0 - 8 * hf;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (t * 32 + (i & 8) * 2 + (i & 7) > lim) s[t][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int off = t * 32 + (i & 8) * 2 + (i & 7);
+          if (off > lim || (MASKED && off < lim_lo)) s[t][i] = -INFINITY;
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -602,6 +636,7 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
 #pragma unroll
       for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
     }
+    const float m_use = (MASKED && m_run == -INFINITY) ? 0.f : m_run;   // no key seen yet
     float lsum = 0.f;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
@@ -610,7 +645,7 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(s[t][8 * g + e], scale_log2e, -m_run));
+          p[e] = fast_exp2(fmaf(s[t][8 * g + e], scale_log2e, -m_use));
           lsum += p[e];
         }
         pf[2 * t + g] = O::from_f32(p);
@@ -688,10 +723,13 @@ int run_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   int grid = device_cus() * per_cu;
   if (units < grid) grid = units;
   const float scale = 1.4426950408889634f / sqrtf((float)DK);
-  hipLaunchKernelGGL((attention_kernel<T, DK, BQ, BKV, SPLIT>), dim3(grid), dim3(BQ * 2), 0, s,
+  // window / chunk masks run the general-mask instance; plain causal or no mask the other
+  auto kern = (L.window || L.chunk) ? attention_kernel<T, DK, BQ, BKV, SPLIT, true>
+                                    : attention_kernel<T, DK, BQ, BKV, SPLIT, false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(BQ * 2), 0, s,
                      (T*)L.q, (const T*)L.k, (const T*)L.vt, (T*)L.q_lo, (const T*)L.k_lo,
-                     (const T*)L.vt_lo, L.seq_len, L.seq_pad, L.n_heads, L.d_model, L.causal, scale,
-                     nqb, n_bh, L.lse);
+                     (const T*)L.vt_lo, L.seq_len, L.seq_pad, L.n_heads, L.d_model, L.causal,
+                     L.window, L.chunk, scale, nqb, n_bh, L.lse);
   return check_launch("attention", err, n);
 }
 
@@ -704,9 +742,11 @@ int run_attn_pair(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   int grid = device_cus();
   if (units < grid) grid = units;
   const float scale = 1.4426950408889634f / sqrtf((float)DK);
-  hipLaunchKernelGGL((attention_pair_kernel<DK, BKV>), dim3(grid), dim3(512), 0, s, (bf16*)L.q,
+  auto kern = (L.window || L.chunk) ? attention_pair_kernel<DK, BKV, true>
+                                    : attention_pair_kernel<DK, BKV, false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, (bf16*)L.q,
                      (const bf16*)L.k, (const bf16*)L.vt, L.seq_len, L.seq_pad, L.n_heads,
-                     L.d_model, L.causal, scale, nqb, n_bh, L.lse);
+                     L.d_model, L.causal, L.window, L.chunk, scale, nqb, n_bh, L.lse);
   return check_launch("attention", err, n);
 }
 

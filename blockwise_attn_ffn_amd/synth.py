@@ -43,6 +43,8 @@ class Workload:
     ln_eps: float = 1e-5
     sample_rows: int = 0  # 0 = compare every row; otherwise sampled rows
     precision: int = 0    # 0: bf16 operands; 1: bf16 (hi, lo) pairs for computed operands
+    window: int = 0       # attention window (causal): query p sees keys p - window + 1 .. p
+    chunk: int = 0        # chunked streaming (causal): query p sees keys j with j // chunk <= p // chunk
 
     @property
     def rows(self) -> int:
@@ -56,7 +58,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads the library is measured and checked on.
+# The workloads the library is measured and checked on.
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", batch=1, seq_len=256, d_model=128, n_heads=2,
                           d_ff=512, causal=False, block_q=64, block_kv=64, dtype="f32"),
@@ -71,6 +73,11 @@ WORKLOADS = {
     "stack4_32k": Workload("stack4_32k", batch=1, seq_len=32768, d_model=4096, n_heads=32,
                            d_ff=16384, causal=True, block_q=128, block_kv=128, dtype="bf16",
                            n_layers=4, w_std_layer_decay=True, sample_rows=128, precision=1),
+    # the long-context layer with a 4096-token attention window (the window the
+    # transformer-cost page quotes for Mistral 7B)
+    "long_128k_w4096": Workload("long_128k_w4096", batch=1, seq_len=131072, d_model=2048,
+                                n_heads=16, d_ff=8192, causal=True, block_q=128, block_kv=64,
+                                dtype="bf16", sample_rows=256, window=4096),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}

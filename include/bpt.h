@@ -86,6 +86,12 @@ typedef struct {
                          values hi + lo (~16 significant bits), each product
                          taken over both halves; the FFN then runs staged (see
                          the workspace note)                                    */
+  int32_t window;     /* 0: none. w > 0 (causal only): query p sees keys
+                         max(0, p - w + 1) .. p ("transformer-cost" page, Section
+                         5, the windowed mask)                                  */
+  int32_t chunk;      /* 0: none. C > 0 (causal only, not with window): query p
+                         sees every key j with j / C <= p / C, its whole chunk and
+                         the earlier ones (same section, chunked streaming)     */
 } bpt_layer_desc_t;
 
 /* Device pointers to one layer's parameters (layouts above). */

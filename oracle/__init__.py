@@ -9,4 +9,4 @@ from .bpt_oracle import (WEIGHT_KEYS, attention_backward_dq_rows,  # noqa: F401
                          blockwise_layer_forward, gelu_tanh, layer_forward, layer_forward_rows,
                          layer_lse, layer_lse_rows, layer_norm,
                          max_abs_err, online_softmax_tiles, rel_fro_err, softmax_rows,
-                         stack_forward, stack_forward_rows)
+                         stack_forward, stack_forward_rows, visible)

@@ -24,6 +24,10 @@ Readings of points the pages leave open (each also listed in the design notes):
     1/sqrt(d_k); head outputs are concatenated in head order before W_O.
   * causal: query at position p sees key q iff q <= p (positions within one
     sequence); different sequences of a batch never attend to each other.
+  * masks of [COST]'s Section 5 (both on top of the causal mask): a window of w
+    keys, query p reads keys max(0, p - w + 1) .. p; chunked streaming with chunk
+    size C, query p reads every key of its own chunk and of earlier chunks,
+    j // C <= p // C.
 
 Every function below is float64 end to end. "Unfused" functions are the plain
 definition (full softmax, full [N, d_ff] hidden state); the blockwise function is
@@ -40,6 +44,44 @@ F64 = np.float64
 # The weight names of one layer, in the pages' notation.
 WEIGHT_KEYS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o",
                "ln2_g", "ln2_b", "w_1", "w_2")
+
+
+# ---------------------------------------------------------------------------
+# Which keys a query sees
+# ---------------------------------------------------------------------------
+
+def visible(q_pos: np.ndarray, k_pos: np.ndarray, causal: bool, window: int = 0,
+            chunk: int = 0) -> np.ndarray:
+    """[len(q_pos), len(k_pos)] booleans: key position j is visible to query
+    position p (positions within one sequence).
+      no mask:       every key;
+      causal:        j <= p;
+      window w > 0:  p - w < j <= p   ([COST] windowed mask: the oldest key query p
+                                       reads is max(0, p - w + 1));
+      chunk C > 0:   j // C <= p // C ([COST] chunked streaming: every token sees
+                                       its whole chunk, earlier chunks stay readable).
+    window and chunk apply to the causal setting only and not together."""
+    qp = np.asarray(q_pos, np.int64)[:, None]
+    kp = np.asarray(k_pos, np.int64)[None, :]
+    assert window >= 0 and chunk >= 0 and not (window and chunk)
+    if not causal:
+        assert window == 0 and chunk == 0
+        return np.ones((qp.shape[0], kp.shape[1]), dtype=bool)
+    if chunk:
+        return kp // chunk <= qp // chunk
+    vis = kp <= qp
+    if window:
+        vis &= kp > qp - window
+    return vis
+
+
+def keys_needed(pos_max: int, seq_len: int, causal: bool, chunk: int = 0) -> int:
+    """Number of leading keys of a sequence that queries up to position pos_max can see."""
+    if not causal:
+        return seq_len
+    if chunk:
+        return min(seq_len, (pos_max // chunk + 1) * chunk)
+    return pos_max + 1
 
 
 # ---------------------------------------------------------------------------
@@ -82,7 +124,7 @@ def softmax_rows(s: np.ndarray) -> np.ndarray:
 
 def attention_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
                        causal: bool, q_pos: np.ndarray | None = None,
-                       q_chunk: int | None = None) -> np.ndarray:
+                       q_chunk: int | None = None, window: int = 0, chunk: int = 0) -> np.ndarray:
     """Multi-head attention of one sequence with a full softmax.
 
     q: [nq, d] queries at positions q_pos (default 0..nq-1); k, v: [nk, d] keys and
@@ -92,11 +134,13 @@ def attention_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int
     q_chunk, if given, evaluates the query rows in groups of that many rows to
     bound memory; every row's scores, softmax and output are the same (rows are
     independent: [BPT] fused algorithm, outer loop over query blocks).
+    window / chunk: the masks of `visible`.
     """
     if q_chunk is not None and q.shape[0] > q_chunk:
         qp = np.arange(q.shape[0]) if q_pos is None else np.asarray(q_pos)
         return np.concatenate([attention_sequence(q[c:c + q_chunk], k, v, n_heads, causal,
-                                                  q_pos=qp[c:c + q_chunk])
+                                                  q_pos=qp[c:c + q_chunk], window=window,
+                                                  chunk=chunk)
                                for c in range(0, q.shape[0], q_chunk)])
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
@@ -109,7 +153,7 @@ def attention_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int
     out = np.empty((nq, d), dtype=F64)
     scale = 1.0 / math.sqrt(dk)
     if causal:
-        hidden = np.arange(nk)[None, :] > np.asarray(q_pos)[:, None]
+        hidden = ~visible(q_pos, np.arange(nk), causal, window, chunk)
     for h in range(n_heads):
         cols = slice(h * dk, (h + 1) * dk)
         s = (q[:, cols] @ k[:, cols].T) * scale
@@ -120,7 +164,8 @@ def attention_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int
 
 
 def attention_lse_sequence(q: np.ndarray, k: np.ndarray, n_heads: int, causal: bool,
-                           q_pos: np.ndarray | None = None) -> np.ndarray:
+                           q_pos: np.ndarray | None = None, window: int = 0,
+                           chunk: int = 0) -> np.ndarray:
     """Per head and query row, the natural log of the softmax normaliser of the
     scaled scores: lse[h, i] = log sum_{j visible to i} exp(q_i . k_j / sqrt(d_k)).
 
@@ -142,7 +187,7 @@ def attention_lse_sequence(q: np.ndarray, k: np.ndarray, n_heads: int, causal: b
     scale = 1.0 / math.sqrt(dk)
     out = np.empty((n_heads, nq), dtype=F64)
     if causal:
-        hidden = np.arange(nk)[None, :] > np.asarray(q_pos)[:, None]
+        hidden = ~visible(q_pos, np.arange(nk), causal, window, chunk)
     for h in range(n_heads):
         cols = slice(h * dk, (h + 1) * dk)
         s = (q[:, cols] @ k[:, cols].T) * scale
@@ -154,7 +199,7 @@ def attention_lse_sequence(q: np.ndarray, k: np.ndarray, n_heads: int, causal: b
 
 
 def layer_lse(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal: bool,
-              eps: float = 1e-5) -> np.ndarray:
+              eps: float = 1e-5, window: int = 0, chunk: int = 0) -> np.ndarray:
     """The attention statistics of one layer: [B, n_heads, seq_len], lse of every
     row of every sequence (attention_lse_sequence on Q = LN1(x) W_Q, K = LN1(x) W_K)."""
     x = np.asarray(x, F64)
@@ -164,12 +209,14 @@ def layer_lse(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal: boo
     x1 = layer_norm(x, p["ln1_g"], p["ln1_b"], eps)
     q = x1 @ p["w_q"]
     k = x1 @ p["w_k"]
-    return np.stack([attention_lse_sequence(q[s0:s0 + seq_len], k[s0:s0 + seq_len], n_heads, causal)
+    return np.stack([attention_lse_sequence(q[s0:s0 + seq_len], k[s0:s0 + seq_len], n_heads, causal,
+                                            window=window, chunk=chunk)
                      for s0 in range(0, rows, seq_len)])
 
 
 def layer_lse_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int, n_heads: int,
-                   causal: bool, eps: float = 1e-5, row_chunk: int = 4096) -> np.ndarray:
+                   causal: bool, eps: float = 1e-5, row_chunk: int = 4096, window: int = 0,
+                   chunk: int = 0) -> np.ndarray:
     """layer_lse at the given global rows only: [len(rows), n_heads]. Keys are formed
     for the prefix each sampled query can see (in chunks of row_chunk rows, for
     memory), queries for the sampled rows."""
@@ -182,13 +229,14 @@ def layer_lse_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int, n_
         sel = np.nonzero(seq_of == sidx)[0]
         pos = rows[sel] - sidx * seq_len
         base = sidx * seq_len
-        n_keys = int(pos.max()) + 1 if causal else seq_len
+        n_keys = keys_needed(int(pos.max()), seq_len, causal, chunk)
         k = np.empty((n_keys, x.shape[1]), F64)
         for c0 in range(0, n_keys, row_chunk):
             c1 = min(n_keys, c0 + row_chunk)
             k[c0:c1] = layer_norm(x[base + c0: base + c1], p["ln1_g"], p["ln1_b"], eps) @ p["w_k"]
         q = layer_norm(x[base + pos], p["ln1_g"], p["ln1_b"], eps) @ p["w_q"]
-        out[sel] = attention_lse_sequence(q, k, n_heads, causal, q_pos=pos).T
+        out[sel] = attention_lse_sequence(q, k, n_heads, causal, q_pos=pos, window=window,
+                                          chunk=chunk).T
     return out
 
 
@@ -299,7 +347,8 @@ def _as_f64_layer(p: dict) -> dict:
 
 
 def layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal: bool,
-                  eps: float = 1e-5, return_parts: bool = False, q_chunk: int | None = None):
+                  eps: float = 1e-5, return_parts: bool = False, q_chunk: int | None = None,
+                  window: int = 0, chunk: int = 0):
     """One pre-LN layer, unfused ([BPT] fused-algorithm section, last paragraph: the
     whole [N, d] attention output first, then a full [N, d_ff] hidden state).
 
@@ -321,7 +370,8 @@ def layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal:
     a = np.empty_like(x)
     for s0 in range(0, rows, seq_len):
         sl = slice(s0, s0 + seq_len)
-        a[sl] = attention_sequence(q[sl], k[sl], v[sl], n_heads, causal, q_chunk=q_chunk)
+        a[sl] = attention_sequence(q[sl], k[sl], v[sl], n_heads, causal, q_chunk=q_chunk,
+                                   window=window, chunk=chunk)
     y = x + a @ p["w_o"]
     hidden = gelu_tanh(layer_norm(y, p["ln2_g"], p["ln2_b"], eps) @ p["w_1"])
     z = y + hidden @ p["w_2"]
@@ -332,7 +382,7 @@ def layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int, causal:
 
 def layer_forward_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int,
                        n_heads: int, causal: bool, eps: float = 1e-5,
-                       row_chunk: int = 4096) -> np.ndarray:
+                       row_chunk: int = 4096, window: int = 0, chunk: int = 0) -> np.ndarray:
     """The same layer, evaluated only at the given output rows (global row indices).
 
     Keys and values are computed for every row a sampled query can see (with
@@ -352,7 +402,7 @@ def layer_forward_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int
         sel = np.nonzero(seq_of == sidx)[0]
         pos = rows[sel] - sidx * seq_len
         base = sidx * seq_len
-        n_keys = int(pos.max()) + 1 if causal else seq_len
+        n_keys = keys_needed(int(pos.max()), seq_len, causal, chunk)
         k = np.empty((n_keys, d), F64)
         v = np.empty((n_keys, d), F64)
         for c0 in range(0, n_keys, row_chunk):
@@ -362,7 +412,7 @@ def layer_forward_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int
             v[c0:c1] = xk @ p["w_v"]
         xq = x[base + pos]
         q = layer_norm(xq, p["ln1_g"], p["ln1_b"], eps) @ p["w_q"]
-        a = attention_sequence(q, k, v, n_heads, causal, q_pos=pos)
+        a = attention_sequence(q, k, v, n_heads, causal, q_pos=pos, window=window, chunk=chunk)
         y = xq + a @ p["w_o"]
         hidden = gelu_tanh(layer_norm(y, p["ln2_g"], p["ln2_b"], eps) @ p["w_1"])
         out[sel] = y + hidden @ p["w_2"]
@@ -370,27 +420,28 @@ def layer_forward_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int
 
 
 def stack_forward(x: np.ndarray, layers: list, *, seq_len: int, n_heads: int,
-                  causal: bool, eps: float = 1e-5) -> np.ndarray:
+                  causal: bool, eps: float = 1e-5, window: int = 0, chunk: int = 0) -> np.ndarray:
     """L layers applied in turn, Z_l = layer_l(Z_{l-1}), in float64 with no rounding
     between layers and no final LN."""
     z = np.asarray(x, F64)
     for p in layers:
-        z = layer_forward(z, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps)
+        z = layer_forward(z, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps,
+                          window=window, chunk=chunk)
     return z
 
 
 def stack_forward_rows(x: np.ndarray, layers: list, rows: np.ndarray, *, seq_len: int,
                        n_heads: int, causal: bool, eps: float = 1e-5,
-                       q_chunk: int | None = None) -> np.ndarray:
+                       q_chunk: int | None = None, window: int = 0, chunk: int = 0) -> np.ndarray:
     """Sampled rows of the stack's output: every layer but the last in full (a causal
     row depends on all earlier rows of every earlier layer), the last one at the
     sampled rows only. q_chunk bounds the attention's memory (attention_sequence)."""
     z = np.asarray(x, F64)
     for p in layers[:-1]:
         z = layer_forward(z, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps,
-                          q_chunk=q_chunk)
+                          q_chunk=q_chunk, window=window, chunk=chunk)
     return layer_forward_rows(z, layers[-1], rows, seq_len=seq_len, n_heads=n_heads,
-                              causal=causal, eps=eps)
+                              causal=causal, eps=eps, window=window, chunk=chunk)
 
 
 # ---------------------------------------------------------------------------
@@ -423,7 +474,7 @@ def online_softmax_tiles(s: np.ndarray, v: np.ndarray, tile: int):
 
 def blockwise_layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int,
                             causal: bool, block_q: int, block_kv: int,
-                            eps: float = 1e-5) -> np.ndarray:
+                            eps: float = 1e-5, window: int = 0, chunk: int = 0) -> np.ndarray:
     """The fused blockwise layer, one sequence at a time ([BPT] fused algorithm).
 
     Outer loop over query blocks i; per head an inner loop over key/value blocks j
@@ -433,6 +484,9 @@ def blockwise_layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: in
     block skipping), the rest are masked per element. Then the body finishes the
     block: y_i = x_i + (o / l) W_O, h_i = act(LN(y_i) W_1), Z[i] = y_i + h_i W_2.
     Ragged tails (seq_len not a multiple of the block sizes) use shorter last blocks.
+    With a window or chunk mask (`visible`) the blocks no query of the block sees
+    are skipped the same way; a row that sees no key of a visited block keeps its
+    state (its shift stays 0 while its maximum is -inf).
     Slow; meant for small inputs.
     """
     x = np.asarray(x, F64)
@@ -451,10 +505,14 @@ def blockwise_layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: in
             m = np.full((n_heads, nb), -np.inf)
             l = np.zeros((n_heads, nb))
             o = np.zeros((n_heads, nb, dk))
+            last_key = keys_needed(i1 - 1, seq_len, causal, chunk) - 1
+            first_key = max(0, i0 - window + 1) if window else 0
             for j0 in range(0, seq_len, block_kv):
-                if causal and j0 > i1 - 1:
+                if j0 > last_key:
                     break                      # block entirely in the future: skipped
                 j1 = min(seq_len, j0 + block_kv)
+                if j1 - 1 < first_key:
+                    continue                   # block entirely before every row's window
                 xj = layer_norm(xs[j0:j1], p["ln1_g"], p["ln1_b"], eps)
                 k_j = xj @ p["w_k"]
                 v_j = xj @ p["w_v"]
@@ -462,8 +520,8 @@ def blockwise_layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: in
                     cols = slice(h * dk, (h + 1) * dk)
                     s = (q_i[:, cols] @ k_j[:, cols].T) * scale
                     if causal:
-                        fut = np.arange(j0, j1)[None, :] > np.arange(i0, i1)[:, None]
-                        s = np.where(fut, -np.inf, s)
+                        vis = visible(np.arange(i0, i1), np.arange(j0, j1), causal, window, chunk)
+                        s = np.where(vis, s, -np.inf)
                     m_new = np.maximum(m[h], s.max(axis=1))
                     shift = np.where(np.isfinite(m_new), m_new, 0.0)
                     alpha = np.where(np.isfinite(m[h]), np.exp(m[h] - shift), 0.0)

@@ -77,14 +77,14 @@ def oracle_full(w: synth.Workload, inputs: dict, seqs=None) -> np.ndarray:
         x = np.concatenate([x[s * w.seq_len:(s + 1) * w.seq_len] for s in seqs])
     layers = [synth.oracle_weights(l) for l in inputs["layers"]]
     return oracle.stack_forward(x, layers, seq_len=w.seq_len, n_heads=w.n_heads,
-                                causal=w.causal, eps=w.ln_eps)
+                                causal=w.causal, eps=w.ln_eps, window=w.window, chunk=w.chunk)
 
 
 def oracle_rows(w: synth.Workload, inputs: dict, rows: np.ndarray) -> np.ndarray:
     x = synth.to_f64(inputs["x"])
     layers = [synth.oracle_weights(l) for l in inputs["layers"]]
     return oracle.stack_forward_rows(x, layers, rows, seq_len=w.seq_len, n_heads=w.n_heads,
-                                     causal=w.causal, eps=w.ln_eps)
+                                     causal=w.causal, eps=w.ln_eps, window=w.window, chunk=w.chunk)
 
 
 def seq_rows(w: synth.Workload, seqs) -> np.ndarray:

@@ -155,6 +155,7 @@ def call_layer(dsc, x=FAKE, z=FAKE + (1 << 36), ws=FAKE + (2 << 36), nbytes=1 <<
     ("dtype", 7, 2), ("out_dtype", -1, 2), ("act", 1, 3), ("precision", 2, 2),
     ("d_model", 640, 3), ("n_heads", 8, 3),           # d_head 32
     ("block_q", 96, 3), ("block_kv", 256, 3), ("d_ff", 1000, 3),
+    ("window", -1, 2), ("chunk", -3, 2),
 ])
 def test_invalid_descriptor(field, value, status):
     dsc = desc()
@@ -162,6 +163,23 @@ def test_invalid_descriptor(field, value, status):
     assert call_layer(dsc) == status
     assert bpt.last_error() != ""
     assert bpt.layer_workspace_bytes(dsc) == 0
+
+
+def test_mask_combinations():
+    """window and chunk need the causal mask and cannot be combined."""
+    dsc = desc(causal=0)
+    dsc.window = 16
+    assert call_layer(dsc) == 2 and "causal" in bpt.last_error()
+    dsc = desc(causal=0)
+    dsc.chunk = 16
+    assert call_layer(dsc) == 2
+    dsc = desc(causal=1)
+    dsc.window, dsc.chunk = 16, 16
+    assert call_layer(dsc) == 2 and "combined" in bpt.last_error()
+    for field in ("window", "chunk"):          # valid: the workspace does not change
+        dsc = desc(causal=1)
+        setattr(dsc, field, 100)
+        assert bpt.layer_workspace_bytes(dsc) == bpt.layer_workspace_bytes(desc(causal=1)) > 0
 
 
 def test_row_count_overflow():

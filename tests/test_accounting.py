@@ -70,3 +70,20 @@ def test_workload_flops_of_the_five_workloads():
     assert round(A.workload_flops(64, 1024, 1024, 4096, True) / 1e12, 3) == 1.787
     assert round(A.workload_flops(1, 131072, 2048, 8192, True) / 1e12, 2) == 83.56
     assert round(A.workload_flops(1, 32768, 4096, 16384, True, 4) / 1e12, 2) == 87.96
+
+
+@pytest.mark.parametrize("n", [1, 7, 64, 130, 257])
+@pytest.mark.parametrize("mask", [dict(), dict(window=1), dict(window=5), dict(window=64),
+                                  dict(window=1000), dict(chunk=1), dict(chunk=3), dict(chunk=16),
+                                  dict(chunk=1000)])
+def test_visible_pairs_count_by_brute_force(n, mask):
+    w, c = mask.get("window", 0), mask.get("chunk", 0)
+    count = 0
+    for p in range(n):
+        for j in range(n):
+            if c:
+                count += j // c <= p // c
+            else:
+                count += j <= p and (not w or j > p - w)
+    assert A.visible_pairs(n, True, **mask) == count
+    assert A.visible_pairs(n, False) == n * n

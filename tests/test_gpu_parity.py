@@ -330,7 +330,8 @@ def oracle_lse(w, inp, seqs=None):
     if seqs is not None:
         x = np.concatenate([x[s * w.seq_len:(s + 1) * w.seq_len] for s in seqs])
     return oracle.layer_lse(x, synth.oracle_weights(inp["layers"][0]), seq_len=w.seq_len,
-                            n_heads=w.n_heads, causal=w.causal, eps=w.ln_eps)
+                            n_heads=w.n_heads, causal=w.causal, eps=w.ln_eps, window=w.window,
+                            chunk=w.chunk)
 
 
 @pytest.mark.parametrize("case", [

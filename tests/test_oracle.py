@@ -320,13 +320,13 @@ def test_pins_catch_planted_oracle_mistakes(mutation, monkeypatch):
     if mutation == "scale_1_over_dk":
         orig = O.attention_sequence
 
-        def bad(q, k, v, n_heads, causal, q_pos=None, q_chunk=None):
-            return orig(q * math.sqrt(d // n_heads) ** -1, k, v, n_heads, causal, q_pos, q_chunk)
+        def bad(q, k, v, n_heads, causal, q_pos=None, q_chunk=None, **kw):
+            return orig(q * math.sqrt(d // n_heads) ** -1, k, v, n_heads, causal, q_pos, q_chunk, **kw)
         monkeypatch.setattr(O, "attention_sequence", bad)
     elif mutation == "no_causal_mask":
         orig = O.attention_sequence
         monkeypatch.setattr(O, "attention_sequence",
-                            lambda q, k, v, n_heads, causal, q_pos=None, q_chunk=None:
+                            lambda q, k, v, n_heads, causal, q_pos=None, q_chunk=None, **kw:
                             orig(q, k, v, n_heads, False, q_pos, q_chunk))
     elif mutation == "erf_gelu":
         monkeypatch.setattr(O, "gelu_tanh", lambda u: 0.5 * u * (1 + scipy.special.erf(u / math.sqrt(2))))
@@ -598,3 +598,119 @@ def test_attention_backward_kv_rows_equal_full(causal):
         assert np.max(np.abs(got_k - dk[rows])) < 1e-12
         assert np.max(np.abs(got_v - dv[rows])) < 1e-12
         assert np.max(np.abs(got_v[-1])) > 0          # key 18 is seen by query 18 (live)
+
+
+# --------------------------------------------------------------------------
+# Window and chunked-streaming masks (transformer-cost page, Section 5)
+# --------------------------------------------------------------------------
+
+def _mask_pins(attn):
+    """True iff attn(q, k, v, h, causal, window=, chunk=) -> [n, d] passes the mask pins."""
+    rng = np.random.default_rng(41)
+    n, d, h = 13, 8, 2
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    causal = oracle.attention_sequence(q, k, v, h, True)
+    full = oracle.attention_sequence(q, k, v, h, False)
+    checks = [
+        np.max(np.abs(attn(q, k, v, h, True, window=1) - v)) < 1e-12,        # a token sees only itself
+        np.max(np.abs(attn(q, k, v, h, True, window=n) - causal)) < 1e-12,   # full length: causal
+        np.max(np.abs(attn(q, k, v, h, True, window=n + 5) - causal)) < 1e-12,
+        np.max(np.abs(attn(q, k, v, h, True, chunk=1) - causal)) < 1e-12,    # chunk 1: causal
+        np.max(np.abs(attn(q, k, v, h, True, chunk=n) - full)) < 1e-12,      # whole length: no mask
+    ]
+    # the page's example: chunk size 4, token 9 reads tokens 10 and 11 but not 12
+    for key, seen in ((10, True), (11, True), (12, False), (8, True)):
+        k2 = k.copy()
+        k2[key] += 1.0
+        moved = np.max(np.abs(attn(q, k2, v, h, True, chunk=4)[9] - attn(q, k, v, h, True, chunk=4)[9])) > 1e-9
+        checks.append(moved == seen)
+    # window w: row i reads key i - w + 1 and not key i - w
+    w, i = 4, 10
+    for key, seen in ((i - w + 1, True), (i - w, False), (i, True)):
+        k2 = k.copy()
+        k2[key] += 1.0
+        moved = np.max(np.abs(attn(q, k2, v, h, True, window=w)[i] - attn(q, k, v, h, True, window=w)[i])) > 1e-9
+        checks.append(moved == seen)
+    return all(checks)
+
+
+def test_mask_pins_hold_for_the_oracle():
+    assert _mask_pins(oracle.attention_sequence)
+
+
+def test_mask_pins_catch_planted_mistakes():
+    base = oracle.attention_sequence
+
+    def shifted_window(q, k, v, h, causal, window=0, chunk=0):
+        return base(q, k, v, h, causal, window=window + 1 if window else 0, chunk=chunk)
+
+    def chunk_as_causal_within(q, k, v, h, causal, window=0, chunk=0):
+        # keys of the own chunk only up to the query (a plain causal mask inside the chunk)
+        return base(q, k, v, h, causal, window=window) if chunk else base(q, k, v, h, causal, window=window)
+
+    def chunk_next_chunk(q, k, v, h, causal, window=0, chunk=0):
+        # one chunk too many: the next chunk visible as well
+        return base(q, k, v, h, causal, window=window, chunk=2 * chunk) if chunk else base(
+            q, k, v, h, causal, window=window)
+
+    for planted in (shifted_window, chunk_as_causal_within, chunk_next_chunk):
+        assert not _mask_pins(planted), planted.__name__
+
+
+@pytest.mark.parametrize("mask", [dict(window=3), dict(window=17), dict(chunk=5), dict(chunk=16)])
+def test_masked_attention_matches_torch_sdpa_with_explicit_mask(mask):
+    """The masked softmax attention itself against torch's float64 SDPA given the same
+    boolean mask (built here by a loop over the page's rule)."""
+    rng = np.random.default_rng(43)
+    n, d, h = 37, 16, 2
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    allowed = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        if "window" in mask:
+            allowed[i, max(0, i - mask["window"] + 1):i + 1] = True
+        else:
+            allowed[i, :min(n, (i // mask["chunk"] + 1) * mask["chunk"])] = True
+    split = lambda a: torch.from_numpy(a.copy()).view(n, h, d // h).transpose(0, 1)[None]  # noqa: E731
+    ref = F.scaled_dot_product_attention(split(q), split(k), split(v),
+                                         attn_mask=torch.from_numpy(allowed))
+    ref = ref[0].transpose(0, 1).reshape(n, d).numpy()
+    got = oracle.attention_sequence(q, k, v, h, True, **mask)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("mask", [dict(window=5), dict(window=40), dict(chunk=7), dict(chunk=32)])
+def test_blockwise_loop_with_masks_equals_unfused(mask):
+    rng = np.random.default_rng(45)
+    seq, d, h = 45, 16, 2
+    x = rng.standard_normal((2 * seq, d))
+    p = rand_layer(rng, d, 64, std=0.3)
+    ref = oracle.layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, **mask)
+    for bq, bkv in ((8, 8), (16, 4), (4, 16)):
+        got = oracle.blockwise_layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, block_q=bq,
+                                             block_kv=bkv, **mask)
+        assert np.max(np.abs(got - ref)) < 1e-10, (bq, bkv)
+
+
+@pytest.mark.parametrize("mask", [dict(window=6), dict(chunk=8)])
+def test_masked_rows_and_lse_equal_full(mask):
+    rng = np.random.default_rng(47)
+    seq, d, h = 40, 16, 2
+    x = rng.standard_normal((2 * seq, d))
+    p = rand_layer(rng, d, 64, std=0.3)
+    rows = np.array([0, 5, 17, 39, 40, 47, 79])
+    full = oracle.layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, **mask)
+    got = oracle.layer_forward_rows(x, p, rows, seq_len=seq, n_heads=h, causal=True, **mask)
+    assert np.max(np.abs(got - full[rows])) < 1e-12
+    lse = oracle.layer_lse(x, p, seq_len=seq, n_heads=h, causal=True, **mask)
+    lse_r = oracle.layer_lse_rows(x, p, rows, seq_len=seq, n_heads=h, causal=True, **mask)
+    assert np.max(np.abs(lse_r - lse[rows // seq, :, rows % seq])) < 1e-12
+
+
+def test_window_one_lse_is_the_diagonal_score():
+    rng = np.random.default_rng(49)
+    n, d, h = 9, 8, 2
+    q, k = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    lse = oracle.attention_lse_sequence(q, k, h, True, window=1)
+    for hh in range(h):
+        c = slice(hh * 4, hh * 4 + 4)
+        assert np.max(np.abs(lse[hh] - (q[:, c] * k[:, c]).sum(1) / 2.0)) < 1e-12
