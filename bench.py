@@ -103,7 +103,7 @@ def kernel_flops(w) -> dict:
     from blockwise_attn_ffn_amd import accounting as A
     b, n, d, f = w.batch, w.seq_len, w.d_model, w.d_ff
     return {"prep": 0,
-            "qkv": b * 6 * n * d * d,
+            "qkv": b * (2 * n * d * d + 4 * n * d * w.d_kv),
             "attention": b * A.attention_flops(n, d, w.causal, w.window, w.chunk),
             "ffn_epilogue": b * (2 * n * d * d + A.ffn_flops(n, d, f))}
 
@@ -147,12 +147,12 @@ def cpu_baseline(w, inputs, target_s: float) -> dict:
             xs = synth.to_f64(x[:k * w.seq_len])
             t0 = time.perf_counter()
             oracle.layer_forward(xs, layers[0], seq_len=w.seq_len, n_heads=w.n_heads,
-                                 causal=w.causal, eps=w.ln_eps)
+                                 causal=w.causal, eps=w.ln_eps, window=w.window, chunk=w.chunk)
             return time.perf_counter() - t0
         t1 = run(1)
         k = int(max(1, min(w.batch, round(target_s / max(t1, 1e-3)))))
         t = run(k) if k > 1 else t1
-        flops = k * A.layer_flops(w.seq_len, w.d_model, w.d_ff, w.causal, w.window, w.chunk)
+        flops = k * A.layer_flops(w.seq_len, w.d_model, w.d_ff, w.causal, w.window, w.chunk, w.d_kv)
         sample = f"{k} of {w.batch} sequences, full layer (unfused, fp64)"
     else:
         # sampled rows of one layer: K, V for the visible prefix, the rest per row
@@ -160,12 +160,18 @@ def cpu_baseline(w, inputs, target_s: float) -> dict:
         xs = synth.to_f64(x)
         t0 = time.perf_counter()
         oracle.layer_forward_rows(xs, layers[0], rows, seq_len=w.seq_len, n_heads=w.n_heads,
-                                  causal=w.causal, eps=w.ln_eps)
+                                  causal=w.causal, eps=w.ln_eps, window=w.window, chunk=w.chunk)
         t = time.perf_counter() - t0
         d, f = w.d_model, w.d_ff
         nk = int(rows.max()) + 1
         pos = rows % w.seq_len
-        flops = 4 * nk * d * d + len(rows) * (4 * d * d + 4 * d * f) + int(np.sum(4 * d * (pos + 1)))
+        if w.chunk:
+            seen = np.minimum(w.seq_len, (pos // w.chunk + 1) * w.chunk)
+        elif w.window:
+            seen = np.minimum(pos + 1, w.window)
+        else:
+            seen = pos + 1
+        flops = 4 * nk * d * w.d_kv + len(rows) * (4 * d * d + 4 * d * f) + int(np.sum(4 * d * seen))
         sample = f"{len(rows)} sampled rows of layer 1 (K/V for {nk} rows), fp64"
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": sample, "seconds": round(t, 3), "flops": int(flops)}
@@ -361,7 +367,7 @@ def main():
             hip.destroy(e)
 
     total_flops = A.workload_flops(w.batch, w.seq_len, w.d_model, w.d_ff, w.causal, w.n_layers,
-                                   w.window, w.chunk)
+                                   w.window, w.chunk, w.d_kv)
     tflops = total_flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     kf = kernel_flops(w)

@@ -45,9 +45,11 @@ def attention_bwd_flops(n: int, d: int, causal: bool) -> int:
     return 5 * attention_flops(n, d, causal) // 2
 
 
-def projection_flops(n: int, d: int) -> int:
-    """W_Q, W_K, W_V, W_O: 4 matmuls of [N, d] x [d, d]."""
-    return 8 * n * d * d
+def projection_flops(n: int, d: int, d_kv: int | None = None) -> int:
+    """W_Q, W_K, W_V, W_O: 4 matmuls of [N, d] x [d, d] (8 N d^2); with d_kv-wide
+    key/value projections (grouped-query attention) W_K and W_V are [d, d_kv]."""
+    d_kv = d if d_kv is None else d_kv
+    return 4 * n * d * d + 4 * n * d * d_kv
 
 
 def ffn_flops(n: int, d: int, d_ff: int) -> int:
@@ -55,15 +57,16 @@ def ffn_flops(n: int, d: int, d_ff: int) -> int:
     return 4 * n * d * d_ff
 
 
-def layer_flops(n: int, d: int, d_ff: int, causal: bool, window: int = 0, chunk: int = 0) -> int:
+def layer_flops(n: int, d: int, d_ff: int, causal: bool, window: int = 0, chunk: int = 0,
+                d_kv: int | None = None) -> int:
     """Algorithmic FLOPs of one layer on one sequence of N tokens."""
-    return (attention_flops(n, d, causal, window, chunk) + projection_flops(n, d)
+    return (attention_flops(n, d, causal, window, chunk) + projection_flops(n, d, d_kv)
             + ffn_flops(n, d, d_ff))
 
 
 def workload_flops(batch: int, n: int, d: int, d_ff: int, causal: bool, n_layers: int = 1,
-                   window: int = 0, chunk: int = 0) -> int:
-    return batch * n_layers * layer_flops(n, d, d_ff, causal, window, chunk)
+                   window: int = 0, chunk: int = 0, d_kv: int | None = None) -> int:
+    return batch * n_layers * layer_flops(n, d, d_ff, causal, window, chunk, d_kv)
 
 
 def attention_crossover_tokens(d: int) -> int:

@@ -30,7 +30,7 @@ class LayerDesc(ctypes.Structure):
                 ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("precision", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("chunk", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32)]
 
 
 class AttnDesc(ctypes.Structure):
@@ -99,10 +99,11 @@ def lib() -> ctypes.CDLL:
 
 def make_desc(*, batch, seq_len, d_model, n_heads, d_ff, block_q, block_kv, causal,
               dtype, out_dtype=F32, ln_eps=1e-5, act=0, precision=0, window=0,
-              chunk=0) -> LayerDesc:
+              chunk=0, n_kv_heads=0) -> LayerDesc:
     as_code = lambda t: t if isinstance(t, int) else {"f32": F32, "bf16": BF16}[t]  # noqa: E731
     return LayerDesc(batch, seq_len, d_model, n_heads, d_ff, block_q, block_kv, int(causal),
-                     ln_eps, as_code(dtype), as_code(out_dtype), act, precision, window, chunk)
+                     ln_eps, as_code(dtype), as_code(out_dtype), act, precision, window, chunk,
+                     n_kv_heads)
 
 
 def desc_for(w, out_dtype=F32) -> LayerDesc:
@@ -111,7 +112,7 @@ def desc_for(w, out_dtype=F32) -> LayerDesc:
                      d_ff=w.d_ff, block_q=w.block_q, block_kv=w.block_kv, causal=w.causal,
                      dtype=w.dtype, out_dtype=out_dtype, ln_eps=w.ln_eps,
                      precision=getattr(w, "precision", 0), window=getattr(w, "window", 0),
-                     chunk=getattr(w, "chunk", 0))
+                     chunk=getattr(w, "chunk", 0), n_kv_heads=getattr(w, "n_kv_heads", 0))
 
 
 def layer_workspace_bytes(desc: LayerDesc) -> int:

@@ -35,6 +35,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 size_t seq_pad_of(const bpt_layer_desc_t* d) { return round_up((size_t)d->seq_len, 128); }
+int kv_heads(const bpt_layer_desc_t* d) { return d->n_kv_heads ? d->n_kv_heads : d->n_heads; }
+size_t kv_width(const bpt_layer_desc_t* d) {
+  return (size_t)kv_heads(d) * (size_t)(d->d_model / d->n_heads);
+}
 size_t rows_pad_of(const bpt_layer_desc_t* d) { return round_up((size_t)d->batch * seq_pad_of(d), 256); }
 
 // Layout of the layer workspace, plus the stack's fp32 residual buffer.
@@ -46,6 +50,7 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   const size_t rp = rows_pad_of(d);
   const bool split = d->precision == 1;
   const bool staged = bpt::staged_epilogue(d->d_model, split);
+  const size_t dkv = kv_width(d);
   // K and V^T cover rows_pad rows on the staged path, so that the fp32 Y [rows_pad, d]
   // fits over them once attention is done
   const size_t used = staged ? rp : (size_t)d->batch * seq_pad_of(d);
@@ -54,17 +59,20 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   off = round_up(off + rp * dm * es, kAlign);
   L.q_off = off;      // Q, then O, packed
   off = round_up(off + rp * dm * es, kAlign);
-  L.k_off = off;      // K, packed per (sequence, head)
-  off = round_up(off + used * dm * es, kAlign);
-  L.vt_off = off;     // V^T, packed per (sequence, head)
-  off = round_up(off + used * dm * es, kAlign);
-  L.wpack_off = off;  // W_Q, W_K, W_V, W_O, W_1, W_2 back to back, fragment order
-  off = round_up(off + (4 * dm * dm + 2 * df * dm) * es, kAlign);
+  L.k_off = off;      // K, packed per (sequence, key/value head)
+  off = round_up(off + used * dkv * es, kAlign);
+  L.vt_off = off;     // V^T, packed per (sequence, key/value head)
+  off = round_up(off + used * dkv * es, kAlign);
+  if (staged && off - L.k_off < rp * dm * 4)   // fewer key/value heads: room for Y
+    off = L.k_off + round_up(rp * dm * 4, kAlign);
+  L.wpack_off = off;  // W_Q, W_K, W_V (padded), W_O, W_1, W_2 back to back, fragment order
+  const int kvp = bpt::kv_pad_cols((int)dkv, d->dtype == BPT_F32);
+  off = round_up(off + (bpt::qkv_pack_elems(d->d_model, kvp) + dm * dm + 2 * df * dm) * es, kAlign);
   L.h_off = off;      // staged epilogue: hidden block [hidden_block_rows, d_ff]
   const size_t hr = bpt::hidden_block_rows(d->d_model, rp);
   if (staged) off = round_up(off + hr * df * es, kAlign);
   if (split) {        // lo halves, same shapes as the hi ones
-    const size_t sizes[5] = {rp * dm * es, rp * dm * es, used * dm * es, used * dm * es, hr * df * es};
+    const size_t sizes[5] = {rp * dm * es, rp * dm * es, used * dkv * es, used * dkv * es, hr * df * es};
     for (int i = 0; i < 5; ++i) {
       L.lo_off[i] = off;
       off = round_up(off + sizes[i], kAlign);
@@ -92,6 +100,9 @@ bpt_status_t validate_desc(const bpt_layer_desc_t* d) {
   if ((d->window || d->chunk) && !d->causal)
     return fail(BPT_ERR_SHAPE, "window and chunk apply to the causal mask only");
   if (d->window && d->chunk) return fail(BPT_ERR_SHAPE, "window and chunk cannot be combined");
+  if (d->n_kv_heads < 0 || (d->n_kv_heads && d->n_heads % d->n_kv_heads != 0))
+    return fail(BPT_ERR_SHAPE, "n_kv_heads %d must be 0 or divide n_heads %d", d->n_kv_heads,
+                d->n_heads);
   if (!(d->ln_eps > 0.0f) || !isfinite(d->ln_eps))
     return fail(BPT_ERR_SHAPE, "ln_eps must be finite and > 0");
   if ((d->dtype != BPT_F32 && d->dtype != BPT_BF16) ||
@@ -151,6 +162,9 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   p.n_heads = d->n_heads;
   p.d_head = d->d_model / d->n_heads;
   p.d_ff = d->d_ff;
+  p.n_kv_heads = kv_heads(d);
+  p.d_kv = (int)kv_width(d);
+  p.kv_pad = bpt::kv_pad_cols(p.d_kv, d->dtype == BPT_F32);
   p.block_q = d->block_q;
   p.block_kv = d->block_kv;
   p.causal = d->causal;

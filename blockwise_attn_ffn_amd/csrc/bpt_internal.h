@@ -14,6 +14,7 @@ namespace bpt {
 struct LayerLaunch {
   // shape
   int batch, seq_len, d_model, n_heads, d_head, d_ff;
+  int n_kv_heads, d_kv, kv_pad;   // key/value heads g, g * d_head, kv_pad_cols(d_kv)
   int block_q, block_kv, causal;
   int window, chunk;   // attention masks on top of the causal one (0: none)
   float ln_eps;
@@ -92,6 +93,19 @@ struct AttnBwdLaunch {
   // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
   void* const* events;
 };
+
+// Output features of the K (and of the V) part of the projection product: the
+// key/value width rounded up to a whole product tile (256 features for bf16
+// operands, 128 for fp32), so that each tile of the QKV product lies inside one
+// of Q, K, V (extra features are dropped).
+inline int kv_pad_cols(int d_kv, int compute_f32) {
+  const int tile = compute_f32 ? 128 : 256;
+  return (d_kv + tile - 1) / tile * tile;
+}
+// Elements of the packed W_Q | W_K | W_V block (kv_pad: kv_pad_cols of d_kv).
+inline size_t qkv_pack_elems(int d_model, int kv_pad) {
+  return (size_t)(d_model + 2 * kv_pad) * d_model;
+}
 
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).
 int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t errlen);

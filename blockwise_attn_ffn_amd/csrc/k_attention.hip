@@ -56,8 +56,8 @@ template <typename T, int DK, int BQ, int BKV, bool SPLIT = false, bool MASKED =
 __global__ __launch_bounds__(BQ * 2, (4 * BKV * DK * (int)sizeof(T) * (SPLIT ? 2 : 1) <= 65536) ? 2 : 1) void
 attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* QPlo,
                  const T* __restrict__ KPlo, const T* __restrict__ VPlo, int N, int Np, int H,
-                 int d, int causal, int window, int chunk, float scale_log2e, int nqb, int n_bh,
-                 float* lse) {
+                 int G, int d, int causal, int window, int chunk, float scale_log2e, int nqb,
+                 int n_bh, float* lse) {
   using O = Op<T>;
   using F = typename O::frag;
   constexpr int NW = BQ / 32;
@@ -94,8 +94,9 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
 
   // Visible keys of query position p (p past the end behaves as the last row):
   // causal: [0, p]; window w: [p - w + 1, p]; chunk C: up to the end of p's chunk.
-  // MASKED instances (a window or chunk mask) evaluate the general form; the others
-  // compile to the plain causal / unmasked bounds.
+  // MASKED instances (a window or chunk mask, or fewer key/value heads than query
+  // heads) evaluate the general forms; the others compile to the plain causal /
+  // unmasked bounds and read K and V of their own head.
   auto key_hi = [&](int p) {
     const int pc = min(p, N - 1);
     if (!causal) return N - 1;
@@ -106,9 +107,20 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
     if constexpr (MASKED) return window ? max(0, min(p, N - 1) - window + 1) : 0;
     return 0;
   };
+  // query head h of sequence b reads key/value head h / (H / G) (grouped-query attention)
+  // (MASKED instances only; the others have G == H)
+  auto kv_head = [&](int bh) {
+    const int bi = bh / H;
+    return bi * G + (bh - bi * H) / (H / G);
+  };
   // ---- visit cursor (wave-uniform): unit u, half w of it, query block qb,
   //      key/value block kb of kend, (sequence, head) bh
-  struct Cur { int u, w, qb, kb, kend, bh; };
+  // bh: (sequence, query head); kvh: (sequence, key/value head) of its K and V
+  struct Cur { int u, w, qb, kb, kend, bh, kvh; };
+  auto kvh_of = [&](const Cur& c) {
+    if constexpr (MASKED) return c.kvh;
+    return c.bh;
+  };
   auto qblock = [&](int u, int w) {     // query block of half w of unit u, -1 if none
     const int p = u % n_pairs;
     if (!causal) return w == 0 ? p : -1;
@@ -120,6 +132,7 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
     c.kb = key_lo(c.qb * BQ) / BKV;
     c.kend = key_hi(c.qb * BQ + BQ - 1) / BKV + 1;
     c.bh = c.u / n_pairs;
+    c.kvh = MASKED ? kv_head(c.bh) : 0;   // unused by the plain instance
   };
   auto advance = [&](Cur& c) {          // c.u >= u_hi afterwards means: no more visits
     if (c.kb + 1 < c.kend) { ++c.kb; return; }
@@ -158,7 +171,7 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
       unsigned char* dst = buf + f_first * FB;
       if (c_k) {
         const char* kb = reinterpret_cast<const char*>(
-            (c_lo ? KPlo : KP) + ((size_t)c.bh * (Np / 32) + kv0 / 32) * KSD * kFragElems) +
+            (c_lo ? KPlo : KP) + ((size_t)kvh_of(c) * (Np / 32) + kv0 / 32) * KSD * kFragElems) +
             (size_t)f_kind * FB;
 #pragma unroll
         for (int q = 0; q < CPW; ++q) dma16(kb + q * FB + lane_off, dst + q * FB);
@@ -166,14 +179,14 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
         // V fragment ff = f_kind - KFR + q: feature tile ff / KK, key step ff % KK
         const size_t S = (size_t)(Np / 16) * FB;          // bytes per feature tile
         const char* vb = reinterpret_cast<const char*>(
-            (c_lo ? VPlo : VP) + ((size_t)c.bh * DT * (Np / 16) + kv0 / 16) * kFragElems) +
+            (c_lo ? VPlo : VP) + ((size_t)kvh_of(c) * DT * (Np / 16) + kv0 / 16) * kFragElems) +
             (size_t)((f_kind - KFR) / KK) * S;
 #pragma unroll
         for (int q = 0; q < CPW; ++q) dma16(vb + (q / KK) * S + (q % KK) * FB + lane_off, dst + q * FB);
       }
     } else {
-      const size_t koff = (size_t)c.bh * (Np / 32) * KSD * kFragElems;
-      const size_t voff = (size_t)c.bh * DT * (Np / 16) * kFragElems;
+      const size_t koff = (size_t)kvh_of(c) * (Np / 32) * KSD * kFragElems;
+      const size_t voff = (size_t)kvh_of(c) * DT * (Np / 16) * kFragElems;
 #pragma unroll
       for (int q = 0; q < CPW; ++q) {
         const int idx = wave * CPW + q;
@@ -413,7 +426,8 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
 template <int DK, int BKV, bool MASKED = false>
 __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     bf16* QP, const bf16* __restrict__ KP, const bf16* __restrict__ VP, int N, int Np, int H,
-    int d, int causal, int window, int chunk, float scale_log2e, int nqb, int n_bh, float* lse) {
+    int G, int d, int causal, int window, int chunk, float scale_log2e, int nqb, int n_bh,
+    float* lse) {
   using O = Op<bf16>;
   using F = O::frag;
   constexpr int BQ = 128, NWG = 4, FB = 1024;
@@ -446,8 +460,9 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
 
   // Visible keys of query position p (p past the end behaves as the last row):
   // causal: [0, p]; window w: [p - w + 1, p]; chunk C: up to the end of p's chunk.
-  // MASKED instances (a window or chunk mask) evaluate the general form; the others
-  // compile to the plain causal / unmasked bounds.
+  // MASKED instances (a window or chunk mask, or fewer key/value heads than query
+  // heads) evaluate the general forms; the others compile to the plain causal /
+  // unmasked bounds and read K and V of their own head.
   auto key_hi = [&](int p) {
     const int pc = min(p, N - 1);
     if (!causal) return N - 1;
@@ -458,8 +473,18 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     if constexpr (MASKED) return window ? max(0, min(p, N - 1) - window + 1) : 0;
     return 0;
   };
+  // query head h of sequence b reads key/value head h / (H / G) (grouped-query attention)
+  // (MASKED instances only; the others have G == H)
+  auto kv_head = [&](int bh) {
+    const int bi = bh / H;
+    return bi * G + (bh - bi * H) / (H / G);
+  };
   // visit cursor over super-blocks (wave-uniform), as in the one-group kernel
-  struct Cur { int u, w, sb, kb, kend, bh; };
+  struct Cur { int u, w, sb, kb, kend, bh, kvh; };
+  auto kvh_of = [&](const Cur& c) {
+    if constexpr (MASKED) return c.kvh;
+    return c.bh;
+  };
   auto sblock = [&](int u, int w) {
     const int p = u % n_pairs;
     if (!causal) return w == 0 ? p : -1;
@@ -471,6 +496,7 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     c.kb = key_lo(c.sb * 2 * BQ) / BKV;
     c.kend = key_hi(c.sb * 2 * BQ + 2 * BQ - 1) / BKV + 1;
     c.bh = c.u / n_pairs;
+    c.kvh = MASKED ? kv_head(c.bh) : 0;   // unused by the plain instance
   };
   auto advance = [&](Cur& c) {          // c.u >= u_hi afterwards: no more visits
     if (c.kb + 1 < c.kend) { ++c.kb; return; }
@@ -502,14 +528,14 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
   // steps of one feature tile per wave)
   auto issue_k = [&](const Cur& c, unsigned char* buf) __attribute__((always_inline)) {
     const char* src = reinterpret_cast<const char*>(
-        KP + (((size_t)c.bh * (Np / 32) + c.kb * BKV / 32) * KSD + wq * KCPW) * kFragElems);
+        KP + (((size_t)kvh_of(c) * (Np / 32) + c.kb * BKV / 32) * KSD + wq * KCPW) * kFragElems);
 #pragma unroll
     for (int q = 0; q < KCPW; ++q) dma16(src + q * FB + lane_off, buf + (wq * KCPW + q) * FB);
   };
   auto issue_v = [&](const Cur& c, unsigned char* buf) __attribute__((always_inline)) {
     const int dt = wq * VCPW / KK, kk0 = wq * VCPW % KK;
     const char* src = reinterpret_cast<const char*>(
-        VP + (((size_t)c.bh * DT + dt) * (Np / 16) + c.kb * BKV / 16 + kk0) * kFragElems);
+        VP + (((size_t)kvh_of(c) * DT + dt) * (Np / 16) + c.kb * BKV / 16 + kk0) * kFragElems);
 #pragma unroll
     for (int q = 0; q < VCPW; ++q) dma16(src + q * FB + lane_off, buf + (wq * VCPW + q) * FB);
   };
@@ -723,13 +749,15 @@ int run_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   int grid = device_cus() * per_cu;
   if (units < grid) grid = units;
   const float scale = 1.4426950408889634f / sqrtf((float)DK);
-  // window / chunk masks run the general-mask instance; plain causal or no mask the other
-  auto kern = (L.window || L.chunk) ? attention_kernel<T, DK, BQ, BKV, SPLIT, true>
-                                    : attention_kernel<T, DK, BQ, BKV, SPLIT, false>;
+  // window / chunk masks and grouped key/value heads run the general instance;
+  // plain causal or unmasked multi-head attention the other
+  const bool general = L.window || L.chunk || L.n_kv_heads != L.n_heads;
+  auto kern = general ? attention_kernel<T, DK, BQ, BKV, SPLIT, true>
+                      : attention_kernel<T, DK, BQ, BKV, SPLIT, false>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(BQ * 2), 0, s,
                      (T*)L.q, (const T*)L.k, (const T*)L.vt, (T*)L.q_lo, (const T*)L.k_lo,
-                     (const T*)L.vt_lo, L.seq_len, L.seq_pad, L.n_heads, L.d_model, L.causal,
-                     L.window, L.chunk, scale, nqb, n_bh, L.lse);
+                     (const T*)L.vt_lo, L.seq_len, L.seq_pad, L.n_heads, L.n_kv_heads, L.d_model,
+                     L.causal, L.window, L.chunk, scale, nqb, n_bh, L.lse);
   return check_launch("attention", err, n);
 }
 
@@ -742,11 +770,11 @@ int run_attn_pair(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   int grid = device_cus();
   if (units < grid) grid = units;
   const float scale = 1.4426950408889634f / sqrtf((float)DK);
-  auto kern = (L.window || L.chunk) ? attention_pair_kernel<DK, BKV, true>
-                                    : attention_pair_kernel<DK, BKV, false>;
+  const bool general = L.window || L.chunk || L.n_kv_heads != L.n_heads;
+  auto kern = general ? attention_pair_kernel<DK, BKV, true> : attention_pair_kernel<DK, BKV, false>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, (bf16*)L.q,
                      (const bf16*)L.k, (const bf16*)L.vt, L.seq_len, L.seq_pad, L.n_heads,
-                     L.d_model, L.causal, L.window, L.chunk, scale, nqb, n_bh, L.lse);
+                     L.n_kv_heads, L.d_model, L.causal, L.window, L.chunk, scale, nqb, n_bh, L.lse);
   return check_launch("attention", err, n);
 }
 

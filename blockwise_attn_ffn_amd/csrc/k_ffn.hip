@@ -315,7 +315,7 @@ int run_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   if (set_smem(k, smem, err, n)) return 1;
   // one workgroup per BM packed rows
   hipLaunchKernelGGL(k, dim3(L.batch * L.seq_pad / BM), dim3(256), smem, s, (const TX*)L.x,
-                     (const T*)L.q, (const T*)L.wpack + 3 * (size_t)L.d_model * L.d_model,
+                     (const T*)L.q, (const T*)L.wpack + qkv_pack_elems(L.d_model, L.kv_pad),
                      (const T*)L.w.ln2_g, (const T*)L.w.ln2_b, (TO*)L.z, L.seq_len, L.seq_pad,
                      L.d_ff, L.ln_eps);
   return check_launch("ffn_epilogue", err, n);

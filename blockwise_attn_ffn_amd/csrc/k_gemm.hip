@@ -40,6 +40,7 @@ struct GemmArgs {
   T *q, *k, *vt;
   T *q_lo, *k_lo, *vt_lo;         // optional lo halves of the outputs
   int d, H, dk;
+  int G, dkv, kvp;                // key/value heads, their width, that width padded to BN
   // other modes
   int n_out;                      // features of the output row
   const void* x;                  // residual X (real rows), kModeResidY
@@ -222,10 +223,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
   };
   const int Np = g.Np;
   if constexpr (MODE == kModeQKV) {
-    const int d = g.d, dk = g.dk, H = g.H, rows_used = g.rows_used;
-    const int ng0 = nt * BN;                 // first output feature in [0, 3d)
-    const int which = ng0 / d;               // 0 Q, 1 K, 2 V
-    const int nc0 = ng0 - which * d;         // first column inside that matrix
+    const int d = g.d, dk = g.dk, G = g.G, dkv = g.dkv, kvp = g.kvp, rows_used = g.rows_used;
+    const int ng0 = nt * BN;                 // first output feature in [0, d + 2 kvp)
+    // 0 Q, 1 K, 2 V: d and kvp are multiples of BN, so a tile lies inside one part;
+    // K and V features at or past dkv (the padding) are not stored
+    const int which = ng0 < d ? 0 : (ng0 < d + kvp ? 1 : 2);
+    const int nc0 = ng0 - (which == 0 ? 0 : (which == 1 ? d : d + kvp));   // column inside it
     const int KSD = dk / 16, KSQ = d / 16;
     if (which != 2) {
       main_loop(std::false_type{});
@@ -243,9 +246,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
             frag_vals(acc[a][b], gg, v);
             if (which == 0) {
               st_pair(g.q, g.q_lo, ((size_t)(p >> 5) * KSQ + (n >> 4)) * kFragElems, 32 * hf + (p & 31), v);
-            } else {
+            } else if (n < dkv) {
               const int head = n / dk, j0 = n - head * dk;
-              const size_t frag = (((size_t)bi * H + head) * (Np / 32) + (pos >> 5)) * KSD + (j0 >> 4);
+              const size_t frag = (((size_t)bi * G + head) * (Np / 32) + (pos >> 5)) * KSD + (j0 >> 4);
               st_pair(g.k, g.k_lo, frag * kFragElems, 32 * hf + pi_row(pos & 31), v);   // = lane
             }
           }
@@ -265,8 +268,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
 #pragma unroll
         for (int a = 0; a < TN; ++a) {
           const int n0 = nc0 + wn * (BN / 2) + a * 32;      // first feature of the tile
+          if (n0 >= dkv) continue;                           // padding features
           const int head = n0 / dk, dt = (n0 - head * dk) >> 5;
-          const size_t vbase = ((((size_t)bi * H + head) * (dk / 32) + dt) * (Np / 16) + (pos0 >> 4)) * kFragElems;
+          const size_t vbase = ((((size_t)bi * G + head) * (dk / 32) + dt) * (Np / 16) + (pos0 >> 4)) * kFragElems;
 #pragma unroll
           for (int gg = 0; gg < 2; ++gg) {
             float v[8];
@@ -368,7 +372,15 @@ int run_qkv(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   g.d = L.d_model;
   g.H = L.n_heads;
   g.dk = L.d_head;
-  return run_gemm<T, BN, BM, kModeQKV>(g, 3 * L.d_model, L.rows_pad, s, "qkv_gemm", err, n);
+  g.G = L.n_kv_heads;
+  g.dkv = L.d_kv;
+  g.kvp = L.kv_pad;
+  if (L.d_model % BN != 0 || L.kv_pad % BN != 0) {
+    set_err(err, n, "qkv product: widths not multiples of the %s%d-feature tile", "", BN);
+    return 1;
+  }
+  return run_gemm<T, BN, BM, kModeQKV>(g, L.d_model + 2 * L.kv_pad, L.rows_pad, s, "qkv_gemm", err,
+                                       n);
 }
 
 }  // namespace
@@ -390,7 +402,7 @@ int launch_ffn_staged(const LayerLaunch& L, hipStream_t s, char* err, size_t n) 
     return 1;
   }
   const int d = L.d_model, f = L.d_ff;
-  const size_t dd = (size_t)d * d;
+  const size_t dd = (size_t)d * d, qkv = qkv_pack_elems(d, L.kv_pad);
   const T* wp = static_cast<const T*>(L.wpack);
   GemmArgs<T> g{};
   g.N = L.seq_len;
@@ -402,7 +414,7 @@ int launch_ffn_staged(const LayerLaunch& L, hipStream_t s, char* err, size_t n) 
   g.z = L.z;
   g.z_f32 = L.z_f32;
   // Y = X + O W_O; O's rows are in natural order inside a tile
-  g.w = wp + 3 * dd;
+  g.w = wp + qkv;
   g.a = static_cast<const T*>(L.q);
   g.a_lo = L.split ? static_cast<const T*>(L.q_lo) : nullptr;
   g.K = d;
@@ -414,7 +426,7 @@ int launch_ffn_staged(const LayerLaunch& L, hipStream_t s, char* err, size_t n) 
   for (int r0 = 0; r0 < L.rows_pad; r0 += L.h_rows) {
     const int rows = L.rows_pad - r0 < L.h_rows ? L.rows_pad - r0 : L.h_rows;
     GemmArgs<T> u = g;
-    u.w = wp + 4 * dd;
+    u.w = wp + qkv + dd;
     u.a = static_cast<const T*>(L.xpack) + (size_t)(r0 / 32) * (d / 16) * kFragElems;
     u.a_lo = L.split ? static_cast<const T*>(L.xpack_lo) + (size_t)(r0 / 32) * (d / 16) * kFragElems
                      : nullptr;
@@ -426,7 +438,7 @@ int launch_ffn_staged(const LayerLaunch& L, hipStream_t s, char* err, size_t n) 
     u.h_lo = L.split ? static_cast<T*>(L.hbuf_lo) : nullptr;
     if (run_gemm<T, 256, 256, kModeGeluH>(u, f, rows, s, "w1_gemm", err, n)) return 1;
     GemmArgs<T> o = g;
-    o.w = wp + 4 * dd + (size_t)f * d;
+    o.w = wp + qkv + dd + (size_t)f * d;
     o.a = static_cast<const T*>(L.hbuf);
     o.a_lo = L.split ? static_cast<const T*>(L.hbuf_lo) : nullptr;
     o.K = f;

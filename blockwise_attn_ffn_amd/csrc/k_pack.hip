@@ -67,24 +67,26 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(PackJob<T> job) {
   }
 }
 
-// Packed region: W_Q, W_K, W_V (one [3d, d] operand), then the epilogue stream
-// holding W_O, W_1 and W_2 (d^2 + 2 d d_ff elements); for the staged epilogue
-// W_O, W_1, W_2 in plain fragment order instead.
+// Packed region: W_Q, W_K, W_V (one [d + 2 kvp, d] operand: W_K and W_V hold d_kv =
+// n_kv_heads * d_head rows each, at offsets d and d + kvp, kvp = d_kv rounded up to
+// a product tile; the rows in between are never written and the product's
+// features there are dropped), then the epilogue stream holding W_O, W_1 and W_2 (d^2 + 2 d d_ff
+// elements); for the staged epilogue W_O, W_1, W_2 in plain fragment order instead.
 template <typename T>
 int pack_all(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
-  const int d = L.d_model, f = L.d_ff;
-  const size_t dd = (size_t)d * d;
+  const int d = L.d_model, f = L.d_ff, dkv = L.d_kv, kvp = L.kv_pad;
+  const size_t dd = (size_t)d * d, qkv = qkv_pack_elems(d, kvp);
   T* p = static_cast<T*>(L.wpack);
   PackJob<T> job{};
   job.fs = FfnStream{d, f};
   const void* srcs[6] = {L.w.w_q, L.w.w_k, L.w.w_v, L.w.w_o, L.w.w_1, L.w.w_2};
   const bool staged = staged_epilogue(d, L.split);
-  T* dsts[6] = {p, p + dd, p + 2 * dd, p + 3 * dd, p + 3 * dd, p + 3 * dd};
-  const int rows[6] = {d, d, d, d, f, d}, Ks[6] = {d, d, d, d, d, f};
+  T* dsts[6] = {p, p + dd, p + dd + (size_t)kvp * d, p + qkv, p + qkv, p + qkv};
+  const int rows[6] = {d, dkv, dkv, d, f, d}, Ks[6] = {d, d, d, d, d, f};
   int orders[6] = {kPlain, kPlain, kPlain, kStreamWO, kStreamW1, kStreamW2};
   if (staged) {   // the staged epilogue's GEMMs take W_O, W_1, W_2 in plain order
-    dsts[4] = p + 4 * dd;
-    dsts[5] = p + 4 * dd + (size_t)f * d;
+    dsts[4] = p + qkv + dd;
+    dsts[5] = p + qkv + dd + (size_t)f * d;
     orders[3] = orders[4] = orders[5] = kPlain;
   }
   job.first_item[0] = 0;

@@ -45,6 +45,7 @@ class Workload:
     precision: int = 0    # 0: bf16 operands; 1: bf16 (hi, lo) pairs for computed operands
     window: int = 0       # attention window (causal): query p sees keys p - window + 1 .. p
     chunk: int = 0        # chunked streaming (causal): query p sees keys j with j // chunk <= p // chunk
+    n_kv_heads: int = 0   # key/value heads (grouped-query attention); 0: n_heads
 
     @property
     def rows(self) -> int:
@@ -53,6 +54,10 @@ class Workload:
     @property
     def d_head(self) -> int:
         return self.d_model // self.n_heads
+
+    @property
+    def d_kv(self) -> int:
+        return (self.n_kv_heads or self.n_heads) * self.d_head
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -78,6 +83,10 @@ WORKLOADS = {
     "long_128k_w4096": Workload("long_128k_w4096", batch=1, seq_len=131072, d_model=2048,
                                 n_heads=16, d_ff=8192, causal=True, block_q=128, block_kv=64,
                                 dtype="bf16", sample_rows=256, window=4096),
+    # the long-context layer with grouped-query attention: 4 key/value heads
+    "long_128k_gqa4": Workload("long_128k_gqa4", batch=1, seq_len=131072, d_model=2048,
+                               n_heads=16, d_ff=8192, causal=True, block_q=128, block_kv=64,
+                               dtype="bf16", sample_rows=256, n_kv_heads=4),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -97,7 +106,8 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
 
     Returns {"x": tensor, "layers": [dict(name -> tensor), ...]} with names
     ln1_g, ln1_b, w_q, w_k, w_v, w_o, ln2_g, ln2_b, w_1, w_2.
-    Shapes: LN parameters [d]; w_q/w_k/w_v/w_o [d, d]; w_1 [d_ff, d]; w_2 [d, d_ff].
+    Shapes: LN parameters [d]; w_q/w_o [d, d]; w_k/w_v [d_kv, d] (d_kv = key/value
+    heads x d_head, d for multi-head attention); w_1 [d_ff, d]; w_2 [d, d_ff].
     """
     dt = TORCH_DTYPE[w.dtype]
     d, f = w.d_model, w.d_ff
@@ -115,8 +125,8 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
 
         ln1_g, ln1_b = ln_pair()
         wq = _draw(gen, (d, d), std, 0.0, dt)
-        wk = _draw(gen, (d, d), std, 0.0, dt)
-        wv = _draw(gen, (d, d), std, 0.0, dt)
+        wk = _draw(gen, (w.d_kv, d), std, 0.0, dt)
+        wv = _draw(gen, (w.d_kv, d), std, 0.0, dt)
         wo = _draw(gen, (d, d), std, 0.0, dt)
         ln2_g, ln2_b = ln_pair()
         w1 = _draw(gen, (f, d), std, 0.0, dt)

@@ -92,9 +92,14 @@ typedef struct {
   int32_t chunk;      /* 0: none. C > 0 (causal only, not with window): query p
                          sees every key j with j / C <= p / C, its whole chunk and
                          the earlier ones (same section, chunked streaming)     */
+  int32_t n_kv_heads; /* key/value heads g (0: n_heads). Grouped-query attention
+                         (same page, MQA and GQA): query head h reads key/value
+                         head h / (n_heads / g); g must divide n_heads; 1 is MQA.
+                         W_K and W_V are then [g * d_head, d_model]             */
 } bpt_layer_desc_t;
 
-/* Device pointers to one layer's parameters (layouts above). */
+/* Device pointers to one layer's parameters (layouts above; with n_kv_heads = g,
+ * w_k and w_v are [g * d_head, d_model]). */
 typedef struct {
   const void *ln1_g, *ln1_b, *w_q, *w_k, *w_v, *w_o;
   const void *ln2_g, *ln2_b, *w_1, *w_2;
@@ -119,6 +124,10 @@ typedef struct {
  * at d_model 2048), and keeps Y fp32 [rows, d_model] over the K and V^T space;
  * precision 1 doubles every activation buffer (the lo halves). */
 size_t bpt_layer_workspace_bytes(const bpt_layer_desc_t* desc);
+/* With g = n_kv_heads key/value heads, K and V^T are [rows, g * d_head] and the
+ * packed projection block is [d_model + 2 kvp, d_model] with kvp = g * d_head
+ * rounded up to 256 (the K and V parts are padded to whole product tiles); on the
+ * staged path the K and V^T space is at least the fp32 Y [rows, d_model]. */
 
 /* Workspace of bpt_stack_fwd: the layer workspace, plus one fp32 residual
  * buffer [rows, d_model] when n_layers > 1 and out_dtype is not BPT_F32. */

@@ -24,6 +24,9 @@ Readings of points the pages leave open (each also listed in the design notes):
     1/sqrt(d_k); head outputs are concatenated in head order before W_O.
   * causal: query at position p sees key q iff q <= p (positions within one
     sequence); different sequences of a batch never attend to each other.
+  * grouped-query attention ([COST], MQA and GQA): K and V hold g heads of d_k
+    columns; query head h reads key/value head h // (n_heads / g) (g is read from
+    the widths: K has g d_k columns). g = n_heads is plain multi-head attention.
   * masks of [COST]'s Section 5 (both on top of the causal mask): a window of w
     keys, query p reads keys max(0, p - w + 1) .. p; chunked streaming with chunk
     size C, query p reads every key of its own chunk and of earlier chunks,
@@ -73,6 +76,15 @@ def visible(q_pos: np.ndarray, k_pos: np.ndarray, causal: bool, window: int = 0,
     if window:
         vis &= kp > qp - window
     return vis
+
+
+def _group_size(q: np.ndarray, k: np.ndarray, n_heads: int) -> int:
+    """Query heads per key/value head: K holds g heads of d_k = q width / n_heads
+    columns; g must divide n_heads."""
+    dk = q.shape[1] // n_heads
+    g = k.shape[1] // dk
+    assert g * dk == k.shape[1] and g >= 1 and n_heads % g == 0
+    return n_heads // g
 
 
 def keys_needed(pos_max: int, seq_len: int, causal: bool, chunk: int = 0) -> int:
@@ -154,12 +166,14 @@ def attention_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int
     scale = 1.0 / math.sqrt(dk)
     if causal:
         hidden = ~visible(q_pos, np.arange(nk), causal, window, chunk)
+    group = _group_size(q, k, n_heads)
     for h in range(n_heads):
         cols = slice(h * dk, (h + 1) * dk)
-        s = (q[:, cols] @ k[:, cols].T) * scale
+        kv = slice((h // group) * dk, (h // group + 1) * dk)
+        s = (q[:, cols] @ k[:, kv].T) * scale
         if causal:
             s = np.where(hidden, -np.inf, s)
-        out[:, cols] = softmax_rows(s) @ v[:, cols]
+        out[:, cols] = softmax_rows(s) @ v[:, kv]
     return out
 
 
@@ -188,9 +202,11 @@ def attention_lse_sequence(q: np.ndarray, k: np.ndarray, n_heads: int, causal: b
     out = np.empty((n_heads, nq), dtype=F64)
     if causal:
         hidden = ~visible(q_pos, np.arange(nk), causal, window, chunk)
+    group = _group_size(q, k, n_heads)
     for h in range(n_heads):
         cols = slice(h * dk, (h + 1) * dk)
-        s = (q[:, cols] @ k[:, cols].T) * scale
+        kv = slice((h // group) * dk, (h // group + 1) * dk)
+        s = (q[:, cols] @ k[:, kv].T) * scale
         if causal:
             s = np.where(hidden, -np.inf, s)
         m = s.max(axis=1)
@@ -230,7 +246,7 @@ def layer_lse_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int, n_
         pos = rows[sel] - sidx * seq_len
         base = sidx * seq_len
         n_keys = keys_needed(int(pos.max()), seq_len, causal, chunk)
-        k = np.empty((n_keys, x.shape[1]), F64)
+        k = np.empty((n_keys, p["w_k"].shape[1]), F64)
         for c0 in range(0, n_keys, row_chunk):
             c1 = min(n_keys, c0 + row_chunk)
             k[c0:c1] = layer_norm(x[base + c0: base + c1], p["ln1_g"], p["ln1_b"], eps) @ p["w_k"]
@@ -257,6 +273,7 @@ def attention_backward_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, do:
     """
     q, k, v, do = (np.asarray(a, F64) for a in (q, k, v, do))
     n, d = q.shape
+    assert k.shape[1] == d, "the backward takes one key/value head per query head"
     dk_ = d // n_heads
     scale = 1.0 / math.sqrt(dk_)
     dq = np.empty_like(q)
@@ -403,8 +420,8 @@ def layer_forward_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int
         pos = rows[sel] - sidx * seq_len
         base = sidx * seq_len
         n_keys = keys_needed(int(pos.max()), seq_len, causal, chunk)
-        k = np.empty((n_keys, d), F64)
-        v = np.empty((n_keys, d), F64)
+        k = np.empty((n_keys, p["w_k"].shape[1]), F64)
+        v = np.empty((n_keys, p["w_v"].shape[1]), F64)
         for c0 in range(0, n_keys, row_chunk):
             c1 = min(n_keys, c0 + row_chunk)
             xk = layer_norm(x[base + c0: base + c1], p["ln1_g"], p["ln1_b"], eps)
@@ -516,9 +533,11 @@ def blockwise_layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: in
                 xj = layer_norm(xs[j0:j1], p["ln1_g"], p["ln1_b"], eps)
                 k_j = xj @ p["w_k"]
                 v_j = xj @ p["w_v"]
+                group = n_heads // (k_j.shape[1] // dk)    # query heads per key/value head
                 for h in range(n_heads):
                     cols = slice(h * dk, (h + 1) * dk)
-                    s = (q_i[:, cols] @ k_j[:, cols].T) * scale
+                    kv = slice((h // group) * dk, (h // group + 1) * dk)
+                    s = (q_i[:, cols] @ k_j[:, kv].T) * scale
                     if causal:
                         vis = visible(np.arange(i0, i1), np.arange(j0, j1), causal, window, chunk)
                         s = np.where(vis, s, -np.inf)
@@ -527,7 +546,7 @@ def blockwise_layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: in
                     alpha = np.where(np.isfinite(m[h]), np.exp(m[h] - shift), 0.0)
                     e = np.exp(s - shift[:, None])
                     l[h] = alpha * l[h] + e.sum(axis=1)
-                    o[h] = alpha[:, None] * o[h] + e @ v_j[:, cols]
+                    o[h] = alpha[:, None] * o[h] + e @ v_j[:, kv]
                     m[h] = m_new
             attn = np.concatenate([o[h] / l[h][:, None] for h in range(n_heads)], axis=1)
             y_i = x_i + attn @ p["w_o"]

@@ -58,7 +58,7 @@ def hidden_rows(d, rows_pad):
     return min(rows_pad, max(4096, (2 ** 25 // d) // 256 * 256))
 
 
-def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=False):
+def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=False, dkv=None):
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     rows = batch * n
     npad = (n + 127) // 128 * 128
@@ -66,10 +66,18 @@ def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=Fals
     rows_pad = up(used)
     staged = d > 1024 or split  # staged epilogue: K, V^T over rows_pad rows + hidden block
     f = 4 * d if d_ff is None else d_ff
+    dkv = d if dkv is None else dkv          # key/value width (grouped-query attention)
+    tile = 128 if es == 4 else 256
+    kvp = (dkv + tile - 1) // tile * tile    # K and V parts of the projection, padded
     kv_rows = rows_pad if staged else used
-    acts = 2 * up(rows_pad * d * es) + 2 * up(kv_rows * d * es)
+    kv_space = 2 * up(kv_rows * dkv * es)
+    if staged:                               # room for the fp32 Y over K and V^T
+        kv_space = max(kv_space, up(rows_pad * d * 4))
+    acts = 2 * up(rows_pad * d * es) + kv_space
     hidden = up(hidden_rows(d, rows_pad) * f * es) if staged else 0
-    tot = acts + up((4 * d * d + 2 * d * f) * es) + hidden
+    tot = acts + up(((d + 2 * kvp) * d + d * d + 2 * d * f) * es) + hidden
+    if split:                   # lo halves: no Y room there
+        acts = 2 * up(rows_pad * d * es) + 2 * up(kv_rows * dkv * es)
     if split:                   # lo halves of the bf16 pairs
         tot += acts + hidden
     if stack_resid:
@@ -100,6 +108,30 @@ def test_workspace_formula_bf16_pairs(batch, n, d, h):
     assert bpt.layer_workspace_bytes(dsc) == expected_workspace(batch, n, d, 2, split=True)
     dsc.out_dtype = bpt.BF16
     assert bpt.stack_workspace_bytes(dsc, 4) == expected_workspace(batch, n, d, 2, True, split=True)
+
+
+@pytest.mark.parametrize("batch,n,d,h,g,dt,split", [
+    (2, 200, 256, 4, 1, "bf16", False), (2, 200, 256, 4, 2, "bf16", False),
+    (1, 131072, 2048, 16, 4, "bf16", False), (1, 300, 2048, 16, 1, "bf16", False),
+    (64, 1024, 1024, 16, 8, "bf16", False), (1, 77, 128, 2, 1, "f32", False),
+    (2, 200, 256, 4, 2, "bf16", True), (1, 5000, 2048, 16, 2, "bf16", True)])
+def test_workspace_formula_grouped_kv_heads(batch, n, d, h, g, dt, split):
+    dsc = desc(batch=batch, seq_len=n, d_model=d, n_heads=h, d_ff=4 * d, dtype=dt,
+               block_q=64, block_kv=64, precision=int(split))
+    dsc.n_kv_heads = g
+    es = 4 if dt == "f32" else 2
+    assert bpt.layer_workspace_bytes(dsc) == expected_workspace(batch, n, d, es, split=split,
+                                                                dkv=g * (d // h))
+    dsc.n_kv_heads = h                       # g = n_heads is multi-head attention
+    assert bpt.layer_workspace_bytes(dsc) == expected_workspace(batch, n, d, es, split=split)
+
+
+@pytest.mark.parametrize("g", [-1, 3, 5])
+def test_invalid_kv_heads(g):
+    dsc = desc(n_heads=4)
+    dsc.n_kv_heads = g
+    assert call_layer(dsc) == 2 and "n_kv_heads" in bpt.last_error()
+    assert bpt.layer_workspace_bytes(dsc) == 0
 
 
 def test_bf16_pairs_need_bf16_inputs():

@@ -87,3 +87,10 @@ def test_visible_pairs_count_by_brute_force(n, mask):
                 count += j <= p and (not w or j > p - w)
     assert A.visible_pairs(n, True, **mask) == count
     assert A.visible_pairs(n, False) == n * n
+
+
+def test_projection_flops_with_grouped_kv_heads():
+    n, d = 1000, 1024
+    assert A.projection_flops(n, d) == 8 * n * d * d
+    assert A.projection_flops(n, d, 256) == 4 * n * d * d + 4 * n * d * 256
+    assert A.layer_flops(n, d, 4 * d, True, d_kv=d) == A.layer_flops(n, d, 4 * d, True)

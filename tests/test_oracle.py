@@ -714,3 +714,76 @@ def test_window_one_lse_is_the_diagonal_score():
     for hh in range(h):
         c = slice(hh * 4, hh * 4 + 4)
         assert np.max(np.abs(lse[hh] - (q[:, c] * k[:, c]).sum(1) / 2.0)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Grouped-query attention (transformer-cost page, MQA and GQA)
+# --------------------------------------------------------------------------
+
+def _gqa_pins(attn):
+    """True iff attn(q, k, v, n_heads, causal) with K, V of g heads passes the pins."""
+    rng = np.random.default_rng(51)
+    n, h, dk = 11, 8, 4
+    ok = []
+    for g in (1, 2, 4):
+        q = rng.standard_normal((n, h * dk))
+        k, v = rng.standard_normal((n, g * dk)), rng.standard_normal((n, g * dk))
+        for causal in (False, True):
+            # torch's SDPA with enable_gqa (float64)
+            sq = torch.from_numpy(q.copy()).view(n, h, dk).transpose(0, 1)[None]
+            sk = torch.from_numpy(k.copy()).view(n, g, dk).transpose(0, 1)[None]
+            sv = torch.from_numpy(v.copy()).view(n, g, dk).transpose(0, 1)[None]
+            ref = F.scaled_dot_product_attention(sq, sk, sv, is_causal=causal, enable_gqa=True)
+            ref = ref[0].transpose(0, 1).reshape(n, h * dk).numpy()
+            ok.append(np.max(np.abs(attn(q, k, v, h, causal) - ref)) < 1e-12)
+            # the page's construction: each key/value head repeated for its group
+            rep = lambda a: np.repeat(a.reshape(n, g, dk), h // g, axis=1).reshape(n, h * dk)  # noqa: E731
+            ok.append(np.max(np.abs(attn(q, k, v, h, causal) - attn(q, rep(k), rep(v), h, causal))) < 1e-12)
+    return all(ok)
+
+
+def test_gqa_pins_hold_for_the_oracle():
+    assert _gqa_pins(lambda q, k, v, h, c: oracle.attention_sequence(q, k, v, h, c))
+
+
+def test_gqa_pins_catch_planted_mistake():
+    def modulo_mapping(q, k, v, h, causal):
+        # query head h reads key/value head h % g instead of h // (h / g)
+        dk = q.shape[1] // h
+        g = k.shape[1] // dk
+        perm = np.concatenate([np.arange((hh % g) * dk, (hh % g + 1) * dk) for hh in range(h)])
+        return oracle.attention_sequence(q, k[:, perm], v[:, perm], h, causal)
+    assert not _gqa_pins(modulo_mapping)
+
+
+def test_mqa_every_head_reads_the_same_keys():
+    rng = np.random.default_rng(53)
+    n, h, dk = 9, 4, 8
+    q = rng.standard_normal((n, dk))
+    q4 = np.tile(q, (1, h))                          # the same query in every head
+    k, v = rng.standard_normal((n, dk)), rng.standard_normal((n, dk))
+    out = oracle.attention_sequence(q4, k, v, h, True)
+    one = oracle.attention_sequence(q, k, v, 1, True)
+    for hh in range(h):
+        assert np.max(np.abs(out[:, hh * dk:(hh + 1) * dk] - one)) < 1e-12
+
+
+@pytest.mark.parametrize("g,mask", [(1, {}), (2, dict(window=6)), (2, dict(chunk=8))])
+def test_gqa_layer_blockwise_and_rows_equal_unfused(g, mask):
+    rng = np.random.default_rng(55)
+    seq, d, h = 37, 16, 4
+    x = rng.standard_normal((2 * seq, d))
+    p = rand_layer(rng, d, 64, std=0.3)
+    dkv = g * (d // h)
+    p["w_k"] = p["w_k"][:, :dkv].copy()
+    p["w_v"] = p["w_v"][:, :dkv].copy()
+    ref = oracle.layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, **mask)
+    got = oracle.blockwise_layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, block_q=8,
+                                         block_kv=16, **mask)
+    assert np.max(np.abs(got - ref)) < 1e-10
+    rows = np.array([0, 9, 36, 37, 73])
+    assert np.max(np.abs(oracle.layer_forward_rows(x, p, rows, seq_len=seq, n_heads=h, causal=True,
+                                                   **mask) - ref[rows])) < 1e-12
+    lse = oracle.layer_lse(x, p, seq_len=seq, n_heads=h, causal=True, **mask)
+    lse_r = oracle.layer_lse_rows(x, p, rows, seq_len=seq, n_heads=h, causal=True, **mask)
+    assert np.max(np.abs(lse_r - lse[rows // seq, :, rows % seq])) < 1e-12
