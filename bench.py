@@ -69,6 +69,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attention-bwd", action="store_true",
                     help="time the attention backward on the workload's attention shape")
+    ap.add_argument("--host", action="store_true",
+                    help="time the host (CPU) fused layer instead (default workload slm_1b_4k)")
+    ap.add_argument("--threads", type=int, default=0,
+                    help="host layer threads (default: the CPUs available, at most 16)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample")
     return ap.parse_args()
@@ -293,8 +297,50 @@ def bench_attention_bwd(args, w):
     print(json.dumps(line), flush=True)
 
 
+def bench_host(args, w):
+    """The host (CPU) fused layer: W warm-up calls, then K timed calls (wall clock)."""
+    import torch
+    from blockwise_attn_ffn_amd import accounting as A, bpt, synth
+
+    n_threads = args.threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    inputs = synth.make_inputs(w, seed=args.seed)
+    desc = bpt.desc_for(w, out_dtype="f32")
+    ws_bytes = bpt.layer_host_workspace_bytes(desc, n_threads)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8)
+    z = torch.empty((w.rows, w.d_model), dtype=torch.float32)
+    for _ in range(args.warmup):
+        bpt.layer_fwd_host(desc, inputs["x"], inputs["layers"][0], z, ws, n_threads)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bpt.layer_fwd_host(desc, inputs["x"], inputs["layers"][0], z, ws, n_threads)
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flops = A.workload_flops(w.batch, w.seq_len, w.d_model, w.d_ff, w.causal, 1, w.window, w.chunk,
+                             w.d_kv)
+    line = {
+        "metric": "fused BPT layer fwd on the host CPU, TFLOP/s (fp32 arithmetic)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 4), "unit": "TFLOP/s", "n_gpus": 0,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Gaussian X and weights, random-init)",
+        "config": {"workload": w.name + " (host)", "batch": w.batch, "seq_len": w.seq_len,
+                   "d_model": w.d_model, "n_heads": w.n_heads, "d_ff": w.d_ff, "causal": w.causal,
+                   "block_q": w.block_q, "input_dtype": w.dtype, "threads": n_threads},
+        "flops_per_step": flops,
+        "memory": {"workspace_bytes": ws_bytes,
+                   "ffn_hidden_unfused_bytes": w.rows * w.d_ff * 2,
+                   "ffn_hidden_tile_bytes_per_thread": w.block_q * 512 * 4},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
+    if args.host:
+        from blockwise_attn_ffn_amd import synth
+        wl = args.workload if args.workload != "gpt2_medium" else "slm_1b_4k"
+        return bench_host(args, synth.WORKLOADS[wl])
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))

@@ -18,7 +18,8 @@ WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o", "ln2_g", "ln2_b",
 EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer_fwd",
             "bpt_layer_fwd_profiled", "bpt_layer_fwd_lse", "bpt_stack_fwd",
             "bpt_attention_bwd_workspace_bytes", "bpt_attention_bwd",
-            "bpt_attention_bwd_profiled", "bpt_status_str",
+            "bpt_attention_bwd_profiled", "bpt_layer_host_workspace_bytes", "bpt_layer_fwd_host",
+            "bpt_status_str",
             "bpt_last_error", "bpt_version")
 
 
@@ -87,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.bpt_attention_bwd.restype = ctypes.c_int
         L.bpt_attention_bwd_profiled.argtypes = L.bpt_attention_bwd.argtypes + [P(ctypes.c_void_p)]
         L.bpt_attention_bwd_profiled.restype = ctypes.c_int
+        L.bpt_layer_host_workspace_bytes.argtypes = [P(LayerDesc), ctypes.c_int32]
+        L.bpt_layer_host_workspace_bytes.restype = ctypes.c_size_t
+        L.bpt_layer_fwd_host.argtypes = [P(LayerDesc), ctypes.c_void_p, P(LayerWeights),
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_int32]
+        L.bpt_layer_fwd_host.restype = ctypes.c_int
         L.bpt_status_str.argtypes = [ctypes.c_int]
         L.bpt_status_str.restype = ctypes.c_char_p
         L.bpt_last_error.argtypes = []
@@ -204,6 +211,28 @@ def attention_bwd_profiled(desc: AttnDesc, q, k, v, o, do, lse, dq, dk, dv, work
     _check(lib().bpt_attention_bwd_profiled(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                             _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                             _ptr(workspace), nbytes, _stream(stream), arr))
+
+
+def layer_host_workspace_bytes(desc: LayerDesc, n_threads: int) -> int:
+    return int(lib().bpt_layer_host_workspace_bytes(ctypes.byref(desc), n_threads))
+
+
+def _hptr(t) -> int:
+    if t is None:
+        return 0
+    if t.is_cuda:
+        raise ValueError("host tensors are required")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensors are required")
+    return t.data_ptr()
+
+
+def layer_fwd_host(desc: LayerDesc, x, layer: dict, z, workspace, n_threads: int) -> None:
+    """The host (CPU) fused layer on CPU tensors (synchronous)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    w = LayerWeights(*[_hptr(layer[n]) for n in WEIGHT_FIELDS])
+    _check(lib().bpt_layer_fwd_host(ctypes.byref(desc), _hptr(x), ctypes.byref(w), _hptr(z),
+                                    _hptr(workspace), nbytes, n_threads))
 
 
 def stack_fwd(desc: LayerDesc, x, layers: list, z, workspace, stream=None) -> None:

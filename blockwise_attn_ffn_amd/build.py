@@ -30,11 +30,13 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
 
 KERNEL_SOURCES = ["k_ln_qkv.hip", "k_gemm.hip", "k_attention.hip", "k_ffn.hip", "k_pack.hip",
                   "k_attention_bwd.hip", "bpt_launch.hip"]
-HOST_SOURCES = ["bpt_api.cpp", "bpt_support.cpp"]
+HOST_SOURCES = ["bpt_api.cpp", "bpt_support.cpp", "bpt_host.cpp"]
 # Per-source extra flags. The attention backward keeps its matrix-core results in
 # ordinary VGPRs (they feed the softmax arithmetic at once); left to itself the
 # compiler places them in AGPRs and copies every value back.
-EXTRA_FLAGS = {"k_attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"k_attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               # the host (CPU) layer: 8-wide fp32 vectors with fused multiply-add
+               "bpt_host.cpp": ["-O3", "-mavx2", "-mfma", "-pthread"]}
 
 
 def hipcc() -> str:
@@ -61,13 +63,13 @@ def build(verbose: bool = False) -> str:
         jobs.append([cc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append(["g++", *HOST_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for f in [ex.submit(_run, j) for j in jobs]:
             f.result()
     objs = [j[-1] for j in jobs]
     tmp = LIB_PATH + ".tmp"
-    _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    _run([cc, "-shared", f"--offload-arch={ARCH}", "-pthread", "-o", tmp, *objs])
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")

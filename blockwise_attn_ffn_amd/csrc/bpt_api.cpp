@@ -421,6 +421,107 @@ bpt_status_t bpt_attention_bwd_profiled(const bpt_attn_desc_t* desc, const void*
   return BPT_OK;
 }
 
+namespace {
+
+bpt_status_t validate_host_desc(const bpt_layer_desc_t* d, int32_t n_threads) {
+  if (!d) return fail(BPT_ERR_NULL, "desc is NULL");
+  if (d->batch < 0 || d->seq_len < 0) return fail(BPT_ERR_SHAPE, "batch and seq_len must be >= 0");
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->d_ff <= 0 || d->block_q <= 0)
+    return fail(BPT_ERR_SHAPE, "d_model, n_heads, d_ff and block_q must be > 0");
+  if (d->d_model % d->n_heads != 0)
+    return fail(BPT_ERR_SHAPE, "d_model %d is not a multiple of n_heads %d", d->d_model, d->n_heads);
+  if (d->causal != 0 && d->causal != 1) return fail(BPT_ERR_SHAPE, "causal must be 0 or 1");
+  if (d->window < 0 || d->chunk < 0) return fail(BPT_ERR_SHAPE, "window and chunk must be >= 0");
+  if ((d->window || d->chunk) && !d->causal)
+    return fail(BPT_ERR_SHAPE, "window and chunk apply to the causal mask only");
+  if (d->window && d->chunk) return fail(BPT_ERR_SHAPE, "window and chunk cannot be combined");
+  if (d->n_kv_heads < 0 || (d->n_kv_heads && d->n_heads % d->n_kv_heads != 0))
+    return fail(BPT_ERR_SHAPE, "n_kv_heads %d must be 0 or divide n_heads %d", d->n_kv_heads,
+                d->n_heads);
+  if (!(d->ln_eps > 0.0f) || !isfinite(d->ln_eps))
+    return fail(BPT_ERR_SHAPE, "ln_eps must be finite and > 0");
+  if ((d->dtype != BPT_F32 && d->dtype != BPT_BF16) ||
+      (d->out_dtype != BPT_F32 && d->out_dtype != BPT_BF16))
+    return fail(BPT_ERR_SHAPE, "dtype / out_dtype must be BPT_F32 or BPT_BF16");
+  if (d->act != 0) return fail(BPT_ERR_UNSUPPORTED, "act %d unsupported (0 = GELU tanh)", d->act);
+  if (d->precision != 0) return fail(BPT_ERR_UNSUPPORTED, "the host layer computes in fp32 (precision 0)");
+  if (d->d_model % 8 || (d->d_model / d->n_heads) % 8 || d->d_ff % 8)
+    return fail(BPT_ERR_UNSUPPORTED, "d_model, d_head and d_ff must be multiples of 8");
+  if (n_threads < 1 || n_threads > 1024) return fail(BPT_ERR_SHAPE, "n_threads must be in [1, 1024]");
+  if ((int64_t)d->batch * d->seq_len > (int64_t)INT32_MAX)
+    return fail(BPT_ERR_SHAPE, "batch * seq_len exceeds the 32-bit row index range");
+  return BPT_OK;
+}
+
+size_t host_workspace(const bpt_layer_desc_t* d, int32_t n_threads, size_t* kv_bytes) {
+  const size_t kvb = round_up((size_t)d->batch * d->seq_len * kv_width(d) * sizeof(float), kAlign);
+  if (kv_bytes) *kv_bytes = kvb;
+  const size_t per = bpt::host_scratch_floats(d->d_model, d->n_heads, d->block_q) * sizeof(float);
+  return 2 * kvb + (size_t)n_threads * round_up(per, kAlign);
+}
+
+}  // namespace
+
+size_t bpt_layer_host_workspace_bytes(const bpt_layer_desc_t* desc, int32_t n_threads) {
+  if (validate_host_desc(desc, n_threads) != BPT_OK) return 0;
+  if (is_empty(desc)) return 0;
+  return host_workspace(desc, n_threads, nullptr);
+}
+
+bpt_status_t bpt_layer_fwd_host(const bpt_layer_desc_t* desc, const void* X,
+                                const bpt_layer_weights_t* weights, void* Z, void* workspace,
+                                size_t workspace_bytes, int32_t n_threads) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_host_desc(desc, n_threads);
+  if (st != BPT_OK) return st;
+  if (is_empty(desc)) return BPT_OK;
+  if (!weights) return fail(BPT_ERR_NULL, "weights is NULL");
+  const void* p[10] = {weights->ln1_g, weights->ln1_b, weights->w_q, weights->w_k, weights->w_v,
+                       weights->w_o,   weights->ln2_g, weights->ln2_b, weights->w_1, weights->w_2};
+  for (int i = 0; i < 10; ++i)
+    if (!p[i]) return fail(BPT_ERR_NULL, "weights[0] entry %d is NULL", i);
+  if (!X) return fail(BPT_ERR_NULL, "X is NULL");
+  if (!Z) return fail(BPT_ERR_NULL, "Z is NULL");
+  if (!workspace) return fail(BPT_ERR_NULL, "workspace is NULL");
+  size_t kvb = 0;
+  const size_t need = host_workspace(desc, n_threads, &kvb);
+  if (workspace_bytes < need)
+    return fail(BPT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 3u) != 0) return fail(BPT_ERR_ALIGN, "workspace is not 4-byte aligned");
+  const size_t rows = (size_t)desc->batch * desc->seq_len;
+  const size_t xb = rows * desc->d_model * esize(desc->dtype);
+  const size_t zb = rows * desc->d_model * esize(desc->out_dtype);
+  if (overlap(X, xb, Z, zb)) return fail(BPT_ERR_ALIAS, "X and Z overlap");
+  if (overlap(workspace, need, X, xb)) return fail(BPT_ERR_ALIAS, "workspace overlaps X");
+  if (overlap(workspace, need, Z, zb)) return fail(BPT_ERR_ALIAS, "workspace overlaps Z");
+  bpt::HostLaunch L{};
+  L.batch = desc->batch;
+  L.seq_len = desc->seq_len;
+  L.d_model = desc->d_model;
+  L.n_heads = desc->n_heads;
+  L.n_kv_heads = kv_heads(desc);
+  L.d_kv = (int)kv_width(desc);
+  L.d_ff = desc->d_ff;
+  L.block_q = desc->block_q;
+  L.causal = desc->causal;
+  L.window = desc->window;
+  L.chunk = desc->chunk;
+  L.ln_eps = desc->ln_eps;
+  L.x_f32 = desc->dtype == BPT_F32;
+  L.w_f32 = desc->dtype == BPT_F32;
+  L.z_f32 = desc->out_dtype == BPT_F32;
+  L.x = X;
+  L.w = *weights;
+  L.z = Z;
+  char* ws = static_cast<char*>(workspace);
+  L.kbuf = reinterpret_cast<float*>(ws);
+  L.vbuf = reinterpret_cast<float*>(ws + kvb);
+  L.scratch = reinterpret_cast<float*>(ws + 2 * kvb);
+  L.n_threads = n_threads;
+  if (bpt::launch_layer_host(L)) return fail(BPT_ERR_UNSUPPORTED, "no host instance for these types");
+  return BPT_OK;
+}
+
 const char* bpt_status_str(bpt_status_t s) {
   switch (s) {
     case BPT_OK: return "ok";

@@ -107,6 +107,22 @@ inline size_t qkv_pack_elems(int d_model, int kv_pad) {
   return (size_t)(d_model + 2 * kv_pad) * d_model;
 }
 
+// The host (CPU) fused layer: HOST pointers, fp32 arithmetic.
+struct HostLaunch {
+  int batch, seq_len, d_model, n_heads, n_kv_heads, d_kv, d_ff, block_q, causal, window, chunk;
+  float ln_eps;
+  int x_f32, w_f32, z_f32;
+  const void* x;
+  bpt_layer_weights_t w;
+  void* z;
+  float* kbuf;      // K [batch * seq_len, d_kv]
+  float* vbuf;      // V
+  float* scratch;   // n_threads x host_scratch_floats
+  int n_threads;
+};
+size_t host_scratch_floats(int d_model, int n_heads, int block_q);
+int launch_layer_host(const HostLaunch& L);
+
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).
 int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t errlen);
 

@@ -83,6 +83,11 @@ WORKLOADS = {
     "long_128k_w4096": Workload("long_128k_w4096", batch=1, seq_len=131072, d_model=2048,
                                 n_heads=16, d_ff=8192, causal=True, block_q=128, block_kv=64,
                                 dtype="bf16", sample_rows=256, window=4096),
+    # the BPT page's CPU case: a 1B-parameter model's layer (d 2048) on a 4096-token
+    # prompt, blocks of 128 rows (the [128, 4d] tile is 2 MB in bf16)
+    "slm_1b_4k": Workload("slm_1b_4k", batch=1, seq_len=4096, d_model=2048, n_heads=16,
+                          d_ff=8192, causal=True, block_q=128, block_kv=64, dtype="bf16",
+                          sample_rows=64),
     # the long-context layer with grouped-query attention: 4 key/value heads
     "long_128k_gqa4": Workload("long_128k_gqa4", batch=1, seq_len=131072, d_model=2048,
                                n_heads=16, d_ff=8192, causal=True, block_q=128, block_kv=64,

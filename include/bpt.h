@@ -219,6 +219,23 @@ bpt_status_t bpt_attention_bwd_profiled(const bpt_attn_desc_t* desc, const void*
                                         void* workspace, size_t workspace_bytes, void* hip_stream,
                                         void* const events[5]);
 
+/* The same layer on the host CPU: the fused blockwise loop of the BPT page (and
+ * its section "On CPUs and small language models": per block of block_q rows the
+ * [block_q, d_ff] hidden state is produced and consumed in cache-sized chunks and
+ * never written out), query blocks spread over n_threads threads (>= 1). X, Z,
+ * the weights and the workspace are HOST pointers (no alignment needed); the
+ * arithmetic is fp32 whatever dtype says (bf16 inputs are widened; a bf16 Z is
+ * rounded to nearest even). Every descriptor field means what it means for
+ * bpt_layer_fwd, with these limits instead of the GPU's kernel table: d_model,
+ * d_head and d_ff multiples of 8, any block_q >= 1, precision 0, dtype BPT_F32
+ * with fp32 or bf16 weights not distinguished (the weights have dtype's type).
+ * Synchronous: returns when Z is written. The workspace holds K and V in fp32
+ * [batch * seq_len, n_kv_heads * d_head] and per-thread block scratch. */
+size_t bpt_layer_host_workspace_bytes(const bpt_layer_desc_t* desc, int32_t n_threads);
+bpt_status_t bpt_layer_fwd_host(const bpt_layer_desc_t* desc, const void* X,
+                                const bpt_layer_weights_t* weights, void* Z, void* workspace,
+                                size_t workspace_bytes, int32_t n_threads);
+
 /* n_layers >= 1 layers applied in turn, all with the shape of *desc; layers is
  * a HOST array of n_layers weight sets (each holding device pointers). Layer 0
  * reads X in desc->dtype; the residual stream between layers is fp32; the last

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "../blockwise_attn_ffn_amd/csrc/bpt_internal.h"
 #include "bpt.h"
 
@@ -186,6 +188,33 @@ int main() {
   EXPECT(bpt_attention_bwd(&ab, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                            nullptr, nullptr, 0, nullptr) == BPT_OK);
   EXPECT(bpt::g_bwd_launches == 0);
+  // the host layer runs for real here: small fp32 layer, window mask, grouped heads
+  {
+    bpt_layer_desc_t hd{};
+    hd.batch = 2; hd.seq_len = 37; hd.d_model = 32; hd.n_heads = 4; hd.d_ff = 64;
+    hd.block_q = 16; hd.block_kv = 64; hd.causal = 1; hd.ln_eps = 1e-5f;
+    hd.dtype = BPT_F32; hd.out_dtype = BPT_F32; hd.window = 9; hd.n_kv_heads = 2;
+    const int rows = 2 * 37, dm = 32, dkv = 16, ff = 64;
+    std::vector<float> x(rows * dm), z(rows * dm, -1.f), g(dm, 1.f), bz(dm, 0.f);
+    std::vector<float> wq(dm * dm), wk(dkv * dm), wv(dkv * dm), wo(dm * dm), w1(ff * dm), w2(dm * ff);
+    unsigned seed = 1;
+    auto rnd = [&]() { seed = seed * 1664525u + 1013904223u; return ((seed >> 8) & 0xFFFF) / 65536.f - 0.5f; };
+    for (auto* v : {&x, &wq, &wk, &wv, &wo, &w1, &w2})
+      for (auto& e : *v) e = rnd();
+    bpt_layer_weights_t hw = {g.data(), bz.data(), wq.data(), wk.data(), wv.data(), wo.data(),
+                              g.data(), bz.data(), w1.data(), w2.data()};
+    const size_t nb = bpt_layer_host_workspace_bytes(&hd, 3);
+    EXPECT(nb > 0);
+    std::vector<float> ws(nb / 4 + 1);
+    EXPECT(bpt_layer_fwd_host(&hd, x.data(), &hw, z.data(), ws.data(), nb, 3) == BPT_OK);
+    bool finite = true;
+    for (float e : z) finite = finite && isfinite(e) && e != -1.f;
+    EXPECT(finite);
+    EXPECT(bpt_layer_fwd_host(&hd, x.data(), &hw, z.data(), ws.data(), nb - 4, 3) == BPT_ERR_WORKSPACE);
+    EXPECT(bpt_layer_fwd_host(&hd, x.data(), &hw, x.data(), ws.data(), nb, 3) == BPT_ERR_ALIAS);
+    EXPECT(bpt_layer_fwd_host(&hd, x.data(), nullptr, z.data(), ws.data(), nb, 3) == BPT_ERR_NULL);
+    EXPECT(bpt_layer_host_workspace_bytes(&hd, 0) == 0);
+  }
   if (!g_fail) printf("ALL OK\n");
   return g_fail;
 }

@@ -281,7 +281,8 @@ def test_host_abi_under_address_and_ub_sanitizers(tmp_path):
     exe = str(tmp_path / "abi_host")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
            "-fno-sanitize-recover=all", f"-I{os.path.join(ROOT, 'include')}",
-           os.path.join(csrc, "bpt_api.cpp"), os.path.join(csrc, "bpt_support.cpp"), drv, "-o", exe]
+           "-mavx2", "-mfma", "-pthread", os.path.join(csrc, "bpt_api.cpp"),
+           os.path.join(csrc, "bpt_support.cpp"), os.path.join(csrc, "bpt_host.cpp"), drv, "-o", exe]
     subprocess.run(cmd, check=True)
     res = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
                          timeout=120)
