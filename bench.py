@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attention-bwd", action="store_true",
                     help="time the attention backward on the workload's attention shape")
+    ap.add_argument("--ring", type=int, default=0,
+                    help="time one device's share of Ring Attention over this many devices "
+                         "(default workload long_128k: shards of seq_len / devices tokens)")
     ap.add_argument("--host", action="store_true",
                     help="time the host (CPU) fused layer instead (default workload slm_1b_4k)")
     ap.add_argument("--threads", type=int, default=0,
@@ -335,8 +338,81 @@ def bench_host(args, w):
     print(json.dumps(line), flush=True)
 
 
+def bench_ring(args, w, R):
+    """The last device of an R-device ring (it meets every shard: R - 1 earlier ones
+    unmasked and its own causal): R steps + R merges per timed iteration; also one
+    unmasked step alone."""
+    import torch
+    from blockwise_attn_ffn_amd import accounting as A, bpt, synth
+
+    n = w.seq_len // R
+    d, h = w.d_model, w.n_heads
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(args.seed)
+    shards = {x: [(torch.randn(n, d, generator=gen)).to(torch.bfloat16).cuda() for _ in range(R)]
+              for x in ("q", "k", "v")}
+    desc_full = bpt.make_attn_desc(batch=1, seq_len=n, d_model=d, n_heads=h, causal=False)
+    desc_diag = bpt.make_attn_desc(batch=1, seq_len=n, d_model=d, n_heads=h, causal=True)
+    ws = bpt.alloc_workspace(bpt.attention_fwd_workspace_bytes(desc_full))
+    o = torch.empty(n, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(1, h, n, dtype=torch.float32, device="cuda")
+    o_acc = torch.zeros(n, d, dtype=torch.float32, device="cuda")
+    lse_acc = torch.empty(1, h, n, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    q = shards["q"][R - 1]
+
+    def ring():
+        lse_acc.fill_(float("-inf"))
+        for s_ in range(R):
+            dsc = desc_diag if s_ == R - 1 else desc_full
+            bpt.attention_fwd(dsc, q, shards["k"][s_], shards["v"][s_], o, lse, ws, stream)
+            bpt.attention_merge(desc_full, o_acc, lse_acc, o, lse, stream)
+
+    def one_step():
+        bpt.attention_fwd(desc_full, q, shards["k"][0], shards["v"][0], o, lse, ws, stream)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms_ring = timed(ring, args.steps)
+    ms_step = timed(one_step, args.steps)
+    flops_ring = (R - 1) * A.attention_flops(n, d, False) + A.attention_flops(n, d, True)
+    flops_step = A.attention_flops(n, d, False)
+    line = {
+        "metric": "Ring Attention, one device's share: TFLOP/s of its steps (1 MI355X)",
+        "value": round(flops_ring / (ms_ring * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_ring, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian Q, K, V)",
+        "config": {"workload": f"{w.name} over {R} devices, the last device", "shard_tokens": n,
+                   "d_model": d, "n_heads": h, "ring_steps": R, "parallelism": "none (one device's share)"},
+        "flops_per_step": flops_ring,
+        "one_unmasked_step": {"ms": round(ms_step, 3), "flops": flops_step,
+                              "tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 2)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
+    if args.ring:
+        import torch
+        from blockwise_attn_ffn_amd import synth
+        if not torch.cuda.is_available():
+            print(json.dumps({"error": "no GPU visible"}))
+            sys.exit(1)
+        wl = args.workload if args.workload != "gpt2_medium" else "long_128k"
+        return bench_ring(args, synth.WORKLOADS[wl], args.ring)
     if args.host:
         from blockwise_attn_ffn_amd import synth
         wl = args.workload if args.workload != "gpt2_medium" else "slm_1b_4k"

@@ -18,7 +18,8 @@ WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o", "ln2_g", "ln2_b",
 EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer_fwd",
             "bpt_layer_fwd_profiled", "bpt_layer_fwd_lse", "bpt_stack_fwd",
             "bpt_attention_bwd_workspace_bytes", "bpt_attention_bwd",
-            "bpt_attention_bwd_profiled", "bpt_layer_host_workspace_bytes", "bpt_layer_fwd_host",
+            "bpt_attention_bwd_profiled", "bpt_attention_fwd_workspace_bytes", "bpt_attention_fwd",
+            "bpt_attention_merge", "bpt_layer_host_workspace_bytes", "bpt_layer_fwd_host",
             "bpt_status_str",
             "bpt_last_error", "bpt_version")
 
@@ -88,6 +89,13 @@ def lib() -> ctypes.CDLL:
         L.bpt_attention_bwd.restype = ctypes.c_int
         L.bpt_attention_bwd_profiled.argtypes = L.bpt_attention_bwd.argtypes + [P(ctypes.c_void_p)]
         L.bpt_attention_bwd_profiled.restype = ctypes.c_int
+        L.bpt_attention_fwd_workspace_bytes.argtypes = [P(AttnDesc)]
+        L.bpt_attention_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.bpt_attention_fwd.argtypes = [P(AttnDesc)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t,
+                                                                               ctypes.c_void_p]
+        L.bpt_attention_fwd.restype = ctypes.c_int
+        L.bpt_attention_merge.argtypes = [P(AttnDesc)] + [ctypes.c_void_p] * 5
+        L.bpt_attention_merge.restype = ctypes.c_int
         L.bpt_layer_host_workspace_bytes.argtypes = [P(LayerDesc), ctypes.c_int32]
         L.bpt_layer_host_workspace_bytes.restype = ctypes.c_size_t
         L.bpt_layer_fwd_host.argtypes = [P(LayerDesc), ctypes.c_void_p, P(LayerWeights),
@@ -211,6 +219,23 @@ def attention_bwd_profiled(desc: AttnDesc, q, k, v, o, do, lse, dq, dk, dv, work
     _check(lib().bpt_attention_bwd_profiled(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                             _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                             _ptr(workspace), nbytes, _stream(stream), arr))
+
+
+def attention_fwd_workspace_bytes(desc: AttnDesc) -> int:
+    return int(lib().bpt_attention_fwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def attention_fwd(desc: AttnDesc, q, k, v, o, lse, workspace, stream=None) -> None:
+    """One ring step: attention of the query shard q against the key/value shard (k, v)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bpt_attention_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   _ptr(workspace), nbytes, _stream(stream)))
+
+
+def attention_merge(desc: AttnDesc, o_acc, lse_acc, o_part, lse_part, stream=None) -> None:
+    """Fold one ring step's (o_part, lse_part) into the running (o_acc, lse_acc)."""
+    _check(lib().bpt_attention_merge(ctypes.byref(desc), _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
+                                     _ptr(lse_part), _stream(stream)))
 
 
 def layer_host_workspace_bytes(desc: LayerDesc, n_threads: int) -> int:

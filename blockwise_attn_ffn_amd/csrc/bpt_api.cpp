@@ -421,6 +421,83 @@ bpt_status_t bpt_attention_bwd_profiled(const bpt_attn_desc_t* desc, const void*
   return BPT_OK;
 }
 
+size_t bpt_attention_fwd_workspace_bytes(const bpt_attn_desc_t* desc) {
+  if (validate_attn_desc(desc) != BPT_OK) return 0;
+  if (attn_empty(desc)) return 0;
+  return 3 * round_up((size_t)desc->batch * round_up((size_t)desc->seq_len, 128) * desc->d_model * 2,
+                      kAlign);
+}
+
+bpt_status_t bpt_attention_fwd(const bpt_attn_desc_t* desc, const void* Q, const void* K,
+                               const void* V, void* O, float* lse, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_attn_desc(desc);
+  if (st != BPT_OK) return st;
+  if (attn_empty(desc)) return BPT_OK;
+  const void* ptrs[] = {Q, K, V, O, lse, workspace};
+  const char* names[] = {"Q", "K", "V", "O", "lse", "workspace"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(BPT_ERR_NULL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(BPT_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t need = bpt_attention_fwd_workspace_bytes(desc);
+  if (workspace_bytes < need)
+    return fail(BPT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t rows = (size_t)desc->batch * desc->seq_len;
+  const size_t in_b = rows * desc->d_model * 2, lse_b = rows * desc->n_heads * sizeof(float);
+  const size_t sizes[] = {in_b, in_b, in_b, in_b, lse_b, need};
+  for (int i = 3; i < 6; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (j != i && overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
+        return fail(BPT_ERR_ALIAS, "%s overlaps %s", names[i], names[j]);
+  bpt::AttnFwdLaunch p{};
+  p.batch = desc->batch;
+  p.seq_len = desc->seq_len;
+  p.seq_pad = (int)round_up((size_t)desc->seq_len, 128);
+  p.d_model = desc->d_model;
+  p.n_heads = desc->n_heads;
+  p.d_head = desc->d_model / desc->n_heads;
+  p.causal = desc->causal;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = lse;
+  const size_t pb = need / 3;
+  for (int i = 0; i < 3; ++i) p.packed[i] = static_cast<char*>(workspace) + i * pb;
+  char msg[256] = "";
+  if (bpt::launch_attention_fwd(p, hip_stream, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
+  return BPT_OK;
+}
+
+bpt_status_t bpt_attention_merge(const bpt_attn_desc_t* desc, float* O_acc, float* lse_acc,
+                                 const void* O_part, const float* lse_part, void* hip_stream) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_attn_desc(desc);
+  if (st != BPT_OK) return st;
+  if (attn_empty(desc)) return BPT_OK;
+  const void* ptrs[] = {O_acc, lse_acc, O_part, lse_part};
+  const char* names[] = {"O_acc", "lse_acc", "O_part", "lse_part"};
+  for (int i = 0; i < 4; ++i) {
+    if (!ptrs[i]) return fail(BPT_ERR_NULL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(BPT_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t rows = (size_t)desc->batch * desc->seq_len;
+  const size_t sizes[] = {rows * desc->d_model * 4, rows * desc->n_heads * 4, rows * desc->d_model * 2,
+                          rows * desc->n_heads * 4};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (j != i && overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
+        return fail(BPT_ERR_ALIAS, "%s overlaps %s", names[i], names[j]);
+  char msg[256] = "";
+  if (bpt::launch_attention_merge(desc->batch, desc->seq_len, desc->n_heads,
+                                  desc->d_model / desc->n_heads, O_acc, lse_acc, O_part, lse_part,
+                                  hip_stream, msg, sizeof(msg)))
+    return fail(BPT_ERR_HIP, "%s", msg);
+  return BPT_OK;
+}
+
 namespace {
 
 bpt_status_t validate_host_desc(const bpt_layer_desc_t* d, int32_t n_threads) {

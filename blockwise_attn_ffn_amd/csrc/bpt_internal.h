@@ -107,6 +107,20 @@ inline size_t qkv_pack_elems(int d_model, int kv_pad) {
   return (size_t)(d_model + 2 * kv_pad) * d_model;
 }
 
+// Attention forward of one (query shard, key/value shard) pair: row-major bf16 Q,
+// K, V in, O (bf16) and lse out; packed: Q (then O), K, V^T copies in the workspace.
+struct AttnFwdLaunch {
+  int batch, seq_len, seq_pad, d_model, n_heads, d_head, causal;
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  void* packed[3];
+};
+int launch_attention_fwd(const AttnFwdLaunch& L, void* stream, char* err, size_t errlen);
+int launch_attention_merge(int batch, int seq_len, int n_heads, int d_head, float* o_acc,
+                           float* lse_acc, const void* o_part, const float* lse_part, void* stream,
+                           char* err, size_t errlen);
+
 // The host (CPU) fused layer: HOST pointers, fp32 arithmetic.
 struct HostLaunch {
   int batch, seq_len, d_model, n_heads, n_kv_heads, d_kv, d_ff, block_q, causal, window, chunk;

@@ -24,6 +24,7 @@
 // A first kernel also writes, per (sequence, head) and padded to Np rows,
 // D = rowsum(dO * O) and lse * log2(e) (+inf past seq_len, so that padded query
 // rows get P = 0).
+#include "attn_pack.hpp"
 #include "bpt_device.hpp"
 #include "bpt_launch.hpp"
 
@@ -65,48 +66,6 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const bf16* __restrict__
     const size_t i = ((size_t)b * H + h) * Np + pos;
     Dp[i] = acc;
     L2[i] = pos < N ? lse[((size_t)b * H + h) * N + pos] * kLog2e : __builtin_inff();
-  }
-}
-
-// Transpose into cols-A fragments. One workgroup per (tensor, sequence, head,
-// 64-token tile, 64-feature tile): the tile is read row by row (coalesced) into
-// LDS, then written as 8 whole fragments (2 feature tiles of 32 x 4 token k-steps).
-struct TransposeJob {
-  const bf16* src[3];
-  bf16* dst[3];
-};
-
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(TransposeJob job, int N, int Np, int H,
-                                                            int dk) {
-  __shared__ __align__(16) bf16 tile[64][72];     // [token][feature], rows padded to 144 B
-  const bf16* __restrict__ src = job.src[blockIdx.y];
-  bf16* __restrict__ dst = job.dst[blockIdx.y];
-  const int d = H * dk, ftiles = dk / 64, ttiles = Np / 64;
-  int x = blockIdx.x;
-  const int ft = x % ftiles;
-  x /= ftiles;
-  const int tt = x % ttiles;
-  const int bh = x / ttiles;
-  const int b = bh / H, h = bh - b * H;
-#pragma unroll
-  for (int i = threadIdx.x; i < 512; i += 256) {
-    const int r = i >> 3, c = i & 7, pos = tt * 64 + r;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (pos < N)
-      v = *reinterpret_cast<const uint4*>(src + ((size_t)b * N + pos) * d + (size_t)h * dk + ft * 64 + c * 8);
-    *reinterpret_cast<uint4*>(&tile[r][c * 8]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = threadIdx.x; i < 512; i += 256) {
-    const int f = i >> 6, slot = i & 63;
-    const int dtl = f >> 2, ks = f & 3;
-    const int feat = dtl * 32 + pi_row(slot & 31), tok0 = ks * 16 + 8 * (slot >> 5);
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tile[tok0 + e][feat];
-    const size_t frag = ((size_t)bh * (dk / 32) + ft * 2 + dtl) * (Np / 16) + tt * 4 + ks;
-    *reinterpret_cast<bf16x8*>(dst + frag * kFragElems + slot * 8) = v;
   }
 }
 

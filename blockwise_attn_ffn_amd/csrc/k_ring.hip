@@ -1,0 +1,105 @@
+// One device's share of Ring Attention (gfx950).
+//
+// "Blockwise Parallel Transformer — BPT" (aicassindra.com), section "BPT and Ring
+// Attention": the sequence is sharded across devices, each device keeps its query
+// shard, and key/value shards travel around a ring until every query has met every
+// key; BPT's inner loop already consumes K/V a block at a time, so only where the
+// next block comes from changes. On one device a step is attention of the local
+// query shard against the shard that arrived (causal within the device's own shard,
+// unmasked against earlier shards, nothing against later ones), and the steps'
+// normalised outputs are combined through their saved statistics:
+//   lse = ln(e^lse_a + e^lse_b),   O = e^(lse_a - lse) O_a + e^(lse_b - lse) O_b,
+// the same rescaling the online softmax applies between key/value blocks.
+//
+// attention_fwd: row-major Q, K, V (bf16) are copied into the attention kernel's
+// fragment layouts, the layer's attention kernel runs on them (writing O over Q's
+// copy and lse), and O is copied back to row-major. merge: the running state (fp32)
+// absorbs one step's (O, lse).
+#include "attn_pack.hpp"
+#include "bpt_device.hpp"
+#include "bpt_launch.hpp"
+
+namespace bpt {
+
+// Running state update, one thread per (row, head): acc <- merge(acc, part).
+__global__ __launch_bounds__(256) void attn_merge_kernel(float* __restrict__ o_acc,
+                                                         float* __restrict__ lse_acc,
+                                                         const bf16* __restrict__ o_part,
+                                                         const float* __restrict__ lse_part, int B,
+                                                         int N, int H, int dk) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;   // ((b H + h) N + pos)
+  if (t >= (long long)B * H * N) return;
+  const int pos = (int)(t % N);
+  const long long bh = t / N;
+  const int h = (int)(bh % H), b = (int)(bh / H);
+  const float la = lse_acc[t], lb = lse_part[t];
+  const float m = fmaxf(la, lb);                     // lb is finite: a row sees its own key
+  const float lse = m + logf(expf(la - m) + expf(lb - m));
+  const float wa = expf(la - lse), wb = expf(lb - lse);   // wa = 0 while acc is empty (-inf)
+  const size_t off = ((size_t)b * N + pos) * (size_t)(H * dk) + (size_t)h * dk;
+  for (int j = 0; j < dk; j += 8) {
+    float a[8], p[8];
+    load8_f32(o_acc + off + j, a);
+    load8_f32(o_part + off + j, p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = wa == 0.f ? wb * p[e] : fmaf(wa, a[e], wb * p[e]);
+    store8_f32(o_acc + off + j, a);
+  }
+  lse_acc[t] = lse;
+}
+
+int launch_attention_fwd(const AttnFwdLaunch& A, void* stream, char* err, size_t n) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int B = A.batch, N = A.seq_len, Np = A.seq_pad, H = A.n_heads, dk = A.d_head, d = A.d_model;
+  if (d != H * dk || Np % 128 != 0 || Np < N || N < 1) {
+    set_err(err, n, "attention forward: inconsistent launch shape%s (seq_pad %d)", "", Np);
+    return 1;
+  }
+  bf16* qp = static_cast<bf16*>(A.packed[0]);
+  bf16* kp = static_cast<bf16*>(A.packed[1]);
+  bf16* vtp = static_cast<bf16*>(A.packed[2]);
+  const long long chunks = (long long)B * Np * (d / 8);
+  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16*>(A.q), qp, (int)kRowsB, B, N, Np, H, dk);
+  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16*>(A.k), kp, (int)kRowsA, B, N, Np, H, dk);
+  TransposeJob job{{static_cast<const bf16*>(A.v), nullptr, nullptr}, {vtp, nullptr, nullptr}};
+  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(B * H * (Np / 64) * (dk / 64)), 1),
+                     dim3(256), 0, s, job, N, Np, H, dk);
+  if (check_launch("attention_fwd pack", err, n)) return 1;
+  // the layer's attention kernels on the packed operands (block sizes of the
+  // tuned path: 128-row query blocks; 64-key blocks at d_k 128, 128 at d_k 64)
+  LayerLaunch L{};
+  L.batch = B;
+  L.seq_len = N;
+  L.seq_pad = Np;
+  L.d_model = d;
+  L.n_heads = H;
+  L.n_kv_heads = H;
+  L.d_kv = d;
+  L.d_head = dk;
+  L.block_q = 128;
+  L.block_kv = dk == 128 ? 64 : 128;
+  L.causal = A.causal;
+  L.q = qp;
+  L.k = kp;
+  L.vt = vtp;
+  L.lse = A.lse;
+  if (launch_attention(L, s, err, n)) return 1;
+  const long long out_chunks = (long long)B * N * (d / 8);
+  hipLaunchKernelGGL(unpack_rows_kernel, dim3((unsigned)((out_chunks + 255) / 256)), dim3(256), 0, s,
+                     qp, static_cast<bf16*>(A.o), B, N, Np, d);
+  return check_launch("attention_fwd unpack", err, n);
+}
+
+int launch_attention_merge(int B, int N, int H, int dk, float* o_acc, float* lse_acc,
+                           const void* o_part, const float* lse_part, void* stream, char* err,
+                           size_t n) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const long long t = (long long)B * H * N;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((t + 255) / 256)), dim3(256), 0, s, o_acc,
+                     lse_acc, static_cast<const bf16*>(o_part), lse_part, B, N, H, dk);
+  return check_launch("attention_merge", err, n);
+}
+
+}  // namespace bpt

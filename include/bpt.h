@@ -236,6 +236,28 @@ bpt_status_t bpt_layer_fwd_host(const bpt_layer_desc_t* desc, const void* X,
                                 const bpt_layer_weights_t* weights, void* Z, void* workspace,
                                 size_t workspace_bytes, int32_t n_threads);
 
+/* One device's share of Ring Attention ("Blockwise Parallel Transformer — BPT",
+ * section "BPT and Ring Attention": each device keeps its query shard while the
+ * key/value shards travel around a ring). A step is the attention of the local
+ * query shard against one arrived key/value shard of the same length N:
+ * desc->causal = 1 for the device's own shard, 0 for an earlier one (a later one
+ * is skipped). bpt_attention_fwd writes that step's normalised output O (bf16,
+ * [batch * N, d_model] row-major, heads concatenated) and its statistic lse
+ * ([batch, n_heads, N] fp32, as bpt_layer_fwd_lse); Q, K, V are bf16 row-major
+ * DEVICE buffers like bpt_attention_bwd's. bpt_attention_merge folds one step into
+ * the running state (O_acc fp32 [batch * N, d_model], lse_acc [batch, n_heads, N],
+ * which start at 0 and -inf): lse = ln(e^lse_acc + e^lse_part), O_acc =
+ * e^(lse_acc - lse) O_acc + e^(lse_part - lse) O_part; after every shard it holds
+ * the attention of the query shard over the whole sequence. Errors and
+ * asynchrony as for every entry point; the workspace holds packed copies of Q, K
+ * and V ([batch * Np, d_model] bf16 each, Np = N rounded up to 128). */
+size_t bpt_attention_fwd_workspace_bytes(const bpt_attn_desc_t* desc);
+bpt_status_t bpt_attention_fwd(const bpt_attn_desc_t* desc, const void* Q, const void* K,
+                               const void* V, void* O, float* lse, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
+bpt_status_t bpt_attention_merge(const bpt_attn_desc_t* desc, float* O_acc, float* lse_acc,
+                                 const void* O_part, const float* lse_part, void* hip_stream);
+
 /* n_layers >= 1 layers applied in turn, all with the shape of *desc; layers is
  * a HOST array of n_layers weight sets (each holding device pointers). Layer 0
  * reads X in desc->dtype; the residual stream between layers is fp32; the last

@@ -26,6 +26,18 @@ int launch_attention_bwd(const AttnBwdLaunch& L, void*, char*, size_t) {
   ++g_bwd_launches;
   return 0;
 }
+static int g_fwd_launches = 0, g_merge_launches = 0;
+static AttnFwdLaunch g_fwd;
+int launch_attention_fwd(const AttnFwdLaunch& L, void*, char*, size_t) {
+  g_fwd = L;
+  ++g_fwd_launches;
+  return 0;
+}
+int launch_attention_merge(int, int, int, int, float*, float*, const void*, const float*, void*, char*,
+                           size_t) {
+  ++g_merge_launches;
+  return 0;
+}
 }  // namespace bpt
 
 static int g_fail = 0;
@@ -188,6 +200,33 @@ int main() {
   EXPECT(bpt_attention_bwd(&ab, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                            nullptr, nullptr, 0, nullptr) == BPT_OK);
   EXPECT(bpt::g_bwd_launches == 0);
+  // ring attention step and merge: carving and validation
+  {
+    bpt_attn_desc_t r = {2, 200, 256, 2, 1, BPT_BF16};
+    const size_t need = bpt_attention_fwd_workspace_bytes(&r);
+    EXPECT(need == 3 * (size_t)2 * 256 * 256 * 2);
+    char* fb = fake(10ull << 36);
+    const size_t io = (size_t)400 * 256 * 2;
+    float* lse_r = reinterpret_cast<float*>(fake(11ull << 36));
+    char* wsr = fake(12ull << 36);
+    EXPECT(bpt_attention_fwd(&r, fb, fb + io, fb + 2 * io, fb + 3 * io, lse_r, wsr, need, nullptr) == BPT_OK);
+    EXPECT(bpt::g_fwd_launches == 1 && bpt::g_fwd.seq_pad == 256 && bpt::g_fwd.d_head == 128);
+    EXPECT((char*)bpt::g_fwd.packed[2] == wsr + 2 * (need / 3) && bpt::g_fwd.o == fb + 3 * io);
+    EXPECT(bpt_attention_fwd(&r, fb, fb + io, fb + 2 * io, fb + 3 * io, lse_r, wsr, need - 1, nullptr) ==
+           BPT_ERR_WORKSPACE);
+    EXPECT(bpt_attention_fwd(&r, fb, fb + io, fb + 2 * io, fb + 2 * io + 512, lse_r, wsr, need, nullptr) ==
+           BPT_ERR_ALIAS);
+    EXPECT(bpt_attention_fwd(&r, fb, fb + io, fb + 2 * io, fb + 3 * io, lse_r + 1, wsr, need, nullptr) ==
+           BPT_ERR_ALIGN);
+    EXPECT(bpt_attention_fwd(&r, nullptr, fb + io, fb + 2 * io, fb + 3 * io, lse_r, wsr, need, nullptr) ==
+           BPT_ERR_NULL);
+    float* oacc = reinterpret_cast<float*>(fake(13ull << 36));
+    float* lacc = reinterpret_cast<float*>(fake(14ull << 36));
+    EXPECT(bpt_attention_merge(&r, oacc, lacc, fb + 3 * io, lse_r, nullptr) == BPT_OK);
+    EXPECT(bpt_attention_merge(&r, oacc, lse_r, fb + 3 * io, lse_r, nullptr) == BPT_ERR_ALIAS);
+    EXPECT(bpt_attention_merge(&r, nullptr, lacc, fb + 3 * io, lse_r, nullptr) == BPT_ERR_NULL);
+    EXPECT(bpt::g_merge_launches == 1);
+  }
   // the host layer runs for real here: small fp32 layer, window mask, grouped heads
   {
     bpt_layer_desc_t hd{};
