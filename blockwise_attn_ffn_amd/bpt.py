@@ -38,7 +38,9 @@ class LayerDesc(ctypes.Structure):
 class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
-                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -193,9 +195,10 @@ def layer_fwd_lse(desc: LayerDesc, x, layer: dict, z, lse, workspace, stream=Non
                                    _ptr(z), _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
 
 
-def make_attn_desc(*, batch, seq_len, d_model, n_heads, causal, dtype="bf16") -> AttnDesc:
+def make_attn_desc(*, batch, seq_len, d_model, n_heads, causal, dtype="bf16", window=0, chunk=0,
+                   n_kv_heads=0) -> AttnDesc:
     code = dtype if isinstance(dtype, int) else {"f32": F32, "bf16": BF16}[dtype]
-    return AttnDesc(batch, seq_len, d_model, n_heads, int(causal), code)
+    return AttnDesc(batch, seq_len, d_model, n_heads, int(causal), code, window, chunk, n_kv_heads)
 
 
 def attention_bwd_workspace_bytes(desc: AttnDesc) -> int:

@@ -255,8 +255,17 @@ bpt_status_t validate_attn_desc(const bpt_attn_desc_t* d) {
   const size_t np = round_up((size_t)d->seq_len, 128);
   if ((size_t)d->batch * np * (size_t)d->d_model >= ((size_t)1 << 31))
     return fail(BPT_ERR_SHAPE, "batch * seq_len * d_model exceeds the 31-bit element index range");
+  if (d->window < 0 || d->chunk < 0) return fail(BPT_ERR_SHAPE, "window and chunk must be >= 0");
+  if ((d->window || d->chunk) && !d->causal)
+    return fail(BPT_ERR_SHAPE, "window and chunk apply to the causal mask only");
+  if (d->window && d->chunk) return fail(BPT_ERR_SHAPE, "window and chunk cannot be combined");
+  if (d->n_kv_heads < 0 || (d->n_kv_heads && d->n_heads % d->n_kv_heads != 0))
+    return fail(BPT_ERR_SHAPE, "n_kv_heads %d must be 0 or divide n_heads %d", d->n_kv_heads,
+                d->n_heads);
   return BPT_OK;
 }
+
+int attn_kv_heads(const bpt_attn_desc_t* d) { return d->n_kv_heads ? d->n_kv_heads : d->n_heads; }
 
 // The two row statistics first, then the transposed copies, each on a 256-byte boundary.
 size_t attn_bwd_layout(const bpt_attn_desc_t* d, size_t* stat_bytes, size_t* packed_bytes) {
@@ -386,10 +395,12 @@ bpt_status_t bpt_attention_bwd_profiled(const bpt_attn_desc_t* desc, const void*
   if (workspace_bytes < need)
     return fail(BPT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   const size_t rows = (size_t)desc->batch * desc->seq_len;
+  const size_t dkv = (size_t)attn_kv_heads(desc) * (desc->d_model / desc->n_heads);
   const size_t in_b = rows * desc->d_model * 2, out_b = rows * desc->d_model * sizeof(float);
+  const size_t kv_b = rows * dkv * 2, dkv_b = rows * dkv * sizeof(float);
   const size_t lse_b = rows * desc->n_heads * sizeof(float);
   // outputs and workspace against every other buffer
-  const size_t sizes[] = {in_b, in_b, in_b, in_b, in_b, lse_b, out_b, out_b, out_b, need};
+  const size_t sizes[] = {in_b, kv_b, kv_b, in_b, in_b, lse_b, out_b, dkv_b, dkv_b, need};
   for (int i = 6; i < 10; ++i)
     for (int j = 0; j < 10; ++j)
       if (j != i && overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
@@ -401,6 +412,9 @@ bpt_status_t bpt_attention_bwd_profiled(const bpt_attn_desc_t* desc, const void*
   p.n_heads = desc->n_heads;
   p.d_head = desc->d_model / desc->n_heads;
   p.causal = desc->causal;
+  p.n_kv_heads = attn_kv_heads(desc);
+  p.window = desc->window;
+  p.chunk = desc->chunk;
   p.seq_pad = (int)round_up((size_t)desc->seq_len, 128);
   p.q = Q;
   p.k = K;
@@ -434,6 +448,8 @@ bpt_status_t bpt_attention_fwd(const bpt_attn_desc_t* desc, const void* Q, const
   g_err[0] = 0;
   bpt_status_t st = validate_attn_desc(desc);
   if (st != BPT_OK) return st;
+  if (desc->window || desc->chunk || attn_kv_heads(desc) != desc->n_heads)
+    return fail(BPT_ERR_UNSUPPORTED, "a ring step takes no window, chunk or grouped heads");
   if (attn_empty(desc)) return BPT_OK;
   const void* ptrs[] = {Q, K, V, O, lse, workspace};
   const char* names[] = {"Q", "K", "V", "O", "lse", "workspace"};

@@ -80,6 +80,7 @@ inline size_t hidden_block_rows(int d_model, size_t rows_pad) {
 constexpr int kAttnBwdPacked = 3;
 struct AttnBwdLaunch {
   int batch, seq_len, d_model, n_heads, d_head, causal;
+  int n_kv_heads, window, chunk;   // grouped key/value heads (K, V, dK, dV: n_kv_heads * d_head wide), masks
   int seq_pad;              // seq_len rounded up to 128
   const void *q, *k, *v, *out, *dout;   // bf16 [batch * seq_len, d_model]
   const float* lse;         // [batch, n_heads, seq_len]

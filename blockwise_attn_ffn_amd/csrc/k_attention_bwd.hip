@@ -78,8 +78,25 @@ struct BwdArgs {
   const float *L2, *Dp;                           // [B H, Np]
   float *dq, *dk, *dv;                            // [B N, d] row-major
   int B, N, Np, H, d, causal;
+  int G, dkv, window, chunk;                      // key/value heads, their width, masks
   float scale_log2e, scale;                       // log2(e) / sqrt(d_k), 1 / sqrt(d_k)
 };
+
+// Visible keys [lo, hi] of query position p (the forward's masks; p past the end
+// behaves as the last row). GENERAL instances only; the others are plain causal /
+// unmasked with one key/value head per query head.
+template <bool GENERAL>
+__device__ inline int bwd_key_hi(const BwdArgs& g, int p) {
+  const int pc = min(p, g.N - 1);
+  if (!g.causal) return g.N - 1;
+  if constexpr (GENERAL) return g.chunk ? min((pc / g.chunk + 1) * g.chunk, g.N) - 1 : pc;
+  return pc;
+}
+template <bool GENERAL>
+__device__ inline int bwd_key_lo(const BwdArgs& g, int p) {
+  if constexpr (GENERAL) return g.window ? max(0, min(p, g.N - 1) - g.window + 1) : 0;
+  return 0;
+}
 
 // Lane's fragment of a B operand over token rows from row-major X: row `pos`
 // (zero past N), features f0 + [0, 8).
@@ -92,7 +109,7 @@ __device__ inline bf16x8 ld_row_frag(const bf16* X, int b, int pos, int N, int d
 // lane per query row. Key/value blocks of 64 keys are copied into LDS (K and V as A
 // fragments over keys, straight from the row-major inputs; K^T as A fragments over
 // features from the transposed copy), two stages shared by all NW waves.
-template <int DK, int NW>
+template <int DK, int NW, bool GENERAL>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
   using O = Op<bf16>;
   using F = O::frag;
@@ -112,9 +129,14 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
   const int nqb = (N + BQ - 1) / BQ;
   const int bh = blockIdx.x / nqb, qb = nqb - 1 - (int)(blockIdx.x - bh * nqb);   // longest first
   const int b = bh / H, h = bh - b * H;
-  const int kend = g.causal ? (min(qb * BQ + BQ, N) - 1) / BKV + 1 : (N + BKV - 1) / BKV;
+  const int gk = GENERAL ? h / (H / g.G) : h;   // key/value head read by this query head
+  const int bg = GENERAL ? b * g.G + gk : bh;
+  const int dkv = GENERAL ? g.dkv : d;
+  const int kbeg = bwd_key_lo<GENERAL>(g, qb * BQ) / BKV;
+  const int kend = bwd_key_hi<GENERAL>(g, qb * BQ + BQ - 1) / BKV + 1;
   const int wave_q_first = qb * BQ + wave * 32, qpos = wave_q_first + rho;
   const int fcol = h * DK + 8 * hf;             // this lane's feature offset in a row
+  const int fkv = gk * DK + 8 * hf;             // the same in a K / V row
   const int prho = pi_row(rho);
   static_assert(KSD % NW == 0 && NW % KK == 0, "copy slots");
 
@@ -125,10 +147,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
     const int kv0 = kb * BKV;
     size_t rowoff[KT];                            // this lane's key row in each 32-key tile
 #pragma unroll
-    for (int t = 0; t < KT; ++t) rowoff[t] = ((size_t)b * N + min(kv0 + t * 32 + prho, N - 1)) * d + fcol;
+    for (int t = 0; t < KT; ++t) rowoff[t] = ((size_t)b * N + min(kv0 + t * 32 + prho, N - 1)) * dkv + fkv;
     // K^T fragment (dt, k-step) = (slot / KK, slot % KK); the wave adds (w / KK, w % KK)
     const bf16* kt_base =
-        g.kT + (((size_t)bh * DT + wave / KK) * (Np / 16) + kv0 / 16 + wave % KK) * kFragElems + lane * 8;
+        g.kT + (((size_t)bg * DT + wave / KK) * (Np / 16) + kv0 / 16 + wave % KK) * kFragElems + lane * 8;
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
       const int f0 = NW * q;
@@ -161,12 +183,16 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
 
   auto visit = [&](int kb, const unsigned char* buf) __attribute__((always_inline)) {
     const int kv0 = kb * BKV;
-    if (g.causal && kv0 > wave_q_first + 31) return;   // every key of the block is later
-    const bool need_mask = (g.causal && kv0 + BKV - 1 > wave_q_first) || kv0 + BKV > N;
+    // no row of the wave sees a key of the block
+    if (kv0 > bwd_key_hi<GENERAL>(g, wave_q_first + 31)) return;
+    if (GENERAL && kv0 + BKV - 1 < bwd_key_lo<GENERAL>(g, wave_q_first)) return;
+    const bool need_mask = kv0 + BKV - 1 > bwd_key_hi<GENERAL>(g, wave_q_first) ||
+                           (GENERAL && kv0 < bwd_key_lo<GENERAL>(g, wave_q_first + 31));
     f32x16 s[KT], dp[KT];
     F dsf[KK];
     // register i of tile t holds key kv0 + t*32 + (i&8)*2 + 8hf + (i&7)
-    const int lim = (g.causal ? min(qpos, N - 1) : N - 1) - kv0 - 8 * hf;
+    const int lim = bwd_key_hi<GENERAL>(g, qpos) - kv0 - 8 * hf;
+    const int lim_lo = bwd_key_lo<GENERAL>(g, qpos) - kv0 - 8 * hf;
     auto softmax_grad = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
@@ -177,7 +203,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
           for (int e = 0; e < 8; ++e) {
             const int i = 8 * gg + e;
             float p = fast_exp2(fmaf(s[t][i], g.scale_log2e, -l2));
-            if (decltype(masked)::value && t * 32 + (i & 8) * 2 + (i & 7) > lim) p = 0.f;
+            const int off = t * 32 + (i & 8) * 2 + (i & 7);
+            if (decltype(masked)::value && (off > lim || (GENERAL && off < lim_lo))) p = 0.f;
             v[e] = p * (dp[t][i] - Dq);
           }
           dsf[2 * t + gg] = O::from_f32(v);
@@ -209,8 +236,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
     body(RuntimeTag{});
   };
 
-  issue(0, lds0);
-  for (int kb = 0; kb < kend; kb += 2) {
+  issue(kbeg, lds0);
+  for (int kb = kbeg; kb < kend; kb += 2) {
     wait_vmem();
     __syncthreads();                     // stage 0 landed; stage 1 is free
     if (kb + 1 < kend) issue(kb + 1, lds1);
@@ -240,7 +267,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
 // per key. Query blocks of BQS rows are copied into LDS (Q and dO as A fragments
 // over queries from the row-major inputs, Q^T and dO^T from the transposed copies,
 // and the rows' statistics), two stages shared by all NW waves.
-template <int DK, int NW, int BQS>
+template <int DK, int NW, int BQS, bool GENERAL>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
   using O = Op<bf16>;
   using F = O::frag;
@@ -259,19 +286,34 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
   const int rho = lane & 31, hf = lane >> 5;
   const int N = g.N, Np = g.Np, H = g.H, d = g.d;
   const int nkb = (N + BK - 1) / BK;
-  const int bh = blockIdx.x / nkb, kbk = blockIdx.x - bh * nkb;   // longest first under the mask
-  const int b = bh / H, h = bh - b * H;
+  // workgroup: (sequence, key/value head, key block); with grouped heads it sums
+  // over the query heads of its group (GS of them), one run of query stages each
+  const int G = GENERAL ? g.G : H, GS = GENERAL ? H / g.G : 1, dkv = GENERAL ? g.dkv : d;
+  const int bg = blockIdx.x / nkb, kbk = blockIdx.x - bg * nkb;   // longest first under the mask
+  const int b = bg / G, gk = bg - b * G;
   const int wave_k_first = kbk * BK + wave * 32, kpos = wave_k_first + rho;
   const int nqs = (N + BQS - 1) / BQS;
-  const int qs_begin = g.causal ? (kbk * BK) / BQS : 0;
-  const int fcol = h * DK + 8 * hf;
+  // query stages that can see a key of the block: from the first query whose
+  // visible range reaches the block's first key to the last one reaching its last
+  int qs_begin = 0, qs_end = nqs;
+  if (g.causal) {
+    const int k0 = kbk * BK, k1 = min(k0 + BK, N) - 1;
+    int q_first = k0;                                        // causal: q >= k
+    if (GENERAL && g.chunk) q_first = k0 / g.chunk * g.chunk;   // the key's whole chunk
+    qs_begin = q_first / BQS;
+    if (GENERAL && g.window) qs_end = min(nqs, (k1 + g.window - 1) / BQS + 1);
+  }
+  const int nst = qs_end - qs_begin, n_it = GS * nst;
+  const int fkv = gk * DK + 8 * hf;
   const int prho = pi_row(rho);
   static_assert(KSD % NW == 0 && NW % QK == 0, "copy slots");
 
   // Copy slot q of wave w moves fragment NW q + w of the stage (the kind of copy is
   // the same in every wave); wave 0 also copies the BQS rows' statistics.
-  auto issue = [&](int qs, unsigned char* buf) __attribute__((always_inline)) {
-    const int q0 = qs * BQS;
+  auto issue = [&](int it, unsigned char* buf) __attribute__((always_inline)) {
+    const int hq = GENERAL ? gk * GS + it / nst : gk;
+    const int q0 = (qs_begin + (GENERAL ? it % nst : it)) * BQS;
+    const int bh = b * H + hq, fcol = hq * DK + 8 * hf;
     size_t rowoff[QT];                            // this lane's query row in each 32-row tile
 #pragma unroll
     for (int t = 0; t < QT; ++t) rowoff[t] = ((size_t)b * N + min(q0 + t * 32 + prho, N - 1)) * d + fcol;
@@ -304,17 +346,20 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
   F kf[KSD], vf[KSD];
 #pragma unroll
   for (int kk = 0; kk < KSD; ++kk) {
-    kf[kk] = ld_row_frag(g.k, b, kpos, N, d, fcol + kk * 16);
-    vf[kk] = ld_row_frag(g.v, b, kpos, N, d, fcol + kk * 16);
+    kf[kk] = ld_row_frag(g.k, b, kpos, N, dkv, fkv + kk * 16);
+    vf[kk] = ld_row_frag(g.v, b, kpos, N, dkv, fkv + kk * 16);
   }
   f32x16 dkacc[DT], dvacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) { dkacc[t] = f32x16{}; dvacc[t] = f32x16{}; }
 
-  auto visit = [&](int qs, const unsigned char* buf) __attribute__((always_inline)) {
-    const int q0 = qs * BQS;
-    if (g.causal && wave_k_first > q0 + BQS - 1) return;   // every query of the block is earlier
-    const bool need_mask = g.causal && wave_k_first + 31 > q0;
+  auto visit = [&](int it, const unsigned char* buf) __attribute__((always_inline)) {
+    const int q0 = (qs_begin + (GENERAL ? it % nst : it)) * BQS;
+    // no query of the stage sees a key of the wave
+    if (wave_k_first > bwd_key_hi<GENERAL>(g, q0 + BQS - 1)) return;
+    if (GENERAL && wave_k_first + 31 < bwd_key_lo<GENERAL>(g, q0)) return;
+    const bool need_mask = wave_k_first + 31 > bwd_key_hi<GENERAL>(g, q0) ||
+                           (GENERAL && wave_k_first < bwd_key_lo<GENERAL>(g, q0 + BQS - 1));
     f32x16 s[QT], dp[QT];
     F pf[QK], dsf[QK];
     // register i of tile t holds query q0 + t*32 + (i&8)*2 + 8hf + (i&7); lane holds key kpos
@@ -335,7 +380,12 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float p = fast_exp2(fmaf(s[t][8 * gg + e], g.scale_log2e, -l8[e]));
-            if (decltype(masked)::value && kpos > q0 + qoff + e) p = 0.f;
+            if constexpr (decltype(masked)::value) {
+              const int qq = q0 + qoff + e;
+              if (GENERAL ? (kpos > bwd_key_hi<true>(g, qq) || kpos < bwd_key_lo<true>(g, qq))
+                          : (g.causal && kpos > qq))
+                p = 0.f;
+            }
             pv[e] = p;
             dv8[e] = p * (dp[t][8 * gg + e] - d8[e]);
           }
@@ -372,22 +422,22 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
     body(RuntimeTag{});
   };
 
-  issue(qs_begin, lds0);
-  for (int qs = qs_begin; qs < nqs; qs += 2) {
+  if (n_it > 0) issue(0, lds0);
+  for (int it = 0; it < n_it; it += 2) {
     wait_vmem();
     __syncthreads();
-    if (qs + 1 < nqs) issue(qs + 1, lds1);
-    visit(qs, lds0);
-    if (qs + 1 >= nqs) break;
+    if (it + 1 < n_it) issue(it + 1, lds1);
+    visit(it, lds0);
+    if (it + 1 >= n_it) break;
     wait_vmem();
     __syncthreads();
-    if (qs + 2 < nqs) issue(qs + 2, lds0);
-    visit(qs + 1, lds1);
+    if (it + 2 < n_it) issue(it + 2, lds0);
+    visit(it + 1, lds1);
   }
   // register group gg of feature tile t holds features t*32 + 16gg + 8hf + [0, 8)
   if (kpos < N) {
-    float* ok = g.dk + ((size_t)b * N + kpos) * d + (size_t)h * DK;
-    float* ov = g.dv + ((size_t)b * N + kpos) * d + (size_t)h * DK;
+    float* ok = g.dk + ((size_t)b * N + kpos) * dkv + (size_t)gk * DK;
+    float* ov = g.dv + ((size_t)b * N + kpos) * dkv + (size_t)gk * DK;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -445,6 +495,10 @@ int run_bwd(const AttnBwdLaunch& L, hipStream_t s, char* err, size_t n) {
   g.H = L.n_heads;
   g.d = L.d_model;
   g.causal = L.causal;
+  g.G = L.n_kv_heads;
+  g.dkv = L.n_kv_heads * DK;
+  g.window = L.window;
+  g.chunk = L.chunk;
   g.scale = 1.0f / sqrtf((float)DK);
   g.scale_log2e = kLog2e * g.scale;
   const int bhs = L.batch * L.n_heads;
@@ -454,9 +508,14 @@ int run_bwd(const AttnBwdLaunch& L, hipStream_t s, char* err, size_t n) {
                      g.dout, static_cast<const bf16*>(L.out), L.lse, L.stat_d, L.stat_l2, L.batch,
                      L.seq_len, L.seq_pad, L.n_heads);
   if (check_launch("bwd_stats", err, n) || mark(L, 1, s, err, n)) return 1;
-  TransposeJob job{{g.k, g.q, g.dout}, {kT, qT, doT}};
-  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(bhs * (L.seq_pad / 64) * (DK / 64)), 3),
+  // Q^T, dO^T per (sequence, query head); K^T per (sequence, key/value head)
+  TransposeJob job{{g.q, g.dout, nullptr}, {qT, doT, nullptr}};
+  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(bhs * (L.seq_pad / 64) * (DK / 64)), 2),
                      dim3(256), 0, s, job, L.seq_len, L.seq_pad, L.n_heads, DK);
+  TransposeJob kjob{{g.k, nullptr, nullptr}, {kT, nullptr, nullptr}};
+  const int bgs = L.batch * L.n_kv_heads;
+  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(bgs * (L.seq_pad / 64) * (DK / 64)), 1),
+                     dim3(256), 0, s, kjob, L.seq_len, L.seq_pad, L.n_kv_heads, DK);
   if (check_launch("bwd_transpose", err, n) || mark(L, 2, s, err, n)) return 1;
   // d_k 128: 8 waves share each key/value stage (two per SIMD, 256 query rows);
   // d_k 64: 4 waves, and two workgroups fit one compute unit
@@ -466,9 +525,13 @@ int run_bwd(const AttnBwdLaunch& L, hipStream_t s, char* err, size_t n) {
   constexpr int DKW = 4, DKQ = 64;
   const int nqb = (L.seq_len + 32 * DQW - 1) / (32 * DQW);
   const int nkb = (L.seq_len + 32 * DKW - 1) / (32 * DKW);
-  hipLaunchKernelGGL((bwd_dq_kernel<DK, DQW>), dim3(bhs * nqb), dim3(64 * DQW), 0, s, g);
+  // masks or grouped key/value heads run the general instances
+  const bool general = L.window || L.chunk || L.n_kv_heads != L.n_heads;
+  auto kdq = general ? bwd_dq_kernel<DK, DQW, true> : bwd_dq_kernel<DK, DQW, false>;
+  auto kdkv = general ? bwd_dkv_kernel<DK, DKW, DKQ, true> : bwd_dkv_kernel<DK, DKW, DKQ, false>;
+  hipLaunchKernelGGL(kdq, dim3(bhs * nqb), dim3(64 * DQW), 0, s, g);
   if (check_launch("bwd_dq", err, n) || mark(L, 3, s, err, n)) return 1;
-  hipLaunchKernelGGL((bwd_dkv_kernel<DK, DKW, DKQ>), dim3(bhs * nkb), dim3(64 * DKW), 0, s, g);
+  hipLaunchKernelGGL(kdkv, dim3(bgs * nkb), dim3(64 * DKW), 0, s, g);
   return check_launch("bwd_dkv", err, n) || mark(L, 4, s, err, n);
 }
 

@@ -174,9 +174,15 @@ typedef struct {
   int32_t n_heads;    /* d_head = d_model / n_heads: 64 or 128                   */
   int32_t causal;     /* 1: key j visible to query p iff j <= p; 0: no mask      */
   int32_t dtype;      /* of Q, K, V, O and dO: BPT_BF16 (the only value)         */
+  int32_t window;     /* as bpt_layer_desc_t (causal only; bpt_attention_bwd)     */
+  int32_t chunk;      /* as bpt_layer_desc_t (causal only; bpt_attention_bwd)     */
+  int32_t n_kv_heads; /* as bpt_layer_desc_t (bpt_attention_bwd): K, V, dK and dV
+                         are then [batch * seq_len, n_kv_heads * d_head]        */
 } bpt_attn_desc_t;
 
-/* Bytes of workspace bpt_attention_bwd needs (0 for an empty call, or 0 with
+/* (bpt_attention_fwd and bpt_attention_merge take window = chunk = 0 and
+ * n_kv_heads 0 or n_heads.)
+ * Bytes of workspace bpt_attention_bwd needs (0 for an empty call, or 0 with
  * bpt_last_error() set when desc is invalid): two fp32 row statistics [batch,
  * n_heads, Np] (D = rowsum(dO * O) and lse in base 2), with Np = seq_len rounded
  * up to 128, and transposed bf16 copies of K, Q and dO, each [batch * Np,

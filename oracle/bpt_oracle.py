@@ -257,102 +257,118 @@ def layer_lse_rows(x: np.ndarray, p: dict, rows: np.ndarray, *, seq_len: int, n_
 
 
 def attention_backward_sequence(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
-                                n_heads: int, causal: bool):
+                                n_heads: int, causal: bool, window: int = 0, chunk: int = 0):
     """Gradients of one sequence's attention output A (attention_sequence) with
     respect to Q, K and V, given dA = do. Per head, with S = Q_h K_h^T / sqrt(d_k)
-    (masked as in the forward) and P = softmax(S) by rows:
+    (masked as in the forward: `visible`) and P = softmax(S) by rows:
         dV_h = P^T dO_h
         dP   = dO_h V_h^T
         dS   = P * (dP - rowsum(P * dP))      (the softmax's Jacobian, row by row)
         dQ_h = dS K_h / sqrt(d_k),   dK_h = dS^T Q_h / sqrt(d_k)
+    With g key/value heads (grouped-query attention, g read from the widths), a
+    key/value head's dK and dV sum those of the query heads that read it.
     This is the attention part of the backward pass the saved statistics serve
     ([BPT] "The backward pass": each block recomputes s and the attention output
     from the saved (m, l) and accumulates gradients); the plain definition here
     builds the whole P. rowsum(P * dP) equals rowsum(dO * A), the form a block
-    recomputation uses. Returns (dq, dk, dv), each [n, d].
+    recomputation uses. Returns (dq [n, d], dk, dv [n, g d_k]).
     """
     q, k, v, do = (np.asarray(a, F64) for a in (q, k, v, do))
     n, d = q.shape
-    assert k.shape[1] == d, "the backward takes one key/value head per query head"
     dk_ = d // n_heads
+    group = _group_size(q, k, n_heads)
     scale = 1.0 / math.sqrt(dk_)
     dq = np.empty_like(q)
-    dkk = np.empty_like(k)
-    dv = np.empty_like(v)
-    hidden = np.arange(n)[None, :] > np.arange(n)[:, None] if causal else None
+    dkk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    hidden = ~visible(np.arange(n), np.arange(n), causal, window, chunk) if causal else None
     for h in range(n_heads):
         c = slice(h * dk_, (h + 1) * dk_)
-        s = (q[:, c] @ k[:, c].T) * scale
+        kv = slice((h // group) * dk_, (h // group + 1) * dk_)
+        s = (q[:, c] @ k[:, kv].T) * scale
         if causal:
             s = np.where(hidden, -np.inf, s)
         pm = softmax_rows(s)
-        dv[:, c] = pm.T @ do[:, c]
-        dp = do[:, c] @ v[:, c].T
+        dv[:, kv] += pm.T @ do[:, c]
+        dp = do[:, c] @ v[:, kv].T
         ds = pm * (dp - (pm * dp).sum(axis=1, keepdims=True))
-        dq[:, c] = ds @ k[:, c] * scale
-        dkk[:, c] = ds.T @ q[:, c] * scale
+        dq[:, c] = ds @ k[:, kv] * scale
+        dkk[:, kv] += ds.T @ q[:, c] * scale
     return dq, dkk, dv
 
 
+def _row_keys(p: int, nk_all: int, causal: bool, window: int, chunk: int) -> np.ndarray:
+    """Positions of the keys query p sees (within the first nk_all keys)."""
+    keys = np.arange(nk_all)
+    return keys[visible(np.array([p]), keys, causal, window, chunk)[0]]
+
+
 def attention_backward_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
-                               n_heads: int, causal: bool, rows: np.ndarray) -> np.ndarray:
+                               n_heads: int, causal: bool, rows: np.ndarray, window: int = 0,
+                               chunk: int = 0) -> np.ndarray:
     """dQ of attention_backward_sequence at the given query rows only (a row's dQ
     needs its own row of P and dP, i.e. every key it sees): [len(rows), d]."""
     q, k, v, do = (np.asarray(a, F64) for a in (q, k, v, do))
     rows = np.asarray(rows, dtype=np.int64)
     d = q.shape[1]
     dk_ = d // n_heads
+    group = _group_size(q, k, n_heads)
     scale = 1.0 / math.sqrt(dk_)
     out = np.empty((rows.size, d), F64)
     for r_i, r in enumerate(rows):
-        nk = r + 1 if causal else k.shape[0]
+        keys = _row_keys(int(r), k.shape[0], causal, window, chunk)
         for h in range(n_heads):
             c = slice(h * dk_, (h + 1) * dk_)
-            s = (k[:nk, c] @ q[r, c]) * scale
+            kv = slice((h // group) * dk_, (h // group + 1) * dk_)
+            s = (k[keys, kv] @ q[r, c]) * scale
             pm = np.exp(s - s.max())
             pm /= pm.sum()
-            dp = v[:nk, c] @ do[r, c]
+            dp = v[keys, kv] @ do[r, c]
             ds = pm * (dp - (pm * dp).sum())
-            out[r_i, c] = ds @ k[:nk, c] * scale
+            out[r_i, c] = ds @ k[keys, kv] * scale
     return out
 
 
-
 def attention_backward_kv_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
-                               n_heads: int, causal: bool, rows: np.ndarray):
+                               n_heads: int, causal: bool, rows: np.ndarray, window: int = 0,
+                               chunk: int = 0):
     """dK and dV of attention_backward_sequence at the given key rows only:
-    (dk [len(rows), d], dv [len(rows), d]).
+    (dk, dv), each [len(rows), width of K].
 
-    Key j's gradients sum over the queries p that see it: dV_j = sum_p P[p, j] dO_p
-    and dK_j = sum_p dS[p, j] Q_p / sqrt(d_k), where P[p, :] is query p's whole
-    softmax row (every key it sees) and dS[p, j] = P[p, j] (dO_p . V_j - dO_p . A_p).
+    Key j's gradients sum over the queries p that see it (and, with grouped heads,
+    over the query heads of its group): dV_j = sum_p P[p, j] dO_p and dK_j =
+    sum_p dS[p, j] Q_p / sqrt(d_k), where P[p, :] is query p's whole softmax row
+    (every key it sees) and dS[p, j] = P[p, j] (dO_p . V_j - dO_p . A_p).
     A query whose dO row is zero has dS[p, :] = 0 and P[p, :] dO_p = 0, so it adds
     nothing and is skipped: with dO nonzero on a few rows only, the cost is those
     rows times the sequence length.
     """
     q, k, v, do = (np.asarray(a, F64) for a in (q, k, v, do))
     rows = np.asarray(rows, dtype=np.int64)
-    n, d = q.shape
+    d = q.shape[1]
     dk_ = d // n_heads
+    group = _group_size(q, k, n_heads)
     scale = 1.0 / math.sqrt(dk_)
-    dk_out = np.zeros((rows.size, d), F64)
-    dv_out = np.zeros((rows.size, d), F64)
+    dk_out = np.zeros((rows.size, k.shape[1]), F64)
+    dv_out = np.zeros((rows.size, v.shape[1]), F64)
     live = np.flatnonzero(np.any(do != 0.0, axis=1))
     for p in live:
-        nk = p + 1 if causal else k.shape[0]
-        seen = rows < nk                      # the requested keys query p sees
+        keys = _row_keys(int(p), k.shape[0], causal, window, chunk)
+        pos_in = {int(j): i for i, j in enumerate(keys)}
+        seen = np.array([int(r) in pos_in for r in rows])   # the requested keys query p sees
         if not np.any(seen):
             continue
+        idx = np.array([pos_in[int(r)] for r in rows[seen]])
         for h in range(n_heads):
             c = slice(h * dk_, (h + 1) * dk_)
-            s = (k[:nk, c] @ q[p, c]) * scale
+            kv = slice((h // group) * dk_, (h // group + 1) * dk_)
+            s = (k[keys, kv] @ q[p, c]) * scale
             pm = np.exp(s - s.max())
             pm /= pm.sum()
-            dp = v[:nk, c] @ do[p, c]
+            dp = v[keys, kv] @ do[p, c]
             ds = pm * (dp - (pm * dp).sum())
-            r = rows[seen]
-            dv_out[seen, c] += pm[r, None] * do[p, c][None, :]
-            dk_out[seen, c] += ds[r, None] * q[p, c][None, :] * scale
+            dv_out[seen, kv] += pm[idx, None] * do[p, c][None, :]
+            dk_out[seen, kv] += ds[idx, None] * q[p, c][None, :] * scale
     return dk_out, dv_out
 
 # ---------------------------------------------------------------------------

@@ -166,3 +166,51 @@ def test_attention_bwd_long_context_shape():
     err = float((dv.double().sum(0) - want).abs().max())
     say(f"  sum_k dV - sum_q dO: max {err:.3e} (|sum dO| <= {float(want.abs().max()):.3g})")
     assert err < 2e-2 * max(1.0, float(want.abs().max()))
+
+
+VARIANTS = [
+    # batch, seq_len, d_model, n_heads, mask / heads
+    (2, 200, 256, 4, dict(window=37)),
+    (1, 300, 256, 2, dict(window=100)),              # d_k 128
+    (2, 257, 256, 4, dict(chunk=16)),
+    (1, 400, 256, 2, dict(chunk=100)),
+    (2, 200, 256, 4, dict(n_kv_heads=1)),
+    (1, 333, 512, 4, dict(n_kv_heads=2)),            # d_k 128
+    (2, 180, 256, 4, dict(n_kv_heads=2, window=50)),
+    (1, 300, 512, 4, dict(n_kv_heads=1, chunk=64)),
+]
+
+
+@pytest.mark.parametrize("case", VARIANTS, ids=lambda c: "b{}-n{}-d{}-h{}-".format(*c[:4]) +
+                         "-".join(f"{k}{v}" for k, v in c[4].items()))
+def test_attention_bwd_masks_and_grouped_heads(case):
+    batch, n, d, h, var = case
+    window, chunk, g = var.get("window", 0), var.get("chunk", 0), var.get("n_kv_heads", 0)
+    dkv = (g or h) * (d // h)
+    say(f"case {case}")
+    inp = synth.make_attention_inputs(batch, n, d, seed=17)
+    inp["k"] = inp["k"][:, :dkv].contiguous()
+    inp["v"] = inp["v"][:, :dkv].contiguous()
+    q, k, v = (synth.to_f64(inp[x]) for x in ("q", "k", "v"))
+    o = np.zeros((batch * n, d))
+    lse = np.zeros((batch, h, n))
+    for b in range(batch):
+        r = slice(b * n, (b + 1) * n)
+        o[r] = oracle.attention_sequence(q[r], k[r], v[r], h, True, window=window, chunk=chunk)
+        lse[b] = oracle.attention_lse_sequence(q[r], k[r], h, True, window=window, chunk=chunk)
+    desc = bpt.make_attn_desc(batch=batch, seq_len=n, d_model=d, n_heads=h, causal=True,
+                              window=window, chunk=chunk, n_kv_heads=g)
+    dev = {x: t.cuda() for x, t in inp.items()}
+    dq = torch.full((batch * n, d), float("nan"), device="cuda")
+    dk = torch.full((batch * n, dkv), float("nan"), device="cuda")
+    dv = torch.full((batch * n, dkv), float("nan"), device="cuda")
+    ws = bpt.alloc_workspace(bpt.attention_bwd_workspace_bytes(desc))
+    bpt.attention_bwd(desc, dev["q"], dev["k"], dev["v"], torch.from_numpy(o).to(torch.bfloat16).cuda(),
+                      dev["do"], torch.from_numpy(lse).float().cuda(), dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        r = slice(b * n, (b + 1) * n)
+        ref = oracle.attention_backward_sequence(q[r], k[r], v[r], synth.to_f64(inp["do"][r]), h, True,
+                                                 window=window, chunk=chunk)
+        for name, got, want in (("dQ", dq, ref[0]), ("dK", dk, ref[1]), ("dV", dv, ref[2])):
+            check(got.cpu()[r], want, f"{name} seq {b}")

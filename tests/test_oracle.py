@@ -787,3 +787,69 @@ def test_gqa_layer_blockwise_and_rows_equal_unfused(g, mask):
     lse = oracle.layer_lse(x, p, seq_len=seq, n_heads=h, causal=True, **mask)
     lse_r = oracle.layer_lse_rows(x, p, rows, seq_len=seq, n_heads=h, causal=True, **mask)
     assert np.max(np.abs(lse_r - lse[rows // seq, :, rows % seq])) < 1e-12
+
+
+
+def _bwd_pins_general(fn, mask, g):
+    """Central finite differences of sum(A * G) through attention_sequence (pinned on
+    its own) with a mask and g key/value heads."""
+    rng = np.random.default_rng(61)
+    n, h, dkh = 7, 4, 2
+    q = rng.standard_normal((n, h * dkh))
+    k, v = rng.standard_normal((n, g * dkh)), rng.standard_normal((n, g * dkh))
+    gg = rng.standard_normal((n, h * dkh))
+    loss = lambda q_, k_, v_: float((oracle.attention_sequence(q_, k_, v_, h, True, **mask) * gg).sum())  # noqa: E731
+    dq, dk, dv = fn(q, k, v, gg, h, True, **mask)
+    eps = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            a_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            a_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd[idx] = (loss(*a_p) - loss(*a_m)) / (2 * eps)
+        if np.max(np.abs(fd - grad)) > 1e-7:
+            return False
+    return True
+
+
+@pytest.mark.parametrize("mask,g", [(dict(window=3), 4), (dict(chunk=3), 4), ({}, 2), ({}, 1),
+                                    (dict(window=2), 2), (dict(chunk=2), 1)])
+def test_backward_with_masks_and_grouped_heads_pinned_by_finite_differences(mask, g):
+    assert _bwd_pins_general(oracle.attention_backward_sequence, mask, g)
+
+
+def test_backward_general_pins_catch_planted_mistakes():
+    base = oracle.attention_backward_sequence
+
+    def grouped_dk_not_summed(q, k, v, do, h, causal, **mask):
+        # dK of a key/value head taken from its first query head only
+        dq, dk, dv = base(q, k, v, do, h, causal, **mask)
+        g = k.shape[1] // (q.shape[1] // h)
+        dkh = q.shape[1] // h
+        first = np.concatenate([q[:, (hh * (h // g)) * dkh:(hh * (h // g) + 1) * dkh] for hh in range(g)], axis=1)
+        _, dk1, _ = base(first, k, v, do[:, :first.shape[1]], g, causal, **mask)
+        return dq, dk1, dv
+
+    def mask_ignored(q, k, v, do, h, causal, **mask):
+        return base(q, k, v, do, h, causal)
+
+    assert not _bwd_pins_general(grouped_dk_not_summed, {}, 2)
+    assert not _bwd_pins_general(mask_ignored, dict(window=3), 4)
+
+
+@pytest.mark.parametrize("mask,g", [(dict(window=5), 2), (dict(chunk=4), 1), ({}, 2)])
+def test_backward_rows_forms_equal_full_with_masks_and_groups(mask, g):
+    rng = np.random.default_rng(63)
+    n, h, dkh = 21, 4, 4
+    q = rng.standard_normal((n, h * dkh))
+    k, v = rng.standard_normal((n, g * dkh)), rng.standard_normal((n, g * dkh))
+    gg = rng.standard_normal((n, h * dkh))
+    gg[np.setdiff1d(np.arange(n), [3, 11, 20])] = 0.0
+    dq, dk, dv = oracle.attention_backward_sequence(q, k, v, gg, h, True, **mask)
+    rows = np.array([0, 3, 11, 19, 20])
+    assert np.max(np.abs(oracle.attention_backward_dq_rows(q, k, v, gg, h, True, rows, **mask) - dq[rows])) < 1e-12
+    rk, rv = oracle.attention_backward_kv_rows(q, k, v, gg, h, True, rows, **mask)
+    assert np.max(np.abs(rk - dk[rows])) < 1e-12 and np.max(np.abs(rv - dv[rows])) < 1e-12
