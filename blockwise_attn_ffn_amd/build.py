@@ -29,7 +29,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
 
 KERNEL_SOURCES = ["k_ln_qkv.hip", "k_gemm.hip", "k_attention.hip", "k_ffn.hip", "k_pack.hip",
-                  "k_attention_bwd.hip", "k_ring.hip", "bpt_launch.hip"]
+                  "k_attention_bwd.hip", "k_attention_bwd_dkv.hip", "k_ring.hip", "bpt_launch.hip"]
 HOST_SOURCES = ["bpt_api.cpp", "bpt_support.cpp", "bpt_host.cpp"]
 # Per-source extra flags. The attention backward keeps its matrix-core results in
 # ordinary VGPRs (they feed the softmax arithmetic at once); left to itself the
