@@ -9,11 +9,11 @@
 // inner-loop visit; the values are the same); y_i = x_i + (o/l) W_O,
 // h_i = act(LN(y_i) W_1), Z[i] = y_i + h_i W_2.
 //
-// One kernel, C^T = W A^T on packed fragments, 256 x 256 tiles, operands copied
-// global -> LDS by the LDS-DMA path into two static stages (the next k-tile in
-// flight while the current one is multiplied), the next k-step's fragments read
-// from LDS during the current k-step's products, XCD-contiguous grouped tile
-// order. The epilogue mode decides the output:
+// One kernel, C^T = W A^T on packed fragments, 256 x 256 tiles (bf16: 8 waves,
+// two per SIMD, each 128 features x 64 rows), operands copied global -> LDS by
+// the LDS-DMA path into two static stages (the next k-tile in flight while the
+// current one is multiplied), the next k-step's fragments read from LDS during
+// the current k-step's products, XCD-contiguous grouped tile order. The epilogue mode decides the output:
 //   kModeQKV:    Q (packed B fragments), K and V^T (the attention kernel's operands);
 //   kModeResidY: Y = X + O W_O, fp32 row-major over packed rows;
 //   kModeGeluH:  GELU(LN2(Y) W_1) for a block of rows, as packed B fragments;
@@ -55,12 +55,13 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // C^T[features, rows] = W[features, K] . A[rows, K]^T on packed operands: W in
 // plain fragment order (k_pack.hip), A as packed B fragments. Tile BN features x
-// BM rows; 4 waves in a 2 x 2 grid, each (BN/2) x (BM/2) as 32x32 tiles. A
-// k-tile is 4 k-steps. LDS stage = [W: BN/32 tiles][4 k-steps][fragment] then
+// BM rows; NW waves in a 2 x (NW/2) grid, each (BN/2) x (BM/(NW/2)) as 32x32
+// tiles (NW = 8: two waves per SIMD, so one wave's copy issue and barrier waits
+// are covered by the other's products). A k-tile is 4 k-steps. LDS stage = [W: BN/32 tiles][4 k-steps][fragment] then
 // [A: BM/32 tiles][...]. The epilogue (MODE) decides what the tile becomes.
 // ---------------------------------------------------------------------------
-template <typename T, int BN, int BM, int MODE>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
+template <typename T, int BN, int BM, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs<T> g) {
   using O = Op<T>;
   using F = typename O::frag;
   constexpr int PCS = frag_pieces<T>();
@@ -68,16 +69,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
   constexpr int TA = BN / 32, TB = BM / 32;         // 32-row tiles per operand
   constexpr int STAGE_A = TA * 4 * FB, STAGE = (TA + TB) * 4 * FB;
   constexpr int NCOPY = (TA + TB) * 4 * PCS;        // 1 KB copies per k-tile
-  constexpr int CPW = NCOPY / 4;                    // per wave
-  constexpr int TN = TA / 2, TR = TB / 2;           // 32x32 tiles per wave
-  static_assert(NCOPY % 4 == 0, "copies per wave");
+  constexpr int WR = NW / 2;                        // waves along the rows
+  constexpr int CPW = NCOPY / NW;                   // per wave
+  constexpr int TN = TA / 2, TR = TB / WR;          // 32x32 tiles per wave
+  static_assert(NCOPY % NW == 0 && TR >= 1 && TB % WR == 0, "copies and tiles per wave");
   __shared__ __align__(16) unsigned char lds0[STAGE];
   __shared__ __align__(16) unsigned char lds1[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rho = lane & 31, hf = lane >> 5;
-  const int wn = wave >> 1, wr = wave & 1;
+  const int wn = wave / WR, wr = wave % WR;
   // Tile order: dispatch is round-robin over the 8 XCDs, so consecutive workgroup
   // ids are renumbered to give each XCD a contiguous range of tiles, and inside
   // that range tiles run in groups of G row tiles per column tile: the ~32
@@ -98,11 +100,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
   const T* __restrict__ XP = g.a;
 
   // Copy k-tile kt into an LDS stage: wave w issues copies [w CPW, (w+1) CPW). With
-  // square tiles the first two waves copy W and the other two A, so a wave has one
+  // square tiles the first half of the waves copy W and the others A, so a wave has one
   // source base; copy q's byte offset in k-tile 0 is loop-invariant (k-tile kw adds
   // kw * 4 fragments), and so is its LDS destination.
-  static_assert(TA == TB, "square tiles: waves 0-1 copy W, waves 2-3 copy A");
-  const bool w_copier = wave < 2;
+  static_assert(TA == TB, "square tiles: the first NW/2 waves copy W, the others A");
+  const bool w_copier = wave < NW / 2;
   uint32_t c_off[CPW];
 #pragma unroll
   for (int q = 0; q < CPW; ++q) {
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
   // tile, r = pi(rho) when the A operand's rows are pi-ordered, and per register
   // group gg the 8 consecutive features 16 gg + 8 hf + [0, 8) of its feature tile.
   auto row_of = [&](int b) {
-    return g.row0 + rt * BM + wr * (BM / 2) + b * 32 + (g.a_pi ? pi_row(rho) : rho);
+    return g.row0 + rt * BM + wr * (BM / WR) + b * 32 + (g.a_pi ? pi_row(rho) : rho);
   };
   auto frag_vals = [&](const f32x16& t, int gg, float* v) {
 #pragma unroll
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
       // keys) per group.
 #pragma unroll
       for (int b = 0; b < TR; ++b) {
-        const int p0 = g.row0 + rt * BM + wr * (BM / 2) + b * 32;   // first token of the tile
+        const int p0 = g.row0 + rt * BM + wr * (BM / WR) + b * 32;  // first token of the tile
         if (p0 >= rows_used) continue;
         const int bi = p0 / Np, pos0 = p0 - bi * Np;        // a tile lies inside one sequence
 #pragma unroll
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs<T> g) {
 
 namespace {
 
-template <typename T, int BN, int BM, int MODE>
+template <typename T, int BN, int BM, int MODE, int NW = (sizeof(T) == 2 ? 8 : 4)>
 int run_gemm(const GemmArgs<T>& g, int n_feat, int rows, hipStream_t s, const char* what, char* err,
              size_t n) {
   // copy offsets are 32-bit byte offsets from each operand's base
@@ -345,7 +347,7 @@ int run_gemm(const GemmArgs<T>& g, int n_feat, int rows, hipStream_t s, const ch
   GemmArgs<T> a = g;
   a.n_tiles_n = n_feat / BN;
   const int ntr = rows / BM;
-  hipLaunchKernelGGL((gemm_kernel<T, BN, BM, MODE>), dim3(a.n_tiles_n * ntr), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<T, BN, BM, MODE, NW>), dim3(a.n_tiles_n * ntr), dim3(64 * NW), 0, s, a);
   return check_launch(what, err, n);
 }
 
