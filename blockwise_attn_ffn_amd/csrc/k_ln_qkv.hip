@@ -115,97 +115,162 @@ __global__ __launch_bounds__(256) void ln_pack_kernel(const TX* __restrict__ X,
   }
 }
 
-// LDS-staged variant (d <= 2048): eight waves read the tile's 32 rows once
-// (4 rows each, coalesced), normalise them in registers and write the packed
-// fragments into LDS; the tile then leaves LDS for global memory as contiguous
-// 16-byte chunks. X is read exactly once.
+// 8 consecutive elements of a row as loaded: bf16 rows stay packed (4 registers)
+// until the row is normalised; fp32 rows are held as loaded.
+template <typename TX>
+struct RowChunk;
+template <>
+struct RowChunk<bf16> {
+  uint4 u;
+  __device__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ void zero() { u = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ void widen(float* v) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct RowChunk<float> {
+  float f[8];
+  __device__ void load(const float* p) { load8_f32(p, f); }
+  __device__ void zero() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = 0.f;
+  }
+  __device__ void widen(float* v) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f[e];
+  }
+};
+
+// LDS-staged variant (d <= 2048): eight waves read a tile's 32 rows once (4 rows
+// each, coalesced), normalise them in registers and write the packed fragments
+// into LDS; the tile then leaves LDS for global memory as contiguous 16-byte
+// chunks. X is read exactly once. Workgroups are persistent over the tiles: as
+// soon as a tile is in LDS, the rows of the workgroup's next tile are requested
+// into the same registers, so their reads overlap the current tile's writes.
 template <typename TX, typename T, int CPL>
-__global__ __launch_bounds__(512) void ln_pack_lds_kernel(const TX* __restrict__ X,
+__global__ __launch_bounds__(512, (CPL <= 2 && sizeof(TX) == 2) ? 4 : 2) void ln_pack_lds_kernel(const TX* __restrict__ X,
                                                           const T* __restrict__ ln_g,
                                                           const T* __restrict__ ln_b,
                                                           T* __restrict__ XP, int B, int N, int Np,
-                                                          int d, float eps) {
+                                                          int d, float eps, int n_tiles) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* tile_lds = reinterpret_cast<T*>(smem_raw);          // [d/16] packed fragments
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tile = blockIdx.x;
   const int nch = d >> 3;
-  // all four rows of this wave are loaded before any arithmetic (four rows of
+  int tile = blockIdx.x;
+  if (tile >= n_tiles) return;
+  // all four rows of this wave are requested before any arithmetic (four rows of
   // loads in flight per wave), and the LN gain and bias once per wave
-  float v[4][CPL][8], g[CPL][8], b[CPL][8];
+  RowChunk<TX> raw[4][CPL];
+  RowChunk<T> gc[CPL], bc[CPL];
   bool live[4];
+  auto load_rows = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = tile * 32 + wave + 8 * i;
-    const int bi = row / Np, pos = row - bi * Np;
-    live[i] = bi < B && pos < N;
-    const TX* xr = X + ((size_t)bi * N + pos) * d;
+    for (int i = 0; i < 4; ++i) {
+      const int row = t * 32 + wave + 8 * i;
+      const int bi = row / Np, pos = row - bi * Np;
+      live[i] = bi < B && pos < N;
+      const TX* xr = X + ((size_t)bi * N + pos) * d;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      if (live[i] && c < nch) {
-        load8_f32(xr + 8 * c, v[i][j]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[i][j][e] = 0.f;
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        if (live[i] && c < nch) raw[i][j].load(xr + 8 * c);
+        else raw[i][j].zero();
       }
     }
-  }
+  };
+  load_rows(tile);
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = lane + 64 * j;
     if (c < nch) {
-      load8_f32(ln_g + 8 * c, g[j]);
-      load8_f32(ln_b + 8 * c, b[j]);
+      gc[j].load(ln_g + 8 * c);
+      bc[j].load(ln_b + 8 * c);
+    } else {
+      gc[j].zero();
+      bc[j].zero();
     }
   }
+  const int n16 = (32 * d * (int)sizeof(T)) >> 4;         // 16-byte chunks in a tile
+  for (;;) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave + 8 * i;
-    if (live[i]) {
-      float sum = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave + 8 * i;
+      float v[CPL][8];
 #pragma unroll
-      for (int j = 0; j < CPL; ++j)
+      for (int j = 0; j < CPL; ++j) raw[i][j].widen(v[j]);   // chunks past d hold 0
+      if (live[i]) {
+        float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum += v[i][j][e];   // chunks past d hold 0
-      const float mean = wave_sum(sum) / (float)d;
-      float q = 0.f;
+        for (int j = 0; j < CPL; ++j)
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
-        if (c < nch) {
+          for (int e = 0; e < 8; ++e) sum += v[j][e];
+        const float mean = wave_sum(sum) / (float)d;
+        float q = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float t = v[i][j][e] - mean;
-            q += t * t;
+        for (int j = 0; j < CPL; ++j) {
+          const int c = lane + 64 * j;
+          if (c < nch) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float t = v[j][e] - mean;
+              q += t * t;
+            }
+          }
+        }
+        const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = lane + 64 * j;
+          if (c < nch) {
+            float g[8], b[8];
+            gc[j].widen(g);
+            bc[j].widen(b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[j][e] = (v[j][e] - mean) * rstd * g[e] + b[e];
           }
         }
       }
-      const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+      // chunk c (k = 8c .. 8c+7) of row r: fragment c/2, slot 32 (c&1) + pi(r)
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const int c = lane + 64 * j;
-        if (c < nch) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[i][j][e] = (v[i][j][e] - mean) * rstd * g[j][e] + b[j][e];
-        }
+        if (c < nch) st_packed(tile_lds + (size_t)(c >> 1) * kFragElems, 32 * (c & 1) + pi_row(r), v[j]);
       }
     }
-    // chunk c (k = 8c .. 8c+7) of row r: fragment c/2, slot 32 (c&1) + pi(r)
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nch) st_packed(tile_lds + (size_t)(c >> 1) * kFragElems, 32 * (c & 1) + pi_row(r), v[i][j]);
-    }
+    __syncthreads();                     // the tile is in LDS; the row registers are free
+    const int next = tile + gridDim.x;
+    if (next < n_tiles) load_rows(next);
+    const uint4* src = reinterpret_cast<const uint4*>(tile_lds);
+    uint4* dst = reinterpret_cast<uint4*>(XP + (size_t)tile * 32 * d);
+    for (int q = threadIdx.x; q < n16; q += 512) dst[q] = src[q];
+    if (next >= n_tiles) break;
+    __syncthreads();                     // every wave has copied the tile out of LDS
+    tile = next;
   }
-  __syncthreads();
-  const int n16 = (32 * d * (int)sizeof(T)) >> 4;         // 16-byte chunks in the tile
-  const uint4* src = reinterpret_cast<const uint4*>(tile_lds);
-  uint4* dst = reinterpret_cast<uint4*>(XP + (size_t)tile * 32 * d);
-  for (int q = threadIdx.x; q < n16; q += 512) dst[q] = src[q];
 }
 
 namespace {
+
+// Persistent grid of the LDS-staged kernel: as many workgroups as the compute units
+// hold at once (registers and LDS, as the runtime reports them), or one per tile.
+template <typename K>
+int ln_grid(K kernel, int n_tiles, size_t smem) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 512, smem) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int grid = cus * per_cu;
+  return n_tiles < grid ? n_tiles : grid;
+}
 
 template <typename TX, typename T>
 int run_ln_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
@@ -215,9 +280,10 @@ int run_ln_pack(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
                       : (d <= 1024 ? ln_pack_lds_kernel<TX, T, 2> : ln_pack_lds_kernel<TX, T, 4>);
     const size_t smem = (size_t)32 * d * sizeof(T);
     if (set_smem(k, smem, err, n)) return 1;
-    hipLaunchKernelGGL(k, dim3(L.rows_pad / 32), dim3(512), smem, s, (const TX*)L.x,
+    const int n_tiles = L.rows_pad / 32;
+    hipLaunchKernelGGL(k, dim3(ln_grid(k, n_tiles, smem)), dim3(512), smem, s, (const TX*)L.x,
                        (const T*)L.w.ln1_g, (const T*)L.w.ln1_b, (T*)L.xpack, L.batch, L.seq_len,
-                       L.seq_pad, d, L.ln_eps);
+                       L.seq_pad, d, L.ln_eps, n_tiles);
     return check_launch("ln_pack", err, n);
   }
   auto k = d <= 1024 ? ln_pack_kernel<TX, T, 2>
@@ -249,9 +315,9 @@ int launch_ln_rows(const LayerLaunch& L, const void* y, int rows, hipStream_t s,
                       : (d <= 1024 ? ln_pack_lds_kernel<float, bf16, 2> : ln_pack_lds_kernel<float, bf16, 4>);
     const size_t smem = (size_t)32 * d * sizeof(bf16);
     if (set_smem(k, smem, err, n)) return 1;
-    hipLaunchKernelGGL(k, dim3(rows / 32), dim3(512), smem, s, (const float*)y,
+    hipLaunchKernelGGL(k, dim3(ln_grid(k, rows / 32, smem)), dim3(512), smem, s, (const float*)y,
                        (const bf16*)L.w.ln2_g, (const bf16*)L.w.ln2_b, (bf16*)L.xpack,
-                       rows / L.seq_pad, L.seq_pad, L.seq_pad, d, L.ln_eps);
+                       rows / L.seq_pad, L.seq_pad, L.seq_pad, d, L.ln_eps, rows / 32);
     return check_launch("ln2_rows", err, n);
   }
   auto k = d <= 1024 ? ln_pack_kernel<float, bf16, 2>
