@@ -418,7 +418,7 @@ def main():
         wl = args.workload if args.workload != "gpt2_medium" else "slm_1b_4k"
         return bench_host(args, synth.WORKLOADS[wl])
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.attention_bwd:
