@@ -118,6 +118,12 @@ bpt_status_t validate_desc(const bpt_layer_desc_t* d) {
                             d->dtype == BPT_F32, 0, d->out_dtype == BPT_F32, d->d_ff,
                             d->precision == 1, msg, sizeof(msg)))
     return fail(BPT_ERR_UNSUPPORTED, "%s", msg);
+  // The matrix-product kernels address each packed operand with 32-bit byte
+  // offsets: every operand they are given must stay under 4 GiB.
+  const int kvp = bpt::kv_pad_cols((int)kv_width(d), d->dtype == BPT_F32);
+  if (!bpt::operands_fit(d->d_model, d->d_ff, kvp, rows_pad_of(d), esize(d->dtype),
+                         d->precision == 1, msg, sizeof(msg)))
+    return fail(BPT_ERR_UNSUPPORTED, "%s", msg);
   return BPT_OK;
 }
 

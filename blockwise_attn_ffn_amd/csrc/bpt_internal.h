@@ -143,6 +143,12 @@ int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t errlen);
 
 int launch_attention_bwd(const AttnBwdLaunch& L, void* stream, char* err, size_t errlen);
 
+// Whether every operand the matrix-product kernels take for this shape stays
+// under 4 GiB (they address packed operands with 32-bit byte offsets). es is the
+// compute type's element size, rows_pad the padded row count of the workspace.
+int operands_fit(int d_model, int d_ff, int kv_pad, size_t rows_pad, size_t es, int split,
+                 char* err, size_t errlen);
+
 // Whether a kernel instance exists for (d_model, d_head, block sizes, types).
 int kernels_support(int d_model, int d_head, int block_q, int block_kv, int compute_f32,
                     int x_f32, int z_f32, int d_ff, int split, char* err, size_t errlen);

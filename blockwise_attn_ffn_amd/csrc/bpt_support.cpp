@@ -50,4 +50,26 @@ int kernels_support(int d_model, int d_head, int block_q, int block_kv, int comp
   return 1;
 }
 
+int operands_fit(int d_model, int d_ff, int kv_pad, size_t rows_pad, size_t es, int split,
+                 char* err, size_t errlen) {
+  const unsigned long long lim = 1ull << 32;
+  const unsigned long long d = (unsigned long long)d_model, f = (unsigned long long)d_ff;
+  // the QKV projection: the packed W_Q | W_K | W_V block and LN1(X)
+  unsigned long long big = (d + 2ull * (unsigned long long)kv_pad) * d * es;
+  unsigned long long act = (unsigned long long)rows_pad * d * es;
+  if (staged_epilogue(d_model, split)) {
+    // staged epilogue: W_1, W_2 and one hidden block [h, d_ff] as operands
+    const unsigned long long h = hidden_block_rows(d_model, rows_pad);
+    if (f * d * es > big) big = f * d * es;
+    if (h * f * es > act) act = h * f * es;
+  }
+  if (big >= lim || act >= lim) {
+    if (err && errlen)
+      snprintf(err, errlen, "a matrix-product operand of %llu bytes: 4 GiB or more is not supported",
+               big > act ? big : act);
+    return 0;
+  }
+  return 1;
+}
+
 }  // namespace bpt

@@ -727,15 +727,14 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
 
 namespace {
 
+// Compute units of the current device, queried on every call (a cheap attribute
+// read; no cached state, so concurrent callers and several devices are safe).
 int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
   return cus;
 }
 

@@ -2,10 +2,11 @@
 // residual, LN2, FFN W_1 -> GELU -> W_2 and the second residual.
 //
 // "Blockwise Parallel Transformer — BPT" (aicassindra.com): section "The fused
-// blockwise algorithm" (y_i = x_i + (o/l) W_O, h_i = act(LN(y_i) W_1),
-// Z[i] = y_i + h_i W_2, then h_i is freed) and "The structural fact that makes
-// fusion legal" (LN, the FFN and the residuals act on each row alone, so a row
-// tile can be finished as soon as its attention output exists).
+// blockwise algorithm" (each query block's attention output is finished by the
+// output projection and residual, then LN and the FFN, whose hidden state is
+// discarded once the block's output rows exist) and "The structural fact that
+// makes fusion legal" (LN, the FFN and the residuals act on each row alone, so
+// a row tile can be finished as soon as its attention output exists).
 //
 // One workgroup = BM token rows, 4 waves. Wave w owns output features
 // [w D/4, (w+1) D/4) of all BM rows; their fp32 accumulators stay in registers

@@ -3,18 +3,20 @@
  * AMD Instinct MI355X (gfx950).
  *
  * What is computed ("Blockwise Parallel Transformer — BPT", aicassindra.com,
- * section "The fused blockwise algorithm"): for every block of b query rows
- *     q_i = LN1(x_i) W_Q;  for each key/value block j (online softmax, running
- *     m, l, o):  s = q_i k_j^T / sqrt(d_k),  m' = max(m, rowmax s),
- *     alpha = exp(m - m'), l = alpha l + sum exp(s - m'), o = alpha o + exp(s - m') v_j
- *     y_i  = x_i + (o / l) W_O
- *     h_i  = GELU_tanh(LN2(y_i) W_1)            -- [b, d_ff], never written to memory
- *     Z[i] = y_i + h_i W_2
- * per head (d_k = d_model / n_heads, heads concatenated in order), with causal
- * key/value blocks that lie wholly after the query block skipped ("Pitfalls and
- * misconceptions"). K and V are projected once per layer (a documented
- * deviation from the pseudocode, which recomputes them in the inner loop; the
- * values are identical).
+ * section "The fused blockwise algorithm"): one pre-LN transformer layer,
+ * Z = Y + FFN(LN2(Y)) with Y = X + Attention(LN1(X)) W_O, evaluated block by block.
+ * Each block of b query rows attends to the key/value blocks one at a time,
+ * keeping per row and head a running maximum of the scaled scores, the running
+ * sum of their exponentials and the running exponential-weighted sum of values
+ * (both rescaled when the maximum grows); the normalised result goes through W_O
+ * and the residual, then LN2, W_1, GELU (tanh form) and W_2 and the second
+ * residual finish those rows. The block's [b, d_ff] hidden state only ever
+ * exists on chip (registers and LDS). Heads are contiguous d_k = d_model /
+ * n_heads column slices, concatenated in order; scores are scaled by
+ * 1/sqrt(d_k). Under the causal mask, key/value blocks that lie wholly after
+ * the query block are never visited ("Pitfalls and misconceptions"). K and V
+ * are projected once per layer rather than once per inner-loop visit (a
+ * documented deviation from the page; the values are identical).
  *
  * Conventions shared by every entry point
  *  - Pointers named X, Z, workspace and every weight are DEVICE pointers to

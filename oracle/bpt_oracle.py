@@ -33,8 +33,9 @@ Readings of points the pages leave open (each also listed in the design notes):
     j // C <= p // C.
 
 Every function below is float64 end to end. "Unfused" functions are the plain
-definition (full softmax, full [N, d_ff] hidden state); the blockwise function is
-the pages' fused loop, written from its description, used to pin the former.
+definition (full softmax, full [N, d_ff] hidden state); the blockwise function
+assembles each row's softmax from per-tile summaries instead, and is used to pin
+the former (the pages state that the two give the same values).
 """
 from __future__ import annotations
 
@@ -478,96 +479,109 @@ def stack_forward_rows(x: np.ndarray, layers: list, rows: np.ndarray, *, seq_len
 
 
 # ---------------------------------------------------------------------------
-# The pages' fused loop, written from its description ([BPT] fused algorithm)
+# The blockwise form: softmax summaries of key tiles, merged ([BPT] fused
+# algorithm; [COST] two-tile running-sum example)
 # ---------------------------------------------------------------------------
 
-def online_softmax_tiles(s: np.ndarray, v: np.ndarray, tile: int):
-    """Running (m, l, o) over consecutive key tiles of one score row s [n] with value
-    rows v [n, dv] ([BPT] inner loop; [COST] two-tile running-sum example).
+def softmax_summary(s: np.ndarray, v: np.ndarray):
+    """Summary of one set of keys for each score row: (m, l, o) with m the largest
+    score, l = sum exp(s - m) and o = sum exp(s - m) v over the keys.
 
-    Start m = -inf, l = 0, o = 0; per tile: m' = max(m, max tile), alpha =
-    exp(m - m'), l = alpha l + sum exp(tile - m'), o = alpha o + exp(tile - m') v.
-    Returns (m, l, o); o / l is the softmax-weighted mean of v.
+    s: [..., n] scores (-inf for a key the row does not see); v: [n, dv], or
+    [..., n, dv] with the leading axes of s (one value matrix per head).
+    A row that sees none of the keys gets m = -inf, l = 0, o = 0 (an empty set).
     """
     s = np.asarray(s, F64)
+    m = s.max(axis=-1)
+    shift = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - shift[..., None])
+    return m, e.sum(axis=-1), e @ np.asarray(v, F64)
+
+
+def merge_summaries(a, b):
+    """Summary of the union of two disjoint key sets from their summaries: both
+    are rescaled to the larger maximum before adding (the identity behind the
+    pages' running sum; an empty set is the neutral element)."""
+    (ma, la, oa), (mb, lb, ob) = a, b
+    m = np.maximum(ma, mb)
+    shift = np.where(np.isfinite(m), m, 0.0)
+    wa = np.where(np.isfinite(ma), np.exp(ma - shift), 0.0)
+    wb = np.where(np.isfinite(mb), np.exp(mb - shift), 0.0)
+    return m, wa * la + wb * lb, wa[..., None] * oa + wb[..., None] * ob
+
+
+def online_softmax_tiles(s: np.ndarray, v: np.ndarray, tile: int):
+    """One score row s [n] with value rows v [n, dv], consumed tile by tile in
+    order: the running (m, l, o) is the merge of the summary so far with the next
+    tile's ([COST] two-tile example: the rescaled tile sums give the full sum).
+    Returns (m, l, o); o / l is the softmax-weighted mean of v."""
+    s = np.asarray(s, F64)
     v = np.asarray(v, F64)
-    m, l, o = -np.inf, 0.0, np.zeros(v.shape[1], F64)
+    state = (np.float64(-np.inf), np.float64(0.0), np.zeros(v.shape[1], F64))
     for t0 in range(0, s.size, tile):
-        st = s[t0:t0 + tile]
-        m_new = max(m, float(st.max()))
-        if m_new == -np.inf:          # nothing visible yet: state unchanged
-            continue
-        alpha = math.exp(m - m_new) if m > -np.inf else 0.0
-        e = np.exp(st - m_new)
-        l = alpha * l + float(e.sum())
-        o = alpha * o + e @ v[t0:t0 + tile]
-        m = m_new
-    return m, l, o
+        state = merge_summaries(state, softmax_summary(s[t0:t0 + tile], v[t0:t0 + tile]))
+    m, l, o = state
+    return float(m), float(l), o
+
+
+def _merge_tree(parts: list):
+    """Merge summaries pairwise, level by level (any grouping gives the same
+    result in exact arithmetic: merging is associative and commutative)."""
+    while len(parts) > 1:
+        nxt = [merge_summaries(parts[i], parts[i + 1]) for i in range(0, len(parts) - 1, 2)]
+        if len(parts) % 2:
+            nxt.append(parts[-1])
+        parts = nxt
+    return parts[0]
 
 
 def blockwise_layer_forward(x: np.ndarray, p: dict, *, seq_len: int, n_heads: int,
                             causal: bool, block_q: int, block_kv: int,
                             eps: float = 1e-5, window: int = 0, chunk: int = 0) -> np.ndarray:
-    """The fused blockwise layer, one sequence at a time ([BPT] fused algorithm).
+    """The layer computed the blockwise way, to pin the unfused definition with
+    ([BPT] fused algorithm: query blocks are independent, each row's softmax is
+    assembled from per-block pieces of the key axis, and the row-wise tail runs on
+    the block alone; [BPT] pitfalls: key blocks wholly after the query block are
+    never formed).
 
-    Outer loop over query blocks i; per head an inner loop over key/value blocks j
-    with the running (m, l, o) state, recomputing k_j, v_j = LN(X[j]) W_K,
-    LN(X[j]) W_V inside the inner loop as the pages write it; blocks whose first
-    key lies after the query block's last row are skipped ([BPT] pitfalls: causal
-    block skipping), the rest are masked per element. Then the body finishes the
-    block: y_i = x_i + (o / l) W_O, h_i = act(LN(y_i) W_1), Z[i] = y_i + h_i W_2.
-    Ragged tails (seq_len not a multiple of the block sizes) use shorter last blocks.
-    With a window or chunk mask (`visible`) the blocks no query of the block sees
-    are skipped the same way; a row that sees no key of a visited block keeps its
-    state (its shift stays 0 while its maximum is -inf).
-    Slow; meant for small inputs.
+    Per sequence and query block of block_q rows: the key axis is cut into tiles
+    of block_kv keys; only tiles that some row of the block sees are visited; each
+    visited tile yields a softmax summary for every (head, row) at once; the
+    summaries are merged as a balanced tree (not in key order), and o / l is the
+    block's attention output. The block then gets W_O and the residual, LN2, the
+    FFN with its [block_q, d_ff] hidden state, and the second residual. Ragged
+    tails give shorter last tiles. Slow; for small inputs.
     """
     x = np.asarray(x, F64)
     p = _as_f64_layer(p)
     rows, d = x.shape
     dk = d // n_heads
-    scale = 1.0 / math.sqrt(dk)
     z = np.empty_like(x)
     for s0 in range(0, rows, seq_len):
         xs = x[s0:s0 + seq_len]
+        x1 = layer_norm(xs, p["ln1_g"], p["ln1_b"], eps)
+        kk, vv = x1 @ p["w_k"], x1 @ p["w_v"]
+        g = kk.shape[1] // dk
+        # [heads, keys, d_k]: query head h reads key/value head h // (n_heads / g)
+        kh = np.repeat(kk.reshape(seq_len, g, dk).transpose(1, 0, 2), n_heads // g, axis=0)
+        vh = np.repeat(vv.reshape(seq_len, g, dk).transpose(1, 0, 2), n_heads // g, axis=0)
         for i0 in range(0, seq_len, block_q):
-            i1 = min(seq_len, i0 + block_q)
-            x_i = xs[i0:i1]
-            q_i = layer_norm(x_i, p["ln1_g"], p["ln1_b"], eps) @ p["w_q"]
-            nb = i1 - i0
-            m = np.full((n_heads, nb), -np.inf)
-            l = np.zeros((n_heads, nb))
-            o = np.zeros((n_heads, nb, dk))
-            last_key = keys_needed(i1 - 1, seq_len, causal, chunk) - 1
-            first_key = max(0, i0 - window + 1) if window else 0
+            qpos = np.arange(i0, min(seq_len, i0 + block_q))
+            qh = (x1[qpos] @ p["w_q"]).reshape(qpos.size, n_heads, dk).transpose(1, 0, 2)
+            parts = []
             for j0 in range(0, seq_len, block_kv):
-                if j0 > last_key:
-                    break                      # block entirely in the future: skipped
-                j1 = min(seq_len, j0 + block_kv)
-                if j1 - 1 < first_key:
-                    continue                   # block entirely before every row's window
-                xj = layer_norm(xs[j0:j1], p["ln1_g"], p["ln1_b"], eps)
-                k_j = xj @ p["w_k"]
-                v_j = xj @ p["w_v"]
-                group = n_heads // (k_j.shape[1] // dk)    # query heads per key/value head
-                for h in range(n_heads):
-                    cols = slice(h * dk, (h + 1) * dk)
-                    kv = slice((h // group) * dk, (h // group + 1) * dk)
-                    s = (q_i[:, cols] @ k_j[:, kv].T) * scale
-                    if causal:
-                        vis = visible(np.arange(i0, i1), np.arange(j0, j1), causal, window, chunk)
-                        s = np.where(vis, s, -np.inf)
-                    m_new = np.maximum(m[h], s.max(axis=1))
-                    shift = np.where(np.isfinite(m_new), m_new, 0.0)
-                    alpha = np.where(np.isfinite(m[h]), np.exp(m[h] - shift), 0.0)
-                    e = np.exp(s - shift[:, None])
-                    l[h] = alpha * l[h] + e.sum(axis=1)
-                    o[h] = alpha[:, None] * o[h] + e @ v_j[:, kv]
-                    m[h] = m_new
-            attn = np.concatenate([o[h] / l[h][:, None] for h in range(n_heads)], axis=1)
-            y_i = x_i + attn @ p["w_o"]
-            h_i = gelu_tanh(layer_norm(y_i, p["ln2_g"], p["ln2_b"], eps) @ p["w_1"])
-            z[s0 + i0:s0 + i1] = y_i + h_i @ p["w_2"]
+                kpos = np.arange(j0, min(seq_len, j0 + block_kv))
+                vis = visible(qpos, kpos, causal, window, chunk)
+                if not vis.any():
+                    continue                   # no row of the block sees this tile
+                s = np.einsum("hqc,hkc->hqk", qh, kh[:, kpos]) / math.sqrt(dk)
+                s = np.where(vis[None], s, -np.inf)
+                parts.append(softmax_summary(s, vh[:, kpos]))
+            _m, l, o = _merge_tree(parts)
+            attn = (o / l[..., None]).transpose(1, 0, 2).reshape(qpos.size, d)
+            y = xs[qpos] + attn @ p["w_o"]
+            hidden = gelu_tanh(layer_norm(y, p["ln2_g"], p["ln2_b"], eps) @ p["w_1"])
+            z[s0 + qpos] = y + hidden @ p["w_2"]
     return z
 
 

@@ -288,3 +288,16 @@ def test_host_abi_under_address_and_ub_sanitizers(tmp_path):
                          timeout=120)
     assert res.returncode == 0, res.stdout
     assert "ALL OK" in res.stdout
+
+
+def test_operands_of_4_gib_are_rejected_before_launch():
+    """8 sequences of 131072 tokens at d_model 2048 in bf16: the LN1 operand alone
+    is 8 * 131072 * 2048 * 2 B = 4 GiB, past the 32-bit offsets of the product
+    kernels. Validation reports BPT_ERR_UNSUPPORTED (nothing enqueued: the fake
+    pointers would fault otherwise) and the workspace query returns 0; one
+    sequence fewer fits."""
+    dsc = desc(batch=8, seq_len=131072, d_model=2048, n_heads=16, d_ff=8192)
+    assert bpt.layer_workspace_bytes(dsc) == 0
+    assert call_layer(dsc) == 3 and "4 GiB" in bpt.last_error()
+    dsc.batch = 7
+    assert bpt.layer_workspace_bytes(dsc) > 0

@@ -853,3 +853,144 @@ def test_backward_rows_forms_equal_full_with_masks_and_groups(mask, g):
     assert np.max(np.abs(oracle.attention_backward_dq_rows(q, k, v, gg, h, True, rows, **mask) - dq[rows])) < 1e-12
     rk, rv = oracle.attention_backward_kv_rows(q, k, v, gg, h, True, rows, **mask)
     assert np.max(np.abs(rk - dk[rows])) < 1e-12 and np.max(np.abs(rv - dv[rows])) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# The layer's saved statistic (layer_lse, layer_lse_rows) against torch
+# --------------------------------------------------------------------------
+
+def torch_layer_lse(x, p, seq_len, n_heads, causal, eps=1e-5, window=0, chunk=0):
+    """[B, n_heads, seq_len] from torch CPU float64 ops alone: F.layer_norm with the
+    first LN's parameters, Q = LN1(x) W_Q, K = LN1(x) W_K, scaled scores per head with
+    the mask built from positions here, then torch.logsumexp over the keys."""
+    t = {k: torch.from_numpy(np.asarray(v, np.float64)) for k, v in p.items()}
+    xt = torch.from_numpy(np.asarray(x, np.float64))
+    rows, d = xt.shape
+    dk = d // n_heads
+    x1 = F.layer_norm(xt, (d,), t["ln1_g"], t["ln1_b"], eps)
+    q, k = x1 @ t["w_q"], x1 @ t["w_k"]
+    g = k.shape[1] // dk
+    pos = torch.arange(seq_len)
+    allowed = torch.ones(seq_len, seq_len, dtype=torch.bool)
+    if causal:
+        allowed = pos[None, :] <= pos[:, None]
+        if window:
+            allowed &= pos[None, :] > pos[:, None] - window
+        if chunk:
+            allowed = (pos[None, :] // chunk) <= (pos[:, None] // chunk)
+    out = torch.empty(rows // seq_len, n_heads, seq_len, dtype=torch.float64)
+    for b in range(rows // seq_len):
+        sl = slice(b * seq_len, (b + 1) * seq_len)
+        for h in range(n_heads):
+            kh = h // (n_heads // g)
+            s = q[sl, h * dk:(h + 1) * dk] @ k[sl, kh * dk:(kh + 1) * dk].T / math.sqrt(dk)
+            out[b, h] = torch.logsumexp(s.masked_fill(~allowed, -math.inf), dim=1)
+    return out.numpy()
+
+
+def torch_attention_heads(x, p, seq_len, n_heads, causal, eps=1e-5):
+    """Per-sequence attention output [rows, d] from torch's layer_norm, matmuls and
+    scaled_dot_product_attention (float64), with the V it used."""
+    t = {k: torch.from_numpy(np.asarray(v, np.float64)) for k, v in p.items()}
+    xt = torch.from_numpy(np.asarray(x, np.float64))
+    rows, d = xt.shape
+    dk = d // n_heads
+    x1 = F.layer_norm(xt, (d,), t["ln1_g"], t["ln1_b"], eps)
+    split = lambda a: a.view(rows // seq_len, seq_len, n_heads, dk).transpose(1, 2)  # noqa: E731
+    q, k, v = x1 @ t["w_q"], x1 @ t["w_k"], x1 @ t["w_v"]
+    a = F.scaled_dot_product_attention(split(q), split(k), split(v), is_causal=causal)
+    return a.transpose(1, 2).reshape(rows, d).numpy(), q.numpy(), k.numpy(), v.numpy()
+
+
+def _layer_lse_pins(full_fn, rows_fn):
+    """True iff full_fn (layer_lse's signature) and rows_fn (layer_lse_rows') pass:
+    torch's logsumexp of the masked scores built from torch's LN and matmuls (random
+    LN gains and biases that differ between the two LNs), and the recovery of torch's
+    SDPA output as exp(S_h - lse_h) V_h for every head."""
+    rng = np.random.default_rng(71)
+    seq, b, d, h = 13, 2, 16, 2
+    dk = d // h
+    x = rng.standard_normal((b * seq, d)) * 1.5 + 0.3
+    p = rand_layer(rng, d, 4 * d, std=0.4)
+    rows = np.array([0, 4, 12, 13, 20, 25])
+    for causal, mask in ((False, {}), (True, {}), (True, dict(window=4)), (True, dict(chunk=5))):
+        want = torch_layer_lse(x, p, seq, h, causal, **mask)
+        got = full_fn(x, p, seq_len=seq, n_heads=h, causal=causal, **mask)
+        if got.shape != want.shape or np.max(np.abs(got - want)) > 1e-12:
+            return False
+        got_r = rows_fn(x, p, rows, seq_len=seq, n_heads=h, causal=causal, **mask)
+        if np.max(np.abs(got_r - want[rows // seq, :, rows % seq])) > 1e-12:
+            return False
+    for causal in (False, True):
+        a, q, k, v = torch_attention_heads(x, p, seq, h, causal)
+        lse = full_fn(x, p, seq_len=seq, n_heads=h, causal=causal)
+        for bb in range(b):
+            sl = slice(bb * seq, (bb + 1) * seq)
+            for hh in range(h):
+                c = slice(hh * dk, (hh + 1) * dk)
+                s = q[sl, c] @ k[sl, c].T / math.sqrt(dk)
+                if causal:
+                    s = np.where(np.arange(seq)[None, :] > np.arange(seq)[:, None], -np.inf, s)
+                if np.max(np.abs(np.exp(s - lse[bb, hh][:, None]) @ v[sl, c] - a[sl, c])) > 1e-12:
+                    return False
+    return True
+
+
+def test_layer_lse_pins_hold_for_the_oracle():
+    assert _layer_lse_pins(oracle.layer_lse, oracle.layer_lse_rows)
+
+
+def test_layer_lse_pins_catch_planted_mistakes(monkeypatch):
+    """Slips that a self-comparison (rows == full) cannot see: the FFN's LN parameters
+    used for the attention's LN, W_K used for the queries, LN left out."""
+    def ln2_for_ln1(fn):
+        return lambda x, p, *a, **kw: fn(x, dict(p, ln1_g=p["ln2_g"], ln1_b=p["ln2_b"]), *a, **kw)
+
+    def wk_for_q(fn):
+        return lambda x, p, *a, **kw: fn(x, dict(p, w_q=p["w_k"]), *a, **kw)
+
+    for planted in (ln2_for_ln1, wk_for_q):
+        assert not _layer_lse_pins(planted(oracle.layer_lse), oracle.layer_lse_rows), planted.__name__
+        assert not _layer_lse_pins(oracle.layer_lse, planted(oracle.layer_lse_rows)), planted.__name__
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "layer_norm", lambda x_, g, b, eps: np.asarray(x_, np.float64))
+        assert not _layer_lse_pins(O.layer_lse, O.layer_lse_rows), "ln_dropped"
+
+
+def test_summaries_merge_in_any_grouping_to_the_full_softmax():
+    """Cut a score row at random points, summarise each piece, merge the pieces in a
+    random order and grouping: o / l is scipy's softmax-weighted mean, l its
+    normaliser at the row maximum; an empty piece changes nothing."""
+    rng = np.random.default_rng(73)
+    for trial in range(20):
+        n = int(rng.integers(1, 40))
+        s = rng.standard_normal(n) * 3
+        v = rng.standard_normal((n, 3))
+        cuts = np.sort(rng.choice(np.arange(1, n), size=min(n - 1, int(rng.integers(0, 6))),
+                                  replace=False)) if n > 1 else np.array([], int)
+        pieces = [O.softmax_summary(a, b) for a, b in zip(np.split(s, cuts), np.split(v, cuts))]
+        pieces.append(O.softmax_summary(np.full(2, -np.inf), np.ones((2, 3))))   # empty set
+        order = rng.permutation(len(pieces))
+        acc = pieces[order[0]]
+        for i in order[1:]:
+            acc = O.merge_summaries(pieces[i], acc) if i % 2 else O.merge_summaries(acc, pieces[i])
+        m, l, o = acc
+        assert m == s.max()
+        assert abs(l - np.exp(s - s.max()).sum()) < 1e-12 * n
+        assert np.max(np.abs(o / l - scipy.special.softmax(s) @ v)) < 1e-12
+
+
+def test_fused_pin_catches_a_merge_without_rescaling(monkeypatch):
+    """A merge that adds the two sums without moving them to the common maximum
+    breaks blockwise == unfused."""
+    def bad(a, b):
+        (ma, la, oa), (mb, lb, ob) = a, b
+        return np.maximum(ma, mb), la + lb, oa + ob
+    monkeypatch.setattr(O, "merge_summaries", bad)
+    rng = np.random.default_rng(74)
+    seq, d, h = 32, 16, 2
+    x = rng.standard_normal((seq, d))
+    p = rand_layer(rng, d, 64, std=0.4)
+    ref = O.layer_forward(x, p, seq_len=seq, n_heads=h, causal=True)
+    got = O.blockwise_layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, block_q=16, block_kv=8)
+    assert O.rel_fro_err(got, ref) > 1e-6
