@@ -20,7 +20,7 @@ EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer
             "bpt_attention_bwd_workspace_bytes", "bpt_attention_bwd",
             "bpt_attention_bwd_profiled", "bpt_attention_fwd_workspace_bytes", "bpt_attention_fwd",
             "bpt_attention_merge", "bpt_layer_host_workspace_bytes", "bpt_layer_fwd_host",
-            "bpt_status_str",
+            "bpt_layer_fwd_noalloc", "bpt_status_str",
             "bpt_last_error", "bpt_version")
 
 
@@ -104,6 +104,9 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_int32]
         L.bpt_layer_fwd_host.restype = ctypes.c_int
+        L.bpt_layer_fwd_noalloc.argtypes = [P(LayerDesc), ctypes.c_void_p, P(LayerWeights),
+                                            ctypes.c_void_p, ctypes.c_void_p]
+        L.bpt_layer_fwd_noalloc.restype = ctypes.c_int
         L.bpt_status_str.argtypes = [ctypes.c_int]
         L.bpt_status_str.restype = ctypes.c_char_p
         L.bpt_last_error.argtypes = []
@@ -177,6 +180,15 @@ def layer_fwd(desc: LayerDesc, x, layer: dict, z, workspace, stream=None) -> Non
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().bpt_layer_fwd(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)),
                                _ptr(z), _ptr(workspace), nbytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # BPT_NOALLOC_SCRATCH_BYTES
+
+
+def layer_fwd_noalloc(desc: LayerDesc, x, layer: dict, z, stream=None) -> None:
+    """bpt_layer_fwd_noalloc: the workspace is the library's fixed device scratch."""
+    _check(lib().bpt_layer_fwd_noalloc(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)),
+                                       _ptr(z), _stream(stream)))
 
 
 def layer_fwd_profiled(desc: LayerDesc, x, layer: dict, z, workspace, events, stream=None) -> None:

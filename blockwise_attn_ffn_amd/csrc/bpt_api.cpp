@@ -364,6 +364,35 @@ bpt_status_t bpt_stack_fwd(const bpt_layer_desc_t* desc, int32_t n_layers, const
   return BPT_OK;
 }
 
+bpt_status_t bpt_layer_fwd_noalloc(const bpt_layer_desc_t* desc, const void* X,
+                                   const bpt_layer_weights_t* weights, void* Z, void* hip_stream) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_desc(desc);
+  if (st != BPT_OK) return st;
+  if (is_empty(desc)) return BPT_OK;
+  if ((st = validate_weights(weights, 0)) != BPT_OK) return st;
+  const bpt::WorkspaceLayout L = layout(desc, false);
+  if (L.total > bpt::kNoallocScratchBytes)
+    return fail(BPT_ERR_WORKSPACE,
+                "this layer needs %zu bytes of workspace; the fixed scratch of the no-allocation "
+                "entry point holds %zu",
+                L.total, bpt::kNoallocScratchBytes);
+  // the caller's buffers first (no device access for these checks)
+  if ((st = validate_buffers(desc, X, Z, nullptr, 0, 0)) != BPT_OK) return st;
+  char msg[256] = "";
+  void* ws = nullptr;
+  if (bpt::noalloc_scratch(&ws, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
+  if ((st = validate_buffers(desc, X, Z, ws, bpt::kNoallocScratchBytes, L.total)) != BPT_OK)
+    return st;
+  bpt::LayerLaunch p = make_launch(desc, L, ws);
+  p.x = X;
+  p.x_f32 = desc->dtype == BPT_F32;
+  p.z = Z;
+  p.z_f32 = desc->out_dtype == BPT_F32;
+  p.w = *weights;
+  return run(p, hip_stream);
+}
+
 size_t bpt_attention_bwd_workspace_bytes(const bpt_attn_desc_t* desc) {
   if (validate_attn_desc(desc) != BPT_OK) return 0;
   if (attn_empty(desc)) return 0;

@@ -138,6 +138,12 @@ struct HostLaunch {
 size_t host_scratch_floats(int d_model, int n_heads, int block_q);
 int launch_layer_host(const HostLaunch& L);
 
+// bpt_layer_fwd_noalloc: bytes of the fixed per-device scratch array, and its
+// device address on the current device (resolved once per device). Returns 0 on
+// success, otherwise writes a message into err.
+constexpr size_t kNoallocScratchBytes = BPT_NOALLOC_SCRATCH_BYTES;
+int noalloc_scratch(void** ptr, char* err, size_t errlen);
+
 // Returns 0 on success, otherwise writes a message into err (errlen bytes).
 int launch_layer(const LayerLaunch& L, void* stream, char* err, size_t errlen);
 

@@ -266,6 +266,22 @@ bpt_status_t bpt_attention_fwd(const bpt_attn_desc_t* desc, const void* Q, const
 bpt_status_t bpt_attention_merge(const bpt_attn_desc_t* desc, float* O_acc, float* lse_acc,
                                  const void* O_part, const float* lse_part, void* hip_stream);
 
+/* bpt_layer_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * workspace is not passed in: the library carves it from a fixed device array of
+ * BPT_NOALLOC_SCRATCH_BYTES bytes that each GPU it runs on holds from the first
+ * call until the process ends; the call itself allocates nothing (no hipMalloc,
+ * no allocating library routine). X, Z and the weights are the caller's, with
+ * every rule of bpt_layer_fwd. A descriptor whose bpt_layer_workspace_bytes
+ * exceeds BPT_NOALLOC_SCRATCH_BYTES returns BPT_ERR_WORKSPACE before anything is
+ * enqueued or any device is touched. Every call on one GPU shares that GPU's
+ * array (it keeps the last call's contents; the layer overwrites all of it that
+ * it reads), so calls that overlap on one GPU race: issue them on one stream,
+ * or otherwise one after another. */
+#define BPT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+bpt_status_t bpt_layer_fwd_noalloc(const bpt_layer_desc_t* desc, const void* X,
+                                   const bpt_layer_weights_t* weights, void* Z, void* hip_stream);
+
 /* n_layers >= 1 layers applied in turn, all with the shape of *desc; layers is
  * a HOST array of n_layers weight sets (each holding device pointers). Layer 0
  * reads X in desc->dtype; the residual stream between layers is fp32; the last

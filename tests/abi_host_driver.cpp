@@ -38,6 +38,13 @@ int launch_attention_merge(int, int, int, int, float*, float*, const void*, cons
   ++g_merge_launches;
   return 0;
 }
+// the no-allocation entry point's fixed scratch: a fake device address
+static int g_scratch_queries = 0;
+int noalloc_scratch(void** ptr, char*, size_t) {
+  ++g_scratch_queries;
+  *ptr = reinterpret_cast<void*>(uintptr_t(0x7f0000000000ull + (5ull << 36)));
+  return 0;
+}
 }  // namespace bpt
 
 static int g_fail = 0;
@@ -71,6 +78,21 @@ int main() {
   EXPECT(bpt::g_last[0].xpack == fake(2ull << 36) && bpt::g_last[0].rows_pad == 512);
   EXPECT((char*)bpt::g_last[0].vt > (char*)bpt::g_last[0].k && (char*)bpt::g_last[0].k > (char*)bpt::g_last[0].q);
   EXPECT(bpt::g_last[0].lse == nullptr);
+  // the no-allocation entry point carves the same layout from its fixed scratch
+  bpt::g_launches = 0;
+  EXPECT(bpt_layer_fwd_noalloc(&d, fake(0), &w[0], fake(1ull << 36), nullptr) == BPT_OK);
+  EXPECT(bpt::g_launches == 1 && bpt::g_scratch_queries == 1);
+  EXPECT(bpt::g_last[0].xpack == fake(5ull << 36) && bpt::g_last[0].rows_pad == 512);
+  {  // too large for the scratch: rejected before the scratch is looked up
+    bpt_layer_desc_t big = d;
+    big.batch = 64; big.seq_len = 1024; big.d_model = 1024; big.n_heads = 16; big.d_ff = 4096;
+    EXPECT(bpt_layer_workspace_bytes(&big) > BPT_NOALLOC_SCRATCH_BYTES);
+    EXPECT(bpt_layer_fwd_noalloc(&big, fake(0), &w[0], fake(1ull << 36), nullptr) == BPT_ERR_WORKSPACE);
+    EXPECT(bpt::g_scratch_queries == 1 && bpt::g_launches == 1);
+    EXPECT(bpt_layer_fwd_noalloc(&d, nullptr, &w[0], fake(1ull << 36), nullptr) == BPT_ERR_NULL);
+    EXPECT(bpt_layer_fwd_noalloc(&d, fake(4), &w[0], fake(1ull << 36), nullptr) == BPT_ERR_ALIGN);
+    EXPECT(bpt::g_scratch_queries == 1);
+  }
   // the statistics entry passes its lse buffer to the launcher
   float* lse = reinterpret_cast<float*>(fake(3ull << 35));
   bpt::g_launches = 0;

@@ -301,3 +301,20 @@ def test_operands_of_4_gib_are_rejected_before_launch():
     assert call_layer(dsc) == 3 and "4 GiB" in bpt.last_error()
     dsc.batch = 7
     assert bpt.layer_workspace_bytes(dsc) > 0
+
+
+def test_noalloc_rejects_without_touching_a_device():
+    """bpt_layer_fwd_noalloc validates on the host first: a layer whose workspace
+    exceeds the fixed scratch is BPT_ERR_WORKSPACE, an invalid descriptor
+    BPT_ERR_SHAPE, a NULL X BPT_ERR_NULL (no GPU in this test)."""
+    lib = bpt.lib()
+    w = bpt.LayerWeights(*[FAKE + (3 << 36) + i * (1 << 30) for i in range(10)])
+    big = desc(batch=64, seq_len=1024, d_model=1024, n_heads=16, d_ff=4096)
+    assert bpt.layer_workspace_bytes(big) > bpt.NOALLOC_SCRATCH_BYTES
+    assert lib.bpt_layer_fwd_noalloc(ctypes.byref(big), FAKE, ctypes.byref(w), FAKE + (1 << 36), None) == 5
+    assert "scratch" in bpt.last_error()
+    bad = desc(causal=2)
+    assert lib.bpt_layer_fwd_noalloc(ctypes.byref(bad), FAKE, ctypes.byref(w), FAKE + (1 << 36), None) == 2
+    ok = desc()
+    assert lib.bpt_layer_fwd_noalloc(ctypes.byref(ok), None, ctypes.byref(w), FAKE + (1 << 36), None) == 1
+    assert lib.bpt_layer_fwd_noalloc(ctypes.byref(ok), FAKE, None, FAKE + (1 << 36), None) == 1
