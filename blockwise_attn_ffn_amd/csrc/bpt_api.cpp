@@ -49,7 +49,8 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   const size_t dm = d->d_model, df = d->d_ff;
   const size_t rp = rows_pad_of(d);
   const bool split = d->precision == 1;
-  const bool staged = bpt::staged_epilogue(d->d_model, split);
+  const bool staged = bpt::staged_epilogue(d->d_model, split, d->d_ff);
+  const bool coop = bpt::coop_epilogue(d->d_model, split, d->d_ff);
   const size_t dkv = kv_width(d);
   // K and V^T cover rows_pad rows on the staged path, so that the fp32 Y [rows_pad, d]
   // fits over them once attention is done
@@ -71,6 +72,13 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   L.h_off = off;      // staged epilogue: hidden block [hidden_block_rows, d_ff]
   const size_t hr = bpt::hidden_block_rows(d->d_model, rp);
   if (staged) off = round_up(off + hr * df * es, kAlign);
+  L.coop_off = off;   // cooperative epilogue: the clusters' exchange regions, then counters
+  if (coop) {
+    const size_t clusters = bpt::kCoopMaxWorkgroups / (d->d_model / bpt::kCoopCols);
+    off = round_up(off + clusters * bpt::coop_region(d->d_model).bytes(), kAlign);
+    L.coop_ctr_off = off;
+    off = round_up(off + (size_t)bpt::kCoopCtrWords * 4, kAlign);
+  }
   if (split) {        // lo halves, same shapes as the hi ones
     const size_t sizes[5] = {rp * dm * es, rp * dm * es, used * dkv * es, used * dkv * es, hr * df * es};
     for (int i = 0; i < 5; ++i) {
@@ -187,7 +195,11 @@ bpt::LayerLaunch make_launch(const bpt_layer_desc_t* d, const bpt::WorkspaceLayo
   p.k = base + L.k_off;
   p.vt = base + L.vt_off;
   p.wpack = base + L.wpack_off;
-  if (bpt::staged_epilogue(d->d_model, p.split)) {
+  if (bpt::coop_epilogue(d->d_model, p.split, d->d_ff)) {
+    p.coop_buf = base + L.coop_off;
+    p.coop_ctr = base + L.coop_ctr_off;
+  }
+  if (bpt::staged_epilogue(d->d_model, p.split, d->d_ff)) {
     p.ybuf = base + L.k_off;
     p.hbuf = base + L.h_off;
     p.h_rows = (int)bpt::hidden_block_rows(p.d_model, (size_t)p.rows_pad);

@@ -46,6 +46,10 @@ struct LayerLaunch {
   void* k_lo;
   void* vt_lo;
   void* hbuf_lo;
+  // cooperative epilogue (d_model 2048 / 4096): the clusters' exchange regions and
+  // the counters (kCoopCtrWords words, zeroed by the launch sequence)
+  void* coop_buf;
+  void* coop_ctr;
   // optional: 5 hipEvent_t recorded around the 4 kernels (measurement only)
   void* const* events;
   // optional: attention statistic lse [batch, n_heads, seq_len] fp32
@@ -54,9 +58,38 @@ struct LayerLaunch {
 
 // Element counts/byte sizes of the workspace pieces (shared by sizing and carving).
 struct WorkspaceLayout {
-  size_t xpack_off, q_off, k_off, vt_off, wpack_off, h_off, resid_off, total;
+  size_t xpack_off, q_off, k_off, vt_off, wpack_off, h_off, coop_off, coop_ctr_off, resid_off, total;
   size_t lo_off[5];   // split: lo halves of xpack, q, k, vt, hidden block
 };
+
+// The cooperative epilogue (k_ffn_coop.hip): clusters of G = d_model / 512
+// workgroups on one XCD finish tiles of 128 rows; member g holds output features
+// [512 g, 512 g + 512) and computes 256 hidden units of every chunk of 256 G.
+constexpr int kCoopRows = 128;
+constexpr int kCoopCols = 512;
+constexpr int kCoopUnits = 256;
+constexpr int kCoopXcds = 8;              // XCDs of the device; workgroups go round-robin
+constexpr int kCoopMaxWorkgroups = 256;   // grid bound: sizes the exchange regions
+// counter words: per-XCD tickets, the error word, then 4 per cluster (stats, LN2
+// operand, hidden chunks, spare)
+constexpr int kCoopCtrTickets = 0;
+constexpr int kCoopCtrError = 16;
+constexpr int kCoopCtrCluster = 32;
+constexpr int kCoopCtrWords = kCoopCtrCluster + 4 * kCoopMaxWorkgroups;
+// One cluster's exchange region: LN2(Y) of the tile as packed fragments [4 row
+// tiles][d/16 k-steps]; two hidden chunks [2][4][hc/16]; the per-row partial
+// statistics [2][G][128] (float2); 4 KB aligned.
+struct CoopRegion {
+  int d, hc, g;
+  constexpr size_t a_off() const { return 0; }
+  constexpr size_t h_off() const { return (size_t)4 * (d / 16) * 1024; }
+  constexpr size_t s_off() const { return h_off() + (size_t)2 * 4 * (hc / 16) * 1024; }
+  constexpr size_t bytes() const { return (s_off() + (size_t)2 * g * kCoopRows * 8 + 4095) / 4096 * 4096; }
+};
+inline CoopRegion coop_region(int d_model) {
+  const int g = d_model / kCoopCols;
+  return CoopRegion{d_model, kCoopUnits * g, g};
+}
 
 // Widest d_model that runs the fused epilogue. Its per-tile fp32 accumulator
 // [rows, d_model] lives in registers, which caps the rows per tile (64 at d 1024,
@@ -66,7 +99,20 @@ struct WorkspaceLayout {
 // precision 1, use the staged epilogue: one GEMM per step, Y in fp32 and the FFN
 // hidden state for a block of rows in the workspace.
 constexpr int kFusedMaxWidth = 1024;
-inline bool staged_epilogue(int d_model, int split = 0) { return split || d_model > kFusedMaxWidth; }
+// The cooperative epilogue takes d_model 2048 and 4096 in bf16 operands, with
+// d_ff a multiple of its chunk (256 d_model / 512 units).
+inline bool coop_epilogue(int d_model, int split, int d_ff) {
+  return !split && (d_model == 2048 || d_model == 4096) && d_ff % (kCoopUnits * (d_model / kCoopCols)) == 0;
+}
+// The staged epilogue: precision 1, and wide layers the cooperative one does not take.
+inline bool staged_epilogue(int d_model, int split, int d_ff) {
+  return split || (d_model > kFusedMaxWidth && !coop_epilogue(d_model, split, d_ff));
+}
+// W_O, W_1, W_2 in plain fragment order (cooperative or staged epilogue) rather
+// than the fused epilogue's per-wave stream.
+inline bool plain_epilogue_weights(int d_model, int split, int d_ff) {
+  return split || d_model > kFusedMaxWidth;
+}
 // Rows of the staged epilogue's hidden block: enough that the W_2 product
 // (rows x d_model) spans 512 output tiles of 256 x 256 (2^25 / d_model, a
 // multiple of 256), at least 4096, at most the padded rows.

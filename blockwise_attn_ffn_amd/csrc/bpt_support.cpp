@@ -57,7 +57,7 @@ int operands_fit(int d_model, int d_ff, int kv_pad, size_t rows_pad, size_t es, 
   // the QKV projection: the packed W_Q | W_K | W_V block and LN1(X)
   unsigned long long big = (d + 2ull * (unsigned long long)kv_pad) * d * es;
   unsigned long long act = (unsigned long long)rows_pad * d * es;
-  if (staged_epilogue(d_model, split)) {
+  if (staged_epilogue(d_model, split, d_ff)) {
     // staged epilogue: W_1, W_2 and one hidden block [h, d_ff] as operands
     const unsigned long long h = hidden_block_rows(d_model, rows_pad);
     if (f * d * es > big) big = f * d * es;

@@ -341,7 +341,8 @@ int dispatch_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
 }  // namespace
 
 int launch_ffn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
-  if (staged_epilogue(L.d_model, L.split)) return launch_ffn_staged(L, s, err, n);
+  if (coop_epilogue(L.d_model, L.split, L.d_ff)) return launch_ffn_coop(L, s, err, n);
+  if (staged_epilogue(L.d_model, L.split, L.d_ff)) return launch_ffn_staged(L, s, err, n);
   if (L.compute_f32)
     return L.z_f32 ? dispatch_ffn<float, float, float>(L, s, err, n)
                    : dispatch_ffn<float, float, bf16>(L, s, err, n);

@@ -80,11 +80,11 @@ int pack_all(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   PackJob<T> job{};
   job.fs = FfnStream{d, f};
   const void* srcs[6] = {L.w.w_q, L.w.w_k, L.w.w_v, L.w.w_o, L.w.w_1, L.w.w_2};
-  const bool staged = staged_epilogue(d, L.split);
+  const bool staged = plain_epilogue_weights(d, L.split, f);
   T* dsts[6] = {p, p + dd, p + dd + (size_t)kvp * d, p + qkv, p + qkv, p + qkv};
   const int rows[6] = {d, dkv, dkv, d, f, d}, Ks[6] = {d, d, d, d, d, f};
   int orders[6] = {kPlain, kPlain, kPlain, kStreamWO, kStreamW1, kStreamW2};
-  if (staged) {   // the staged epilogue's GEMMs take W_O, W_1, W_2 in plain order
+  if (staged) {   // the cooperative and staged epilogues take W_O, W_1, W_2 in plain order
     dsts[4] = p + qkv + dd;
     dsts[5] = p + qkv + dd + (size_t)f * d;
     orders[3] = orders[4] = orders[5] = kPlain;

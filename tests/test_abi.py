@@ -58,14 +58,32 @@ def hidden_rows(d, rows_pad):
     return min(rows_pad, max(4096, (2 ** 25 // d) // 256 * 256))
 
 
+def coop_exchange_bytes(d):
+    """The cooperative epilogue's exchange regions (one per cluster of d / 512
+    workgroups, 256 workgroups at most) and its counters: per cluster LN2(Y) of a
+    128-row tile, two hidden chunks of 256 d / 512 units and the per-row partial
+    statistics, 4 KB aligned; independent of the number of rows."""
+    g = d // 512
+    hc = 256 * g
+    region = 4 * (d // 16) * 1024 + 2 * 4 * (hc // 16) * 1024 + 2 * g * 128 * 8
+    region = (region + 4095) // 4096 * 4096
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return up((256 // g) * region) + up((32 + 4 * 256) * 4)
+
+
+def is_coop(d, f, split):
+    return not split and d in (2048, 4096) and f % (256 * (d // 512)) == 0
+
+
 def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=False, dkv=None):
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     rows = batch * n
     npad = (n + 127) // 128 * 128
     used = batch * npad
     rows_pad = up(used)
-    staged = d > 1024 or split  # staged epilogue: K, V^T over rows_pad rows + hidden block
     f = 4 * d if d_ff is None else d_ff
+    coop = is_coop(d, f, split)    # cooperative epilogue: an exchange region, nothing [rows, d_ff]
+    staged = (d > 1024 and not coop) or split  # staged: K, V^T over rows_pad rows + hidden block
     dkv = d if dkv is None else dkv          # key/value width (grouped-query attention)
     tile = 128 if es == 4 else 256
     kvp = (dkv + tile - 1) // tile * tile    # K and V parts of the projection, padded
@@ -76,6 +94,8 @@ def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=Fals
     acts = 2 * up(rows_pad * d * es) + kv_space
     hidden = up(hidden_rows(d, rows_pad) * f * es) if staged else 0
     tot = acts + up(((d + 2 * kvp) * d + d * d + 2 * d * f) * es) + hidden
+    if coop:
+        tot += coop_exchange_bytes(d)
     if split:                   # lo halves: no Y room there
         acts = 2 * up(rows_pad * d * es) + 2 * up(kv_rows * dkv * es)
     if split:                   # lo halves of the bf16 pairs
@@ -152,14 +172,20 @@ def test_workspace_is_block_shaped_not_ffn_shaped():
         weights = (4 * w.d_model * w.d_model + 2 * w.d_model * w.d_ff) * 2
         act = ws - weights
         nd = w.rows * w.d_model * 2
-        staged = w.d_model > 1024
-        hidden_block = hidden_rows(w.d_model, w.rows) * w.d_ff * 2 if staged else 0
-        assert act <= 4 * nd + hidden_block + 8 * 256 + 256 * w.d_model * 2 * 2
+        exchange = coop_exchange_bytes(w.d_model) if is_coop(w.d_model, w.d_ff, False) else 0
+        assert act <= 4 * nd + exchange + 8 * 256 + 256 * w.d_model * 2 * 2
         assert act < 2 * w.rows * w.d_ff * 2          # the unfused FFN hidden pair
         assert act < 14 * nd                          # after-Flash, unfused
     w = synth.WORKLOADS["long_128k"]
     assert bpt.layer_workspace_bytes(bpt.desc_for(w)) < w.seq_len * w.seq_len * 2
-    assert hidden_rows(w.d_model, w.rows) * 8 == w.rows   # 1/8 of the [N, d_ff] hidden
+    # no term grows with rows x d_ff: the exchange region is under 1/30 of the [N, d_ff] hidden
+    # here, and the same at any sequence length
+    assert coop_exchange_bytes(w.d_model) * 30 < w.rows * w.d_ff * 2
+    longer = bpt.desc_for(w)
+    longer.seq_len *= 2
+    ws1, ws2 = bpt.layer_workspace_bytes(bpt.desc_for(w)), bpt.layer_workspace_bytes(longer)
+    weights = (4 * w.d_model * w.d_model + 2 * w.d_model * w.d_ff) * 2
+    assert ws2 - weights == 2 * (ws1 - weights - coop_exchange_bytes(w.d_model)) + coop_exchange_bytes(w.d_model)
     # the stack runs in bf16 pairs (precision 1), which doubles every activation
     w = synth.WORKLOADS["stack4_32k"]
     assert w.precision == 1
