@@ -75,12 +75,13 @@ bpt::WorkspaceLayout layout(const bpt_layer_desc_t* d, bool stack_resid) {
   L.coop_off = off;   // cooperative epilogue: the clusters' exchange regions, then counters
   if (coop) {
     const size_t clusters = bpt::kCoopMaxWorkgroups / (d->d_model / bpt::kCoopCols);
-    off = round_up(off + clusters * bpt::coop_region(d->d_model).bytes(), kAlign);
+    off = round_up(off + clusters * bpt::coop_region(d->d_model, split).bytes(), kAlign);
     L.coop_ctr_off = off;
     off = round_up(off + (size_t)bpt::kCoopCtrWords * 4, kAlign);
   }
   if (split) {        // lo halves, same shapes as the hi ones
-    const size_t sizes[5] = {rp * dm * es, rp * dm * es, used * dkv * es, used * dkv * es, hr * df * es};
+    const size_t sizes[5] = {rp * dm * es, rp * dm * es, used * dkv * es, used * dkv * es,
+                             staged ? hr * df * es : 0};
     for (int i = 0; i < 5; ++i) {
       L.lo_off[i] = off;
       off = round_up(off + sizes[i], kAlign);

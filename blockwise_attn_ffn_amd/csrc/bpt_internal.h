@@ -76,19 +76,20 @@ constexpr int kCoopCtrTickets = 0;
 constexpr int kCoopCtrError = 16;
 constexpr int kCoopCtrCluster = 32;
 constexpr int kCoopCtrWords = kCoopCtrCluster + 4 * kCoopMaxWorkgroups;
-// One cluster's exchange region: LN2(Y) of the tile as packed fragments [4 row
-// tiles][d/16 k-steps]; two hidden chunks [2][4][hc/16]; the per-row partial
-// statistics [2][G][128] (float2); 4 KB aligned.
+// One cluster's exchange region: LN2(Y) of the tile as packed fragments [na
+// halves][4 row tiles][d/16 k-steps]; two hidden chunks [2][na][4][hc/16]; the
+// per-row partial statistics [2][G][128] (float2); 4 KB aligned. na = 2 with
+// bf16 pairs (hi and lo halves), else 1.
 struct CoopRegion {
-  int d, hc, g;
+  int d, hc, g, na;
   constexpr size_t a_off() const { return 0; }
-  constexpr size_t h_off() const { return (size_t)4 * (d / 16) * 1024; }
-  constexpr size_t s_off() const { return h_off() + (size_t)2 * 4 * (hc / 16) * 1024; }
+  constexpr size_t h_off() const { return (size_t)na * 4 * (d / 16) * 1024; }
+  constexpr size_t s_off() const { return h_off() + (size_t)2 * na * 4 * (hc / 16) * 1024; }
   constexpr size_t bytes() const { return (s_off() + (size_t)2 * g * kCoopRows * 8 + 4095) / 4096 * 4096; }
 };
-inline CoopRegion coop_region(int d_model) {
+inline CoopRegion coop_region(int d_model, int split) {
   const int g = d_model / kCoopCols;
-  return CoopRegion{d_model, kCoopUnits * g, g};
+  return CoopRegion{d_model, kCoopUnits * g, g, split ? 2 : 1};
 }
 
 // Widest d_model that runs the fused epilogue. Its per-tile fp32 accumulator
@@ -99,14 +100,16 @@ inline CoopRegion coop_region(int d_model) {
 // precision 1, use the staged epilogue: one GEMM per step, Y in fp32 and the FFN
 // hidden state for a block of rows in the workspace.
 constexpr int kFusedMaxWidth = 1024;
-// The cooperative epilogue takes d_model 2048 and 4096 in bf16 operands, with
-// d_ff a multiple of its chunk (256 d_model / 512 units).
+// The cooperative epilogue takes d_model 2048 and 4096 in bf16 operands or bf16
+// pairs, with d_ff a multiple of its chunk (256 d_model / 512 units).
 inline bool coop_epilogue(int d_model, int split, int d_ff) {
-  return !split && (d_model == 2048 || d_model == 4096) && d_ff % (kCoopUnits * (d_model / kCoopCols)) == 0;
+  (void)split;
+  return (d_model == 2048 || d_model == 4096) && d_ff % (kCoopUnits * (d_model / kCoopCols)) == 0;
 }
-// The staged epilogue: precision 1, and wide layers the cooperative one does not take.
+// The staged epilogue: what neither fused epilogue takes (precision 1 at d_model
+// 1024 and below, and wide layers whose d_ff is not a multiple of the chunk).
 inline bool staged_epilogue(int d_model, int split, int d_ff) {
-  return split || (d_model > kFusedMaxWidth && !coop_epilogue(d_model, split, d_ff));
+  return !coop_epilogue(d_model, split, d_ff) && (split || d_model > kFusedMaxWidth);
 }
 // W_O, W_1, W_2 in plain fragment order (cooperative or staged epilogue) rather
 // than the fused epilogue's per-wave stream.

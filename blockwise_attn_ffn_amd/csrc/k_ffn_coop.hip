@@ -47,6 +47,7 @@ namespace bpt {
 struct CoopArgs {
   const void* x;          // residual X [batch * N, d] (real rows), TX
   const bf16* o;          // attention output: packed B fragments [packed rows / 32][d / 16]
+  const bf16* o_lo;       // its lo half (bf16 pairs), same layout
   const bf16* w_o;        // plain fragment order [d / 32 tiles][d / 16 k-steps]
   const bf16* w_1;        // [d_ff / 32][d / 16]
   const bf16* w_2;        // [d / 32][d_ff / 16]
@@ -65,7 +66,9 @@ namespace {
 constexpr int kRows = kCoopRows;           // 128 rows per tile
 constexpr int kRT = kRows / 32;            // 4 row tiles of 32
 constexpr int kNW = 8;                     // waves
-constexpr int kStage = 40 * 1024;          // bytes per LDS stage
+// bytes per LDS stage: NA activation halves (8 KB each) and 32 KB of weights
+template <bool SPLIT>
+constexpr int stage_bytes() { return (SPLIT ? 16 : 8) * 1024 + 32 * 1024; }
 
 // The XCD (XCC) this wave runs on (hardware register XCC_ID, bits 3:0).
 __device__ inline unsigned xcc_id() {
@@ -143,6 +146,51 @@ __device__ inline void ld_stage8(uint32_t abase, uint32_t wbase, bf16x8 (&a)[2][
       : "v"(abase), "v"(wbase));
 }
 
+// One k-step of the pair mode: act hi [4] at abase + b KB, act lo [4] at abase +
+// 8 KB + b KB, weights [2] at wbase + 2 t KB.
+__device__ inline void ld_step10(uint32_t abase, uint32_t wbase, bf16x8 (&a)[4], bf16x8 (&al)[4],
+                                 bf16x8 (&w)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %10 offset:0\n\t"
+      "ds_read_b128 %1, %10 offset:1024\n\t"
+      "ds_read_b128 %2, %10 offset:2048\n\t"
+      "ds_read_b128 %3, %10 offset:3072\n\t"
+      "ds_read_b128 %4, %10 offset:8192\n\t"
+      "ds_read_b128 %5, %10 offset:9216\n\t"
+      "ds_read_b128 %6, %10 offset:10240\n\t"
+      "ds_read_b128 %7, %10 offset:11264\n\t"
+      "ds_read_b128 %8, %11 offset:0\n\t"
+      "ds_read_b128 %9, %11 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(a[0]), "=v"(a[1]), "=v"(a[2]), "=v"(a[3]), "=v"(al[0]), "=v"(al[1]), "=v"(al[2]),
+        "=v"(al[3]), "=v"(w[0]), "=v"(w[1])
+      : "v"(abase), "v"(wbase));
+}
+// act hi [2] at abase + b KB, act lo [2] at abase + 8 KB + b KB, weights [2] at wbase + 2 t KB.
+__device__ inline void ld_step6(uint32_t abase, uint32_t wbase, bf16x8 (&a)[2], bf16x8 (&al)[2],
+                                bf16x8 (&w)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %6 offset:0\n\t"
+      "ds_read_b128 %1, %6 offset:1024\n\t"
+      "ds_read_b128 %2, %6 offset:8192\n\t"
+      "ds_read_b128 %3, %6 offset:9216\n\t"
+      "ds_read_b128 %4, %7 offset:0\n\t"
+      "ds_read_b128 %5, %7 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(a[0]), "=v"(a[1]), "=v"(al[0]), "=v"(al[1]), "=v"(w[0]), "=v"(w[1])
+      : "v"(abase), "v"(wbase));
+}
+
+// v as a bf16 pair: hi = v rounded to bf16 at p, lo = v - hi rounded at plo.
+__device__ inline void st_pair_packed(bf16* p, bf16* plo, int lane, float* v, bool split) {
+  st_packed(p, lane, v);
+  if (split) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] -= bf16_round(v[e]);
+    st_packed(plo, lane, v);
+  }
+}
+
 __device__ inline void post(unsigned* c) {
   __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -168,7 +216,7 @@ __device__ inline float2 load_l2_f2(const float2* p) {
 
 }  // namespace
 
-template <typename TX, typename TO, int G>
+template <typename TX, typename TO, int G, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
   using O = Op<bf16>;
   using F = O::frag;
@@ -178,7 +226,11 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
   constexpr int NKB_D = D / 32, NKB_H = HC / 32;   // k-blocks of 2 k-steps
   constexpr int OWN_D = kCoopCols / 32;    // k-blocks of d that are this member's features
   constexpr int OWN_H = kCoopUnits / 32;   // k-blocks of a chunk that are this member's units
-  constexpr CoopRegion R{D, HC, G};
+  constexpr int NA = SPLIT ? 2 : 1;        // activation halves: hi, and lo for bf16 pairs
+  constexpr int AKB = 8 * NA;              // KB of activation fragments per stage
+  constexpr int CPZ = NA + 4, CPU = NA + 2;   // copies per wave per stage (Z side, W_1)
+  constexpr int kStage = stage_bytes<SPLIT>();
+  constexpr CoopRegion R{D, HC, G, NA};
   // three distinct stage arrays (not one indexed array): the compiler then sees
   // that copies into one stage never alias reads of another, and does not wait for
   // the copies in flight before reading the current stage
@@ -214,8 +266,9 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
   if (cluster < 0) return;
   const int n_clusters = a.n_xcc * (a.per_xcc / G);
   unsigned char* const region = a.xbuf + (size_t)cluster * R.bytes();
-  bf16* const A = reinterpret_cast<bf16*>(region + R.a_off());      // [kRT][KSD] fragments
-  bf16* const H = reinterpret_cast<bf16*>(region + R.h_off());      // [2][kRT][KSH] fragments
+  bf16* const A = reinterpret_cast<bf16*>(region + R.a_off());      // [NA][kRT][KSD] fragments
+  bf16* const H = reinterpret_cast<bf16*>(region + R.h_off());      // [2][NA][kRT][KSH] fragments
+  constexpr size_t A_HALF = (size_t)kRT * KSD * kFragElems, H_HALF = (size_t)kRT * KSH * kFragElems;
   float2* const S = reinterpret_cast<float2*>(region + R.s_off());  // [2][G][kRows]
   unsigned* const c_stats = a.ctr + kCoopCtrCluster + 4 * cluster;
   unsigned* const c_a = c_stats + 1;
@@ -262,20 +315,42 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
     if (kb + 1 < n_kb) step(kb + 1, st1, st0);
     __syncthreads();     // stages free for the next phase
   };
-  // The copies of one k-block: activation fragments (row tile b, k-step j) at
-  // stage byte (4 j + b) KB, weight fragments (tile t, k-step j) at (8 + 2 t + j) KB.
+  // The copies of one k-block: activation fragments (half hh, row tile b, k-step
+  // j) at stage byte (8 hh + 4 j + b) KB, weight fragments (tile t, k-step j) at
+  // (AKB + 2 t + j) KB; copy idx of a k-block lands at idx KB.
   auto zcompute = [&](const unsigned char* st, auto issue) __attribute__((always_inline)) {
-    F af[2][kRT], wf[2][2];
-    ld_stage12(lds_addr(st) + lane * 16, lds_addr(st) + 8 * 1024 + zt0 * 2048 + lane * 16, af, wf);
-    __builtin_amdgcn_sched_barrier(0);
-    issue();
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!SPLIT) {
+      F af[2][kRT], wf[2][2];
+      ld_stage12(lds_addr(st) + lane * 16, lds_addr(st) + AKB * 1024 + zt0 * 2048 + lane * 16, af, wf);
+      __builtin_amdgcn_sched_barrier(0);
+      issue();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int b = 0; b < kRT; ++b) O::mma(acc[t][b], wf[j][t], af[j][b]);
+          for (int b = 0; b < kRT; ++b) O::mma(acc[t][b], wf[j][t], af[j][b]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        F af[kRT], al[kRT], wf[2];
+        ld_step10(lds_addr(st) + j * 4096 + lane * 16, lds_addr(st) + AKB * 1024 + zt0 * 2048 + j * 1024 + lane * 16,
+                  af, al, wf);
+        if (j == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int b = 0; b < kRT; ++b) {
+            O::mma(acc[t][b], wf[t], af[b]);
+            O::mma(acc[t][b], wf[t], al[b]);
+          }
+      }
+    }
   };
   auto no_hook = [](int) {};
 
@@ -302,23 +377,24 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
     // ---- Y^T = X^T + W_O[slice] O^T over all d
     {
       const bf16* osrc = a.o + (size_t)(r0 / 32) * KSD * kFragElems;
+      const bf16* osrc_lo = SPLIT ? a.o_lo + (size_t)(r0 / 32) * KSD * kFragElems : osrc;
       const bf16* wsrc = a.w_o + (size_t)(g * 16) * KSD * kFragElems;
       // copy q of this wave: fragment (row tile or weight tile, k-step j) of
       // k-block 0; k-block kb is 2 kb fragments further
-      const char* base[5];
+      const char* base[CPZ];
 #pragma unroll
-      for (int q = 0; q < 5; ++q) {
-        const int idx = wave * 5 + q;
+      for (int q = 0; q < CPZ; ++q) {
+        const int idx = wave * CPZ + q, i = idx & 7;
         base[q] = reinterpret_cast<const char*>(
-            idx < 8 ? osrc + ((size_t)(idx & 3) * KSD + (idx >> 2)) * kFragElems
-                    : wsrc + ((size_t)((idx - 8) >> 1) * KSD + ((idx - 8) & 1)) * kFragElems);
+            idx < AKB ? (idx < 8 ? osrc : osrc_lo) + ((size_t)(i & 3) * KSD + (i >> 2)) * kFragElems
+                      : wsrc + ((size_t)((idx - AKB) >> 1) * KSD + ((idx - AKB) & 1)) * kFragElems);
       }
       auto copy = [&](int kb, unsigned char* st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 5; ++q)
-          dma16_l2(base[q] + (size_t)kb * 2048 + lane * 16, st + (wave * 5 + q) * 1024);
+        for (int q = 0; q < CPZ; ++q)
+          dma16_l2(base[q] + (size_t)kb * 2048 + lane * 16, st + (wave * CPZ + q) * 1024);
       };
-      phase(NKB_D, std::integral_constant<int, 5>{}, copy, zcompute, no_hook);
+      phase(NKB_D, std::integral_constant<int, CPZ>{}, copy, zcompute, no_hook);
     }
 
     // ---- LN2 statistics of every row: this member's slice, then the cluster's
@@ -406,7 +482,8 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
           float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = (acc[t][b][8 * gg + e] - st.x) * st.y * gv[e] + bv[e];
-          st_packed(A + ((size_t)b * KSD + (n >> 4)) * kFragElems, lane, v);
+          const size_t f = ((size_t)b * KSD + (n >> 4)) * kFragElems;
+          st_pair_packed(A + f, A + A_HALF + f, lane, v, SPLIT);
         }
       }
     wait_vmem();
@@ -425,33 +502,54 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
         for (int b = 0; b < 2; ++b) u[t][b] = f32x16{};
       {
         const bf16* w1src = a.w_1 + (size_t)(c * 8 * G + 8 * g) * KSD * kFragElems;
-        const char* base[3];
+        const char* base[CPU];
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          const int idx = wave * 3 + q;
+        for (int q = 0; q < CPU; ++q) {
+          const int idx = wave * CPU + q, i = idx & 7;
           base[q] = reinterpret_cast<const char*>(
-              idx < 8 ? A + ((size_t)(idx & 3) * KSD + (idx >> 2)) * kFragElems
-                      : w1src + ((size_t)((idx - 8) >> 1) * KSD + ((idx - 8) & 1)) * kFragElems);
+              idx < AKB ? A + (idx < 8 ? 0 : A_HALF) + ((size_t)(i & 3) * KSD + (i >> 2)) * kFragElems
+                        : w1src + ((size_t)((idx - AKB) >> 1) * KSD + ((idx - AKB) & 1)) * kFragElems);
         }
         auto copy = [&](int kb, unsigned char* st) __attribute__((always_inline)) {
           const int kp = (kb + OWN_D * g) % NKB_D;
 #pragma unroll
-          for (int q = 0; q < 3; ++q)
-            dma16_l2(base[q] + (size_t)kp * 2048 + lane * 16, st + (wave * 3 + q) * 1024);
+          for (int q = 0; q < CPU; ++q)
+            dma16_l2(base[q] + (size_t)kp * 2048 + lane * 16, st + (wave * CPU + q) * 1024);
         };
         auto compute = [&](const unsigned char* st, auto issue) __attribute__((always_inline)) {
-          F af[2][2], wf[2][2];
-          ld_stage8(lds_addr(st) + rb0 * 1024 + lane * 16, lds_addr(st) + 8 * 1024 + ut0 * 2048 + lane * 16,
-                    af, wf);
-          __builtin_amdgcn_sched_barrier(0);
-          issue();
-          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (!SPLIT) {
+            F af[2][2], wf[2][2];
+            ld_stage8(lds_addr(st) + rb0 * 1024 + lane * 16, lds_addr(st) + AKB * 1024 + ut0 * 2048 + lane * 16,
+                      af, wf);
+            __builtin_amdgcn_sched_barrier(0);
+            issue();
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+              for (int t = 0; t < 2; ++t)
 #pragma unroll
-              for (int b = 0; b < 2; ++b) O::mma(u[t][b], wf[j][t], af[j][b]);
+                for (int b = 0; b < 2; ++b) O::mma(u[t][b], wf[j][t], af[j][b]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              F af[2], al[2], wf[2];
+              ld_step6(lds_addr(st) + j * 4096 + rb0 * 1024 + lane * 16,
+                       lds_addr(st) + AKB * 1024 + ut0 * 2048 + j * 1024 + lane * 16, af, al, wf);
+              if (j == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue();
+                __builtin_amdgcn_sched_barrier(0);
+              }
+#pragma unroll
+              for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                  O::mma(u[t][b], wf[t], af[b]);
+                  O::mma(u[t][b], wf[t], al[b]);
+                }
+            }
+          }
         };
         // the other members' features of LN2(Y) are needed from k-block OWN_D on
         auto hook = [&](int kb) __attribute__((always_inline)) {
@@ -459,7 +557,7 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
               !wait_count(c_a, (unsigned)G * (it + 1), err, a.spin_limit))
             s_failed = 1;
         };
-        phase(NKB_D, std::integral_constant<int, 3>{}, copy, compute, hook);
+        phase(NKB_D, std::integral_constant<int, CPU>{}, copy, compute, hook);
       }
       // H = GELU(U) -> the member's units of the chunk in the cluster's hidden buffer
 #pragma unroll
@@ -472,7 +570,8 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gelu_tanh(u[t][b][8 * gg + e]);
-            st_packed(H + (((size_t)hp * kRT + rb0 + b) * KSH + ks) * kFragElems, lane, v);
+            const size_t f = (size_t)hp * NA * H_HALF + ((size_t)(rb0 + b) * KSH + ks) * kFragElems;
+            st_pair_packed(H + f, H + H_HALF + f, lane, v, SPLIT);
           }
         }
       wait_vmem();
@@ -480,21 +579,21 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
       if (tid == 0) post(c_h);
       // Z^T += W_2[slice, chunk] H^T, k over the chunk starting at the own units
       {
-        const bf16* hsrc = H + (size_t)hp * kRT * KSH * kFragElems;
+        const bf16* hsrc = H + (size_t)hp * NA * H_HALF;
         const bf16* w2src = a.w_2 + ((size_t)(g * 16) * KS2 + (size_t)c * KSH) * kFragElems;
-        const char* base[5];
+        const char* base[CPZ];
 #pragma unroll
-        for (int q = 0; q < 5; ++q) {
-          const int idx = wave * 5 + q;
+        for (int q = 0; q < CPZ; ++q) {
+          const int idx = wave * CPZ + q, i = idx & 7;
           base[q] = reinterpret_cast<const char*>(
-              idx < 8 ? hsrc + ((size_t)(idx & 3) * KSH + (idx >> 2)) * kFragElems
-                      : w2src + ((size_t)((idx - 8) >> 1) * KS2 + ((idx - 8) & 1)) * kFragElems);
+              idx < AKB ? hsrc + (idx < 8 ? 0 : H_HALF) + ((size_t)(i & 3) * KSH + (i >> 2)) * kFragElems
+                        : w2src + ((size_t)((idx - AKB) >> 1) * KS2 + ((idx - AKB) & 1)) * kFragElems);
         }
         auto copy = [&](int kb, unsigned char* st) __attribute__((always_inline)) {
           const int kp = (kb + OWN_H * g) % NKB_H;
 #pragma unroll
-          for (int q = 0; q < 5; ++q)
-            dma16_l2(base[q] + (size_t)kp * 2048 + lane * 16, st + (wave * 5 + q) * 1024);
+          for (int q = 0; q < CPZ; ++q)
+            dma16_l2(base[q] + (size_t)kp * 2048 + lane * 16, st + (wave * CPZ + q) * 1024);
         };
         // the other members' units of the chunk are needed from k-block OWN_H on
         auto hook = [&](int kb) __attribute__((always_inline)) {
@@ -502,7 +601,7 @@ __global__ __launch_bounds__(512, 1) void ffn_coop_kernel(CoopArgs a) {
               !wait_count(c_h, (unsigned)G * (gc + 1), err, a.spin_limit))
             s_failed = 1;
         };
-        phase(NKB_H, std::integral_constant<int, 5>{}, copy, zcompute, hook);
+        phase(NKB_H, std::integral_constant<int, CPZ>{}, copy, zcompute, hook);
       }
     }
     failed = failed || s_failed;
@@ -532,7 +631,7 @@ __global__ void zero_words_kernel(unsigned* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
-template <typename TX, typename TO, int G>
+template <typename TX, typename TO, int G, bool SPLIT>
 int run_coop(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -558,6 +657,7 @@ int run_coop(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const bf16* wp = static_cast<const bf16*>(L.wpack);
   a.x = L.x;
   a.o = static_cast<const bf16*>(L.q);
+  a.o_lo = static_cast<const bf16*>(L.q_lo);
   a.w_o = wp + qkv;
   a.w_1 = wp + qkv + dd;
   a.w_2 = wp + qkv + dd + (size_t)L.d_ff * d;
@@ -574,7 +674,7 @@ int run_coop(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   a.n_xcc = n_xcc;
   a.spin_limit = 1u << 22;
   a.eps = L.ln_eps;
-  auto k = ffn_coop_kernel<TX, TO, G>;
+  auto k = ffn_coop_kernel<TX, TO, G, SPLIT>;
   void* args[] = {&a};
   hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(n_xcc * per_xcc),
                                             dim3(512), args, 0, s);
@@ -588,8 +688,10 @@ int run_coop(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
 template <typename TX, typename TO>
 int dispatch_coop(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   switch (L.d_model) {
-    case 2048: return run_coop<TX, TO, 4>(L, s, err, n);
-    case 4096: return run_coop<TX, TO, 8>(L, s, err, n);
+    case 2048:
+      return L.split ? run_coop<TX, TO, 4, true>(L, s, err, n) : run_coop<TX, TO, 4, false>(L, s, err, n);
+    case 4096:
+      return L.split ? run_coop<TX, TO, 8, true>(L, s, err, n) : run_coop<TX, TO, 8, false>(L, s, err, n);
     default: break;
   }
   set_err(err, n, "no cooperative epilogue for d_model %s%d", "", L.d_model);

@@ -58,21 +58,22 @@ def hidden_rows(d, rows_pad):
     return min(rows_pad, max(4096, (2 ** 25 // d) // 256 * 256))
 
 
-def coop_exchange_bytes(d):
+def coop_exchange_bytes(d, split=False):
     """The cooperative epilogue's exchange regions (one per cluster of d / 512
     workgroups, 256 workgroups at most) and its counters: per cluster LN2(Y) of a
     128-row tile, two hidden chunks of 256 d / 512 units and the per-row partial
     statistics, 4 KB aligned; independent of the number of rows."""
     g = d // 512
     hc = 256 * g
-    region = 4 * (d // 16) * 1024 + 2 * 4 * (hc // 16) * 1024 + 2 * g * 128 * 8
+    na = 2 if split else 1                    # bf16 pairs: hi and lo halves
+    region = na * 4 * (d // 16) * 1024 + 2 * na * 4 * (hc // 16) * 1024 + 2 * g * 128 * 8
     region = (region + 4095) // 4096 * 4096
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     return up((256 // g) * region) + up((32 + 4 * 256) * 4)
 
 
 def is_coop(d, f, split):
-    return not split and d in (2048, 4096) and f % (256 * (d // 512)) == 0
+    return d in (2048, 4096) and f % (256 * (d // 512)) == 0
 
 
 def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=False, dkv=None):
@@ -83,7 +84,7 @@ def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=Fals
     rows_pad = up(used)
     f = 4 * d if d_ff is None else d_ff
     coop = is_coop(d, f, split)    # cooperative epilogue: an exchange region, nothing [rows, d_ff]
-    staged = (d > 1024 and not coop) or split  # staged: K, V^T over rows_pad rows + hidden block
+    staged = not coop and (d > 1024 or split)  # staged: K, V^T over rows_pad rows + hidden block
     dkv = d if dkv is None else dkv          # key/value width (grouped-query attention)
     tile = 128 if es == 4 else 256
     kvp = (dkv + tile - 1) // tile * tile    # K and V parts of the projection, padded
@@ -95,7 +96,7 @@ def expected_workspace(batch, n, d, es, stack_resid=False, d_ff=None, split=Fals
     hidden = up(hidden_rows(d, rows_pad) * f * es) if staged else 0
     tot = acts + up(((d + 2 * kvp) * d + d * d + 2 * d * f) * es) + hidden
     if coop:
-        tot += coop_exchange_bytes(d)
+        tot += coop_exchange_bytes(d, split)
     if split:                   # lo halves: no Y room there
         acts = 2 * up(rows_pad * d * es) + 2 * up(kv_rows * dkv * es)
     if split:                   # lo halves of the bf16 pairs
@@ -192,9 +193,10 @@ def test_workspace_is_block_shaped_not_ffn_shaped():
     ws = bpt.layer_workspace_bytes(bpt.desc_for(w))
     weights = (4 * w.d_model * w.d_model + 2 * w.d_model * w.d_ff) * 2
     nd = w.rows * w.d_model * 2
-    hidden_block = hidden_rows(w.d_model, w.rows) * w.d_ff * 2
-    assert ws - weights <= 2 * (4 * nd + hidden_block) + 16 * 256
-    assert hidden_block * 4 == w.rows * w.d_ff * 2      # 1/4 of the [N, d_ff] hidden
+    # the cooperative epilogue in bf16 pairs: no hidden block, a bounded exchange region
+    exchange = coop_exchange_bytes(w.d_model, split=True)
+    assert ws - weights <= 2 * 4 * nd + exchange + 16 * 256
+    assert exchange * 7 < w.rows * w.d_ff * 2           # under 1/7 of the [N, d_ff] hidden
 
 
 def call_layer(dsc, x=FAKE, z=FAKE + (1 << 36), ws=FAKE + (2 << 36), nbytes=1 << 40,
