@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the fused BPT layer forward on one MI355X.
 
-    python bench.py [--workload gpt2_medium] [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--workload long_128k] [--steps K] [--warmup W] [--gpus 1]
     python bench.py --attention-bwd [--workload gpt2_medium] ...
 
 A step is one bpt_layer_fwd (or bpt_stack_fwd) call over one batch of seeded
@@ -54,8 +54,8 @@ KERNEL_SOURCES = {
     "prep": ("k_pack.hip", "k_ln_qkv.hip", "ffn_stream.hpp", "bpt_device.hpp"),
     "qkv": ("k_gemm.hip", "bpt_device.hpp"),
     "attention": ("k_attention.hip", "bpt_device.hpp"),
-    "ffn_epilogue": ("k_ffn.hip", "k_gemm.hip", "k_ln_qkv.hip", "ffn_stream.hpp", "bpt_device.hpp",
-                     "bpt_internal.h"),
+    "ffn_epilogue": ("k_ffn.hip", "k_ffn_coop.hip", "k_gemm.hip", "k_ln_qkv.hip", "ffn_stream.hpp",
+                     "bpt_device.hpp", "bpt_internal.h"),
 }
 
 
@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt2_medium")
+    ap.add_argument("--workload", default="long_128k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attention-bwd", action="store_true",
@@ -123,18 +123,32 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from a committed counter summary, if still current."""
+def recorded_entry(tag: str, workload: str, kernel: str):
+    """A machine-readable entry <!-- tag {...} --> of a committed profile summary for
+    this workload and stage, if the stage's source files are unchanged since."""
     digest = source_digest(kernel)
-    pat = re.compile(r"<!--\s*traffic\s*(\{.*?\})\s*-->")
+    pat = re.compile(r"<!--\s*" + tag + r"\s*(\{.*?\})\s*-->")
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as f:
             for m in pat.finditer(f.read()):
                 e = json.loads(m.group(1))
                 if (e.get("workload") == workload and e.get("kernel") == kernel
                         and e.get("source_sha256") == digest):
-                    return int(e["fetch_bytes"]) + int(e["write_bytes"])
+                    return e
     return None
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch (rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated)."""
+    e = recorded_entry("traffic", workload, kernel)
+    return int(e["fetch_bytes"]) + int(e["write_bytes"]) if e else None
+
+
+def recorded_trace_ms(workload: str, kernel: str):
+    """Average duration (ms) of the stage's kernels per layer from a committed
+    rocprofv3 --kernel-trace --stats summary of the same bench command."""
+    e = recorded_entry("trace", workload, kernel)
+    return float(e["avg_ms"]) if e else None
 
 
 def cpu_baseline(w, inputs, target_s: float) -> dict:
@@ -488,19 +502,49 @@ def main():
         for e in ev:
             hip.destroy(e)
 
+    breakdown_note = None
+    if not single:
+        # Per-stage breakdown of a stack: after the timed steps, one profiled layer
+        # call per layer (its weights, the bf16 X, the stack's workspace) runs the
+        # same kernels on the same shapes; the stages are summed over the layers.
+        # Untimed as a whole; the stack's ms_per_step above is the timed figure.
+        n_prof = 2
+        pevs = [[[hip.event() for _ in range(5)] for _ in range(w.n_layers)] for _ in range(n_prof + 1)]
+        for rep_ in range(n_prof + 1):
+            for li in range(w.n_layers):
+                bpt.layer_fwd_profiled(desc, dev_x, dev_layers[li], z, ws, pevs[rep_][li], stream)
+        torch.cuda.synchronize()
+        for rep_ in range(1, n_prof + 1):          # the first pass is a warm-up
+            for li in range(w.n_layers):
+                for i, k in enumerate(KERNELS):
+                    per_kernel[k] += hip.elapsed_ms(pevs[rep_][li][i], pevs[rep_][li][i + 1]) / n_prof
+        for rep_ in pevs:
+            for lv in rep_:
+                for e in lv:
+                    hip.destroy(e)
+        breakdown_note = (f"stages from {n_prof} profiled passes of {w.n_layers} single-layer calls "
+                          "(same kernels and shapes as the stack), summed over the layers")
+
     total_flops = A.workload_flops(w.batch, w.seq_len, w.d_model, w.d_ff, w.causal, w.n_layers,
                                    w.window, w.chunk, w.d_kv)
     tflops = total_flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    kf = kernel_flops(w)
+    kf = {k: v * w.n_layers for k, v in kernel_flops(w).items()}   # per step (all layers)
     roofline = None
-    if single:
+    if any(v > 0 for v in per_kernel.values()):
         dom = max(KERNELS, key=lambda k: per_kernel[k])
         achieved = kf[dom] / (per_kernel[dom] * 1e-3) / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                     "traffic": recorded_traffic(w.name, dom), "traffic_unit": "bytes",
-                    "avg_ms": round(per_kernel[dom], 4), "flops_per_launch": kf[dom]}
+                    "avg_ms": round(per_kernel[dom], 4), "flops_per_launch": kf[dom],
+                    "launches_per_step": w.n_layers}
+        # the same stage's average duration in the committed kernel-trace summary
+        tr = recorded_trace_ms(w.name, dom)
+        if tr:
+            roofline.update({"trace_avg_ms": round(tr, 4),
+                             "trace_frac": round(kf[dom] / (tr * 1e-3) / 1e12 / peak, 4),
+                             "event_over_trace": round(per_kernel[dom] / tr, 4)})
     act_bytes = ws_bytes + dev_x.numel() * dev_x.element_size() + z.numel() * z.element_size()
     line = {
         "metric": METRIC,
@@ -532,6 +576,13 @@ def main():
                    "logits_one_head_bytes": w.batch * w.seq_len * w.seq_len * 2},
         "roofline": roofline,
     }
+    if breakdown_note:
+        line["kernel_ms_note"] = breakdown_note
+    if w.precision:
+        line["precision_note"] = ("bf16 pairs: each activation operand is hi + lo bf16, so the "
+                                  "projections and FFN run two matrix products and attention three "
+                                  "per algorithmic product; plain bf16 misses max|err| 2e-2 at this "
+                                  "width (the pages' tolerance), which is why the pairs are used")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)

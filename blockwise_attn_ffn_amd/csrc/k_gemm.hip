@@ -1,13 +1,15 @@
 // Matrix products of the layer on packed operands (gfx950): the QKV projection
-// and, for widths whose per-tile fp32 accumulator [rows, d] does not fit one
-// workgroup's registers (d = 4096), the staged epilogue W_O -> LN2 -> W_1 ->
-// GELU -> W_2.
+// and the row-block FFN (Y = X + O W_O, LN2, then per block of rows W_1 -> GELU
+// -> W_2), which serves the shapes neither fused epilogue takes: bf16 pairs up
+// to d_model 1024, and wide layers whose d_ff is not a multiple of the
+// cooperative epilogue's chunk.
 //
 // "Blockwise Parallel Transformer — BPT" (aicassindra.com), section "The fused
-// blockwise algorithm": q_i = LN(x_i) W_Q and k_j, v_j = LN(X[j]) W_K,
-// LN(X[j]) W_V (K and V are projected once for all rows instead of once per
-// inner-loop visit; the values are the same); y_i = x_i + (o/l) W_O,
-// h_i = act(LN(y_i) W_1), Z[i] = y_i + h_i W_2.
+// blockwise algorithm": the queries of a block come from its LN1 rows through
+// W_Q, its keys and values from LN1 of the key rows through W_K and W_V (here
+// projected once for all rows instead of once per inner-loop visit; the values
+// are the same), and a block is finished by W_O with the residual, LN, the FFN
+// and the second residual.
 //
 // One kernel, C^T = W A^T on packed fragments, 256 x 256 tiles (bf16: 8 waves,
 // two per SIMD, each 128 features x 64 rows), operands copied global -> LDS by

@@ -2,7 +2,7 @@
 // is in k_gemm.hip.
 //
 // "Blockwise Parallel Transformer — BPT" (aicassindra.com), section "The fused
-// blockwise algorithm": q_i = LN(x_i) W_Q and k_j, v_j = LN(X[j]) W_K, LN(X[j]) W_V.
+// blockwise algorithm": queries, keys and values are projections of the LN1 rows.
 // K and V are projected once for all rows instead of once per inner-loop visit;
 // the values are the same.
 //

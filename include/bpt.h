@@ -107,32 +107,46 @@ typedef struct {
   const void *ln2_g, *ln2_b, *w_1, *w_2;
 } bpt_layer_weights_t;
 
-/* Kernel instances exist for d_model 256, 512, 768, 1024, 2048 (BPT_BF16) and
- * 128, 256 (BPT_F32), head sizes 64 and 128, block_q and block_kv 64 or 128
+/* Kernel instances exist for d_model 256, 512, 768, 1024, 2048, 4096 (BPT_BF16)
+ * and 128, 256 (BPT_F32), head sizes 64 and 128, block_q and block_kv 64 or 128
  * (BPT_F32 with head size 128: block_kv 64), d_ff a multiple of 256. Any other
- * combination returns BPT_ERR_UNSUPPORTED before anything is enqueued. Batch and
- * sequence length are free; a sequence length that is not a multiple of the
- * block sizes gets a shorter last block. */
+ * combination returns BPT_ERR_UNSUPPORTED before anything is enqueued, and so
+ * does a shape whose matrix-product operands reach 4 GiB (e.g. 8 x 131072 tokens
+ * at d_model 2048). Batch and sequence length are free otherwise; a sequence
+ * length that is not a multiple of the block sizes gets a shorter last block.
+ * The FFN epilogue: d_model up to 1024 in bf16 (or fp32) finishes each row tile
+ * on one compute unit; d_model 2048 and 4096 (bf16, or bf16 pairs) finish tiles
+ * of 128 rows on clusters of d_model / 512 compute units that exchange the LN2
+ * operand and chunks of 256 d_model / 512 hidden units (d_ff must be a multiple
+ * of that chunk); other shapes (bf16 pairs up to d_model 1024, or a d_ff that is
+ * not such a multiple) run the FFN over blocks of rows, one GEMM at a time. */
 
 /* Bytes of workspace bpt_layer_fwd needs for *desc (0 for an empty call), or 0
- * with bpt_last_error() set when desc is invalid. Holds, in the compute type:
- * LN1(X) [rows rounded up to 256, d_model]; Q (reused for the attention
- * output), K and V^T, each [rows, d_model]; and a copy of the six projection
- * matrices repacked in matrix-core fragment order (4 d_model^2 + 2 d_model d_ff
- * elements). Nothing of size rows x d_ff or seq_len x seq_len is ever part of
- * it. The staged epilogue (d_model above 1024, or precision 1) adds one block
- * of the FFN hidden state, [h, d_ff] with h = 2^25 / d_model rounded down to a
- * multiple of 256, at least 4096 and at most rows rounded up to 256 (16384 rows
- * at d_model 2048), and keeps Y fp32 [rows, d_model] over the K and V^T space;
- * precision 1 doubles every activation buffer (the lo halves). */
+ * with bpt_last_error() set when desc is invalid ("Blockwise Parallel Transformer
+ * — BPT", section "Memory accounting: what actually shrinks": per layer only the
+ * residual-stream-shaped tensors and block-shaped tiles remain). Holds, in the
+ * compute type: LN1(X) [rows rounded up to 256, d_model]; Q (reused for the
+ * attention output), K and V^T, each [rows, d_model]; and a copy of the six
+ * projection matrices repacked in matrix-core fragment order (4 d_model^2 +
+ * 2 d_model d_ff elements). Nothing of size rows x d_ff or seq_len x seq_len is
+ * ever part of it. d_model 2048 and 4096 add the clusters' exchange regions,
+ * whose size does not depend on the rows: (256 / G) regions, G = d_model / 512,
+ * each holding LN2 of a 128-row tile [128, d_model], two hidden chunks [128,
+ * 256 G] and per-row statistics (about 64 MiB in all, twice that in bf16 pairs),
+ * plus 4 KiB of counters. The row-block FFN (see above) instead adds one block of
+ * the hidden state, [h, d_ff] with h = 2^25 / d_model rounded down to a multiple
+ * of 256, at least 4096 and at most rows rounded up to 256, and keeps Y fp32
+ * [rows, d_model] over the K and V^T space. precision 1 doubles every activation
+ * buffer (the lo halves). */
 size_t bpt_layer_workspace_bytes(const bpt_layer_desc_t* desc);
 /* With g = n_kv_heads key/value heads, K and V^T are [rows, g * d_head] and the
  * packed projection block is [d_model + 2 kvp, d_model] with kvp = g * d_head
  * rounded up to 256 (the K and V parts are padded to whole product tiles); on the
- * staged path the K and V^T space is at least the fp32 Y [rows, d_model]. */
+ * row-block FFN the K and V^T space is at least the fp32 Y [rows, d_model]. */
 
-/* Workspace of bpt_stack_fwd: the layer workspace, plus one fp32 residual
- * buffer [rows, d_model] when n_layers > 1 and out_dtype is not BPT_F32. */
+/* Workspace of bpt_stack_fwd (same section): the layer workspace, reused by
+ * every layer, plus one fp32 residual buffer [rows, d_model] when n_layers > 1
+ * and out_dtype is not BPT_F32. */
 size_t bpt_stack_workspace_bytes(const bpt_layer_desc_t* desc, int32_t n_layers);
 
 /* One layer: Z = layer(X). X and Z must not overlap; workspace must overlap
@@ -282,10 +296,13 @@ bpt_status_t bpt_attention_merge(const bpt_attn_desc_t* desc, float* O_acc, floa
 bpt_status_t bpt_layer_fwd_noalloc(const bpt_layer_desc_t* desc, const void* X,
                                    const bpt_layer_weights_t* weights, void* Z, void* hip_stream);
 
-/* n_layers >= 1 layers applied in turn, all with the shape of *desc; layers is
- * a HOST array of n_layers weight sets (each holding device pointers). Layer 0
- * reads X in desc->dtype; the residual stream between layers is fp32; the last
- * layer writes Z in desc->out_dtype. No final LN. */
+/* n_layers >= 1 layers applied in turn ("Blockwise Parallel Transformer — BPT",
+ * section "A worked example at 32k context": a model is a stack of such layers
+ * joined by the residual stream, and only that stream is sequence-shaped between
+ * them), all with the shape of *desc; layers is a HOST array of n_layers weight
+ * sets (each holding device pointers). Layer 0 reads X in desc->dtype; the
+ * residual stream between layers is fp32; the last layer writes Z in
+ * desc->out_dtype. No final LN. */
 bpt_status_t bpt_stack_fwd(const bpt_layer_desc_t* desc, int32_t n_layers, const void* X,
                            const bpt_layer_weights_t* layers, void* Z,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
