@@ -479,6 +479,85 @@ def stack_forward_rows(x: np.ndarray, layers: list, rows: np.ndarray, *, seq_len
 
 
 # ---------------------------------------------------------------------------
+# The layer's backward pass ([BPT] "The backward pass": gradients of the loss with
+# respect to the layer input and every parameter, the block's softmax rebuilt
+# from its saved statistics; here the plain definition, every intermediate held)
+# ---------------------------------------------------------------------------
+
+def layer_norm_backward(x: np.ndarray, gain: np.ndarray, dy: np.ndarray, eps: float):
+    """Gradients through y = LN(x) gain + bias given dy = dL/dy, row by row:
+    returns (dx, dgain, dbias). With xh = (x - mean) / sqrt(var + eps) and
+    g = dy gain: dx = (g - mean(g) - xh mean(g xh)) / sqrt(var + eps);
+    dgain = sum over rows of dy xh, dbias = sum over rows of dy."""
+    x = np.asarray(x, F64)
+    dy = np.asarray(dy, F64)
+    mean = x.mean(axis=-1, keepdims=True)
+    xc = x - mean
+    rstd = 1.0 / np.sqrt((xc * xc).mean(axis=-1, keepdims=True) + eps)
+    xh = xc * rstd
+    g = dy * np.asarray(gain, F64)
+    dx = rstd * (g - g.mean(axis=-1, keepdims=True) - xh * (g * xh).mean(axis=-1, keepdims=True))
+    return dx, (dy * xh).sum(axis=0), dy.sum(axis=0)
+
+
+def gelu_tanh_derivative(u: np.ndarray) -> np.ndarray:
+    """d/du of gelu_tanh: 0.5 (1 + tanh z) + 0.5 u (1 - tanh^2 z) dz/du with
+    z = c (u + 0.044715 u^3), c = sqrt(2/pi)."""
+    u = np.asarray(u, F64)
+    c = math.sqrt(2.0 / math.pi)
+    t = np.tanh(c * (u + 0.044715 * u ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * u * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * u * u)
+
+
+def layer_backward(x: np.ndarray, p: dict, dz: np.ndarray, *, seq_len: int, n_heads: int,
+                   causal: bool, eps: float = 1e-5) -> dict:
+    """Gradients of a loss L through one layer (layer_forward), given dz = dL/dZ.
+
+    Returns a dict with dx (= dL/dX) and, in the pages' (in, out) orientation of
+    the weights, dw_q, dw_k, dw_v, dw_o, dw_1, dw_2, and dln1_g, dln1_b, dln2_g,
+    dln2_b. Backwards through the forward's steps:
+      Z = Y + H W_2:                dY = dZ + (FFN part), dW_2 = H^T dZ, dH = dZ W_2^T
+      H = act(U), U = LN2(Y) W_1:   dU = dH act'(U), dW_1 = LN2(Y)^T dU, dLN2 = dU W_1^T
+      LN2:                          dY += LN backward of dLN2 (and the LN2 gain / bias)
+      Y = X + A W_O:                dX = dY + (attention part), dW_O = A^T dY, dA = dY W_O^T
+      attention (per sequence):     dQ, dK, dV = attention_backward_sequence(Q, K, V, dA)
+      Q, K, V = LN1(X) W_{Q,K,V}:   dW_Q = LN1(X)^T dQ (and K, V), dLN1 = sum dQ W_Q^T ...
+      LN1:                          dX += LN backward of dLN1 (and the LN1 gain / bias)
+    """
+    x = np.asarray(x, F64)
+    dz = np.asarray(dz, F64)
+    p = _as_f64_layer(p)
+    rows = x.shape[0]
+    assert rows % seq_len == 0 and dz.shape == x.shape
+    _z, parts = layer_forward(x, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps,
+                              return_parts=True)
+    x1, q, k, v, a, y = (parts[n] for n in ("x1", "q", "k", "v", "a", "y"))
+    y2 = layer_norm(y, p["ln2_g"], p["ln2_b"], eps)
+    u = y2 @ p["w_1"]
+    h = gelu_tanh(u)
+    g = {}
+    g["dw_2"] = h.T @ dz
+    du = (dz @ p["w_2"].T) * gelu_tanh_derivative(u)
+    g["dw_1"] = y2.T @ du
+    dy_ln, g["dln2_g"], g["dln2_b"] = layer_norm_backward(y, p["ln2_g"], du @ p["w_1"].T, eps)
+    dy = dz + dy_ln
+    g["dw_o"] = a.T @ dy
+    da = dy @ p["w_o"].T
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for s0 in range(0, rows, seq_len):
+        sl = slice(s0, s0 + seq_len)
+        dq[sl], dk[sl], dv[sl] = attention_backward_sequence(q[sl], k[sl], v[sl], da[sl], n_heads,
+                                                             causal)
+    g["dw_q"], g["dw_k"], g["dw_v"] = x1.T @ dq, x1.T @ dk, x1.T @ dv
+    dx1 = dq @ p["w_q"].T + dk @ p["w_k"].T + dv @ p["w_v"].T
+    dx_ln, g["dln1_g"], g["dln1_b"] = layer_norm_backward(x, p["ln1_g"], dx1, eps)
+    g["dx"] = dy + dx_ln
+    return g
+
+
+# ---------------------------------------------------------------------------
 # The blockwise form: softmax summaries of key tiles, merged ([BPT] fused
 # algorithm; [COST] two-tile running-sum example)
 # ---------------------------------------------------------------------------

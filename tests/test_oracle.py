@@ -994,3 +994,109 @@ def test_fused_pin_catches_a_merge_without_rescaling(monkeypatch):
     ref = O.layer_forward(x, p, seq_len=seq, n_heads=h, causal=True)
     got = O.blockwise_layer_forward(x, p, seq_len=seq, n_heads=h, causal=True, block_q=16, block_kv=8)
     assert O.rel_fro_err(got, ref) > 1e-6
+
+
+# --------------------------------------------------------------------------
+# The layer backward (block-recompute backward: the plain definition it must match)
+# --------------------------------------------------------------------------
+
+_GRAD_KEYS = ("dw_q", "dw_k", "dw_v", "dw_o", "dw_1", "dw_2", "dln1_g", "dln1_b", "dln2_g", "dln2_b")
+_PARAM_OF = {"dw_q": "w_q", "dw_k": "w_k", "dw_v": "w_v", "dw_o": "w_o", "dw_1": "w_1", "dw_2": "w_2",
+             "dln1_g": "ln1_g", "dln1_b": "ln1_b", "dln2_g": "ln2_g", "dln2_b": "ln2_b"}
+
+
+def torch_layer_grads(x, p, dz, seq_len, n_heads, causal, eps=1e-5):
+    """dL/dX and dL/dparam for L = sum(Z * dz), Z from the torch-built layer
+    (F.layer_norm, matmuls, scaled_dot_product_attention, gelu), by torch float64
+    autograd."""
+    t = {k: torch.tensor(np.asarray(v, np.float64), requires_grad=True) for k, v in p.items()}
+    xt = torch.tensor(np.asarray(x, np.float64), requires_grad=True)
+    rows, d = xt.shape
+    dk = d // n_heads
+    x1 = F.layer_norm(xt, (d,), t["ln1_g"], t["ln1_b"], eps)
+    split = lambda a: a.view(rows // seq_len, seq_len, n_heads, dk).transpose(1, 2)  # noqa: E731
+    a = F.scaled_dot_product_attention(split(x1 @ t["w_q"]), split(x1 @ t["w_k"]),
+                                       split(x1 @ t["w_v"]), is_causal=causal)
+    a = a.transpose(1, 2).reshape(rows, d)
+    y = xt + a @ t["w_o"]
+    h = F.gelu(F.layer_norm(y, (d,), t["ln2_g"], t["ln2_b"], eps) @ t["w_1"], approximate="tanh")
+    z = y + h @ t["w_2"]
+    (z * torch.from_numpy(np.asarray(dz, np.float64))).sum().backward()
+    out = {"dx": xt.grad.numpy()}
+    for gk, pk in _PARAM_OF.items():
+        out[gk] = t[pk].grad.numpy()
+    return out
+
+
+def _layer_bwd_pins(fn):
+    """True iff fn (layer_backward's signature) agrees with torch autograd (every
+    gradient, causal and not, random LN parameters) and with central finite
+    differences of L = sum(Z * dz) on sampled entries of X and of every parameter."""
+    rng = np.random.default_rng(81)
+    seq, b, d, h = 6, 2, 8, 2
+    for causal in (False, True):
+        x = rng.standard_normal((b * seq, d))
+        p = rand_layer(rng, d, 4 * d, std=0.5)
+        dz = rng.standard_normal((b * seq, d))
+        got = fn(x, p, dz, seq_len=seq, n_heads=h, causal=causal)
+        want = torch_layer_grads(x, p, dz, seq, h, causal)
+        for key in ("dx",) + _GRAD_KEYS:
+            if got[key].shape != want[key].shape or np.max(np.abs(got[key] - want[key])) > 1e-10:
+                return False
+    # finite differences on a few entries of each input (causal)
+    x = rng.standard_normal((seq, d))
+    p = rand_layer(rng, d, 4 * d, std=0.5)
+    dz = rng.standard_normal((seq, d))
+    got = fn(x, p, dz, seq_len=seq, n_heads=h, causal=True)
+    loss = lambda xx, pp: float((oracle.layer_forward(xx, pp, seq_len=seq, n_heads=h, causal=True) * dz).sum())  # noqa: E731
+    eps = 1e-6
+    for key in ("dx",) + _GRAD_KEYS:
+        base = x if key == "dx" else p[_PARAM_OF[key]]
+        for _ in range(3):
+            idx = tuple(int(rng.integers(0, n)) for n in base.shape)
+            bp, bm = base.copy(), base.copy()
+            bp[idx] += eps
+            bm[idx] -= eps
+            if key == "dx":
+                fd = (loss(bp, p) - loss(bm, p)) / (2 * eps)
+            else:
+                fd = (loss(x, dict(p, **{_PARAM_OF[key]: bp})) - loss(x, dict(p, **{_PARAM_OF[key]: bm}))) / (2 * eps)
+            if abs(fd - got[key][idx]) > 1e-6 * max(1.0, abs(fd)):
+                return False
+    return True
+
+
+def test_layer_backward_pins_hold_for_the_oracle():
+    assert _layer_bwd_pins(oracle.layer_backward)
+
+
+def test_layer_backward_pins_catch_planted_mistakes(monkeypatch):
+    """Each slip fails a pin: the LN backward without its mean(g xh) term, GELU's
+    derivative taken as the erf form's, W_1's gradient transposed into the wrong
+    product, the first residual's gradient dropped."""
+    def ln_no_second_term(x, gain, dy, eps):
+        x = np.asarray(x, np.float64)
+        xc = x - x.mean(axis=-1, keepdims=True)
+        rstd = 1.0 / np.sqrt((xc * xc).mean(axis=-1, keepdims=True) + eps)
+        g = dy * gain
+        return rstd * (g - g.mean(axis=-1, keepdims=True)), (dy * xc * rstd).sum(0), dy.sum(0)
+
+    def erf_derivative(u):
+        return 0.5 * (1 + scipy.special.erf(u / math.sqrt(2))) + u * np.exp(-u * u / 2) / math.sqrt(2 * math.pi)
+
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "layer_norm_backward", ln_no_second_term)
+        assert not _layer_bwd_pins(O.layer_backward), "ln backward"
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "gelu_tanh_derivative", erf_derivative)
+        assert not _layer_bwd_pins(O.layer_backward), "gelu derivative"
+
+    def w1_from_wrong_product(x, p, dz, **kw):
+        g = O.layer_backward(x, p, dz, **kw)
+        return dict(g, dw_1=g["dw_1"][::-1].copy())
+    assert not _layer_bwd_pins(w1_from_wrong_product)
+
+    def residual_dropped(x, p, dz, **kw):
+        g = O.layer_backward(x, p, dz, **kw)
+        return dict(g, dx=g["dx"] - np.asarray(dz, np.float64))
+    assert not _layer_bwd_pins(residual_dropped)
