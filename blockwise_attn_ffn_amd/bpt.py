@@ -20,7 +20,7 @@ EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer
             "bpt_attention_bwd_workspace_bytes", "bpt_attention_bwd",
             "bpt_attention_bwd_profiled", "bpt_attention_fwd_workspace_bytes", "bpt_attention_fwd",
             "bpt_attention_merge", "bpt_layer_host_workspace_bytes", "bpt_layer_fwd_host",
-            "bpt_layer_fwd_noalloc", "bpt_status_str",
+            "bpt_layer_fwd_noalloc", "bpt_layer_bwd_workspace_bytes", "bpt_layer_bwd", "bpt_status_str",
             "bpt_last_error", "bpt_version")
 
 
@@ -44,6 +44,10 @@ class AttnDesc(ctypes.Structure):
 
 
 class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class LayerGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
 
 
@@ -107,6 +111,12 @@ def lib() -> ctypes.CDLL:
         L.bpt_layer_fwd_noalloc.argtypes = [P(LayerDesc), ctypes.c_void_p, P(LayerWeights),
                                             ctypes.c_void_p, ctypes.c_void_p]
         L.bpt_layer_fwd_noalloc.restype = ctypes.c_int
+        L.bpt_layer_bwd_workspace_bytes.argtypes = [P(LayerDesc)]
+        L.bpt_layer_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.bpt_layer_bwd.argtypes = [P(LayerDesc), ctypes.c_void_p, P(LayerWeights), ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, P(LayerGrads), ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]
+        L.bpt_layer_bwd.restype = ctypes.c_int
         L.bpt_status_str.argtypes = [ctypes.c_int]
         L.bpt_status_str.restype = ctypes.c_char_p
         L.bpt_last_error.argtypes = []
@@ -205,6 +215,22 @@ def layer_fwd_lse(desc: LayerDesc, x, layer: dict, z, lse, workspace, stream=Non
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().bpt_layer_fwd_lse(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)),
                                    _ptr(z), _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def layer_bwd_workspace_bytes(desc: LayerDesc) -> int:
+    return lib().bpt_layer_bwd_workspace_bytes(ctypes.byref(desc))
+
+
+def layer_bwd(desc: LayerDesc, x, layer: dict, lse, dz, dx, grads: dict, workspace,
+              stream=None) -> None:
+    """Enqueue the layer backward: dX and every parameter's gradient (``grads``: fp32
+    tensors keyed like the weights, written) from X, the weights, the forward's lse
+    and dZ."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    g = LayerGrads(*[_ptr(grads[n]) for n in WEIGHT_FIELDS])
+    _check(lib().bpt_layer_bwd(ctypes.byref(desc), _ptr(x), ctypes.byref(_weights(layer)), _ptr(lse),
+                               _ptr(dz), _ptr(dx), ctypes.byref(g), _ptr(workspace), nbytes,
+                               _stream(stream)))
 
 
 def make_attn_desc(*, batch, seq_len, d_model, n_heads, causal, dtype="bf16", window=0, chunk=0,

@@ -663,6 +663,182 @@ bpt_status_t bpt_layer_fwd_host(const bpt_layer_desc_t* desc, const void* X,
   return BPT_OK;
 }
 
+namespace {
+
+// The backward's limits on top of the forward's (bpt_layer_bwd).
+bpt_status_t validate_bwd_desc(const bpt_layer_desc_t* d) {
+  bpt_status_t st = validate_desc(d);
+  if (st != BPT_OK) return st;
+  if (d->dtype != BPT_BF16) return fail(BPT_ERR_UNSUPPORTED, "the layer backward takes BPT_BF16 only");
+  if (d->precision != 0) return fail(BPT_ERR_UNSUPPORTED, "the layer backward computes at precision 0");
+  if (d->window || d->chunk) return fail(BPT_ERR_UNSUPPORTED, "the layer backward takes no window or chunk");
+  if (kv_heads(d) != d->n_heads)
+    return fail(BPT_ERR_UNSUPPORTED, "the layer backward takes no grouped key/value heads");
+  if ((size_t)d->batch * seq_pad_of(d) * (size_t)d->d_model >= ((size_t)1 << 31))
+    return fail(BPT_ERR_SHAPE, "batch * seq_len * d_model exceeds the 31-bit element index range");
+  return BPT_OK;
+}
+
+// Byte offsets of the backward's workspace pieces. Buffers that are dead by the
+// time a later one is written share its space: dA over dZ (bf16), dQ/dK/dV in
+// bf16 over Q, K, V, dQ over Y and dLN1 over dLN2 (fp32).
+struct BwdLayout {
+  size_t x1, q, k, v, attn, y2, dzb, dyb;   // bf16 [rows, d]
+  size_t y, dy2, dy, dk, dv;                // fp32 [rows, d]
+  size_t stats1, stats2, lse_re, stat_d, stat_l2, packed[3];
+  size_t ublk, hblk, dublk, partials, ln_part, total;
+  int block_rows, wgrad_splits, ln_parts;
+};
+
+BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
+  BwdLayout L{};
+  const size_t rows = (size_t)d->batch * d->seq_len, dm = d->d_model, f = d->d_ff;
+  const size_t np = seq_pad_of(d), bh = (size_t)d->batch * d->n_heads;
+  size_t r = (((size_t)1 << 25) / f) / 128 * 128;
+  if (r < 128) r = 128;
+  L.block_rows = (int)(r < rows ? r : rows);
+  const size_t tiles = ((dm + 127) / 128) * ((dm + 127) / 128);
+  size_t splits = (512 + tiles - 1) / tiles;
+  if (splits > 16) splits = 16;
+  if (splits > rows / 256) splits = rows / 256;
+  if (splits < 1) splits = 1;
+  L.wgrad_splits = (int)splits;
+  const size_t parts = (rows + 3) / 4;
+  L.ln_parts = (int)(parts < 512 ? parts : 512);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round_up(bytes, kAlign);
+    return o;
+  };
+  const size_t rb = rows * dm * 2, rf = rows * dm * 4;
+  L.x1 = take(rb); L.q = take(rb); L.k = take(rb); L.v = take(rb);
+  L.attn = take(rb); L.y2 = take(rb); L.dzb = take(rb); L.dyb = take(rb);
+  L.y = take(rf); L.dy2 = take(rf); L.dy = take(rf); L.dk = take(rf); L.dv = take(rf);
+  L.stats1 = take(rows * 8);
+  L.stats2 = take(rows * 8);
+  L.lse_re = take(bh * d->seq_len * 4);
+  L.stat_d = take(bh * np * 4);
+  L.stat_l2 = take(bh * np * 4);
+  for (int i = 0; i < 3; ++i) L.packed[i] = take((size_t)d->batch * np * dm * 2);
+  L.ublk = take((size_t)L.block_rows * f * 4);
+  L.hblk = take((size_t)L.block_rows * f * 2);
+  L.dublk = take((size_t)L.block_rows * f * 2);
+  L.partials = take(splits > 1 ? splits * dm * dm * 4 : 0);
+  L.ln_part = take((size_t)L.ln_parts * 2 * dm * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t bpt_layer_bwd_workspace_bytes(const bpt_layer_desc_t* desc) {
+  if (validate_bwd_desc(desc) != BPT_OK) return 0;
+  if (is_empty(desc)) return 0;
+  return bwd_layout(desc).total;
+}
+
+bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
+                           const bpt_layer_weights_t* weights, const float* lse, const float* dZ,
+                           float* dX, const bpt_layer_grads_t* grads, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_bwd_desc(desc);
+  if (st != BPT_OK) return st;
+  if (is_empty(desc)) return BPT_OK;
+  if ((st = validate_weights(weights, 0)) != BPT_OK) return st;
+  if (!grads) return fail(BPT_ERR_NULL, "grads is NULL");
+  const BwdLayout W = bwd_layout(desc);
+  const size_t rows = (size_t)desc->batch * desc->seq_len, dm = desc->d_model, f = desc->d_ff;
+  const size_t rd = rows * dm, dd = dm * dm, df = dm * f;
+  // every buffer: the inputs, then the outputs (dX, the gradients, the workspace)
+  const void* ptrs[24] = {X, weights->ln1_g, weights->ln1_b, weights->w_q, weights->w_k, weights->w_v,
+                          weights->w_o, weights->ln2_g, weights->ln2_b, weights->w_1, weights->w_2, lse,
+                          dZ, dX, grads->ln1_g, grads->ln1_b, grads->w_q, grads->w_k, grads->w_v,
+                          grads->w_o, grads->ln2_g, grads->ln2_b, grads->w_1, grads->w_2};
+  static const char* names[25] = {"X", "ln1_g", "ln1_b", "w_q", "w_k", "w_v", "w_o", "ln2_g", "ln2_b",
+                                  "w_1", "w_2", "lse", "dZ", "dX", "grads.ln1_g", "grads.ln1_b",
+                                  "grads.w_q", "grads.w_k", "grads.w_v", "grads.w_o", "grads.ln2_g",
+                                  "grads.ln2_b", "grads.w_1", "grads.w_2", "workspace"};
+  const size_t elems[24] = {rd, dm, dm, dd, dd, dd, dd, dm, dm, df, df,
+                            (size_t)desc->batch * desc->n_heads * desc->seq_len, rd, rd,
+                            dm, dm, dd, dd, dd, dd, dm, dm, df, df};
+  const void* all[25];
+  size_t bytes[25];
+  for (int i = 0; i < 24; ++i) {
+    all[i] = ptrs[i];
+    bytes[i] = elems[i] * (i <= 10 ? 2 : 4);
+  }
+  all[24] = workspace;
+  bytes[24] = W.total;
+  for (int i = 11; i < 25; ++i) {
+    if (!all[i]) return fail(BPT_ERR_NULL, "%s is NULL", names[i]);
+    if (!aligned16(all[i])) return fail(BPT_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  if (!X) return fail(BPT_ERR_NULL, "X is NULL");
+  if (!aligned16(X)) return fail(BPT_ERR_ALIGN, "X is not 16-byte aligned");
+  if (workspace_bytes < W.total)
+    return fail(BPT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, W.total);
+  for (int i = 13; i < 25; ++i)
+    for (int j = 0; j < 25; ++j)
+      if (j != i && overlap(all[i], bytes[i], all[j], bytes[j]))
+        return fail(BPT_ERR_ALIAS, "%s overlaps %s", names[i], names[j]);
+  char* ws = static_cast<char*>(workspace);
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  bpt::LayerBwdLaunch p{};
+  p.batch = desc->batch;
+  p.seq_len = desc->seq_len;
+  p.seq_pad = (int)seq_pad_of(desc);
+  p.d_model = desc->d_model;
+  p.n_heads = desc->n_heads;
+  p.d_ff = desc->d_ff;
+  p.causal = desc->causal;
+  p.rows = (int)rows;
+  p.ln_eps = desc->ln_eps;
+  p.block_rows = W.block_rows;
+  p.wgrad_splits = W.wgrad_splits;
+  p.ln_parts = W.ln_parts;
+  p.x = X;
+  p.w = *weights;
+  p.lse = lse;
+  p.dz = dZ;
+  p.dx = dX;
+  p.g = *grads;
+  p.x1 = ws + W.x1;
+  p.q = ws + W.q;
+  p.k = ws + W.k;
+  p.v = ws + W.v;
+  p.attn = ws + W.attn;
+  p.y2 = ws + W.y2;
+  p.dzb = ws + W.dzb;
+  p.dyb = ws + W.dyb;
+  p.da = ws + W.dzb;    // dZ (bf16) is dead once the FFN blocks are done
+  p.dqb = ws + W.q;     // Q, K, V are dead once the attention backward is done
+  p.dkb = ws + W.k;
+  p.dvb = ws + W.v;
+  p.hblk = ws + W.hblk;
+  p.dublk = ws + W.dublk;
+  p.ublk = F(W.ublk);
+  p.y = F(W.y);
+  p.dy2 = F(W.dy2);
+  p.dy = F(W.dy);
+  p.dq = F(W.y);        // Y is dead once the LN2 backward is done
+  p.dk = F(W.dk);
+  p.dv = F(W.dv);
+  p.dx1 = F(W.dy2);     // dLN2 is dead once the LN2 backward is done
+  p.stats1 = F(W.stats1);
+  p.stats2 = F(W.stats2);
+  p.lse_re = F(W.lse_re);
+  p.stat_d = F(W.stat_d);
+  p.stat_l2 = F(W.stat_l2);
+  for (int i = 0; i < 3; ++i) p.packed[i] = ws + W.packed[i];
+  p.partials = F(W.partials);
+  p.ln_part = F(W.ln_part);
+  char msg[256] = "";
+  if (bpt::launch_layer_bwd(p, hip_stream, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
+  return BPT_OK;
+}
+
 const char* bpt_status_str(bpt_status_t s) {
   switch (s) {
     case BPT_OK: return "ok";

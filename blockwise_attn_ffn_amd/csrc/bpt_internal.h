@@ -171,6 +171,35 @@ int launch_attention_merge(int batch, int seq_len, int n_heads, int d_head, floa
                            float* lse_acc, const void* o_part, const float* lse_part, void* stream,
                            char* err, size_t errlen);
 
+// Layer backward (k_layer_bwd.hip) after validation: device pointers; bf16
+// buffers are void*. Every [rows, d_model] buffer is row-major over the
+// batch * seq_len rows.
+struct LayerBwdLaunch {
+  int batch, seq_len, seq_pad, d_model, n_heads, d_ff, causal, rows;
+  float ln_eps;
+  int block_rows;     // FFN rows per block (the [block_rows, d_ff] hidden state)
+  int wgrad_splits;   // workgroup layers over the rows for the [d, d] weight gradients
+  int ln_parts;       // workgroups of the LN backward (column partial sums)
+  const void* x;      // bf16 [rows, d]
+  bpt_layer_weights_t w;
+  const float* lse;   // [batch, n_heads, seq_len]
+  const float* dz;    // fp32 [rows, d]
+  float* dx;          // fp32 [rows, d]
+  bpt_layer_grads_t g;
+  // workspace (see bpt_api.cpp: bwd_layout for sizes and the reuse of dead buffers)
+  void *x1, *q, *k, *v, *attn, *y2, *dzb, *dyb, *da, *dqb, *dkb, *dvb;   // bf16 [rows, d]
+  void *hblk, *dublk;   // bf16 [block_rows, d_ff]
+  float* ublk;          // fp32 [block_rows, d_ff]
+  float *y, *dy2, *dy, *dq, *dk, *dv, *dx1;   // fp32 [rows, d]
+  float *stats1, *stats2;   // (mean, rstd) per row: 2 floats each
+  float* lse_re;        // the recomputed forward's statistic (not used further)
+  float *stat_d, *stat_l2;   // attention backward row statistics [batch * n_heads, seq_pad]
+  void* packed[3];      // attention operands in fragment order, [batch * seq_pad, d] bf16 each
+  float* partials;      // split-k partial sums: wgrad_splits x [d, d]
+  float* ln_part;       // LN backward column partials: ln_parts x 2 x [d]
+};
+int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t errlen);
+
 // The host (CPU) fused layer: HOST pointers, fp32 arithmetic.
 struct HostLaunch {
   int batch, seq_len, d_model, n_heads, n_kv_heads, d_kv, d_ff, block_q, causal, window, chunk;

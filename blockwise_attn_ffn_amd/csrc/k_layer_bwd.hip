@@ -1,0 +1,560 @@
+// Backward pass of the BPT layer (gfx950): the block-recompute backward.
+//
+// "Blockwise Parallel Transformer — BPT" (aicassindra.com), section "The backward
+// pass": the forward keeps the layer input and each row's softmax statistics;
+// the backward recomputes the block's scores, attention output and FFN hidden
+// state from them and accumulates the gradients of every weight. Here:
+//   recompute  LN1(X), Q, K, V (row-major), the attention output A (the attention
+//              forward kernel), Y = X + A W_O^T, LN2(Y);
+//   FFN        per block of R rows: U = LN2(Y) W_1^T and H = GELU(U) (the block's
+//              [R, d_ff] hidden state, never more), dU = (dZ W_2) * GELU'(U),
+//              dW_2 += dZ^T H, dW_1 += dU^T LN2(Y), dLN2 = dU W_1;
+//   LN2        dY = dZ + LN2 backward of dLN2, and the LN2 gain / bias gradients;
+//   W_O        dA = dY W_O, dW_O = dY^T A;
+//   attention  dQ, dK, dV from the saved statistic lse (the attention backward);
+//   QKV        dLN1 = dQ W_Q + dK W_K + dV W_V, dW_{Q,K,V} = d{Q,K,V}^T LN1(X);
+//   LN1        dX = dY + LN1 backward of dLN1, and the LN1 gain / bias gradients.
+// Weights are [out, in] row-major, so y = x W^T; gradients come out in the same
+// layouts, in fp32. Matrix products take bf16 operands with fp32 accumulation.
+//
+// The products have every operand orientation, so they run on one general
+// kernel: C[M, N] = sum_k opA[m, k] opB[k, n] with either operand stored with k
+// contiguous or with m (n) contiguous, 128 x 128 tiles, k-tiles of 32 staged in
+// LDS (register-prefetched double buffer), v_mfma_f32_32x32x16_bf16, optional
+// split of k over workgroups (partial sums reduced in a fixed order), and
+// epilogues that fuse GELU, GELU' and residuals.
+#include <type_traits>
+
+#include "bpt_device.hpp"
+#include "bpt_launch.hpp"
+
+namespace bpt {
+
+enum BwdGemmMode {
+  kGStoreF32 = 0,   // C = acc (fp32)
+  kGAccF32 = 1,     // C += acc (fp32)
+  kGStoreBF16 = 2,  // C = bf16(acc)
+  kGResid = 3,      // C = R + acc (fp32 out; R fp32 or bf16)
+  kGGeluU = 4,      // U = acc (fp32), H = bf16(GELU(acc))
+  kGDGelu = 5,      // C = bf16(acc * GELU'(U))
+  kGPartial = 6     // P[z] = acc (split-k partial sums, fp32)
+};
+
+struct BwdGemm {
+  const bf16* a;   // opA[m, k] at a[m * lda + k] (A_KC) or a[k * lda + m]
+  const bf16* b;   // opB[k, n] at b[n * ldb + k] (B_KC) or b[k * ldb + n]
+  int lda, ldb;
+  int M, N, K;
+  int k_per_split; // multiple of 32; split z covers k in [z kps, (z + 1) kps)
+  void* c;         // output (C, H or P)
+  int ldc;
+  const void* r;   // residual (kGResid), or U (kGDGelu)
+  int ldr, r_f32;
+  float* u;        // kGGeluU: U output
+  int ldu;
+};
+
+// GELU (tanh form) and its derivative: with s = 1 / (1 + exp(-2 z)), z = sqrt(2/pi)
+// (u + 0.044715 u^3): GELU(u) = u s, GELU'(u) = s + 2 u s (1 - s) dz/du.
+__device__ inline float gelu_tanh_grad(float u) {
+  const float k = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  const float z = u * (1.0f + 0.044715f * u * u);
+  const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(k * z));
+  const float dz = 0.7978845608028654f * (1.0f + 3.0f * 0.044715f * u * u);
+  return sg + 2.0f * u * sg * (1.0f - sg) * dz;
+}
+
+namespace {
+
+constexpr int kGBM = 128, kGBN = 128, kGBK = 32;
+constexpr int kGLd = kGBK + 8;   // LDS row stride in elements (padding against bank conflicts)
+
+// One k-tile of an operand into registers: 512 chunks of 8 elements per 128 x 32
+// tile, two per thread. KC: a chunk is 8 consecutive k of one row (16-byte load);
+// otherwise 8 consecutive rows of one k (16-byte load, scattered into LDS later).
+template <bool KC>
+struct TileLoad {
+  uint4 v[2];
+  __device__ void load(const bf16* p, int ld, int rows, int K, int r0, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      if constexpr (KC) {
+        const int r = c >> 2, kc = (c & 3) * 8;
+        const int gr = r0 + r, gk = k0 + kc;
+        v[i] = (gr < rows && gk < K) ? *reinterpret_cast<const uint4*>(p + (size_t)gr * ld + gk)
+                                     : make_uint4(0, 0, 0, 0);
+      } else {
+        const int k = c >> 4, rc = (c & 15) * 8;
+        const int gk = k0 + k, gr = r0 + rc;
+        // rows are padded to a multiple of 8 by the caller's leading dimension check
+        v[i] = (gk < K && gr < rows) ? *reinterpret_cast<const uint4*>(p + (size_t)gk * ld + gr)
+                                     : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ void store(bf16* s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      if constexpr (KC) {
+        const int r = c >> 2, kc = (c & 3) * 8;
+        *reinterpret_cast<uint4*>(s + r * kGLd + kc) = v[i];
+      } else {
+        const int k = c >> 4, rc = (c & 15) * 8;
+        const bf16* e = reinterpret_cast<const bf16*>(&v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[(rc + j) * kGLd + k] = e[j];
+      }
+    }
+  }
+};
+
+}  // namespace
+
+// 256 threads = 4 waves in 2 x 2, each 64 x 64 of the tile (2 x 2 products of 32 x 32).
+template <bool A_KC, bool B_KC, int MODE>
+__global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm g) {
+  __shared__ __align__(16) bf16 As[2][kGBM * kGLd];
+  __shared__ __align__(16) bf16 Bs[2][kGBN * kGLd];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * kGBM, n0 = blockIdx.x * kGBN;
+  const int kb = blockIdx.z * g.k_per_split;
+  const int ke = min(g.K, kb + g.k_per_split);
+  const int nkt = ke > kb ? (ke - kb + kGBK - 1) / kGBK : 0;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  TileLoad<A_KC> la;
+  TileLoad<B_KC> lb;
+  if (nkt > 0) {
+    la.load(g.a, g.lda, g.M, ke, m0, kb, tid);
+    lb.load(g.b, g.ldb, g.N, ke, n0, kb, tid);
+    la.store(As[0], tid);
+    lb.store(Bs[0], tid);
+  }
+  __syncthreads();
+  for (int t = 0; t < nkt; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < nkt) {
+      la.load(g.a, g.lda, g.M, ke, m0, kb + (t + 1) * kGBK, tid);
+      lb.load(g.b, g.ldb, g.N, ke, n0, kb + (t + 1) * kGBK, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kGBK / 16; ++ks) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * 64 + i * 32 + (lane & 31)) * kGLd + ks * 16 +
+                                                        8 * (lane >> 5)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][(wn * 64 + j * 32 + (lane & 31)) * kGLd + ks * 16 +
+                                                         8 * (lane >> 5)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (t + 1 < nkt) {
+      la.store(As[cur ^ 1], tid);
+      lb.store(Bs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // C layout: lane l holds column l % 32; register q holds row 8 (q / 4) + 4 (l / 32) + q % 4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (m >= g.M) continue;
+        const float v = acc[i][j][q];
+        const size_t o = (size_t)m * g.ldc + n;
+        if constexpr (MODE == kGStoreF32) {
+          static_cast<float*>(g.c)[o] = v;
+        } else if constexpr (MODE == kGAccF32) {
+          static_cast<float*>(g.c)[o] += v;
+        } else if constexpr (MODE == kGStoreBF16) {
+          static_cast<bf16*>(g.c)[o] = (bf16)v;
+        } else if constexpr (MODE == kGResid) {
+          const size_t ro = (size_t)m * g.ldr + n;
+          const float r = g.r_f32 ? static_cast<const float*>(g.r)[ro] : (float)static_cast<const bf16*>(g.r)[ro];
+          static_cast<float*>(g.c)[o] = r + v;
+        } else if constexpr (MODE == kGGeluU) {
+          g.u[(size_t)m * g.ldu + n] = v;
+          static_cast<bf16*>(g.c)[o] = (bf16)gelu_tanh(v);
+        } else if constexpr (MODE == kGDGelu) {
+          const float u = static_cast<const float*>(g.r)[(size_t)m * g.ldr + n];
+          static_cast<bf16*>(g.c)[o] = (bf16)(v * gelu_tanh_grad(u));
+        } else {   // kGPartial
+          static_cast<float*>(g.c)[(size_t)blockIdx.z * g.M * g.N + (size_t)m * g.N + n] = v;
+        }
+      }
+    }
+}
+
+// C (fp32 [M, N], ldc) = [C +] sum over z of P[z] (the split-k partials, in order).
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(float* c, int ldc, const float* p, int M, int N,
+                                                         int splits, int accumulate) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)M * N) return;
+  const int m = (int)(t / N), n = (int)(t % N);
+  float s = accumulate ? c[(size_t)m * ldc + n] : 0.f;
+  for (int z = 0; z < splits; ++z) s += p[(size_t)z * M * N + t];
+  c[(size_t)m * ldc + n] = s;
+}
+
+// LN of each row (one wave per row, d <= 4096): out = bf16(LN(x) g + b), stats =
+// (mean, rstd).
+template <typename TX>
+__global__ __launch_bounds__(256) void bwd_ln_fwd_kernel(const TX* __restrict__ x, const bf16* __restrict__ gain,
+                                                         const bf16* __restrict__ bias, bf16* __restrict__ out,
+                                                         float2* __restrict__ stats, int rows, int d, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const TX* xr = x + (size_t)row * d;
+  float s = 0.f;
+  for (int c = lane * 8; c < d; c += 512) {
+    float v[8];
+    load8_f32(xr + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += v[e];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  const float mean = s / d;
+  float q = 0.f;
+  for (int c = lane * 8; c < d; c += 512) {
+    float v[8];
+    load8_f32(xr + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q += (v[e] - mean) * (v[e] - mean);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o, 64);
+  const float rstd = 1.0f / sqrtf(q / d + eps);
+  for (int c = lane * 8; c < d; c += 512) {
+    float v[8], gv[8], bv[8];
+    load8_f32(xr + c, v);
+    load8_f32(gain + c, gv);
+    load8_f32(bias + c, bv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (v[e] - mean) * rstd * gv[e] + bv[e];
+    store8_f32(out + (size_t)row * d + c, v);
+  }
+  if (lane == 0) stats[row] = make_float2(mean, rstd);
+}
+
+// LN backward of each row: out = resid + rstd (g - mean(g) - xh mean(g xh)),
+// g = dy * gain, xh = (x - mean) rstd; optionally a bf16 copy of out. Column
+// sums of dy xh and dy over the workgroup's rows go to part[blockIdx][2][d]
+// (summed in a fixed order afterwards). One wave per row, rows strided over the
+// workgroups; d <= 4096 (8 slabs of 512 columns, 8 per lane).
+template <typename TX>
+__global__ __launch_bounds__(256) void bwd_ln_bwd_kernel(const TX* __restrict__ x, const float2* __restrict__ stats,
+                                                         const bf16* __restrict__ gain, const float* __restrict__ dy,
+                                                         const float* __restrict__ resid, float* __restrict__ out,
+                                                         bf16* __restrict__ out_bf16, float* __restrict__ part,
+                                                         int rows, int d) {
+  __shared__ float red[4][2][512];     // per wave column partials of one 512-column slab
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float cg[8][8], cb[8][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cg[j][e] = cb[j][e] = 0.f;
+  for (int row = blockIdx.x * 4 + wave; row < rows; row += gridDim.x * 4) {
+    const float2 st = stats[row];
+    const TX* xr = x + (size_t)row * d;
+    const float* dr = dy + (size_t)row * d;
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = lane * 8 + 512 * j;
+      if (c < d) {
+        float xv[8], dv[8], gv[8];
+        load8_f32(xr + c, xv);
+        load8_f32(dr + c, dv);
+        load8_f32(gain + c, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (xv[e] - st.x) * st.y, gg = dv[e] * gv[e];
+          sg += gg;
+          sgx += gg * xh;
+          cg[j][e] += dv[e] * xh;
+          cb[j][e] += dv[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      sg += __shfl_xor(sg, o, 64);
+      sgx += __shfl_xor(sgx, o, 64);
+    }
+    sg /= d;
+    sgx /= d;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = lane * 8 + 512 * j;
+      if (c < d) {
+        float xv[8], dv[8], gv[8], rv[8], o8[8];
+        load8_f32(xr + c, xv);
+        load8_f32(dr + c, dv);
+        load8_f32(gain + c, gv);
+        load8_f32(resid + (size_t)row * d + c, rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (xv[e] - st.x) * st.y;
+          o8[e] = rv[e] + st.y * (dv[e] * gv[e] - sg - xh * sgx);
+        }
+        store8_f32(out + (size_t)row * d + c, o8);
+        if (out_bf16) store8_f32(out_bf16 + (size_t)row * d + c, o8);
+      }
+    }
+  }
+  // column partials: the four waves combine through LDS, slab by slab
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (512 * j >= d) break;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      red[wave][0][lane * 8 + e] = cg[j][e];
+      red[wave][1][lane * 8 + e] = cb[j][e];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 512; c += 256) {
+      const int col = 512 * j + c;
+      if (col < d) {
+        part[((size_t)blockIdx.x * 2 + 0) * d + col] = red[0][0][c] + red[1][0][c] + red[2][0][c] + red[3][0][c];
+        part[((size_t)blockIdx.x * 2 + 1) * d + col] = red[0][1][c] + red[1][1][c] + red[2][1][c] + red[3][1][c];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// dgain[c], dbias[c] = sum over the workgroups' partials, in order.
+__global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict__ part, int nparts, int d,
+                                                         float* __restrict__ dgain, float* __restrict__ dbias) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  float sg = 0.f, sb = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    sg += part[((size_t)p * 2 + 0) * d + c];
+    sb += part[((size_t)p * 2 + 1) * d + c];
+  }
+  dgain[c] = sg;
+  dbias[c] = sb;
+}
+
+// bf16 copy of an fp32 array (8 elements per thread; n a multiple of 8).
+__global__ __launch_bounds__(256) void bwd_cast_kernel(const float* __restrict__ in, bf16* __restrict__ out,
+                                                       long long n8) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n8) return;
+  float v[8];
+  load8_f32(in + t * 8, v);
+  store8_f32(out + t * 8, v);
+}
+
+namespace {
+
+template <bool A_KC, bool B_KC, int MODE>
+int run_bwd_gemm(const BwdGemm& g0, int splits, hipStream_t s, const char* what, char* err, size_t n) {
+  BwdGemm g = g0;
+  if (g.M <= 0 || g.N <= 0) return 0;
+  if (splits < 1) splits = 1;
+  g.k_per_split = ((g.K + splits - 1) / splits + kGBK - 1) / kGBK * kGBK;
+  splits = (g.K + g.k_per_split - 1) / g.k_per_split;
+  if (splits < 1) splits = 1;
+  dim3 grid((g.N + kGBN - 1) / kGBN, (g.M + kGBM - 1) / kGBM, splits);
+  hipLaunchKernelGGL((bwd_gemm_kernel<A_KC, B_KC, MODE>), grid, dim3(256), 0, s, g);
+  return check_launch(what, err, n);
+}
+
+// C (+)= opA opB with k split over `splits` workgroup layers into the partial
+// buffer, then reduced in order into C.
+template <bool A_KC, bool B_KC>
+int run_bwd_gemm_split(BwdGemm g, int splits, float* partials, bool accumulate, hipStream_t s,
+                       const char* what, char* err, size_t n) {
+  if (splits <= 1)
+    return accumulate ? run_bwd_gemm<A_KC, B_KC, kGAccF32>(g, 1, s, what, err, n)
+                      : run_bwd_gemm<A_KC, B_KC, kGStoreF32>(g, 1, s, what, err, n);
+  float* c = static_cast<float*>(g.c);
+  const int ldc = g.ldc;
+  g.c = partials;
+  g.k_per_split = ((g.K + splits - 1) / splits + kGBK - 1) / kGBK * kGBK;
+  const int used = (g.K + g.k_per_split - 1) / g.k_per_split;
+  if (run_bwd_gemm<A_KC, B_KC, kGPartial>(g, splits, s, what, err, n)) return 1;
+  const long long mn = (long long)g.M * g.N;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, c, ldc, partials,
+                     g.M, g.N, used, accumulate ? 1 : 0);
+  return check_launch("bwd_reduce", err, n);
+}
+
+int cast_bf16(const float* in, bf16* out, size_t count, hipStream_t s, char* err, size_t n) {
+  const long long n8 = (long long)(count / 8);
+  hipLaunchKernelGGL(bwd_cast_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, in, out, n8);
+  return check_launch("bwd_cast", err, n);
+}
+
+template <typename TX>
+int ln_bwd(const TX* x, const float2* stats, const bf16* gain, const float* dy, const float* resid, float* out,
+           bf16* out_bf16, float* part, int nparts, float* dgain, float* dbias, int rows, int d, hipStream_t s,
+           char* err, size_t n) {
+  hipLaunchKernelGGL(bwd_ln_bwd_kernel<TX>, dim3(nparts), dim3(256), 0, s, x, stats, gain, dy, resid, out, out_bf16,
+                     part, rows, d);
+  if (check_launch("bwd_ln_bwd", err, n)) return 1;
+  hipLaunchKernelGGL(bwd_colsum_kernel, dim3((d + 255) / 256), dim3(256), 0, s, part, nparts, d, dgain, dbias);
+  return check_launch("bwd_colsum", err, n);
+}
+
+}  // namespace
+
+int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int rows = L.rows, d = L.d_model, f = L.d_ff;
+  if (d % 64 != 0 || d > 4096 || f % 256 != 0 || L.block_rows < 1 || L.ln_parts < 1) {
+    set_err(err, n, "layer backward: inconsistent launch shape%s (d_model %d)", "", d);
+    return 1;
+  }
+  const size_t rd = (size_t)rows * d;
+  auto B = [](void* p) { return static_cast<bf16*>(p); };
+  auto CB = [](const void* p) { return static_cast<const bf16*>(p); };
+  const bf16* const x = CB(L.x);
+  const bf16* const wq = CB(L.w.w_q);
+  const bf16* const wk = CB(L.w.w_k);
+  const bf16* const wv = CB(L.w.w_v);
+  const bf16* const wo = CB(L.w.w_o);
+  const bf16* const w1 = CB(L.w.w_1);
+  const bf16* const w2 = CB(L.w.w_2);
+  bf16 *const x1 = B(L.x1), *const q = B(L.q), *const k = B(L.k), *const v = B(L.v);
+  bf16 *const attn = B(L.attn), *const y2 = B(L.y2), *const dzb = B(L.dzb), *const dyb = B(L.dyb);
+  bf16 *const hblk = B(L.hblk), *const dublk = B(L.dublk), *const da = B(L.da);
+  bf16* const dqkvb[3] = {B(L.dqb), B(L.dkb), B(L.dvb)};
+  const int wsplit = L.wgrad_splits;
+  float2* const stats1 = reinterpret_cast<float2*>(L.stats1);
+  float2* const stats2 = reinterpret_cast<float2*>(L.stats2);
+
+  // ---- recompute: LN1(X), Q, K, V, A, Y = X + A W_O^T, LN2(Y)
+  hipLaunchKernelGGL(bwd_ln_fwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, x, CB(L.w.ln1_g),
+                     CB(L.w.ln1_b), x1, stats1, rows, d, L.ln_eps);
+  if (check_launch("bwd_ln1", err, n)) return 1;
+  {
+    const bf16* ws[3] = {wq, wk, wv};
+    bf16* outs[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+      BwdGemm g{};
+      g.a = x1; g.lda = d; g.b = ws[i]; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = outs[i]; g.ldc = d;
+      if (run_bwd_gemm<true, true, kGStoreBF16>(g, 1, s, "bwd_qkv", err, n)) return 1;
+    }
+  }
+  {
+    AttnFwdLaunch a{};
+    a.batch = L.batch; a.seq_len = L.seq_len; a.seq_pad = L.seq_pad; a.d_model = d;
+    a.n_heads = L.n_heads; a.d_head = d / L.n_heads; a.causal = L.causal;
+    a.q = q; a.k = k; a.v = v; a.o = attn; a.lse = L.lse_re;
+    for (int i = 0; i < 3; ++i) a.packed[i] = L.packed[i];
+    if (launch_attention_fwd(a, stream, err, n)) return 1;
+  }
+  {
+    BwdGemm g{};
+    g.a = attn; g.lda = d; g.b = wo; g.ldb = d; g.M = rows; g.N = d; g.K = d;
+    g.c = L.y; g.ldc = d; g.r = x; g.ldr = d; g.r_f32 = 0;
+    if (run_bwd_gemm<true, true, kGResid>(g, 1, s, "bwd_wo_fwd", err, n)) return 1;
+  }
+  hipLaunchKernelGGL(bwd_ln_fwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, L.y, CB(L.w.ln2_g),
+                     CB(L.w.ln2_b), y2, stats2, rows, d, L.ln_eps);
+  if (check_launch("bwd_ln2", err, n)) return 1;
+  if (cast_bf16(L.dz, dzb, rd, s, err, n)) return 1;
+
+  // ---- FFN, one block of at most block_rows rows at a time
+  for (int r0 = 0; r0 < rows; r0 += L.block_rows) {
+    const int R = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
+    BwdGemm g{};
+    // U = LN2(Y) W_1^T, H = GELU(U)
+    g.a = y2 + (size_t)r0 * d; g.lda = d; g.b = w1; g.ldb = d; g.M = R; g.N = f; g.K = d;
+    g.c = hblk; g.ldc = f; g.u = L.ublk; g.ldu = f;
+    if (run_bwd_gemm<true, true, kGGeluU>(g, 1, s, "bwd_w1_fwd", err, n)) return 1;
+    // dU = (dZ W_2) * GELU'(U); W_2 is [d, d_ff]: opB[k = output feature, n = unit] at w2[k d_ff + n]
+    g = BwdGemm{};
+    g.a = dzb + (size_t)r0 * d; g.lda = d; g.b = w2; g.ldb = f; g.M = R; g.N = f; g.K = d;
+    g.c = dublk; g.ldc = f; g.r = L.ublk; g.ldr = f;
+    if (run_bwd_gemm<true, false, kGDGelu>(g, 1, s, "bwd_du", err, n)) return 1;
+    // dW_2 (+)= dZ^T H: opA[m = output feature, k = row] at dz[row d + m], opB[k = row, n = unit] at h[row d_ff + n]
+    g = BwdGemm{};
+    g.a = dzb + (size_t)r0 * d; g.lda = d; g.b = hblk; g.ldb = f; g.M = d; g.N = f; g.K = R;
+    g.c = L.g.w_2; g.ldc = f;
+    if (run_bwd_gemm_split<false, false>(g, 1, L.partials, r0 > 0, s, "bwd_dw2", err, n)) return 1;
+    // dW_1 (+)= dU^T LN2(Y)
+    g = BwdGemm{};
+    g.a = dublk; g.lda = f; g.b = y2 + (size_t)r0 * d; g.ldb = d; g.M = f; g.N = d; g.K = R;
+    g.c = L.g.w_1; g.ldc = d;
+    if (run_bwd_gemm_split<false, false>(g, 1, L.partials, r0 > 0, s, "bwd_dw1", err, n)) return 1;
+    // dLN2 = dU W_1; W_1 is [d_ff, d]: opB[k = unit, n = feature] at w1[k d + n]
+    g = BwdGemm{};
+    g.a = dublk; g.lda = f; g.b = w1; g.ldb = d; g.M = R; g.N = d; g.K = f;
+    g.c = L.dy2 + (size_t)r0 * d; g.ldc = d;
+    if (run_bwd_gemm<true, false, kGStoreF32>(g, 1, s, "bwd_dln2", err, n)) return 1;
+  }
+  // ---- LN2 backward: dY = dZ + LN2'(dLN2) (and a bf16 copy); LN2 gain / bias gradients
+  if (ln_bwd<float>(L.y, stats2, CB(L.w.ln2_g), L.dy2, L.dz, L.dy, dyb, L.ln_part, L.ln_parts, L.g.ln2_g,
+                    L.g.ln2_b, rows, d, s, err, n))
+    return 1;
+  // ---- W_O: dA = dY W_O, dW_O = dY^T A
+  {
+    BwdGemm g{};
+    g.a = dyb; g.lda = d; g.b = wo; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = da; g.ldc = d;
+    if (run_bwd_gemm<true, false, kGStoreBF16>(g, 1, s, "bwd_da", err, n)) return 1;
+    g = BwdGemm{};
+    g.a = dyb; g.lda = d; g.b = attn; g.ldb = d; g.M = d; g.N = d; g.K = rows; g.c = L.g.w_o; g.ldc = d;
+    if (run_bwd_gemm_split<false, false>(g, wsplit, L.partials, false, s, "bwd_dwo", err, n)) return 1;
+  }
+  // ---- attention backward from the saved statistic
+  {
+    AttnBwdLaunch a{};
+    a.batch = L.batch; a.seq_len = L.seq_len; a.d_model = d; a.n_heads = L.n_heads;
+    a.d_head = d / L.n_heads; a.causal = L.causal; a.n_kv_heads = L.n_heads; a.window = 0; a.chunk = 0;
+    a.seq_pad = L.seq_pad;
+    a.q = q; a.k = k; a.v = v; a.out = attn; a.dout = da; a.lse = L.lse;
+    a.dq = L.dq; a.dk = L.dk; a.dv = L.dv;
+    a.stat_d = L.stat_d; a.stat_l2 = L.stat_l2;
+    for (int i = 0; i < kAttnBwdPacked; ++i) a.packed[i] = L.packed[i];
+    if (launch_attention_bwd(a, stream, err, n)) return 1;
+  }
+  // ---- QKV: dLN1 = dQ W_Q + dK W_K + dV W_V, dW_{Q,K,V} = d{Q,K,V}^T LN1(X)
+  {
+    const float* dg[3] = {L.dq, L.dk, L.dv};
+    const bf16* ws[3] = {wq, wk, wv};
+    float* dw[3] = {L.g.w_q, L.g.w_k, L.g.w_v};
+    for (int i = 0; i < 3; ++i) {
+      if (cast_bf16(dg[i], dqkvb[i], rd, s, err, n)) return 1;
+      BwdGemm g{};
+      g.a = dqkvb[i]; g.lda = d; g.b = ws[i]; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = L.dx1; g.ldc = d;
+      if (i == 0 ? run_bwd_gemm<true, false, kGStoreF32>(g, 1, s, "bwd_dx1", err, n)
+                 : run_bwd_gemm<true, false, kGAccF32>(g, 1, s, "bwd_dx1", err, n))
+        return 1;
+      g = BwdGemm{};
+      g.a = dqkvb[i]; g.lda = d; g.b = x1; g.ldb = d; g.M = d; g.N = d; g.K = rows; g.c = dw[i]; g.ldc = d;
+      if (run_bwd_gemm_split<false, false>(g, wsplit, L.partials, false, s, "bwd_dwqkv", err, n)) return 1;
+    }
+  }
+  // ---- LN1 backward: dX = dY + LN1'(dLN1); LN1 gain / bias gradients
+  return ln_bwd<bf16>(x, stats1, CB(L.w.ln1_g), L.dx1, L.dy, L.dx, nullptr, L.ln_part, L.ln_parts, L.g.ln1_g,
+                      L.g.ln1_b, rows, d, s, err, n);
+}
+
+}  // namespace bpt

@@ -201,3 +201,18 @@ def make_attention_inputs(batch: int, seq_len: int, d_model: int, seed: int = 0,
         keep[torch.from_numpy(np.asarray(live_rows, np.int64))] = True
         do[~keep] = 0
     return {"q": q, "k": k, "v": v, "do": do}
+
+
+def make_grad_output(rows: int, d_model: int, seed: int = 0,
+                     live_rows: np.ndarray | None = None) -> torch.Tensor:
+    """Draw dZ (the gradient of a loss with respect to a layer's output) on the CPU:
+    fp32 [rows, d_model], N(0, 1). live_rows, if given, keeps dZ only on those rows
+    and zeroes the rest."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed + 7919)
+    dz = _draw(gen, (rows, d_model), 1.0, 0.0, torch.float32)
+    if live_rows is not None:
+        keep = torch.zeros(rows, dtype=torch.bool)
+        keep[torch.from_numpy(np.asarray(live_rows, np.int64))] = True
+        dz[~keep] = 0
+    return dz

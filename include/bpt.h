@@ -307,6 +307,57 @@ bpt_status_t bpt_stack_fwd(const bpt_layer_desc_t* desc, int32_t n_layers, const
                            const bpt_layer_weights_t* layers, void* Z,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Gradients of one layer's parameters: DEVICE pointers, fp32, each with the shape
+ * and layout of the weight it belongs to (w_q, w_k, w_v, w_o [d_model, d_model],
+ * w_1 [d_ff, d_model], w_2 [d_model, d_ff], all [out, in] row-major; the LN gains
+ * and biases [d_model]). */
+typedef struct {
+  float *ln1_g, *ln1_b, *w_q, *w_k, *w_v, *w_o;
+  float *ln2_g, *ln2_b, *w_1, *w_2;
+} bpt_layer_grads_t;
+
+/* Bytes of workspace bpt_layer_bwd needs for *desc (0 for an empty call), or 0
+ * with bpt_last_error() set when desc is invalid or outside the backward's limits
+ * (see bpt_layer_bwd). With rows = batch * seq_len and Np = seq_len rounded up to
+ * 128, it holds: bf16 [rows, d_model] copies of LN1(X), Q, K, V, the attention
+ * output A, LN2(Y), dZ, dY, dQ/dK/dV (over Q, K, V once they are dead); fp32
+ * [rows, d_model] Y (then dQ), dLN2 (then dLN1), dY, dK, dV; per-row LN
+ * statistics; the attention operands in fragment order (3 x [batch * Np,
+ * d_model] bf16) and its row statistics; one FFN block: U fp32, H and dU bf16,
+ * each [r, d_ff] with r = min(rows, 2^25 / d_ff); split-k partial sums (up to 16
+ * x [d_model, d_model] fp32) and the LN column partials. The only d_ff-wide
+ * buffers are the block's: nothing of size rows x d_ff or seq_len x seq_len. */
+size_t bpt_layer_bwd_workspace_bytes(const bpt_layer_desc_t* desc);
+
+/* Backward of one layer (bpt_layer_fwd's computation) by block recomputation.
+ * "Blockwise Parallel Transformer — BPT" (aicassindra.com), section "The backward
+ * pass": the forward keeps the layer input and each attention row's softmax
+ * statistic; the backward recomputes what it needs from them (LN1(X), Q, K, V,
+ * the attention output, Y and LN2(Y) here; each block's softmax inside the
+ * attention backward; the FFN hidden state one block of rows at a time) while
+ * the gradients of the weights accumulate. Given dZ = dL/dZ for a loss L:
+ *  - dX = dL/dX (fp32 [rows, d_model], written);
+ *  - grads: every parameter's gradient (bpt_layer_grads_t, written, not added to).
+ * Arguments:
+ *  - X, weights: the forward's input and parameters (DEVICE, bf16, layouts of
+ *    bpt_layer_fwd).
+ *  - lse: DEVICE fp32 [batch, n_heads, seq_len], the statistic bpt_layer_fwd_lse
+ *    wrote for this X and these weights.
+ *  - dZ: DEVICE fp32 [rows, d_model].
+ * Limits (else BPT_ERR_UNSUPPORTED before anything is enqueued): dtype BPT_BF16,
+ * precision 0, window = chunk = 0, n_kv_heads 0 or n_heads; every other shape
+ * bpt_layer_fwd takes (block_q, block_kv and out_dtype do not matter here).
+ * Products take bf16 operands (activations and gradients rounded to bf16 where
+ * they enter a product) with fp32 accumulation; the weight gradients sum over the
+ * rows in a fixed order, so repeated calls give identical bits. Every device
+ * pointer 16-byte aligned (BPT_ERR_ALIGN), none NULL (BPT_ERR_NULL); dX, the
+ * gradients and the workspace overlap no other buffer (BPT_ERR_ALIAS).
+ * Asynchronous on hip_stream. */
+bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
+                           const bpt_layer_weights_t* weights, const float* lse, const float* dZ,
+                           float* dX, const bpt_layer_grads_t* grads, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
+
 /* Static text for a status code. */
 const char* bpt_status_str(bpt_status_t status);
 

@@ -38,6 +38,13 @@ int launch_attention_merge(int, int, int, int, float*, float*, const void*, cons
   ++g_merge_launches;
   return 0;
 }
+static int g_layer_bwd_launches = 0;
+static LayerBwdLaunch g_layer_bwd;
+int launch_layer_bwd(const LayerBwdLaunch& L, void*, char*, size_t) {
+  g_layer_bwd = L;
+  ++g_layer_bwd_launches;
+  return 0;
+}
 // the no-allocation entry point's fixed scratch: a fake device address
 static int g_scratch_queries = 0;
 int noalloc_scratch(void** ptr, char*, size_t) {
@@ -275,6 +282,35 @@ int main() {
     EXPECT(bpt_layer_fwd_host(&hd, x.data(), &hw, x.data(), ws.data(), nb, 3) == BPT_ERR_ALIAS);
     EXPECT(bpt_layer_fwd_host(&hd, x.data(), nullptr, z.data(), ws.data(), nb, 3) == BPT_ERR_NULL);
     EXPECT(bpt_layer_host_workspace_bytes(&hd, 0) == 0);
+  }
+  // the layer backward: a valid call reaches its launcher with the carved workspace
+  {
+    bpt_layer_desc_t bd = d;
+    bpt_layer_grads_t g;
+    float** gp = reinterpret_cast<float**>(&g);
+    for (int i = 0; i < 10; ++i) gp[i] = reinterpret_cast<float*>(fake((7ull << 36) + (uint64_t)i * (1ull << 30)));
+    float* blse = reinterpret_cast<float*>(fake(3ull << 35));
+    const float* dz = reinterpret_cast<const float*>(fake(9ull << 36));
+    float* dx = reinterpret_cast<float*>(fake(10ull << 36));
+    const size_t nb = bpt_layer_bwd_workspace_bytes(&bd);
+    EXPECT(nb > 0);
+    char* bws = fake(11ull << 36);
+    EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, dx, &g, bws, nb, nullptr) == BPT_OK);
+    EXPECT(bpt::g_layer_bwd_launches == 1);
+    const bpt::LayerBwdLaunch& L = bpt::g_layer_bwd;
+    EXPECT(L.rows == 400 && L.seq_pad == 256 && L.block_rows == 400 && L.wgrad_splits == 1);
+    EXPECT(L.x1 == bws && L.lse == blse && L.dz == dz && L.dx == dx && L.g.w_2 == g.w_2);
+    EXPECT((char*)L.ln_part + (size_t)L.ln_parts * 2 * 256 * 4 <= bws + nb);
+    EXPECT(L.dq == L.y && L.dx1 == L.dy2 && L.da == L.dzb && L.dqb == L.q);
+    EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, dx, &g, bws, nb - 1, nullptr) == BPT_ERR_WORKSPACE);
+    EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, dx, nullptr, bws, nb, nullptr) == BPT_ERR_NULL);
+    EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, reinterpret_cast<float*>(fake(9ull << 36) + 64), &g,
+                         bws, nb, nullptr) == BPT_ERR_ALIAS);
+    g.w_o = reinterpret_cast<float*>(fake(3ull << 36));   // over the forward's w_q
+    EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, dx, &g, bws, nb, nullptr) == BPT_ERR_ALIAS);
+    bd.precision = 1;
+    EXPECT(bpt_layer_bwd_workspace_bytes(&bd) == 0);
+    EXPECT(bpt::g_layer_bwd_launches == 1);
   }
   if (!g_fail) printf("ALL OK\n");
   return g_fail;

@@ -346,3 +346,60 @@ def test_noalloc_rejects_without_touching_a_device():
     ok = desc()
     assert lib.bpt_layer_fwd_noalloc(ctypes.byref(ok), None, ctypes.byref(w), FAKE + (1 << 36), None) == 1
     assert lib.bpt_layer_fwd_noalloc(ctypes.byref(ok), FAKE, None, FAKE + (1 << 36), None) == 1
+
+
+def bwd_call(dsc, nbytes=None, **over):
+    """bpt_layer_bwd on fake, disjoint pointers (validation only)."""
+    lib = bpt.lib()
+    w = bpt.LayerWeights(*[FAKE + (3 << 36) + i * (1 << 30) for i in range(10)])
+    g = bpt.LayerGrads(*[FAKE + (7 << 36) + i * (1 << 30) for i in range(10)])
+    args = dict(x=FAKE, lse=FAKE + (1 << 35), dz=FAKE + (9 << 36), dx=FAKE + (10 << 36),
+                ws=FAKE + (11 << 36))
+    args.update(over)
+    if nbytes is None:
+        nbytes = 1 << 40
+    return lib.bpt_layer_bwd(ctypes.byref(dsc), args["x"], ctypes.byref(w), args["lse"], args["dz"],
+                             args["dx"], ctypes.byref(g), args["ws"], nbytes, None)
+
+
+@pytest.mark.parametrize("field,value", [("dtype", bpt.F32), ("precision", 1), ("window", 16),
+                                         ("chunk", 64), ("n_kv_heads", 2)])
+def test_layer_bwd_limits(field, value):
+    """The backward takes bf16 at precision 0, with no window, chunk or grouped heads:
+    anything else is BPT_ERR_UNSUPPORTED (nothing enqueued) and a workspace of 0."""
+    dsc = desc()
+    setattr(dsc, field, value)
+    if field == "dtype":
+        dsc.out_dtype = bpt.F32
+    assert bpt.layer_bwd_workspace_bytes(dsc) == 0
+    assert bwd_call(dsc) == 3
+    assert bpt.last_error() != ""
+
+
+def test_layer_bwd_null_alignment_alias():
+    dsc = desc()
+    need = bpt.layer_bwd_workspace_bytes(dsc)
+    assert need > 0
+    assert bwd_call(dsc, nbytes=need - 1) == 5
+    assert bwd_call(dsc, lse=0) == 1 and "lse" in bpt.last_error()
+    assert bwd_call(dsc, dz=FAKE + (9 << 36) + 4) == 4
+    assert bwd_call(dsc, x=0) == 1
+    assert bwd_call(dsc, dx=FAKE + (9 << 36) + 256) == 6          # dX over dZ
+    assert bwd_call(dsc, ws=FAKE + (3 << 36) - 4096) == 6          # workspace over w_q
+    empty = desc(batch=0)
+    assert bpt.lib().bpt_layer_bwd(ctypes.byref(empty), None, None, None, None, None, None, None, 0,
+                                   None) == 0
+
+
+def test_layer_bwd_workspace_has_no_rows_by_d_ff_term():
+    """The backward's workspace grows with the rows by the same amount whatever d_ff
+    is, once the rows exceed the FFN block (2^25 / d_ff rows): only the block's
+    [block, d_ff] buffers depend on d_ff, never rows x d_ff ("The backward pass":
+    the hidden state is recomputed one block at a time)."""
+    def ws(batch, d_ff):
+        return bpt.layer_bwd_workspace_bytes(desc(batch=batch, seq_len=4096, d_model=1024,
+                                                  n_heads=16, d_ff=d_ff))
+    growth = {f: ws(8, f) - ws(4, f) for f in (2048, 4096, 8192, 16384)}
+    assert len(set(growth.values())) == 1, growth
+    # per extra row: 8 bf16 and 5 fp32 [d] vectors, 3 bf16 attention copies, statistics
+    assert growth[4096] <= 4 * 4096 * (1024 * (8 * 2 + 5 * 4 + 3 * 2) + 16 + 16 * 3 * 4) + 64 * 256
