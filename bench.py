@@ -64,11 +64,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long_128k")
+    ap.add_argument("--workload", default=None,
+                    help="default: long_128k (the layer forward and --ring), gpt2_medium "
+                         "(--attention-bwd, --layer-bwd), slm_1b_4k (--host)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attention-bwd", action="store_true",
                     help="time the attention backward on the workload's attention shape")
+    ap.add_argument("--layer-bwd", action="store_true",
+                    help="time the layer backward (bpt_layer_bwd) on the workload's layer shape")
     ap.add_argument("--ring", type=int, default=0,
                     help="time one device's share of Ring Attention over this many devices "
                          "(default workload long_128k: shards of seq_len / devices tokens)")
@@ -314,6 +318,74 @@ def bench_attention_bwd(args, w):
     print(json.dumps(line), flush=True)
 
 
+def bench_layer_bwd(args, w):
+    """The layer backward: one forward with lse (untimed), W warm-up backward calls,
+    then K timed calls, each writing dX and every parameter gradient."""
+    import torch
+    from blockwise_attn_ffn_amd import accounting as A, bpt, synth
+
+    assert w.n_layers == 1
+    inputs = synth.make_inputs(w, seed=args.seed)
+    dev = {"x": inputs["x"].cuda(), "layer": {k: t.cuda() for k, t in inputs["layers"][0].items()}}
+    desc = bpt.desc_for(w, out_dtype="f32")
+    z = torch.empty((w.rows, w.d_model), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.n_heads, w.seq_len), dtype=torch.float32, device="cuda")
+    ws = bpt.alloc_workspace(bpt.layer_workspace_bytes(desc))
+    bpt.layer_fwd_lse(desc, dev["x"], dev["layer"], z, lse, ws)
+    torch.cuda.synchronize()
+    del ws
+    dz = synth.make_grad_output(w.rows, w.d_model, seed=args.seed).cuda()
+    dx = torch.empty_like(dz)
+    grads = {k: torch.empty(t.shape, dtype=torch.float32, device="cuda") for k, t in dev["layer"].items()}
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    ws_bytes = bpt.layer_bwd_workspace_bytes(desc)
+    bws = bpt.alloc_workspace(ws_bytes)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bpt.layer_bwd(desc, dev["x"], dev["layer"], lse, dz, dx, grads, bws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    peak_extra = torch.cuda.max_memory_allocated() - base
+    n, d, f = w.seq_len, w.d_model, w.d_ff
+    flops = w.batch * A.layer_bwd_flops(n, d, f, w.causal)
+    executed = flops + w.batch * A.layer_flops(n, d, f, w.causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    block_rows = min(w.rows, max(128, ((1 << 25) // f) // 128 * 128))
+    line = {
+        "metric": "layer backward TFLOP/s (1 MI355X) + % bf16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian X, weights, dZ)",
+        "config": {"workload": w.name + " layer backward", "batch": w.batch, "seq_len": n,
+                   "d_model": d, "n_heads": w.n_heads, "d_ff": f, "causal": w.causal,
+                   "parallelism": "none"},
+        "pct_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2), "flops_per_step": flops,
+        "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 2),
+        "flops_note": "value counts the backward's products (2x the forward's dense products, "
+                      "2.5x its attention products); executed_tflops adds the forward recomputed "
+                      "from X and lse",
+        "memory": {"workspace_bytes": ws_bytes, "peak_allocated_during_backward": int(peak_extra),
+                   "ffn_block_rows": block_rows,
+                   "largest_d_ff_wide_buffer_bytes": block_rows * f * 4,
+                   "rows_x_d_ff_bf16_bytes": w.rows * f * 2},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_host(args, w):
     """The host (CPU) fused layer: W warm-up calls, then K timed calls (wall clock)."""
     import torch
@@ -425,11 +497,11 @@ def main():
         if not torch.cuda.is_available():
             print(json.dumps({"error": "no GPU visible"}))
             sys.exit(1)
-        wl = args.workload if args.workload != "gpt2_medium" else "long_128k"
+        wl = args.workload or "long_128k"
         return bench_ring(args, synth.WORKLOADS[wl], args.ring)
     if args.host:
         from blockwise_attn_ffn_amd import synth
-        wl = args.workload if args.workload != "gpt2_medium" else "slm_1b_4k"
+        wl = args.workload or "slm_1b_4k"
         return bench_host(args, synth.WORKLOADS[wl])
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1",
@@ -441,7 +513,14 @@ def main():
         if not torch.cuda.is_available():
             print(json.dumps({"error": "no GPU visible"}))
             sys.exit(1)
-        return bench_attention_bwd(args, synth.WORKLOADS[args.workload])
+        return bench_attention_bwd(args, synth.WORKLOADS[args.workload or "gpt2_medium"])
+    if args.layer_bwd:
+        import torch
+        from blockwise_attn_ffn_amd import synth
+        if not torch.cuda.is_available():
+            print(json.dumps({"error": "no GPU visible"}))
+            sys.exit(1)
+        return bench_layer_bwd(args, synth.WORKLOADS[args.workload or "gpt2_medium"])
 
     import torch
     from blockwise_attn_ffn_amd import accounting as A, bpt, synth
@@ -449,7 +528,7 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[args.workload or "long_128k"]
     torch.cuda.init()
     free_start, total_mem = torch.cuda.mem_get_info()
 

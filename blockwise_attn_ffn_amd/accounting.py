@@ -64,6 +64,15 @@ def layer_flops(n: int, d: int, d_ff: int, causal: bool, window: int = 0, chunk:
             + ffn_flops(n, d, d_ff))
 
 
+def layer_bwd_flops(n: int, d: int, d_ff: int, causal: bool) -> int:
+    """Backward of one layer on one sequence, without recomputation: each dense
+    product y = x W has two in the backward (dx = dy W^T and dW = x^T dy), twice the
+    forward's projection and FFN FLOPs; the attention backward is attention_bwd_flops.
+    (The block-recompute backward also runs the forward's products once more:
+    layer_flops on top of this.)"""
+    return 2 * (projection_flops(n, d) + ffn_flops(n, d, d_ff)) + attention_bwd_flops(n, d, causal)
+
+
 def workload_flops(batch: int, n: int, d: int, d_ff: int, causal: bool, n_layers: int = 1,
                    window: int = 0, chunk: int = 0, d_kv: int | None = None) -> int:
     return batch * n_layers * layer_flops(n, d, d_ff, causal, window, chunk, d_kv)

@@ -94,3 +94,11 @@ def test_projection_flops_with_grouped_kv_heads():
     assert A.projection_flops(n, d) == 8 * n * d * d
     assert A.projection_flops(n, d, 256) == 4 * n * d * d + 4 * n * d * 256
     assert A.layer_flops(n, d, 4 * d, True, d_kv=d) == A.layer_flops(n, d, 4 * d, True)
+
+
+def test_layer_bwd_flops_closed_form():
+    """Backward without recompute: 48 N d^2 dense at d_ff = 4d (twice the forward's
+    24 N d^2) plus 2.5 times the attention's 2 d N (N + 1) (causal)."""
+    n, d = 1024, 1024
+    assert A.layer_bwd_flops(n, d, 4 * d, True) == 48 * n * d * d + 5 * d * n * (n + 1)
+    assert A.layer_bwd_flops(n, d, 4 * d, False) == 48 * n * d * d + 10 * n * n * d
