@@ -681,13 +681,15 @@ bpt_status_t validate_bwd_desc(const bpt_layer_desc_t* d) {
 
 // Byte offsets of the backward's workspace pieces. Buffers that are dead by the
 // time a later one is written share its space: dA over dZ (bf16), dQ/dK/dV in
-// bf16 over Q, K, V, dQ over Y and dLN1 over dLN2 (fp32).
+// bf16 over Q, K, V, dQ over Y and dLN1 over dLN2 (fp32); of the transposed
+// copies, dY^T over dZ^T, dQ^T over LN2(Y)^T and dK^T over A^T.
 struct BwdLayout {
   size_t x1, q, k, v, attn, y2, dzb, dyb;   // bf16 [rows, d]
+  size_t x1t, attnt, y2t, dzt, dvt;         // bf16 [d, rows_t]
   size_t y, dy2, dy, dk, dv;                // fp32 [rows, d]
   size_t stats1, stats2, lse_re, stat_d, stat_l2, packed[3];
-  size_t ublk, hblk, dublk, partials, ln_part, total;
-  int block_rows, wgrad_splits, ln_parts;
+  size_t ublk, hblk, dublk, dub, wt[6], partials, ln_part, total;
+  int block_rows, blk_ld, rows_t, wgrad_splits, ffn_splits, ln_parts;
 };
 
 BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
@@ -697,12 +699,22 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   size_t r = (((size_t)1 << 25) / f) / 128 * 128;
   if (r < 128) r = 128;
   L.block_rows = (int)(r < rows ? r : rows);
+  L.blk_ld = (int)round_up((size_t)L.block_rows, 8);
+  L.rows_t = (int)round_up(rows, 8);
   const size_t tiles = ((dm + 127) / 128) * ((dm + 127) / 128);
   size_t splits = (512 + tiles - 1) / tiles;
   if (splits > 16) splits = 16;
   if (splits > rows / 256) splits = rows / 256;
   if (splits < 1) splits = 1;
   L.wgrad_splits = (int)splits;
+  // dW_1, dW_2 per block: [d, d_ff] tiles, the block's rows split to reach ~1024
+  // workgroups, each layer at least 1024 rows
+  const size_t ftiles = ((dm + 127) / 128) * ((f + 127) / 128);
+  size_t fsplits = (1024 + ftiles - 1) / ftiles;
+  if (fsplits > (size_t)L.block_rows / 1024) fsplits = (size_t)L.block_rows / 1024;
+  if (fsplits > 16) fsplits = 16;
+  if (fsplits < 1) fsplits = 1;
+  L.ffn_splits = (int)fsplits;
   const size_t parts = (rows + 3) / 4;
   L.ln_parts = (int)(parts < 512 ? parts : 512);
   size_t off = 0;
@@ -711,9 +723,10 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
     off += round_up(bytes, kAlign);
     return o;
   };
-  const size_t rb = rows * dm * 2, rf = rows * dm * 4;
+  const size_t rb = rows * dm * 2, rf = rows * dm * 4, tb = dm * (size_t)L.rows_t * 2;
   L.x1 = take(rb); L.q = take(rb); L.k = take(rb); L.v = take(rb);
   L.attn = take(rb); L.y2 = take(rb); L.dzb = take(rb); L.dyb = take(rb);
+  L.x1t = take(tb); L.attnt = take(tb); L.y2t = take(tb); L.dzt = take(tb); L.dvt = take(tb);
   L.y = take(rf); L.dy2 = take(rf); L.dy = take(rf); L.dk = take(rf); L.dv = take(rf);
   L.stats1 = take(rows * 8);
   L.stats2 = take(rows * 8);
@@ -721,10 +734,15 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   L.stat_d = take(bh * np * 4);
   L.stat_l2 = take(bh * np * 4);
   for (int i = 0; i < 3; ++i) L.packed[i] = take((size_t)d->batch * np * dm * 2);
-  L.ublk = take((size_t)L.block_rows * f * 4);
-  L.hblk = take((size_t)L.block_rows * f * 2);
-  L.dublk = take((size_t)L.block_rows * f * 2);
-  L.partials = take(splits > 1 ? splits * dm * dm * 4 : 0);
+  L.ublk = take(f * (size_t)L.blk_ld * 4);
+  L.hblk = take(f * (size_t)L.blk_ld * 2);
+  L.dublk = take(f * (size_t)L.blk_ld * 2);
+  L.dub = take((size_t)L.block_rows * f * 2);
+  L.wt[0] = take(dm * f * 2);   // W_1^T
+  L.wt[1] = take(dm * f * 2);   // W_2^T
+  for (int i = 2; i < 6; ++i) L.wt[i] = take(dm * dm * 2);   // W_O^T, W_Q^T, W_K^T, W_V^T
+  const size_t pw = splits > 1 ? splits * dm * dm * 4 : 0, pf = fsplits > 1 ? fsplits * dm * f * 4 : 0;
+  L.partials = take(pw > pf ? pw : pf);
   L.ln_part = take((size_t)L.ln_parts * 2 * dm * 4);
   L.total = off;
   return L;
@@ -794,9 +812,12 @@ bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
   p.d_ff = desc->d_ff;
   p.causal = desc->causal;
   p.rows = (int)rows;
+  p.rows_t = W.rows_t;
   p.ln_eps = desc->ln_eps;
   p.block_rows = W.block_rows;
+  p.blk_ld = W.blk_ld;
   p.wgrad_splits = W.wgrad_splits;
+  p.ffn_splits = W.ffn_splits;
   p.ln_parts = W.ln_parts;
   p.x = X;
   p.w = *weights;
@@ -816,8 +837,23 @@ bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
   p.dqb = ws + W.q;     // Q, K, V are dead once the attention backward is done
   p.dkb = ws + W.k;
   p.dvb = ws + W.v;
+  p.x1t = ws + W.x1t;
+  p.attnt = ws + W.attnt;
+  p.y2t = ws + W.y2t;
+  p.dzt = ws + W.dzt;
+  p.dyt = ws + W.dzt;   // dZ^T is dead once the FFN blocks are done
+  p.dqt = ws + W.y2t;   // LN2(Y)^T likewise
+  p.dkt = ws + W.attnt; // A^T is dead once dW_O is formed, before the attention backward
+  p.dvt = ws + W.dvt;
   p.hblk = ws + W.hblk;
   p.dublk = ws + W.dublk;
+  p.dub = ws + W.dub;
+  p.w1t = ws + W.wt[0];
+  p.w2t = ws + W.wt[1];
+  p.wot = ws + W.wt[2];
+  p.wqt = ws + W.wt[3];
+  p.wkt = ws + W.wt[4];
+  p.wvt = ws + W.wt[5];
   p.ublk = F(W.ublk);
   p.y = F(W.y);
   p.dy2 = F(W.dy2);

@@ -172,13 +172,16 @@ int launch_attention_merge(int batch, int seq_len, int n_heads, int d_head, floa
                            char* err, size_t errlen);
 
 // Layer backward (k_layer_bwd.hip) after validation: device pointers; bf16
-// buffers are void*. Every [rows, d_model] buffer is row-major over the
-// batch * seq_len rows.
+// buffers are void*. Row-major buffers are [rows, d_model] over the batch *
+// seq_len rows; transposed ones ("...t") are [d_model, rows_t].
 struct LayerBwdLaunch {
   int batch, seq_len, seq_pad, d_model, n_heads, d_ff, causal, rows;
+  int rows_t;         // row stride of the transposed activations: rows rounded up to 8
   float ln_eps;
-  int block_rows;     // FFN rows per block (the [block_rows, d_ff] hidden state)
+  int block_rows;     // FFN rows per block (a multiple of 8 unless it is all the rows)
+  int blk_ld;         // row stride of the block's [d_ff, block] buffers (a multiple of 8)
   int wgrad_splits;   // workgroup layers over the rows for the [d, d] weight gradients
+  int ffn_splits;     // likewise for dW_1, dW_2 over a block's rows
   int ln_parts;       // workgroups of the LN backward (column partial sums)
   const void* x;      // bf16 [rows, d]
   bpt_layer_weights_t w;
@@ -188,14 +191,17 @@ struct LayerBwdLaunch {
   bpt_layer_grads_t g;
   // workspace (see bpt_api.cpp: bwd_layout for sizes and the reuse of dead buffers)
   void *x1, *q, *k, *v, *attn, *y2, *dzb, *dyb, *da, *dqb, *dkb, *dvb;   // bf16 [rows, d]
-  void *hblk, *dublk;   // bf16 [block_rows, d_ff]
-  float* ublk;          // fp32 [block_rows, d_ff]
+  void *x1t, *attnt, *y2t, *dzt, *dyt, *dqt, *dkt, *dvt;                 // bf16 [d, rows_t]
+  void *hblk, *dublk;   // bf16 [d_ff, blk_ld]: H^T and dU^T of the block
+  float* ublk;          // fp32 [d_ff, blk_ld]: U^T of the block
+  void* dub;            // bf16 [block_rows, d_ff]: dU of the block
+  void *w1t, *w2t, *wot, *wqt, *wkt, *wvt;   // bf16 weights transposed: [d, d_ff], [d_ff, d], [d, d] x 4
   float *y, *dy2, *dy, *dq, *dk, *dv, *dx1;   // fp32 [rows, d]
   float *stats1, *stats2;   // (mean, rstd) per row: 2 floats each
   float* lse_re;        // the recomputed forward's statistic (not used further)
   float *stat_d, *stat_l2;   // attention backward row statistics [batch * n_heads, seq_pad]
   void* packed[3];      // attention operands in fragment order, [batch * seq_pad, d] bf16 each
-  float* partials;      // split-k partial sums: wgrad_splits x [d, d]
+  float* partials;      // split-k partial sums: wgrad_splits x [d, d] or ffn_splits x [d, d_ff]
   float* ln_part;       // LN backward column partials: ln_parts x 2 x [d]
 };
 int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t errlen);

@@ -17,12 +17,15 @@
 // Weights are [out, in] row-major, so y = x W^T; gradients come out in the same
 // layouts, in fp32. Matrix products take bf16 operands with fp32 accumulation.
 //
-// The products have every operand orientation, so they run on one general
-// kernel: C[M, N] = sum_k opA[m, k] opB[k, n] with either operand stored with k
-// contiguous or with m (n) contiguous, 128 x 128 tiles, k-tiles of 32 staged in
-// LDS (register-prefetched double buffer), v_mfma_f32_32x32x16_bf16, optional
-// split of k over workgroups (partial sums reduced in a fixed order), and
-// epilogues that fuse GELU, GELU' and residuals.
+// Every product runs on one kernel with both operands k-contiguous, C[m, n] =
+// sum_k A[m, k] B[n, k] (128 x 128 tiles, k-tiles of 32 staged in LDS through a
+// register-prefetched double buffer, v_mfma_f32_32x32x16_bf16, an optional split of
+// k over workgroups whose partial sums are added in a fixed order, and epilogues
+// that fuse GELU, GELU' and residuals). Operands whose k is their strided index
+// (the weights for dX-side products, the activations for the weight gradients,
+// which contract over the rows) are first copied transposed by an LDS-tiled
+// transpose kernel; the FFN block's U, H and dU are produced transposed ([d_ff,
+// rows of the block]) by computing C^T = W x^T, so only dU needs a second layout.
 #include <type_traits>
 
 #include "bpt_device.hpp"
@@ -41,9 +44,9 @@ enum BwdGemmMode {
 };
 
 struct BwdGemm {
-  const bf16* a;   // opA[m, k] at a[m * lda + k] (A_KC) or a[k * lda + m]
-  const bf16* b;   // opB[k, n] at b[n * ldb + k] (B_KC) or b[k * ldb + n]
-  int lda, ldb;
+  const bf16* a;   // A[m, k] at a[m * lda + k]
+  const bf16* b;   // B[n, k] at b[n * ldb + k]
+  int lda, ldb;    // multiples of 8, like the base pointers' element offsets
   int M, N, K;
   int k_per_split; // multiple of 32; split z covers k in [z kps, (z + 1) kps)
   void* c;         // output (C, H or P)
@@ -69,27 +72,25 @@ namespace {
 constexpr int kGBM = 128, kGBN = 128, kGBK = 32;
 constexpr int kGLd = kGBK + 8;   // LDS row stride in elements (padding against bank conflicts)
 
-// One k-tile of an operand into registers: 512 chunks of 8 elements per 128 x 32
-// tile, two per thread. KC: a chunk is 8 consecutive k of one row (16-byte load);
-// otherwise 8 consecutive rows of one k (16-byte load, scattered into LDS later).
-template <bool KC>
+// One k-tile of an operand into registers: 128 rows x 32 k = 512 chunks of 8
+// consecutive k (16 bytes), two per thread. A chunk that straddles K is read
+// element by element with zeros past K, so K need not be a multiple of 8.
 struct TileLoad {
   uint4 v[2];
   __device__ void load(const bf16* p, int ld, int rows, int K, int r0, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i;
-      if constexpr (KC) {
-        const int r = c >> 2, kc = (c & 3) * 8;
-        const int gr = r0 + r, gk = k0 + kc;
-        v[i] = (gr < rows && gk < K) ? *reinterpret_cast<const uint4*>(p + (size_t)gr * ld + gk)
-                                     : make_uint4(0, 0, 0, 0);
+      const int r = c >> 2, kc = (c & 3) * 8;
+      const int gr = r0 + r, gk = k0 + kc;
+      const bf16* src = p + (size_t)gr * ld + gk;
+      if (gr < rows && gk + 8 <= K) {
+        v[i] = *reinterpret_cast<const uint4*>(src);
       } else {
-        const int k = c >> 4, rc = (c & 15) * 8;
-        const int gk = k0 + k, gr = r0 + rc;
-        // rows are padded to a multiple of 8 by the caller's leading dimension check
-        v[i] = (gk < K && gr < rows) ? *reinterpret_cast<const uint4*>(p + (size_t)gk * ld + gr)
-                                     : make_uint4(0, 0, 0, 0);
+        bf16 e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = (gr < rows && gk + j < K) ? src[j] : (bf16)0.0f;
+        v[i] = *reinterpret_cast<const uint4*>(e);
       }
     }
   }
@@ -97,15 +98,7 @@ struct TileLoad {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i;
-      if constexpr (KC) {
-        const int r = c >> 2, kc = (c & 3) * 8;
-        *reinterpret_cast<uint4*>(s + r * kGLd + kc) = v[i];
-      } else {
-        const int k = c >> 4, rc = (c & 15) * 8;
-        const bf16* e = reinterpret_cast<const bf16*>(&v[i]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s[(rc + j) * kGLd + k] = e[j];
-      }
+      *reinterpret_cast<uint4*>(s + (c >> 2) * kGLd + (c & 3) * 8) = v[i];
     }
   }
 };
@@ -113,14 +106,28 @@ struct TileLoad {
 }  // namespace
 
 // 256 threads = 4 waves in 2 x 2, each 64 x 64 of the tile (2 x 2 products of 32 x 32).
-template <bool A_KC, bool B_KC, int MODE>
+template <int MODE>
 __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm g) {
   __shared__ __align__(16) bf16 As[2][kGBM * kGLd];
   __shared__ __align__(16) bf16 Bs[2][kGBN * kGLd];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kGBM, n0 = blockIdx.x * kGBN;
+  // Tile order: workgroups are dealt to the 8 XCDs round-robin; when the tile
+  // count divides by 8, XCD x takes a contiguous range of tiles, walked in groups
+  // of 4 M-tiles across N, so the tiles an XCD runs together share operand rows in
+  // its L2.
+  int tm = blockIdx.y, tn = blockIdx.x;
+  {
+    const int gx = gridDim.x, gy = gridDim.y, T = gx * gy, id = blockIdx.x + gx * blockIdx.y;
+    if ((T & 7) == 0 && (gy & 3) == 0) {
+      const int t = (id & 7) * (T >> 3) + (id >> 3);
+      const int grp = t / (4 * gx), w = t - grp * 4 * gx;
+      tm = grp * 4 + (w & 3);
+      tn = w >> 2;
+    }
+  }
+  const int m0 = tm * kGBM, n0 = tn * kGBN;
   const int kb = blockIdx.z * g.k_per_split;
   const int ke = min(g.K, kb + g.k_per_split);
   const int nkt = ke > kb ? (ke - kb + kGBK - 1) / kGBK : 0;
@@ -131,8 +138,7 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  TileLoad<A_KC> la;
-  TileLoad<B_KC> lb;
+  TileLoad la, lb;
   if (nkt > 0) {
     la.load(g.a, g.lda, g.M, ke, m0, kb, tid);
     lb.load(g.b, g.ldb, g.N, ke, n0, kb, tid);
@@ -360,55 +366,78 @@ __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict
   dbias[c] = sb;
 }
 
-// bf16 copy of an fp32 array (8 elements per thread; n a multiple of 8).
-__global__ __launch_bounds__(256) void bwd_cast_kernel(const float* __restrict__ in, bf16* __restrict__ out,
-                                                       long long n8) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n8) return;
-  float v[8];
-  load8_f32(in + t * 8, v);
-  store8_f32(out + t * 8, v);
+// out[c, r] = in[r, c] (bf16 out; ld_out >= nr) for in [nr, nc] with row stride
+// ld_in, through a 64 x 64 LDS tile: reads coalesced along c, writes along r. With
+// out_rm, also a bf16 row-major copy of in (row stride ld_in), for fp32 inputs.
+template <typename TIn>
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const TIn* __restrict__ in, int nr, int nc, int ld_in,
+                                                            bf16* __restrict__ out, int ld_out,
+                                                            bf16* __restrict__ out_rm) {
+  __shared__ bf16 tile[64][66];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 4 * i + tr;
+    bf16 v = (bf16)0.0f;
+    if (r0 + r < nr && c0 + tc < nc) {
+      const size_t o = (size_t)(r0 + r) * ld_in + c0 + tc;
+      v = (bf16)(float)in[o];
+      if (out_rm) out_rm[o] = v;
+    }
+    tile[r][tc] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = 4 * i + tr;
+    if (c0 + c < nc && r0 + tc < nr) out[(size_t)(c0 + c) * ld_out + r0 + tc] = tile[tc][c];
+  }
 }
 
 namespace {
 
-template <bool A_KC, bool B_KC, int MODE>
+template <int MODE>
 int run_bwd_gemm(const BwdGemm& g0, int splits, hipStream_t s, const char* what, char* err, size_t n) {
   BwdGemm g = g0;
   if (g.M <= 0 || g.N <= 0) return 0;
   if (splits < 1) splits = 1;
   g.k_per_split = ((g.K + splits - 1) / splits + kGBK - 1) / kGBK * kGBK;
+  if (g.k_per_split < kGBK) g.k_per_split = kGBK;
   splits = (g.K + g.k_per_split - 1) / g.k_per_split;
   if (splits < 1) splits = 1;
   dim3 grid((g.N + kGBN - 1) / kGBN, (g.M + kGBM - 1) / kGBM, splits);
-  hipLaunchKernelGGL((bwd_gemm_kernel<A_KC, B_KC, MODE>), grid, dim3(256), 0, s, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE>), grid, dim3(256), 0, s, g);
   return check_launch(what, err, n);
 }
 
-// C (+)= opA opB with k split over `splits` workgroup layers into the partial
+// C (+)= A B^T with k split over `splits` workgroup layers into the partial
 // buffer, then reduced in order into C.
-template <bool A_KC, bool B_KC>
 int run_bwd_gemm_split(BwdGemm g, int splits, float* partials, bool accumulate, hipStream_t s,
                        const char* what, char* err, size_t n) {
   if (splits <= 1)
-    return accumulate ? run_bwd_gemm<A_KC, B_KC, kGAccF32>(g, 1, s, what, err, n)
-                      : run_bwd_gemm<A_KC, B_KC, kGStoreF32>(g, 1, s, what, err, n);
+    return accumulate ? run_bwd_gemm<kGAccF32>(g, 1, s, what, err, n)
+                      : run_bwd_gemm<kGStoreF32>(g, 1, s, what, err, n);
   float* c = static_cast<float*>(g.c);
   const int ldc = g.ldc;
   g.c = partials;
-  g.k_per_split = ((g.K + splits - 1) / splits + kGBK - 1) / kGBK * kGBK;
-  const int used = (g.K + g.k_per_split - 1) / g.k_per_split;
-  if (run_bwd_gemm<A_KC, B_KC, kGPartial>(g, splits, s, what, err, n)) return 1;
+  int kps = ((g.K + splits - 1) / splits + kGBK - 1) / kGBK * kGBK;
+  if (kps < kGBK) kps = kGBK;
+  const int used = (g.K + kps - 1) / kps;
+  if (run_bwd_gemm<kGPartial>(g, splits, s, what, err, n)) return 1;
   const long long mn = (long long)g.M * g.N;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, c, ldc, partials,
                      g.M, g.N, used, accumulate ? 1 : 0);
   return check_launch("bwd_reduce", err, n);
 }
 
-int cast_bf16(const float* in, bf16* out, size_t count, hipStream_t s, char* err, size_t n) {
-  const long long n8 = (long long)(count / 8);
-  hipLaunchKernelGGL(bwd_cast_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, in, out, n8);
-  return check_launch("bwd_cast", err, n);
+template <typename TIn>
+int transpose(const TIn* in, int nr, int nc, int ld_in, bf16* out, int ld_out, bf16* out_rm, hipStream_t s,
+              char* err, size_t n) {
+  if (nr <= 0 || nc <= 0) return 0;
+  hipLaunchKernelGGL(bwd_transpose_kernel<TIn>, dim3((nc + 63) / 64, (nr + 63) / 64), dim3(256), 0, s, in, nr, nc,
+                     ld_in, out, ld_out, out_rm);
+  return check_launch("bwd_transpose", err, n);
 }
 
 template <typename TX>
@@ -426,12 +455,12 @@ int ln_bwd(const TX* x, const float2* stats, const bf16* gain, const float* dy, 
 
 int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int rows = L.rows, d = L.d_model, f = L.d_ff;
-  if (d % 64 != 0 || d > 4096 || f % 256 != 0 || L.block_rows < 1 || L.ln_parts < 1) {
+  const int rows = L.rows, d = L.d_model, f = L.d_ff, rt = L.rows_t, bl = L.blk_ld;
+  if (d % 64 != 0 || d > 4096 || f % 256 != 0 || L.block_rows < 1 || L.ln_parts < 1 || rt < rows ||
+      rt % 8 != 0 || bl < L.block_rows || bl % 8 != 0 || (L.block_rows < rows && L.block_rows % 8 != 0)) {
     set_err(err, n, "layer backward: inconsistent launch shape%s (d_model %d)", "", d);
     return 1;
   }
-  const size_t rd = (size_t)rows * d;
   auto B = [](void* p) { return static_cast<bf16*>(p); };
   auto CB = [](const void* p) { return static_cast<const bf16*>(p); };
   const bf16* const x = CB(L.x);
@@ -443,23 +472,36 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
   const bf16* const w2 = CB(L.w.w_2);
   bf16 *const x1 = B(L.x1), *const q = B(L.q), *const k = B(L.k), *const v = B(L.v);
   bf16 *const attn = B(L.attn), *const y2 = B(L.y2), *const dzb = B(L.dzb), *const dyb = B(L.dyb);
-  bf16 *const hblk = B(L.hblk), *const dublk = B(L.dublk), *const da = B(L.da);
+  bf16 *const x1t = B(L.x1t), *const attnt = B(L.attnt), *const y2t = B(L.y2t), *const dzt = B(L.dzt);
+  bf16 *const dyt = B(L.dyt), *const da = B(L.da);
+  bf16 *const hblk = B(L.hblk), *const dublk = B(L.dublk), *const dub = B(L.dub);
+  bf16 *const w1t = B(L.w1t), *const w2t = B(L.w2t), *const wot = B(L.wot);
+  bf16* const wqkvt[3] = {B(L.wqt), B(L.wkt), B(L.wvt)};
   bf16* const dqkvb[3] = {B(L.dqb), B(L.dkb), B(L.dvb)};
-  const int wsplit = L.wgrad_splits;
+  bf16* const dqkvt[3] = {B(L.dqt), B(L.dkt), B(L.dvt)};
   float2* const stats1 = reinterpret_cast<float2*>(L.stats1);
   float2* const stats2 = reinterpret_cast<float2*>(L.stats2);
+  const int wsplit = L.wgrad_splits;
 
-  // ---- recompute: LN1(X), Q, K, V, A, Y = X + A W_O^T, LN2(Y)
+  // ---- the weights with their input index contiguous ([in, out]), for dX-side products
+  if (transpose(w1, f, d, d, w1t, f, nullptr, s, err, n) || transpose(w2, d, f, f, w2t, d, nullptr, s, err, n) ||
+      transpose(wo, d, d, d, wot, d, nullptr, s, err, n) || transpose(wq, d, d, d, wqkvt[0], d, nullptr, s, err, n) ||
+      transpose(wk, d, d, d, wqkvt[1], d, nullptr, s, err, n) || transpose(wv, d, d, d, wqkvt[2], d, nullptr, s, err, n))
+    return 1;
+
+  // ---- recompute: LN1(X), Q, K, V, A, Y = X + A W_O^T, LN2(Y); transposed copies of
+  //      LN1(X), A, LN2(Y) and dZ for the weight gradients
   hipLaunchKernelGGL(bwd_ln_fwd_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, x, CB(L.w.ln1_g),
                      CB(L.w.ln1_b), x1, stats1, rows, d, L.ln_eps);
   if (check_launch("bwd_ln1", err, n)) return 1;
+  if (transpose(x1, rows, d, d, x1t, rt, nullptr, s, err, n)) return 1;
   {
     const bf16* ws[3] = {wq, wk, wv};
     bf16* outs[3] = {q, k, v};
     for (int i = 0; i < 3; ++i) {
       BwdGemm g{};
       g.a = x1; g.lda = d; g.b = ws[i]; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = outs[i]; g.ldc = d;
-      if (run_bwd_gemm<true, true, kGStoreBF16>(g, 1, s, "bwd_qkv", err, n)) return 1;
+      if (run_bwd_gemm<kGStoreBF16>(g, 1, s, "bwd_qkv", err, n)) return 1;
     }
   }
   {
@@ -470,58 +512,63 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
     for (int i = 0; i < 3; ++i) a.packed[i] = L.packed[i];
     if (launch_attention_fwd(a, stream, err, n)) return 1;
   }
+  if (transpose(attn, rows, d, d, attnt, rt, nullptr, s, err, n)) return 1;
   {
     BwdGemm g{};
     g.a = attn; g.lda = d; g.b = wo; g.ldb = d; g.M = rows; g.N = d; g.K = d;
     g.c = L.y; g.ldc = d; g.r = x; g.ldr = d; g.r_f32 = 0;
-    if (run_bwd_gemm<true, true, kGResid>(g, 1, s, "bwd_wo_fwd", err, n)) return 1;
+    if (run_bwd_gemm<kGResid>(g, 1, s, "bwd_wo_fwd", err, n)) return 1;
   }
   hipLaunchKernelGGL(bwd_ln_fwd_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, L.y, CB(L.w.ln2_g),
                      CB(L.w.ln2_b), y2, stats2, rows, d, L.ln_eps);
   if (check_launch("bwd_ln2", err, n)) return 1;
-  if (cast_bf16(L.dz, dzb, rd, s, err, n)) return 1;
+  if (transpose(y2, rows, d, d, y2t, rt, nullptr, s, err, n)) return 1;
+  if (transpose(L.dz, rows, d, d, dzt, rt, dzb, s, err, n)) return 1;   // also dZ in bf16, row-major
 
-  // ---- FFN, one block of at most block_rows rows at a time
+  // ---- FFN, one block of at most block_rows rows at a time; the block's U, H, dU
+  //      are [d_ff, R] (row stride blk_ld), dU also [R, d_ff]
   for (int r0 = 0; r0 < rows; r0 += L.block_rows) {
     const int R = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
     BwdGemm g{};
-    // U = LN2(Y) W_1^T, H = GELU(U)
-    g.a = y2 + (size_t)r0 * d; g.lda = d; g.b = w1; g.ldb = d; g.M = R; g.N = f; g.K = d;
-    g.c = hblk; g.ldc = f; g.u = L.ublk; g.ldu = f;
-    if (run_bwd_gemm<true, true, kGGeluU>(g, 1, s, "bwd_w1_fwd", err, n)) return 1;
-    // dU = (dZ W_2) * GELU'(U); W_2 is [d, d_ff]: opB[k = output feature, n = unit] at w2[k d_ff + n]
+    // U^T = W_1 LN2(Y)^T, H^T = GELU(U^T)
+    g.a = w1; g.lda = d; g.b = y2 + (size_t)r0 * d; g.ldb = d; g.M = f; g.N = R; g.K = d;
+    g.c = hblk; g.ldc = bl; g.u = L.ublk; g.ldu = bl;
+    if (run_bwd_gemm<kGGeluU>(g, 1, s, "bwd_w1_fwd", err, n)) return 1;
+    // dU^T = (W_2^T dZ^T) * GELU'(U^T): W_2^T is [d_ff, d]
     g = BwdGemm{};
-    g.a = dzb + (size_t)r0 * d; g.lda = d; g.b = w2; g.ldb = f; g.M = R; g.N = f; g.K = d;
-    g.c = dublk; g.ldc = f; g.r = L.ublk; g.ldr = f;
-    if (run_bwd_gemm<true, false, kGDGelu>(g, 1, s, "bwd_du", err, n)) return 1;
-    // dW_2 (+)= dZ^T H: opA[m = output feature, k = row] at dz[row d + m], opB[k = row, n = unit] at h[row d_ff + n]
+    g.a = w2t; g.lda = d; g.b = dzb + (size_t)r0 * d; g.ldb = d; g.M = f; g.N = R; g.K = d;
+    g.c = dublk; g.ldc = bl; g.r = L.ublk; g.ldr = bl;
+    if (run_bwd_gemm<kGDGelu>(g, 1, s, "bwd_du", err, n)) return 1;
+    if (transpose(dublk, f, R, bl, dub, f, nullptr, s, err, n)) return 1;
+    // dW_2 (+)= dZ^T H: A = dZ^T [d, rows] (columns of the block), B = H^T [d_ff, R]
     g = BwdGemm{};
-    g.a = dzb + (size_t)r0 * d; g.lda = d; g.b = hblk; g.ldb = f; g.M = d; g.N = f; g.K = R;
+    g.a = dzt + r0; g.lda = rt; g.b = hblk; g.ldb = bl; g.M = d; g.N = f; g.K = R;
     g.c = L.g.w_2; g.ldc = f;
-    if (run_bwd_gemm_split<false, false>(g, 1, L.partials, r0 > 0, s, "bwd_dw2", err, n)) return 1;
-    // dW_1 (+)= dU^T LN2(Y)
+    if (run_bwd_gemm_split(g, L.ffn_splits, L.partials, r0 > 0, s, "bwd_dw2", err, n)) return 1;
+    // dW_1 (+)= dU^T LN2(Y): A = dU^T [d_ff, R], B = LN2(Y)^T [d, rows]
     g = BwdGemm{};
-    g.a = dublk; g.lda = f; g.b = y2 + (size_t)r0 * d; g.ldb = d; g.M = f; g.N = d; g.K = R;
+    g.a = dublk; g.lda = bl; g.b = y2t + r0; g.ldb = rt; g.M = f; g.N = d; g.K = R;
     g.c = L.g.w_1; g.ldc = d;
-    if (run_bwd_gemm_split<false, false>(g, 1, L.partials, r0 > 0, s, "bwd_dw1", err, n)) return 1;
-    // dLN2 = dU W_1; W_1 is [d_ff, d]: opB[k = unit, n = feature] at w1[k d + n]
+    if (run_bwd_gemm_split(g, L.ffn_splits, L.partials, r0 > 0, s, "bwd_dw1", err, n)) return 1;
+    // dLN2 = dU W_1: A = dU [R, d_ff], B = W_1^T [d, d_ff]
     g = BwdGemm{};
-    g.a = dublk; g.lda = f; g.b = w1; g.ldb = d; g.M = R; g.N = d; g.K = f;
+    g.a = dub; g.lda = f; g.b = w1t; g.ldb = f; g.M = R; g.N = d; g.K = f;
     g.c = L.dy2 + (size_t)r0 * d; g.ldc = d;
-    if (run_bwd_gemm<true, false, kGStoreF32>(g, 1, s, "bwd_dln2", err, n)) return 1;
+    if (run_bwd_gemm<kGStoreF32>(g, 1, s, "bwd_dln2", err, n)) return 1;
   }
   // ---- LN2 backward: dY = dZ + LN2'(dLN2) (and a bf16 copy); LN2 gain / bias gradients
   if (ln_bwd<float>(L.y, stats2, CB(L.w.ln2_g), L.dy2, L.dz, L.dy, dyb, L.ln_part, L.ln_parts, L.g.ln2_g,
                     L.g.ln2_b, rows, d, s, err, n))
     return 1;
+  if (transpose(dyb, rows, d, d, dyt, rt, nullptr, s, err, n)) return 1;
   // ---- W_O: dA = dY W_O, dW_O = dY^T A
   {
     BwdGemm g{};
-    g.a = dyb; g.lda = d; g.b = wo; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = da; g.ldc = d;
-    if (run_bwd_gemm<true, false, kGStoreBF16>(g, 1, s, "bwd_da", err, n)) return 1;
+    g.a = dyb; g.lda = d; g.b = wot; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = da; g.ldc = d;
+    if (run_bwd_gemm<kGStoreBF16>(g, 1, s, "bwd_da", err, n)) return 1;
     g = BwdGemm{};
-    g.a = dyb; g.lda = d; g.b = attn; g.ldb = d; g.M = d; g.N = d; g.K = rows; g.c = L.g.w_o; g.ldc = d;
-    if (run_bwd_gemm_split<false, false>(g, wsplit, L.partials, false, s, "bwd_dwo", err, n)) return 1;
+    g.a = dyt; g.lda = rt; g.b = attnt; g.ldb = rt; g.M = d; g.N = d; g.K = rows; g.c = L.g.w_o; g.ldc = d;
+    if (run_bwd_gemm_split(g, wsplit, L.partials, false, s, "bwd_dwo", err, n)) return 1;
   }
   // ---- attention backward from the saved statistic
   {
@@ -538,18 +585,17 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
   // ---- QKV: dLN1 = dQ W_Q + dK W_K + dV W_V, dW_{Q,K,V} = d{Q,K,V}^T LN1(X)
   {
     const float* dg[3] = {L.dq, L.dk, L.dv};
-    const bf16* ws[3] = {wq, wk, wv};
     float* dw[3] = {L.g.w_q, L.g.w_k, L.g.w_v};
     for (int i = 0; i < 3; ++i) {
-      if (cast_bf16(dg[i], dqkvb[i], rd, s, err, n)) return 1;
+      if (transpose(dg[i], rows, d, d, dqkvt[i], rt, dqkvb[i], s, err, n)) return 1;
       BwdGemm g{};
-      g.a = dqkvb[i]; g.lda = d; g.b = ws[i]; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = L.dx1; g.ldc = d;
-      if (i == 0 ? run_bwd_gemm<true, false, kGStoreF32>(g, 1, s, "bwd_dx1", err, n)
-                 : run_bwd_gemm<true, false, kGAccF32>(g, 1, s, "bwd_dx1", err, n))
+      g.a = dqkvb[i]; g.lda = d; g.b = wqkvt[i]; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = L.dx1; g.ldc = d;
+      if (i == 0 ? run_bwd_gemm<kGStoreF32>(g, 1, s, "bwd_dx1", err, n)
+                 : run_bwd_gemm<kGAccF32>(g, 1, s, "bwd_dx1", err, n))
         return 1;
       g = BwdGemm{};
-      g.a = dqkvb[i]; g.lda = d; g.b = x1; g.ldb = d; g.M = d; g.N = d; g.K = rows; g.c = dw[i]; g.ldc = d;
-      if (run_bwd_gemm_split<false, false>(g, wsplit, L.partials, false, s, "bwd_dwqkv", err, n)) return 1;
+      g.a = dqkvt[i]; g.lda = rt; g.b = x1t; g.ldb = rt; g.M = d; g.N = d; g.K = rows; g.c = dw[i]; g.ldc = d;
+      if (run_bwd_gemm_split(g, wsplit, L.partials, false, s, "bwd_dwqkv", err, n)) return 1;
     }
   }
   // ---- LN1 backward: dX = dY + LN1'(dLN1); LN1 gain / bias gradients

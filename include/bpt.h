@@ -320,13 +320,15 @@ typedef struct {
  * with bpt_last_error() set when desc is invalid or outside the backward's limits
  * (see bpt_layer_bwd). With rows = batch * seq_len and Np = seq_len rounded up to
  * 128, it holds: bf16 [rows, d_model] copies of LN1(X), Q, K, V, the attention
- * output A, LN2(Y), dZ, dY, dQ/dK/dV (over Q, K, V once they are dead); fp32
- * [rows, d_model] Y (then dQ), dLN2 (then dLN1), dY, dK, dV; per-row LN
- * statistics; the attention operands in fragment order (3 x [batch * Np,
- * d_model] bf16) and its row statistics; one FFN block: U fp32, H and dU bf16,
- * each [r, d_ff] with r = min(rows, 2^25 / d_ff); split-k partial sums (up to 16
- * x [d_model, d_model] fp32) and the LN column partials. The only d_ff-wide
- * buffers are the block's: nothing of size rows x d_ff or seq_len x seq_len. */
+ * output A, LN2(Y), dZ, dY (dA, dQ, dK, dV over those that are dead by then);
+ * bf16 transposed copies [d_model, rows] of LN1(X), A, LN2(Y), dZ and dV (dY, dQ,
+ * dK over dead ones); fp32 [rows, d_model] Y (then dQ), dLN2 (then dLN1), dY, dK,
+ * dV; per-row LN statistics; the attention operands in fragment order (3 x
+ * [batch * Np, d_model] bf16) and its row statistics; one FFN block of r = min(rows,
+ * 2^25 / d_ff) rows: U fp32, H, dU (twice) bf16, each [r, d_ff]; the six weights
+ * transposed in bf16; split-k partial sums (up to 16 x [d_model, d_model] or
+ * [d_model, d_ff] fp32) and the LN column partials. The only d_ff-wide buffers are the block's: nothing of
+ * size rows x d_ff or seq_len x seq_len. */
 size_t bpt_layer_bwd_workspace_bytes(const bpt_layer_desc_t* desc);
 
 /* Backward of one layer (bpt_layer_fwd's computation) by block recomputation.

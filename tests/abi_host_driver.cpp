@@ -302,6 +302,7 @@ int main() {
     EXPECT(L.x1 == bws && L.lse == blse && L.dz == dz && L.dx == dx && L.g.w_2 == g.w_2);
     EXPECT((char*)L.ln_part + (size_t)L.ln_parts * 2 * 256 * 4 <= bws + nb);
     EXPECT(L.dq == L.y && L.dx1 == L.dy2 && L.da == L.dzb && L.dqb == L.q);
+    EXPECT(L.dyt == L.dzt && L.dqt == L.y2t && L.dkt == L.attnt && L.rows_t == 400 && L.blk_ld == 400);
     EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, dx, &g, bws, nb - 1, nullptr) == BPT_ERR_WORKSPACE);
     EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, dx, nullptr, bws, nb, nullptr) == BPT_ERR_NULL);
     EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, reinterpret_cast<float*>(fake(9ull << 36) + 64), &g,

@@ -401,5 +401,6 @@ def test_layer_bwd_workspace_has_no_rows_by_d_ff_term():
                                                   n_heads=16, d_ff=d_ff))
     growth = {f: ws(8, f) - ws(4, f) for f in (2048, 4096, 8192, 16384)}
     assert len(set(growth.values())) == 1, growth
-    # per extra row: 8 bf16 and 5 fp32 [d] vectors, 3 bf16 attention copies, statistics
-    assert growth[4096] <= 4 * 4096 * (1024 * (8 * 2 + 5 * 4 + 3 * 2) + 16 + 16 * 3 * 4) + 64 * 256
+    # per extra row: 8 bf16 row-major and 5 bf16 transposed [d] vectors, 5 fp32 [d]
+    # vectors, 3 bf16 attention copies, statistics
+    assert growth[4096] <= 4 * 4096 * (1024 * (8 * 2 + 5 * 2 + 5 * 4 + 3 * 2) + 16 + 16 * 3 * 4) + 64 * 256
