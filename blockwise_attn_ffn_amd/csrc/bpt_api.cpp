@@ -701,7 +701,9 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   L.block_rows = (int)(r < rows ? r : rows);
   L.blk_ld = (int)round_up((size_t)L.block_rows, 8);
   L.rows_t = (int)round_up(rows, 8);
-  const size_t tiles = ((dm + 127) / 128) * ((dm + 127) / 128);
+  // the product kernel's tiles are 256 x 128
+  auto tiles_of = [](size_t m, size_t n) { return ((m + 255) / 256) * ((n + 127) / 128); };
+  const size_t tiles = tiles_of(dm, dm);
   size_t splits = (512 + tiles - 1) / tiles;
   if (splits > 16) splits = 16;
   if (splits > rows / 256) splits = rows / 256;
@@ -709,7 +711,7 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   L.wgrad_splits = (int)splits;
   // dW_1, dW_2 per block: [d, d_ff] tiles, the block's rows split to reach ~1024
   // workgroups, each layer at least 1024 rows
-  const size_t ftiles = ((dm + 127) / 128) * ((f + 127) / 128);
+  const size_t ftiles = tiles_of(dm, f) < tiles_of(f, dm) ? tiles_of(dm, f) : tiles_of(f, dm);
   size_t fsplits = (1024 + ftiles - 1) / ftiles;
   if (fsplits > (size_t)L.block_rows / 1024) fsplits = (size_t)L.block_rows / 1024;
   if (fsplits > 16) fsplits = 16;
