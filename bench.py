@@ -447,12 +447,23 @@ def bench_ring(args, w, R):
     stream = torch.cuda.current_stream()
     q = shards["q"][R - 1]
 
-    def ring():
+    def ring_steps():
         lse_acc.fill_(float("-inf"))
         for s_ in range(R):
             dsc = desc_diag if s_ == R - 1 else desc_full
             bpt.attention_fwd(dsc, q, shards["k"][s_], shards["v"][s_], o, lse, ws, stream)
             bpt.attention_merge(desc_full, o_acc, lse_acc, o, lse, stream)
+
+    # the shards as they travel: packed once by their owners (outside the timed share)
+    kv = []
+    for s_ in range(R):
+        buf = bpt.alloc_workspace(bpt.ring_kv_bytes(desc_diag))
+        bpt.ring_pack_kv(desc_diag, shards["k"][s_], shards["v"][s_], buf, stream)
+        kv.append(buf)
+    ws_share = bpt.alloc_workspace(bpt.ring_share_workspace_bytes(desc_diag))
+
+    def ring():
+        bpt.ring_share_fwd(desc_diag, R - 1, q, kv, o, lse, ws_share, stream)
 
     def one_step():
         bpt.attention_fwd(desc_full, q, shards["k"][0], shards["v"][0], o, lse, ws, stream)
@@ -471,6 +482,7 @@ def bench_ring(args, w, R):
         return t0.elapsed_time(t1) / steps
 
     ms_ring = timed(ring, args.steps)
+    ms_ring_steps = timed(ring_steps, args.steps)
     ms_step = timed(one_step, args.steps)
     flops_ring = (R - 1) * A.attention_flops(n, d, False) + A.attention_flops(n, d, True)
     flops_step = A.attention_flops(n, d, False)
@@ -483,6 +495,9 @@ def bench_ring(args, w, R):
         "config": {"workload": f"{w.name} over {R} devices, the last device", "shard_tokens": n,
                    "d_model": d, "n_heads": h, "ring_steps": R, "parallelism": "none (one device's share)"},
         "flops_per_step": flops_ring,
+        "share_path": "bpt_ring_share_fwd: Q packed once, shards arrive packed, steps merged in the "
+                      "attention kernel",
+        "step_and_merge_path_ms": round(ms_ring_steps, 3),
         "one_unmasked_step": {"ms": round(ms_step, 3), "flops": flops_step,
                               "tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 2)},
     }

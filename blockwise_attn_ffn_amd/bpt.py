@@ -20,7 +20,9 @@ EXPORTED = ("bpt_layer_workspace_bytes", "bpt_stack_workspace_bytes", "bpt_layer
             "bpt_attention_bwd_workspace_bytes", "bpt_attention_bwd",
             "bpt_attention_bwd_profiled", "bpt_attention_fwd_workspace_bytes", "bpt_attention_fwd",
             "bpt_attention_merge", "bpt_layer_host_workspace_bytes", "bpt_layer_fwd_host",
-            "bpt_layer_fwd_noalloc", "bpt_layer_bwd_workspace_bytes", "bpt_layer_bwd", "bpt_status_str",
+            "bpt_layer_fwd_noalloc", "bpt_layer_bwd_workspace_bytes", "bpt_layer_bwd",
+            "bpt_ring_kv_bytes", "bpt_ring_pack_kv", "bpt_ring_share_workspace_bytes",
+            "bpt_ring_share_fwd", "bpt_status_str",
             "bpt_last_error", "bpt_version")
 
 
@@ -117,6 +119,16 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_void_p, ctypes.c_void_p, P(LayerGrads), ctypes.c_void_p,
                                     ctypes.c_size_t, ctypes.c_void_p]
         L.bpt_layer_bwd.restype = ctypes.c_int
+        L.bpt_ring_kv_bytes.argtypes = [P(AttnDesc)]
+        L.bpt_ring_kv_bytes.restype = ctypes.c_size_t
+        L.bpt_ring_pack_kv.argtypes = [P(AttnDesc)] + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+        L.bpt_ring_pack_kv.restype = ctypes.c_int
+        L.bpt_ring_share_workspace_bytes.argtypes = [P(AttnDesc)]
+        L.bpt_ring_share_workspace_bytes.restype = ctypes.c_size_t
+        L.bpt_ring_share_fwd.argtypes = [P(AttnDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         P(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.bpt_ring_share_fwd.restype = ctypes.c_int
         L.bpt_status_str.argtypes = [ctypes.c_int]
         L.bpt_status_str.restype = ctypes.c_char_p
         L.bpt_last_error.argtypes = []
@@ -277,6 +289,31 @@ def attention_merge(desc: AttnDesc, o_acc, lse_acc, o_part, lse_part, stream=Non
     """Fold one ring step's (o_part, lse_part) into the running (o_acc, lse_acc)."""
     _check(lib().bpt_attention_merge(ctypes.byref(desc), _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
                                      _ptr(lse_part), _stream(stream)))
+
+
+def ring_kv_bytes(desc: AttnDesc) -> int:
+    return lib().bpt_ring_kv_bytes(ctypes.byref(desc))
+
+
+def ring_pack_kv(desc: AttnDesc, k, v, kv, stream=None) -> None:
+    """Pack one key/value shard into the attention kernels' layout (kv: a device
+    buffer of ring_kv_bytes)."""
+    nbytes = kv.numel() * kv.element_size()
+    _check(lib().bpt_ring_pack_kv(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(kv), nbytes, _stream(stream)))
+
+
+def ring_share_workspace_bytes(desc: AttnDesc) -> int:
+    return lib().bpt_ring_share_workspace_bytes(ctypes.byref(desc))
+
+
+def ring_share_fwd(desc: AttnDesc, own: int, q, kv_shards: list, o, lse, workspace, stream=None) -> None:
+    """One device's share of Ring Attention: q against the packed shards (a list of
+    device buffers or None for shards the causal mask never reaches)."""
+    n = len(kv_shards)
+    arr = (ctypes.c_void_p * n)(*[_ptr(t) if t is not None else 0 for t in kv_shards])
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().bpt_ring_share_fwd(ctypes.byref(desc), n, own, _ptr(q), arr, _ptr(o), _ptr(lse),
+                                    _ptr(workspace), nbytes, _stream(stream)))
 
 
 def layer_host_workspace_bytes(desc: LayerDesc, n_threads: int) -> int:

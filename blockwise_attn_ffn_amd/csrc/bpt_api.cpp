@@ -535,6 +535,143 @@ bpt_status_t bpt_attention_fwd(const bpt_attn_desc_t* desc, const void* Q, const
   return BPT_OK;
 }
 
+namespace {
+
+// Shapes the ring entry points take: those of bpt_attention_fwd.
+bpt_status_t validate_ring_desc(const bpt_attn_desc_t* d) {
+  bpt_status_t st = validate_attn_desc(d);
+  if (st != BPT_OK) return st;
+  if (d->window || d->chunk || attn_kv_heads(d) != d->n_heads)
+    return fail(BPT_ERR_UNSUPPORTED, "a ring share takes no window, chunk or grouped heads");
+  return BPT_OK;
+}
+
+size_t ring_half_bytes(const bpt_attn_desc_t* d) {
+  return round_up((size_t)d->batch * round_up((size_t)d->seq_len, 128) * d->d_model * 2, kAlign);
+}
+
+// Workspace of the share: Q in fragment layout, the fp32 running output in the
+// same layout, the running statistic.
+size_t ring_share_layout(const bpt_attn_desc_t* d, size_t* acc_off, size_t* lse_off) {
+  const size_t q = ring_half_bytes(d);
+  const size_t acc = 2 * q;
+  const size_t lse = round_up((size_t)d->batch * d->n_heads * d->seq_len * 4, kAlign);
+  if (acc_off) *acc_off = q;
+  if (lse_off) *lse_off = q + acc;
+  return q + acc + lse;
+}
+
+}  // namespace
+
+size_t bpt_ring_kv_bytes(const bpt_attn_desc_t* desc) {
+  if (validate_ring_desc(desc) != BPT_OK) return 0;
+  if (attn_empty(desc)) return 0;
+  return 2 * ring_half_bytes(desc);
+}
+
+bpt_status_t bpt_ring_pack_kv(const bpt_attn_desc_t* desc, const void* K, const void* V, void* kv,
+                              size_t kv_bytes, void* hip_stream) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_ring_desc(desc);
+  if (st != BPT_OK) return st;
+  if (attn_empty(desc)) return BPT_OK;
+  const void* ptrs[] = {K, V, kv};
+  const char* names[] = {"K", "V", "kv"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ptrs[i]) return fail(BPT_ERR_NULL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(BPT_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t need = 2 * ring_half_bytes(desc);
+  if (kv_bytes < need) return fail(BPT_ERR_WORKSPACE, "kv has %zu bytes, %zu needed", kv_bytes, need);
+  const size_t in_b = (size_t)desc->batch * desc->seq_len * desc->d_model * 2;
+  if (overlap(kv, need, K, in_b)) return fail(BPT_ERR_ALIAS, "kv overlaps K");
+  if (overlap(kv, need, V, in_b)) return fail(BPT_ERR_ALIAS, "kv overlaps V");
+  bpt::RingKvLaunch p{};
+  p.batch = desc->batch;
+  p.seq_len = desc->seq_len;
+  p.seq_pad = (int)round_up((size_t)desc->seq_len, 128);
+  p.d_model = desc->d_model;
+  p.n_heads = desc->n_heads;
+  p.d_head = desc->d_model / desc->n_heads;
+  p.k = K;
+  p.v = V;
+  p.kv = kv;
+  p.half_bytes = ring_half_bytes(desc);
+  char msg[256] = "";
+  if (bpt::launch_ring_pack_kv(p, hip_stream, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
+  return BPT_OK;
+}
+
+size_t bpt_ring_share_workspace_bytes(const bpt_attn_desc_t* desc) {
+  if (validate_ring_desc(desc) != BPT_OK) return 0;
+  if (attn_empty(desc)) return 0;
+  return ring_share_layout(desc, nullptr, nullptr);
+}
+
+bpt_status_t bpt_ring_share_fwd(const bpt_attn_desc_t* desc, int32_t n_shards, int32_t own,
+                                const void* Q, const void* const* kv, void* O, float* lse,
+                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_err[0] = 0;
+  bpt_status_t st = validate_ring_desc(desc);
+  if (st != BPT_OK) return st;
+  if (n_shards < 1 || n_shards > 4096) return fail(BPT_ERR_SHAPE, "n_shards %d must be in [1, 4096]", n_shards);
+  if (own < 0 || own >= n_shards) return fail(BPT_ERR_SHAPE, "own %d must be in [0, n_shards)", own);
+  if (attn_empty(desc)) return BPT_OK;
+  if (!kv) return fail(BPT_ERR_NULL, "kv is NULL");
+  // shards the share reads: all, or up to its own under the causal mask
+  const int used = desc->causal ? own + 1 : n_shards;
+  const size_t kv_b = 2 * ring_half_bytes(desc);
+  size_t acc_off = 0, lse_off = 0;
+  const size_t need = ring_share_layout(desc, &acc_off, &lse_off);
+  const size_t rows = (size_t)desc->batch * desc->seq_len;
+  const size_t in_b = rows * desc->d_model * 2, lse_b = rows * desc->n_heads * 4;
+  const void* outs[] = {O, lse, workspace};
+  const size_t out_b[] = {in_b, lse_b, need};
+  const char* out_names[] = {"O", "lse", "workspace"};
+  if (!Q) return fail(BPT_ERR_NULL, "Q is NULL");
+  if (!aligned16(Q)) return fail(BPT_ERR_ALIGN, "Q is not 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if (!outs[i]) return fail(BPT_ERR_NULL, "%s is NULL", out_names[i]);
+    if (!aligned16(outs[i])) return fail(BPT_ERR_ALIGN, "%s is not 16-byte aligned", out_names[i]);
+  }
+  if (workspace_bytes < need)
+    return fail(BPT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  for (int s = 0; s < used; ++s) {
+    if (!kv[s]) return fail(BPT_ERR_NULL, "kv[%d] is NULL", s);
+    if (!aligned16(kv[s])) return fail(BPT_ERR_ALIGN, "kv[%d] is not 16-byte aligned", s);
+  }
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], out_b[i], Q, in_b)) return fail(BPT_ERR_ALIAS, "%s overlaps Q", out_names[i]);
+    for (int j = 0; j < 3; ++j)
+      if (j != i && overlap(outs[i], out_b[i], outs[j], out_b[j]))
+        return fail(BPT_ERR_ALIAS, "%s overlaps %s", out_names[i], out_names[j]);
+    for (int s = 0; s < used; ++s)
+      if (overlap(outs[i], out_b[i], kv[s], kv_b)) return fail(BPT_ERR_ALIAS, "%s overlaps kv[%d]", out_names[i], s);
+  }
+  bpt::RingShareLaunch p{};
+  p.batch = desc->batch;
+  p.seq_len = desc->seq_len;
+  p.seq_pad = (int)round_up((size_t)desc->seq_len, 128);
+  p.d_model = desc->d_model;
+  p.n_heads = desc->n_heads;
+  p.d_head = desc->d_model / desc->n_heads;
+  p.causal = desc->causal;
+  p.n_shards = n_shards;
+  p.own = own;
+  p.q = Q;
+  p.kv = kv;
+  p.kv_half_bytes = ring_half_bytes(desc);
+  p.o = O;
+  p.lse = lse;
+  char* ws = static_cast<char*>(workspace);
+  p.q_packed = ws;
+  p.o_acc = reinterpret_cast<float*>(ws + acc_off);
+  p.lse_acc = reinterpret_cast<float*>(ws + lse_off);
+  char msg[256] = "";
+  if (bpt::launch_ring_share(p, hip_stream, msg, sizeof(msg))) return fail(BPT_ERR_HIP, "%s", msg);
+  return BPT_OK;
+}
+
 bpt_status_t bpt_attention_merge(const bpt_attn_desc_t* desc, float* O_acc, float* lse_acc,
                                  const void* O_part, const float* lse_part, void* hip_stream) {
   g_err[0] = 0;

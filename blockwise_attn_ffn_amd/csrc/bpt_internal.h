@@ -54,6 +54,11 @@ struct LayerLaunch {
   void* const* events;
   // optional: attention statistic lse [batch, n_heads, seq_len] fp32
   float* lse;
+  // optional (attention only, ring share): instead of writing O over Q's copy, merge
+  // each finished row into a running state: o_acc fp32 in Q's fragment layout
+  // [batch * seq_pad, d], lse_acc [batch, n_heads, seq_len] (natural log)
+  float* o_acc;
+  float* lse_acc;
 };
 
 // Element counts/byte sizes of the workspace pieces (shared by sizing and carving).
@@ -205,6 +210,35 @@ struct LayerBwdLaunch {
   float* ln_part;       // LN backward column partials: ln_parts x 2 x [d]
 };
 int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t errlen);
+
+// Ring Attention, one device's share (k_ring.hip). A key/value shard in the
+// attention kernels' fragment layouts: K (rows-A) then V^T (cols-A), each
+// [batch * seq_pad, d_model] bf16 on a 256-byte boundary.
+struct RingKvLaunch {
+  int batch, seq_len, seq_pad, d_model, n_heads, d_head;
+  const void *k, *v;   // bf16 row-major [batch * seq_len, d_model]
+  void* kv;            // packed shard
+  size_t half_bytes;   // bytes of each of the two parts
+};
+int launch_ring_pack_kv(const RingKvLaunch& L, void* stream, char* err, size_t errlen);
+
+// The share: this device's query shard against n_shards packed key/value shards
+// (shard s holds the tokens before this device's own shard for s < own, its own
+// shard for s == own); with the causal mask shards after own are not visited and
+// shard own is causal, otherwise every shard is unmasked. The steps' results are
+// merged in the attention kernel's finalisation into o_acc / lse_acc.
+struct RingShareLaunch {
+  int batch, seq_len, seq_pad, d_model, n_heads, d_head, causal, n_shards, own;
+  const void* q;             // bf16 row-major [batch * seq_len, d_model]
+  const void* const* kv;     // HOST array of n_shards device pointers
+  size_t kv_half_bytes;
+  void* o;                   // bf16 row-major [batch * seq_len, d_model]
+  float* lse;                // [batch, n_heads, seq_len]
+  void* q_packed;            // workspace: Q in rows-B fragments
+  float* o_acc;              // workspace: fp32 in the same layout
+  float* lse_acc;            // workspace: [batch, n_heads, seq_len]
+};
+int launch_ring_share(const RingShareLaunch& L, void* stream, char* err, size_t errlen);
 
 // The host (CPU) fused layer: HOST pointers, fp32 arithmetic.
 struct HostLaunch {

@@ -40,6 +40,37 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Ring share: fold a finished row (o * inv, statistic lse_s, natural log) into the
+// running state instead of writing it out. acc points at this wave's first output
+// fragment in the fp32 copy of Q's fragment layout; lane holds 8 features of each
+// of the 2 DT fragments. The state's statistic is read by both lane halves of the
+// row before the lower half writes it back. A row's first merge (lse_acc = -inf)
+// ignores whatever acc held.
+//   lse = ln(e^la + e^ls),  O = e^(la - lse) O_acc + e^(ls - lse) o / l
+template <int DT>
+__device__ inline void merge_row(float* acc, int lane, const f32x16 (&oacc)[DT], float inv, float lse_s,
+                                 float* lse_row, bool real_row, bool writer) {
+  const float la = real_row ? *lse_row : -INFINITY;
+  const float mx = fmaxf(la, lse_s);
+  const float lse = mx + logf(expf(la - mx) + expf(lse_s - mx));
+  const float wa = expf(la - lse), wb = expf(lse_s - lse) * inv;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float* p = acc + (size_t)(2 * t + g) * kFragElems + lane * 8;
+      float a[8];
+      if (wa != 0.f) load8_f32(p, a);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = oacc[t][8 * g + e] * wb;
+        a[e] = wa != 0.f ? fmaf(wa, a[e], v) : v;
+      }
+      store8_f32(p, a);
+    }
+  if (writer && real_row) *lse_row = lse;
+}
+
 // Workgroups per CU the one-group kernel is built for: 2 when its two LDS stages
 // fit 64 KB, else 1; bf16 at d_k 64 with 64-key tiles (32 KB of stages) runs 3,
 // which leaves each wave 170 VGPRs and gives every SIMD a third wave to overlap
@@ -63,12 +94,12 @@ constexpr int attn_wgs_per_cu() {
 // (hi = bf16(v), lo = bf16(v - hi)), so that products keep ~16 significant bits:
 // S = Qhi Khi + Qhi Klo + Qlo Khi and O += Vhi Phi + Vlo Phi + Vhi Plo; O is written
 // as such a pair too. The LDS stage holds the hi fragments, then the lo ones.
-template <typename T, int DK, int BQ, int BKV, bool SPLIT = false, bool MASKED = false>
+template <typename T, int DK, int BQ, int BKV, bool SPLIT = false, bool MASKED = false, bool MERGE = false>
 __global__ __launch_bounds__(BQ * 2, (attn_wgs_per_cu<T, DK, BKV, SPLIT>())) void
 attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* QPlo,
                  const T* __restrict__ KPlo, const T* __restrict__ VPlo, int N, int Np, int H,
                  int G, int d, int causal, int window, int chunk, float scale_log2e, int nqb,
-                 int n_bh, float* lse) {
+                 int n_bh, float* lse, float* o_acc, float* lse_acc) {
   using O = Op<T>;
   using F = typename O::frag;
   constexpr int NW = BQ / 32;
@@ -370,18 +401,25 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
       // softmax normaliser of the scaled scores is exp(ln2 (m_run + log2 l_tot))
       if (lse != nullptr && hf == 0 && qpos < N)
         lse[(size_t)c.bh * N + qpos] = (m_run + log2f(l_tot)) * kLn2;
+      // the ring share's merge (instances for bf16 operands only: fp32 fragments
+      // have two pieces)
+      if constexpr (MERGE && sizeof(T) == 2 && !SPLIT) {
+        merge_row<DT>(o_acc + (qp - QP), lane, oacc, inv, (m_run + log2f(l_tot)) * kLn2,
+                      lse_acc + (size_t)c.bh * N + min(qpos, N - 1), qpos < N, hf == 0);
+      } else {
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
+        for (int t = 0; t < DT; ++t) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          float v[8];
+          for (int g = 0; g < 2; ++g) {
+            float v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = oacc[t][8 * g + e] * inv;
-          st_packed(qp + (2 * t + g) * kFragElems, lane, v);
-          if constexpr (SPLIT) {
+            for (int e = 0; e < 8; ++e) v[e] = oacc[t][8 * g + e] * inv;
+            st_packed(qp + (2 * t + g) * kFragElems, lane, v);
+            if constexpr (SPLIT) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] -= bf16_round(v[e]);
-            st_packed(QPlo + (qp - QP) + (2 * t + g) * kFragElems, lane, v);
+              for (int e = 0; e < 8; ++e) v[e] -= bf16_round(v[e]);
+              st_packed(QPlo + (qp - QP) + (2 * t + g) * kFragElems, lane, v);
+            }
           }
         }
       }
@@ -434,11 +472,11 @@ attention_kernel(T* QP, const T* __restrict__ KP, const T* __restrict__ VP, T* Q
 // step k+1, when they are first read. Work units are pairs of super-blocks
 // (S-1-p, p) with the causal mask, as for the one-group kernel.
 // ---------------------------------------------------------------------------
-template <int DK, int BKV, bool MASKED = false>
+template <int DK, int BKV, bool MASKED = false, bool MERGE = false>
 __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
     bf16* QP, const bf16* __restrict__ KP, const bf16* __restrict__ VP, int N, int Np, int H,
     int G, int d, int causal, int window, int chunk, float scale_log2e, int nqb, int n_bh,
-    float* lse) {
+    float* lse, float* o_acc, float* lse_acc) {
   using O = Op<bf16>;
   using F = O::frag;
   constexpr int BQ = 128, NWG = 4, FB = 1024;
@@ -599,14 +637,19 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
         const int qpos = qb * BQ + wq * 32 + rho;
         if (lse != nullptr && hf == 0 && qpos < N)
           lse[(size_t)cp.bh * N + qpos] = (m_run + log2f(l_tot)) * kLn2;
+        if constexpr (MERGE) {
+          merge_row<DT>(o_acc + (qp - QP), lane, oacc, inv, (m_run + log2f(l_tot)) * kLn2,
+                        lse_acc + (size_t)cp.bh * N + min(qpos, N - 1), qpos < N, hf == 0);
+        } else {
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
+          for (int t = 0; t < DT; ++t) {
 #pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            float v[8];
+            for (int g = 0; g < 2; ++g) {
+              float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = oacc[t][8 * g + e] * inv;
-            st_packed(qp + (2 * t + g) * kFragElems, lane, v);
+              for (int e = 0; e < 8; ++e) v[e] = oacc[t][8 * g + e] * inv;
+              st_packed(qp + (2 * t + g) * kFragElems, lane, v);
+            }
           }
         }
       }
@@ -764,10 +807,24 @@ int run_attn(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const bool general = L.window || L.chunk || L.n_kv_heads != L.n_heads;
   auto kern = general ? attention_kernel<T, DK, BQ, BKV, SPLIT, true>
                       : attention_kernel<T, DK, BQ, BKV, SPLIT, false>;
+  if (L.o_acc != nullptr) {
+    // the ring share's merging instance exists for the tiling it uses at d_k 64
+    bool have = false;
+    if constexpr (sizeof(T) == 2 && !SPLIT && DK == 64 && BQ == 128 && BKV == 64) {
+      if (!general) {
+        kern = attention_kernel<T, DK, BQ, BKV, SPLIT, false, true>;
+        have = true;
+      }
+    }
+    if (!have) {
+      set_err(err, n, "attention: no merging instance for this shape%s", "");
+      return 1;
+    }
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(BQ * 2), 0, s,
                      (T*)L.q, (const T*)L.k, (const T*)L.vt, (T*)L.q_lo, (const T*)L.k_lo,
                      (const T*)L.vt_lo, L.seq_len, L.seq_pad, L.n_heads, L.n_kv_heads, L.d_model,
-                     L.causal, L.window, L.chunk, scale, nqb, n_bh, L.lse);
+                     L.causal, L.window, L.chunk, scale, nqb, n_bh, L.lse, L.o_acc, L.lse_acc);
   return check_launch("attention", err, n);
 }
 
@@ -782,9 +839,24 @@ int run_attn_pair(const LayerLaunch& L, hipStream_t s, char* err, size_t n) {
   const float scale = 1.4426950408889634f / sqrtf((float)DK);
   const bool general = L.window || L.chunk || L.n_kv_heads != L.n_heads;
   auto kern = general ? attention_pair_kernel<DK, BKV, true> : attention_pair_kernel<DK, BKV, false>;
+  if (L.o_acc != nullptr) {
+    // the ring share's merging instance exists for the tiling it uses at d_k 128
+    bool have = false;
+    if constexpr (DK == 128 && BKV == 64) {
+      if (!general) {
+        kern = attention_pair_kernel<DK, BKV, false, true>;
+        have = true;
+      }
+    }
+    if (!have) {
+      set_err(err, n, "attention: no merging instance for this shape%s", "");
+      return 1;
+    }
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, (bf16*)L.q,
                      (const bf16*)L.k, (const bf16*)L.vt, L.seq_len, L.seq_pad, L.n_heads,
-                     L.n_kv_heads, L.d_model, L.causal, L.window, L.chunk, scale, nqb, n_bh, L.lse);
+                     L.n_kv_heads, L.d_model, L.causal, L.window, L.chunk, scale, nqb, n_bh, L.lse,
+                     L.o_acc, L.lse_acc);
   return check_launch("attention", err, n);
 }
 

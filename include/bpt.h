@@ -280,7 +280,43 @@ bpt_status_t bpt_attention_fwd(const bpt_attn_desc_t* desc, const void* Q, const
 bpt_status_t bpt_attention_merge(const bpt_attn_desc_t* desc, float* O_acc, float* lse_acc,
                                  const void* O_part, const float* lse_part, void* hip_stream);
 
-/* bpt_layer_fwd for callers that cannot allocate device memory: code under HIP
+/* One device's share of Ring Attention with the shards kept in the attention
+ * kernels' layout ("Blockwise Parallel Transformer — BPT", aicassindra.com,
+ * section "BPT and Ring Attention": each device keeps its query shard while the
+ * key/value shards travel around the ring; each arrived shard is one more block
+ * source for the inner loop). A device packs its own key/value shard once
+ * (bpt_ring_pack_kv) and the packed shard is what travels; the share then runs its
+ * query shard against every arrived shard and merges the steps' results inside
+ * the attention kernel, as each row finishes, through the saved statistic
+ * (lse = ln(e^a + e^b), O = e^(a - lse) O_a + e^(b - lse) O_b): no per-step copies
+ * of Q, O or K/V and no separate merge pass.
+ *  - desc: one shard's shape (batch sequences of seq_len tokens each), dtype
+ *    BPT_BF16, window = chunk = 0, n_kv_heads 0 or n_heads.
+ *  - bpt_ring_kv_bytes: bytes of a packed shard (K then V^T, each [batch * Np,
+ *    d_model] bf16, Np = seq_len rounded up to 128); 0 (bpt_last_error set) when
+ *    desc is invalid or an empty call.
+ *  - bpt_ring_pack_kv: K, V DEVICE bf16 [batch * seq_len, d_model] row-major ->
+ *    kv (DEVICE, kv_bytes >= bpt_ring_kv_bytes, overlapping neither K nor V).
+ *  - bpt_ring_share_fwd: Q DEVICE bf16 [batch * seq_len, d_model]; kv a HOST
+ *    array of n_shards (1..4096) DEVICE pointers to packed shards, shard s holding
+ *    the tokens [s seq_len, (s + 1) seq_len) of the whole sequence and own the
+ *    index of Q's shard. With desc->causal = 1, shards s < own are seen whole,
+ *    shard own with the causal mask and shards s > own not at all (their pointers
+ *    may be NULL); with causal = 0 every shard is seen whole. Writes O (DEVICE
+ *    bf16 [batch * seq_len, d_model]) and lse (DEVICE fp32 [batch, n_heads,
+ *    seq_len], the natural-log statistic over every key the rows saw). Workspace:
+ *    bpt_ring_share_workspace_bytes (Q packed, an fp32 running output [batch * Np,
+ *    d_model] and the running statistic). O, lse and the workspace overlap no
+ *    other buffer; pointers 16-byte aligned; asynchronous on hip_stream. */
+size_t bpt_ring_kv_bytes(const bpt_attn_desc_t* desc);
+bpt_status_t bpt_ring_pack_kv(const bpt_attn_desc_t* desc, const void* K, const void* V, void* kv,
+                              size_t kv_bytes, void* hip_stream);
+size_t bpt_ring_share_workspace_bytes(const bpt_attn_desc_t* desc);
+bpt_status_t bpt_ring_share_fwd(const bpt_attn_desc_t* desc, int32_t n_shards, int32_t own,
+                                const void* Q, const void* const* kv, void* O, float* lse,
+                                void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* bpt_layer_fwd for callers that cannot allocate device memory/* bpt_layer_fwd for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
  * workspace is not passed in: the library carves it from a fixed device array of
  * BPT_NOALLOC_SCRATCH_BYTES bytes that each GPU it runs on holds from the first

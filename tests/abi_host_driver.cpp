@@ -45,6 +45,17 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void*, char*, size_t) {
   ++g_layer_bwd_launches;
   return 0;
 }
+static int g_ring_pack = 0, g_ring_share = 0;
+static RingShareLaunch g_ring;
+int launch_ring_pack_kv(const RingKvLaunch&, void*, char*, size_t) {
+  ++g_ring_pack;
+  return 0;
+}
+int launch_ring_share(const RingShareLaunch& L, void*, char*, size_t) {
+  g_ring = L;
+  ++g_ring_share;
+  return 0;
+}
 // the no-allocation entry point's fixed scratch: a fake device address
 static int g_scratch_queries = 0;
 int noalloc_scratch(void** ptr, char*, size_t) {
@@ -312,6 +323,34 @@ int main() {
     bd.precision = 1;
     EXPECT(bpt_layer_bwd_workspace_bytes(&bd) == 0);
     EXPECT(bpt::g_layer_bwd_launches == 1);
+  }
+  // the ring share: packing and the share reach their launchers with the carve-up
+  {
+    bpt_attn_desc_t ad{};
+    ad.batch = 1; ad.seq_len = 300; ad.d_model = 256; ad.n_heads = 2; ad.causal = 1; ad.dtype = BPT_BF16;
+    const size_t kvb = bpt_ring_kv_bytes(&ad);
+    EXPECT(kvb == 2 * (size_t)384 * 256 * 2);
+    EXPECT(bpt_ring_pack_kv(&ad, fake(0), fake(1ull << 30), fake(2ull << 30), kvb, nullptr) == BPT_OK);
+    EXPECT(bpt_ring_pack_kv(&ad, fake(0), fake(1ull << 30), fake(2ull << 30), kvb - 1, nullptr) == BPT_ERR_WORKSPACE);
+    EXPECT(bpt_ring_pack_kv(&ad, fake(0), fake(1ull << 30), fake(64), kvb, nullptr) == BPT_ERR_ALIAS);
+    const void* shards[4] = {fake(3ull << 30), fake(4ull << 30), fake(5ull << 30), nullptr};
+    const size_t wsb = bpt_ring_share_workspace_bytes(&ad);
+    EXPECT(wsb > 0);
+    float* rl = reinterpret_cast<float*>(fake(7ull << 30));
+    EXPECT(bpt_ring_share_fwd(&ad, 4, 2, fake(0), shards, fake(6ull << 30), rl, fake(8ull << 30), wsb, nullptr) == BPT_OK);
+    EXPECT(bpt::g_ring_share == 1 && bpt::g_ring.own == 2 && bpt::g_ring.n_shards == 4 && bpt::g_ring.seq_pad == 384);
+    EXPECT((char*)bpt::g_ring.o_acc == fake(8ull << 30) + (size_t)384 * 256 * 2);
+    // a shard the causal share reads may not be NULL; without the mask every one is read
+    EXPECT(bpt_ring_share_fwd(&ad, 4, 3, fake(0), shards, fake(6ull << 30), rl, fake(8ull << 30), wsb, nullptr) == BPT_ERR_NULL);
+    ad.causal = 0;
+    EXPECT(bpt_ring_share_fwd(&ad, 4, 2, fake(0), shards, fake(6ull << 30), rl, fake(8ull << 30), wsb, nullptr) == BPT_ERR_NULL);
+    ad.causal = 1;
+    EXPECT(bpt_ring_share_fwd(&ad, 4, 4, fake(0), shards, fake(6ull << 30), rl, fake(8ull << 30), wsb, nullptr) == BPT_ERR_SHAPE);
+    EXPECT(bpt_ring_share_fwd(&ad, 4, 2, fake(0), shards, fake(3ull << 30), rl, fake(8ull << 30), wsb, nullptr) == BPT_ERR_ALIAS);
+    EXPECT(bpt_ring_share_fwd(&ad, 4, 2, fake(0), shards, fake(6ull << 30), rl, fake(8ull << 30), wsb - 1, nullptr) == BPT_ERR_WORKSPACE);
+    ad.window = 8;
+    EXPECT(bpt_ring_kv_bytes(&ad) == 0 && bpt_ring_share_workspace_bytes(&ad) == 0);
+    EXPECT(bpt::g_ring_share == 1 && bpt::g_ring_pack == 1);
   }
   if (!g_fail) printf("ALL OK\n");
   return g_fail;
