@@ -70,54 +70,59 @@ __device__ inline float gelu_tanh_grad(float u) {
 namespace {
 
 constexpr int kGBM = 256, kGBN = 128, kGBK = 32;
-constexpr int kGLd = kGBK + 8;   // LDS row stride in elements (padding against bank conflicts)
+constexpr int kGStageA = kGBM * kGBK * 2;          // bytes of A per stage (16 KB)
+constexpr int kGStage = (kGBM + kGBN) * kGBK * 2;  // bytes per stage (24 KB)
+constexpr int kGCopies = kGStage / 1024 / 4;        // 1 KB copies per wave and stage (6)
 
-// One k-tile of an operand into registers: ROWS rows x 32 k = ROWS x 4 chunks of
-// 8 consecutive k (16 bytes), ROWS / 64 per thread. A chunk that straddles K is
-// read element by element with zeros past K, so K need not be a multiple of 8.
-template <int ROWS>
-struct TileLoad {
-  static constexpr int NC = ROWS / 64;
-  uint4 v[NC];
-  __device__ void load(const bf16* p, int ld, int rows, int K, int r0, int k0, int tid) {
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 2, kc = (c & 3) * 8;
-      const int gr = r0 + r, gk = k0 + kc;
-      const bf16* src = p + (size_t)gr * ld + gk;
-      if (gr < rows && gk + 8 <= K) {
-        v[i] = *reinterpret_cast<const uint4*>(src);
-      } else {
-        bf16 e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = (gr < rows && gk + j < K) ? src[j] : (bf16)0.0f;
-        v[i] = *reinterpret_cast<const uint4*>(e);
-      }
-    }
-  }
-  __device__ void store(bf16* s, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(s + (c >> 2) * kGLd + (c & 3) * 8) = v[i];
-    }
-  }
-};
+// LDS layout of a stage: the 16-byte chunk (row r, k-chunk c of 4) of an operand
+// tile sits in slot 4 r + (c ^ ((r >> 2) & 3)). The copies write 64 consecutive
+// slots per wave instruction (the LDS-DMA path puts lane l at slot base + l), and a
+// fragment read (32 consecutive rows, one chunk) hits 16 distinct 16-byte bank
+// groups in every 16 lanes.
+__device__ inline int chunk_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+
+// Workgroup barrier without a memory fence (__syncthreads() would also wait for
+// every copy in flight, including the two k-tiles ahead).
+__device__ inline void stage_barrier_bwd() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One k-step's fragments from a stage: A rows at a + 2 KB i (i < 4), B rows at b +
+// 2 KB j (j < 2), LDS byte addresses, with the wait for them in the same statement.
+// Reads written in C++ would make the compiler wait first for every LDS copy in
+// flight (it cannot tell that the copies target other stages).
+__device__ inline void ld_frags6(uint32_t a, uint32_t b, bf16x8 (&af)[4], bf16x8 (&bf)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %6 offset:0\n\t"
+      "ds_read_b128 %1, %6 offset:2048\n\t"
+      "ds_read_b128 %2, %6 offset:4096\n\t"
+      "ds_read_b128 %3, %6 offset:6144\n\t"
+      "ds_read_b128 %4, %7 offset:0\n\t"
+      "ds_read_b128 %5, %7 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(af[0]), "=v"(af[1]), "=v"(af[2]), "=v"(af[3]), "=v"(bf[0]), "=v"(bf[1])
+      : "v"(a), "v"(b));
+}
 
 }  // namespace
 
 // 256 threads = 4 waves in 2 x 2, each 128 x 64 of the 256 x 128 tile (4 x 2
-// products of 32 x 32 per k-step: 6 fragment reads from LDS for 8 products). Two
-// LDS buffers per operand (60 KB, two workgroups per CU): k-tile t + 1 is loaded
-// into registers while t is multiplied, then stored into the other buffer.
-// (Measured alternatives on the 64 x 1024-token layer backward: 128 x 128 tiles of
-// 64 x 64 per wave 21.2 ms; 64-wide k-tiles in one buffer 27.2 ms, with spills;
-// this form 20.9 ms.)
+// products of 32 x 32 per k-step: 6 fragment reads from LDS for 8 products). The
+// k-tiles (32 wide) are copied global -> LDS by the LDS-DMA path into three stages,
+// two k-tiles ahead of the products (the copy of tile t + 2 is issued once tile t
+// has landed), so the loads' latency is covered by two tiles of products and no
+// registers stage the data. Rows past M or N read row M - 1 (N - 1), and chunks past
+// K read chunk 0: finite values whose products land in discarded outputs or are
+// zeroed in the last k-tile's fragments.
+// (Measured on the 64 x 1024-token layer backward: registers staging one k-tile
+// ahead 20.9 ms; without its LDS stores, a timing copy, 10.7 ms.)
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdGemm g) {
-  __shared__ __align__(16) bf16 As[2][kGBM * kGLd];
-  __shared__ __align__(16) bf16 Bs[2][kGBN * kGLd];
+  __shared__ __align__(16) unsigned char st0[kGStage];
+  __shared__ __align__(16) unsigned char st1[kGStage];
+  __shared__ __align__(16) unsigned char st2[kGStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -140,49 +145,88 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdGemm g) {
   const int ke = min(g.K, kb + g.k_per_split);
   const int nkt = ke > kb ? (ke - kb + kGBK - 1) / kGBK : 0;
 
+  // this wave's copies: A instructions [4 wave, 4 wave + 4), B [2 wave, 2 wave + 2);
+  // per copy the source row and k-chunk of this lane (fixed over the k-tiles)
+  const bf16* src[kGCopies];
+  int ck[kGCopies];
+#pragma unroll
+  for (int q = 0; q < kGCopies; ++q) {
+    const bool isa = q < 4;
+    const int slot = (isa ? 4 * wave + q : 2 * wave + (q - 4)) * 64 + lane;
+    const int r = slot >> 2, c = (slot & 3) ^ ((r >> 2) & 3);
+    const int rows = isa ? g.M : g.N, r0 = isa ? m0 : n0;
+    const int gr = min(r0 + r, rows - 1);
+    src[q] = (isa ? g.a + (size_t)gr * g.lda : g.b + (size_t)gr * g.ldb);
+    ck[q] = 8 * c;
+  }
+  auto issue = [&](int t, unsigned char* st) __attribute__((always_inline)) {
+    const int k0 = kb + t * kGBK;
+#pragma unroll
+    for (int q = 0; q < kGCopies; ++q) {
+      const int gk = k0 + ck[q] < ke ? k0 + ck[q] : 0;
+      unsigned char* dst = st + (q < 4 ? (4 * wave + q) * 1024 : kGStageA + (2 * wave + (q - 4)) * 1024);
+      dma16(src[q] + gk, dst);
+    }
+  };
+
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  TileLoad<kGBM> la;
-  TileLoad<kGBN> lb;
-  if (nkt > 0) {
-    la.load(g.a, g.lda, g.M, ke, m0, kb, tid);
-    lb.load(g.b, g.ldb, g.N, ke, n0, kb, tid);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
-  }
-  __syncthreads();
-  for (int t = 0; t < nkt; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < nkt) {
-      la.load(g.a, g.lda, g.M, ke, m0, kb + (t + 1) * kGBK, tid);
-      lb.load(g.b, g.ldb, g.N, ke, n0, kb + (t + 1) * kGBK, tid);
-    }
+  // byte offsets within a stage of this lane's fragment rows for k-step ks: row r
+  // = 32 q + (lane & 31) (q a multiple of 32 rows) sits at 64 r + 16 (c ^ ((r >> 2) &
+  // 3)), c = 2 ks + lane / 32, and (r >> 2) & 3 depends on the lane only
+  uint32_t lofs[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    lofs[ks] = 64u * (uint32_t)(lane & 31) + 16u * (uint32_t)((2 * ks + (lane >> 5)) ^ ((lane >> 2) & 3));
+  const uint32_t aofs = 64u * 128u * (uint32_t)wm, bofs = (uint32_t)kGStageA + 64u * 64u * (uint32_t)wn;
+  auto compute = [&](int t, const unsigned char* st) __attribute__((always_inline)) {
+    const int k0 = kb + t * kGBK;
+    const bool edge = k0 + kGBK > ke;   // the last k-tile runs past K
+    const uint32_t sb = (uint32_t)(uintptr_t)st;   // LDS byte address of the stage
 #pragma unroll
     for (int ks = 0; ks < kGBK / 16; ++ks) {
+      const int c = 2 * ks + (lane >> 5);
       bf16x8 af[4], bfr[2];
+      ld_frags6(sb + aofs + lofs[ks], sb + bofs + lofs[ks], af, bfr);
+      if (edge) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * 128 + i * 32 + (lane & 31)) * kGLd + ks * 16 +
-                                                        8 * (lane >> 5)]);
+        for (int e = 0; e < 8; ++e) {
+          if (k0 + 8 * c + e >= ke) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][(wn * 64 + j * 32 + (lane & 31)) * kGLd + ks * 16 +
-                                                         8 * (lane >> 5)]);
+            for (int i = 0; i < 4; ++i) af[i][e] = (bf16)0.0f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bfr[j][e] = (bf16)0.0f;
+          }
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (t + 1 < nkt) {
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
-    }
-    __syncthreads();
+  };
+
+  if (nkt > 0) issue(0, st0);
+  if (nkt > 1) issue(1, st1);
+  // step t: wait for this wave's copies of tile t (those of t + 1 may still run),
+  // barrier (every wave's copies of t landed; every wave is done with t - 1, whose
+  // stage takes t + 2), issue t + 2, multiply t
+  auto step = [&](int t, const unsigned char* rd, unsigned char* wr) __attribute__((always_inline)) {
+    if (t + 1 < nkt) __builtin_amdgcn_s_waitcnt(0x0070 | kGCopies);
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    stage_barrier_bwd();
+    if (t + 2 < nkt) issue(t + 2, wr);
+    compute(t, rd);
+  };
+  for (int t = 0; t < nkt; t += 3) {
+    step(t, st0, st2);
+    if (t + 1 < nkt) step(t + 1, st1, st0);
+    if (t + 2 < nkt) step(t + 2, st2, st1);
   }
 
   // C layout: lane l holds column l % 32; register q holds row 8 (q / 4) + 4 (l / 32) + q % 4

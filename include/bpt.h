@@ -316,7 +316,7 @@ bpt_status_t bpt_ring_share_fwd(const bpt_attn_desc_t* desc, int32_t n_shards, i
                                 const void* Q, const void* const* kv, void* O, float* lse,
                                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* bpt_layer_fwd for callers that cannot allocate device memory/* bpt_layer_fwd for callers that cannot allocate device memory: code under HIP
+/* bpt_layer_fwd for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
  * workspace is not passed in: the library carves it from a fixed device array of
  * BPT_NOALLOC_SCRATCH_BYTES bytes that each GPU it runs on holds from the first
