@@ -817,15 +817,16 @@ bpt_status_t validate_bwd_desc(const bpt_layer_desc_t* d) {
 }
 
 // Byte offsets of the backward's workspace pieces. Buffers that are dead by the
-// time a later one is written share its space: dA over dZ (bf16), dQ/dK/dV in
-// bf16 over Q, K, V, dQ over Y and dLN1 over dLN2 (fp32); of the transposed
-// copies, dY^T over dZ^T, dQ^T over LN2(Y)^T and dK^T over A^T.
+// time a later one is written share its space: dA over dZ (bf16), [dQ dK dV] in
+// bf16 ([rows, 3d]) over Q, K, V (one piece of 3 [rows, d]), dQ over Y and dLN1
+// over dLN2 (fp32); of the transposed copies, dY^T over dZ^T, dQ^T over LN2(Y)^T
+// and dK^T over A^T.
 struct BwdLayout {
   size_t x1, q, k, v, attn, y2, dzb, dyb;   // bf16 [rows, d]
   size_t x1t, attnt, y2t, dzt, dvt;         // bf16 [d, rows_t]
   size_t y, dy2, dy, dk, dv;                // fp32 [rows, d]
   size_t stats1, stats2, lse_re, stat_d, stat_l2, packed[3];
-  size_t ublk, hblk, dublk, dub, wt[6], partials, ln_part, total;
+  size_t ublk, hblk, dublk, dub, wt[4], partials, ln_part, total;
   int block_rows, blk_ld, rows_t, wgrad_splits, ffn_splits, ln_parts;
 };
 
@@ -839,7 +840,7 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   L.blk_ld = (int)round_up((size_t)L.block_rows, 8);
   L.rows_t = (int)round_up(rows, 8);
   // the product kernel's tiles are 256 x 128
-  auto tiles_of = [](size_t m, size_t n) { return ((m + 255) / 256) * ((n + 127) / 128); };
+  auto tiles_of = [](size_t m, size_t n) { return ((m + 255) / 256) * ((n + 255) / 256); };
   const size_t tiles = tiles_of(dm, dm);
   size_t splits = (512 + tiles - 1) / tiles;
   if (splits > 16) splits = 16;
@@ -863,7 +864,7 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
     return o;
   };
   const size_t rb = rows * dm * 2, rf = rows * dm * 4, tb = dm * (size_t)L.rows_t * 2;
-  L.x1 = take(rb); L.q = take(rb); L.k = take(rb); L.v = take(rb);
+  L.x1 = take(rb); L.q = take(3 * rb); L.k = L.q + rb; L.v = L.q + 2 * rb;
   L.attn = take(rb); L.y2 = take(rb); L.dzb = take(rb); L.dyb = take(rb);
   L.x1t = take(tb); L.attnt = take(tb); L.y2t = take(tb); L.dzt = take(tb); L.dvt = take(tb);
   L.y = take(rf); L.dy2 = take(rf); L.dy = take(rf); L.dk = take(rf); L.dv = take(rf);
@@ -879,7 +880,8 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   L.dub = take((size_t)L.block_rows * f * 2);
   L.wt[0] = take(dm * f * 2);   // W_1^T
   L.wt[1] = take(dm * f * 2);   // W_2^T
-  for (int i = 2; i < 6; ++i) L.wt[i] = take(dm * dm * 2);   // W_O^T, W_Q^T, W_K^T, W_V^T
+  L.wt[2] = take(dm * dm * 2);       // W_O^T
+  L.wt[3] = take(3 * dm * dm * 2);   // W_Q^T | W_K^T | W_V^T
   const size_t pw = splits > 1 ? splits * dm * dm * 4 : 0, pf = fsplits > 1 ? fsplits * dm * f * 4 : 0;
   L.partials = take(pw > pf ? pw : pf);
   L.ln_part = take((size_t)L.ln_parts * 2 * dm * 4);
@@ -973,9 +975,7 @@ bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
   p.dzb = ws + W.dzb;
   p.dyb = ws + W.dyb;
   p.da = ws + W.dzb;    // dZ (bf16) is dead once the FFN blocks are done
-  p.dqb = ws + W.q;     // Q, K, V are dead once the attention backward is done
-  p.dkb = ws + W.k;
-  p.dvb = ws + W.v;
+  p.dqkvb = ws + W.q;   // Q, K, V are dead once the attention backward is done
   p.x1t = ws + W.x1t;
   p.attnt = ws + W.attnt;
   p.y2t = ws + W.y2t;
@@ -990,9 +990,7 @@ bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
   p.w1t = ws + W.wt[0];
   p.w2t = ws + W.wt[1];
   p.wot = ws + W.wt[2];
-  p.wqt = ws + W.wt[3];
-  p.wkt = ws + W.wt[4];
-  p.wvt = ws + W.wt[5];
+  p.wqkvt = ws + W.wt[3];
   p.ublk = F(W.ublk);
   p.y = F(W.y);
   p.dy2 = F(W.dy2);

@@ -195,12 +195,14 @@ struct LayerBwdLaunch {
   float* dx;          // fp32 [rows, d]
   bpt_layer_grads_t g;
   // workspace (see bpt_api.cpp: bwd_layout for sizes and the reuse of dead buffers)
-  void *x1, *q, *k, *v, *attn, *y2, *dzb, *dyb, *da, *dqb, *dkb, *dvb;   // bf16 [rows, d]
+  void *x1, *q, *k, *v, *attn, *y2, *dzb, *dyb, *da;   // bf16 [rows, d]
+  void* dqkvb;          // bf16 [rows, 3d]: dQ | dK | dV per row
   void *x1t, *attnt, *y2t, *dzt, *dyt, *dqt, *dkt, *dvt;                 // bf16 [d, rows_t]
   void *hblk, *dublk;   // bf16 [d_ff, blk_ld]: H^T and dU^T of the block
   float* ublk;          // fp32 [d_ff, blk_ld]: U^T of the block
   void* dub;            // bf16 [block_rows, d_ff]: dU of the block
-  void *w1t, *w2t, *wot, *wqt, *wkt, *wvt;   // bf16 weights transposed: [d, d_ff], [d_ff, d], [d, d] x 4
+  void *w1t, *w2t, *wot;   // bf16 weights transposed: [d, d_ff], [d_ff, d], [d, d]
+  void* wqkvt;              // bf16 [d, 3d]: W_Q^T | W_K^T | W_V^T
   float *y, *dy2, *dy, *dq, *dk, *dv, *dx1;   // fp32 [rows, d]
   float *stats1, *stats2;   // (mean, rstd) per row: 2 floats each
   float* lse_re;        // the recomputed forward's statistic (not used further)

@@ -69,10 +69,10 @@ __device__ inline float gelu_tanh_grad(float u) {
 
 namespace {
 
-constexpr int kGBM = 256, kGBN = 128, kGBK = 32;
+constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
 constexpr int kGStageA = kGBM * kGBK * 2;          // bytes of A per stage (16 KB)
 constexpr int kGStage = (kGBM + kGBN) * kGBK * 2;  // bytes per stage (24 KB)
-constexpr int kGCopies = kGStage / 1024 / 4;        // 1 KB copies per wave and stage (6)
+constexpr int kGCopies = kGStage / 1024 / 8;        // 1 KB copies per wave and stage (4)
 
 // LDS layout of a stage: the 16-byte chunk (row r, k-chunk c of 4) of an operand
 // tile sits in slot 4 r + (c ^ ((r >> 2) & 3)). The copies write 64 consecutive
@@ -108,7 +108,7 @@ __device__ inline void ld_frags6(uint32_t a, uint32_t b, bf16x8 (&af)[4], bf16x8
 
 }  // namespace
 
-// 256 threads = 4 waves in 2 x 2, each 128 x 64 of the 256 x 128 tile (4 x 2
+// 512 threads = 8 waves in 2 x 4, each 128 x 64 of the 256 x 256 tile (4 x 2
 // products of 32 x 32 per k-step: 6 fragment reads from LDS for 8 products). The
 // k-tiles (32 wide) are copied global -> LDS by the LDS-DMA path into three stages,
 // two k-tiles ahead of the products (the copy of tile t + 2 is issued once tile t
@@ -117,15 +117,16 @@ __device__ inline void ld_frags6(uint32_t a, uint32_t b, bf16x8 (&af)[4], bf16x8
 // K read chunk 0: finite values whose products land in discarded outputs or are
 // zeroed in the last k-tile's fragments.
 // (Measured on the 64 x 1024-token layer backward: registers staging one k-tile
-// ahead 20.9 ms; without its LDS stores, a timing copy, 10.7 ms.)
+// ahead 20.9 ms; without its LDS stores, a timing copy, 10.7 ms; this form with 4
+// waves on 256 x 128 tiles 12.55 ms, with 8 waves on 256 x 256 tiles 12.2 ms.)
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdGemm g) {
+__global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
   __shared__ __align__(16) unsigned char st0[kGStage];
   __shared__ __align__(16) unsigned char st1[kGStage];
   __shared__ __align__(16) unsigned char st2[kGStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   // Tile order: workgroups are dealt to the 8 XCDs round-robin; when the tile
   // count divides by 8, XCD x takes a contiguous range of tiles, walked in groups
   // of 4 M-tiles across N, so the tiles an XCD runs together share operand rows in
@@ -151,8 +152,8 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdGemm g) {
   int ck[kGCopies];
 #pragma unroll
   for (int q = 0; q < kGCopies; ++q) {
-    const bool isa = q < 4;
-    const int slot = (isa ? 4 * wave + q : 2 * wave + (q - 4)) * 64 + lane;
+    const bool isa = q < 2;
+    const int slot = (isa ? 2 * wave + q : 2 * wave + (q - 2)) * 64 + lane;
     const int r = slot >> 2, c = (slot & 3) ^ ((r >> 2) & 3);
     const int rows = isa ? g.M : g.N, r0 = isa ? m0 : n0;
     const int gr = min(r0 + r, rows - 1);
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdGemm g) {
 #pragma unroll
     for (int q = 0; q < kGCopies; ++q) {
       const int gk = k0 + ck[q] < ke ? k0 + ck[q] : 0;
-      unsigned char* dst = st + (q < 4 ? (4 * wave + q) * 1024 : kGStageA + (2 * wave + (q - 4)) * 1024);
+      unsigned char* dst = st + (q < 2 ? (2 * wave + q) * 1024 : kGStageA + (2 * wave + (q - 2)) * 1024);
       dma16(src[q] + gk, dst);
     }
   };
@@ -421,11 +422,11 @@ __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict
 
 // out[c, r] = in[r, c] (bf16 out; ld_out >= nr) for in [nr, nc] with row stride
 // ld_in, through a 64 x 64 LDS tile: reads coalesced along c, writes along r. With
-// out_rm, also a bf16 row-major copy of in (row stride ld_in), for fp32 inputs.
+// out_rm, also a bf16 row-major copy of in (row stride ld_rm), for fp32 inputs.
 template <typename TIn>
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(const TIn* __restrict__ in, int nr, int nc, int ld_in,
                                                             bf16* __restrict__ out, int ld_out,
-                                                            bf16* __restrict__ out_rm) {
+                                                            bf16* __restrict__ out_rm, int ld_rm) {
   __shared__ bf16 tile[64][66];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
@@ -434,9 +435,8 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const TIn* __restric
     const int r = 4 * i + tr;
     bf16 v = (bf16)0.0f;
     if (r0 + r < nr && c0 + tc < nc) {
-      const size_t o = (size_t)(r0 + r) * ld_in + c0 + tc;
-      v = (bf16)(float)in[o];
-      if (out_rm) out_rm[o] = v;
+      v = (bf16)(float)in[(size_t)(r0 + r) * ld_in + c0 + tc];
+      if (out_rm) out_rm[(size_t)(r0 + r) * ld_rm + c0 + tc] = v;
     }
     tile[r][tc] = v;
   }
@@ -460,7 +460,7 @@ int run_bwd_gemm(const BwdGemm& g0, int splits, hipStream_t s, const char* what,
   splits = (g.K + g.k_per_split - 1) / g.k_per_split;
   if (splits < 1) splits = 1;
   dim3 grid((g.N + kGBN - 1) / kGBN, (g.M + kGBM - 1) / kGBM, splits);
-  hipLaunchKernelGGL((bwd_gemm_kernel<MODE>), grid, dim3(256), 0, s, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE>), grid, dim3(512), 0, s, g);
   return check_launch(what, err, n);
 }
 
@@ -486,10 +486,10 @@ int run_bwd_gemm_split(BwdGemm g, int splits, float* partials, bool accumulate, 
 
 template <typename TIn>
 int transpose(const TIn* in, int nr, int nc, int ld_in, bf16* out, int ld_out, bf16* out_rm, hipStream_t s,
-              char* err, size_t n) {
+              char* err, size_t n, int ld_rm = 0) {
   if (nr <= 0 || nc <= 0) return 0;
   hipLaunchKernelGGL(bwd_transpose_kernel<TIn>, dim3((nc + 63) / 64, (nr + 63) / 64), dim3(256), 0, s, in, nr, nc,
-                     ld_in, out, ld_out, out_rm);
+                     ld_in, out, ld_out, out_rm, ld_rm ? ld_rm : ld_in);
   return check_launch("bwd_transpose", err, n);
 }
 
@@ -529,8 +529,8 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
   bf16 *const dyt = B(L.dyt), *const da = B(L.da);
   bf16 *const hblk = B(L.hblk), *const dublk = B(L.dublk), *const dub = B(L.dub);
   bf16 *const w1t = B(L.w1t), *const w2t = B(L.w2t), *const wot = B(L.wot);
-  bf16* const wqkvt[3] = {B(L.wqt), B(L.wkt), B(L.wvt)};
-  bf16* const dqkvb[3] = {B(L.dqb), B(L.dkb), B(L.dvb)};
+  bf16* const wqkvt = B(L.wqkvt);   // [d, 3d]: W_Q^T | W_K^T | W_V^T
+  bf16* const dqkvb = B(L.dqkvb);   // [rows, 3d]: dQ | dK | dV in bf16
   bf16* const dqkvt[3] = {B(L.dqt), B(L.dkt), B(L.dvt)};
   float2* const stats1 = reinterpret_cast<float2*>(L.stats1);
   float2* const stats2 = reinterpret_cast<float2*>(L.stats2);
@@ -538,8 +538,9 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
 
   // ---- the weights with their input index contiguous ([in, out]), for dX-side products
   if (transpose(w1, f, d, d, w1t, f, nullptr, s, err, n) || transpose(w2, d, f, f, w2t, d, nullptr, s, err, n) ||
-      transpose(wo, d, d, d, wot, d, nullptr, s, err, n) || transpose(wq, d, d, d, wqkvt[0], d, nullptr, s, err, n) ||
-      transpose(wk, d, d, d, wqkvt[1], d, nullptr, s, err, n) || transpose(wv, d, d, d, wqkvt[2], d, nullptr, s, err, n))
+      transpose(wo, d, d, d, wot, d, nullptr, s, err, n) || transpose(wq, d, d, d, wqkvt, 3 * d, nullptr, s, err, n) ||
+      transpose(wk, d, d, d, wqkvt + d, 3 * d, nullptr, s, err, n) ||
+      transpose(wv, d, d, d, wqkvt + 2 * d, 3 * d, nullptr, s, err, n))
     return 1;
 
   // ---- recompute: LN1(X), Q, K, V, A, Y = X + A W_O^T, LN2(Y); transposed copies of
@@ -635,21 +636,19 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
     for (int i = 0; i < kAttnBwdPacked; ++i) a.packed[i] = L.packed[i];
     if (launch_attention_bwd(a, stream, err, n)) return 1;
   }
-  // ---- QKV: dLN1 = dQ W_Q + dK W_K + dV W_V, dW_{Q,K,V} = d{Q,K,V}^T LN1(X)
+  // ---- QKV: dLN1 = [dQ dK dV] [W_Q; W_K; W_V] (one product over 3d), dW_{Q,K,V} = d{Q,K,V}^T LN1(X)
   {
     const float* dg[3] = {L.dq, L.dk, L.dv};
     float* dw[3] = {L.g.w_q, L.g.w_k, L.g.w_v};
     for (int i = 0; i < 3; ++i) {
-      if (transpose(dg[i], rows, d, d, dqkvt[i], rt, dqkvb[i], s, err, n)) return 1;
+      if (transpose(dg[i], rows, d, d, dqkvt[i], rt, dqkvb + (size_t)i * d, s, err, n, 3 * d)) return 1;
       BwdGemm g{};
-      g.a = dqkvb[i]; g.lda = d; g.b = wqkvt[i]; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = L.dx1; g.ldc = d;
-      if (i == 0 ? run_bwd_gemm<kGStoreF32>(g, 1, s, "bwd_dx1", err, n)
-                 : run_bwd_gemm<kGAccF32>(g, 1, s, "bwd_dx1", err, n))
-        return 1;
-      g = BwdGemm{};
       g.a = dqkvt[i]; g.lda = rt; g.b = x1t; g.ldb = rt; g.M = d; g.N = d; g.K = rows; g.c = dw[i]; g.ldc = d;
       if (run_bwd_gemm_split(g, wsplit, L.partials, false, s, "bwd_dwqkv", err, n)) return 1;
     }
+    BwdGemm g{};
+    g.a = dqkvb; g.lda = 3 * d; g.b = wqkvt; g.ldb = 3 * d; g.M = rows; g.N = d; g.K = 3 * d; g.c = L.dx1; g.ldc = d;
+    if (run_bwd_gemm<kGStoreF32>(g, 1, s, "bwd_dx1", err, n)) return 1;
   }
   // ---- LN1 backward: dX = dY + LN1'(dLN1); LN1 gain / bias gradients
   return ln_bwd<bf16>(x, stats1, CB(L.w.ln1_g), L.dx1, L.dy, L.dx, nullptr, L.ln_part, L.ln_parts, L.g.ln1_g,

@@ -312,7 +312,8 @@ int main() {
     EXPECT(L.rows == 400 && L.seq_pad == 256 && L.block_rows == 400 && L.wgrad_splits == 1);
     EXPECT(L.x1 == bws && L.lse == blse && L.dz == dz && L.dx == dx && L.g.w_2 == g.w_2);
     EXPECT((char*)L.ln_part + (size_t)L.ln_parts * 2 * 256 * 4 <= bws + nb);
-    EXPECT(L.dq == L.y && L.dx1 == L.dy2 && L.da == L.dzb && L.dqb == L.q);
+    EXPECT(L.dq == L.y && L.dx1 == L.dy2 && L.da == L.dzb && L.dqkvb == L.q);
+    EXPECT((char*)L.k == (char*)L.q + (size_t)400 * 256 * 2 && (char*)L.v == (char*)L.k + (size_t)400 * 256 * 2);
     EXPECT(L.dyt == L.dzt && L.dqt == L.y2t && L.dkt == L.attnt && L.rows_t == 400 && L.blk_ld == 400);
     EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, dx, &g, bws, nb - 1, nullptr) == BPT_ERR_WORKSPACE);
     EXPECT(bpt_layer_bwd(&bd, fake(0), &w[0], blse, dz, dx, nullptr, bws, nb, nullptr) == BPT_ERR_NULL);
