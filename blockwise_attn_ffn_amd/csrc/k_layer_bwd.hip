@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const TIn* __restric
                                                             bf16* __restrict__ out, int ld_out,
                                                             bf16* __restrict__ out_rm, int ld_rm) {
   __shared__ bf16 tile[64][66];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;   // rows on x: up to 2^31 - 1 blocks
   const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -460,6 +460,10 @@ int run_bwd_gemm(const BwdGemm& g0, int splits, hipStream_t s, const char* what,
   splits = (g.K + g.k_per_split - 1) / g.k_per_split;
   if (splits < 1) splits = 1;
   dim3 grid((g.N + kGBN - 1) / kGBN, (g.M + kGBM - 1) / kGBM, splits);
+  if (grid.y > 65535 || grid.z > 65535) {
+    set_err(err, n, "%s: product too tall for the grid", what);
+    return 1;
+  }
   hipLaunchKernelGGL((bwd_gemm_kernel<MODE>), grid, dim3(512), 0, s, g);
   return check_launch(what, err, n);
 }
@@ -488,7 +492,11 @@ template <typename TIn>
 int transpose(const TIn* in, int nr, int nc, int ld_in, bf16* out, int ld_out, bf16* out_rm, hipStream_t s,
               char* err, size_t n, int ld_rm = 0) {
   if (nr <= 0 || nc <= 0) return 0;
-  hipLaunchKernelGGL(bwd_transpose_kernel<TIn>, dim3((nc + 63) / 64, (nr + 63) / 64), dim3(256), 0, s, in, nr, nc,
+  if ((nc + 63) / 64 > 65535) {
+    set_err(err, n, "bwd_transpose: too many columns%s (%d)", "", nc);
+    return 1;
+  }
+  hipLaunchKernelGGL(bwd_transpose_kernel<TIn>, dim3((nr + 63) / 64, (nc + 63) / 64), dim3(256), 0, s, in, nr, nc,
                      ld_in, out, ld_out, out_rm, ld_rm ? ld_rm : ld_in);
   return check_launch("bwd_transpose", err, n);
 }
