@@ -363,7 +363,7 @@ def bench_layer_bwd(args, w):
     flops = w.batch * A.layer_bwd_flops(n, d, f, w.causal)
     executed = flops + w.batch * A.layer_flops(n, d, f, w.causal)
     tflops = flops / (ms * 1e-3) / 1e12
-    block_rows = min(w.rows, max(128, ((1 << 25) // f) // 128 * 128))
+    block_rows = min(w.rows, max(128, ((1 << 26) // f) // 128 * 128))
     line = {
         "metric": "layer backward TFLOP/s (1 MI355X) + % bf16 MFMA peak",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

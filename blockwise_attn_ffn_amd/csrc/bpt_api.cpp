@@ -834,12 +834,12 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   BwdLayout L{};
   const size_t rows = (size_t)d->batch * d->seq_len, dm = d->d_model, f = d->d_ff;
   const size_t np = seq_pad_of(d), bh = (size_t)d->batch * d->n_heads;
-  size_t r = (((size_t)1 << 25) / f) / 128 * 128;
+  size_t r = (((size_t)1 << 26) / f) / 128 * 128;
   if (r < 128) r = 128;
   L.block_rows = (int)(r < rows ? r : rows);
   L.blk_ld = (int)round_up((size_t)L.block_rows, 8);
   L.rows_t = (int)round_up(rows, 8);
-  // the product kernel's tiles are 256 x 128
+  // the product kernel's tiles are 256 x 256
   auto tiles_of = [](size_t m, size_t n) { return ((m + 255) / 256) * ((n + 255) / 256); };
   const size_t tiles = tiles_of(dm, dm);
   size_t splits = (512 + tiles - 1) / tiles;
@@ -847,10 +847,11 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   if (splits > rows / 256) splits = rows / 256;
   if (splits < 1) splits = 1;
   L.wgrad_splits = (int)splits;
-  // dW_1, dW_2 per block: [d, d_ff] tiles, the block's rows split to reach ~1024
-  // workgroups, each layer at least 1024 rows
+  // dW_1, dW_2 per block: [d, d_ff] tiles, the block's rows split to reach ~256
+  // workgroups (one per CU; more splits only add partial sums to write and add up),
+  // each layer at least 1024 rows
   const size_t ftiles = tiles_of(dm, f) < tiles_of(f, dm) ? tiles_of(dm, f) : tiles_of(f, dm);
-  size_t fsplits = (1024 + ftiles - 1) / ftiles;
+  size_t fsplits = (256 + ftiles - 1) / ftiles;
   if (fsplits > (size_t)L.block_rows / 1024) fsplits = (size_t)L.block_rows / 1024;
   if (fsplits > 16) fsplits = 16;
   if (fsplits < 1) fsplits = 1;
@@ -874,7 +875,7 @@ BwdLayout bwd_layout(const bpt_layer_desc_t* d) {
   L.stat_d = take(bh * np * 4);
   L.stat_l2 = take(bh * np * 4);
   for (int i = 0; i < 3; ++i) L.packed[i] = take((size_t)d->batch * np * dm * 2);
-  L.ublk = take(f * (size_t)L.blk_ld * 4);
+  L.ublk = take(round_up(f, 256) * round_up((size_t)L.block_rows, 256) * 4);   // whole tiles, fragment order
   L.hblk = take(f * (size_t)L.blk_ld * 2);
   L.dublk = take(f * (size_t)L.blk_ld * 2);
   L.dub = take((size_t)L.block_rows * f * 2);

@@ -199,7 +199,7 @@ struct LayerBwdLaunch {
   void* dqkvb;          // bf16 [rows, 3d]: dQ | dK | dV per row
   void *x1t, *attnt, *y2t, *dzt, *dyt, *dqt, *dkt, *dvt;                 // bf16 [d, rows_t]
   void *hblk, *dublk;   // bf16 [d_ff, blk_ld]: H^T and dU^T of the block
-  float* ublk;          // fp32 [d_ff, blk_ld]: U^T of the block
+  float* ublk;          // fp32: U^T of the block in the product kernel's tile fragment order
   void* dub;            // bf16 [block_rows, d_ff]: dU of the block
   void *w1t, *w2t, *wot;   // bf16 weights transposed: [d, d_ff], [d_ff, d], [d, d]
   void* wqkvt;              // bf16 [d, 3d]: W_Q^T | W_K^T | W_V^T

@@ -38,8 +38,8 @@ enum BwdGemmMode {
   kGAccF32 = 1,     // C += acc (fp32)
   kGStoreBF16 = 2,  // C = bf16(acc)
   kGResid = 3,      // C = R + acc (fp32 out; R fp32 or bf16)
-  kGGeluU = 4,      // U = acc (fp32), H = bf16(GELU(acc))
-  kGDGelu = 5,      // C = bf16(acc * GELU'(U))
+  kGGeluU = 4,      // U = acc (fp32, tile fragment order), H = bf16(GELU(acc))
+  kGDGelu = 5,      // C = bf16(acc * GELU'(U)), U as kGGeluU wrote it
   kGPartial = 6     // P[z] = acc (split-k partial sums, fp32)
 };
 
@@ -51,10 +51,14 @@ struct BwdGemm {
   int k_per_split; // multiple of 32; split z covers k in [z kps, (z + 1) kps)
   void* c;         // output (C, H or P)
   int ldc;
-  const void* r;   // residual (kGResid), or U (kGDGelu)
+  const void* r;   // residual (kGResid)
   int ldr, r_f32;
-  float* u;        // kGGeluU: U output
-  int ldu;
+  // U of kGGeluU (written) and kGDGelu (read), in tile fragment order: per tile
+  // (tile row, tile column of the grid), per wave, per 32 x 32 product (i, j), the
+  // 16 values of each lane as 4 float4 ([q / 4][lane]); both products have the
+  // same M, N and grid, so every lane reads back exactly what it wrote, with
+  // 16-byte accesses. ceil(M / 256) * ceil(N / 256) * 65536 floats.
+  float* u;
 };
 
 // GELU (tanh form) and its derivative: with s = 1 / (1 + exp(-2 z)), z = sqrt(2/pi)
@@ -231,10 +235,30 @@ __global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
   }
 
   // C layout: lane l holds column l % 32; register q holds row 8 (q / 4) + 4 (l / 32) + q % 4
+  float* const ut = (MODE == kGGeluU || MODE == kGDGelu)
+                        ? g.u + ((((size_t)tm * gridDim.x + tn) * 8 + wave) << 13)   // 8192 floats per wave
+                        : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      float uv[16];
+      if constexpr (MODE == kGGeluU || MODE == kGDGelu) {
+        float4* up = reinterpret_cast<float4*>(ut + ((i * 2 + j) << 10)) + lane;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if constexpr (MODE == kGGeluU) {
+            up[q4 * 64] = make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                                      acc[i][j][4 * q4 + 3]);
+          } else {
+            const float4 t = up[q4 * 64];
+            uv[4 * q4] = t.x;
+            uv[4 * q4 + 1] = t.y;
+            uv[4 * q4 + 2] = t.z;
+            uv[4 * q4 + 3] = t.w;
+          }
+        }
+      }
       const int n = n0 + wn * 64 + j * 32 + (lane & 31);
       if (n >= g.N) continue;
 #pragma unroll
@@ -254,11 +278,9 @@ __global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
           const float r = g.r_f32 ? static_cast<const float*>(g.r)[ro] : (float)static_cast<const bf16*>(g.r)[ro];
           static_cast<float*>(g.c)[o] = r + v;
         } else if constexpr (MODE == kGGeluU) {
-          g.u[(size_t)m * g.ldu + n] = v;
           static_cast<bf16*>(g.c)[o] = (bf16)gelu_tanh(v);
         } else if constexpr (MODE == kGDGelu) {
-          const float u = static_cast<const float*>(g.r)[(size_t)m * g.ldr + n];
-          static_cast<bf16*>(g.c)[o] = (bf16)(v * gelu_tanh_grad(u));
+          static_cast<bf16*>(g.c)[o] = (bf16)(v * gelu_tanh_grad(uv[q]));
         } else {   // kGPartial
           static_cast<float*>(g.c)[(size_t)blockIdx.z * g.M * g.N + (size_t)m * g.N + n] = v;
         }
@@ -594,12 +616,12 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
     BwdGemm g{};
     // U^T = W_1 LN2(Y)^T, H^T = GELU(U^T)
     g.a = w1; g.lda = d; g.b = y2 + (size_t)r0 * d; g.ldb = d; g.M = f; g.N = R; g.K = d;
-    g.c = hblk; g.ldc = bl; g.u = L.ublk; g.ldu = bl;
+    g.c = hblk; g.ldc = bl; g.u = L.ublk;
     if (run_bwd_gemm<kGGeluU>(g, 1, s, "bwd_w1_fwd", err, n)) return 1;
     // dU^T = (W_2^T dZ^T) * GELU'(U^T): W_2^T is [d_ff, d]
     g = BwdGemm{};
     g.a = w2t; g.lda = d; g.b = dzb + (size_t)r0 * d; g.ldb = d; g.M = f; g.N = R; g.K = d;
-    g.c = dublk; g.ldc = bl; g.r = L.ublk; g.ldr = bl;
+    g.c = dublk; g.ldc = bl; g.u = L.ublk;
     if (run_bwd_gemm<kGDGelu>(g, 1, s, "bwd_du", err, n)) return 1;
     if (transpose(dublk, f, R, bl, dub, f, nullptr, s, err, n)) return 1;
     // dW_2 (+)= dZ^T H: A = dZ^T [d, rows] (columns of the block), B = H^T [d_ff, R]

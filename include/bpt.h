@@ -361,9 +361,9 @@ typedef struct {
  * dK over dead ones); fp32 [rows, d_model] Y (then dQ), dLN2 (then dLN1), dY, dK,
  * dV; per-row LN statistics; the attention operands in fragment order (3 x
  * [batch * Np, d_model] bf16) and its row statistics; one FFN block of r = min(rows,
- * 2^25 / d_ff) rows: U fp32, H, dU (twice) bf16, each [r, d_ff]; the six weights
- * transposed in bf16; split-k partial sums (up to 16 x [d_model, d_model] or
- * [d_model, d_ff] fp32) and the LN column partials. The only d_ff-wide buffers are the block's: nothing of
+ * 2^26 / d_ff) rows: U fp32 (rounded up to 256 x 256 tiles), H, dU (twice) bf16, each
+ * [r, d_ff]; the six weights transposed in bf16; split-k partial sums (up to 16 x
+ * [d_model, d_model] or a few [d_model, d_ff] fp32) and the LN column partials. The only d_ff-wide buffers are the block's: nothing of
  * size rows x d_ff or seq_len x seq_len. */
 size_t bpt_layer_bwd_workspace_bytes(const bpt_layer_desc_t* desc);
 

@@ -393,14 +393,14 @@ def test_layer_bwd_null_alignment_alias():
 
 def test_layer_bwd_workspace_has_no_rows_by_d_ff_term():
     """The backward's workspace grows with the rows by the same amount whatever d_ff
-    is, once the rows exceed the FFN block (2^25 / d_ff rows): only the block's
+    is, once the rows exceed the FFN block (2^26 / d_ff rows): only the block's
     [block, d_ff] buffers depend on d_ff, never rows x d_ff ("The backward pass":
     the hidden state is recomputed one block at a time)."""
     def ws(batch, d_ff):
         return bpt.layer_bwd_workspace_bytes(desc(batch=batch, seq_len=4096, d_model=1024,
                                                   n_heads=16, d_ff=d_ff))
-    growth = {f: ws(8, f) - ws(4, f) for f in (2048, 4096, 8192, 16384)}
+    growth = {f: ws(16, f) - ws(8, f) for f in (2048, 4096, 8192, 16384)}
     assert len(set(growth.values())) == 1, growth
     # per extra row: 8 bf16 row-major and 5 bf16 transposed [d] vectors, 5 fp32 [d]
     # vectors, 3 bf16 attention copies, statistics
-    assert growth[4096] <= 4 * 4096 * (1024 * (8 * 2 + 5 * 2 + 5 * 4 + 3 * 2) + 16 + 16 * 3 * 4) + 64 * 256
+    assert growth[4096] <= 8 * 4096 * (1024 * (8 * 2 + 5 * 2 + 5 * 4 + 3 * 2) + 16 + 16 * 3 * 4) + 64 * 256

@@ -110,7 +110,7 @@ SMALL = [
     ("dk64_causal_ragged", 2, 200, 256, 4, 1024, True),
     ("dk128_full_ragged", 1, 130, 256, 2, 512, False),
     ("one_token", 3, 1, 256, 4, 512, True),
-    ("ffn_two_blocks", 1, 1100, 256, 2, 32768, True),   # blocks of 1024 rows: 1024 + 76
+    ("ffn_two_blocks", 1, 1100, 256, 2, 65536, True),   # blocks of 2^26 / d_ff = 1024 rows: 1024 + 76
     ("split_k", 2, 1100, 256, 4, 4096, True),           # dW_1, dW_2 over 2 row layers, dW_O, dW_QKV over 8
 ]
 
