@@ -443,30 +443,62 @@ __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict
 }
 
 // out[c, r] = in[r, c] (bf16 out; ld_out >= nr) for in [nr, nc] with row stride
-// ld_in, through a 64 x 64 LDS tile: reads coalesced along c, writes along r. With
-// out_rm, also a bf16 row-major copy of in (row stride ld_rm), for fp32 inputs.
+// ld_in, through a 64 x 64 LDS tile. With out_rm, also a bf16 row-major copy of in
+// (row stride ld_rm), for fp32 inputs. Global accesses are 8 elements per lane
+// (16 bytes of bf16) where the strides and base addresses allow (vec_in: in and
+// out_rm; vec_out: out), else element by element; the tile's row pitch of 65
+// elements keeps the column reads of the second phase on distinct LDS banks.
 template <typename TIn>
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(const TIn* __restrict__ in, int nr, int nc, int ld_in,
                                                             bf16* __restrict__ out, int ld_out,
-                                                            bf16* __restrict__ out_rm, int ld_rm) {
-  __shared__ bf16 tile[64][66];
+                                                            bf16* __restrict__ out_rm, int ld_rm, int vec_in,
+                                                            int vec_out) {
+  constexpr int P = 65;
+  __shared__ bf16 tile[64 * P];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;   // rows on x: up to 2^31 - 1 blocks
-  const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
+  const int sub = threadIdx.x & 7, rr = threadIdx.x >> 3;
+  // phase 1: rows rr, rr + 32 of the tile, columns 8 sub .. 8 sub + 7
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 4 * i + tr;
-    bf16 v = (bf16)0.0f;
-    if (r0 + r < nr && c0 + tc < nc) {
-      v = (bf16)(float)in[(size_t)(r0 + r) * ld_in + c0 + tc];
-      if (out_rm) out_rm[(size_t)(r0 + r) * ld_rm + c0 + tc] = v;
+  for (int p = 0; p < 2; ++p) {
+    const int r = rr + 32 * p, gr = r0 + r, gc = c0 + 8 * sub;
+    float v[8];
+    const bool full = gr < nr && gc + 8 <= nc;
+    if (full && vec_in) {
+      load8_f32(in + (size_t)gr * ld_in + gc, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = (gr < nr && gc + e < nc) ? (float)in[(size_t)gr * ld_in + gc + e] : 0.f;
     }
-    tile[r][tc] = v;
+    if (out_rm != nullptr) {
+      if (full && vec_in) {
+        store8_f32(out_rm + (size_t)gr * ld_rm + gc, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gr < nr && gc + e < nc) out_rm[(size_t)gr * ld_rm + gc + e] = (bf16)v[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r * P + 8 * sub + e] = (bf16)v[e];
   }
   __syncthreads();
+  // phase 2: output rows (input columns) rr, rr + 32, input rows 8 sub .. 8 sub + 7
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = 4 * i + tr;
-    if (c0 + c < nc && r0 + tc < nr) out[(size_t)(c0 + c) * ld_out + r0 + tc] = tile[tc][c];
+  for (int p = 0; p < 2; ++p) {
+    const int c = rr + 32 * p, gc = c0 + c, gr = r0 + 8 * sub;
+    if (gc >= nc) continue;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (float)tile[(8 * sub + j) * P + c];
+    bf16* o = out + (size_t)gc * ld_out + gr;
+    if (gr + 8 <= nr && vec_out) {
+      store8_f32(o, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (gr + j < nr) o[j] = (bf16)v[j];
+    }
   }
 }
 
@@ -518,8 +550,12 @@ int transpose(const TIn* in, int nr, int nc, int ld_in, bf16* out, int ld_out, b
     set_err(err, n, "bwd_transpose: too many columns%s (%d)", "", nc);
     return 1;
   }
+  if (!ld_rm) ld_rm = ld_in;
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const int vec_in = (ld_in % 8 == 0) && a16(in) && (out_rm == nullptr || ((ld_rm % 8 == 0) && a16(out_rm)));
+  const int vec_out = (ld_out % 8 == 0) && a16(out);
   hipLaunchKernelGGL(bwd_transpose_kernel<TIn>, dim3((nr + 63) / 64, (nc + 63) / 64), dim3(256), 0, s, in, nr, nc,
-                     ld_in, out, ld_out, out_rm, ld_rm ? ld_rm : ld_in);
+                     ld_in, out, ld_out, out_rm, ld_rm, vec_in, vec_out);
   return check_launch("bwd_transpose", err, n);
 }
 
