@@ -238,26 +238,35 @@ __global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
   float* const ut = (MODE == kGGeluU || MODE == kGDGelu)
                         ? g.u + ((((size_t)tm * gridDim.x + tn) * 8 + wave) << 13)   // 8192 floats per wave
                         : nullptr;
+  // kGDGelu: U of product (i, j) is loaded one product ahead, before the stores of
+  // the current one (which the compiler would not move the loads across)
+  float4 unext[4];
+  auto load_u = [&](int ij) __attribute__((always_inline)) {
+    const float4* up = reinterpret_cast<const float4*>(ut + (ij << 10)) + lane;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) unext[q4] = up[q4 * 64];
+  };
+  if constexpr (MODE == kGDGelu) load_u(0);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       float uv[16];
-      if constexpr (MODE == kGGeluU || MODE == kGDGelu) {
+      if constexpr (MODE == kGGeluU) {
         float4* up = reinterpret_cast<float4*>(ut + ((i * 2 + j) << 10)) + lane;
 #pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          up[q4 * 64] = make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                                    acc[i][j][4 * q4 + 3]);
+      } else if constexpr (MODE == kGDGelu) {
+#pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          if constexpr (MODE == kGGeluU) {
-            up[q4 * 64] = make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
-                                      acc[i][j][4 * q4 + 3]);
-          } else {
-            const float4 t = up[q4 * 64];
-            uv[4 * q4] = t.x;
-            uv[4 * q4 + 1] = t.y;
-            uv[4 * q4 + 2] = t.z;
-            uv[4 * q4 + 3] = t.w;
-          }
+          uv[4 * q4] = unext[q4].x;
+          uv[4 * q4 + 1] = unext[q4].y;
+          uv[4 * q4 + 2] = unext[q4].z;
+          uv[4 * q4 + 3] = unext[q4].w;
         }
+        if (i * 2 + j + 1 < 8) load_u(i * 2 + j + 1);
       }
       const int n = n0 + wn * 64 + j * 32 + (lane & 31);
       if (n >= g.N) continue;
@@ -428,18 +437,34 @@ __global__ __launch_bounds__(256) void bwd_ln_bwd_kernel(const TX* __restrict__ 
   }
 }
 
-// dgain[c], dbias[c] = sum over the workgroups' partials, in order.
+// dgain[c], dbias[c] = sum over the workgroups' partials: 32 columns per workgroup,
+// 8 slices per column (parts s, s + 8, ...), each added in order, then the 8 slice
+// sums in order (a fixed order, so results repeat bit for bit).
 __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict__ part, int nparts, int d,
                                                          float* __restrict__ dgain, float* __restrict__ dbias) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= d) return;
+  __shared__ float red[2][8][32];
+  const int cl = threadIdx.x & 31, sl = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + cl;
   float sg = 0.f, sb = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    sg += part[((size_t)p * 2 + 0) * d + c];
-    sb += part[((size_t)p * 2 + 1) * d + c];
+  if (c < d) {
+    for (int p = sl; p < nparts; p += 8) {
+      sg += part[((size_t)p * 2 + 0) * d + c];
+      sb += part[((size_t)p * 2 + 1) * d + c];
+    }
   }
-  dgain[c] = sg;
-  dbias[c] = sb;
+  red[0][sl][cl] = sg;
+  red[1][sl][cl] = sb;
+  __syncthreads();
+  if (sl == 0 && c < d) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a += red[0][k][cl];
+      b += red[1][k][cl];
+    }
+    dgain[c] = a;
+    dbias[c] = b;
+  }
 }
 
 // out[c, r] = in[r, c] (bf16 out; ld_out >= nr) for in [nr, nc] with row stride
@@ -566,7 +591,7 @@ int ln_bwd(const TX* x, const float2* stats, const bf16* gain, const float* dy, 
   hipLaunchKernelGGL(bwd_ln_bwd_kernel<TX>, dim3(nparts), dim3(256), 0, s, x, stats, gain, dy, resid, out, out_bf16,
                      part, rows, d);
   if (check_launch("bwd_ln_bwd", err, n)) return 1;
-  hipLaunchKernelGGL(bwd_colsum_kernel, dim3((d + 255) / 256), dim3(256), 0, s, part, nparts, d, dgain, dbias);
+  hipLaunchKernelGGL(bwd_colsum_kernel, dim3((d + 31) / 32), dim3(256), 0, s, part, nparts, d, dgain, dbias);
   return check_launch("bwd_colsum", err, n);
 }
 
