@@ -48,7 +48,7 @@ struct BwdGemm {
   const bf16* b;   // B[n, k] at b[n * ldb + k]
   int lda, ldb;    // multiples of 8, like the base pointers' element offsets
   int M, N, K;
-  int k_per_split; // multiple of 32; split z covers k in [z kps, (z + 1) kps)
+  int k_per_split; // multiple of 64; split z covers k in [z kps, (z + 1) kps)
   void* c;         // output (C, H or P)
   int ldc;
   const void* r;   // residual (kGResid)
@@ -73,38 +73,39 @@ __device__ inline float gelu_tanh_grad(float u) {
 
 namespace {
 
-constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
-constexpr int kGStageA = kGBM * kGBK * 2;          // bytes of A per stage (16 KB)
-constexpr int kGStage = (kGBM + kGBN) * kGBK * 2;  // bytes per stage (24 KB)
-constexpr int kGCopies = kGStage / 1024 / 8;        // 1 KB copies per wave and stage (4)
+constexpr int kGBM = 256, kGBN = 256, kGBK = 64;
+constexpr int kGStageA = kGBM * kGBK * 2;          // bytes of A per stage (32 KB)
+constexpr int kGStage = (kGBM + kGBN) * kGBK * 2;  // bytes per stage (64 KB)
+constexpr int kGCopies = kGStage / 1024 / 8;        // 1 KB copies per wave and stage (8)
+constexpr int kGCopiesA = kGStageA / 1024 / 8;      // of which A (4)
 
-// LDS layout of a stage: the 16-byte chunk (row r, k-chunk c of 4) of an operand
-// tile sits in slot 4 r + (c ^ ((r >> 2) & 3)). The copies write 64 consecutive
+// LDS layout of a stage: the 16-byte chunk (row r, k-chunk c of 8) of an operand
+// tile sits in slot 8 r + (c ^ ((r >> 1) & 7)). The copies write 64 consecutive
 // slots per wave instruction (the LDS-DMA path puts lane l at slot base + l), and a
 // fragment read (32 consecutive rows, one chunk) hits 16 distinct 16-byte bank
 // groups in every 16 lanes.
-__device__ inline int chunk_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+__device__ inline int chunk_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
 
 // Workgroup barrier without a memory fence (__syncthreads() would also wait for
-// every copy in flight, including the two k-tiles ahead).
+// every copy in flight, including the next k-tile's).
 __device__ inline void stage_barrier_bwd() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// One k-step's fragments from a stage: A rows at a + 2 KB i (i < 4), B rows at b +
-// 2 KB j (j < 2), LDS byte addresses, with the wait for them in the same statement.
+// One k-step's fragments from a stage: A rows at a + 4 KB i (i < 4), B rows at b +
+// 4 KB j (j < 2), LDS byte addresses, with the wait for them in the same statement.
 // Reads written in C++ would make the compiler wait first for every LDS copy in
 // flight (it cannot tell that the copies target other stages).
 __device__ inline void ld_frags6(uint32_t a, uint32_t b, bf16x8 (&af)[4], bf16x8 (&bf)[2]) {
   asm volatile(
       "ds_read_b128 %0, %6 offset:0\n\t"
-      "ds_read_b128 %1, %6 offset:2048\n\t"
-      "ds_read_b128 %2, %6 offset:4096\n\t"
-      "ds_read_b128 %3, %6 offset:6144\n\t"
+      "ds_read_b128 %1, %6 offset:4096\n\t"
+      "ds_read_b128 %2, %6 offset:8192\n\t"
+      "ds_read_b128 %3, %6 offset:12288\n\t"
       "ds_read_b128 %4, %7 offset:0\n\t"
-      "ds_read_b128 %5, %7 offset:2048\n\t"
+      "ds_read_b128 %5, %7 offset:4096\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=v"(af[0]), "=v"(af[1]), "=v"(af[2]), "=v"(af[3]), "=v"(bf[0]), "=v"(bf[1])
       : "v"(a), "v"(b));
@@ -114,20 +115,16 @@ __device__ inline void ld_frags6(uint32_t a, uint32_t b, bf16x8 (&af)[4], bf16x8
 
 // 512 threads = 8 waves in 2 x 4, each 128 x 64 of the 256 x 256 tile (4 x 2
 // products of 32 x 32 per k-step: 6 fragment reads from LDS for 8 products). The
-// k-tiles (32 wide) are copied global -> LDS by the LDS-DMA path into three stages,
-// two k-tiles ahead of the products (the copy of tile t + 2 is issued once tile t
-// has landed), so the loads' latency is covered by two tiles of products and no
-// registers stage the data. Rows past M or N read row M - 1 (N - 1), and chunks past
-// K read chunk 0: finite values whose products land in discarded outputs or are
-// zeroed in the last k-tile's fragments.
-// (Measured on the 64 x 1024-token layer backward: registers staging one k-tile
-// ahead 20.9 ms; without its LDS stores, a timing copy, 10.7 ms; this form with 4
-// waves on 256 x 128 tiles 12.55 ms, with 8 waves on 256 x 256 tiles 12.2 ms.)
+// k-tiles (64 wide) are copied global -> LDS by the LDS-DMA path into two 64 KB
+// stages, one k-tile ahead of the products (the copy of tile t + 1 is issued once
+// tile t has landed), so the loads' latency is covered by a tile of products (four
+// k-steps) and no registers stage the data. Rows past M or N read row M - 1 (N - 1),
+// and chunks past K read chunk 0: finite values whose products land in discarded
+// outputs or are zeroed in the last k-tile's fragments.
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
   __shared__ __align__(16) unsigned char st0[kGStage];
   __shared__ __align__(16) unsigned char st1[kGStage];
-  __shared__ __align__(16) unsigned char st2[kGStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -156,9 +153,9 @@ __global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
   int ck[kGCopies];
 #pragma unroll
   for (int q = 0; q < kGCopies; ++q) {
-    const bool isa = q < 2;
-    const int slot = (isa ? 2 * wave + q : 2 * wave + (q - 2)) * 64 + lane;
-    const int r = slot >> 2, c = (slot & 3) ^ ((r >> 2) & 3);
+    const bool isa = q < kGCopiesA;
+    const int slot = (isa ? kGCopiesA * wave + q : kGCopiesA * wave + (q - kGCopiesA)) * 64 + lane;
+    const int r = slot >> 3, c = (slot & 7) ^ ((r >> 1) & 7);
     const int rows = isa ? g.M : g.N, r0 = isa ? m0 : n0;
     const int gr = min(r0 + r, rows - 1);
     src[q] = (isa ? g.a + (size_t)gr * g.lda : g.b + (size_t)gr * g.ldb);
@@ -169,7 +166,8 @@ __global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
 #pragma unroll
     for (int q = 0; q < kGCopies; ++q) {
       const int gk = k0 + ck[q] < ke ? k0 + ck[q] : 0;
-      unsigned char* dst = st + (q < 2 ? (2 * wave + q) * 1024 : kGStageA + (2 * wave + (q - 2)) * 1024);
+      unsigned char* dst = st + (q < kGCopiesA ? (kGCopiesA * wave + q) * 1024
+                                               : kGStageA + (kGCopiesA * wave + (q - kGCopiesA)) * 1024);
       dma16(src[q] + gk, dst);
     }
   };
@@ -181,30 +179,40 @@ __global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   // byte offsets within a stage of this lane's fragment rows for k-step ks: row r
-  // = 32 q + (lane & 31) (q a multiple of 32 rows) sits at 64 r + 16 (c ^ ((r >> 2) &
-  // 3)), c = 2 ks + lane / 32, and (r >> 2) & 3 depends on the lane only
-  uint32_t lofs[2];
+  // = 32 q + (lane & 31) (q a multiple of 32 rows) sits at 128 r + 16 (c ^ ((r >> 1)
+  // & 7)), c = 2 ks + lane / 32, and (r >> 1) & 7 depends on the lane only
+  uint32_t lofs[kGBK / 16];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    lofs[ks] = 64u * (uint32_t)(lane & 31) + 16u * (uint32_t)((2 * ks + (lane >> 5)) ^ ((lane >> 2) & 3));
-  const uint32_t aofs = 64u * 128u * (uint32_t)wm, bofs = (uint32_t)kGStageA + 64u * 64u * (uint32_t)wn;
+  for (int ks = 0; ks < kGBK / 16; ++ks)
+    lofs[ks] = 128u * (uint32_t)(lane & 31) + 16u * (uint32_t)((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7));
+  const uint32_t aofs = 128u * 128u * (uint32_t)wm, bofs = (uint32_t)kGStageA + 128u * 64u * (uint32_t)wn;
+  // fragments of k-step ks from stage st (C++ reads: the stages are separate arrays
+  // chosen at compile time, so the compiler does not wait for the copy into the
+  // other stage before them), the next k-step's read while this one's products run
+  auto frags = [&](const unsigned char* st, int ks, bf16x8 (&af)[4], bf16x8 (&bf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + aofs + lofs[ks] + 4096 * i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(st + bofs + lofs[ks] + 4096 * j);
+  };
   auto compute = [&](int t, const unsigned char* st) __attribute__((always_inline)) {
     const int k0 = kb + t * kGBK;
     const bool edge = k0 + kGBK > ke;   // the last k-tile runs past K
-    const uint32_t sb = (uint32_t)(uintptr_t)st;   // LDS byte address of the stage
+    bf16x8 af[2][4], bfr[2][2];
+    frags(st, 0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < kGBK / 16; ++ks) {
-      const int c = 2 * ks + (lane >> 5);
-      bf16x8 af[4], bfr[2];
-      ld_frags6(sb + aofs + lofs[ks], sb + bofs + lofs[ks], af, bfr);
+      const int cur = ks & 1;
+      if (ks + 1 < kGBK / 16) frags(st, ks + 1, af[cur ^ 1], bfr[cur ^ 1]);
       if (edge) {
+        const int c = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if (k0 + 8 * c + e >= ke) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i][e] = (bf16)0.0f;
+            for (int i = 0; i < 4; ++i) af[cur][i][e] = (bf16)0.0f;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bfr[j][e] = (bf16)0.0f;
+            for (int j = 0; j < 2; ++j) bfr[cur][j][e] = (bf16)0.0f;
           }
         }
       }
@@ -212,26 +220,23 @@ __global__ __launch_bounds__(512, 1) void bwd_gemm_kernel(BwdGemm g) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
     }
   };
 
   if (nkt > 0) issue(0, st0);
-  if (nkt > 1) issue(1, st1);
-  // step t: wait for this wave's copies of tile t (those of t + 1 may still run),
-  // barrier (every wave's copies of t landed; every wave is done with t - 1, whose
-  // stage takes t + 2), issue t + 2, multiply t
+  // step t: wait for this wave's copies of tile t, barrier (every wave's copies of t
+  // landed; every wave is done with t - 1, whose stage takes t + 1), issue t + 1,
+  // multiply t
   auto step = [&](int t, const unsigned char* rd, unsigned char* wr) __attribute__((always_inline)) {
-    if (t + 1 < nkt) __builtin_amdgcn_s_waitcnt(0x0070 | kGCopies);
-    else __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_waitcnt(0x0070);
     stage_barrier_bwd();
-    if (t + 2 < nkt) issue(t + 2, wr);
+    if (t + 1 < nkt) issue(t + 1, wr);
     compute(t, rd);
   };
-  for (int t = 0; t < nkt; t += 3) {
-    step(t, st0, st2);
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, st0, st1);
     if (t + 1 < nkt) step(t + 1, st1, st0);
-    if (t + 2 < nkt) step(t + 2, st2, st1);
   }
 
   // C layout: lane l holds column l % 32; register q holds row 8 (q / 4) + 4 (l / 32) + q % 4
