@@ -489,13 +489,8 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
   constexpr int VCPW = VFR / NWG;              // V copies per group-1 wave
   static_assert(KFR % NWG == 0 && VFR % NWG == 0 && VCPW <= KK && KK % VCPW == 0,
                 "a group-1 wave copies consecutive key steps of one feature tile of V");
-  // separate arrays per stage, selected at compile time: the compiler can then see
-  // that a copy into one stage does not write the stage being read, and does not
-  // wait for the copy before the reads
-  __shared__ __align__(16) unsigned char kbuf0[KFR * FB];
-  __shared__ __align__(16) unsigned char kbuf1[KFR * FB];
-  __shared__ __align__(16) unsigned char vbuf0[VFR * FB];
-  __shared__ __align__(16) unsigned char vbuf1[VFR * FB];
+  __shared__ __align__(16) unsigned char kbuf[2][KFR * FB];
+  __shared__ __align__(16) unsigned char vbuf[2][VFR * FB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -749,47 +744,35 @@ __global__ __launch_bounds__(512, 1) void attention_pair_kernel(
   auto run = [&](auto group) __attribute__((always_inline)) {
     constexpr int G = decltype(group)::value;
     load_q(ck);
-    if constexpr (G == 0) issue_k(ck, kbuf0);
+    if constexpr (G == 0) issue_k(ck, kbuf[0]);
     Cur cp = ck;                     // visit k-1 (valid from k = 1)
     Cur cn = ck;                     // visit k+1
     advance(cn);
-    // step k reads K(k) from kc and V(k-1) from vp; copies K(k+1) into kn and V(k)
-    // into vc. Returns false after the final step.
-    auto step = [&](int k, unsigned char* kc, unsigned char* kn, unsigned char* vc,
-                    unsigned char* vp) __attribute__((always_inline)) {
+    for (int k = 0;; ++k) {
       const bool has_k = ck.u < u_hi, has_n = cn.u < u_hi, has_p = k > 0;
       wait_vmem();
       __syncthreads();               // K(k) and V(k-1) have landed
       // a new half starts at visit k: both groups are done with the old Q (their S
       // of visit k-1 ran in the previous step), so its Q is read now, ahead of the
-      // copies, and waited for at once (left pending, it would make the compiler
-      // wait for the copies in flight before the S product)
-      if (has_p && has_k && cp.kb == cp.kend - 1) {
-        load_q(ck);
-        wait_vmem();
-      }
+      // copies (waiting for it does not wait for them)
+      if (has_p && has_k && cp.kb == cp.kend - 1) load_q(ck);
       if constexpr (G == 0) {
-        if (has_n) issue_k(cn, kn);
-        mstep(cp, has_p, ck, has_k, kc, vp);
+        if (has_n) issue_k(cn, kbuf[(k + 1) & 1]);
+        mstep(cp, has_p, ck, has_k, kbuf[k & 1], vbuf[(k + 1) & 1]);
       } else {
-        if (has_k) issue_v(ck, vc);
+        if (has_k) issue_v(ck, vbuf[k & 1]);
         if (has_p) vstep(cp);
       }
       __builtin_amdgcn_s_barrier();  // half step: no copy is waited for here
       if constexpr (G == 0) {
         if (has_k) vstep(ck);
       } else {
-        mstep(cp, has_p, ck, has_k, kc, vp);
+        mstep(cp, has_p, ck, has_k, kbuf[k & 1], vbuf[(k + 1) & 1]);
       }
-      if (!has_k) return false;
+      if (!has_k) break;
       cp = ck;
       ck = cn;
       advance(cn);
-      return true;
-    };
-    for (int k = 0;; k += 2) {
-      if (!step(k, kbuf0, kbuf1, vbuf0, vbuf1)) break;
-      if (!step(k + 1, kbuf1, kbuf0, vbuf1, vbuf0)) break;
     }
   };
   if (grp == 0) run(std::integral_constant<int, 0>{});
