@@ -150,3 +150,27 @@ def test_layer_bwd_full_size_sampled_sequences():
     assert torch.equal(dx1, dx2), "dX differs between two calls"
     for k in GRAD_KEYS:
         assert torch.equal(g1[k], g2[k]), f"d{k} differs between two calls"
+
+
+def test_layer_bwd_long_context_prefix():
+    """The long-context layer: 1 x 131072 tokens, d_model 2048, 16 heads of 128,
+    d_ff 8192, causal (query blocks of 128, key blocks of 64, 16 FFN blocks of 8192
+    rows). With dZ kept on the first 768 rows only, the causal mask makes the whole
+    backward that of the 768-token prefix (row i reaches only outputs j >= i, and
+    the prefix's forward reads no later row): every parameter gradient and dX of the
+    prefix equal the oracle's backward of the prefix, and dX is exactly zero past it."""
+    w = synth.WORKLOADS["long_128k"]
+    inputs = synth.make_inputs(w, seed=0)
+    m = 768
+    dz = synth.make_grad_output(w.rows, w.d_model, seed=5, live_rows=np.arange(m))
+    say(f"layer_bwd long context: {w.name}, dZ on rows [0, {m})")
+    (dx, grads), = run_fwd_bwd(w, inputs, dz)
+    assert torch.count_nonzero(dx[m:]).item() == 0, "dX nonzero past the rows dZ reaches"
+    p = synth.oracle_weights(inputs["layers"][0])
+    g = oracle.layer_backward(synth.to_f64(inputs["x"][:m]), p, synth.to_f64(dz[:m]), seq_len=m,
+                              n_heads=w.n_heads, causal=True, eps=w.ln_eps)
+    ref = {"dx": g["dx"]}
+    for k in GRAD_KEYS:
+        a = g[ORACLE_KEY[k]]
+        ref[k] = a.T if a.ndim == 2 else a
+    check_all(dx[:m], grads, ref, "long(prefix)")
