@@ -808,9 +808,6 @@ bpt_status_t validate_bwd_desc(const bpt_layer_desc_t* d) {
   if (st != BPT_OK) return st;
   if (d->dtype != BPT_BF16) return fail(BPT_ERR_UNSUPPORTED, "the layer backward takes BPT_BF16 only");
   if (d->precision != 0) return fail(BPT_ERR_UNSUPPORTED, "the layer backward computes at precision 0");
-  if (d->window || d->chunk) return fail(BPT_ERR_UNSUPPORTED, "the layer backward takes no window or chunk");
-  if (kv_heads(d) != d->n_heads)
-    return fail(BPT_ERR_UNSUPPORTED, "the layer backward takes no grouped key/value heads");
   if ((size_t)d->batch * seq_pad_of(d) * (size_t)d->d_model >= ((size_t)1 << 31))
     return fail(BPT_ERR_SHAPE, "batch * seq_len * d_model exceeds the 31-bit element index range");
   return BPT_OK;
@@ -911,6 +908,7 @@ bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
   const BwdLayout W = bwd_layout(desc);
   const size_t rows = (size_t)desc->batch * desc->seq_len, dm = desc->d_model, f = desc->d_ff;
   const size_t rd = rows * dm, dd = dm * dm, df = dm * f;
+  const size_t kd = (size_t)kv_heads(desc) * (dm / desc->n_heads) * dm;   // W_K, W_V: [d_kv, d]
   // every buffer: the inputs, then the outputs (dX, the gradients, the workspace)
   const void* ptrs[24] = {X, weights->ln1_g, weights->ln1_b, weights->w_q, weights->w_k, weights->w_v,
                           weights->w_o, weights->ln2_g, weights->ln2_b, weights->w_1, weights->w_2, lse,
@@ -920,9 +918,9 @@ bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
                                   "w_1", "w_2", "lse", "dZ", "dX", "grads.ln1_g", "grads.ln1_b",
                                   "grads.w_q", "grads.w_k", "grads.w_v", "grads.w_o", "grads.ln2_g",
                                   "grads.ln2_b", "grads.w_1", "grads.w_2", "workspace"};
-  const size_t elems[24] = {rd, dm, dm, dd, dd, dd, dd, dm, dm, df, df,
+  const size_t elems[24] = {rd, dm, dm, dd, kd, kd, dd, dm, dm, df, df,
                             (size_t)desc->batch * desc->n_heads * desc->seq_len, rd, rd,
-                            dm, dm, dd, dd, dd, dd, dm, dm, df, df};
+                            dm, dm, dd, kd, kd, dd, dm, dm, df, df};
   const void* all[25];
   size_t bytes[25];
   for (int i = 0; i < 24; ++i) {
@@ -953,6 +951,9 @@ bpt_status_t bpt_layer_bwd(const bpt_layer_desc_t* desc, const void* X,
   p.n_heads = desc->n_heads;
   p.d_ff = desc->d_ff;
   p.causal = desc->causal;
+  p.n_kv_heads = kv_heads(desc);
+  p.window = desc->window;
+  p.chunk = desc->chunk;
   p.rows = (int)rows;
   p.rows_t = W.rows_t;
   p.ln_eps = desc->ln_eps;

@@ -166,6 +166,8 @@ inline size_t qkv_pack_elems(int d_model, int kv_pad) {
 // K, V in, O (bf16) and lse out; packed: Q (then O), K, V^T copies in the workspace.
 struct AttnFwdLaunch {
   int batch, seq_len, seq_pad, d_model, n_heads, d_head, causal;
+  int n_kv_heads;     // 0: n_heads; K and V are [rows, n_kv_heads * d_head]
+  int window, chunk;  // masks of the causal setting (0: none)
   const void *q, *k, *v;
   void* o;
   float* lse;
@@ -181,6 +183,8 @@ int launch_attention_merge(int batch, int seq_len, int n_heads, int d_head, floa
 // seq_len rows; transposed ones ("...t") are [d_model, rows_t].
 struct LayerBwdLaunch {
   int batch, seq_len, seq_pad, d_model, n_heads, d_ff, causal, rows;
+  int n_kv_heads;     // key/value heads (divides n_heads); K, V are [rows, n_kv_heads * d_head]
+  int window, chunk;  // masks of the causal setting (0: none)
   int rows_t;         // row stride of the transposed activations: rows rounded up to 8
   float ln_eps;
   int block_rows;     // FFN rows per block (a multiple of 8 unless it is all the rows)

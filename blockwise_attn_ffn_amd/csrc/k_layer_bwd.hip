@@ -605,7 +605,11 @@ int ln_bwd(const TX* x, const float2* stats, const bf16* gain, const float* dy, 
 int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int rows = L.rows, d = L.d_model, f = L.d_ff, rt = L.rows_t, bl = L.blk_ld;
+  // K and V are [rows, dkv] with n_kv_heads key/value heads; [dQ dK dV] and the stacked
+  // transposed W_Q, W_K, W_V are k3 = d + 2 dkv wide
+  const int G = L.n_kv_heads > 0 ? L.n_kv_heads : L.n_heads, dkv = G * (d / L.n_heads), k3 = d + 2 * dkv;
   if (d % 64 != 0 || d > 4096 || f % 256 != 0 || L.block_rows < 1 || L.ln_parts < 1 || rt < rows ||
+      L.n_heads % G != 0 || dkv % 64 != 0 ||
       rt % 8 != 0 || bl < L.block_rows || bl % 8 != 0 || (L.block_rows < rows && L.block_rows % 8 != 0)) {
     set_err(err, n, "layer backward: inconsistent launch shape%s (d_model %d)", "", d);
     return 1;
@@ -625,8 +629,8 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
   bf16 *const dyt = B(L.dyt), *const da = B(L.da);
   bf16 *const hblk = B(L.hblk), *const dublk = B(L.dublk), *const dub = B(L.dub);
   bf16 *const w1t = B(L.w1t), *const w2t = B(L.w2t), *const wot = B(L.wot);
-  bf16* const wqkvt = B(L.wqkvt);   // [d, 3d]: W_Q^T | W_K^T | W_V^T
-  bf16* const dqkvb = B(L.dqkvb);   // [rows, 3d]: dQ | dK | dV in bf16
+  bf16* const wqkvt = B(L.wqkvt);   // [d, k3]: W_Q^T | W_K^T | W_V^T
+  bf16* const dqkvb = B(L.dqkvb);   // [rows, k3]: dQ | dK | dV in bf16
   bf16* const dqkvt[3] = {B(L.dqt), B(L.dkt), B(L.dvt)};
   float2* const stats1 = reinterpret_cast<float2*>(L.stats1);
   float2* const stats2 = reinterpret_cast<float2*>(L.stats2);
@@ -634,9 +638,9 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
 
   // ---- the weights with their input index contiguous ([in, out]), for dX-side products
   if (transpose(w1, f, d, d, w1t, f, nullptr, s, err, n) || transpose(w2, d, f, f, w2t, d, nullptr, s, err, n) ||
-      transpose(wo, d, d, d, wot, d, nullptr, s, err, n) || transpose(wq, d, d, d, wqkvt, 3 * d, nullptr, s, err, n) ||
-      transpose(wk, d, d, d, wqkvt + d, 3 * d, nullptr, s, err, n) ||
-      transpose(wv, d, d, d, wqkvt + 2 * d, 3 * d, nullptr, s, err, n))
+      transpose(wo, d, d, d, wot, d, nullptr, s, err, n) || transpose(wq, d, d, d, wqkvt, k3, nullptr, s, err, n) ||
+      transpose(wk, dkv, d, d, wqkvt + d, k3, nullptr, s, err, n) ||
+      transpose(wv, dkv, d, d, wqkvt + d + dkv, k3, nullptr, s, err, n))
     return 1;
 
   // ---- recompute: LN1(X), Q, K, V, A, Y = X + A W_O^T, LN2(Y); transposed copies of
@@ -649,8 +653,9 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
     const bf16* ws[3] = {wq, wk, wv};
     bf16* outs[3] = {q, k, v};
     for (int i = 0; i < 3; ++i) {
+      const int w = i == 0 ? d : dkv;
       BwdGemm g{};
-      g.a = x1; g.lda = d; g.b = ws[i]; g.ldb = d; g.M = rows; g.N = d; g.K = d; g.c = outs[i]; g.ldc = d;
+      g.a = x1; g.lda = d; g.b = ws[i]; g.ldb = d; g.M = rows; g.N = w; g.K = d; g.c = outs[i]; g.ldc = w;
       if (run_bwd_gemm<kGStoreBF16>(g, 1, s, "bwd_qkv", err, n)) return 1;
     }
   }
@@ -658,6 +663,7 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
     AttnFwdLaunch a{};
     a.batch = L.batch; a.seq_len = L.seq_len; a.seq_pad = L.seq_pad; a.d_model = d;
     a.n_heads = L.n_heads; a.d_head = d / L.n_heads; a.causal = L.causal;
+    a.n_kv_heads = G; a.window = L.window; a.chunk = L.chunk;
     a.q = q; a.k = k; a.v = v; a.o = attn; a.lse = L.lse_re;
     for (int i = 0; i < 3; ++i) a.packed[i] = L.packed[i];
     if (launch_attention_fwd(a, stream, err, n)) return 1;
@@ -724,7 +730,7 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
   {
     AttnBwdLaunch a{};
     a.batch = L.batch; a.seq_len = L.seq_len; a.d_model = d; a.n_heads = L.n_heads;
-    a.d_head = d / L.n_heads; a.causal = L.causal; a.n_kv_heads = L.n_heads; a.window = 0; a.chunk = 0;
+    a.d_head = d / L.n_heads; a.causal = L.causal; a.n_kv_heads = G; a.window = L.window; a.chunk = L.chunk;
     a.seq_pad = L.seq_pad;
     a.q = q; a.k = k; a.v = v; a.out = attn; a.dout = da; a.lse = L.lse;
     a.dq = L.dq; a.dk = L.dk; a.dv = L.dv;
@@ -732,18 +738,20 @@ int launch_layer_bwd(const LayerBwdLaunch& L, void* stream, char* err, size_t n)
     for (int i = 0; i < kAttnBwdPacked; ++i) a.packed[i] = L.packed[i];
     if (launch_attention_bwd(a, stream, err, n)) return 1;
   }
-  // ---- QKV: dLN1 = [dQ dK dV] [W_Q; W_K; W_V] (one product over 3d), dW_{Q,K,V} = d{Q,K,V}^T LN1(X)
+  // ---- QKV: dLN1 = [dQ dK dV] [W_Q; W_K; W_V] (one product over k3), dW_{Q,K,V} = d{Q,K,V}^T LN1(X)
   {
     const float* dg[3] = {L.dq, L.dk, L.dv};
     float* dw[3] = {L.g.w_q, L.g.w_k, L.g.w_v};
+    const int width[3] = {d, dkv, dkv}, col[3] = {0, d, d + dkv};
     for (int i = 0; i < 3; ++i) {
-      if (transpose(dg[i], rows, d, d, dqkvt[i], rt, dqkvb + (size_t)i * d, s, err, n, 3 * d)) return 1;
+      if (transpose(dg[i], rows, width[i], width[i], dqkvt[i], rt, dqkvb + col[i], s, err, n, k3)) return 1;
       BwdGemm g{};
-      g.a = dqkvt[i]; g.lda = rt; g.b = x1t; g.ldb = rt; g.M = d; g.N = d; g.K = rows; g.c = dw[i]; g.ldc = d;
+      g.a = dqkvt[i]; g.lda = rt; g.b = x1t; g.ldb = rt; g.M = width[i]; g.N = d; g.K = rows; g.c = dw[i];
+      g.ldc = d;
       if (run_bwd_gemm_split(g, wsplit, L.partials, false, s, "bwd_dwqkv", err, n)) return 1;
     }
     BwdGemm g{};
-    g.a = dqkvb; g.lda = 3 * d; g.b = wqkvt; g.ldb = 3 * d; g.M = rows; g.N = d; g.K = 3 * d; g.c = L.dx1; g.ldc = d;
+    g.a = dqkvb; g.lda = k3; g.b = wqkvt; g.ldb = k3; g.M = rows; g.N = d; g.K = k3; g.c = L.dx1; g.ldc = d;
     if (run_bwd_gemm<kGStoreF32>(g, 1, s, "bwd_dx1", err, n)) return 1;
   }
   // ---- LN1 backward: dX = dY + LN1'(dLN1); LN1 gain / bias gradients

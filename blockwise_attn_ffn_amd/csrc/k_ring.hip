@@ -51,21 +51,23 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(float* __restrict__ o_a
 int launch_attention_fwd(const AttnFwdLaunch& A, void* stream, char* err, size_t n) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int B = A.batch, N = A.seq_len, Np = A.seq_pad, H = A.n_heads, dk = A.d_head, d = A.d_model;
-  if (d != H * dk || Np % 128 != 0 || Np < N || N < 1) {
+  const int G = A.n_kv_heads > 0 ? A.n_kv_heads : H, dkv = G * dk;
+  if (d != H * dk || Np % 128 != 0 || Np < N || N < 1 || H % G != 0) {
     set_err(err, n, "attention forward: inconsistent launch shape%s (seq_pad %d)", "", Np);
     return 1;
   }
   bf16* qp = static_cast<bf16*>(A.packed[0]);
   bf16* kp = static_cast<bf16*>(A.packed[1]);
   bf16* vtp = static_cast<bf16*>(A.packed[2]);
-  const long long chunks = (long long)B * Np * (d / 8);
+  const long long chunks = (long long)B * Np * (d / 8), kv_chunks = (long long)B * Np * (dkv / 8);
   hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
                      static_cast<const bf16*>(A.q), qp, (int)kRowsB, B, N, Np, H, dk);
-  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const bf16*>(A.k), kp, (int)kRowsA, B, N, Np, H, dk);
+  // K and V^T per key/value head
+  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((kv_chunks + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16*>(A.k), kp, (int)kRowsA, B, N, Np, G, dk);
   TransposeJob job{{static_cast<const bf16*>(A.v), nullptr, nullptr}, {vtp, nullptr, nullptr}};
-  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(B * H * (Np / 64) * (dk / 64)), 1),
-                     dim3(256), 0, s, job, N, Np, H, dk);
+  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(B * G * (Np / 64) * (dk / 64)), 1),
+                     dim3(256), 0, s, job, N, Np, G, dk);
   if (check_launch("attention_fwd pack", err, n)) return 1;
   // the layer's attention kernels on the packed operands (block sizes of the
   // tuned path: 128-row query blocks; 64-key blocks at d_k 128, 128 at d_k 64)
@@ -75,8 +77,10 @@ int launch_attention_fwd(const AttnFwdLaunch& A, void* stream, char* err, size_t
   L.seq_pad = Np;
   L.d_model = d;
   L.n_heads = H;
-  L.n_kv_heads = H;
-  L.d_kv = d;
+  L.n_kv_heads = G;
+  L.d_kv = dkv;
+  L.window = A.window;
+  L.chunk = A.chunk;
   L.d_head = dk;
   L.block_q = 128;
   L.block_kv = dk == 128 ? 64 : 128;

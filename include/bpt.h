@@ -382,9 +382,12 @@ size_t bpt_layer_bwd_workspace_bytes(const bpt_layer_desc_t* desc);
  *  - lse: DEVICE fp32 [batch, n_heads, seq_len], the statistic bpt_layer_fwd_lse
  *    wrote for this X and these weights.
  *  - dZ: DEVICE fp32 [rows, d_model].
+ * The masks (causal, window, chunk) and key/value heads (n_kv_heads; W_K, W_V and
+ * their gradients [n_kv_heads * d_head, d_model]) are those of bpt_layer_fwd; a
+ * key/value head's gradients sum over the query heads that read it.
  * Limits (else BPT_ERR_UNSUPPORTED before anything is enqueued): dtype BPT_BF16,
- * precision 0, window = chunk = 0, n_kv_heads 0 or n_heads; every other shape
- * bpt_layer_fwd takes (block_q, block_kv and out_dtype do not matter here).
+ * precision 0; every other shape bpt_layer_fwd takes (block_q, block_kv and
+ * out_dtype do not matter here).
  * Products take bf16 operands (activations and gradients rounded to bf16 where
  * they enter a product) with fp32 accumulation; the weight gradients sum over the
  * rows in a fixed order, so repeated calls give identical bits. Every device

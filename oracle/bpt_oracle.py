@@ -510,7 +510,7 @@ def gelu_tanh_derivative(u: np.ndarray) -> np.ndarray:
 
 
 def layer_backward(x: np.ndarray, p: dict, dz: np.ndarray, *, seq_len: int, n_heads: int,
-                   causal: bool, eps: float = 1e-5) -> dict:
+                   causal: bool, eps: float = 1e-5, window: int = 0, chunk: int = 0) -> dict:
     """Gradients of a loss L through one layer (layer_forward), given dz = dL/dZ.
 
     Returns a dict with dx (= dL/dX) and, in the pages' (in, out) orientation of
@@ -523,6 +523,8 @@ def layer_backward(x: np.ndarray, p: dict, dz: np.ndarray, *, seq_len: int, n_he
       attention (per sequence):     dQ, dK, dV = attention_backward_sequence(Q, K, V, dA)
       Q, K, V = LN1(X) W_{Q,K,V}:   dW_Q = LN1(X)^T dQ (and K, V), dLN1 = sum dQ W_Q^T ...
       LN1:                          dX += LN backward of dLN1 (and the LN1 gain / bias)
+    window / chunk: the mask of the forward (`visible`); fewer key/value heads than
+    query heads come from the widths of W_K and W_V, as in the forward.
     """
     x = np.asarray(x, F64)
     dz = np.asarray(dz, F64)
@@ -530,7 +532,7 @@ def layer_backward(x: np.ndarray, p: dict, dz: np.ndarray, *, seq_len: int, n_he
     rows = x.shape[0]
     assert rows % seq_len == 0 and dz.shape == x.shape
     _z, parts = layer_forward(x, p, seq_len=seq_len, n_heads=n_heads, causal=causal, eps=eps,
-                              return_parts=True)
+                              return_parts=True, window=window, chunk=chunk)
     x1, q, k, v, a, y = (parts[n] for n in ("x1", "q", "k", "v", "a", "y"))
     y2 = layer_norm(y, p["ln2_g"], p["ln2_b"], eps)
     u = y2 @ p["w_1"]
@@ -549,7 +551,7 @@ def layer_backward(x: np.ndarray, p: dict, dz: np.ndarray, *, seq_len: int, n_he
     for s0 in range(0, rows, seq_len):
         sl = slice(s0, s0 + seq_len)
         dq[sl], dk[sl], dv[sl] = attention_backward_sequence(q[sl], k[sl], v[sl], da[sl], n_heads,
-                                                             causal)
+                                                             causal, window, chunk)
     g["dw_q"], g["dw_k"], g["dw_v"] = x1.T @ dq, x1.T @ dk, x1.T @ dv
     dx1 = dq @ p["w_q"].T + dk @ p["w_k"].T + dv @ p["w_v"].T
     dx_ln, g["dln1_g"], g["dln1_b"] = layer_norm_backward(x, p["ln1_g"], dx1, eps)

@@ -362,11 +362,10 @@ def bwd_call(dsc, nbytes=None, **over):
                              args["dx"], ctypes.byref(g), args["ws"], nbytes, None)
 
 
-@pytest.mark.parametrize("field,value", [("dtype", bpt.F32), ("precision", 1), ("window", 16),
-                                         ("chunk", 64), ("n_kv_heads", 2)])
+@pytest.mark.parametrize("field,value", [("dtype", bpt.F32), ("precision", 1)])
 def test_layer_bwd_limits(field, value):
-    """The backward takes bf16 at precision 0, with no window, chunk or grouped heads:
-    anything else is BPT_ERR_UNSUPPORTED (nothing enqueued) and a workspace of 0."""
+    """The backward takes bf16 at precision 0: anything else is BPT_ERR_UNSUPPORTED
+    (nothing enqueued) and a workspace of 0."""
     dsc = desc()
     setattr(dsc, field, value)
     if field == "dtype":
@@ -374,6 +373,21 @@ def test_layer_bwd_limits(field, value):
     assert bpt.layer_bwd_workspace_bytes(dsc) == 0
     assert bwd_call(dsc) == 3
     assert bpt.last_error() != ""
+
+
+@pytest.mark.parametrize("field,value", [("window", 16), ("chunk", 64), ("n_kv_heads", 2), ("n_kv_heads", 1)])
+def test_layer_bwd_takes_masks_and_kv_heads(field, value):
+    """Window, chunk and grouped key/value heads are accepted (a workspace is sized);
+    inconsistent ones are rejected as for the forward."""
+    dsc = desc()
+    setattr(dsc, field, value)
+    assert bpt.layer_bwd_workspace_bytes(dsc) > 0
+    if field == "n_kv_heads":
+        dsc.n_kv_heads = 3                      # does not divide 4 heads
+    else:
+        dsc.causal = False                      # masks of the causal setting only
+    assert bpt.layer_bwd_workspace_bytes(dsc) == 0
+    assert bwd_call(dsc) == 2
 
 
 def test_layer_bwd_null_alignment_alias():

@@ -24,6 +24,8 @@ gradient, and max |err| 3e-2 times the largest reference magnitude.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -76,7 +78,7 @@ def oracle_grads(w: synth.Workload, inputs: dict, dz: torch.Tensor, seqs=None) -
         x, d = x[take], d[take]
     p = synth.oracle_weights(inputs["layers"][0])
     g = oracle.layer_backward(x, p, d, seq_len=w.seq_len, n_heads=w.n_heads, causal=w.causal,
-                              eps=w.ln_eps)
+                              eps=w.ln_eps, window=w.window, chunk=w.chunk)
     out = {"dx": g["dx"]}
     for k in GRAD_KEYS:
         a = g[ORACLE_KEY[k]]
@@ -123,6 +125,35 @@ def test_layer_bwd_small_every_element(case):
     inputs = synth.make_inputs(w, seed=11)
     dz = synth.make_grad_output(w.rows, d, seed=11)
     say(f"layer_bwd {name}: batch {batch} seq {n} d {d} heads {h} d_ff {f} causal {causal}")
+    (dx, grads), = run_fwd_bwd(w, inputs, dz)
+    check_all(dx, grads, oracle_grads(w, inputs, dz), name)
+
+
+MASKED = [
+    # name, batch, seq_len, d_model, n_heads, d_ff, window, chunk, n_kv_heads
+    ("window_dk64", 2, 200, 256, 4, 1024, 100, 0, 0),
+    ("chunk_dk64", 1, 300, 256, 4, 1024, 0, 96, 0),
+    ("gqa2_dk64", 2, 200, 256, 4, 1024, 0, 0, 2),
+    ("mqa_dk128", 1, 257, 256, 2, 512, 0, 0, 1),
+    ("window_gqa2_dk128", 1, 300, 512, 4, 1024, 64, 0, 2),
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=[c[0] for c in MASKED])
+def test_layer_bwd_masks_and_kv_heads(case):
+    """Every element against the oracle with a window, a chunked mask and fewer
+    key/value heads (W_K, W_V and their gradients [n_kv_heads d_k, d_model]), ragged
+    lengths. Weights of std 0.08 sqrt(256 / d_model), so that the projections (and
+    the scores' spread) match the d_model 256 cases: the relative error of the bf16
+    backward grows with the scores' spread (d_model 512 at std 0.08: ~1.1e-2 with no
+    mask and all heads, as with the mask and grouped heads)."""
+    name, batch, n, d, h, f, window, chunk, g = case
+    w = synth.Workload(name, batch=batch, seq_len=n, d_model=d, n_heads=h, d_ff=f, causal=True,
+                       block_q=128, block_kv=128 if d // h == 64 else 64, dtype="bf16", ln_random=True,
+                       w_std=0.08 * math.sqrt(256 / d), window=window, chunk=chunk, n_kv_heads=g)
+    inputs = synth.make_inputs(w, seed=13)
+    dz = synth.make_grad_output(w.rows, d, seed=13)
+    say(f"layer_bwd {name}: batch {batch} seq {n} d {d} heads {h}/{g or h} window {window} chunk {chunk}")
     (dx, grads), = run_fwd_bwd(w, inputs, dz)
     check_all(dx, grads, oracle_grads(w, inputs, dz), name)
 

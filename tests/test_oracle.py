@@ -1070,6 +1070,92 @@ def test_layer_backward_pins_hold_for_the_oracle():
     assert _layer_bwd_pins(oracle.layer_backward)
 
 
+def torch_layer_grads_masked(x, p, dz, seq_len, n_heads, eps=1e-5, window=0, chunk=0):
+    """As torch_layer_grads (causal), with the attention written out from torch ops:
+    per head the scaled scores, the mask built from positions here, torch.softmax and
+    the values; query head h reads key/value head h // (n_heads / g), g from the
+    width of W_K."""
+    t = {k: torch.tensor(np.asarray(v, np.float64), requires_grad=True) for k, v in p.items()}
+    xt = torch.tensor(np.asarray(x, np.float64), requires_grad=True)
+    rows, d = xt.shape
+    dk = d // n_heads
+    x1 = F.layer_norm(xt, (d,), t["ln1_g"], t["ln1_b"], eps)
+    q, k, v = x1 @ t["w_q"], x1 @ t["w_k"], x1 @ t["w_v"]
+    g = k.shape[1] // dk
+    pos = torch.arange(seq_len)
+    allowed = pos[None, :] <= pos[:, None]
+    if window:
+        allowed &= pos[None, :] > pos[:, None] - window
+    if chunk:
+        allowed = (pos[None, :] // chunk) <= (pos[:, None] // chunk)
+    seqs = []
+    for b in range(rows // seq_len):
+        sl = slice(b * seq_len, (b + 1) * seq_len)
+        heads = []
+        for h in range(n_heads):
+            kh = h // (n_heads // g)
+            s_ = q[sl, h * dk:(h + 1) * dk] @ k[sl, kh * dk:(kh + 1) * dk].T / math.sqrt(dk)
+            heads.append(torch.softmax(s_.masked_fill(~allowed, -math.inf), dim=1) @ v[sl, kh * dk:(kh + 1) * dk])
+        seqs.append(torch.cat(heads, dim=1))
+    a = torch.cat(seqs, dim=0)
+    y = xt + a @ t["w_o"]
+    h_ = F.gelu(F.layer_norm(y, (d,), t["ln2_g"], t["ln2_b"], eps) @ t["w_1"], approximate="tanh")
+    z = y + h_ @ t["w_2"]
+    (z * torch.from_numpy(np.asarray(dz, np.float64))).sum().backward()
+    out = {"dx": xt.grad.numpy()}
+    for gk, pk in _PARAM_OF.items():
+        out[gk] = t[pk].grad.numpy()
+    return out
+
+
+_MASK_CASES = [dict(window=3, g=2), dict(chunk=4, g=2), dict(g=1), dict(window=2, g=1)]
+
+
+def _layer_bwd_mask_pins(fn):
+    """True iff fn agrees with torch autograd (every gradient to 1e-10) on causal
+    layers with a window, a chunked mask, one key/value head, and a window with one
+    key/value head (2 query heads)."""
+    rng = np.random.default_rng(97)
+    seq, b, d, h = 8, 2, 8, 2
+    dk = d // h
+    for case in _MASK_CASES:
+        x = rng.standard_normal((b * seq, d))
+        p = rand_layer(rng, d, 4 * d, std=0.5)
+        p["w_k"] = p["w_k"][:, :case["g"] * dk].copy()
+        p["w_v"] = p["w_v"][:, :case["g"] * dk].copy()
+        dz = rng.standard_normal((b * seq, d))
+        kw = dict(window=case.get("window", 0), chunk=case.get("chunk", 0))
+        got = fn(x, p, dz, seq_len=seq, n_heads=h, causal=True, **kw)
+        want = torch_layer_grads_masked(x, p, dz, seq, h, **kw)
+        for key in ("dx",) + _GRAD_KEYS:
+            if got[key].shape != want[key].shape or np.max(np.abs(got[key] - want[key])) > 1e-10:
+                return False
+    return True
+
+
+def test_layer_backward_masks_and_kv_heads_match_torch_autograd():
+    assert _layer_bwd_mask_pins(oracle.layer_backward)
+
+
+def test_layer_backward_mask_pins_catch_planted_mistakes(monkeypatch):
+    """The attention backward run without the window / chunk, or a key/value head's
+    gradients averaged over its query heads instead of summed, each fail."""
+    real = O.attention_backward_sequence
+
+    def unmasked(q, k, v, do, n_heads, causal, window=0, chunk=0):
+        return real(q, k, v, do, n_heads, causal)
+
+    def averaged(q, k, v, do, n_heads, causal, window=0, chunk=0):
+        dq, dk, dv = real(q, k, v, do, n_heads, causal, window, chunk)
+        r = n_heads * (q.shape[1] // n_heads) // k.shape[1]
+        return dq, dk / r, dv / r
+
+    for planted in (unmasked, averaged):
+        with monkeypatch.context() as mp:
+            mp.setattr(O, "attention_backward_sequence", planted)
+            assert not _layer_bwd_mask_pins(O.layer_backward), planted.__name__
+
+
 def test_layer_backward_pins_catch_planted_mistakes(monkeypatch):
     """Each slip fails a pin: the LN backward without its mean(g xh) term, GELU's
     derivative taken as the erf form's, W_1's gradient transposed into the wrong
