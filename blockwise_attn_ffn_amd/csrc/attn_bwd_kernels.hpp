@@ -461,4 +461,281 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
 }
 
 
+// dK, dV split by gradient: one workgroup of 8 waves per (sequence, key/value head,
+// 128-key block), two waves per 32 keys on one SIMD. Wave w < 4 (the P wave) forms
+// S = Q K^T and P and accumulates dV^T += dO^T P; its partner w + 4 (the dS wave)
+// forms dP = dO V^T for the same keys, dS = P * (dP - D) with the P handed over
+// through LDS (bf16, in the accumulator layout), and accumulates dK^T += Q^T dS.
+// Each wave holds one accumulator set and one of K, V, so the two fit on one SIMD.
+// Every query stage takes two half steps separated by barriers:
+//   first half:  P wave  S, P (exp2), P -> LDS     dS wave  dK^T += Q^T dS (previous stage)
+//   second half: P wave  dV^T += dO^T P            dS wave  dP, dS
+// so in each half one wave's matrix products run beside the other wave's vector
+// work. Stage operands (Q, dO^T, dO, Q^T as A fragments, and the rows' lse and D)
+// are double-buffered per kind and copied by the LDS-DMA path a step ahead; Q^T is
+// kept one half step longer, so its copy is issued at the middle barrier. Only the
+// step barrier waits for copies.
+template <int DK, int BQS, bool GENERAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkv_split_kernel(BwdArgs g) {
+  using O = Op<bf16>;
+  using F = O::frag;
+  constexpr int NW = 8, BK = 128, FB = 1024;
+  constexpr int KSD = DK / 16, QT = BQS / 32, DT = DK / 32, QK = BQS / 16;
+  constexpr int AFR = QT * KSD;                 // Q (or dO) fragments per stage
+  constexpr int TFR = DT * QK;                  // Q^T (or dO^T) fragments per stage
+  static_assert(AFR % NW == 0 && TFR % NW == 0 && KSD % NW == 0 && NW % QK == 0, "copy slots");
+  static_assert(BQS == 64, "statistics copy: one 16-byte slot per 4 rows of each statistic");
+  // per kind and stage parity; st: lse log2 e then D of the stage's rows (1 KB slot)
+  __shared__ __align__(16) unsigned char qa0[AFR * FB], qa1[AFR * FB];     // Q
+  __shared__ __align__(16) unsigned char da0[AFR * FB], da1[AFR * FB];     // dO
+  __shared__ __align__(16) unsigned char qt0[TFR * FB], qt1[TFR * FB];     // Q^T
+  __shared__ __align__(16) unsigned char dt0[TFR * FB], dt1[TFR * FB];     // dO^T
+  __shared__ __align__(16) unsigned char st0[FB], st1[FB];
+  __shared__ __align__(16) unsigned char px[4 * QK * FB];                 // P of the 4 P waves
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rho = lane & 31, hf = lane >> 5;
+  const bool pwave = wave < 4;
+  const int kg = wave & 3;                      // the wave pair's 32 keys
+  const int N = g.N, Np = g.Np, H = g.H, d = g.d;
+  const int nkb = (N + BK - 1) / BK;
+  const int G = GENERAL ? g.G : H, GS = GENERAL ? H / g.G : 1, dkv = GENERAL ? g.dkv : d;
+  const int bg = blockIdx.x / nkb, kbk = blockIdx.x - bg * nkb;
+  const int b = bg / G, gk = bg - b * G;
+  const int wave_k_first = kbk * BK + kg * 32, kpos = wave_k_first + rho;
+  const int nqs = (N + BQS - 1) / BQS;
+  int qs_begin = 0, qs_end = nqs;
+  if (g.causal) {
+    const int k0 = kbk * BK, k1 = min(k0 + BK, N) - 1;
+    int q_first = k0;
+    if (GENERAL && g.chunk) q_first = k0 / g.chunk * g.chunk;
+    qs_begin = q_first / BQS;
+    if (GENERAL && g.window) qs_end = min(nqs, (k1 + g.window - 1) / BQS + 1);
+  }
+  const int nst = qs_end - qs_begin, n_it = GS * nst;
+  const int fkv = gk * DK + 8 * hf;
+  const int prho = pi_row(rho);
+
+  auto stage_q0 = [&](int it) __attribute__((always_inline)) {
+    return (qs_begin + (GENERAL ? it % nst : it)) * BQS;
+  };
+  auto stage_bh = [&](int it) __attribute__((always_inline)) {
+    return b * H + (GENERAL ? gk * GS + it / nst : gk);
+  };
+  // A fragments over the stage's query rows (32-row tile t, feature k-step kk) from
+  // row-major X; copy slot q of wave w moves fragment NW q + w
+  auto issue_rows = [&](int it, const bf16* X, unsigned char* buf) __attribute__((always_inline)) {
+    const int q0 = stage_q0(it), bh = stage_bh(it);
+    const int fcol = (bh - b * H) * DK + 8 * hf;
+#pragma unroll
+    for (int q = 0; q < AFR / NW; ++q) {
+      const int f0 = NW * q, t = f0 / KSD, kk = f0 % KSD + wave;
+      const size_t row = (size_t)b * N + min(q0 + t * 32 + prho, N - 1);
+      dma16(X + row * d + fcol + kk * 16, buf + (f0 + wave) * FB);
+    }
+  };
+  // A fragments over features (32-feature tile, query k-step) from a transposed copy
+  auto issue_cols = [&](int it, const bf16* XT, unsigned char* buf) __attribute__((always_inline)) {
+    const int q0 = stage_q0(it), bh = stage_bh(it);
+    const size_t toff =
+        (((size_t)bh * DT + wave / QK) * (Np / 16) + q0 / 16 + wave % QK) * kFragElems + lane * 8;
+#pragma unroll
+    for (int q = 0; q < TFR / NW; ++q) {
+      const int f0 = NW * q, dt = f0 / QK;
+      dma16(XT + toff + (size_t)dt * (Np / 16) * kFragElems, buf + (f0 + wave) * FB);
+    }
+  };
+  // everything of stage it except Q^T; wave 0 copies the statistics (lanes 0-15:
+  // lse log2 e of the 64 rows, lanes 16-31: D; the other lanes repeat them)
+  auto issue_step = [&](int it, unsigned char* qa, unsigned char* da, unsigned char* dt,
+                        unsigned char* st) __attribute__((always_inline)) {
+    issue_rows(it, g.q, qa);
+    issue_cols(it, g.doT, dt);
+    issue_rows(it, g.dout, da);
+    if (wave == 0) {
+      const int l = lane & 31;
+      const float* src = (l < 16 ? g.L2 : g.Dp) + (size_t)stage_bh(it) * Np + stage_q0(it) + 4 * (l & 15);
+      dma16(src, st);
+    }
+  };
+
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool PW = decltype(role)::value;   // P wave or dS wave
+    // the wave's K (P waves) or V (dS waves) as B fragments over its 32 keys
+    F kvf[KSD];
+#pragma unroll
+    for (int kk = 0; kk < KSD; ++kk) kvf[kk] = ld_row_frag(PW ? g.k : g.v, b, kpos, N, dkv, fkv + kk * 16);
+    f32x16 acc[DT];                               // dV^T (P waves) or dK^T (dS waves)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
+    F pf[QK];                                     // P wave: P of the current stage
+    F dsf[QK];                                    // dS wave: dS of the previous stage
+    bool carry = false;                           // the held P / dS belongs to a live stage
+
+    auto stage_live = [&](int q0) __attribute__((always_inline)) {
+      if (wave_k_first > bwd_key_hi<GENERAL>(g, q0 + BQS - 1)) return false;
+      if (GENERAL && wave_k_first + 31 < bwd_key_lo<GENERAL>(g, q0)) return false;
+      return true;
+    };
+    // 8 consecutive rows' statistic (0: lse log2 e, 1: D) from a stage's slot
+    auto stat8 = [&](const unsigned char* st, int which, int qoff, float* v) __attribute__((always_inline)) {
+      const float* p = reinterpret_cast<const float*>(st) + 64 * which + qoff;
+      const float4 a = *reinterpret_cast<const float4*>(p);
+      const float4 c = *reinterpret_cast<const float4*>(p + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    };
+
+    // first half, P wave: S = Q K^T, P = exp2(S log2e / sqrt(d_k) - lse log2e) -> pf, px.
+    // Register i of tile t holds query q0 + t*32 + (i&8)*2 + 8hf + (i&7).
+    auto half_s = [&](int it, const unsigned char* qa, const unsigned char* st) __attribute__((always_inline)) {
+      const int q0 = stage_q0(it);
+      carry = stage_live(q0);
+      if (!carry) return;
+      const bool need_mask = wave_k_first + 31 > bwd_key_hi<GENERAL>(g, q0) ||
+                             (GENERAL && wave_k_first < bwd_key_lo<GENERAL>(g, q0 + BQS - 1));
+      f32x16 s[QT];
+#pragma unroll
+      for (int t = 0; t < QT; ++t) s[t] = f32x16{};
+      __builtin_amdgcn_s_setprio(1);              // its products first: the softmax waits on them
+#pragma unroll
+      for (int kk = 0; kk < KSD; ++kk)
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+          O::mma(s[t], ld_packed(reinterpret_cast<const bf16*>(qa + (t * KSD + kk) * FB), lane), kvf[kk]);
+      __builtin_amdgcn_s_setprio(0);
+      auto softmax = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            const int qoff = t * 32 + 16 * gg + 8 * hf;
+            float l8[8], pv[8];
+            stat8(st, 0, qoff, l8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float p = fast_exp2(fmaf(s[t][8 * gg + e], g.scale_log2e, -l8[e]));
+              if constexpr (decltype(masked)::value) {
+                const int qq = q0 + qoff + e;
+                if (GENERAL ? (kpos > bwd_key_hi<true>(g, qq) || kpos < bwd_key_lo<true>(g, qq))
+                            : (g.causal && kpos > qq))
+                  p = 0.f;
+              }
+              pv[e] = p;
+            }
+            pf[2 * t + gg] = O::from_f32(pv);
+          }
+      };
+      if (need_mask) softmax(BoolTag<true>{});
+      else softmax(BoolTag<false>{});
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk) *reinterpret_cast<F*>(px + (kg * QK + kk) * FB + lane * 16) = pf[kk];
+    };
+    // second half, P wave: dV^T += dO^T P
+    auto half_dv = [&](const unsigned char* dt) __attribute__((always_inline)) {
+      if (!carry) return;
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk)
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          O::mma(acc[t], ld_packed(reinterpret_cast<const bf16*>(dt + (t * QK + kk) * FB), lane), pf[kk]);
+    };
+    // second half, dS wave: dP = dO V^T, dS = P (dP - D) -> dsf
+    auto half_dp = [&](int it, const unsigned char* da, const unsigned char* st) __attribute__((always_inline)) {
+      carry = stage_live(stage_q0(it));
+      if (!carry) return;
+      f32x16 dp[QT];
+#pragma unroll
+      for (int t = 0; t < QT; ++t) dp[t] = f32x16{};
+      __builtin_amdgcn_s_setprio(1);              // its products first: dS waits on them
+#pragma unroll
+      for (int kk = 0; kk < KSD; ++kk)
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+          O::mma(dp[t], ld_packed(reinterpret_cast<const bf16*>(da + (t * KSD + kk) * FB), lane), kvf[kk]);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const F p8 = *reinterpret_cast<const F*>(px + (kg * QK + 2 * t + gg) * FB + lane * 16);
+          float d8[8], v[8];
+          stat8(st, 1, t * 32 + 16 * gg + 8 * hf, d8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (float)p8[e] * (dp[t][8 * gg + e] - d8[e]);
+          dsf[2 * t + gg] = O::from_f32(v);
+        }
+    };
+    // first half, dS wave: dK^T += Q^T dS of the previous stage
+    auto half_dk = [&](const unsigned char* qt) __attribute__((always_inline)) {
+      if (!carry) return;
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk)
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          O::mma(acc[t], ld_packed(reinterpret_cast<const bf16*>(qt + (t * QK + kk) * FB), lane), dsf[kk]);
+    };
+    // middle barrier: P's LDS stores complete, no copy waited for
+    auto half_barrier = []() __attribute__((always_inline)) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    // Step j (0..n_it) works on stage j, whose operands are in the parity-(j&1)
+    // buffers (Q^T of stage j-1 in qt[(j-1)&1]); stage j+1's copies go to the other
+    // parity, its Q^T at the middle barrier, once the dS waves are done with stage
+    // j-1's. Unrolled by two so that every buffer is chosen at compile time. Each role
+    // runs its own copy of the loop; both execute the same sequence of barriers.
+    if (n_it > 0) {
+      issue_step(0, qa0, da0, dt0, st0);
+      issue_cols(0, g.qT, qt0);
+    }
+    for (int it = 0; it <= n_it && n_it > 0; it += 2) {
+      wait_vmem();
+      __syncthreads();
+      if (it + 1 < n_it) issue_step(it + 1, qa1, da1, dt1, st1);
+      if constexpr (PW) {
+        if (it < n_it) half_s(it, qa0, st0);
+      } else {
+        half_dk(qt1);
+      }
+      half_barrier();
+      if (it + 1 < n_it) issue_cols(it + 1, g.qT, qt1);
+      if (it < n_it) {
+        if constexpr (PW) half_dv(dt0);
+        else half_dp(it, da0, st0);
+      }
+      if (it + 1 > n_it) break;
+      wait_vmem();
+      __syncthreads();
+      if (it + 2 < n_it) issue_step(it + 2, qa0, da0, dt0, st0);
+      if constexpr (PW) {
+        if (it + 1 < n_it) half_s(it + 1, qa1, st1);
+      } else {
+        half_dk(qt0);
+      }
+      half_barrier();
+      if (it + 2 < n_it) issue_cols(it + 2, g.qT, qt0);
+      if (it + 1 < n_it) {
+        if constexpr (PW) half_dv(dt1);
+        else half_dp(it + 1, da1, st1);
+      }
+    }
+    // register group gg of feature tile t holds features t*32 + 16gg + 8hf + [0, 8)
+    if (kpos < N) {
+      float* out = (PW ? g.dv : g.dk) + ((size_t)b * N + kpos) * dkv + (size_t)gk * DK;
+      const float sc = PW ? 1.f : g.scale;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = acc[t][8 * gg + e] * sc;
+          store8_f32(out + t * 32 + 16 * gg + 8 * hf, v);
+        }
+    }
+  };
+  if (pwave) run(BoolTag<true>{});
+  else run(BoolTag<false>{});
+}
+
 }  // namespace bpt
