@@ -22,8 +22,8 @@
 // dO are first transposed into packed fragments in the workspace ("cols-A": per
 // (sequence, head) A fragments over [d_k (pi order), tokens], zero past seq_len).
 // A first kernel also writes, per (sequence, head) and padded to Np rows,
-// D = rowsum(dO * O) and lse * log2(e) (+inf past seq_len, so that padded query
-// rows get P = 0).
+// -D = -rowsum(dO * O) (negated, so that it can start the dP accumulator) and
+// lse * log2(e) (+inf past seq_len, so that padded query rows get P = 0).
 //
 // The kernels are templates instantiated by the translation units that launch
 // them: k_attention_bwd.hip (compiled with the products kept in VGPRs) and
@@ -40,7 +40,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // Row statistics. One group of DK/8 consecutive threads per (token row, head),
 // each thread 8 consecutive features, so a wave reads whole rows contiguously:
-//   Dp[bh * Np + pos] = sum over the head's features of dO * O   (0 past N)
+//   Dp[bh * Np + pos] = -(sum over the head's features of dO * O)   (0 past N)
 //   L2[bh * Np + pos] = lse * log2(e)                          (+inf past N)
 template <int DK>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const bf16* __restrict__ dO,
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const bf16* __restrict__
   for (int o = CH / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
   if (c == 0) {
     const size_t i = ((size_t)b * H + h) * Np + pos;
-    Dp[i] = acc;
+    Dp[i] = -acc;
     L2[i] = pos < N ? lse[((size_t)b * H + h) * N + pos] * kLog2e : __builtin_inff();
   }
 }
@@ -81,7 +81,7 @@ struct RuntimeTag {};   // decide the masking inside the body, around the softma
 struct BwdArgs {
   const bf16 *q, *k, *v, *dout;                   // row-major [B N, d]
   const bf16 *kT, *qT, *doT;                      // cols-A fragments per (sequence, head)
-  const float *L2, *Dp;                           // [B H, Np]
+  const float *L2, *Dp;                           // [B H, Np]: lse log2 e, -D
   float *dq, *dk, *dv;                            // [B N, d] row-major
   int B, N, Np, H, d, causal;
   int G, dkv, window, chunk;                      // key/value heads, their width, masks
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
   // rows past N (the last block may reach beyond the padded Np rows): P = 0
   const bool live = qpos < N;
   const float l2 = live ? g.L2[(size_t)bh * Np + qpos] : __builtin_inff();
-  const float Dq = live ? g.Dp[(size_t)bh * Np + qpos] : 0.f;
+  const float nDq = live ? g.Dp[(size_t)bh * Np + qpos] : 0.f;   // -D
   f32x16 dq[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x16{};
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
             float p = fast_exp2(fmaf(s[t][i], g.scale_log2e, -l2));
             const int off = t * 32 + (i & 8) * 2 + (i & 7);
             if (decltype(masked)::value && (off > lim || (GENERAL && off < lim_lo))) p = 0.f;
-            v[e] = p * (dp[t][i] - Dq);
+            v[e] = p * (dp[t][i] + nDq);
           }
           dsf[2 * t + gg] = O::from_f32(v);
         }
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
                 p = 0.f;
             }
             pv[e] = p;
-            dv8[e] = p * (dp[t][8 * gg + e] - d8[e]);
+            dv8[e] = p * (dp[t][8 * gg + e] + d8[e]);   // d8: -D
           }
           pf[2 * t + gg] = O::from_f32(pv);
           dsf[2 * t + gg] = O::from_f32(dv8);
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_split_kernel(BwdArgs g) {
     }
   };
   // everything of stage it except Q^T; wave 0 copies the statistics (lanes 0-15:
-  // lse log2 e of the 64 rows, lanes 16-31: D; the other lanes repeat them)
+  // lse log2 e of the 64 rows, lanes 16-31: -D; the other lanes repeat them)
   auto issue_step = [&](int it, unsigned char* qa, unsigned char* da, unsigned char* dt,
                         unsigned char* st) __attribute__((always_inline)) {
     issue_rows(it, g.q, qa);
@@ -577,13 +577,43 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_split_kernel(BwdArgs g) {
       if (GENERAL && wave_k_first + 31 < bwd_key_lo<GENERAL>(g, q0)) return false;
       return true;
     };
-    // 8 consecutive rows' statistic (0: lse log2 e, 1: D) from a stage's slot
+    // 8 consecutive rows' statistic (0: lse log2 e, 1: -D) from a stage's slot
     auto stat8 = [&](const unsigned char* st, int which, int qoff, float* v) __attribute__((always_inline)) {
       const float* p = reinterpret_cast<const float*>(st) + 64 * which + qoff;
       const float4 a = *reinterpret_cast<const float4*>(p);
       const float4 c = *reinterpret_cast<const float4*>(p + 4);
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
     };
+
+    // c[t] += A(t, kk) B[kk] over all (kk, t), kk outer; A(t, kk) is the packed
+    // fragment at base + (t * TS + kk * KS) KB; its LDS reads run four products ahead
+    auto stream = [&](auto nt, auto nk, auto ts, auto ks, f32x16* c, const unsigned char* base,
+                      const F* bfr) __attribute__((always_inline)) {
+      constexpr int NT = decltype(nt)::value, NK = decltype(nk)::value;
+      constexpr int TS = decltype(ts)::value, KS = decltype(ks)::value;
+      constexpr int NN = NT * NK, DD = 4;
+      auto ld = [&](int j) __attribute__((always_inline)) {
+        return ld_packed(reinterpret_cast<const bf16*>(base + ((j % NT) * TS + (j / NT) * KS) * FB), lane);
+      };
+      F ring[DD];
+#pragma unroll
+      for (int j = 0; j < DD; ++j) ring[j] = ld(j);
+#pragma unroll
+      for (int j = 0; j < NN; ++j) {
+        // the order as written: the scheduler would otherwise pull each read down
+        // next to its product
+        __builtin_amdgcn_sched_barrier(0);
+        const F a = ring[j % DD];
+        if (j + DD < NN) ring[j % DD] = ld(j + DD);
+        O::mma(c[j % NT], a, bfr[j / NT]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using IQT = std::integral_constant<int, QT>;
+    using IDT = std::integral_constant<int, DT>;
+    using IKSD = std::integral_constant<int, KSD>;
+    using IQK = std::integral_constant<int, QK>;
+    using I1 = std::integral_constant<int, 1>;
 
     // first half, P wave: S = Q K^T, P = exp2(S log2e / sqrt(d_k) - lse log2e) -> pf, px.
     // Register i of tile t holds query q0 + t*32 + (i&8)*2 + 8hf + (i&7).
@@ -597,11 +627,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_split_kernel(BwdArgs g) {
 #pragma unroll
       for (int t = 0; t < QT; ++t) s[t] = f32x16{};
       __builtin_amdgcn_s_setprio(1);              // its products first: the softmax waits on them
-#pragma unroll
-      for (int kk = 0; kk < KSD; ++kk)
-#pragma unroll
-        for (int t = 0; t < QT; ++t)
-          O::mma(s[t], ld_packed(reinterpret_cast<const bf16*>(qa + (t * KSD + kk) * FB), lane), kvf[kk]);
+      stream(IQT{}, IKSD{}, IKSD{}, I1{}, s, qa, kvf);
       __builtin_amdgcn_s_setprio(0);
       auto softmax = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
@@ -633,46 +659,41 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_split_kernel(BwdArgs g) {
     // second half, P wave: dV^T += dO^T P
     auto half_dv = [&](const unsigned char* dt) __attribute__((always_inline)) {
       if (!carry) return;
-#pragma unroll
-      for (int kk = 0; kk < QK; ++kk)
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-          O::mma(acc[t], ld_packed(reinterpret_cast<const bf16*>(dt + (t * QK + kk) * FB), lane), pf[kk]);
+      stream(IDT{}, IQK{}, IQK{}, I1{}, acc, dt, pf);
     };
     // second half, dS wave: dP = dO V^T, dS = P (dP - D) -> dsf
     auto half_dp = [&](int it, const unsigned char* da, const unsigned char* st) __attribute__((always_inline)) {
       carry = stage_live(stage_q0(it));
       if (!carry) return;
+      // the accumulators start from -D of their rows: dP - D comes out of the products
       f32x16 dp[QT];
 #pragma unroll
-      for (int t = 0; t < QT; ++t) dp[t] = f32x16{};
+      for (int t = 0; t < QT; ++t)
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          float d8[8];
+          stat8(st, 1, t * 32 + 16 * gg + 8 * hf, d8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dp[t][8 * gg + e] = d8[e];
+        }
       __builtin_amdgcn_s_setprio(1);              // its products first: dS waits on them
-#pragma unroll
-      for (int kk = 0; kk < KSD; ++kk)
-#pragma unroll
-        for (int t = 0; t < QT; ++t)
-          O::mma(dp[t], ld_packed(reinterpret_cast<const bf16*>(da + (t * KSD + kk) * FB), lane), kvf[kk]);
+      stream(IQT{}, IKSD{}, IKSD{}, I1{}, dp, da, kvf);
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int t = 0; t < QT; ++t)
 #pragma unroll
         for (int gg = 0; gg < 2; ++gg) {
           const F p8 = *reinterpret_cast<const F*>(px + (kg * QK + 2 * t + gg) * FB + lane * 16);
-          float d8[8], v[8];
-          stat8(st, 1, t * 32 + 16 * gg + 8 * hf, d8);
+          float v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (float)p8[e] * (dp[t][8 * gg + e] - d8[e]);
+          for (int e = 0; e < 8; ++e) v[e] = (float)p8[e] * dp[t][8 * gg + e];
           dsf[2 * t + gg] = O::from_f32(v);
         }
     };
     // first half, dS wave: dK^T += Q^T dS of the previous stage
     auto half_dk = [&](const unsigned char* qt) __attribute__((always_inline)) {
       if (!carry) return;
-#pragma unroll
-      for (int kk = 0; kk < QK; ++kk)
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-          O::mma(acc[t], ld_packed(reinterpret_cast<const bf16*>(qt + (t * QK + kk) * FB), lane), dsf[kk]);
+      stream(IDT{}, IQK{}, IQK{}, I1{}, acc, qt, dsf);
     };
     // middle barrier: P's LDS stores complete, no copy waited for
     auto half_barrier = []() __attribute__((always_inline)) {

@@ -200,7 +200,7 @@ typedef struct {
  * n_kv_heads 0 or n_heads.)
  * Bytes of workspace bpt_attention_bwd needs (0 for an empty call, or 0 with
  * bpt_last_error() set when desc is invalid): two fp32 row statistics [batch,
- * n_heads, Np] (D = rowsum(dO * O) and lse in base 2), with Np = seq_len rounded
+ * n_heads, Np] (-D, D = rowsum(dO * O), and lse in base 2), with Np = seq_len rounded
  * up to 128, and transposed bf16 copies of K, Q and dO, each [batch * Np,
  * d_model]. Nothing of size seq_len x seq_len. */
 size_t bpt_attention_bwd_workspace_bytes(const bpt_attn_desc_t* desc);
