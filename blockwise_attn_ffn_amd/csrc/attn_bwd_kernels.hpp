@@ -524,39 +524,49 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_split_kernel(BwdArgs g) {
   };
   // A fragments over the stage's query rows (32-row tile t, feature k-step kk) from
   // row-major X; copy slot q of wave w moves fragment NW q + w
+  // Copy addresses are a wave-uniform base plus a per-lane byte offset fixed for the
+  // whole kernel (rows inside the sequence: every stage but a ragged last one).
+  const unsigned lane_row_b = (unsigned)(prho * d + 8 * hf) * 2u;   // row-major operand
+  const unsigned lane_frag_b = (unsigned)lane * 16u;                // packed fragment
   auto issue_rows = [&](int it, const bf16* X, unsigned char* buf) __attribute__((always_inline)) {
     const int q0 = stage_q0(it), bh = stage_bh(it);
-    const int fcol = (bh - b * H) * DK + 8 * hf;
+    const int fcol = (bh - b * H) * DK;
+    if (q0 + BQS <= N) {
+      const char* base = reinterpret_cast<const char*>(X + ((size_t)b * N + q0) * d + fcol + wave * 16);
 #pragma unroll
-    for (int q = 0; q < AFR / NW; ++q) {
-      const int f0 = NW * q, t = f0 / KSD, kk = f0 % KSD + wave;
-      const size_t row = (size_t)b * N + min(q0 + t * 32 + prho, N - 1);
-      dma16(X + row * d + fcol + kk * 16, buf + (f0 + wave) * FB);
+      for (int q = 0; q < AFR / NW; ++q) {
+        const int f0 = NW * q, t = f0 / KSD;
+        dma16(base + (size_t)t * 32 * d * 2 + lane_row_b, buf + (f0 + wave) * FB);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < AFR / NW; ++q) {
+        const int f0 = NW * q, t = f0 / KSD, kk = f0 % KSD + wave;
+        const size_t row = (size_t)b * N + min(q0 + t * 32 + prho, N - 1);
+        dma16(X + row * d + fcol + 8 * hf + kk * 16, buf + (f0 + wave) * FB);
+      }
     }
   };
   // A fragments over features (32-feature tile, query k-step) from a transposed copy
   auto issue_cols = [&](int it, const bf16* XT, unsigned char* buf) __attribute__((always_inline)) {
     const int q0 = stage_q0(it), bh = stage_bh(it);
-    const size_t toff =
-        (((size_t)bh * DT + wave / QK) * (Np / 16) + q0 / 16 + wave % QK) * kFragElems + lane * 8;
+    const char* base = reinterpret_cast<const char*>(
+        XT + (((size_t)bh * DT + wave / QK) * (Np / 16) + q0 / 16 + wave % QK) * kFragElems);
 #pragma unroll
     for (int q = 0; q < TFR / NW; ++q) {
       const int f0 = NW * q, dt = f0 / QK;
-      dma16(XT + toff + (size_t)dt * (Np / 16) * kFragElems, buf + (f0 + wave) * FB);
+      dma16(base + (size_t)dt * (Np / 16) * kFragElems * 2 + lane_frag_b, buf + (f0 + wave) * FB);
     }
   };
   // everything of stage it except Q^T; wave 0 copies the statistics (lanes 0-15:
   // lse log2 e of the 64 rows, lanes 16-31: -D; the other lanes repeat them)
+  const float* stat_lane = ((lane & 31) < 16 ? g.L2 : g.Dp) + 4 * (lane & 15);
   auto issue_step = [&](int it, unsigned char* qa, unsigned char* da, unsigned char* dt,
                         unsigned char* st) __attribute__((always_inline)) {
     issue_rows(it, g.q, qa);
     issue_cols(it, g.doT, dt);
     issue_rows(it, g.dout, da);
-    if (wave == 0) {
-      const int l = lane & 31;
-      const float* src = (l < 16 ? g.L2 : g.Dp) + (size_t)stage_bh(it) * Np + stage_q0(it) + 4 * (l & 15);
-      dma16(src, st);
-    }
+    if (wave == 0) dma16(stat_lane + (size_t)stage_bh(it) * Np + stage_q0(it), st);
   };
 
   auto run = [&](auto role) __attribute__((always_inline)) {
