@@ -219,25 +219,42 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs g) {
     };
     // The body branches around the softmax only: a body specialised per masking
     // mode (straight-line) holds more registers live and measured no faster.
+    auto ld_a = [&](int f) __attribute__((always_inline)) {
+      return ld_packed(reinterpret_cast<const bf16*>(buf + f * FB), lane);
+    };
     auto body = [&](RuntimeTag) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < KT; ++t) { s[t] = f32x16{}; dp[t] = f32x16{}; }
+      // products in the order written, each LDS read four products ahead
+      constexpr int DD = 4, N1 = 2 * KT * KSD, N2 = DT * KK;
+      // first: (kk, t, S or dP) -> fragment (S: t KSD + kk, dP: KFR + t KSD + kk)
+      auto f1 = [](int x) { const int kk = x / (2 * KT), t = (x / 2) % KT; return (x & 1) * KFR + t * KSD + kk; };
+      F ring[DD];
 #pragma unroll
-      for (int kk = 0; kk < KSD; ++kk)
+      for (int x = 0; x < DD; ++x) ring[x] = ld_a(f1(x));
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          O::mma(s[t], ld_packed(reinterpret_cast<const bf16*>(buf + (t * KSD + kk) * FB), lane), qf[kk]);
-          O::mma(dp[t], ld_packed(reinterpret_cast<const bf16*>(buf + (KFR + t * KSD + kk) * FB), lane),
-                 of[kk]);
-        }
+      for (int x = 0; x < N1; ++x) {
+        __builtin_amdgcn_sched_barrier(0);
+        const F a = ring[x % DD];
+        if (x + DD < N1) ring[x % DD] = ld_a(f1(x + DD));
+        const int kk = x / (2 * KT), t = (x / 2) % KT;
+        if (x & 1) O::mma(dp[t], a, of[kk]);
+        else O::mma(s[t], a, qf[kk]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       if (need_mask) softmax_grad(BoolTag<true>{});
       else softmax_grad(BoolTag<false>{});
+      // then dQ^T: (kk, t) -> fragment 2 KFR + t KK + kk
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
+      for (int x = 0; x < DD; ++x) ring[x] = ld_a(2 * KFR + (x % DT) * KK + x / DT);
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-          O::mma(dq[t], ld_packed(reinterpret_cast<const bf16*>(buf + (2 * KFR + t * KK + kk) * FB), lane),
-                 dsf[kk]);
+      for (int x = 0; x < N2; ++x) {
+        __builtin_amdgcn_sched_barrier(0);
+        const F a = ring[x % DD];
+        if (x + DD < N2) ring[x % DD] = ld_a(2 * KFR + ((x + DD) % DT) * KK + (x + DD) / DT);
+        O::mma(dq[x % DT], a, dsf[x / DT]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
     body(RuntimeTag{});
   };
