@@ -178,6 +178,10 @@ VARIANTS = [
     (1, 333, 512, 4, dict(n_kv_heads=2)),            # d_k 128
     (2, 180, 256, 4, dict(n_kv_heads=2, window=50)),
     (1, 300, 512, 4, dict(n_kv_heads=1, chunk=64)),
+    # d_k 128 over many 64-row query stages, a ragged last stage and two query heads
+    # per key/value head (the split dK / dV kernel's grouped-head stage loop)
+    (1, 2000, 512, 4, dict(n_kv_heads=2, window=300)),
+    (1, 1500, 512, 4, dict(n_kv_heads=2, chunk=256)),
 ]
 
 
