@@ -1,9 +1,8 @@
 // Attention backward: host launch sequence (the kernels: attn_bwd_kernels.hpp).
 // Compiled with the matrix-core results kept in VGPRs (they feed the softmax
-// arithmetic at once); the d_k 128 dK / dV kernel, whose accumulators do not fit
-// beside its other state, is instantiated in k_attention_bwd_dkv.hip without that
-// setting (measured 215.7 -> 190.6 ms on the 131072-token backward, while the d_k
-// 64 instance is 45% slower without it).
+// arithmetic at once; the d_k 64 instances are 45% slower without it); the d_k 128
+// dK / dV kernel (split by gradient over two waves per SIMD) is instantiated in
+// k_attention_bwd_dkv.hip without that setting.
 #include "attn_bwd_kernels.hpp"
 
 namespace bpt {
@@ -76,21 +75,21 @@ int run_bwd(const AttnBwdLaunch& L, hipStream_t s, char* err, size_t n) {
   // d_k 128: 8 waves share each key/value stage (two per SIMD, 256 query rows);
   // d_k 64: 4 waves, and two workgroups fit one compute unit
   constexpr int DQW = DK == 128 ? 8 : 4;
-  // dK / dV: 4 waves and 64-row query stages (8 waves with 32-row stages would
-  // give two waves per SIMD at d_k 128, but the accumulators then spill: slower)
+  // dK / dV at d_k 64: 4 waves and 64-row query stages; at d_k 128 the split kernel
+  // of k_attention_bwd_dkv.hip, also one workgroup per 128 keys
   constexpr int DKW = 4, DKQ = 64;
   const int nqb = (L.seq_len + 32 * DQW - 1) / (32 * DQW);
   const int nkb = (L.seq_len + 32 * DKW - 1) / (32 * DKW);
   // masks or grouped key/value heads run the general instances
   const bool general = L.window || L.chunk || L.n_kv_heads != L.n_heads;
   auto kdq = general ? bwd_dq_kernel<DK, DQW, true> : bwd_dq_kernel<DK, DQW, false>;
-  // (d_k 128: instantiated in k_attention_bwd_dkv.hip)
+  // (d_k 128: launch_bwd_dkv128)
   auto kdkv = general ? bwd_dkv_kernel<DK == 128 ? 64 : DK, DKW, DKQ, true>
                       : bwd_dkv_kernel<DK == 128 ? 64 : DK, DKW, DKQ, false>;
   hipLaunchKernelGGL(kdq, dim3(bhs * nqb), dim3(64 * DQW), 0, s, g);
   if (check_launch("bwd_dq", err, n) || mark(L, 3, s, err, n)) return 1;
   if constexpr (DK == 128) {
-    static_assert(DKW == 4 && DKQ == 64, "launch_bwd_dkv128 instantiates <128, 4, 64>");
+    static_assert(32 * DKW == 128, "launch_bwd_dkv128 takes one workgroup per 128 keys");
     launch_bwd_dkv128(g, bgs * nkb, general, s);
   } else {
     hipLaunchKernelGGL(kdkv, dim3(bgs * nkb), dim3(64 * DKW), 0, s, g);
