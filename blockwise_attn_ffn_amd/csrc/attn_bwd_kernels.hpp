@@ -488,7 +488,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
 //   first half:  P wave  S, P (exp2), P -> LDS     dS wave  dK^T += Q^T dS (previous stage)
 //   second half: P wave  dV^T += dO^T P            dS wave  dP, dS
 // so in each half one wave's matrix products run beside the other wave's vector
-// work. Stage operands (Q, dO^T, dO, Q^T as A fragments, and the rows' lse and D)
+// work. Stage operands (Q, dO^T, dO, Q^T as A fragments, and the rows' lse and -D)
 // are double-buffered per kind and copied by the LDS-DMA path a step ahead; Q^T is
 // kept one half step longer, so its copy is issued at the middle barrier. Only the
 // step barrier waits for copies.
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_split_kernel(BwdArgs g) {
   constexpr int TFR = DT * QK;                  // Q^T (or dO^T) fragments per stage
   static_assert(AFR % NW == 0 && TFR % NW == 0 && KSD % NW == 0 && NW % QK == 0, "copy slots");
   static_assert(BQS == 64, "statistics copy: one 16-byte slot per 4 rows of each statistic");
-  // per kind and stage parity; st: lse log2 e then D of the stage's rows (1 KB slot)
+  // per kind and stage parity; st: lse log2 e then -D of the stage's rows (1 KB slot)
   __shared__ __align__(16) unsigned char qa0[AFR * FB], qa1[AFR * FB];     // Q
   __shared__ __align__(16) unsigned char da0[AFR * FB], da1[AFR * FB];     // dO
   __shared__ __align__(16) unsigned char qt0[TFR * FB], qt1[TFR * FB];     // Q^T
