@@ -395,10 +395,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
           const int qoff = t * 32 + 16 * gg + 8 * hf;          // 8 consecutive queries
           const float4 la = *reinterpret_cast<const float4*>(st + qoff);
           const float4 lb = *reinterpret_cast<const float4*>(st + qoff + 4);
-          const float4 da = *reinterpret_cast<const float4*>(st + BQS + qoff);
-          const float4 db = *reinterpret_cast<const float4*>(st + BQS + qoff + 4);
           const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-          const float d8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
           float pv[8], dv8[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -410,7 +407,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
                 p = 0.f;
             }
             pv[e] = p;
-            dv8[e] = p * (dp[t][8 * gg + e] + d8[e]);   // d8: -D
+            dv8[e] = p * dp[t][8 * gg + e];   // dp holds dP - D
           }
           pf[2 * t + gg] = O::from_f32(pv);
           dsf[2 * t + gg] = O::from_f32(dv8);
@@ -419,8 +416,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkv_kernel(BwdArgs g) {
     };
     // branching around the softmax only (as in dQ)
     auto body = [&](RuntimeTag) __attribute__((always_inline)) {
+      // the dP accumulators start from -D of their rows: dP - D comes out of the products
 #pragma unroll
-      for (int t = 0; t < QT; ++t) { s[t] = f32x16{}; dp[t] = f32x16{}; }
+      for (int t = 0; t < QT; ++t) {
+        s[t] = f32x16{};
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const float4 da = *reinterpret_cast<const float4*>(st + BQS + t * 32 + 16 * gg + 8 * hf);
+          const float4 db = *reinterpret_cast<const float4*>(st + BQS + t * 32 + 16 * gg + 8 * hf + 4);
+          dp[t][8 * gg + 0] = da.x; dp[t][8 * gg + 1] = da.y; dp[t][8 * gg + 2] = da.z; dp[t][8 * gg + 3] = da.w;
+          dp[t][8 * gg + 4] = db.x; dp[t][8 * gg + 5] = db.y; dp[t][8 * gg + 6] = db.z; dp[t][8 * gg + 7] = db.w;
+        }
+      }
 #pragma unroll
       for (int kk = 0; kk < KSD; ++kk)
 #pragma unroll
