@@ -81,6 +81,7 @@ SMALL = [
     (1, 1000, 512, 4, True, 2.0),
     (3, 200, 128, 1, False, 1.5),
     (1, 513, 256, 4, False, 0.5),
+    (2, 700, 256, 2, True, 1.0),        # d_k 128, causal, two sequences, ragged last stage
 ]
 
 
